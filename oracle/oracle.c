@@ -1,0 +1,242 @@
+/*
+ * CPU oracle for the decomposed tensor-parallel collective matmuls.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
+ * load this file; only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark use it.  It shares no code, header, helper or
+ * constant with the GPU library.
+ *
+ * What it computes is the monolithic definition that the decomposed method
+ * must reproduce exactly (up to floating-point summation order):
+ *
+ *   AllGather -> GEMM   (column-parallel linear after a sequence-sharded
+ *                        activation; "Hiding Tensor-Parallel Collectives:
+ *                        AG/RS Overlap in Megatron", sections 1-2):
+ *       Xfull = concat_r X_r   (rows, rank order)
+ *       Y_r   = Xfull . W_r^T  for every rank r
+ *
+ *   GEMM -> ReduceScatter (row-parallel linear; same page, section 4):
+ *       Z_r   = H_r . W_r^T
+ *       Out_q = sum_r Z_r[q*m:(q+1)*m, :]   (sum taken in rank order)
+ *
+ *   AllReduce (used only as an invariant: "Tensor Parallelism > Communication
+ *   Patterns", the paragraph on all-reduce being a reduce-scatter followed by
+ *   an all-gather):
+ *       AR = sum_r Z_r
+ *
+ * The decomposition page ("Overlap Communication with Dependent Computation
+ * via Decomposition in Large Deep Learning Models", sections "The idea" and
+ * "Why it works") states that the decomposed computation equals this
+ * monolithic one because concatenation and summation are linear, so the
+ * oracle is the definition written out, with no blocking or reordering.
+ *
+ * Conventions
+ *   - Inputs are bf16 bit patterns (uint16).  A bf16 value is by definition
+ *     the upper 16 bits of an IEEE binary32, so each converts exactly to
+ *     float and then to double.
+ *   - Weights are stored [n][k] (row j of W_r holds output feature j, its k
+ *     entries contiguous), so Y[i][j] = sum_k A[i][k] * W[j][k].
+ *   - All accumulation is fp64, in increasing k.
+ *   - "mag" outputs, when not NULL, receive sum_k |a_ik| * |w_jk| over the
+ *     same (full) contraction, which scales the floating-point error bound.
+ *
+ * Parity pins: see the tests (brute force on tiny shapes, closed forms,
+ * N = 1 against a library matmul, the AllReduce invariant, planted
+ * mistakes).  The bf16 rounding routine is pinned by hand-derived tie cases.
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static double bf16_value(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* out[j] = sum_kk a[kk] * w[j][kk] for one activation row a (length k)
+ * against every row j of one weight matrix w ([n][k]); mag likewise with
+ * absolute values. */
+static void row_times_weight(const uint16_t *a, const uint16_t *w, int k, int n,
+                             double *out, double *mag) {
+  for (int j = 0; j < n; ++j) {
+    const uint16_t *wj = w + (size_t)j * k;
+    double acc = 0.0;
+    for (int kk = 0; kk < k; ++kk) acc += bf16_value(a[kk]) * bf16_value(wj[kk]);
+    out[j] = acc;
+    if (mag) {
+      double accabs = 0.0;
+      for (int kk = 0; kk < k; ++kk) accabs += fabs(bf16_value(a[kk])) * fabs(bf16_value(wj[kk]));
+      mag[j] = accabs;
+    }
+  }
+}
+
+int orc_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* Row i (0 <= i < N*m) of Xfull = concat_r X_r: shard i / m, local row i % m. */
+static const uint16_t *xfull_row(const uint16_t *x, int m, int k, int i) {
+  int shard = i / m;
+  int local = i % m;
+  return x + ((size_t)shard * m + local) * k;
+}
+
+/*
+ * AllGather -> GEMM, monolithic.
+ *   x   [N][m][k]     shard r = X_r
+ *   w   [N][n][k]     W_r
+ *   y   [N][N*m][n]   Y_r = Xfull . W_r^T
+ *   mag same shape as y, or NULL
+ */
+void orc_ag_gemm(int N, int m, int k, int n, const uint16_t *x, const uint16_t *w,
+                 double *y, double *mag) {
+  const int T = N * m;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int r = 0; r < N; ++r)
+    for (int i = 0; i < T; ++i) {
+      size_t o = ((size_t)r * T + i) * n;
+      row_times_weight(xfull_row(x, m, k, i), w + (size_t)r * n * k, k, n, y + o,
+                       mag ? mag + o : NULL);
+    }
+}
+
+/*
+ * The same definition evaluated only at selected (rank, row) pairs, for
+ * checking sampled outputs of full-size runs and for timing a bounded sample.
+ *   rank[s], row[s]: rank r and row i of Y_r (0 <= i < N*m)
+ *   y   [ns][n], mag [ns][n] or NULL
+ */
+void orc_ag_gemm_rows(int N, int m, int k, int n, const uint16_t *x, const uint16_t *w,
+                      int ns, const int *rank, const int *row, double *y, double *mag) {
+  (void)N;
+#pragma omp parallel for schedule(dynamic)
+  for (int s = 0; s < ns; ++s)
+    row_times_weight(xfull_row(x, m, k, row[s]), w + (size_t)rank[s] * n * k, k, n,
+                     y + (size_t)s * n, mag ? mag + (size_t)s * n : NULL);
+}
+
+/* Out_q row i: sum over ranks r (in rank order) of Z_r[q*m + i][:]. */
+static void rs_row(int N, int m, int k, int n, const uint16_t *h, const uint16_t *w, int q,
+                   int i, double *out, double *mag, double *zrow, double *zmag) {
+  const size_t T = (size_t)N * m;
+  for (int j = 0; j < n; ++j) {
+    out[j] = 0.0;
+    if (mag) mag[j] = 0.0;
+  }
+  for (int r = 0; r < N; ++r) {
+    const uint16_t *hrow = h + ((size_t)r * T + (size_t)q * m + i) * k;
+    row_times_weight(hrow, w + (size_t)r * n * k, k, n, zrow, zmag);
+    for (int j = 0; j < n; ++j) {
+      out[j] += zrow[j];
+      if (mag) mag[j] += zmag[j];
+    }
+  }
+}
+
+/*
+ * GEMM -> ReduceScatter, monolithic.
+ *   h   [N][N*m][k]   H_r (rank r's full-sequence activation, its k = f/N slice)
+ *   w   [N][n][k]     W_r
+ *   out [N][m][n]     Out_q
+ *   mag same shape as out, or NULL (sum over all ranks' contraction)
+ */
+void orc_gemm_rs(int N, int m, int k, int n, const uint16_t *h, const uint16_t *w, double *out,
+                 double *mag) {
+#pragma omp parallel
+  {
+    double *zrow = (double *)malloc(sizeof(double) * 2 * (size_t)n);
+    double *zmag = zrow + n;
+#pragma omp for collapse(2) schedule(static)
+    for (int q = 0; q < N; ++q)
+      for (int i = 0; i < m; ++i) {
+        size_t o = ((size_t)q * m + i) * n;
+        rs_row(N, m, k, n, h, w, q, i, out + o, mag ? mag + o : NULL, zrow, mag ? zmag : NULL);
+      }
+    free(zrow);
+  }
+}
+
+/* Sampled form: owner[s] = q, row[s] = i (0 <= i < m); out [ns][n]. */
+void orc_gemm_rs_rows(int N, int m, int k, int n, const uint16_t *h, const uint16_t *w, int ns,
+                      const int *owner, const int *row, double *out, double *mag) {
+#pragma omp parallel
+  {
+    double *zrow = (double *)malloc(sizeof(double) * 2 * (size_t)n);
+    double *zmag = zrow + n;
+#pragma omp for schedule(dynamic)
+    for (int s = 0; s < ns; ++s)
+      rs_row(N, m, k, n, h, w, owner[s], row[s], out + (size_t)s * n,
+             mag ? mag + (size_t)s * n : NULL, zrow, mag ? zmag : NULL);
+    free(zrow);
+  }
+}
+
+/*
+ * AllReduce of the row-parallel partials: ar [N*m][n] = sum_r H_r . W_r^T,
+ * over whole T-row matrices (no bucketing), ranks summed in order.
+ */
+void orc_allreduce(int N, int m, int k, int n, const uint16_t *h, const uint16_t *w, double *ar) {
+  const int T = N * m;
+#pragma omp parallel
+  {
+    double *zrow = (double *)malloc(sizeof(double) * (size_t)n);
+#pragma omp for schedule(static)
+    for (int i = 0; i < T; ++i) {
+      double *dst = ar + (size_t)i * n;
+      for (int j = 0; j < n; ++j) dst[j] = 0.0;
+      for (int r = 0; r < N; ++r) {
+        row_times_weight(h + ((size_t)r * T + i) * k, w + (size_t)r * n * k, k, n, zrow, NULL);
+        for (int j = 0; j < n; ++j) dst[j] += zrow[j];
+      }
+    }
+    free(zrow);
+  }
+}
+
+/*
+ * Round each double to the nearest bfloat16 value, ties to the value whose
+ * last significand bit is zero (round-half-to-even), returning bit patterns.
+ * bfloat16: 1 sign bit, 8 exponent bits (bias 127), 7 stored significand
+ * bits; normal values carry 8 significant bits, so the spacing of values in
+ * [2^e, 2^(e+1)) is 2^(e-7); below 2^-126 the spacing is fixed at 2^-133.
+ * Magnitudes that round above the largest finite value become infinity.
+ * Written from that definition (nearbyint rounds ties to even under the
+ * default rounding mode), not from any bit-manipulation shortcut.
+ */
+void orc_round_bf16(const double *in, uint16_t *out, size_t count) {
+  const double max_finite = ldexp(255.0, 127 - 7); /* (2 - 2^-7) * 2^127 */
+  for (size_t t = 0; t < count; ++t) {
+    double v = in[t];
+    double r;
+    if (v == 0.0 || isnan(v) || isinf(v)) {
+      r = v;
+    } else {
+      double a = fabs(v);
+      int e;
+      frexp(a, &e); /* a = f * 2^e with f in [0.5, 1): a in [2^(e-1), 2^e) */
+      int exp2 = e - 1;
+      if (exp2 < -126) exp2 = -126; /* subnormal spacing */
+      double quantum = ldexp(1.0, exp2 - 7);
+      double q = nearbyint(a / quantum) * quantum;
+      if (q > max_finite) q = INFINITY;
+      r = v < 0 ? -q : q;
+    }
+    float f = (float)r; /* exact: r is a bf16 value, representable in binary32 */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if (isnan(r)) u = 0x7FC00000u;
+    out[t] = (uint16_t)(u >> 16);
+  }
+}
