@@ -1,0 +1,239 @@
+"""ctypes binding of libcollmm (include/collmm.h): argument marshalling only.
+
+Every call goes straight to the C ABI; all arithmetic runs in the library's
+HIP kernels and copy engines.  There is no fallback: if libcollmm.so is
+missing the import of these entry points fails loudly.
+"""
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libcollmm.so")
+
+# enums (collmm.h)
+CM_OK, CM_ERR_INVALID_ARG, CM_ERR_SHAPE, CM_ERR_ALIGN, CM_ERR_WORKSPACE, CM_ERR_UNSUPPORTED, CM_ERR_HIP, \
+    CM_ERR_CAPACITY = range(8)
+CM_OP_AG_GEMM, CM_OP_GEMM_RS, CM_OP_GEMM_RS_PIPE = range(3)
+CM_RING_UNI, CM_RING_BI = range(2)
+CM_SCHED_DECOMPOSED, CM_SCHED_NAIVE = range(2)
+CM_BF16, CM_F32 = range(2)
+CM_BUF_X, CM_BUF_W, CM_BUF_Y, CM_BUF_WS = range(4)
+CM_OPK_GEMM, CM_OPK_COPY, CM_OPK_RECORD, CM_OPK_WAIT, CM_OPK_REDUCE = range(5)
+CM_MAX_RANKS, CM_MAX_CHUNKS, CM_MAX_COMM = 64, 16, 32
+
+EXPORTS = ["cm_ring_plan", "cm_workspace_size", "cm_plan_program", "cm_trace_create", "cm_trace_destroy",
+           "cm_trace_read", "cm_ag_gemm", "cm_gemm_rs", "cm_status_string", "cm_last_error", "cm_version"]
+
+
+class cm_plan_desc(ctypes.Structure):
+    _fields_ = [("op", ctypes.c_int), ("n_ranks", ctypes.c_int), ("m", ctypes.c_int), ("k", ctypes.c_int),
+                ("n", ctypes.c_int), ("dir", ctypes.c_int), ("chunks", ctypes.c_int), ("sched", ctypes.c_int),
+                ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int), ("n_comm", ctypes.c_int),
+                ("copy_gbps", ctypes.c_double), ("mfma_tflops", ctypes.c_double), ("launch_us", ctypes.c_double)]
+
+
+class cm_plan(ctypes.Structure):
+    _fields_ = [("desc", cm_plan_desc), ("chunks", ctypes.c_int), ("n_steps", ctypes.c_int),
+                ("arc_cw", ctypes.c_int), ("arc_ccw", ctypes.c_int), ("tile_m", ctypes.c_int),
+                ("tile_n", ctypes.c_int), ("declined", ctypes.c_int), ("n_ops", ctypes.c_int),
+                ("n_jobs", ctypes.c_int), ("n_events", ctypes.c_int), ("ws_bytes", ctypes.c_size_t),
+                ("est_gemm_us", ctypes.c_double), ("est_hop_us", ctypes.c_double)]
+
+
+class cm_op_rec(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int), ("stream", ctypes.c_int), ("event", ctypes.c_int), ("step", ctypes.c_int),
+                ("chunk", ctypes.c_int), ("first_job", ctypes.c_int), ("n_jobs", ctypes.c_int),
+                ("rows", ctypes.c_int), ("cols", ctypes.c_int), ("depth", ctypes.c_int), ("tile_m", ctypes.c_int),
+                ("tile_n", ctypes.c_int), ("src_buf", ctypes.c_int), ("dst_buf", ctypes.c_int),
+                ("src_off", ctypes.c_size_t), ("dst_off", ctypes.c_size_t), ("bytes", ctypes.c_size_t)]
+
+
+class cm_job_rec(ctypes.Structure):
+    _fields_ = [("rank", ctypes.c_int), ("dir", ctypes.c_int), ("index", ctypes.c_int), ("a_buf", ctypes.c_int),
+                ("b_buf", ctypes.c_int), ("c_buf", ctypes.c_int), ("in0_buf", ctypes.c_int),
+                ("in1_buf", ctypes.c_int), ("a_off", ctypes.c_size_t), ("b_off", ctypes.c_size_t),
+                ("c_off", ctypes.c_size_t), ("in0_off", ctypes.c_size_t), ("in1_off", ctypes.c_size_t),
+                ("lda", ctypes.c_int), ("ldb", ctypes.c_int), ("ldc", ctypes.c_int), ("ld_in", ctypes.c_int),
+                ("c_dtype", ctypes.c_int)]
+
+
+class cm_span(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int), ("stream", ctypes.c_int), ("step", ctypes.c_int), ("chunk", ctypes.c_int),
+                ("start_us", ctypes.c_double), ("end_us", ctypes.c_double)]
+
+
+class CMError(RuntimeError):
+    def __init__(self, status, where, detail):
+        self.status = status
+        super().__init__("%s failed: %s (%s)" % (where, _status_name(status), detail))
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libcollmm (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libcollmm.so not found at %s; build it with "
+                               "`python -m collective_matmul_decomposition_amd.build`" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, ci, cs = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.cm_ring_plan.argtypes = [ctypes.POINTER(cm_plan_desc), ctypes.POINTER(cm_plan)]
+        L.cm_workspace_size.argtypes = [ctypes.POINTER(cm_plan), ctypes.POINTER(cs)]
+        L.cm_plan_program.argtypes = [ctypes.POINTER(cm_plan), ctypes.POINTER(cm_op_rec), ci, ctypes.POINTER(ci),
+                                      ctypes.POINTER(cm_job_rec), ci, ctypes.POINTER(ci)]
+        L.cm_trace_create.argtypes = [ci, ctypes.POINTER(vp)]
+        L.cm_trace_destroy.argtypes = [vp]
+        L.cm_trace_read.argtypes = [vp, ctypes.POINTER(cm_span), ci, ctypes.POINTER(ci), ctypes.POINTER(ctypes.c_double)]
+        for f in (L.cm_ag_gemm, L.cm_gemm_rs):
+            f.argtypes = [ctypes.POINTER(cm_plan), vp, vp, vp, vp, cs, vp, ctypes.POINTER(vp), ci, vp]
+        for name in EXPORTS:
+            if name in ("cm_status_string", "cm_last_error", "cm_version"):
+                continue
+            getattr(L, name).restype = ci
+        L.cm_status_string.argtypes = [ci]
+        L.cm_status_string.restype = ctypes.c_char_p
+        L.cm_last_error.argtypes = []
+        L.cm_last_error.restype = ctypes.c_char_p
+        L.cm_version.argtypes = []
+        L.cm_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _status_name(st):
+    try:
+        return lib().cm_status_string(st).decode()
+    except Exception:  # noqa: BLE001 - naming only
+        return str(st)
+
+
+def _check(st, where):
+    if st != CM_OK:
+        raise CMError(st, where, lib().cm_last_error().decode())
+
+
+def last_error():
+    return lib().cm_last_error().decode()
+
+
+def version():
+    return lib().cm_version().decode()
+
+
+_ENUMS = {
+    "op": {"ag": CM_OP_AG_GEMM, "rs": CM_OP_GEMM_RS, "rs_pipe": CM_OP_GEMM_RS_PIPE},
+    "dir": {"uni": CM_RING_UNI, "bi": CM_RING_BI},
+    "sched": {"decomposed": CM_SCHED_DECOMPOSED, "naive": CM_SCHED_NAIVE},
+    "dtype": {"bf16": CM_BF16, "f32": CM_F32},
+}
+
+
+def make_desc(op, n_ranks, m, k, n, dir="uni", chunks=0, sched="decomposed", out_dtype="bf16", n_comm=1,
+              copy_gbps=0.0, mfma_tflops=0.0, launch_us=0.0):
+    """A cm_plan_desc from keyword arguments (strings or enum values)."""
+    def e(kind, v):
+        return _ENUMS[kind][v] if isinstance(v, str) else int(v)
+    return cm_plan_desc(op=e("op", op), n_ranks=n_ranks, m=m, k=k, n=n, dir=e("dir", dir), chunks=chunks,
+                        sched=e("sched", sched), in_dtype=CM_BF16, out_dtype=e("dtype", out_dtype),
+                        n_comm=n_comm, copy_gbps=copy_gbps, mfma_tflops=mfma_tflops, launch_us=launch_us)
+
+
+def cm_ring_plan(desc=None, **kw):
+    """cm_ring_plan(desc) or cm_ring_plan(op=..., n_ranks=..., ...) -> cm_plan."""
+    if desc is None:
+        desc = make_desc(**kw)
+    p = cm_plan()
+    _check(lib().cm_ring_plan(ctypes.byref(desc), ctypes.byref(p)), "cm_ring_plan")
+    return p
+
+
+def cm_ring_plan_status(desc):
+    """Status code of cm_ring_plan without raising (for error-path tests)."""
+    p = cm_plan()
+    return lib().cm_ring_plan(ctypes.byref(desc), ctypes.byref(p)), p
+
+
+def cm_workspace_size(plan):
+    n = ctypes.c_size_t()
+    _check(lib().cm_workspace_size(ctypes.byref(plan), ctypes.byref(n)), "cm_workspace_size")
+    return n.value
+
+
+def cm_plan_program(plan):
+    """(ops, jobs): the plan's program as lists of cm_op_rec / cm_job_rec."""
+    n_ops, n_jobs = ctypes.c_int(), ctypes.c_int()
+    _check(lib().cm_plan_program(ctypes.byref(plan), None, 0, ctypes.byref(n_ops), None, 0, ctypes.byref(n_jobs)),
+           "cm_plan_program")
+    ops = (cm_op_rec * max(1, n_ops.value))()
+    jobs = (cm_job_rec * max(1, n_jobs.value))()
+    _check(lib().cm_plan_program(ctypes.byref(plan), ops, n_ops.value, ctypes.byref(n_ops), jobs, n_jobs.value,
+                                 ctypes.byref(n_jobs)), "cm_plan_program")
+    return list(ops)[:n_ops.value], list(jobs)[:n_jobs.value]
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        return None
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream  # torch.cuda.Stream
+
+
+class Trace:
+    """Owns a cm_trace; pass to cm_ag_gemm / cm_gemm_rs, read after a sync."""
+
+    def __init__(self, capacity=4096):
+        h = ctypes.c_void_p()
+        _check(lib().cm_trace_create(capacity, ctypes.byref(h)), "cm_trace_create")
+        self.handle = h
+        self.capacity = capacity
+
+    def read(self):
+        n = ctypes.c_int()
+        total = ctypes.c_double()
+        spans = (cm_span * self.capacity)()
+        _check(lib().cm_trace_read(self.handle, spans, self.capacity, ctypes.byref(n), ctypes.byref(total)),
+               "cm_trace_read")
+        return [(s.kind, s.stream, s.step, s.chunk, s.start_us, s.end_us) for s in spans[:n.value]], total.value
+
+    def close(self):
+        if self.handle:
+            lib().cm_trace_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001 - interpreter shutdown
+            pass
+
+
+def _call(fn, name, plan, x, w, y, ws, ws_bytes, compute, comm, trace):
+    comm = list(comm or [])
+    arr = (ctypes.c_void_p * max(1, len(comm)))(*[_stream(s) for s in comm])
+    if ws_bytes is None:
+        ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = fn(ctypes.byref(plan), _ptr(x), _ptr(w), _ptr(y), _ptr(ws), ws_bytes, _stream(compute), arr, len(comm),
+            trace.handle if trace is not None else None)
+    _check(st, name)
+
+
+def cm_ag_gemm(plan, x, w, y, ws, compute, comm, trace=None, ws_bytes=None):
+    """AllGather -> GEMM through the C ABI (tensors or raw device pointers)."""
+    _call(lib().cm_ag_gemm, "cm_ag_gemm", plan, x, w, y, ws, ws_bytes, compute, comm, trace)
+
+
+def cm_gemm_rs(plan, x, w, y, ws, compute, comm, trace=None, ws_bytes=None):
+    """GEMM -> ReduceScatter through the C ABI (tensors or raw device pointers)."""
+    _call(lib().cm_gemm_rs, "cm_gemm_rs", plan, x, w, y, ws, ws_bytes, compute, comm, trace)

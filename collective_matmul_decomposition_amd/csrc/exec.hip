@@ -1,0 +1,418 @@
+// Executor and C-ABI entry points: runs a plan's program on the compute
+// stream and the comm streams.
+//
+// Every operation of the program maps to one HIP call:
+//   GEMM   -> one launch of gemm_jobs (all of the step's partial GEMMs),
+//   REDUCE -> one launch of reduce_jobs,
+//   COPY   -> hipMemcpyAsync(..., hipMemcpyDeviceToDeviceNoCU, comm stream):
+//             the hop, executed by an SDMA engine, not by compute units,
+//   RECORD -> hipEventRecord, WAIT -> hipStreamWaitEvent.
+// The transfer start/done pairs of the decomposition page ("Asynchrony with
+// a budget") are the copy enqueue and the event the compute stream waits on.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <memory>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "collmm.h"
+#include "internal.h"
+#include "kernels.h"
+
+struct cm_trace {
+  int device = -1;
+  int capacity = 0;
+  hipEvent_t entry = nullptr;
+  std::vector<hipEvent_t> ev;  // 2 per span: start, end
+  std::vector<cm_span> spans;  // metadata; times filled by cm_trace_read
+  int used = 0;
+  bool overflow = false;
+};
+
+namespace collmm {
+namespace {
+
+// ------------------------------------------------------------ cached programs
+struct Launch {
+  GemmParams p;  // base[] filled per call
+  int tm = 0, tn = 0;
+};
+
+struct Compiled {
+  Program prog;
+  std::vector<Launch> launches;  // one per GEMM / REDUCE op, in op order
+  std::vector<int> launch_of_op; // op index -> launches index (-1 if none)
+};
+
+std::string plan_key(const cm_plan &p) {
+  // Every field the program depends on (struct padding is not part of it).
+  const cm_plan_desc &d = p.desc;
+  char buf[512];
+  std::snprintf(buf, sizeof buf, "%d %d %d %d %d %d %d %d %d %d %d %a %a %a|%d %d %d %d %d %d %d %zu", d.op, d.n_ranks, d.m,
+                d.k, d.n, d.dir, d.chunks, d.sched, d.in_dtype, d.out_dtype, d.n_comm, d.copy_gbps, d.mfma_tflops,
+                d.launch_us, p.chunks, p.n_steps, p.arc_cw, p.arc_ccw, p.tile_m, p.tile_n, p.n_events, p.ws_bytes);
+  return buf;
+}
+
+// The caller's plan must be one that cm_ring_plan produced: re-derive it from
+// its request and chunk count and compare every schedule field.
+cm_status canonical_plan(const cm_plan &pl, cm_plan *canon) {
+  cm_plan_desc d = pl.desc;
+  d.chunks = pl.chunks;
+  cm_status st = plan(&d, canon);
+  if (st != CM_OK) return st;
+  if (canon->chunks != pl.chunks || canon->n_steps != pl.n_steps || canon->arc_cw != pl.arc_cw ||
+      canon->arc_ccw != pl.arc_ccw || canon->tile_m != pl.tile_m || canon->tile_n != pl.tile_n ||
+      canon->ws_bytes != pl.ws_bytes || canon->n_ops != pl.n_ops || canon->n_jobs != pl.n_jobs ||
+      canon->n_events != pl.n_events || canon->desc.dir != pl.desc.dir) {
+    set_error("plan does not match what cm_ring_plan produces for its request");
+    return CM_ERR_INVALID_ARG;
+  }
+  return CM_OK;
+}
+
+cm_status fill_params(const cm_op_rec &o, const cm_job_rec *jobs, Launch &L) {
+  GemmParams &p = L.p;
+  std::memset(&p, 0, sizeof p);
+  if (o.n_jobs < 1 || o.n_jobs > kMaxJobs) {
+    set_error("a launch has %d jobs (limit %d)", o.n_jobs, kMaxJobs);
+    return CM_ERR_SHAPE;
+  }
+  p.M = o.rows;
+  p.N = o.cols;
+  p.K = o.depth;
+  p.n_jobs = o.n_jobs;
+  const cm_job_rec &j0 = jobs[0];
+  p.lda = j0.lda;
+  p.ldb = j0.ldb;
+  p.ldc = j0.ldc;
+  p.ld_in = j0.ld_in;
+  p.c_f32 = j0.c_dtype == CM_F32;
+  auto off16 = [&](size_t off, uint32_t *out) -> bool {
+    if (off % 16 || off / 16 > 0xFFFFFFFFull) return false;
+    *out = (uint32_t)(off / 16);
+    return true;
+  };
+  for (int i = 0; i < o.n_jobs; ++i) {
+    const cm_job_rec &j = jobs[i];
+    if (j.lda != p.lda || j.ldb != p.ldb || j.ldc != p.ldc || j.ld_in != p.ld_in || (j.c_dtype == CM_F32) != (p.c_f32 != 0)) {
+      set_error("jobs of one launch differ in strides or output type");
+      return CM_ERR_SHAPE;
+    }
+    uint32_t sel = 0;
+    bool ok = true;
+    if (o.kind == CM_OPK_GEMM) {
+      ok &= j.a_buf >= 0 && j.b_buf >= 0 && off16(j.a_off, &p.a_off[i]) && off16(j.b_off, &p.b_off[i]);
+      sel |= (uint32_t)(j.a_buf & 3) | ((uint32_t)(j.b_buf & 3) << 2);
+    }
+    ok &= j.c_buf >= 0 && off16(j.c_off, &p.c_off[i]);
+    sel |= (uint32_t)(j.c_buf & 3) << 4;
+    if (j.in0_buf >= 0) {
+      ok &= j.in0_buf == CM_BUF_WS && off16(j.in0_off, &p.in0_off[i]);
+      sel |= 1u << 6;
+    }
+    if (j.in1_buf >= 0) {
+      ok &= j.in1_buf == CM_BUF_WS && off16(j.in1_off, &p.in1_off[i]);
+      sel |= 1u << 7;
+    }
+    if (o.kind == CM_OPK_REDUCE) ok &= j.in0_buf >= 0 && j.in1_buf >= 0;
+    if (!ok) {
+      set_error("job %d of a launch has an unaligned, out-of-range or missing operand", i);
+      return CM_ERR_SHAPE;
+    }
+    p.sel[i] = (uint8_t)sel;
+  }
+  if (o.kind == CM_OPK_GEMM) {
+    if (!gemm_tile_supported(o.tile_m, o.tile_n)) {
+      set_error("no kernel for tile %dx%d", o.tile_m, o.tile_n);
+      return CM_ERR_UNSUPPORTED;
+    }
+    L.tm = o.tile_m;
+    L.tn = o.tile_n;
+    p.tiles_m = (p.M + L.tm - 1) / L.tm;
+    p.tiles_per_job = p.tiles_m * ((p.N + L.tn - 1) / L.tn);
+    if (p.K % 64) {
+      set_error("K %d not a multiple of 64", p.K);
+      return CM_ERR_SHAPE;
+    }
+  } else {
+    if (p.N % 4 || p.ld_in % 4 || p.ldc % 4) {
+      set_error("reduce columns must be multiples of 4");
+      return CM_ERR_SHAPE;
+    }
+  }
+  return CM_OK;
+}
+
+struct ThreadState {
+  std::unordered_map<std::string, std::unique_ptr<Compiled>> programs;
+  std::unordered_map<int, std::vector<hipEvent_t>> events;  // per device
+  std::unordered_map<int, int> arch_ok;                     // per device: 1 ok, 0 not gfx950
+};
+
+ThreadState &tls() {
+  thread_local ThreadState s;
+  return s;
+}
+
+cm_status get_compiled(const cm_plan &pl, const Compiled **out) {
+  ThreadState &ts = tls();
+  std::string key = plan_key(pl);
+  auto it = ts.programs.find(key);
+  if (it != ts.programs.end()) {
+    *out = it->second.get();
+    return CM_OK;
+  }
+  cm_plan canon;
+  cm_status cst = canonical_plan(pl, &canon);
+  if (cst != CM_OK) return cst;
+  auto c = std::make_unique<Compiled>();
+  build_program(canon, c->prog);
+  c->launch_of_op.assign(c->prog.ops.size(), -1);
+  for (size_t i = 0; i < c->prog.ops.size(); ++i) {
+    const cm_op_rec &o = c->prog.ops[i];
+    if (o.kind != CM_OPK_GEMM && o.kind != CM_OPK_REDUCE) continue;
+    Launch L;
+    cm_status st = fill_params(o, c->prog.jobs.data() + o.first_job, L);
+    if (st != CM_OK) return st;
+    c->launch_of_op[i] = (int)c->launches.size();
+    c->launches.push_back(L);
+  }
+  if (ts.programs.size() > 256) ts.programs.clear();
+  *out = c.get();
+  ts.programs.emplace(key, std::move(c));
+  return CM_OK;
+}
+
+cm_status hip_fail(hipError_t e, const char *what) {
+  set_error("%s: %s", what, hipGetErrorString(e));
+  return CM_ERR_HIP;
+}
+
+cm_status check_device(int *dev_out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  ThreadState &ts = tls();
+  auto it = ts.arch_ok.find(dev);
+  if (it == ts.arch_ok.end()) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    int ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    it = ts.arch_ok.emplace(dev, ok).first;
+    if (!ok) set_error("device %d is %s; this library is built for gfx950 only", dev, prop.gcnArchName);
+  }
+  if (!it->second) {
+    set_error("current device is not gfx950");
+    return CM_ERR_UNSUPPORTED;
+  }
+  *dev_out = dev;
+  return CM_OK;
+}
+
+cm_status event_pool(int dev, int n, std::vector<hipEvent_t> **out) {
+  std::vector<hipEvent_t> &v = tls().events[dev];
+  while ((int)v.size() < n) {
+    hipEvent_t ev;
+    hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
+    v.push_back(ev);
+  }
+  *out = &v;
+  return CM_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+cm_status validate_call(const cm_plan *pl, bool want_ag, const void *x, const void *w, void *y, void *ws,
+                        size_t ws_bytes, void *compute, void *const *comm, int n_comm) {
+  if (!pl) { set_error("null plan"); return CM_ERR_INVALID_ARG; }
+  cm_status st = validate_desc(pl->desc);
+  if (st != CM_OK) return st;
+  const bool is_ag = pl->desc.op == CM_OP_AG_GEMM;
+  if (is_ag != want_ag) {
+    set_error(want_ag ? "cm_ag_gemm needs a plan with op CM_OP_AG_GEMM"
+                      : "cm_gemm_rs needs a plan with op CM_OP_GEMM_RS or CM_OP_GEMM_RS_PIPE");
+    return CM_ERR_INVALID_ARG;
+  }
+  if (pl->chunks < 1 || pl->chunks > CM_MAX_CHUNKS) { set_error("plan has invalid chunk count"); return CM_ERR_INVALID_ARG; }
+  if (is_ag ? (pl->desc.m % pl->chunks) : (pl->desc.n % pl->chunks || (pl->desc.n / pl->chunks) % 64)) {
+    set_error("plan chunk count does not divide the shape");
+    return CM_ERR_SHAPE;
+  }
+  if (ws_layout(*pl).total != pl->ws_bytes) { set_error("plan is inconsistent (workspace size)"); return CM_ERR_INVALID_ARG; }
+  if (!x || !w || !y) { set_error("null x, w or y"); return CM_ERR_INVALID_ARG; }
+  if (pl->ws_bytes > 0 && !ws) { set_error("null workspace"); return CM_ERR_INVALID_ARG; }
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (ws && !aligned16(ws))) {
+    set_error("x, w, y and ws must be 16-byte aligned");
+    return CM_ERR_ALIGN;
+  }
+  if (ws_bytes < pl->ws_bytes) {
+    set_error("workspace of %zu bytes, plan needs %zu", ws_bytes, pl->ws_bytes);
+    return CM_ERR_WORKSPACE;
+  }
+  if (n_comm != pl->desc.n_comm || !comm) {
+    set_error("plan was built for %d comm streams, call passes %d", pl->desc.n_comm, n_comm);
+    return CM_ERR_INVALID_ARG;
+  }
+  for (int i = 0; i < n_comm; ++i) {
+    if (!comm[i] || comm[i] == compute) { set_error("comm stream %d is null or equal to the compute stream", i); return CM_ERR_INVALID_ARG; }
+    for (int j = 0; j < i; ++j)
+      if (comm[j] == comm[i]) { set_error("comm streams %d and %d are the same stream", j, i); return CM_ERR_INVALID_ARG; }
+  }
+  return CM_OK;
+}
+
+cm_status run(const cm_plan *pl, bool want_ag, const void *x, const void *w, void *y, void *ws, size_t ws_bytes,
+              void *compute, void *const *comm, int n_comm, cm_trace *trace) {
+  cm_status st = validate_call(pl, want_ag, x, w, y, ws, ws_bytes, compute, comm, n_comm);
+  if (st != CM_OK) return st;
+  int dev;
+  if ((st = check_device(&dev)) != CM_OK) return st;
+  if (trace && trace->device != dev) { set_error("trace was created on another device"); return CM_ERR_INVALID_ARG; }
+  const Compiled *cp;
+  if ((st = get_compiled(*pl, &cp)) != CM_OK) return st;
+  std::vector<hipEvent_t> *evp;
+  if ((st = event_pool(dev, cp->prog.n_events, &evp)) != CM_OK) return st;
+  const std::vector<hipEvent_t> &ev = *evp;
+
+  char *base[4] = {const_cast<char *>(static_cast<const char *>(x)), const_cast<char *>(static_cast<const char *>(w)),
+                   static_cast<char *>(y), static_cast<char *>(ws)};
+  hipStream_t streams[CM_MAX_COMM + 1];
+  streams[0] = static_cast<hipStream_t>(compute);
+  for (int i = 0; i < n_comm; ++i) streams[i + 1] = static_cast<hipStream_t>(comm[i]);
+
+  hipError_t e;
+  if (trace) {
+    trace->used = 0;
+    trace->overflow = false;
+    trace->spans.clear();
+    if ((e = hipEventRecord(trace->entry, streams[0])) != hipSuccess) return hip_fail(e, "hipEventRecord(trace)");
+  }
+  auto span_begin = [&](const cm_op_rec &o) -> int {
+    if (!trace) return -1;
+    if (trace->used >= trace->capacity) { trace->overflow = true; return -1; }
+    int idx = trace->used++;
+    cm_span sp{};
+    sp.kind = o.kind;
+    sp.stream = o.stream;
+    sp.step = o.step;
+    sp.chunk = o.chunk;
+    trace->spans.push_back(sp);
+    (void)hipEventRecord(trace->ev[2 * idx], streams[o.stream]);
+    return idx;
+  };
+  auto span_end = [&](int idx, const cm_op_rec &o) {
+    if (idx >= 0) (void)hipEventRecord(trace->ev[2 * idx + 1], streams[o.stream]);
+  };
+
+  const std::vector<cm_op_rec> &ops = cp->prog.ops;
+  for (size_t i = 0; i < ops.size(); ++i) {
+    const cm_op_rec &o = ops[i];
+    hipStream_t s = streams[o.stream];
+    switch (o.kind) {
+      case CM_OPK_RECORD:
+        if ((e = hipEventRecord(ev[o.event], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+        break;
+      case CM_OPK_WAIT:
+        if ((e = hipStreamWaitEvent(s, ev[o.event], 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+        break;
+      case CM_OPK_COPY: {
+        int sp = span_begin(o);
+        e = hipMemcpyAsync(base[o.dst_buf] + o.dst_off, base[o.src_buf] + o.src_off, o.bytes,
+                           hipMemcpyDeviceToDeviceNoCU, s);
+        if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (ring hop)");
+        span_end(sp, o);
+        break;
+      }
+      case CM_OPK_GEMM:
+      case CM_OPK_REDUCE: {
+        GemmParams p = cp->launches[cp->launch_of_op[i]].p;
+        for (int b = 0; b < 4; ++b) p.base[b] = base[b];
+        int sp = span_begin(o);
+        if (o.kind == CM_OPK_GEMM) {
+          const Launch &L = cp->launches[cp->launch_of_op[i]];
+          e = launch_gemm(p, L.tm, L.tn, s);
+        } else {
+          e = launch_reduce(p, s);
+        }
+        if (e != hipSuccess) return hip_fail(e, o.kind == CM_OPK_GEMM ? "gemm launch" : "reduce launch");
+        span_end(sp, o);
+        break;
+      }
+      default:
+        set_error("corrupt program");
+        return CM_ERR_INVALID_ARG;
+    }
+  }
+  return CM_OK;
+}
+
+}  // namespace
+}  // namespace collmm
+
+extern "C" {
+
+cm_status cm_ag_gemm(const cm_plan *plan, const void *x, const void *w, void *y, void *ws, size_t ws_bytes,
+                     void *compute, void *const *comm, int n_comm, cm_trace *trace) {
+  return collmm::run(plan, true, x, w, y, ws, ws_bytes, compute, comm, n_comm, trace);
+}
+
+cm_status cm_gemm_rs(const cm_plan *plan, const void *x, const void *w, void *y, void *ws, size_t ws_bytes,
+                     void *compute, void *const *comm, int n_comm, cm_trace *trace) {
+  return collmm::run(plan, false, x, w, y, ws, ws_bytes, compute, comm, n_comm, trace);
+}
+
+cm_status cm_trace_create(int capacity, cm_trace **out) {
+  if (!out || capacity < 1 || capacity > (1 << 20)) {
+    collmm::set_error("cm_trace_create: need out != NULL and 1 <= capacity <= 2^20");
+    return CM_ERR_INVALID_ARG;
+  }
+  auto t = std::make_unique<cm_trace>();
+  hipError_t e = hipGetDevice(&t->device);
+  if (e != hipSuccess) return collmm::hip_fail(e, "hipGetDevice");
+  t->capacity = capacity;
+  if ((e = hipEventCreate(&t->entry)) != hipSuccess) return collmm::hip_fail(e, "hipEventCreate");
+  t->ev.resize(2 * (size_t)capacity);
+  for (auto &ev : t->ev)
+    if ((e = hipEventCreate(&ev)) != hipSuccess) return collmm::hip_fail(e, "hipEventCreate");
+  *out = t.release();
+  return CM_OK;
+}
+
+cm_status cm_trace_destroy(cm_trace *t) {
+  if (!t) return CM_OK;
+  if (t->entry) (void)hipEventDestroy(t->entry);
+  for (auto &ev : t->ev)
+    if (ev) (void)hipEventDestroy(ev);
+  delete t;
+  return CM_OK;
+}
+
+cm_status cm_trace_read(cm_trace *t, cm_span *spans, int cap, int *n_spans, double *total_us) {
+  if (!t || !n_spans) { collmm::set_error("null argument"); return CM_ERR_INVALID_ARG; }
+  *n_spans = t->used;
+  if (t->overflow) { collmm::set_error("trace capacity %d exceeded", t->capacity); return CM_ERR_CAPACITY; }
+  if (cap < t->used || (!spans && t->used > 0)) { collmm::set_error("span array too small"); return CM_ERR_CAPACITY; }
+  double last = 0;
+  for (int i = 0; i < t->used; ++i) {
+    float a, b;
+    hipError_t e = hipEventElapsedTime(&a, t->entry, t->ev[2 * i]);
+    if (e != hipSuccess) return collmm::hip_fail(e, "hipEventElapsedTime (synchronise the compute stream first)");
+    e = hipEventElapsedTime(&b, t->entry, t->ev[2 * i + 1]);
+    if (e != hipSuccess) return collmm::hip_fail(e, "hipEventElapsedTime");
+    spans[i] = t->spans[i];
+    spans[i].start_us = a * 1e3;
+    spans[i].end_us = b * 1e3;
+    if (spans[i].end_us > last) last = spans[i].end_us;
+  }
+  if (total_us) *total_us = last;
+  return CM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,34 @@
+// Declarations shared by the planner and the executor (host side only).
+#pragma once
+#include <cstdarg>
+#include <cstddef>
+#include <vector>
+
+#include "collmm.h"
+
+namespace collmm {
+
+// Byte offsets of the workspace regions a plan uses.
+struct WsLayout {
+  size_t slot_dir_bytes = 0;  // AG / RS decomposed: bytes of one direction's slots
+  size_t gather = 0;          // AG naive: gathered activations
+  size_t partial = 0;         // RS pipe / naive: partial products
+  size_t partial_bytes = 0;
+  size_t ring = 0;            // RS pipe / naive: ring slots
+  size_t total = 0;
+};
+
+struct Program {
+  std::vector<cm_op_rec> ops;
+  std::vector<cm_job_rec> jobs;
+  int n_events = 0;
+};
+
+void set_error(const char *fmt, ...);
+const char *last_error();
+cm_status validate_desc(const cm_plan_desc &d);
+cm_status plan(const cm_plan_desc *desc, cm_plan *out);
+WsLayout ws_layout(const cm_plan &p);
+void build_program(const cm_plan &p, Program &prog);
+
+}  // namespace collmm

@@ -1,0 +1,32 @@
+// Launch interface of the gfx950 kernels (host and device see this struct).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace collmm {
+
+constexpr int kMaxJobs = 128;
+
+// One launch: n_jobs independent jobs of the same shape (M x N outputs, K
+// contraction).  Operand addresses are base[buffer] + 16 * offset, with the
+// buffer of A, B and C selected per job (0 = X, 1 = W, 2 = Y, 3 = workspace);
+// the optional fp32 addends in0/in1 always live in the workspace.
+//   sel bits 0-1: A buffer, 2-3: B buffer, 4-5: C buffer, 6: in0 present,
+//   7: in1 present.
+struct GemmParams {
+  char *base[4];
+  int M, N, K;
+  int lda, ldb, ldc, ld_in;  // row strides in elements
+  int c_f32;                 // 1: C is fp32, 0: C is bf16 (round to nearest even)
+  int n_jobs;
+  int tiles_m;               // row tiles per job
+  int tiles_per_job;
+  uint32_t a_off[kMaxJobs], b_off[kMaxJobs], c_off[kMaxJobs], in0_off[kMaxJobs], in1_off[kMaxJobs];
+  uint8_t sel[kMaxJobs];
+};
+
+bool gemm_tile_supported(int tm, int tn);
+hipError_t launch_gemm(const GemmParams &p, int tm, int tn, hipStream_t s);
+hipError_t launch_reduce(const GemmParams &p, hipStream_t s);
+
+}  // namespace collmm

@@ -1,0 +1,824 @@
+// Ring planner: turns a cm_plan_desc into a schedule and the schedule into a
+// program (the exact ordered list of launches, hop copies and event
+// record/wait operations the executor enqueues).  Host-only C++; makes no
+// HIP call, so the CPU tests can run and simulate every program.
+//
+// Schedules (page titles and sections in collmm.h):
+//   AllGather->GEMM, decomposed ("P2P AllGather overlap"; "The idea" on the
+//     decomposition page): at step s rank r multiplies the shard it holds,
+//     (r - s) mod N, into the rows of Y_r that belong to that shard (the
+//     slice update), while the same shard is copied to rank r + 1.  A
+//     bidirectional ring forwards shards both ways: at step s >= 1 rank r
+//     holds (r - s) from the clockwise arc and (r + s) from the
+//     counter-clockwise arc, so ceil((N-1)/2) hops suffice.
+//   GEMM->ReduceScatter, decomposed ("P2P ReduceScatter overlap"; the
+//     circulating accumulator of "The idea"): the bucket owned by q starts at
+//     rank q + 1, every rank adds its partial product for the bucket's rows
+//     and forwards it; after N - 1 hops the owner adds its own share last.
+//     Bidirectional: the bucket is split by direction (ranks q-L..q-1
+//     clockwise, q+R..q+1 counter-clockwise) and the owner sums its own
+//     partial with both arrivals, the realigning addition of "What it costs".
+//   Pipeline-chunk ReduceScatter ("Pipeline-chunk ReduceScatter"): the
+//     output columns are cut into chunks; chunk j's full partial products are
+//     one launch, then a copy-and-add ring reduce-scatters chunk j on the comm
+//     streams while chunk j + 1 computes.
+//   Naive schedules ("Naive AllGather", "Naive ReduceScatter"): the whole
+//     collective then the whole GEMM (AG), or the whole GEMM then the whole
+//     collective (RS), with the same copies.
+//
+// Ordering rules of the programs ("the rank must not overwrite a bucket
+// before downstream consumers are done; it must not read a contribution
+// before the GEMM has produced it", section 5 of the Megatron page):
+//   every read of a receive slot waits for the copy that filled it (RAW);
+//   every copy into a slot waits for the last reader of the slot's previous
+//   contents (WAR); every copy of a bucket waits for the GEMM that produced it.
+//   Two slots per rank and direction alternate by step parity.
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "collmm.h"
+#include "internal.h"
+
+namespace collmm {
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int mod(int a, int n) { return ((a % n) + n) % n; }
+
+// Default cost-model constants for MI355X, from measurements of this
+// library: one comm stream's SDMA copy rate and a sustained GEMM rate.
+constexpr double kDefaultCopyGBps = 55.0;
+constexpr double kDefaultMfmaTflops = 1300.0;
+constexpr double kDefaultLaunchUs = 8.0;
+
+bool is_pow2_chunk(int c) { return c == 1 || c == 2 || c == 4 || c == 8 || c == 16; }
+
+// Tile choice: among the compiled block tiles, pick the one that wastes the
+// least of the chip for `jobs` jobs of rows x cols outputs each.  Score =
+// (useful outputs / launched outputs) x (fraction of the last wave of
+// workgroups that is busy) x (per-tile efficiency: larger tiles re-read
+// operands less).
+struct TileCand { int tm, tn; double eff; };
+constexpr TileCand kTiles[] = {
+    {256, 256, 1.00}, {256, 128, 0.92}, {128, 256, 0.92}, {128, 128, 0.80}, {64, 256, 0.78},
+    {64, 128, 0.65},
+};
+constexpr int kCUs = 256;
+
+void choose_tile(int rows, int cols, int jobs, int *tm, int *tn) {
+  double best = -1;
+  for (const TileCand &t : kTiles) {
+    long tiles_m = (rows + t.tm - 1) / t.tm, tiles_n = (cols + t.tn - 1) / t.tn;
+    long wgs = tiles_m * tiles_n * (long)jobs;
+    double useful = (double)rows * cols / ((double)tiles_m * t.tm * tiles_n * t.tn);
+    long waves = (wgs + kCUs - 1) / kCUs;
+    double fill = (double)wgs / ((double)waves * kCUs);
+    double score = useful * fill * t.eff;
+    if (score > best + 1e-9) { best = score; *tm = t.tm; *tn = t.tn; }
+  }
+}
+
+}  // namespace
+
+void set_error(const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+}
+
+const char *last_error() { return g_last_error.c_str(); }
+
+// ------------------------------------------------------------ workspace map
+// AG decomposed: receive slots, chunk-major so that one chunk of a range of
+//   ranks is contiguous:  slot[dir][p][j][r][m/c][k] bf16.
+// AG naive: gathered activations G[r][T][k] bf16.
+// RS decomposed: buckets  bkt[dir][p][j][r][m][n/c] fp32.
+// RS pipe / naive: partials P[r][j][T][n/c] fp32, then ring slots
+//   R[p][r][m][n/c] fp32.
+WsLayout ws_layout(const cm_plan &pl) {
+  const cm_plan_desc &d = pl.desc;
+  const size_t N = d.n_ranks, m = d.m, k = d.k, n = d.n, c = pl.chunks, T = N * m;
+  WsLayout L{};
+  const int ndir = d.dir == CM_RING_BI ? 2 : 1;
+  if (d.op == CM_OP_AG_GEMM) {
+    if (d.sched == CM_SCHED_NAIVE) {
+      L.gather = 0;
+      L.total = N * T * k * 2;
+    } else {
+      L.slot_dir_bytes = 2 * N * m * k * 2;
+      L.total = ndir * L.slot_dir_bytes;
+    }
+  } else if (d.op == CM_OP_GEMM_RS && d.sched == CM_SCHED_DECOMPOSED) {
+    L.slot_dir_bytes = 2 * N * m * n * 4;  // c chunks of n/c columns
+    L.total = ndir * L.slot_dir_bytes;
+  } else {  // PIPE, or RS naive (PIPE with one chunk)
+    L.partial = 0;
+    L.partial_bytes = N > 1 ? N * T * n * 4 : 0;
+    L.ring = L.partial_bytes;
+    L.total = L.partial_bytes + (N > 1 ? 2 * N * m * (n / c) * 4 : 0);
+  }
+  return L;
+}
+
+// ---------------------------------------------------------------- validation
+cm_status validate_desc(const cm_plan_desc &d) {
+  if (d.op < CM_OP_AG_GEMM || d.op > CM_OP_GEMM_RS_PIPE) { set_error("unknown op %d", d.op); return CM_ERR_INVALID_ARG; }
+  if (d.n_ranks < 1 || d.n_ranks > CM_MAX_RANKS) { set_error("n_ranks %d outside 1..%d", d.n_ranks, CM_MAX_RANKS); return CM_ERR_INVALID_ARG; }
+  if (d.dir != CM_RING_UNI && d.dir != CM_RING_BI) { set_error("unknown ring direction %d", d.dir); return CM_ERR_INVALID_ARG; }
+  if (d.sched != CM_SCHED_DECOMPOSED && d.sched != CM_SCHED_NAIVE) { set_error("unknown schedule %d", d.sched); return CM_ERR_INVALID_ARG; }
+  if (d.n_comm < 1 || d.n_comm > CM_MAX_COMM) { set_error("n_comm %d outside 1..%d", d.n_comm, CM_MAX_COMM); return CM_ERR_INVALID_ARG; }
+  if (d.in_dtype != CM_BF16) { set_error("only bf16 inputs are supported"); return CM_ERR_UNSUPPORTED; }
+  if (d.out_dtype != CM_BF16 && d.out_dtype != CM_F32) { set_error("out dtype must be CM_BF16 or CM_F32"); return CM_ERR_UNSUPPORTED; }
+  if (d.chunks < 0 || d.chunks > CM_MAX_CHUNKS) { set_error("chunks %d outside 0..%d", d.chunks, CM_MAX_CHUNKS); return CM_ERR_SHAPE; }
+  if (d.m < 1 || d.k < 64 || d.n < 64) { set_error("need m >= 1, k >= 64, n >= 64 (got m=%d k=%d n=%d)", d.m, d.k, d.n); return CM_ERR_SHAPE; }
+  if (d.k % 64 || d.n % 64) { set_error("k (%d) and n (%d) must be multiples of 64", d.k, d.n); return CM_ERR_SHAPE; }
+  if ((long long)d.n_ranks * d.m > (1 << 24)) { set_error("N*m too large"); return CM_ERR_SHAPE; }
+  if (d.copy_gbps < 0 || d.mfma_tflops < 0 || d.launch_us < 0) { set_error("cost-model inputs must be >= 0"); return CM_ERR_INVALID_ARG; }
+  return CM_OK;
+}
+
+// ------------------------------------------------------------------ planning
+namespace {
+
+double gemm_us(const cm_plan_desc &d, double flops) { return flops / (d.mfma_tflops * 1e12) * 1e6 + d.launch_us; }
+double hop_us(const cm_plan_desc &d, double bytes_total, int lanes) {
+  int streams = std::min(d.n_comm, std::max(1, lanes));
+  return bytes_total / (streams * d.copy_gbps * 1e9) * 1e6 + d.launch_us;
+}
+
+// Predicted time of the decomposed op with c chunks (the reading of the
+// "simple peak-rate cost model" of "Knowing when to decline": per-step GEMM
+// time at a sustained rate, per-step hop time at the comm streams' rate, and
+// a fixed cost per launch or hop).
+struct Est { double total, g, h; bool hidden; };
+
+Est estimate(const cm_plan_desc &d, int c) {
+  const double N = d.n_ranks, m = d.m, k = d.k, n = d.n;
+  const bool bi = d.dir == CM_RING_BI && d.n_ranks > 2;
+  const int lanes = d.n_ranks * (bi ? 2 : 1);
+  Est e{};
+  if (d.op == CM_OP_AG_GEMM) {
+    const double g = gemm_us(d, N * 2.0 * (m / c) * k * n * (bi ? 2 : 1));
+    const double h = hop_us(d, N * (m / c) * k * 2.0 * (bi ? 2 : 1), lanes);
+    const int steps = bi ? 1 + (d.n_ranks) / 2 : d.n_ranks;
+    e.g = g; e.h = h;
+    // hop(s) runs beside GEMM(s); GEMM(s+1) needs hop(s)
+    e.total = c * steps * std::max(g, h) + std::min(g, h);
+    e.hidden = h <= g;
+  } else if (d.op == CM_OP_GEMM_RS) {
+    const double g = gemm_us(d, N * 2.0 * m * k * (n / c) * (bi ? 2 : 1));
+    const double h = hop_us(d, N * m * (n / c) * 4.0 * (bi ? 2 : 1), lanes);
+    const int steps = bi ? 1 + (d.n_ranks) / 2 : d.n_ranks;
+    e.g = g; e.h = h;
+    // GEMM(s+1, j) needs hop(s, j), which starts after GEMM(s, j): a step
+    // takes the longer of c GEMM chunks and one chunk's GEMM + hop.
+    e.total = steps * std::max(c * g, g + h) + (c > 1 ? 0 : 0);
+    e.hidden = c >= 2 && h <= (c - 1) * g;
+  } else {
+    const double g = gemm_us(d, N * 2.0 * (N * m) * k * (n / c));
+    const double h = hop_us(d, N * m * (n / c) * 4.0, d.n_ranks) + d.launch_us;  // copy + add
+    const double ring = (N - 1) * h;
+    e.g = g; e.h = h;
+    e.total = std::max(c * g + ring, g + c * ring);
+    e.hidden = ring <= g;
+  }
+  return e;
+}
+
+}  // namespace
+
+cm_status plan(const cm_plan_desc *desc, cm_plan *out) {
+  if (!desc || !out) { set_error("null argument"); return CM_ERR_INVALID_ARG; }
+  cm_plan_desc d = *desc;
+  if (d.copy_gbps == 0) d.copy_gbps = kDefaultCopyGBps;
+  if (d.mfma_tflops == 0) d.mfma_tflops = kDefaultMfmaTflops;
+  if (d.launch_us == 0) d.launch_us = kDefaultLaunchUs;
+  cm_status st = validate_desc(d);
+  if (st != CM_OK) return st;
+  // A two-rank ring has one neighbour: the bidirectional ring is the uni ring.
+  if (d.n_ranks <= 2) d.dir = CM_RING_UNI;
+  // The naive RS is the pipeline RS with one chunk: the whole GEMM, then the
+  // whole ring reduce-scatter.
+  if (d.sched == CM_SCHED_NAIVE) d.dir = CM_RING_UNI;
+  // The pipeline-chunk variant runs a one-directional copy-and-add ring.
+  if (d.op == CM_OP_GEMM_RS_PIPE) d.dir = CM_RING_UNI;
+
+  cm_plan p;
+  std::memset(&p, 0, sizeof p);
+  p.desc = d;
+
+  auto chunk_ok = [&](int c) -> bool {
+    if (c < 1 || c > CM_MAX_CHUNKS) return false;
+    if (d.op == CM_OP_AG_GEMM) return d.m % c == 0;
+    return d.n % c == 0 && (d.n / c) % 64 == 0;
+  };
+
+  int c = d.chunks;
+  if (d.sched == CM_SCHED_NAIVE) {
+    c = 1;
+  } else if (c == 0) {
+    // Auto: candidates 1, 2, 4, 8 (RS needs >= 2 for any overlap, the
+    // pipeline variant starts from the pages' default of four); take the
+    // smallest predicted time; decline when nothing hides the hops.
+    int best = -1;
+    double best_t = 0;
+    const int cands[] = {1, 2, 4, 8};
+    for (int cc : cands) {
+      if (!chunk_ok(cc)) continue;
+      if (d.op == CM_OP_GEMM_RS && cc < 2 && d.n_ranks > 1) continue;
+      if (d.op == CM_OP_AG_GEMM && d.m / cc < 32 && cc > 1) continue;
+      Est e = estimate(d, cc);
+      if (best < 0 || e.total < best_t * 0.97) { best = cc; best_t = e.total; }
+    }
+    if (best < 0) best = 1;
+    if (d.op == CM_OP_GEMM_RS_PIPE && chunk_ok(4) && best != 4) {
+      Est e4 = estimate(d, 4), eb = estimate(d, best);
+      if (e4.total <= eb.total * 1.02) best = 4;
+    }
+    c = best;
+  }
+  if (!chunk_ok(c)) {
+    if (d.op == CM_OP_AG_GEMM)
+      set_error("chunks %d must divide m (%d)", c, d.m);
+    else
+      set_error("chunks %d must divide n (%d) into multiples of 64", c, d.n);
+    return CM_ERR_SHAPE;
+  }
+  (void)is_pow2_chunk;
+  p.chunks = c;
+  const int N = d.n_ranks;
+  const bool bi = d.dir == CM_RING_BI;
+  if (d.sched == CM_SCHED_NAIVE || d.op == CM_OP_GEMM_RS_PIPE) {
+    p.n_steps = 1;
+    p.arc_cw = N - 1;
+    p.arc_ccw = 0;
+  } else if (bi) {
+    p.arc_cw = N / 2;            // ceil((N-1)/2)
+    p.arc_ccw = (N - 1) / 2;     // floor((N-1)/2)
+    p.n_steps = 1 + p.arc_cw;
+  } else {
+    p.arc_cw = N - 1;
+    p.arc_ccw = 0;
+    p.n_steps = N;
+  }
+  Est e = estimate(d, c);
+  p.est_gemm_us = e.g;
+  p.est_hop_us = e.h;
+  p.declined = (N > 1 && !e.hidden) ? 1 : 0;
+  int rows = d.op == CM_OP_AG_GEMM ? d.m / c : d.m;
+  int cols = d.op == CM_OP_AG_GEMM ? d.n : d.n / c;
+  choose_tile(rows, cols, N * (bi ? 2 : 1), &p.tile_m, &p.tile_n);
+  p.ws_bytes = ws_layout(p).total;
+
+  Program prog;
+  build_program(p, prog);
+  p.n_ops = (int)prog.ops.size();
+  p.n_jobs = (int)prog.jobs.size();
+  p.n_events = prog.n_events;
+  *out = p;
+  return CM_OK;
+}
+
+// ------------------------------------------------------------ program build
+namespace {
+
+struct Builder {
+  const cm_plan &p;
+  const cm_plan_desc &d;
+  Program &prog;
+  WsLayout L;
+  int N, c, n_comm;
+  size_t m, k, n, T;
+  int cur_step = -1, cur_chunk = 0;
+
+  Builder(const cm_plan &p_, Program &pr)
+      : p(p_), d(p_.desc), prog(pr), L(ws_layout(p_)), N(d.n_ranks), c(p_.chunks), n_comm(d.n_comm),
+        m(d.m), k(d.k), n(d.n), T((size_t)d.n_ranks * d.m) {}
+
+  // Vector clocks of the streams while building: a wait that the stream
+  // already satisfies (through program order or an earlier wait) is left out.
+  std::vector<std::vector<long>> vc;       // [stream][stream]
+  std::vector<std::vector<long>> event_vc;  // [event][stream]
+  void ensure_clocks() {
+    if (vc.empty()) vc.assign(n_comm + 1, std::vector<long>(n_comm + 1, 0));
+  }
+  void tick(int stream) {
+    ensure_clocks();
+    vc[stream][stream]++;
+  }
+
+  int new_event() { return prog.n_events++; }
+  cm_op_rec base(int kind, int stream) {
+    cm_op_rec o;
+    std::memset(&o, 0, sizeof o);
+    o.kind = kind;
+    o.stream = stream;
+    o.step = cur_step;
+    o.chunk = cur_chunk;
+    o.src_buf = o.dst_buf = -1;
+    return o;
+  }
+  int record(int stream) {
+    int e = new_event();
+    cm_op_rec o = base(CM_OPK_RECORD, stream);
+    o.event = e;
+    prog.ops.push_back(o);
+    tick(stream);
+    event_vc.push_back(vc[stream]);
+    return e;
+  }
+  void wait(int stream, int event) {
+    if (event < 0) return;
+    ensure_clocks();
+    const std::vector<long> &ev = event_vc[event];
+    bool implied = true;
+    for (int t = 0; t <= n_comm; ++t)
+      if (ev[t] > vc[stream][t]) { implied = false; break; }
+    if (implied) return;
+    cm_op_rec o = base(CM_OPK_WAIT, stream);
+    o.event = event;
+    prog.ops.push_back(o);
+    for (int t = 0; t <= n_comm; ++t) vc[stream][t] = std::max(vc[stream][t], ev[t]);
+    tick(stream);
+  }
+  void copy(int stream, int sbuf, size_t soff, int dbuf, size_t doff, size_t bytes) {
+    if (bytes == 0) return;
+    cm_op_rec o = base(CM_OPK_COPY, stream);
+    o.src_buf = sbuf; o.src_off = soff; o.dst_buf = dbuf; o.dst_off = doff; o.bytes = bytes;
+    prog.ops.push_back(o);
+    tick(stream);
+  }
+  static cm_job_rec job0() {
+    cm_job_rec j;
+    std::memset(&j, 0, sizeof j);
+    j.a_buf = j.b_buf = j.c_buf = j.in0_buf = j.in1_buf = -1;
+    return j;
+  }
+  void gemm(const std::vector<cm_job_rec> &jobs, int rows, int cols, int depth) {
+    if (jobs.empty()) return;
+    cm_op_rec o = base(CM_OPK_GEMM, 0);
+    o.first_job = (int)prog.jobs.size();
+    o.n_jobs = (int)jobs.size();
+    o.rows = rows; o.cols = cols; o.depth = depth;
+    choose_tile(rows, cols, (int)jobs.size(), &o.tile_m, &o.tile_n);
+    prog.jobs.insert(prog.jobs.end(), jobs.begin(), jobs.end());
+    prog.ops.push_back(o);
+    tick(0);
+  }
+  void reduce(int stream, const std::vector<cm_job_rec> &jobs, int rows, int cols) {
+    if (jobs.empty()) return;
+    cm_op_rec o = base(CM_OPK_REDUCE, stream);
+    o.first_job = (int)prog.jobs.size();
+    o.n_jobs = (int)jobs.size();
+    o.rows = rows; o.cols = cols;
+    prog.jobs.insert(prog.jobs.end(), jobs.begin(), jobs.end());
+    prog.ops.push_back(o);
+    tick(stream);
+  }
+
+  // Comm-stream groups: the ranks of one direction are cut into contiguous
+  // ranges, one range per comm stream (so a hop of a range of ranks is one
+  // or two contiguous copies).  Returns the 1-based stream ids.
+  struct Group { int a, b, stream; };
+  std::vector<Group> groups(int dir, int ndir) {
+    int avail = std::max(1, n_comm / ndir);
+    int first = (ndir == 2 && n_comm >= 2) ? dir * (n_comm / 2) : 0;
+    int ng = std::min(avail, N);
+    std::vector<Group> g;
+    for (int i = 0; i < ng; ++i) {
+      int a = (int)((long)N * i / ng), b = (int)((long)N * (i + 1) / ng);
+      g.push_back({a, b, 1 + first + i});
+    }
+    return g;
+  }
+  static int group_of(const std::vector<Group> &gs, int r) {
+    for (size_t i = 0; i < gs.size(); ++i)
+      if (r >= gs[i].a && r < gs[i].b) return (int)i;
+    return -1;
+  }
+  std::vector<int> comm_streams() {
+    std::vector<int> s;
+    for (int i = 1; i <= n_comm; ++i) s.push_back(i);
+    return s;
+  }
+
+  // Copy rank range [a, b) of a per-rank block array to the ranks shifted by
+  // `shift` (+1 clockwise, -1 counter-clockwise) in another array with the
+  // same per-rank block size; splits at the ring's wrap.
+  void shifted_copy(int stream, int sbuf, size_t sbase, int dbuf, size_t dbase, size_t block, int a, int b,
+                    int shift) {
+    int r = a;
+    while (r < b) {
+      int dr = mod(r + shift, N);
+      int run = 1;
+      while (r + run < b && mod(r + run + shift, N) == dr + run) ++run;
+      copy(stream, sbuf, sbase + (size_t)r * block, dbuf, dbase + (size_t)dr * block, block * run);
+      r += run;
+    }
+  }
+
+  void entry() {
+    cur_step = -1; cur_chunk = 0;
+    int e = record(0);
+    for (int s : comm_streams()) wait(s, e);
+  }
+  void exit_() {
+    cur_step = -1; cur_chunk = 0;
+    ensure_clocks();
+    for (int s : comm_streams()) {
+      if (vc[0][s] >= vc[s][s]) continue;  // the compute stream already follows all of it
+      int e = record(s);
+      wait(0, e);
+    }
+  }
+
+  // ------------------------------------------------------------ AG, decomposed
+  void ag_decomposed() {
+    const int ndir = d.dir == CM_RING_BI ? 2 : 1;
+    const size_t mc = m / c;
+    const size_t chunk_bytes = mc * k * 2;             // one rank's chunk, bf16
+    auto slot_off = [&](int dir, int par, int j, int r) -> size_t {
+      return dir * L.slot_dir_bytes + ((((size_t)par * c + j) * N + r) * chunk_bytes);
+    };
+    std::vector<std::vector<Group>> G(ndir);
+    for (int dr = 0; dr < ndir; ++dr) G[dr] = groups(dr, ndir);
+    // events: hop[s][j][dir][group], gemm[s][j]
+    std::vector<std::vector<std::vector<std::vector<int>>>> ehop(p.n_steps,
+        std::vector<std::vector<std::vector<int>>>(c, std::vector<std::vector<int>>(ndir)));
+    std::vector<std::vector<int>> egemm(p.n_steps, std::vector<int>(c, -1));
+    const int arcs[2] = {p.arc_cw, p.arc_ccw};
+    entry();
+    for (int s = 0; s < p.n_steps; ++s) {
+      for (int j = 0; j < c; ++j) {
+        cur_step = s; cur_chunk = j;
+        // hops of step s: forward what this step multiplies
+        for (int dr = 0; dr < ndir; ++dr) {
+          if (s >= arcs[dr]) continue;
+          const int shift = dr == 0 ? 1 : -1;
+          ehop[s][j][dr].assign(G[dr].size(), -1);
+          for (size_t gi = 0; gi < G[dr].size(); ++gi) {
+            const Group &g = G[dr][gi];
+            // WAR: the destination slot (parity s%2) was read by GEMM(s-1, j)
+            // and, as the source of hop(s-1, j), by the downstream ranks' copies
+            if (s >= 2) {
+              wait(g.stream, egemm[s - 1][j]);
+              for (int r = g.a; r < g.b; ++r) {
+                int down = group_of(G[dr], mod(r + shift, N));
+                if (down != (int)gi) wait(g.stream, ehop[s - 1][j][dr][down]);
+              }
+            }
+            // RAW: the source slot was filled by hop(s-1, j) from the upstream ranks
+            if (s >= 1) {
+              for (int r = g.a; r < g.b; ++r) {
+                int up = group_of(G[dr], mod(r - shift, N));
+                if (up != (int)gi) { wait(g.stream, ehop[s - 1][j][dr][up]); }
+              }
+            }
+            if (s == 0) {
+              // from the user's shards: rank r's chunk j rows
+              for (int r = g.a; r < g.b; ++r)
+                copy(g.stream, CM_BUF_X, ((size_t)r * m + (size_t)j * mc) * k * 2, CM_BUF_WS,
+                     slot_off(dr, 0, j, mod(r + shift, N)), chunk_bytes);
+            } else {
+              shifted_copy(g.stream, CM_BUF_WS, slot_off(dr, (s - 1) % 2, j, 0), CM_BUF_WS,
+                           slot_off(dr, s % 2, j, 0), chunk_bytes, g.a, g.b, shift);
+            }
+            ehop[s][j][dr][gi] = record(g.stream);
+          }
+        }
+        // GEMM(s, j) needs hop(s-1, j)
+        if (s >= 1)
+          for (int dr = 0; dr < ndir; ++dr)
+            if (s - 1 < arcs[dr])
+              for (int e : ehop[s - 1][j][dr]) wait(0, e);
+        std::vector<cm_job_rec> jobs;
+        for (int dr = 0; dr < ndir; ++dr) {
+          if (s > 0 && s > arcs[dr]) continue;
+          if (s == 0 && dr > 0) continue;
+          for (int r = 0; r < N; ++r) {
+            cm_job_rec jb = job0();
+            jb.rank = r;
+            jb.dir = dr;
+            int shard = s == 0 ? r : (dr == 0 ? mod(r - s, N) : mod(r + s, N));
+            jb.index = shard;
+            if (s == 0) {
+              jb.a_buf = CM_BUF_X;
+              jb.a_off = ((size_t)r * m + (size_t)j * mc) * k * 2;
+            } else {
+              jb.a_buf = CM_BUF_WS;
+              jb.a_off = slot_off(dr, (s - 1) % 2, j, r);
+            }
+            jb.lda = (int)k;
+            jb.b_buf = CM_BUF_W;
+            jb.b_off = (size_t)r * n * k * 2;
+            jb.ldb = (int)k;
+            jb.c_buf = CM_BUF_Y;
+            jb.c_dtype = d.out_dtype;
+            jb.c_off = ((size_t)r * T + (size_t)shard * m + (size_t)j * mc) * n * (d.out_dtype == CM_F32 ? 4 : 2);
+            jb.ldc = (int)n;
+            jobs.push_back(jb);
+          }
+        }
+        gemm(jobs, (int)mc, (int)n, (int)k);
+        egemm[s][j] = record(0);
+      }
+    }
+    exit_();
+  }
+
+  // --------------------------------------------------------------- AG, naive
+  void ag_naive() {
+    const size_t shard_bytes = m * k * 2;
+    const size_t rank_bytes = T * k * 2;  // G[r]
+    std::vector<Group> G = groups(0, 1);
+    entry();
+    cur_step = 0; cur_chunk = 0;
+    std::vector<int> prev(G.size(), -1), cur(G.size(), -1);
+    // every rank's own shard into its gathered buffer (the collective's local part)
+    for (size_t gi = 0; gi < G.size(); ++gi)
+      for (int r = G[gi].a; r < G[gi].b; ++r)
+        copy(G[gi].stream, CM_BUF_X, (size_t)r * shard_bytes, CM_BUF_WS, (size_t)r * rank_bytes + (size_t)r * shard_bytes,
+             shard_bytes);
+    for (int h = 0; h < N - 1; ++h) {
+      cur_step = h;
+      for (size_t gi = 0; gi < G.size(); ++gi) {
+        const Group &g = G[gi];
+        if (h >= 1)
+          for (int r = g.a; r < g.b; ++r) {
+            int up = group_of(G, mod(r - 1, N));
+            if (up != (int)gi) wait(g.stream, prev[up]);
+          }
+        for (int r = g.a; r < g.b; ++r) {
+          int shard = mod(r - h, N);
+          int dst = mod(r + 1, N);
+          if (h == 0)
+            copy(g.stream, CM_BUF_X, (size_t)r * shard_bytes, CM_BUF_WS, (size_t)dst * rank_bytes + shard * shard_bytes,
+                 shard_bytes);
+          else
+            copy(g.stream, CM_BUF_WS, (size_t)r * rank_bytes + shard * shard_bytes, CM_BUF_WS,
+                 (size_t)dst * rank_bytes + shard * shard_bytes, shard_bytes);
+        }
+        cur[gi] = record(g.stream);
+      }
+      prev = cur;
+    }
+    cur_step = N - 1;
+    // the whole gathered activation is needed before the GEMM
+    for (size_t gi = 0; gi < G.size(); ++gi) {
+      int e = prev[gi];
+      if (e < 0) e = record(G[gi].stream);  // N == 1: only the local copies
+      wait(0, e);
+    }
+    std::vector<cm_job_rec> jobs;
+    for (int r = 0; r < N; ++r) {
+      cm_job_rec jb = job0();
+      jb.rank = r; jb.index = r;
+      jb.a_buf = CM_BUF_WS; jb.a_off = (size_t)r * rank_bytes; jb.lda = (int)k;
+      jb.b_buf = CM_BUF_W; jb.b_off = (size_t)r * n * k * 2; jb.ldb = (int)k;
+      jb.c_buf = CM_BUF_Y; jb.c_off = (size_t)r * T * n * (d.out_dtype == CM_F32 ? 4 : 2); jb.ldc = (int)n;
+      jb.c_dtype = d.out_dtype;
+      jobs.push_back(jb);
+    }
+    gemm(jobs, (int)T, (int)n, (int)k);
+    exit_();
+  }
+
+  // ------------------------------------------------------------ RS, decomposed
+  void rs_decomposed() {
+    const bool bi = d.dir == CM_RING_BI;
+    const int ndir = bi ? 2 : 1;
+    const size_t nc = n / c;
+    const size_t blk = m * nc * 4;  // one rank's bucket chunk, fp32
+    const int osz = d.out_dtype == CM_F32 ? 4 : 2;
+    auto bkt = [&](int dir, int par, int j, int r) -> size_t {
+      return dir * L.slot_dir_bytes + ((((size_t)par * c + j) * N + r) * blk);
+    };
+    std::vector<std::vector<Group>> G(ndir);
+    for (int dr = 0; dr < ndir; ++dr) G[dr] = groups(dr, ndir);
+    const int Lc = p.arc_cw, R = p.arc_ccw;
+    // step s: clockwise contribution if s < Lc (uni: s < N-1), counter-clockwise if
+    // Lc-R <= s < Lc, the owner's final add at s == last.
+    const int last = bi ? Lc : N - 1;
+    std::vector<std::vector<std::vector<int>>> ehop(c, std::vector<std::vector<int>>(ndir));
+    entry();
+    for (int s = 0; s <= last; ++s) {
+      for (int j = 0; j < c; ++j) {
+        cur_step = s; cur_chunk = j;
+        // RAW: the buckets this step adds into arrived with hop(s-1, j)
+        if (s >= 1)
+          for (int dr = 0; dr < ndir; ++dr)
+            for (int e : ehop[j][dr]) wait(0, e);
+        std::vector<cm_job_rec> jobs;
+        auto mk = [&](int r, int dr, int bucket) {
+          cm_job_rec jb = job0();
+          jb.rank = r; jb.dir = dr; jb.index = bucket;
+          jb.a_buf = CM_BUF_X; jb.a_off = ((size_t)r * T + (size_t)bucket * m) * k * 2; jb.lda = (int)k;
+          jb.b_buf = CM_BUF_W; jb.b_off = ((size_t)r * n + (size_t)j * nc) * k * 2; jb.ldb = (int)k;
+          jb.ld_in = (int)nc;
+          return jb;
+        };
+        for (int r = 0; r < N; ++r) {
+          if (s == last) {
+            // the owner: its own partial + the arriving bucket(s) -> Out_r
+            cm_job_rec jb = mk(r, 0, r);
+            jb.c_buf = CM_BUF_Y; jb.c_off = ((size_t)r * m * n + (size_t)j * nc) * osz; jb.ldc = (int)n;
+            jb.c_dtype = d.out_dtype;
+            if (N > 1) { jb.in0_buf = CM_BUF_WS; jb.in0_off = bkt(0, s % 2, j, r); }
+            if (bi && R >= 1) { jb.in1_buf = CM_BUF_WS; jb.in1_off = bkt(1, s % 2, j, r); }
+            jobs.push_back(jb);
+            continue;
+          }
+          // clockwise: bucket (r + (Lc - s)) in bi, (r - s - 1) in uni -- both
+          // equal r + (arc - s) with arc = N - 1 in uni
+          int arc = bi ? Lc : N - 1;
+          int q = mod(r + (arc - s), N);
+          cm_job_rec jb = mk(r, 0, q);
+          jb.c_buf = CM_BUF_WS; jb.c_off = bkt(0, s % 2, j, r); jb.ldc = (int)nc; jb.c_dtype = CM_F32;
+          if (s > 0) { jb.in0_buf = CM_BUF_WS; jb.in0_off = jb.c_off; }
+          jobs.push_back(jb);
+          if (bi && s >= Lc - R) {
+            int qq = mod(r - (Lc - s), N);
+            cm_job_rec jc = mk(r, 1, qq);
+            jc.c_buf = CM_BUF_WS; jc.c_off = bkt(1, s % 2, j, r); jc.ldc = (int)nc; jc.c_dtype = CM_F32;
+            if (s > Lc - R) { jc.in0_buf = CM_BUF_WS; jc.in0_off = jc.c_off; }
+            jobs.push_back(jc);
+          }
+        }
+        gemm(jobs, (int)m, (int)nc, (int)k);
+        int eg = record(0);
+        if (s == last) continue;
+        for (int dr = 0; dr < ndir; ++dr) {
+          ehop[j][dr].clear();
+          if (dr == 1 && s < Lc - R) continue;
+          const int shift = dr == 0 ? 1 : -1;
+          for (const Group &g : G[dr]) {
+            // RAW: the bucket was produced by GEMM(s, j).  WAR on the
+            // destination slot holds through GEMM(s, j), which waited for
+            // hop(s-1, j), the slot's last reader.
+            wait(g.stream, eg);
+            shifted_copy(g.stream, CM_BUF_WS, bkt(dr, s % 2, j, 0), CM_BUF_WS, bkt(dr, (s + 1) % 2, j, 0), blk, g.a,
+                         g.b, shift);
+            ehop[j][dr].push_back(record(g.stream));
+          }
+        }
+      }
+    }
+    exit_();
+  }
+
+  // ------------------------------------------------- RS, pipeline chunks / naive
+  void rs_pipe() {
+    const size_t nc = n / c;
+    const int osz = d.out_dtype == CM_F32 ? 4 : 2;
+    const size_t part_rank = (size_t)c * T * nc * 4;           // P[r]
+    auto part = [&](int r, int j, int bucket) -> size_t {        // P[r][j] rows of `bucket`
+      return L.partial + (size_t)r * part_rank + ((size_t)j * T + (size_t)bucket * m) * nc * 4;
+    };
+    const size_t blk = m * nc * 4;
+    auto ring = [&](int par, int r) -> size_t { return L.ring + ((size_t)par * N + r) * blk; };
+    std::vector<Group> G = groups(0, 1);
+    const int red_stream = G[0].stream;
+    entry();
+    int prev_chunk_done = -1;
+    for (int j = 0; j < c; ++j) {
+      cur_step = 0; cur_chunk = j;
+      std::vector<cm_job_rec> jobs;
+      for (int r = 0; r < N; ++r) {
+        cm_job_rec jb = job0();
+        jb.rank = r; jb.index = j;
+        jb.a_buf = CM_BUF_X; jb.a_off = (size_t)r * T * k * 2; jb.lda = (int)k;
+        jb.b_buf = CM_BUF_W; jb.b_off = ((size_t)r * n + (size_t)j * nc) * k * 2; jb.ldb = (int)k;
+        if (N == 1) {
+          jb.c_buf = CM_BUF_Y; jb.c_off = (size_t)j * nc * osz; jb.ldc = (int)n; jb.c_dtype = d.out_dtype;
+        } else {
+          jb.c_buf = CM_BUF_WS; jb.c_off = part(r, j, 0); jb.ldc = (int)nc; jb.c_dtype = CM_F32;
+        }
+        jobs.push_back(jb);
+      }
+      gemm(jobs, (int)T, (int)nc, (int)k);
+      int eg = record(0);
+      if (N == 1) continue;
+      int ered = -1;
+      for (int t = 0; t < N - 1; ++t) {
+        cur_step = t;
+        std::vector<int> ecp;
+        for (const Group &g : G) {
+          if (t == 0) {
+            wait(g.stream, eg);                                      // RAW on P[*][j]
+            if (g.stream != red_stream) wait(g.stream, prev_chunk_done);  // WAR on the ring slots
+            for (int r = g.a; r < g.b; ++r)
+              copy(g.stream, CM_BUF_WS, part(r, j, mod(r - 1, N)), CM_BUF_WS, ring(0, mod(r + 1, N)), blk);
+          } else {
+            if (g.stream != red_stream) wait(g.stream, ered);          // RAW: reduce(t-1) wrote the source
+            shifted_copy(g.stream, CM_BUF_WS, ring((t - 1) % 2, 0), CM_BUF_WS, ring(t % 2, 0), blk, g.a, g.b, 1);
+          }
+          if (g.stream != red_stream) ecp.push_back(record(g.stream));
+        }
+        for (int e : ecp) wait(red_stream, e);
+        std::vector<cm_job_rec> rj;
+        for (int r = 0; r < N; ++r) {
+          int q = mod(r - 2 - t, N);  // the bucket rank r received at hop t
+          cm_job_rec jb = job0();
+          jb.rank = r; jb.index = q;
+          jb.in0_buf = CM_BUF_WS; jb.in0_off = ring(t % 2, r);
+          jb.in1_buf = CM_BUF_WS; jb.in1_off = part(r, j, q);
+          jb.ld_in = (int)nc;
+          if (t == N - 2) {
+            jb.c_buf = CM_BUF_Y; jb.c_off = ((size_t)r * m * n + (size_t)j * nc) * osz; jb.ldc = (int)n;
+            jb.c_dtype = d.out_dtype;
+          } else {
+            jb.c_buf = CM_BUF_WS; jb.c_off = ring(t % 2, r); jb.ldc = (int)nc; jb.c_dtype = CM_F32;
+          }
+          rj.push_back(jb);
+        }
+        reduce(red_stream, rj, (int)m, (int)nc);
+        ered = record(red_stream);
+      }
+      prev_chunk_done = ered;
+    }
+    exit_();
+  }
+};
+
+}  // namespace
+
+void build_program(const cm_plan &p, Program &prog) {
+  prog.ops.clear();
+  prog.jobs.clear();
+  prog.n_events = 0;
+  Builder b(p, prog);
+  const cm_plan_desc &d = p.desc;
+  if (d.op == CM_OP_AG_GEMM) {
+    if (d.sched == CM_SCHED_NAIVE) b.ag_naive(); else b.ag_decomposed();
+  } else if (d.op == CM_OP_GEMM_RS && d.sched == CM_SCHED_DECOMPOSED) {
+    b.rs_decomposed();
+  } else {
+    b.rs_pipe();
+  }
+}
+
+}  // namespace collmm
+
+// ------------------------------------------------------------------- C ABI
+extern "C" {
+
+cm_status cm_ring_plan(const cm_plan_desc *desc, cm_plan *out) { return collmm::plan(desc, out); }
+
+cm_status cm_workspace_size(const cm_plan *plan, size_t *bytes) {
+  if (!plan || !bytes) { collmm::set_error("null argument"); return CM_ERR_INVALID_ARG; }
+  *bytes = plan->ws_bytes;
+  return CM_OK;
+}
+
+cm_status cm_plan_program(const cm_plan *plan, cm_op_rec *ops, int op_cap, int *n_ops, cm_job_rec *jobs,
+                          int job_cap, int *n_jobs) {
+  if (!plan) { collmm::set_error("null plan"); return CM_ERR_INVALID_ARG; }
+  cm_status st = collmm::validate_desc(plan->desc);
+  if (st != CM_OK) return st;
+  collmm::Program prog;
+  collmm::build_program(*plan, prog);
+  if (n_ops) *n_ops = (int)prog.ops.size();
+  if (n_jobs) *n_jobs = (int)prog.jobs.size();
+  if (op_cap < 0 || job_cap < 0) { collmm::set_error("negative capacity"); return CM_ERR_INVALID_ARG; }
+  if ((ops == nullptr && op_cap > 0) || (jobs == nullptr && job_cap > 0)) {
+    collmm::set_error("null array with non-zero capacity");
+    return CM_ERR_INVALID_ARG;
+  }
+  if (ops == nullptr && jobs == nullptr) return CM_OK;  // size query
+  if ((int)prog.ops.size() > op_cap || (int)prog.jobs.size() > job_cap) {
+    collmm::set_error("program needs %zu ops and %zu jobs", prog.ops.size(), prog.jobs.size());
+    return CM_ERR_CAPACITY;
+  }
+  std::copy(prog.ops.begin(), prog.ops.end(), ops);
+  std::copy(prog.jobs.begin(), prog.jobs.end(), jobs);
+  return CM_OK;
+}
+
+const char *cm_status_string(cm_status s) {
+  switch (s) {
+    case CM_OK: return "CM_OK";
+    case CM_ERR_INVALID_ARG: return "CM_ERR_INVALID_ARG";
+    case CM_ERR_SHAPE: return "CM_ERR_SHAPE";
+    case CM_ERR_ALIGN: return "CM_ERR_ALIGN";
+    case CM_ERR_WORKSPACE: return "CM_ERR_WORKSPACE";
+    case CM_ERR_UNSUPPORTED: return "CM_ERR_UNSUPPORTED";
+    case CM_ERR_HIP: return "CM_ERR_HIP";
+    case CM_ERR_CAPACITY: return "CM_ERR_CAPACITY";
+  }
+  return "CM_ERR_UNKNOWN";
+}
+
+const char *cm_last_error(void) { return collmm::last_error(); }
+
+const char *cm_version(void) { return "0.1.0"; }
+
+}  // extern "C"

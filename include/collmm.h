@@ -1,0 +1,259 @@
+/*
+ * libcollmm -- tensor-parallel AllGather->GEMM and GEMM->ReduceScatter,
+ * decomposed into per-shard partial GEMMs that overlap with ring hops,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method (cited by page title and section):
+ *   - "Hiding Tensor-Parallel Collectives: AG/RS Overlap in Megatron",
+ *     sections 3 (P2P AllGather overlap), 5 (P2P ReduceScatter overlap),
+ *     6 (pipeline-chunk ReduceScatter), 8 (dependency classes) and 9 (what a
+ *     trace should show).
+ *   - "Overlap Communication with Dependent Computation via Decomposition in
+ *     Large Deep Learning Models", sections "The idea" (AllGather->Einsum with
+ *     a slice-update of each partial result; Einsum->ReduceScatter with a
+ *     circulating accumulator; asynchronous transfer start/done pairs;
+ *     bidirectional rings; a cost model that can decline) and "What it costs"
+ *     (the pre-shift and realigning addition of bidirectional rings).
+ *
+ * Emulation model.  An N-rank tensor-parallel group is emulated on ONE GPU:
+ * every virtual rank's shards, weights, receive slots and buckets are
+ * regions of buffers in that GPU's memory.  A ring hop ("send to one
+ * neighbour, receive from the other") is an asynchronous device-to-device
+ * copy on a communication stream, executed by the SDMA copy engines
+ * (hipMemcpyDeviceToDeviceNoCU), ordered against the compute stream with
+ * events.  The partial GEMMs of all N ranks for one step are one kernel
+ * launch on the compute stream.
+ *
+ * Layouts (all row-major, C order; "bf16" = IEEE binary32 upper half):
+ *   AllGather->GEMM  (column-parallel linear; T = N*m tokens)
+ *     x  [N][m][k]     bf16   rank r's sequence shard X_r
+ *     w  [N][n][k]     bf16   W_r, one output feature per row (k contiguous)
+ *     y  [N][T][n]     out    Y_r = concat_r(X_r) . W_r^T
+ *   GEMM->ReduceScatter  (row-parallel linear)
+ *     x  [N][T][k]     bf16   H_r, rank r's activation for all T tokens
+ *     w  [N][n][k]     bf16   W_r, one output feature per row
+ *     y  [N][m][n]     out    Out_q = sum_r (H_r . W_r^T)[q*m:(q+1)*m, :]
+ *   out dtype: CM_F32 or CM_BF16 (round to nearest even, once, at the end).
+ *   Accumulation is fp32 (MFMA); RS buckets travel in fp32.
+ *
+ * Ownership and ordering.  The caller allocates every device buffer (the
+ * library never allocates or frees device memory; its only resources are
+ * per-thread HIP events).  Calls are asynchronous: they enqueue work on the
+ * compute stream and the comm streams and return.  At entry every comm
+ * stream waits for the work already enqueued on the compute stream; at exit
+ * the compute stream waits for every comm stream, so the caller needs to
+ * synchronise only the compute stream.  Inputs must stay alive and
+ * unmodified, and outputs and the workspace untouched, until the compute
+ * stream passes the operation.  Two calls that share a workspace or streams
+ * must not be issued from different host threads at the same time.
+ *
+ * Errors.  Every entry point returns a cm_status; nothing throws across the
+ * ABI.  Arguments are validated before any HIP call, so an invalid call
+ * enqueues nothing.  CM_ERR_HIP carries the HIP error text in
+ * cm_last_error().  Faults inside kernels surface at the caller's stream
+ * synchronisation, like any other HIP kernel fault.
+ */
+#ifndef COLLMM_H
+#define COLLMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CM_OK = 0,
+  CM_ERR_INVALID_ARG = 1, /* null pointer, N < 1, stream count wrong, bad enum */
+  CM_ERR_SHAPE = 2,       /* divisibility or size limits violated */
+  CM_ERR_ALIGN = 3,       /* a device pointer is not 16-byte aligned */
+  CM_ERR_WORKSPACE = 4,   /* ws_bytes smaller than the plan needs */
+  CM_ERR_UNSUPPORTED = 5, /* dtype or device not supported (gfx950 only) */
+  CM_ERR_HIP = 6,         /* a HIP call failed; see cm_last_error() */
+  CM_ERR_CAPACITY = 7     /* a caller-provided output array is too small */
+} cm_status;
+
+typedef enum {
+  CM_OP_AG_GEMM = 0,     /* AllGather -> GEMM */
+  CM_OP_GEMM_RS = 1,     /* GEMM -> ReduceScatter, circulating bucket */
+  CM_OP_GEMM_RS_PIPE = 2 /* GEMM -> ReduceScatter, pipeline chunks */
+} cm_op;
+
+typedef enum { CM_RING_UNI = 0, CM_RING_BI = 1 } cm_ring_dir;
+
+typedef enum {
+  CM_SCHED_DECOMPOSED = 0, /* partial GEMMs overlapped with ring hops */
+  CM_SCHED_NAIVE = 1       /* the blocking baseline: the whole collective, then the whole GEMM
+                              (AG), or the whole GEMM, then the whole collective (RS) */
+} cm_sched;
+
+typedef enum { CM_BF16 = 0, CM_F32 = 1 } cm_dtype;
+
+#define CM_MAX_RANKS 64
+#define CM_MAX_CHUNKS 16
+#define CM_MAX_COMM 32
+
+/* What the caller asks for. */
+typedef struct {
+  int op;        /* cm_op */
+  int n_ranks;   /* N, 1..CM_MAX_RANKS */
+  int m;         /* rows per sequence shard; T = N*m */
+  int k;         /* contraction length per rank (AG: d; RS: f/N) */
+  int n;         /* output columns per rank (AG: f/N; RS: d) */
+  int dir;       /* cm_ring_dir */
+  int chunks;    /* c: AG row chunks per shard, RS column chunks per bucket,
+                    PIPE output column chunks; 0 = choose with the cost model */
+  int sched;     /* cm_sched */
+  int in_dtype;  /* CM_BF16 */
+  int out_dtype; /* CM_F32 or CM_BF16 */
+  int n_comm;    /* number of comm streams the calls will pass, 1..CM_MAX_COMM */
+  /* Cost-model inputs (0 = built-in defaults for MI355X). */
+  double copy_gbps;      /* sustained hop bandwidth of ONE comm stream, GB/s */
+  double mfma_tflops;    /* sustained bf16 GEMM rate, TFLOP/s */
+  double launch_us;      /* fixed cost per step launch / hop, microseconds */
+} cm_plan_desc;
+
+/* The resolved schedule.  Plain data: no heap, nothing to destroy. */
+typedef struct {
+  cm_plan_desc desc;   /* copy of the request with defaults filled in */
+  int chunks;          /* chosen c */
+  int n_steps;         /* compute steps per chunk (AG uni: N; bi: 1 + ceil((N-1)/2)) */
+  int arc_cw;          /* ring hops clockwise  (uni: N-1; bi: ceil((N-1)/2)) */
+  int arc_ccw;         /* ring hops counter-clockwise (uni: 0; bi: floor((N-1)/2)) */
+  int tile_m, tile_n;  /* GEMM block tile */
+  int declined;        /* 1 if the cost model found no chunking that hides the hops */
+  int n_ops;           /* length of the program cm_plan_program() emits */
+  int n_jobs;          /* total GEMM / reduce jobs in that program */
+  int n_events;        /* events the program uses */
+  size_t ws_bytes;     /* workspace bytes the calls need */
+  double est_gemm_us;  /* cost model: one step's GEMM time (all ranks, one chunk) */
+  double est_hop_us;   /* cost model: one step's hop time (all ranks, one chunk) */
+} cm_plan;
+
+/*
+ * Build a plan.  Fails with CM_ERR_SHAPE unless: N*m rows; k and n are
+ * multiples of 64; AG: c divides m; RS: c divides n and n/c is a multiple
+ * of 64; PIPE: same as RS.  Host only: makes no HIP call.
+ */
+cm_status cm_ring_plan(const cm_plan_desc *desc, cm_plan *out);
+
+/* Workspace bytes a plan needs (same as plan->ws_bytes). */
+cm_status cm_workspace_size(const cm_plan *plan, size_t *bytes);
+
+/*
+ * The plan as a program: the exact sequence of operations the executor
+ * enqueues, in order, for inspection and CPU simulation.  Buffers are named
+ * symbolically and addressed by byte offsets.  Host only.
+ */
+typedef enum { CM_BUF_X = 0, CM_BUF_W = 1, CM_BUF_Y = 2, CM_BUF_WS = 3 } cm_buf;
+
+typedef enum {
+  CM_OPK_GEMM = 0,   /* one launch of partial GEMMs: jobs [first_job, first_job+n_jobs) */
+  CM_OPK_COPY = 1,   /* one hop copy of `bytes` from (src_buf, src_off) to (dst_buf, dst_off) */
+  CM_OPK_RECORD = 2, /* record event `event` on `stream` */
+  CM_OPK_WAIT = 3,   /* `stream` waits for the last record of `event` */
+  CM_OPK_REDUCE = 4  /* one launch of elementwise adds: jobs [first_job, ...) */
+} cm_op_kind;
+
+typedef struct {
+  int kind;      /* cm_op_kind */
+  int stream;    /* 0 = compute stream, 1..n_comm = comm stream (stream-1) */
+  int event;     /* RECORD / WAIT */
+  int step;      /* schedule step this op belongs to (-1 = entry/exit) */
+  int chunk;     /* chunk index */
+  int first_job; /* GEMM / REDUCE */
+  int n_jobs;
+  int rows, cols, depth; /* GEMM: M, N, K of every job; REDUCE: rows, cols */
+  int tile_m, tile_n;    /* GEMM: block tile the launch uses */
+  int src_buf, dst_buf;  /* COPY */
+  size_t src_off, dst_off, bytes;
+} cm_op_rec;
+
+/*
+ * One job of a GEMM op:  C[i][j] = sum_kk A[i][kk] * B[j][kk] + in0[i][j] + in1[i][j]
+ * for i < rows, j < cols, kk < depth.  A, B bf16; in0/in1 fp32, each optional
+ * (buf -1 = absent; in0 may alias C: read-add-write); C in c_dtype.
+ * lda/ldb/ldc/ld_in are row strides in elements.  For a REDUCE op:
+ * C = in0 + in1 (both fp32, both present).  `rank`, `dir` and `index` (the
+ * shard or bucket the job works on) label the job for tests; the executor
+ * does not use them.
+ */
+typedef struct {
+  int rank, dir, index;
+  int a_buf, b_buf, c_buf, in0_buf, in1_buf;
+  size_t a_off, b_off, c_off, in0_off, in1_off;
+  int lda, ldb, ldc, ld_in;
+  int c_dtype;
+} cm_job_rec;
+
+/*
+ * Emit the plan's program.  ops (capacity op_cap) and jobs (capacity
+ * job_cap) are caller-owned host arrays; pass NULL with zero capacity to
+ * query the sizes (also in plan->n_ops / n_jobs).  CM_ERR_CAPACITY if an
+ * array is too small.
+ */
+cm_status cm_plan_program(const cm_plan *plan, cm_op_rec *ops, int op_cap, int *n_ops,
+                          cm_job_rec *jobs, int job_cap, int *n_jobs);
+
+/*
+ * Optional timing trace.  When a non-NULL trace is passed to a call, the
+ * executor records a timing event on the issuing stream before and after
+ * every GEMM launch, every hop group and every reduce launch (the work is
+ * the same as without a trace).  After the compute stream has completed,
+ * cm_trace_read() converts the events into microseconds since the call's
+ * entry event.  The trace owns its events: create once, reuse, destroy.
+ */
+typedef struct cm_trace cm_trace;
+
+typedef struct {
+  int kind;      /* CM_OPK_GEMM, CM_OPK_COPY (one per hop group per stream) or CM_OPK_REDUCE */
+  int stream;    /* as in cm_op_rec */
+  int step, chunk;
+  double start_us, end_us;
+} cm_span;
+
+cm_status cm_trace_create(int capacity, cm_trace **out);
+cm_status cm_trace_destroy(cm_trace *trace);
+/* Spans of the last call that used `trace`; *n_spans receives the count. */
+cm_status cm_trace_read(cm_trace *trace, cm_span *spans, int cap, int *n_spans, double *total_us);
+
+/*
+ * AllGather -> GEMM (see "Layouts").  Decomposed schedule: at step s rank r
+ * multiplies the shard it holds into rows of Y_r belonging to that shard
+ * (the slice update), while the same shard is copied to the next rank.
+ *   plan     from cm_ring_plan with op CM_OP_AG_GEMM
+ *   x, w, y  device pointers, 16-byte aligned
+ *   ws       device workspace of ws_bytes >= plan->ws_bytes (receive slots)
+ *   compute  the compute stream (hipStream_t passed as void*; NULL = default)
+ *   comm     array of plan->desc.n_comm comm streams (distinct, non-NULL)
+ *   trace    optional (NULL)
+ */
+cm_status cm_ag_gemm(const cm_plan *plan, const void *x, const void *w, void *y, void *ws,
+                     size_t ws_bytes, void *compute, void *const *comm, int n_comm,
+                     cm_trace *trace);
+
+/*
+ * GEMM -> ReduceScatter (see "Layouts").  CM_OP_GEMM_RS: at step s rank r
+ * adds its partial product for the bucket it holds into that bucket (fp32),
+ * then the bucket moves to the next rank; the owner adds its share last and
+ * writes Out_q.  CM_OP_GEMM_RS_PIPE: the output columns are split into c
+ * chunks; each chunk's full partial products are computed in one launch and
+ * reduce-scattered around the ring (copy + add) while the next chunk
+ * computes.  Arguments as for cm_ag_gemm; x holds H.
+ */
+cm_status cm_gemm_rs(const cm_plan *plan, const void *x, const void *w, void *y, void *ws,
+                     size_t ws_bytes, void *compute, void *const *comm, int n_comm,
+                     cm_trace *trace);
+
+const char *cm_status_string(cm_status s);
+/* Detail of the last failing call on this thread ("" if none). */
+const char *cm_last_error(void);
+/* Library version, "major.minor.patch". */
+const char *cm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* COLLMM_H */

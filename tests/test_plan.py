@@ -1,0 +1,176 @@
+"""Host logic: the ring planner's programs, simulated on the CPU.
+
+Every program the library would enqueue is executed here in program order on
+byte buffers (tests/ring_sim.py) with a happens-before race check, and its
+result is compared with the oracle exactly (small-integer inputs, so every
+fp32 sum is exact).  This covers, per the pages:
+  * decomposed == monolithic, for every schedule, direction, chunk count and
+    comm-stream count ("The idea" / "Why it works": linearity);
+  * ring completeness: every AllGather output row-slice is written exactly
+    once; every ReduceScatter bucket reaches its owner with all N
+    contributions exactly once (rank-tagged powers of two);
+  * ordering: no read before the producing copy or GEMM, no overwrite
+    before the consumers are done (Megatron page, section 5), and a program
+    with one dependency edge removed is caught;
+  * the hop volume equals that of a ring AllGather / ReduceScatter.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle
+from collective_matmul_decomposition_amd import _native as nat
+from collective_matmul_decomposition_amd import inputs as gen
+from ring_sim import Race, Sim, buffer_sizes
+
+
+def simulate(op, N, m, k, n, dir="uni", chunks=1, sched="decomposed", out="f32", n_comm=1, seed=0, dist="int",
+             data=None):
+    plan = nat.cm_ring_plan(op=op, n_ranks=N, m=m, k=k, n=n, dir=dir, chunks=chunks, sched=sched, out_dtype=out,
+                            n_comm=n_comm)
+    if data is None:
+        if op == "ag":
+            a, w = gen.ag_inputs(N, m, k, n, dist, seed)
+        else:
+            a, w = gen.rs_inputs(N, m, k, n, dist, seed)
+    else:
+        a, w = data
+    sizes = buffer_sizes(plan)
+    sim = Sim(plan, sizes, {nat.CM_BUF_X: a, nat.CM_BUF_W: w}).run()
+    return plan, sim, a, w
+
+
+def output(sim, plan):
+    d = plan.desc
+    y = sim.buf[nat.CM_BUF_Y]
+    if d.out_dtype == nat.CM_F32:
+        return y.view(np.float32).astype(np.float64)
+    return y.view(np.uint16)
+
+
+def expect(op, a, w, out):
+    ref = oracle.ag_gemm(a, w) if op == "ag" else oracle.gemm_rs(a, w)
+    return ref.reshape(-1) if out == "f32" else oracle.round_bf16(ref).reshape(-1)
+
+
+CASES = []
+for N in (1, 2, 3, 4, 5, 8):
+    for op, dir, sched, chunks in [("ag", "uni", "decomposed", 1), ("ag", "uni", "decomposed", 2),
+                                   ("ag", "bi", "decomposed", 1), ("ag", "bi", "decomposed", 4),
+                                   ("ag", "uni", "naive", 1),
+                                   ("rs", "uni", "decomposed", 1), ("rs", "uni", "decomposed", 2),
+                                   ("rs", "bi", "decomposed", 2), ("rs", "bi", "decomposed", 1),
+                                   ("rs_pipe", "uni", "decomposed", 2), ("rs_pipe", "uni", "decomposed", 4),
+                                   ("rs", "uni", "naive", 1)]:
+        for n_comm in sorted({1, 2, 3, N, 2 * N}):
+            CASES.append((op, N, dir, sched, chunks, n_comm))
+
+
+@pytest.mark.parametrize("op,N,dir,sched,chunks,n_comm", CASES)
+def test_program_matches_oracle_and_is_race_free(op, N, dir, sched, chunks, n_comm):
+    m = 4 * chunks if op == "ag" else 3
+    k = 64
+    n = 64 * chunks if op != "ag" else 64
+    for out in ("f32", "bf16"):
+        plan, sim, a, w = simulate(op, N, m, k, n, dir, chunks, sched, out, n_comm)
+        got = output(sim, plan)
+        assert np.array_equal(got, expect(op, a, w, out)), (op, N, dir, sched, chunks, n_comm, out)
+        # every output element is written exactly once
+        assert (sim.writes[nat.CM_BUF_Y] == 1).all()
+
+
+@pytest.mark.parametrize("op,dir,chunks", [("rs", "uni", 1), ("rs", "bi", 2), ("rs_pipe", "uni", 2),
+                                           ("rs", "uni", 4)])
+@pytest.mark.parametrize("N", [2, 3, 5, 8])
+def test_every_bucket_collects_every_rank_once(op, dir, chunks, N):
+    """H_r = 2^r everywhere and W_r = identity: Out_q must be 2^N - 1 (each rank once)."""
+    m, k = 2, 64 * chunks
+    n = k
+    h = np.stack([np.full((N * m, k), 2.0 ** r, np.float32) for r in range(N)])
+    w = np.stack([np.eye(k, dtype=np.float32)] * N)
+    plan, sim, _, _ = simulate(op, N, m, k, n, dir, chunks, "decomposed", "f32", N,
+                               data=(gen.f32_to_bf16_bits(h), gen.f32_to_bf16_bits(w)))
+    got = output(sim, plan).reshape(N, m, n)
+    assert (got == 2.0 ** N - 1).all()
+
+
+@pytest.mark.parametrize("dir", ["uni", "bi"])
+@pytest.mark.parametrize("N", [3, 4, 7, 8])
+def test_allgather_uses_every_shard_once(dir, N):
+    """Each Y_r row block c is written by exactly one job, and that job multiplied shard c."""
+    plan = nat.cm_ring_plan(op="ag", n_ranks=N, m=8, k=64, n=64, dir=dir, chunks=2, n_comm=2)
+    ops, jobs = nat.cm_plan_program(plan)
+    seen = {}
+    for o in ops:
+        if o.kind != nat.CM_OPK_GEMM:
+            continue
+        for j in jobs[o.first_job:o.first_job + o.n_jobs]:
+            key = (j.rank, j.index, o.chunk)
+            assert key not in seen
+            seen[key] = o.step
+            # the output rows are shard `index`'s rows of Y_rank
+            row = (j.c_off // (64 * 2)) - j.rank * N * 8
+            assert row == j.index * 8 + o.chunk * 4
+    assert len(seen) == N * N * 2
+    # compute steps: N (uni) or 1 + ceil((N-1)/2) (bi)
+    assert plan.n_steps == (N if dir == "uni" else 1 + (N - 1 + 1) // 2)
+    assert plan.arc_cw + plan.arc_ccw == N - 1
+
+
+@pytest.mark.parametrize("op", ["ag", "rs", "rs_pipe"])
+@pytest.mark.parametrize("dir", ["uni", "bi"])
+@pytest.mark.parametrize("N", [2, 4, 8])
+def test_hop_volume_is_the_ring_volume(op, dir, N):
+    """Total hop bytes = N (N - 1) shard (AG, bf16) or bucket (RS, fp32) sizes."""
+    m, k, n = 8, 128, 256
+    plan = nat.cm_ring_plan(op=op, n_ranks=N, m=m, k=k, n=n, dir=dir, chunks=2, n_comm=4)
+    ops, _ = nat.cm_plan_program(plan)
+    total = sum(o.bytes for o in ops if o.kind == nat.CM_OPK_COPY)
+    per = m * k * 2 if op == "ag" else m * n * 4
+    assert total == N * (N - 1) * per
+
+
+def _drop_op(sim, index):
+    sim.ops = sim.ops[:index] + sim.ops[index + 1:]
+    return sim
+
+
+@pytest.mark.parametrize("op,dir,chunks", [("ag", "uni", 1), ("ag", "bi", 2), ("rs", "uni", 2), ("rs", "bi", 2),
+                                           ("rs_pipe", "uni", 2), ("ag", "uni", 2)])
+def test_dropped_dependency_is_caught(op, dir, chunks):
+    """Negative control: removing any one wait that orders a hop against a GEMM makes a race."""
+    N, m, k = 4, 4 * chunks, 64
+    n = 64 * chunks
+    plan = nat.cm_ring_plan(op=op, n_ranks=N, m=m if op == "ag" else 3, k=k, n=n if op != "ag" else 64, dir=dir,
+                            chunks=chunks, n_comm=2)
+    sizes = buffer_sizes(plan)
+    if op == "ag":
+        a, w = gen.ag_inputs(N, plan.desc.m, k, plan.desc.n, "int", 0)
+    else:
+        a, w = gen.rs_inputs(N, plan.desc.m, k, plan.desc.n, "int", 0)
+    base = Sim(plan, sizes, {nat.CM_BUF_X: a, nat.CM_BUF_W: w})
+    waits = [i for i, o in enumerate(base.ops) if o.kind == nat.CM_OPK_WAIT and o.step >= 0]
+    assert waits
+    caught = 0
+    for i in waits:
+        sim = _drop_op(Sim(plan, sizes, {nat.CM_BUF_X: a, nat.CM_BUF_W: w}), i)
+        try:
+            sim.run()
+        except Race:
+            caught += 1
+    # every in-schedule wait is load-bearing
+    assert caught == len(waits), "%d of %d dropped waits went unnoticed" % (len(waits) - caught, len(waits))
+
+
+def test_entry_and_exit_edges_are_needed():
+    plan = nat.cm_ring_plan(op="ag", n_ranks=4, m=4, k=64, n=64, n_comm=2)
+    sizes = buffer_sizes(plan)
+    a, w = gen.ag_inputs(4, 4, 64, 64, "int", 0)
+    ops = Sim(plan, sizes).ops
+    exit_waits = [i for i, o in enumerate(ops) if o.kind == nat.CM_OPK_WAIT and o.step < 0 and o.stream == 0]
+    entry_waits = [i for i, o in enumerate(ops) if o.kind == nat.CM_OPK_WAIT and o.step < 0 and o.stream != 0]
+    for i in exit_waits + entry_waits:
+        sim = _drop_op(Sim(plan, sizes, {nat.CM_BUF_X: a, nat.CM_BUF_W: w}), i)
+        with pytest.raises(Race):
+            sim.run()
