@@ -1,0 +1,296 @@
+#!/usr/bin/env python3
+"""Benchmark of the decomposed AllGather->GEMM and GEMM->ReduceScatter on one MI355X.
+
+One step = the tensor-parallel MLP hot path of one layer on N virtual ranks:
+AllGather->GEMM (column-parallel fc1 over the gathered sequence shards)
+followed by GEMM->ReduceScatter (row-parallel fc2 back to sequence shards),
+both decomposed into per-shard partial GEMMs overlapped with SDMA ring hops.
+
+Prints ONE JSON line:
+  value        whole-step TFLOP/s (algorithmic FLOPs of both ops / wall time)
+  roofline     the dominant kernel (the batched step GEMM) against the bf16
+               dense MFMA peak, from HIP events around every launch of it on
+               the compute stream during the timed steps
+  overlap      decomposed time over max(GEMM time, hop time) and the fraction
+               of hop time hidden under GEMMs, per op, from the same events
+  cpu_baseline the CPU oracle timed on a bounded sample of the same workload
+
+Inputs are seeded synthetic tensors (activations N(0,1), weights
+N(0, 0.02^2), bf16) resident in HBM before the timed region.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+WORKLOADS = {
+    # Llama-3-8B MLP: d = 4096, ffn = 14336, 4096 tokens, N = 8 (f/N = 1792)
+    "llama3-8b-mlp": dict(N=8, T=4096, d=4096, f=14336),
+    # GPT-3 175B MLP: d = 12288, ffn = 49152, 2048 tokens, N = 8 (f/N = 6144)
+    "gpt3-175b-mlp": dict(N=8, T=2048, d=12288, f=49152),
+    # the tiny check: d = 256, ffn = 1024, 256 tokens, N = 4
+    "tiny": dict(N=4, T=256, d=256, f=1024),
+}
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBPS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def union_length(intervals):
+    total, end = 0.0, -1e300
+    for a, b in sorted(intervals):
+        if b <= end:
+            continue
+        total += b - max(a, end)
+        end = b
+    return total
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama3-8b-mlp", choices=sorted(WORKLOADS))
+    ap.add_argument("--dir", default="uni", choices=["uni", "bi"])
+    ap.add_argument("--rs-op", default="rs", choices=["rs", "rs_pipe"])
+    ap.add_argument("--chunks-ag", type=int, default=0)
+    ap.add_argument("--chunks-rs", type=int, default=0)
+    ap.add_argument("--n-comm", type=int, default=0, help="comm streams (0: N for uni, 2N for bi)")
+    ap.add_argument("--tile", default="0x0")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time per op")
+    ap.add_argument("--no-naive", action="store_true")
+    ap.add_argument("--no-trace", action="store_true", help="time without the per-launch events")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the N-rank tensor-parallel group is emulated as virtual ranks on a "
+              "single MI355X; --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from collective_matmul_decomposition_amd import _native as nat
+    from collective_matmul_decomposition_amd import buffers
+    from collective_matmul_decomposition_amd import inputs as gen
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    nat.lib()
+
+    wl = WORKLOADS[args.workload]
+    N, T, d, f = wl["N"], wl["T"], wl["d"], wl["f"]
+    m, fN = T // N, f // N
+    n_comm = args.n_comm or (N if args.dir == "uni" else 2 * N)
+    tile = tuple(int(v) for v in args.tile.split("x"))
+    plan_ag = nat.cm_ring_plan(op="ag", n_ranks=N, m=m, k=d, n=fN, dir=args.dir, chunks=args.chunks_ag,
+                               out_dtype="bf16", n_comm=n_comm, tile=tile)
+    plan_rs = nat.cm_ring_plan(op=args.rs_op, n_ranks=N, m=m, k=fN, n=d, dir=args.dir, chunks=args.chunks_rs,
+                               out_dtype="bf16", n_comm=n_comm, tile=tile)
+    log("plans: AG chunks=%d tile=%dx%d ws=%.0fMB | RS(%s) chunks=%d tile=%dx%d ws=%.0fMB | n_comm=%d" % (
+        plan_ag.chunks, plan_ag.tile_m, plan_ag.tile_n, plan_ag.ws_bytes / 1e6, args.rs_op, plan_rs.chunks,
+        plan_rs.tile_m, plan_rs.tile_n, plan_rs.ws_bytes / 1e6, n_comm))
+
+    x, w1 = gen.ag_inputs_torch(N, m, d, fN, "normal", 0, "cuda")
+    h, w2 = gen.rs_inputs_torch(N, m, fN, d, "normal", 0, "cuda")
+    y1, ws1 = buffers.alloc_outputs(plan_ag)
+    y2, ws2 = buffers.alloc_outputs(plan_rs)
+    buffers.check_inputs(plan_ag, x, w1, y1, ws1)
+    buffers.check_inputs(plan_rs, h, w2, y2, ws2)
+    compute = torch.cuda.Stream()
+    comm = buffers.comm_streams(n_comm)
+    flops_op = 2.0 * N * T * d * fN  # each op: N ranks x [T x d] . [d x f/N]
+    flops_step = 2 * flops_op
+
+    def step(tr_ag=None, tr_rs=None, pa=plan_ag, pr=plan_rs):
+        nat.cm_ag_gemm(pa, x, w1, y1, ws1, compute, comm, tr_ag)
+        nat.cm_gemm_rs(pr, h, w2, y2, ws2, compute, comm, tr_rs)
+
+    ops_ag, _ = nat.cm_plan_program(plan_ag)
+    ops_rs, _ = nat.cm_plan_program(plan_rs)
+    cap_ag = sum(1 for o in ops_ag if o.kind in (nat.CM_OPK_GEMM, nat.CM_OPK_COPY, nat.CM_OPK_REDUCE))
+    cap_rs = sum(1 for o in ops_rs if o.kind in (nat.CM_OPK_GEMM, nat.CM_OPK_COPY, nat.CM_OPK_REDUCE))
+    use_trace = not args.no_trace
+    traces = [(nat.Trace(cap_ag), nat.Trace(cap_rs)) for _ in range(args.steps)] if use_trace else None
+
+    with torch.cuda.stream(compute):
+        for _ in range(args.warmup):
+            step()
+    torch.cuda.synchronize()
+    log("warmup done")
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if use_trace:
+            step(*traces[i])
+        else:
+            step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    value = flops_step / (wall / args.steps) / 1e12
+    log("timed: %.3f ms/step, %.1f TFLOP/s" % (ms_per_step, value))
+
+    # ---------------------------------------------------- per-launch event times
+    result_extra = {}
+    roofline = None
+    if use_trace:
+        gemm_stats = {}  # (op, rows, cols, depth, jobs, tile) -> [durations]
+        per_op = {"ag": [], "rs": []}
+
+        def launch_key(ops, name):
+            keys = []
+            for o in ops:
+                if o.kind == nat.CM_OPK_GEMM:
+                    keys.append((name, o.rows, o.cols, o.depth, o.n_jobs, o.tile_m, o.tile_n))
+            return keys
+
+        keys = {"ag": launch_key(ops_ag, "ag"), "rs": launch_key(ops_rs, "rs")}
+        for tr_ag, tr_rs in traces:
+            for name, tr in (("ag", tr_ag), ("rs", tr_rs)):
+                spans, total = tr.read()
+                g = [s for s in spans if s[0] == nat.CM_OPK_GEMM]
+                assert len(g) == len(keys[name])
+                for key, s in zip(keys[name], g):
+                    gemm_stats.setdefault(key, []).append(s[5] - s[4])
+                G = sum(s[5] - s[4] for s in g)
+                C = union_length([(s[4], s[5]) for s in spans if s[0] in (nat.CM_OPK_COPY, nat.CM_OPK_REDUCE)])
+                per_op[name].append((total, G, C))
+        # the dominant kernel: the launch shape with the most total time
+        best = max(gemm_stats.items(), key=lambda kv: sum(kv[1]))
+        (name, rows, cols, depth, jobs, tm, tn), durs = best
+        flops_launch = 2.0 * rows * cols * depth * jobs
+        avg_us = float(np.mean(durs))
+        achieved = flops_launch / (avg_us * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "kernel": "gemm_jobs_kernel<%d,%d> (%s step: %d jobs of [%dx%d].[%dx%d]^T)" % (
+                        tm, tn, name.upper(), jobs, rows, depth, cols, depth),
+                    "avg_launch_us": round(avg_us, 2), "launches": len(durs),
+                    "flops_per_launch": flops_launch}
+        all_launch = {}
+        for (nm, r, c, dd, j, a, b), dl in gemm_stats.items():
+            all_launch["%s %dx%dx%d x%d tile %dx%d" % (nm, r, c, dd, j, a, b)] = {
+                "avg_us": round(float(np.mean(dl)), 2), "count": len(dl),
+                "tflops": round(2.0 * r * c * dd * j / (np.mean(dl) * 1e-6) / 1e12, 1)}
+        result_extra["gemm_launches"] = all_launch
+        ov = {}
+        for name in ("ag", "rs"):
+            arr = np.array(per_op[name])
+            D, G, C = np.median(arr[:, 0]), np.median(arr[:, 1]), np.median(arr[:, 2])
+            ov[name] = {"decomposed_us": round(D, 1), "gemm_busy_us": round(G, 1), "hop_busy_us": round(C, 1),
+                        "overlap_efficiency": round(D / max(G, C), 3),
+                        "hidden_fraction": round((G + C - D) / C, 3) if C > 0 else None,
+                        "tflops": round(flops_op / (D * 1e-6) / 1e12, 1)}
+        plan_for = {"ag": plan_ag, "rs": plan_rs}
+        for name in ("ag", "rs"):
+            p = plan_for[name]
+            elt = 2 if name == "ag" else 4
+            ring_bytes = N * (N - 1) * m * (d if name == "ag" else d) * elt
+            ov[name]["ring_bytes"] = ring_bytes
+            ov[name]["hop_GBps"] = round(ring_bytes / (ov[name]["hop_busy_us"] * 1e-6) / 1e9, 1)
+            ov[name]["chunks"] = p.chunks
+        result_extra["overlap"] = ov
+
+    # -------------------------------------------------------- naive schedule
+    if not args.no_naive:
+        pa = nat.cm_ring_plan(op="ag", n_ranks=N, m=m, k=d, n=fN, sched="naive", out_dtype="bf16", n_comm=n_comm)
+        pr = nat.cm_ring_plan(op="rs", n_ranks=N, m=m, k=fN, n=d, sched="naive", out_dtype="bf16", n_comm=n_comm)
+        yn1, wsn1 = buffers.alloc_outputs(pa)
+        yn2, wsn2 = buffers.alloc_outputs(pr)
+        def naive_step():
+            nat.cm_ag_gemm(pa, x, w1, yn1, wsn1, compute, comm)
+            nat.cm_gemm_rs(pr, h, w2, yn2, wsn2, compute, comm)
+        for _ in range(2):
+            naive_step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ns = max(3, args.steps // 2)
+        for _ in range(ns):
+            naive_step()
+        torch.cuda.synchronize()
+        nwall = (time.perf_counter() - t0) / ns
+        result_extra["naive"] = {"ms_per_step": round(nwall * 1e3, 3),
+                                 "tflops": round(flops_step / nwall / 1e12, 1),
+                                 "speedup_of_decomposed": round(nwall * 1e3 / ms_per_step, 3)}
+        del yn1, wsn1, yn2, wsn2
+
+    # -------------------------------------------------- sampled parity check
+    import oracle
+    xa, w1a = gen.torch_bf16_to_bits(x), gen.torch_bf16_to_bits(w1)
+    ha, w2a = gen.torch_bf16_to_bits(h), gen.torch_bf16_to_bits(w2)
+    rng = np.random.default_rng(0)
+    rk, rw = rng.integers(0, N, 4), rng.integers(0, T, 4)
+    ref, mag = oracle.ag_gemm_rows(xa, w1a, rk, rw, with_mag=True)
+    got = gen.bf16_bits_to_f32(gen.torch_bf16_to_bits(y1)[rk, rw]).astype(np.float64)
+    worst_ag = float((np.abs(got - ref) / (1e-5 * mag + 2.0 ** -8 * np.abs(ref))).max())
+    qo, qr = rng.integers(0, N, 4), rng.integers(0, m, 4)
+    ref, mag = oracle.gemm_rs_rows(ha, w2a, qo, qr, with_mag=True)
+    got = gen.bf16_bits_to_f32(gen.torch_bf16_to_bits(y2)[qo, qr]).astype(np.float64)
+    worst_rs = float((np.abs(got - ref) / (1e-5 * mag + 2.0 ** -8 * np.abs(ref))).max())
+    result_extra["parity_sampled_err_over_bound"] = {"ag": round(worst_ag, 4), "rs": round(worst_rs, 4)}
+
+    # ------------------------------------------------------------ cpu baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        cores = oracle.threads()
+        # calibrate on a few rows, then time about cpu_seconds per op
+        t0 = time.perf_counter()
+        oracle.ag_gemm_rows(xa, w1a, np.zeros(cores, np.int32), np.arange(cores, dtype=np.int32))
+        per_row = (time.perf_counter() - t0) / cores
+        rows_ag = int(max(cores, min(N * T, args.cpu_seconds / max(per_row, 1e-9))))
+        sel = rng.choice(N * T, rows_ag, replace=False)
+        t0 = time.perf_counter()
+        oracle.ag_gemm_rows(xa, w1a, (sel // T).astype(np.int32), (sel % T).astype(np.int32))
+        t_ag = time.perf_counter() - t0
+        # RS rows: each output row sums N ranks' partial rows
+        rows_rs = max(cores, rows_ag // N)
+        sel = rng.choice(N * m, min(rows_rs, N * m), replace=False)
+        t0 = time.perf_counter()
+        oracle.gemm_rs_rows(ha, w2a, (sel // m).astype(np.int32), (sel % m).astype(np.int32))
+        t_rs = time.perf_counter() - t0
+        fl = 2.0 * rows_ag * d * fN + 2.0 * len(sel) * N * fN * d
+        cpu = {"value": round(fl / (t_ag + t_rs) / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+               "sample": "%d of %d AG output rows and %d of %d RS output rows of the same step, fp64, %.1f s" % (
+                   rows_ag, N * T, len(sel), N * m, t_ag + t_rs)}
+
+    out = {
+        "metric": "AG-GEMM / GEMM-RS TFLOP/s + % bf16 MFMA peak + overlap efficiency, 1 GPU",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "virtual_ranks": N, "tokens": T, "hidden": d, "ffn": f,
+                   "ffn_per_rank": fN, "ring": args.dir, "rs_variant": args.rs_op, "n_comm_streams": n_comm,
+                   "chunks_ag": plan_ag.chunks, "chunks_rs": plan_rs.chunks,
+                   "step": "AllGather->GEMM (fc1) then GEMM->ReduceScatter (fc2), decomposed, bf16 in / fp32 "
+                           "accumulate / bf16 out"},
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    out.update(result_extra)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -29,7 +29,8 @@ class cm_plan_desc(ctypes.Structure):
     _fields_ = [("op", ctypes.c_int), ("n_ranks", ctypes.c_int), ("m", ctypes.c_int), ("k", ctypes.c_int),
                 ("n", ctypes.c_int), ("dir", ctypes.c_int), ("chunks", ctypes.c_int), ("sched", ctypes.c_int),
                 ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int), ("n_comm", ctypes.c_int),
-                ("copy_gbps", ctypes.c_double), ("mfma_tflops", ctypes.c_double), ("launch_us", ctypes.c_double)]
+                ("tile_m", ctypes.c_int), ("tile_n", ctypes.c_int), ("copy_gbps", ctypes.c_double),
+                ("mfma_tflops", ctypes.c_double), ("launch_us", ctypes.c_double)]
 
 
 class cm_plan(ctypes.Structure):
@@ -132,13 +133,14 @@ _ENUMS = {
 
 
 def make_desc(op, n_ranks, m, k, n, dir="uni", chunks=0, sched="decomposed", out_dtype="bf16", n_comm=1,
-              copy_gbps=0.0, mfma_tflops=0.0, launch_us=0.0):
+              tile=(0, 0), copy_gbps=0.0, mfma_tflops=0.0, launch_us=0.0):
     """A cm_plan_desc from keyword arguments (strings or enum values)."""
     def e(kind, v):
         return _ENUMS[kind][v] if isinstance(v, str) else int(v)
     return cm_plan_desc(op=e("op", op), n_ranks=n_ranks, m=m, k=k, n=n, dir=e("dir", dir), chunks=chunks,
                         sched=e("sched", sched), in_dtype=CM_BF16, out_dtype=e("dtype", out_dtype),
-                        n_comm=n_comm, copy_gbps=copy_gbps, mfma_tflops=mfma_tflops, launch_us=launch_us)
+                        n_comm=n_comm, tile_m=tile[0], tile_n=tile[1], copy_gbps=copy_gbps,
+                        mfma_tflops=mfma_tflops, launch_us=launch_us)
 
 
 def cm_ring_plan(desc=None, **kw):

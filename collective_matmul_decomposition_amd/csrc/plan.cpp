@@ -71,6 +71,12 @@ constexpr TileCand kTiles[] = {
 };
 constexpr int kCUs = 256;
 
+bool tile_known(int tm, int tn) {
+  for (const TileCand &t : kTiles)
+    if (t.tm == tm && t.tn == tn) return true;
+  return false;
+}
+
 void choose_tile(int rows, int cols, int jobs, int *tm, int *tn) {
   double best = -1;
   for (const TileCand &t : kTiles) {
@@ -143,6 +149,10 @@ cm_status validate_desc(const cm_plan_desc &d) {
   if (d.k % 64 || d.n % 64) { set_error("k (%d) and n (%d) must be multiples of 64", d.k, d.n); return CM_ERR_SHAPE; }
   if ((long long)d.n_ranks * d.m > (1 << 24)) { set_error("N*m too large"); return CM_ERR_SHAPE; }
   if (d.copy_gbps < 0 || d.mfma_tflops < 0 || d.launch_us < 0) { set_error("cost-model inputs must be >= 0"); return CM_ERR_INVALID_ARG; }
+  if ((d.tile_m || d.tile_n) && !tile_known(d.tile_m, d.tile_n)) {
+    set_error("no GEMM tile %dx%d (choose 256x256, 256x128, 128x256, 128x128, 64x256, 64x128 or 0x0)", d.tile_m, d.tile_n);
+    return CM_ERR_UNSUPPORTED;
+  }
   return CM_OK;
 }
 
@@ -276,7 +286,8 @@ cm_status plan(const cm_plan_desc *desc, cm_plan *out) {
   p.declined = (N > 1 && !e.hidden) ? 1 : 0;
   int rows = d.op == CM_OP_AG_GEMM ? d.m / c : d.m;
   int cols = d.op == CM_OP_AG_GEMM ? d.n : d.n / c;
-  choose_tile(rows, cols, N * (bi ? 2 : 1), &p.tile_m, &p.tile_n);
+  if (d.tile_m) { p.tile_m = d.tile_m; p.tile_n = d.tile_n; }
+  else choose_tile(rows, cols, N * (bi ? 2 : 1), &p.tile_m, &p.tile_n);
   p.ws_bytes = ws_layout(p).total;
 
   Program prog;
@@ -369,7 +380,8 @@ struct Builder {
     o.first_job = (int)prog.jobs.size();
     o.n_jobs = (int)jobs.size();
     o.rows = rows; o.cols = cols; o.depth = depth;
-    choose_tile(rows, cols, (int)jobs.size(), &o.tile_m, &o.tile_n);
+    if (d.tile_m) { o.tile_m = d.tile_m; o.tile_n = d.tile_n; }
+    else choose_tile(rows, cols, (int)jobs.size(), &o.tile_m, &o.tile_n);
     prog.jobs.insert(prog.jobs.end(), jobs.begin(), jobs.end());
     prog.ops.push_back(o);
     tick(0);

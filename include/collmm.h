@@ -108,6 +108,8 @@ typedef struct {
   int in_dtype;  /* CM_BF16 */
   int out_dtype; /* CM_F32 or CM_BF16 */
   int n_comm;    /* number of comm streams the calls will pass, 1..CM_MAX_COMM */
+  int tile_m;    /* GEMM block tile rows: 0 = choose per launch, else 64, 128 or 256 */
+  int tile_n;    /* GEMM block tile columns: 0 = choose, else 128 or 256 (with tile_m) */
   /* Cost-model inputs (0 = built-in defaults for MI355X). */
   double copy_gbps;      /* sustained hop bandwidth of ONE comm stream, GB/s */
   double mfma_tflops;    /* sustained bf16 GEMM rate, TFLOP/s */

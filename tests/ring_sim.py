@@ -227,3 +227,34 @@ def buffer_sizes(plan):
     if d.op == nat.CM_OP_AG_GEMM:
         return [N * m * k * 2, N * n * k * 2, N * T * n * osz, plan.ws_bytes]
     return [N * T * k * 2, N * n * k * 2, N * m * n * osz, plan.ws_bytes]
+
+
+def check_program_bounds(plan, sizes=None):
+    """Every access of the program stays inside the documented buffers (no execution)."""
+    sizes = sizes or buffer_sizes(plan)
+    ops, jobs = nat.cm_plan_program(plan)
+
+    def span(b, off, rows, ld_bytes, row_bytes):
+        assert 0 <= b < 4, b
+        end = off + (rows - 1) * ld_bytes + row_bytes
+        assert off >= 0 and end <= sizes[b], "buffer %d: [%d, %d) outside %d" % (b, off, end, sizes[b])
+        assert off % 16 == 0 and ld_bytes % 16 == 0, "unaligned access"
+
+    for o in ops:
+        if o.kind == nat.CM_OPK_COPY:
+            span(o.src_buf, o.src_off, 1, 0, o.bytes)
+            span(o.dst_buf, o.dst_off, 1, 0, o.bytes)
+        elif o.kind in (nat.CM_OPK_GEMM, nat.CM_OPK_REDUCE):
+            assert 1 <= o.n_jobs <= 128
+            for j in jobs[o.first_job:o.first_job + o.n_jobs]:
+                if o.kind == nat.CM_OPK_GEMM:
+                    assert o.depth % 64 == 0
+                    span(j.a_buf, j.a_off, o.rows, j.lda * 2, o.depth * 2)
+                    span(j.b_buf, j.b_off, o.cols, j.ldb * 2, o.depth * 2)
+                for ib, io in ((j.in0_buf, j.in0_off), (j.in1_buf, j.in1_off)):
+                    if ib >= 0:
+                        assert ib == nat.CM_BUF_WS
+                        span(ib, io, o.rows, j.ld_in * 4, o.cols * 4)
+                esz = 4 if j.c_dtype == nat.CM_F32 else 2
+                span(j.c_buf, j.c_off, o.rows, j.ldc * esz, o.cols * esz)
+    return len(ops)

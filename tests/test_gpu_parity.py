@@ -1,0 +1,235 @@
+"""GPU parity: libcollmm (through its C ABI) against the CPU oracle.
+
+Bar (the decomposition is exact by linearity, "Why it works" on the
+decomposition page):
+  * small-integer inputs: fp32 outputs equal the oracle bit for bit (every
+    partial sum is an integer below 2^24, exact in fp32 in any order); bf16
+    outputs equal the oracle rounded to nearest-even bf16;
+  * bf16 N(0,1) / N(0, 0.02^2) inputs: |gpu - oracle| <= 1e-5 * S, where
+    S = sum_k |a_ik * b_kj| over the full contraction, plus 2^-8 |oracle| for
+    bf16 outputs;
+  * repeated runs are bitwise identical (no atomics).
+Shapes span several tiles with ragged tails, every schedule (uni / bi ring,
+naive, pipeline chunks), several chunk and comm-stream counts, N = 1 and
+N = 2 degenerate rings, and the full-size Llama-3-8B and GPT-3 MLP shapes on
+sampled rows.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from collective_matmul_decomposition_amd import _native as nat
+from collective_matmul_decomposition_amd import buffers
+from collective_matmul_decomposition_amd import inputs as gen
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    nat.lib()  # fail loudly if the library is missing
+    yield
+
+
+def run_case(op, N, m, k, n, dist="int", out="f32", dir="uni", chunks=1, sched="decomposed", n_comm=1, seed=0,
+             repeat=1, tile=(0, 0)):
+    plan = nat.cm_ring_plan(op=op, n_ranks=N, m=m, k=k, n=n, dir=dir, chunks=chunks, sched=sched, out_dtype=out,
+                            n_comm=n_comm, tile=tile)
+    if op == "ag":
+        a, w = gen.ag_inputs(N, m, k, n, dist, seed)
+    else:
+        a, w = gen.rs_inputs(N, m, k, n, dist, seed)
+    x_t, w_t = gen.to_torch_bf16(a, "cuda"), gen.to_torch_bf16(w, "cuda")
+    y, ws = buffers.alloc_outputs(plan)
+    comm = buffers.comm_streams(n_comm)
+    results = []
+    for _ in range(repeat):
+        say("  launch %s N=%d m=%d k=%d n=%d %s out=%s dir=%s c=%d(%d) sched=%s n_comm=%d tile=%dx%d" %
+            (op, N, m, k, n, dist, out, dir, chunks, plan.chunks, sched, n_comm, plan.tile_m, plan.tile_n))
+        y.fill_(float("nan")) if out == "f32" else y.fill_(float("nan"))
+        buffers.run(plan, x_t, w_t, y, ws, comm=comm)
+        torch.cuda.synchronize()
+        results.append(y.detach().clone())
+    return plan, a, w, results
+
+
+def check(op, a, w, y, out, dist):
+    ref, mag = (oracle.ag_gemm if op == "ag" else oracle.gemm_rs)(a, w, with_mag=True)
+    if out == "f32":
+        got = y.float().cpu().numpy().astype(np.float64)
+        if dist == "int":
+            assert np.array_equal(got, ref), "max |err| %g" % np.abs(got - ref).max()
+        else:
+            err = np.abs(got - ref)
+            bound = 1e-5 * mag
+            assert (err <= bound).all(), "worst err/bound %g" % (err / np.maximum(bound, 1e-300)).max()
+    else:
+        bits = gen.torch_bf16_to_bits(y)
+        if dist == "int":
+            assert np.array_equal(bits, oracle.round_bf16(ref))
+        else:
+            got = gen.bf16_bits_to_f32(bits).astype(np.float64)
+            err = np.abs(got - ref)
+            bound = 1e-5 * mag + 2.0 ** -8 * np.abs(ref)
+            assert (err <= bound).all(), "worst err/bound %g" % (err / np.maximum(bound, 1e-300)).max()
+
+
+# the tiny configuration: N = 4, 256 tokens (64-row shards), d = 256, ffn 1024 (f/N = 256)
+TINY = []
+for op in ("ag", "rs", "rs_pipe"):
+    for dir, sched, chunks in (("uni", "decomposed", 1), ("uni", "decomposed", 2), ("bi", "decomposed", 1),
+                               ("bi", "decomposed", 2), ("uni", "naive", 1)):
+        if op == "rs_pipe" and (dir == "bi" or sched == "naive"):
+            continue
+        for dist in ("int", "normal"):
+            for out in ("f32", "bf16"):
+                TINY.append((op, dir, sched, chunks, dist, out))
+
+
+@pytest.mark.parametrize("op,dir,sched,chunks,dist,out", TINY)
+def test_tiny_config(op, dir, sched, chunks, dist, out):
+    say("tiny", op, dir, sched, chunks, dist, out)
+    _, a, w, (y,) = run_case(op, 4, 64, 256, 256, dist, out, dir, chunks, sched, n_comm=4)
+    check(op, a, w, y, out, dist)
+
+
+RAGGED = [
+    # op, N, m, k, n, dir, chunks, n_comm
+    ("ag", 3, 40, 192, 320, "uni", 2, 2),
+    ("ag", 5, 100, 128, 448, "bi", 1, 3),
+    ("ag", 1, 70, 64, 64, "uni", 1, 1),
+    ("ag", 2, 33, 320, 960, "bi", 1, 2),
+    ("rs", 3, 37, 192, 320, "uni", 5, 2),
+    ("rs", 5, 21, 128, 448, "bi", 7, 4),
+    ("rs", 1, 50, 64, 128, "uni", 2, 1),
+    ("rs", 2, 19, 256, 640, "uni", 2, 2),
+    ("rs_pipe", 3, 29, 192, 384, "uni", 3, 3),
+    ("rs_pipe", 6, 17, 64, 256, "uni", 4, 6),
+    ("rs_pipe", 1, 30, 128, 128, "uni", 2, 1),
+]
+
+
+@pytest.mark.parametrize("op,N,m,k,n,dir,chunks,n_comm", RAGGED)
+def test_ragged_shapes(op, N, m, k, n, dir, chunks, n_comm):
+    say("ragged", op, N, m, k, n, dir, chunks, n_comm)
+    for dist, out in (("int", "f32"), ("normal", "bf16")):
+        _, a, w, (y,) = run_case(op, N, m, k, n, dist, out, dir, chunks, "decomposed", n_comm)
+        check(op, a, w, y, out, dist)
+
+
+MID = [("ag", "uni", 1), ("ag", "bi", 2), ("rs", "uni", 2), ("rs", "bi", 4), ("rs_pipe", "uni", 4)]
+
+
+@pytest.mark.parametrize("op,dir,chunks", MID)
+def test_mid_size_eight_ranks(op, dir, chunks):
+    """N = 8, 2048 tokens, several 256x256 tiles per rank and step."""
+    N, m = 8, 256
+    k, n = (1024, 768) if op == "ag" else (768, 1024)
+    say("mid", op, dir, chunks)
+    _, a, w, (y,) = run_case(op, N, m, k, n, "int", "f32", dir, chunks, "decomposed", n_comm=8)
+    check(op, a, w, y, "f32", "int")
+
+
+TILES = [(256, 256), (256, 128), (128, 256), (128, 128), (64, 256), (64, 128)]
+
+
+@pytest.mark.parametrize("tile", TILES, ids=lambda t: "%dx%d" % t)
+@pytest.mark.parametrize("op", ["ag", "rs"])
+def test_every_tile_variant(tile, op):
+    """Each compiled block tile, forced, on a shape with ragged rows and columns."""
+    N, m, k = 3, 300, 192
+    n = 320 if op == "ag" else 640
+    say("tile", tile, op)
+    for dist, out in (("int", "f32"), ("normal", "bf16")):
+        _, a, w, (y,) = run_case(op, N, m, k, n, dist, out, "uni", 1 if op == "ag" else 2, "decomposed", 2,
+                                 tile=tile)
+        check(op, a, w, y, out, dist)
+
+
+@pytest.mark.parametrize("op", ["ag", "rs", "rs_pipe"])
+def test_repeatable_bitwise(op):
+    say("repeat", op)
+    n = 512 if op != "ag" else 384
+    _, _, _, ys = run_case(op, 4, 128, 512, n, "normal", "f32", "uni", 2, "decomposed", 4, repeat=3)
+    for y in ys[1:]:
+        assert torch.equal(y, ys[0])
+
+
+def test_bi_equals_uni_on_integers():
+    for op in ("ag", "rs"):
+        say("bi==uni", op)
+        _, _, _, (yu,) = run_case(op, 7, 64, 256, 256, "int", "f32", "uni", 2, "decomposed", 7)
+        _, _, _, (yb,) = run_case(op, 7, 64, 256, 256, "int", "f32", "bi", 2, "decomposed", 14)
+        assert torch.equal(yu, yb)
+
+
+def test_trace_spans():
+    """The timing trace records every GEMM launch and hop with ordered times."""
+    plan = nat.cm_ring_plan(op="ag", n_ranks=4, m=64, k=256, n=256, n_comm=4)
+    a, w = gen.ag_inputs(4, 64, 256, 256, "int", 0)
+    x_t, w_t = gen.to_torch_bf16(a, "cuda"), gen.to_torch_bf16(w, "cuda")
+    y, ws = buffers.alloc_outputs(plan)
+    tr = nat.Trace(256)
+    say("trace")
+    buffers.run(plan, x_t, w_t, y, ws, trace=tr)
+    torch.cuda.synchronize()
+    spans, total = tr.read()
+    kinds = [s[0] for s in spans]
+    assert kinds.count(nat.CM_OPK_GEMM) == 4
+    assert kinds.count(nat.CM_OPK_COPY) >= 3
+    assert all(s[5] >= s[4] >= 0 for s in spans) and total > 0
+    tr.close()
+    check("ag", a, w, y, "bf16", "int")
+
+
+FULL = [
+    # Llama-3-8B MLP: N = 8, 4096 tokens, d = 4096, ffn 14336 (f/N = 1792)
+    ("ag", 8, 512, 4096, 1792, "uni"),
+    ("rs", 8, 512, 1792, 4096, "uni"),
+    ("rs_pipe", 8, 512, 1792, 4096, "uni"),
+    # GPT-3 175B MLP: N = 8, 2048 tokens, d = 12288, ffn 49152 (f/N = 6144)
+    ("ag", 8, 256, 12288, 6144, "uni"),
+    ("ag", 8, 256, 12288, 6144, "bi"),
+    ("rs", 8, 256, 6144, 12288, "uni"),
+    ("rs", 8, 256, 6144, 12288, "bi"),
+]
+
+
+@pytest.mark.parametrize("op,N,m,k,n,dir", FULL)
+def test_full_size_sampled(op, N, m, k, n, dir):
+    """Full-size shapes in the benchmark's launch configuration; sampled rows against the oracle."""
+    n_comm = 8 if dir == "uni" else 16
+    plan = nat.cm_ring_plan(op=op, n_ranks=N, m=m, k=k, n=n, dir=dir, out_dtype="bf16", n_comm=n_comm)
+    mk = gen.ag_inputs_torch if op == "ag" else gen.rs_inputs_torch
+    x_t, w_t = mk(N, m, k, n, "normal", 0, "cuda")
+    y, ws = buffers.alloc_outputs(plan)
+    say("full", op, N, m, k, n, dir, "chunks", plan.chunks, "tile", plan.tile_m, plan.tile_n)
+    buffers.run(plan, x_t, w_t, y, ws)
+    torch.cuda.synchronize()
+    a, w = gen.torch_bf16_to_bits(x_t), gen.torch_bf16_to_bits(w_t)
+    rng = np.random.default_rng(1)
+    yb = gen.torch_bf16_to_bits(y)
+    if op == "ag":
+        ranks = rng.integers(0, N, 12)
+        rows = rng.integers(0, N * m, 12)
+        ref, mag = oracle.ag_gemm_rows(a, w, ranks, rows, with_mag=True)
+        got = gen.bf16_bits_to_f32(yb[ranks, rows]).astype(np.float64)
+    else:
+        owners = rng.integers(0, N, 8)
+        rows = rng.integers(0, m, 8)
+        ref, mag = oracle.gemm_rs_rows(a, w, owners, rows, with_mag=True)
+        got = gen.bf16_bits_to_f32(yb[owners, rows]).astype(np.float64)
+    err = np.abs(got - ref)
+    bound = 1e-5 * mag + 2.0 ** -8 * np.abs(ref)
+    assert (err <= bound).all(), "worst err/bound %g" % (err / bound).max()

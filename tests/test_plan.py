@@ -174,3 +174,33 @@ def test_entry_and_exit_edges_are_needed():
         sim = _drop_op(Sim(plan, sizes, {nat.CM_BUF_X: a, nat.CM_BUF_W: w}), i)
         with pytest.raises(Race):
             sim.run()
+
+
+def _gpu_cases():
+    import test_gpu_parity as g
+    cases = []
+    for op, dir, sched, chunks, dist, out in g.TINY:
+        cases.append(dict(op=op, n_ranks=4, m=64, k=256, n=256, dir=dir, chunks=chunks, sched=sched, out_dtype=out,
+                          n_comm=4))
+    for op, N, m, k, n, dir, chunks, n_comm in g.RAGGED:
+        for out in ("f32", "bf16"):
+            cases.append(dict(op=op, n_ranks=N, m=m, k=k, n=n, dir=dir, chunks=chunks, out_dtype=out, n_comm=n_comm))
+    for op, dir, chunks in g.MID:
+        k, n = (1024, 768) if op == "ag" else (768, 1024)
+        cases.append(dict(op=op, n_ranks=8, m=256, k=k, n=n, dir=dir, chunks=chunks, out_dtype="f32", n_comm=8))
+    for op, N, m, k, n, dir in g.FULL:
+        cases.append(dict(op=op, n_ranks=N, m=m, k=k, n=n, dir=dir, out_dtype="bf16", n_comm=8 if dir == "uni" else 16))
+    for tile in g.TILES:
+        for op in ("ag", "rs"):
+            for out in ("f32", "bf16"):
+                cases.append(dict(op=op, n_ranks=3, m=300, k=192, n=320 if op == "ag" else 640, n_comm=2,
+                                  chunks=1 if op == "ag" else 2, out_dtype=out, tile=tile))
+    return cases
+
+
+def test_gpu_test_programs_stay_in_bounds():
+    """Every program the GPU tests launch is checked on the CPU first: in-bounds, aligned, <= 128 jobs."""
+    from ring_sim import check_program_bounds
+    for kw in _gpu_cases():
+        plan = nat.cm_ring_plan(**kw)
+        check_program_bounds(plan)
