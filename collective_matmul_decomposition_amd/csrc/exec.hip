@@ -11,6 +11,7 @@
 // a budget") are the copy enqueue and the event the compute stream waits on.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdio>
 #include <cstring>
 #include <memory>
@@ -52,9 +53,9 @@ std::string plan_key(const cm_plan &p) {
   // Every field the program depends on (struct padding is not part of it).
   const cm_plan_desc &d = p.desc;
   char buf[512];
-  std::snprintf(buf, sizeof buf, "%d %d %d %d %d %d %d %d %d %d %d %d %d %a %a %a|%d %d %d %d %d %d %d %zu", d.op,
-                d.n_ranks, d.m, d.k, d.n, d.dir, d.chunks, d.sched, d.in_dtype, d.out_dtype, d.n_comm, d.tile_m,
-                d.tile_n, d.copy_gbps, d.mfma_tflops,
+  std::snprintf(buf, sizeof buf, "%d %d %d %d %d %d %d %d %d %d %d %d %d %d %a %a %a|%d %d %d %d %d %d %d %zu",
+                d.op, d.n_ranks, d.m, d.k, d.n, d.dir, d.chunks, d.sched, d.in_dtype, d.out_dtype, d.n_comm, d.tile_m,
+                d.tile_n, d.exec_mode, d.copy_gbps, d.mfma_tflops,
                 d.launch_us, p.chunks, p.n_steps, p.arc_cw, p.arc_ccw, p.tile_m, p.tile_n, p.n_events, p.ws_bytes);
   return buf;
 }
@@ -149,7 +150,21 @@ cm_status fill_params(const cm_op_rec &o, const cm_job_rec *jobs, Launch &L) {
   return CM_OK;
 }
 
+struct GraphEntry {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  std::vector<cm_span> spans;  // trace metadata captured with the graph
+  bool overflow = false;
+  ~GraphEntry() {
+    if (exec) (void)hipGraphExecDestroy(exec);
+    if (graph) (void)hipGraphDestroy(graph);
+  }
+};
+
+constexpr size_t kMaxGraphs = 64;
+
 struct ThreadState {
+  std::unordered_map<std::string, std::unique_ptr<GraphEntry>> graphs;
   std::unordered_map<std::string, std::unique_ptr<Compiled>> programs;
   std::unordered_map<int, std::vector<hipEvent_t>> events;  // per device
   std::unordered_map<int, int> arch_ok;                     // per device: 1 ok, 0 not gfx950
@@ -269,25 +284,10 @@ cm_status validate_call(const cm_plan *pl, bool want_ag, const void *x, const vo
   return CM_OK;
 }
 
-cm_status run(const cm_plan *pl, bool want_ag, const void *x, const void *w, void *y, void *ws, size_t ws_bytes,
-              void *compute, void *const *comm, int n_comm, cm_trace *trace) {
-  cm_status st = validate_call(pl, want_ag, x, w, y, ws, ws_bytes, compute, comm, n_comm);
-  if (st != CM_OK) return st;
-  int dev;
-  if ((st = check_device(&dev)) != CM_OK) return st;
-  if (trace && trace->device != dev) { set_error("trace was created on another device"); return CM_ERR_INVALID_ARG; }
-  const Compiled *cp;
-  if ((st = get_compiled(*pl, &cp)) != CM_OK) return st;
-  std::vector<hipEvent_t> *evp;
-  if ((st = event_pool(dev, cp->prog.n_events, &evp)) != CM_OK) return st;
-  const std::vector<hipEvent_t> &ev = *evp;
-
-  char *base[4] = {const_cast<char *>(static_cast<const char *>(x)), const_cast<char *>(static_cast<const char *>(w)),
-                   static_cast<char *>(y), static_cast<char *>(ws)};
-  hipStream_t streams[CM_MAX_COMM + 1];
-  streams[0] = static_cast<hipStream_t>(compute);
-  for (int i = 0; i < n_comm; ++i) streams[i + 1] = static_cast<hipStream_t>(comm[i]);
-
+// Enqueue the program's operations on the streams (eagerly, or into a
+// graph when the compute stream is capturing).
+cm_status enqueue(const Compiled *cp, const std::vector<hipEvent_t> &ev, char *const base[4],
+                  const hipStream_t *streams, cm_trace *trace) {
   hipError_t e;
   if (trace) {
     trace->used = 0;
@@ -354,7 +354,170 @@ cm_status run(const cm_plan *pl, bool want_ag, const void *x, const void *w, voi
   return CM_OK;
 }
 
+// Build the program as an explicit HIP graph.  Nodes are the launches and
+// copies; edges are exactly the program's happens-before: each node follows
+// the previous node of its stream, and a wait adds every node the waited
+// event's record followed.  (Record and wait are not nodes.)  Trace events,
+// when asked for, become event-record nodes around each op.
+cm_status build_graph(const Compiled *cp, char *const base[4], int n_streams, cm_trace *trace, GraphEntry *g) {
+  hipError_t e;
+  hipGraph_t graph;
+  if ((e = hipGraphCreate(&graph, 0)) != hipSuccess) return hip_fail(e, "hipGraphCreate");
+  g->graph = graph;
+  std::vector<std::vector<hipGraphNode_t>> frontier(n_streams);
+  std::vector<std::vector<hipGraphNode_t>> event_frontier(cp->prog.n_events);
+  auto add_after = [&](int s, hipGraphNode_t node) { frontier[s].assign(1, node); };
+  if (trace) {
+    trace->used = 0;
+    trace->overflow = false;
+    trace->spans.clear();
+    hipGraphNode_t n;
+    if ((e = hipGraphAddEventRecordNode(&n, graph, nullptr, 0, trace->entry)) != hipSuccess)
+      return hip_fail(e, "hipGraphAddEventRecordNode");
+    for (int s = 0; s < n_streams; ++s) add_after(s, n);
+  }
+  auto trace_node = [&](int s, hipEvent_t ev) -> cm_status {
+    hipGraphNode_t n;
+    hipError_t er = hipGraphAddEventRecordNode(&n, graph, frontier[s].data(), frontier[s].size(), ev);
+    if (er != hipSuccess) return hip_fail(er, "hipGraphAddEventRecordNode");
+    add_after(s, n);
+    return CM_OK;
+  };
+  const std::vector<cm_op_rec> &ops = cp->prog.ops;
+  for (size_t i = 0; i < ops.size(); ++i) {
+    const cm_op_rec &o = ops[i];
+    const int s = o.stream;
+    if (o.kind == CM_OPK_RECORD) {
+      event_frontier[o.event] = frontier[s];
+      continue;
+    }
+    if (o.kind == CM_OPK_WAIT) {
+      for (hipGraphNode_t n : event_frontier[o.event])
+        if (std::find(frontier[s].begin(), frontier[s].end(), n) == frontier[s].end()) frontier[s].push_back(n);
+      continue;
+    }
+    int span = -1;
+    if (trace) {
+      if (trace->used < trace->capacity) {
+        span = trace->used++;
+        cm_span sp{};
+        sp.kind = o.kind;
+        sp.stream = o.stream;
+        sp.step = o.step;
+        sp.chunk = o.chunk;
+        trace->spans.push_back(sp);
+        cm_status st = trace_node(s, trace->ev[2 * span]);
+        if (st != CM_OK) return st;
+      } else {
+        trace->overflow = true;
+      }
+    }
+    hipGraphNode_t node;
+    if (o.kind == CM_OPK_COPY) {
+      e = hipGraphAddMemcpyNode1D(&node, graph, frontier[s].data(), frontier[s].size(), base[o.dst_buf] + o.dst_off,
+                                  base[o.src_buf] + o.src_off, o.bytes, hipMemcpyDeviceToDeviceNoCU);
+      if (e != hipSuccess) return hip_fail(e, "hipGraphAddMemcpyNode1D (ring hop)");
+    } else if (o.kind == CM_OPK_GEMM || o.kind == CM_OPK_REDUCE) {
+      const Launch &L = cp->launches[cp->launch_of_op[i]];
+      GemmParams p = L.p;
+      for (int b = 0; b < 4; ++b) p.base[b] = base[b];
+      KernelLaunch kl;
+      if (o.kind == CM_OPK_GEMM) {
+        if (!gemm_launch_config(p, L.tm, L.tn, &kl)) { set_error("no kernel for tile"); return CM_ERR_UNSUPPORTED; }
+      } else {
+        reduce_launch_config(p, &kl);
+      }
+      void *args[] = {&p};
+      hipKernelNodeParams kp{};
+      kp.func = kl.func;
+      kp.gridDim = kl.grid;
+      kp.blockDim = kl.block;
+      kp.sharedMemBytes = 0;
+      kp.kernelParams = args;
+      kp.extra = nullptr;
+      e = hipGraphAddKernelNode(&node, graph, frontier[s].data(), frontier[s].size(), &kp);
+      if (e != hipSuccess) return hip_fail(e, "hipGraphAddKernelNode");
+    } else {
+      set_error("corrupt program");
+      return CM_ERR_INVALID_ARG;
+    }
+    add_after(s, node);
+    if (span >= 0) {
+      cm_status st = trace_node(s, trace->ev[2 * span + 1]);
+      if (st != CM_OK) return st;
+    }
+  }
+  if ((e = hipGraphInstantiate(&g->exec, graph, nullptr, nullptr, 0)) != hipSuccess)
+    return hip_fail(e, "hipGraphInstantiate");
+  if (trace) {
+    g->spans = trace->spans;
+    g->overflow = trace->overflow;
+  }
+  return CM_OK;
+}
+
+std::string graph_key(const cm_plan &pl, char *const base[4], const cm_trace *trace) {
+  char buf[160];
+  std::snprintf(buf, sizeof buf, "|%p %p %p %p %p", (void *)base[0], (void *)base[1], (void *)base[2],
+                (void *)base[3], (const void *)trace);
+  return plan_key(pl) + buf;
+}
+
+cm_status run(const cm_plan *pl, bool want_ag, const void *x, const void *w, void *y, void *ws, size_t ws_bytes,
+              void *compute, void *const *comm, int n_comm, cm_trace *trace) {
+  cm_status st = validate_call(pl, want_ag, x, w, y, ws, ws_bytes, compute, comm, n_comm);
+  if (st != CM_OK) return st;
+  int dev;
+  if ((st = check_device(&dev)) != CM_OK) return st;
+  if (trace && trace->device != dev) { set_error("trace was created on another device"); return CM_ERR_INVALID_ARG; }
+  const Compiled *cp;
+  if ((st = get_compiled(*pl, &cp)) != CM_OK) return st;
+  std::vector<hipEvent_t> *evp;
+  if ((st = event_pool(dev, cp->prog.n_events, &evp)) != CM_OK) return st;
+
+  char *base[4] = {const_cast<char *>(static_cast<const char *>(x)), const_cast<char *>(static_cast<const char *>(w)),
+                   static_cast<char *>(y), static_cast<char *>(ws)};
+  hipStream_t streams[CM_MAX_COMM + 1];
+  streams[0] = static_cast<hipStream_t>(compute);
+  for (int i = 0; i < n_comm; ++i) streams[i + 1] = static_cast<hipStream_t>(comm[i]);
+
+  if (pl->desc.exec_mode == CM_EXEC_EAGER) return enqueue(cp, *evp, base, streams, trace);
+
+  ThreadState &ts = tls();
+  std::string key = graph_key(*pl, base, trace);
+  auto it = ts.graphs.find(key);
+  hipError_t e;
+  if (it == ts.graphs.end()) {
+    if (ts.graphs.size() >= kMaxGraphs) ts.graphs.clear();
+    auto g = std::make_unique<GraphEntry>();
+    if ((st = build_graph(cp, base, n_comm + 1, trace, g.get())) != CM_OK) return st;
+    it = ts.graphs.emplace(key, std::move(g)).first;
+  }
+  if (trace) {
+    trace->spans = it->second->spans;
+    trace->used = (int)trace->spans.size();
+    trace->overflow = it->second->overflow;
+  }
+  if ((e = hipGraphLaunch(it->second->exec, streams[0])) != hipSuccess) return hip_fail(e, "hipGraphLaunch");
+  return CM_OK;
+}
+
 }  // namespace
+
+// Graphs that record a trace's events must not outlive the trace.
+void forget_graphs_of(const cm_trace *t) {
+  char tag[32];
+  std::snprintf(tag, sizeof tag, " %p", (const void *)t);
+  auto &g = tls().graphs;
+  for (auto it = g.begin(); it != g.end();) {
+    const std::string &k = it->first;
+    if (k.size() >= std::strlen(tag) && k.compare(k.size() - std::strlen(tag), std::string::npos, tag) == 0)
+      it = g.erase(it);
+    else
+      ++it;
+  }
+}
+
 }  // namespace collmm
 
 extern "C" {
@@ -388,6 +551,7 @@ cm_status cm_trace_create(int capacity, cm_trace **out) {
 
 cm_status cm_trace_destroy(cm_trace *t) {
   if (!t) return CM_OK;
+  collmm::forget_graphs_of(t);
   if (t->entry) (void)hipEventDestroy(t->entry);
   for (auto &ev : t->ev)
     if (ev) (void)hipEventDestroy(ev);

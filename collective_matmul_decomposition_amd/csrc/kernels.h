@@ -26,6 +26,14 @@ struct GemmParams {
 };
 
 bool gemm_tile_supported(int tm, int tn);
+
+// Kernel handle and launch shape, for adding launches to a HIP graph.
+struct KernelLaunch {
+  void *func;
+  dim3 grid, block;
+};
+bool gemm_launch_config(const GemmParams &p, int tm, int tn, KernelLaunch *out);
+void reduce_launch_config(const GemmParams &p, KernelLaunch *out);
 hipError_t launch_gemm(const GemmParams &p, int tm, int tn, hipStream_t s);
 hipError_t launch_reduce(const GemmParams &p, hipStream_t s);
 

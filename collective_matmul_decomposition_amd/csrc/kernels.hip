@@ -12,13 +12,12 @@
 //  * reduce_jobs: C = in0 + in1 elementwise (the add of the pipeline-chunk
 //    ReduceScatter ring), fp32 in, fp32 or bf16 out.
 //
-// Block tile BM x BN x 64, 256 threads = 4 waves in a WM x (4/WM) grid; each
-// wave owns a (BM/WM) x (BN/(4/WM)) sub-tile made of 32x32 MFMA tiles.
-// Operands are staged through LDS in two buffers (the next K-slab's global
-// loads are in flight while the current slab is multiplied); LDS rows are
-// 128 bytes (64 bf16) with the 16-byte column chunks XOR-swizzled by row so
-// that the MFMA operand reads spread over the banks.  Blocks are numbered so
-// that each of the 8 XCDs (which own separate L2 caches) works on whole jobs.
+// Block tile BM x BN x 64, 512 threads = 8 waves; operands are staged
+// through two LDS buffers by direct-to-LDS loads (the next K-slab is in
+// flight while the current one is multiplied).  LDS rows are 128 bytes (64
+// bf16) with the 16-byte K-chunks XOR-swizzled by row so that the MFMA
+// operand reads spread over the banks.  Blocks are numbered so that each of
+// the 8 XCDs (which own separate L2 caches) works on whole jobs.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -28,11 +27,11 @@ namespace collmm {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void *lds_ptr;
+typedef __attribute__((address_space(1))) void *glob_ptr;
 
 namespace {
 
-constexpr int BK = 64;          // K per LDS slab
-constexpr int ROW_BYTES = 128;  // one LDS row: 64 bf16
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -41,8 +40,6 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
-// Byte offset of 16-byte chunk `chunk` of LDS row `row` (swizzled).
-__device__ __forceinline__ int lds_off(int row, int chunk) { return row * ROW_BYTES + ((chunk ^ (row & 7)) << 4); }
 
 __device__ __forceinline__ int logical_block() {
   // Round-robin dispatch puts block b on XCD b % 8; renumber so that each
@@ -88,19 +85,68 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[TM][TN], const EpiA
     }
 }
 
-template <int BM, int BN, int WM>
-__global__ __launch_bounds__(256) void gemm_jobs_kernel(const GemmParams p) {
-  constexpr int WN = 4 / WM;
+// One workgroup = 8 waves (512 threads, two per SIMD) computes a BM x BN tile
+// of one job; the waves form a WM x WN grid and each owns a (BM/WM) x (BN/WN)
+// sub-tile of 32x32 MFMA tiles.  Operands move HBM/L2 -> LDS with the
+// direct-to-LDS loads of gfx950 (global_load_lds_dwordx4: each lane's 16
+// bytes land at the wave's LDS base + 16 * lane, no VGPR staging) through a
+// ring of STAGES LDS slabs of BK values of K: while slab kt is multiplied,
+// slabs kt+1 .. kt+STAGES-1 are in flight.  Rows past the end of A or B are
+// clamped to the last row: they only feed outputs that are not stored.
+//
+// LDS layout of a slab: rows of 2*BK bytes holding BK/8 16-byte K-chunks;
+// chunk c of row r sits at position c ^ (r / R % (BK/8)) with R = 256 / (2*BK)
+// rows per 256 bytes, so the 16 rows that one 16-lane phase of an MFMA
+// operand read touches cover the 64 banks once.
+template <int BM, int BN, int BK>
+struct LoadPlan {
+  static constexpr int ROWB = 2 * BK;             // bytes per LDS row
+  static constexpr int CH = BK / 8;               // 16-byte chunks per row
+  static constexpr int RPG = 1024 / ROWB;         // rows per 1 KB load group
+  static constexpr int RPB = 256 / ROWB;          // rows per 256 bytes (one bank sweep)
+  static constexpr int A_GROUPS = BM / RPG, B_GROUPS = BN / RPG;
+  static constexpr int GROUPS = A_GROUPS + B_GROUPS;
+  static constexpr int MAX_PER_WAVE = (GROUPS + 7) / 8;
+  static constexpr int MIN_PER_WAVE = GROUPS / 8;
+  static constexpr int SLAB = (BM + BN) * ROWB;
+};
+
+template <int BK>
+__device__ __forceinline__ int lds_pos(int row, int chunk) {
+  constexpr int ROWB = 2 * BK, CH = BK / 8, RPB = 256 / ROWB;
+  return row * ROWB + ((chunk ^ ((row / RPB) % CH)) << 4);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait until at most `rem` slabs of this wave's loads (L per slab) are outstanding.
+template <int L, int STAGES>
+__device__ __forceinline__ void wait_slabs(int rem) {
+  static_assert(L * (STAGES - 2) < 64, "vmcnt range");
+  if (rem <= 0) wait_vmcnt<0>();
+  else if (rem == 1 || STAGES < 4) wait_vmcnt<L>();
+  else if (rem == 2 || STAGES < 5) wait_vmcnt<2 * L>();
+  else if (rem == 3 || STAGES < 6) wait_vmcnt<3 * L>();
+  else wait_vmcnt<4 * L * (STAGES >= 6)>();
+}
+
+template <int BM, int BN, int WM, int WN, int BK, int STAGES>
+__global__ __launch_bounds__(512) void gemm_jobs_kernel(const GemmParams p) {
   constexpr int WTM = BM / WM, WTN = BN / WN;  // wave sub-tile
   constexpr int TM = WTM / 32, TN = WTN / 32;  // MFMA tiles per wave
-  constexpr int A_LOADS = BM * 8 / 256, B_LOADS = BN * 8 / 256;
+  constexpr int KS = BK / 16;                   // MFMA K steps per slab
+  using LP = LoadPlan<BM, BN, BK>;
+  static_assert(WM * WN == 8, "eight waves");
   static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "tile shape");
-  static_assert(A_LOADS >= 1 && B_LOADS >= 1, "tile too small for 256 threads");
+  static_assert(BK == 32 || BK == 64, "slab depth");
+  static_assert(BM % LP::RPG == 0 && BN % LP::RPG == 0 && STAGES >= 2 && STAGES <= 6, "tile shape");
+  static_assert(STAGES * LP::SLAB <= 160 * 1024, "LDS");
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * (BM + BN) * ROW_BYTES];
-  // buffer b: A rows at smem + b*(BM+BN)*ROW_BYTES, then B rows
-  auto sA = [&](int b) -> char * { return smem + b * (BM + BN) * ROW_BYTES; };
-  auto sB = [&](int b) -> char * { return smem + b * (BM + BN) * ROW_BYTES + BM * ROW_BYTES; };
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * LP::SLAB];
 
   const int lb = logical_block();
   const int job = lb / p.tiles_per_job;
@@ -116,35 +162,41 @@ __global__ __launch_bounds__(256) void gemm_jobs_kernel(const GemmParams p) {
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
 
-  // Global -> register staging: thread loads chunk (tid & 7) of rows (tid >> 3) + 32 i.
-  const int ld_chunk = tid & 7, ld_row = tid >> 3;
-  uint4 ra[A_LOADS], rb[B_LOADS];
-
-  auto load_global = [&](int k0) {
+  // Direct-to-LDS addressing.  Load group g (A rows first, then B rows) is
+  // issued by wave g % 8 as its (g / 8)-th load; lane l writes position
+  // l % CH of row l / CH of the group, which holds the swizzled K-chunk.
+  const char *src[LP::MAX_PER_WAVE];
+  int dst[LP::MAX_PER_WAVE];
+  const int my_loads = LP::MIN_PER_WAVE + (wave < LP::GROUPS % 8 ? 1 : 0);
 #pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) {
-      const int r = tm0 + ld_row + 32 * i;
-      if (r < p.M)
-        ra[i] = *reinterpret_cast<const uint4 *>(Abase + ((size_t)r * p.lda + k0 + ld_chunk * 8) * 2);
-      else
-        ra[i] = make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < LP::MAX_PER_WAVE; ++i) {
+    const int g = i * 8 + wave;
+    const int gg = g < LP::GROUPS ? g : 0;
+    const bool is_a = gg < LP::A_GROUPS;
+    const int row = (is_a ? gg : gg - LP::A_GROUPS) * LP::RPG + lane / LP::CH;
+    const int chunk = (lane % LP::CH) ^ ((row / LP::RPB) % LP::CH);
+    if (is_a) {
+      const int r = min(tm0 + row, p.M - 1);
+      src[i] = Abase + ((size_t)r * p.lda + chunk * 8) * 2;
+    } else {
+      const int r = min(tn0 + row, p.N - 1);
+      src[i] = Bbase + ((size_t)r * p.ldb + chunk * 8) * 2;
     }
+    dst[i] = gg * 1024;  // A groups first, then B groups: B rows start at BM * ROWB
+  }
+  auto issue = [&](int kt) {
+    char *slab = smem + (kt % STAGES) * LP::SLAB;
+    const size_t koff = (size_t)kt * BK * 2;
 #pragma unroll
-    for (int i = 0; i < B_LOADS; ++i) {
-      const int r = tn0 + ld_row + 32 * i;
-      if (r < p.N)
-        rb[i] = *reinterpret_cast<const uint4 *>(Bbase + ((size_t)r * p.ldb + k0 + ld_chunk * 8) * 2);
-      else
-        rb[i] = make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < LP::MAX_PER_WAVE; ++i)
+      if (i < LP::MIN_PER_WAVE || i < my_loads)
+        __builtin_amdgcn_global_load_lds((glob_ptr)(src[i] + koff), (lds_ptr)(slab + dst[i]), 16, 0, 0);
   };
-  auto store_lds = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < A_LOADS; ++i)
-      *reinterpret_cast<uint4 *>(sA(buf) + lds_off(ld_row + 32 * i, ld_chunk)) = ra[i];
-#pragma unroll
-    for (int i = 0; i < B_LOADS; ++i)
-      *reinterpret_cast<uint4 *>(sB(buf) + lds_off(ld_row + 32 * i, ld_chunk)) = rb[i];
+  auto wait_for = [&](int rem) {
+    if (LP::MAX_PER_WAVE == LP::MIN_PER_WAVE || my_loads == LP::MAX_PER_WAVE)
+      wait_slabs<LP::MAX_PER_WAVE, STAGES>(rem);
+    else
+      wait_slabs<LP::MIN_PER_WAVE, STAGES>(rem);
   };
 
   f32x16 acc[TM][TN];
@@ -156,34 +208,43 @@ __global__ __launch_bounds__(256) void gemm_jobs_kernel(const GemmParams p) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   const int KT = p.K / BK;
-  load_global(0);
-  store_lds(0);
-  __syncthreads();
+#pragma unroll
+  for (int st = 0; st < STAGES - 1; ++st)
+    if (st < KT) issue(st);
 
   // MFMA operand rows: lane owns row (lane & 31) of each 32-row tile and the
   // 8-element K group (lane >> 5) of each 16-wide K step.
   const int frow = lane & 31, fgrp = lane >> 5;
+  int a_off[TM], b_off[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) a_off[i] = wm * WTM + i * 32 + frow;
+#pragma unroll
+  for (int j = 0; j < TN; ++j) b_off[j] = BM + wn * WTN + j * 32 + frow;
+  bf16x8 fa[2][TM], fb[2][TN];
+  auto load_frags = [&](const char *slab, int ks, int set) {
+    const int chunk = ks * 2 + fgrp;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[set][i] = *reinterpret_cast<const bf16x8 *>(slab + lds_pos<BK>(a_off[i], chunk));
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[set][j] = *reinterpret_cast<const bf16x8 *>(slab + lds_pos<BK>(b_off[j], chunk));
+  };
   for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) load_global((kt + 1) * BK);
+    // slab kt has landed (for every wave) and slab kt-1 is no longer read
+    wait_for(min(STAGES - 2, KT - 1 - kt));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
+    const char *slab = smem + (kt % STAGES) * LP::SLAB;
+    load_frags(slab, 0, 0);
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 fa[TM], fb[TN];
-      const int chunk = ks * 2 + fgrp;
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        fa[i] = *reinterpret_cast<const bf16x8 *>(sA(buf) + lds_off(wm * WTM + i * 32 + frow, chunk));
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        fb[j] = *reinterpret_cast<const bf16x8 *>(sB(buf) + lds_off(wn * WTN + j * 32 + frow, chunk));
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) load_frags(slab, ks + 1, (ks + 1) & 1);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][i], fb[ks & 1][j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < KT) store_lds(buf ^ 1);
-    __syncthreads();
   }
 
   // Epilogue.  Accumulator element e of a 32x32 tile sits at row
@@ -237,37 +298,51 @@ __global__ __launch_bounds__(256) void reduce_jobs_kernel(const GemmParams p) {
   }
 }
 
-template <int BM, int BN, int WM>
-hipError_t launch_tile(const GemmParams &p, hipStream_t s) {
-  const int grid = p.n_jobs * p.tiles_per_job;
-  hipLaunchKernelGGL((gemm_jobs_kernel<BM, BN, WM>), dim3(grid), dim3(256), 0, s, p);
-  return hipGetLastError();
-}
-
 }  // namespace
 
 bool gemm_tile_supported(int tm, int tn) {
-  return (tm == 256 && tn == 256) || (tm == 256 && tn == 128) || (tm == 128 && tn == 256) ||
-         (tm == 128 && tn == 128) || (tm == 64 && tn == 256) || (tm == 64 && tn == 128);
+  KernelLaunch L;
+  GemmParams p{};
+  return gemm_launch_config(p, tm, tn, &L);
 }
 
-hipError_t launch_gemm(const GemmParams &p, int tm, int tn, hipStream_t s) {
-  if (tm == 256 && tn == 256) return launch_tile<256, 256, 2>(p, s);
-  if (tm == 256 && tn == 128) return launch_tile<256, 128, 2>(p, s);
-  if (tm == 128 && tn == 256) return launch_tile<128, 256, 2>(p, s);
-  if (tm == 128 && tn == 128) return launch_tile<128, 128, 2>(p, s);
-  if (tm == 64 && tn == 256) return launch_tile<64, 256, 1>(p, s);
-  if (tm == 64 && tn == 128) return launch_tile<64, 128, 1>(p, s);
-  return hipErrorInvalidValue;
+bool gemm_launch_config(const GemmParams &p, int tm, int tn, KernelLaunch *out) {
+  void *f = nullptr;
+  if (tm == 256 && tn == 256) f = reinterpret_cast<void *>(&gemm_jobs_kernel<256, 256, 2, 4, 64, 2>);
+  else if (tm == 256 && tn == 192) f = reinterpret_cast<void *>(&gemm_jobs_kernel<256, 192, 4, 2, 64, 2>);
+  else if (tm == 256 && tn == 128) f = reinterpret_cast<void *>(&gemm_jobs_kernel<256, 128, 4, 2, 64, 3>);
+  else if (tm == 128 && tn == 256) f = reinterpret_cast<void *>(&gemm_jobs_kernel<128, 256, 2, 4, 64, 3>);
+  else if (tm == 128 && tn == 128) f = reinterpret_cast<void *>(&gemm_jobs_kernel<128, 128, 2, 4, 64, 4>);
+  else if (tm == 64 && tn == 256) f = reinterpret_cast<void *>(&gemm_jobs_kernel<64, 256, 2, 4, 64, 4>);
+  if (!f) return false;
+  out->func = f;
+  out->grid = dim3(p.n_jobs * p.tiles_per_job);
+  out->block = dim3(512);
+  return true;
 }
 
-hipError_t launch_reduce(const GemmParams &p, hipStream_t s) {
+void reduce_launch_config(const GemmParams &p, KernelLaunch *out) {
   const long per_job = (long)p.M * (p.N / 4);
   int bx = (int)((per_job + 255) / 256);
   if (bx > 1024) bx = 1024;
   if (bx < 1) bx = 1;
-  hipLaunchKernelGGL(reduce_jobs_kernel, dim3(bx, p.n_jobs), dim3(256), 0, s, p);
-  return hipGetLastError();
+  out->func = reinterpret_cast<void *>(&reduce_jobs_kernel);
+  out->grid = dim3(bx, p.n_jobs);
+  out->block = dim3(256);
+}
+
+hipError_t launch_gemm(const GemmParams &p, int tm, int tn, hipStream_t s) {
+  KernelLaunch L;
+  if (!gemm_launch_config(p, tm, tn, &L)) return hipErrorInvalidValue;
+  void *args[] = {const_cast<GemmParams *>(&p)};
+  return hipLaunchKernel(L.func, L.grid, L.block, args, 0, s);
+}
+
+hipError_t launch_reduce(const GemmParams &p, hipStream_t s) {
+  KernelLaunch L;
+  reduce_launch_config(p, &L);
+  void *args[] = {const_cast<GemmParams *>(&p)};
+  return hipLaunchKernel(L.func, L.grid, L.block, args, 0, s);
 }
 
 }  // namespace collmm

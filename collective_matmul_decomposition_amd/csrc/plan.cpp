@@ -66,8 +66,7 @@ bool is_pow2_chunk(int c) { return c == 1 || c == 2 || c == 4 || c == 8 || c == 
 // operands less).
 struct TileCand { int tm, tn; double eff; };
 constexpr TileCand kTiles[] = {
-    {256, 256, 1.00}, {256, 128, 0.92}, {128, 256, 0.92}, {128, 128, 0.80}, {64, 256, 0.78},
-    {64, 128, 0.65},
+    {256, 256, 1.00}, {256, 192, 0.97}, {256, 128, 0.90}, {128, 256, 0.90}, {128, 128, 0.75}, {64, 256, 0.72},
 };
 constexpr int kCUs = 256;
 
@@ -149,8 +148,10 @@ cm_status validate_desc(const cm_plan_desc &d) {
   if (d.k % 64 || d.n % 64) { set_error("k (%d) and n (%d) must be multiples of 64", d.k, d.n); return CM_ERR_SHAPE; }
   if ((long long)d.n_ranks * d.m > (1 << 24)) { set_error("N*m too large"); return CM_ERR_SHAPE; }
   if (d.copy_gbps < 0 || d.mfma_tflops < 0 || d.launch_us < 0) { set_error("cost-model inputs must be >= 0"); return CM_ERR_INVALID_ARG; }
+  if (d.exec_mode != CM_EXEC_GRAPH && d.exec_mode != CM_EXEC_EAGER) { set_error("unknown exec_mode %d", d.exec_mode); return CM_ERR_INVALID_ARG; }
   if ((d.tile_m || d.tile_n) && !tile_known(d.tile_m, d.tile_n)) {
-    set_error("no GEMM tile %dx%d (choose 256x256, 256x128, 128x256, 128x128, 64x256, 64x128 or 0x0)", d.tile_m, d.tile_n);
+    set_error("no GEMM tile %dx%d (choose 256x256, 256x192, 256x128, 128x256, 128x128, 64x256 or 0x0)", d.tile_m,
+              d.tile_n);
     return CM_ERR_UNSUPPORTED;
   }
   return CM_OK;

@@ -43,9 +43,9 @@ def gpu_ready():
 
 
 def run_case(op, N, m, k, n, dist="int", out="f32", dir="uni", chunks=1, sched="decomposed", n_comm=1, seed=0,
-             repeat=1, tile=(0, 0)):
+             repeat=1, tile=(0, 0), exec_mode="graph"):
     plan = nat.cm_ring_plan(op=op, n_ranks=N, m=m, k=k, n=n, dir=dir, chunks=chunks, sched=sched, out_dtype=out,
-                            n_comm=n_comm, tile=tile)
+                            n_comm=n_comm, tile=tile, exec_mode=exec_mode)
     if op == "ag":
         a, w = gen.ag_inputs(N, m, k, n, dist, seed)
     else:
@@ -55,8 +55,8 @@ def run_case(op, N, m, k, n, dist="int", out="f32", dir="uni", chunks=1, sched="
     comm = buffers.comm_streams(n_comm)
     results = []
     for _ in range(repeat):
-        say("  launch %s N=%d m=%d k=%d n=%d %s out=%s dir=%s c=%d(%d) sched=%s n_comm=%d tile=%dx%d" %
-            (op, N, m, k, n, dist, out, dir, chunks, plan.chunks, sched, n_comm, plan.tile_m, plan.tile_n))
+        say("  launch %s N=%d m=%d k=%d n=%d %s out=%s dir=%s c=%d(%d) sched=%s n_comm=%d tile=%dx%d %s" %
+            (op, N, m, k, n, dist, out, dir, chunks, plan.chunks, sched, n_comm, plan.tile_m, plan.tile_n, exec_mode))
         y.fill_(float("nan")) if out == "f32" else y.fill_(float("nan"))
         buffers.run(plan, x_t, w_t, y, ws, comm=comm)
         torch.cuda.synchronize()
@@ -97,10 +97,11 @@ for op in ("ag", "rs", "rs_pipe"):
                 TINY.append((op, dir, sched, chunks, dist, out))
 
 
+@pytest.mark.parametrize("exec_mode", ["graph", "eager"])
 @pytest.mark.parametrize("op,dir,sched,chunks,dist,out", TINY)
-def test_tiny_config(op, dir, sched, chunks, dist, out):
-    say("tiny", op, dir, sched, chunks, dist, out)
-    _, a, w, (y,) = run_case(op, 4, 64, 256, 256, dist, out, dir, chunks, sched, n_comm=4)
+def test_tiny_config(op, dir, sched, chunks, dist, out, exec_mode):
+    say("tiny", op, dir, sched, chunks, dist, out, exec_mode)
+    _, a, w, (y,) = run_case(op, 4, 64, 256, 256, dist, out, dir, chunks, sched, n_comm=4, exec_mode=exec_mode)
     check(op, a, w, y, out, dist)
 
 
@@ -141,7 +142,7 @@ def test_mid_size_eight_ranks(op, dir, chunks):
     check(op, a, w, y, "f32", "int")
 
 
-TILES = [(256, 256), (256, 128), (128, 256), (128, 128), (64, 256), (64, 128)]
+TILES = [(256, 256), (256, 192), (256, 128), (128, 256), (128, 128), (64, 256)]
 
 
 @pytest.mark.parametrize("tile", TILES, ids=lambda t: "%dx%d" % t)
@@ -159,10 +160,13 @@ def test_every_tile_variant(tile, op):
 
 @pytest.mark.parametrize("op", ["ag", "rs", "rs_pipe"])
 def test_repeatable_bitwise(op):
+    """Graph replays (the second and third call reuse the captured graph) and
+    the eager path give bit-identical results."""
     say("repeat", op)
     n = 512 if op != "ag" else 384
     _, _, _, ys = run_case(op, 4, 128, 512, n, "normal", "f32", "uni", 2, "decomposed", 4, repeat=3)
-    for y in ys[1:]:
+    _, _, _, ye = run_case(op, 4, 128, 512, n, "normal", "f32", "uni", 2, "decomposed", 4, exec_mode="eager")
+    for y in ys[1:] + ye:
         assert torch.equal(y, ys[0])
 
 
