@@ -161,7 +161,7 @@ struct GraphEntry {
   }
 };
 
-constexpr size_t kMaxGraphs = 64;
+constexpr size_t kMaxGraphs = 256;
 
 struct ThreadState {
   std::unordered_map<std::string, std::unique_ptr<GraphEntry>> graphs;

@@ -52,10 +52,12 @@ thread_local std::string g_last_error;
 int mod(int a, int n) { return ((a % n) + n) % n; }
 
 // Default cost-model constants for MI355X, from measurements of this
-// library: one comm stream's SDMA copy rate and a sustained GEMM rate.
-constexpr double kDefaultCopyGBps = 55.0;
-constexpr double kDefaultMfmaTflops = 1300.0;
-constexpr double kDefaultLaunchUs = 8.0;
+// library (graph replay): the hop rate one comm lane sustains with large
+// copies, the step GEMM's rate at a full, well-shaped launch, and the fixed
+// cost of one graph node (kernel or copy).
+constexpr double kDefaultCopyGBps = 100.0;
+constexpr double kDefaultMfmaTflops = 900.0;
+constexpr double kDefaultLaunchUs = 20.0;
 
 bool is_pow2_chunk(int c) { return c == 1 || c == 2 || c == 4 || c == 8 || c == 16; }
 
@@ -66,7 +68,7 @@ bool is_pow2_chunk(int c) { return c == 1 || c == 2 || c == 4 || c == 8 || c == 
 // operands less).
 struct TileCand { int tm, tn; double eff; };
 constexpr TileCand kTiles[] = {
-    {256, 256, 1.00}, {256, 192, 0.97}, {256, 128, 0.90}, {128, 256, 0.90}, {128, 128, 0.75}, {64, 256, 0.72},
+    {256, 256, 1.00}, {256, 192, 0.90}, {256, 128, 0.88}, {128, 256, 0.88}, {128, 128, 0.75}, {64, 256, 0.65},
 };
 constexpr int kCUs = 256;
 
@@ -76,7 +78,9 @@ bool tile_known(int tm, int tn) {
   return false;
 }
 
-void choose_tile(int rows, int cols, int jobs, int *tm, int *tn) {
+// Returns the chosen tile's score: the fraction of the chip's rate the
+// launch is expected to reach relative to an ideal full launch.
+double choose_tile(int rows, int cols, int jobs, int *tm, int *tn) {
   double best = -1;
   for (const TileCand &t : kTiles) {
     long tiles_m = (rows + t.tm - 1) / t.tm, tiles_n = (cols + t.tn - 1) / t.tn;
@@ -87,6 +91,7 @@ void choose_tile(int rows, int cols, int jobs, int *tm, int *tn) {
     double score = useful * fill * t.eff;
     if (score > best + 1e-9) { best = score; *tm = t.tm; *tn = t.tn; }
   }
+  return best;
 }
 
 }  // namespace
@@ -160,43 +165,55 @@ cm_status validate_desc(const cm_plan_desc &d) {
 // ------------------------------------------------------------------ planning
 namespace {
 
-double gemm_us(const cm_plan_desc &d, double flops) { return flops / (d.mfma_tflops * 1e12) * 1e6 + d.launch_us; }
-double hop_us(const cm_plan_desc &d, double bytes_total, int lanes) {
+// GEMM time of one launch of `jobs` jobs of rows x cols x depth, at the
+// sustained rate scaled by how well the best tile fits the launch.
+double gemm_us(const cm_plan_desc &d, int jobs, double rows, double cols, double depth) {
+  int tm, tn;
+  double eff = choose_tile((int)rows, (int)cols, jobs, &tm, &tn);
+  const double flops = 2.0 * jobs * rows * cols * depth;
+  return flops / (d.mfma_tflops * 1e12 * eff) * 1e6 + d.launch_us;
+}
+// Hop time of one step: `copies` copies per lane over min(n_comm, lanes) lanes.
+double hop_us(const cm_plan_desc &d, double bytes_total, int lanes, int copies_per_lane) {
   int streams = std::min(d.n_comm, std::max(1, lanes));
-  return bytes_total / (streams * d.copy_gbps * 1e9) * 1e6 + d.launch_us;
+  return bytes_total / (streams * d.copy_gbps * 1e9) * 1e6 + copies_per_lane * d.launch_us;
 }
 
 // Predicted time of the decomposed op with c chunks (the reading of the
 // "simple peak-rate cost model" of "Knowing when to decline": per-step GEMM
-// time at a sustained rate, per-step hop time at the comm streams' rate, and
-// a fixed cost per launch or hop).
+// time at a sustained rate, per-step hop time at the comm lanes' rate, and a
+// fixed cost per launch and per copy).
 struct Est { double total, g, h; bool hidden; };
 
 Est estimate(const cm_plan_desc &d, int c) {
   const double N = d.n_ranks, m = d.m, k = d.k, n = d.n;
   const bool bi = d.dir == CM_RING_BI && d.n_ranks > 2;
-  const int lanes = d.n_ranks * (bi ? 2 : 1);
+  const int ndir = bi ? 2 : 1;
+  const int lanes = d.n_ranks * ndir;
+  // copies per lane per step: a lane moves a contiguous range of ranks in one
+  // or two copies (AG step 0 copies rank by rank)
+  const int per_lane = std::max(1, std::min(2, (int)(lanes / std::max(1, d.n_comm))));
   Est e{};
   if (d.op == CM_OP_AG_GEMM) {
-    const double g = gemm_us(d, N * 2.0 * (m / c) * k * n * (bi ? 2 : 1));
-    const double h = hop_us(d, N * (m / c) * k * 2.0 * (bi ? 2 : 1), lanes);
-    const int steps = bi ? 1 + (d.n_ranks) / 2 : d.n_ranks;
+    const double g = gemm_us(d, d.n_ranks * ndir, m / c, n, k);
+    const double h = hop_us(d, N * (m / c) * k * 2.0 * ndir, lanes, per_lane);
+    const int steps = bi ? 1 + d.n_ranks / 2 : d.n_ranks;
     e.g = g; e.h = h;
     // hop(s) runs beside GEMM(s); GEMM(s+1) needs hop(s)
     e.total = c * steps * std::max(g, h) + std::min(g, h);
     e.hidden = h <= g;
   } else if (d.op == CM_OP_GEMM_RS) {
-    const double g = gemm_us(d, N * 2.0 * m * k * (n / c) * (bi ? 2 : 1));
-    const double h = hop_us(d, N * m * (n / c) * 4.0 * (bi ? 2 : 1), lanes);
-    const int steps = bi ? 1 + (d.n_ranks) / 2 : d.n_ranks;
+    const double g = gemm_us(d, d.n_ranks * ndir, m, n / c, k);
+    const double h = hop_us(d, N * m * (n / c) * 4.0 * ndir, lanes, per_lane);
+    const int steps = bi ? 1 + d.n_ranks / 2 : d.n_ranks;
     e.g = g; e.h = h;
     // GEMM(s+1, j) needs hop(s, j), which starts after GEMM(s, j): a step
     // takes the longer of c GEMM chunks and one chunk's GEMM + hop.
-    e.total = steps * std::max(c * g, g + h) + (c > 1 ? 0 : 0);
+    e.total = steps * std::max(c * g, g + h);
     e.hidden = c >= 2 && h <= (c - 1) * g;
   } else {
-    const double g = gemm_us(d, N * 2.0 * (N * m) * k * (n / c));
-    const double h = hop_us(d, N * m * (n / c) * 4.0, d.n_ranks) + d.launch_us;  // copy + add
+    const double g = gemm_us(d, d.n_ranks, N * m, n / c, k);
+    const double h = hop_us(d, N * m * (n / c) * 4.0, d.n_ranks, per_lane) + d.launch_us;  // copy + add
     const double ring = (N - 1) * h;
     e.g = g; e.h = h;
     e.total = std::max(c * g + ring, g + c * ring);
@@ -237,18 +254,19 @@ cm_status plan(const cm_plan_desc *desc, cm_plan *out) {
   if (d.sched == CM_SCHED_NAIVE) {
     c = 1;
   } else if (c == 0) {
-    // Auto: candidates 1, 2, 4, 8 (RS needs >= 2 for any overlap, the
+    // Auto: candidates 1, 2, 3, 4, 6, 8 (RS needs >= 2 for any overlap, the
     // pipeline variant starts from the pages' default of four); take the
-    // smallest predicted time; decline when nothing hides the hops.
+    // smallest predicted time, preferring fewer chunks unless more chunks
+    // win by at least 5%; decline (report) when nothing hides the hops.
     int best = -1;
     double best_t = 0;
-    const int cands[] = {1, 2, 4, 8};
+    const int cands[] = {1, 2, 3, 4, 6, 8};
     for (int cc : cands) {
       if (!chunk_ok(cc)) continue;
       if (d.op == CM_OP_GEMM_RS && cc < 2 && d.n_ranks > 1) continue;
       if (d.op == CM_OP_AG_GEMM && d.m / cc < 32 && cc > 1) continue;
       Est e = estimate(d, cc);
-      if (best < 0 || e.total < best_t * 0.97) { best = cc; best_t = e.total; }
+      if (best < 0 || e.total < best_t * 0.95) { best = cc; best_t = e.total; }
     }
     if (best < 0) best = 1;
     if (d.op == CM_OP_GEMM_RS_PIPE && chunk_ok(4) && best != 4) {
@@ -288,7 +306,7 @@ cm_status plan(const cm_plan_desc *desc, cm_plan *out) {
   int rows = d.op == CM_OP_AG_GEMM ? d.m / c : d.m;
   int cols = d.op == CM_OP_AG_GEMM ? d.n : d.n / c;
   if (d.tile_m) { p.tile_m = d.tile_m; p.tile_n = d.tile_n; }
-  else choose_tile(rows, cols, N * (bi ? 2 : 1), &p.tile_m, &p.tile_n);
+  else (void)choose_tile(rows, cols, N * (bi ? 2 : 1), &p.tile_m, &p.tile_n);
   p.ws_bytes = ws_layout(p).total;
 
   Program prog;
@@ -382,7 +400,7 @@ struct Builder {
     o.n_jobs = (int)jobs.size();
     o.rows = rows; o.cols = cols; o.depth = depth;
     if (d.tile_m) { o.tile_m = d.tile_m; o.tile_n = d.tile_n; }
-    else choose_tile(rows, cols, (int)jobs.size(), &o.tile_m, &o.tile_n);
+    else (void)choose_tile(rows, cols, (int)jobs.size(), &o.tile_m, &o.tile_n);
     prog.jobs.insert(prog.jobs.end(), jobs.begin(), jobs.end());
     prog.ops.push_back(o);
     tick(0);

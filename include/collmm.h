@@ -99,8 +99,8 @@ typedef enum { CM_BF16 = 0, CM_F32 = 1 } cm_dtype;
  * copy engines directly).  CM_EXEC_EAGER: every call enqueues the program op
  * by op on the compute and comm streams.  Both run the same operations with
  * the same ordering; the graph form avoids the host-side cost of enqueueing
- * SDMA copies behind cross-stream waits.  Up to 64 graphs are cached per host
- * thread.
+ * SDMA copies behind cross-stream waits.  Up to 256 graphs are cached per
+ * host thread.
  */
 typedef enum { CM_EXEC_GRAPH = 0, CM_EXEC_EAGER = 1 } cm_exec_mode;
 
