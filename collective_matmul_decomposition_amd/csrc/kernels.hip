@@ -89,64 +89,45 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[TM][TN], const EpiA
 // of one job; the waves form a WM x WN grid and each owns a (BM/WM) x (BN/WN)
 // sub-tile of 32x32 MFMA tiles.  Operands move HBM/L2 -> LDS with the
 // direct-to-LDS loads of gfx950 (global_load_lds_dwordx4: each lane's 16
-// bytes land at the wave's LDS base + 16 * lane, no VGPR staging) through a
-// ring of STAGES LDS slabs of BK values of K: while slab kt is multiplied,
-// slabs kt+1 .. kt+STAGES-1 are in flight.  Rows past the end of A or B are
-// clamped to the last row: they only feed outputs that are not stored.
+// bytes land at the wave's LDS base + 16 * lane, no VGPR staging) through
+// rings of LDS slabs of BK values of K (AST slabs for A, BST for B): while
+// slab kt is multiplied, the following slabs are in flight.  Rows past the
+// end of A or B are clamped to the last row: they only feed outputs that are
+// not stored.
 //
 // LDS layout of a slab: rows of 2*BK bytes holding BK/8 16-byte K-chunks;
 // chunk c of row r sits at position c ^ (r / R % (BK/8)) with R = 256 / (2*BK)
 // rows per 256 bytes, so the 16 rows that one 16-lane phase of an MFMA
 // operand read touches cover the 64 banks once.
-template <int BM, int BN, int BK>
-struct LoadPlan {
-  static constexpr int ROWB = 2 * BK;             // bytes per LDS row
-  static constexpr int CH = BK / 8;               // 16-byte chunks per row
-  static constexpr int RPG = 1024 / ROWB;         // rows per 1 KB load group
-  static constexpr int RPB = 256 / ROWB;          // rows per 256 bytes (one bank sweep)
-  static constexpr int A_GROUPS = BM / RPG, B_GROUPS = BN / RPG;
-  static constexpr int GROUPS = A_GROUPS + B_GROUPS;
-  static constexpr int MAX_PER_WAVE = (GROUPS + 7) / 8;
-  static constexpr int MIN_PER_WAVE = GROUPS / 8;
-  static constexpr int SLAB = (BM + BN) * ROWB;
-};
-
-template <int BK>
-__device__ __forceinline__ int lds_pos(int row, int chunk) {
-  constexpr int ROWB = 2 * BK, CH = BK / 8, RPB = 256 / ROWB;
-  return row * ROWB + ((chunk ^ ((row / RPB) % CH)) << 4);
-}
-
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Wait until at most `rem` slabs of this wave's loads (L per slab) are outstanding.
-template <int L, int STAGES>
-__device__ __forceinline__ void wait_slabs(int rem) {
-  static_assert(L * (STAGES - 2) < 64, "vmcnt range");
-  if (rem <= 0) wait_vmcnt<0>();
-  else if (rem == 1 || STAGES < 4) wait_vmcnt<L>();
-  else if (rem == 2 || STAGES < 5) wait_vmcnt<2 * L>();
-  else if (rem == 3 || STAGES < 6) wait_vmcnt<3 * L>();
-  else wait_vmcnt<4 * L * (STAGES >= 6)>();
-}
-
-template <int BM, int BN, int WM, int WN, int BK, int STAGES>
+template <int BM, int BN, int WM, int WN, int BK, int AST, int BST>
 __global__ __launch_bounds__(512) void gemm_jobs_kernel(const GemmParams p) {
+  // A (activations, shared by every tile of a job and mostly served from L2)
+  // and B (weights, streamed from HBM once per launch) have separate LDS
+  // rings: AST slabs of A, BST slabs of B.  B's ring is deeper, so the
+  // weight stream is requested BST-AST slabs further ahead of its use.
   constexpr int WTM = BM / WM, WTN = BN / WN;  // wave sub-tile
   constexpr int TM = WTM / 32, TN = WTN / 32;  // MFMA tiles per wave
   constexpr int KS = BK / 16;                   // MFMA K steps per slab
-  using LP = LoadPlan<BM, BN, BK>;
+  constexpr int ROWB = 2 * BK, CH = BK / 8, RPG = 1024 / ROWB, RPB = 256 / ROWB;
+  constexpr int A_GROUPS = BM / RPG, B_GROUPS = BN / RPG;  // 1 KB load groups per slab
+  constexpr int A_SLAB = BM * ROWB, B_SLAB = BN * ROWB;
   static_assert(WM * WN == 8, "eight waves");
   static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "tile shape");
   static_assert(BK == 32 || BK == 64, "slab depth");
-  static_assert(BM % LP::RPG == 0 && BN % LP::RPG == 0 && STAGES >= 2 && STAGES <= 6, "tile shape");
-  static_assert(STAGES * LP::SLAB <= 160 * 1024, "LDS");
+  static_assert(A_GROUPS % 8 == 0 && B_GROUPS % 8 == 0, "loads split evenly over the waves");
+  static_assert(AST >= 2 && BST >= AST && BST <= 6, "stages");
+  static_assert(AST * A_SLAB + BST * B_SLAB <= 160 * 1024, "LDS");
+  constexpr int LA = A_GROUPS / 8, LB = B_GROUPS / 8;  // loads per wave per slab
 
-  __shared__ __attribute__((aligned(1024))) char smem[STAGES * LP::SLAB];
+  __shared__ __attribute__((aligned(1024))) char smem[AST * A_SLAB + BST * B_SLAB];
+  char *const sA = smem;
+  char *const sB = smem + AST * A_SLAB;
 
   const int lb = logical_block();
   const int job = lb / p.tiles_per_job;
@@ -162,41 +143,36 @@ __global__ __launch_bounds__(512) void gemm_jobs_kernel(const GemmParams p) {
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
 
-  // Direct-to-LDS addressing.  Load group g (A rows first, then B rows) is
-  // issued by wave g % 8 as its (g / 8)-th load; lane l writes position
-  // l % CH of row l / CH of the group, which holds the swizzled K-chunk.
-  const char *src[LP::MAX_PER_WAVE];
-  int dst[LP::MAX_PER_WAVE];
-  const int my_loads = LP::MIN_PER_WAVE + (wave < LP::GROUPS % 8 ? 1 : 0);
+  // Direct-to-LDS addressing: load i of wave w fills the 1 KB group
+  // (8 i + w); lane l writes position l % CH of row l / CH of the group,
+  // which holds the swizzled K-chunk.
+  const char *a_src[LA];
+  const char *b_src[LB];
 #pragma unroll
-  for (int i = 0; i < LP::MAX_PER_WAVE; ++i) {
-    const int g = i * 8 + wave;
-    const int gg = g < LP::GROUPS ? g : 0;
-    const bool is_a = gg < LP::A_GROUPS;
-    const int row = (is_a ? gg : gg - LP::A_GROUPS) * LP::RPG + lane / LP::CH;
-    const int chunk = (lane % LP::CH) ^ ((row / LP::RPB) % LP::CH);
-    if (is_a) {
-      const int r = min(tm0 + row, p.M - 1);
-      src[i] = Abase + ((size_t)r * p.lda + chunk * 8) * 2;
-    } else {
-      const int r = min(tn0 + row, p.N - 1);
-      src[i] = Bbase + ((size_t)r * p.ldb + chunk * 8) * 2;
-    }
-    dst[i] = gg * 1024;  // A groups first, then B groups: B rows start at BM * ROWB
+  for (int i = 0; i < LA; ++i) {
+    const int row = (i * 8 + wave) * RPG + lane / CH;
+    const int chunk = (lane % CH) ^ ((row / RPB) % CH);
+    a_src[i] = Abase + ((size_t)min(tm0 + row, p.M - 1) * p.lda + chunk * 8) * 2;
   }
-  auto issue = [&](int kt) {
-    char *slab = smem + (kt % STAGES) * LP::SLAB;
+#pragma unroll
+  for (int i = 0; i < LB; ++i) {
+    const int row = (i * 8 + wave) * RPG + lane / CH;
+    const int chunk = (lane % CH) ^ ((row / RPB) % CH);
+    b_src[i] = Bbase + ((size_t)min(tn0 + row, p.N - 1) * p.ldb + chunk * 8) * 2;
+  }
+  auto issue_a = [&](int kt) {
+    char *slab = sA + (kt % AST) * A_SLAB;
     const size_t koff = (size_t)kt * BK * 2;
 #pragma unroll
-    for (int i = 0; i < LP::MAX_PER_WAVE; ++i)
-      if (i < LP::MIN_PER_WAVE || i < my_loads)
-        __builtin_amdgcn_global_load_lds((glob_ptr)(src[i] + koff), (lds_ptr)(slab + dst[i]), 16, 0, 0);
+    for (int i = 0; i < LA; ++i)
+      __builtin_amdgcn_global_load_lds((glob_ptr)(a_src[i] + koff), (lds_ptr)(slab + (i * 8 + wave) * 1024), 16, 0, 0);
   };
-  auto wait_for = [&](int rem) {
-    if (LP::MAX_PER_WAVE == LP::MIN_PER_WAVE || my_loads == LP::MAX_PER_WAVE)
-      wait_slabs<LP::MAX_PER_WAVE, STAGES>(rem);
-    else
-      wait_slabs<LP::MIN_PER_WAVE, STAGES>(rem);
+  auto issue_b = [&](int kt) {
+    char *slab = sB + (kt % BST) * B_SLAB;
+    const size_t koff = (size_t)kt * BK * 2;
+#pragma unroll
+    for (int i = 0; i < LB; ++i)
+      __builtin_amdgcn_global_load_lds((glob_ptr)(b_src[i] + koff), (lds_ptr)(slab + (i * 8 + wave) * 1024), 16, 0, 0);
   };
 
   f32x16 acc[TM][TN];
@@ -207,38 +183,64 @@ __global__ __launch_bounds__(512) void gemm_jobs_kernel(const GemmParams p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
+  // Issue order: slab t's A loads go out together with slab t+D's B loads
+  // (D = BST - AST), so B runs D slabs further ahead.  Prologue: B slabs
+  // 0 .. D-1 alone, then the groups (A t, B t+D) for t = 0 .. AST-2.
+  constexpr int D = BST - AST;
   const int KT = p.K / BK;
 #pragma unroll
-  for (int st = 0; st < STAGES - 1; ++st)
-    if (st < KT) issue(st);
+  for (int t = 0; t < D; ++t)
+    if (t < KT) issue_b(t);
+#pragma unroll
+  for (int t = 0; t < AST - 1; ++t) {
+    if (t < KT) issue_a(t);
+    if (t + D < KT) issue_b(t + D);
+  }
 
-  // MFMA operand rows: lane owns row (lane & 31) of each 32-row tile and the
-  // 8-element K group (lane >> 5) of each 16-wide K step.
   const int frow = lane & 31, fgrp = lane >> 5;
-  int a_off[TM], b_off[TN];
+  int a_row[TM], b_row[TN];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) a_off[i] = wm * WTM + i * 32 + frow;
+  for (int i = 0; i < TM; ++i) a_row[i] = wm * WTM + i * 32 + frow;
 #pragma unroll
-  for (int j = 0; j < TN; ++j) b_off[j] = BM + wn * WTN + j * 32 + frow;
+  for (int j = 0; j < TN; ++j) b_row[j] = wn * WTN + j * 32 + frow;
   bf16x8 fa[2][TM], fb[2][TN];
-  auto load_frags = [&](const char *slab, int ks, int set) {
+  auto load_frags = [&](const char *slab_a, const char *slab_b, int ks, int set) {
     const int chunk = ks * 2 + fgrp;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) fa[set][i] = *reinterpret_cast<const bf16x8 *>(slab + lds_pos<BK>(a_off[i], chunk));
+    for (int i = 0; i < TM; ++i)
+      fa[set][i] = *reinterpret_cast<const bf16x8 *>(slab_a + a_row[i] * ROWB + ((chunk ^ ((a_row[i] / RPB) % CH)) << 4));
 #pragma unroll
-    for (int j = 0; j < TN; ++j) fb[set][j] = *reinterpret_cast<const bf16x8 *>(slab + lds_pos<BK>(b_off[j], chunk));
+    for (int j = 0; j < TN; ++j)
+      fb[set][j] = *reinterpret_cast<const bf16x8 *>(slab_b + b_row[j] * ROWB + ((chunk ^ ((b_row[j] / RPB) % CH)) << 4));
   };
   for (int kt = 0; kt < KT; ++kt) {
-    // slab kt has landed (for every wave) and slab kt-1 is no longer read
-    wait_for(min(STAGES - 2, KT - 1 - kt));
+    // Slab kt's A loads must have landed; they complete in issue order, so
+    // slab kt's B loads (issued earlier when D > 0) have too.  Loads younger
+    // than A kt may stay outstanding: B kt+D (when D > 0) and the groups
+    // (A t, B t+D) for t = kt+1 .. kt+AST-2 that were issued.
+    {
+      int allow = (D > 0 && kt + D < KT) ? LB : 0;
+      const int younger_groups = min(AST - 2, KT - 1 - kt);
+      for (int t = kt + 1; t <= kt + younger_groups; ++t) allow += LA + (t + D < KT ? LB : 0);
+      switch (allow) {
+#define CM_WAIT_CASE(n) case n: wait_vmcnt<n>(); break;
+        CM_WAIT_CASE(0) CM_WAIT_CASE(1) CM_WAIT_CASE(2) CM_WAIT_CASE(3) CM_WAIT_CASE(4) CM_WAIT_CASE(5)
+        CM_WAIT_CASE(6) CM_WAIT_CASE(7) CM_WAIT_CASE(8) CM_WAIT_CASE(9) CM_WAIT_CASE(10) CM_WAIT_CASE(11)
+        CM_WAIT_CASE(12) CM_WAIT_CASE(13) CM_WAIT_CASE(14) CM_WAIT_CASE(15) CM_WAIT_CASE(16)
+#undef CM_WAIT_CASE
+        default: wait_vmcnt<0>(); break;
+      }
+    }
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
-    const char *slab = smem + (kt % STAGES) * LP::SLAB;
-    load_frags(slab, 0, 0);
+    if (kt + AST - 1 < KT) issue_a(kt + AST - 1);
+    if (kt + AST - 1 + D < KT) issue_b(kt + AST - 1 + D);
+    const char *slab_a = sA + (kt % AST) * A_SLAB;
+    const char *slab_b = sB + (kt % BST) * B_SLAB;
+    load_frags(slab_a, slab_b, 0, 0);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      if (ks + 1 < KS) load_frags(slab, ks + 1, (ks + 1) & 1);
+      if (ks + 1 < KS) load_frags(slab_a, slab_b, ks + 1, (ks + 1) & 1);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -308,12 +310,12 @@ bool gemm_tile_supported(int tm, int tn) {
 
 bool gemm_launch_config(const GemmParams &p, int tm, int tn, KernelLaunch *out) {
   void *f = nullptr;
-  if (tm == 256 && tn == 256) f = reinterpret_cast<void *>(&gemm_jobs_kernel<256, 256, 2, 4, 64, 2>);
-  else if (tm == 256 && tn == 192) f = reinterpret_cast<void *>(&gemm_jobs_kernel<256, 192, 4, 2, 64, 2>);
-  else if (tm == 256 && tn == 128) f = reinterpret_cast<void *>(&gemm_jobs_kernel<256, 128, 4, 2, 64, 3>);
-  else if (tm == 128 && tn == 256) f = reinterpret_cast<void *>(&gemm_jobs_kernel<128, 256, 2, 4, 64, 3>);
-  else if (tm == 128 && tn == 128) f = reinterpret_cast<void *>(&gemm_jobs_kernel<128, 128, 2, 4, 64, 4>);
-  else if (tm == 64 && tn == 256) f = reinterpret_cast<void *>(&gemm_jobs_kernel<64, 256, 2, 4, 64, 4>);
+  if (tm == 256 && tn == 256) f = reinterpret_cast<void *>(&gemm_jobs_kernel<256, 256, 2, 4, 64, 2, 3>);
+  else if (tm == 256 && tn == 192) f = reinterpret_cast<void *>(&gemm_jobs_kernel<256, 192, 4, 2, 64, 2, 4>);
+  else if (tm == 256 && tn == 128) f = reinterpret_cast<void *>(&gemm_jobs_kernel<256, 128, 4, 2, 64, 2, 5>);
+  else if (tm == 128 && tn == 256) f = reinterpret_cast<void *>(&gemm_jobs_kernel<128, 256, 2, 4, 64, 2, 3>);
+  else if (tm == 128 && tn == 128) f = reinterpret_cast<void *>(&gemm_jobs_kernel<128, 128, 2, 4, 64, 3, 4>);
+  else if (tm == 64 && tn == 256) f = reinterpret_cast<void *>(&gemm_jobs_kernel<64, 256, 2, 4, 64, 2, 3>);
   if (!f) return false;
   out->func = f;
   out->grid = dim3(p.n_jobs * p.tiles_per_job);
