@@ -109,8 +109,7 @@ template <int BM, int BN, int WM, int WN, int BK, int AST, int BST>
 __global__ __launch_bounds__(512) void gemm_jobs_kernel(const GemmParams p) {
   // A (activations, shared by every tile of a job and mostly served from L2)
   // and B (weights, streamed from HBM once per launch) have separate LDS
-  // rings: AST slabs of A, BST slabs of B.  B's ring is deeper, so the
-  // weight stream is requested BST-AST slabs further ahead of its use.
+  // rings of AST and BST slabs, so each stream gets its own prefetch depth.
   constexpr int WTM = BM / WM, WTN = BN / WN;  // wave sub-tile
   constexpr int TM = WTM / 32, TN = WTN / 32;  // MFMA tiles per wave
   constexpr int KS = BK / 16;                   // MFMA K steps per slab
@@ -121,7 +120,7 @@ __global__ __launch_bounds__(512) void gemm_jobs_kernel(const GemmParams p) {
   static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "tile shape");
   static_assert(BK == 32 || BK == 64, "slab depth");
   static_assert(A_GROUPS % 8 == 0 && B_GROUPS % 8 == 0, "loads split evenly over the waves");
-  static_assert(AST >= 2 && BST >= AST && BST <= 6, "stages");
+  static_assert(AST >= 2 && BST >= 2 && AST <= 6 && BST <= 6, "stages");
   static_assert(AST * A_SLAB + BST * B_SLAB <= 160 * 1024, "LDS");
   constexpr int LA = A_GROUPS / 8, LB = B_GROUPS / 8;  // loads per wave per slab
 
@@ -183,19 +182,35 @@ __global__ __launch_bounds__(512) void gemm_jobs_kernel(const GemmParams p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  // Issue order: slab t's A loads go out together with slab t+D's B loads
-  // (D = BST - AST), so B runs D slabs further ahead.  Prologue: B slabs
-  // 0 .. D-1 alone, then the groups (A t, B t+D) for t = 0 .. AST-2.
-  constexpr int D = BST - AST;
+  // Issue schedule: iteration j (j >= 0, and the prologue as j < 0) issues
+  // A slab j+AST-1 and then B slab j+BST-1, so A runs AST-1 slabs ahead of
+  // its use and B runs BST-1 slabs ahead.
   const int KT = p.K / BK;
+  constexpr int LEAD = (AST > BST ? AST : BST) - 1;
+  auto issue_iter = [&](int j) {
+    if (j + AST - 1 >= 0 && j + AST - 1 < KT) issue_a(j + AST - 1);
+    if (j + BST - 1 >= 0 && j + BST - 1 < KT) issue_b(j + BST - 1);
+  };
 #pragma unroll
-  for (int t = 0; t < D; ++t)
-    if (t < KT) issue_b(t);
-#pragma unroll
-  for (int t = 0; t < AST - 1; ++t) {
-    if (t < KT) issue_a(t);
-    if (t + D < KT) issue_b(t + D);
-  }
+  for (int j = -LEAD; j < 0; ++j) issue_iter(j);
+  // Loads issued after both of slab kt's loads, when iteration kt starts:
+  // they may stay outstanding (loads complete in issue order).
+  auto younger_than = [&](int kt) -> int {
+    const int ja = kt - AST + 1, jb = kt - BST + 1;  // iterations that issued A kt, B kt
+    int allow = 0;
+    int first;  // first iteration all of whose loads are younger
+    if (ja > jb) {  // A kt is the later one; B of the same iteration follows it
+      if (ja + BST - 1 < KT) allow += LB;
+      first = ja + 1;
+    } else {
+      first = jb + 1;
+    }
+    for (int j = first; j < kt; ++j) {
+      if (j + AST - 1 >= 0 && j + AST - 1 < KT) allow += LA;
+      if (j + BST - 1 >= 0 && j + BST - 1 < KT) allow += LB;
+    }
+    return allow;
+  };
 
   const int frow = lane & 31, fgrp = lane >> 5;
   int a_row[TM], b_row[TN];
@@ -214,27 +229,19 @@ __global__ __launch_bounds__(512) void gemm_jobs_kernel(const GemmParams p) {
       fb[set][j] = *reinterpret_cast<const bf16x8 *>(slab_b + b_row[j] * ROWB + ((chunk ^ ((b_row[j] / RPB) % CH)) << 4));
   };
   for (int kt = 0; kt < KT; ++kt) {
-    // Slab kt's A loads must have landed; they complete in issue order, so
-    // slab kt's B loads (issued earlier when D > 0) have too.  Loads younger
-    // than A kt may stay outstanding: B kt+D (when D > 0) and the groups
-    // (A t, B t+D) for t = kt+1 .. kt+AST-2 that were issued.
-    {
-      int allow = (D > 0 && kt + D < KT) ? LB : 0;
-      const int younger_groups = min(AST - 2, KT - 1 - kt);
-      for (int t = kt + 1; t <= kt + younger_groups; ++t) allow += LA + (t + D < KT ? LB : 0);
-      switch (allow) {
+    switch (younger_than(kt)) {
 #define CM_WAIT_CASE(n) case n: wait_vmcnt<n>(); break;
-        CM_WAIT_CASE(0) CM_WAIT_CASE(1) CM_WAIT_CASE(2) CM_WAIT_CASE(3) CM_WAIT_CASE(4) CM_WAIT_CASE(5)
-        CM_WAIT_CASE(6) CM_WAIT_CASE(7) CM_WAIT_CASE(8) CM_WAIT_CASE(9) CM_WAIT_CASE(10) CM_WAIT_CASE(11)
-        CM_WAIT_CASE(12) CM_WAIT_CASE(13) CM_WAIT_CASE(14) CM_WAIT_CASE(15) CM_WAIT_CASE(16)
+      CM_WAIT_CASE(0) CM_WAIT_CASE(1) CM_WAIT_CASE(2) CM_WAIT_CASE(3) CM_WAIT_CASE(4) CM_WAIT_CASE(5)
+      CM_WAIT_CASE(6) CM_WAIT_CASE(7) CM_WAIT_CASE(8) CM_WAIT_CASE(9) CM_WAIT_CASE(10) CM_WAIT_CASE(11)
+      CM_WAIT_CASE(12) CM_WAIT_CASE(13) CM_WAIT_CASE(14) CM_WAIT_CASE(15) CM_WAIT_CASE(16) CM_WAIT_CASE(17)
+      CM_WAIT_CASE(18) CM_WAIT_CASE(19) CM_WAIT_CASE(20) CM_WAIT_CASE(21) CM_WAIT_CASE(22) CM_WAIT_CASE(23)
+      CM_WAIT_CASE(24)
 #undef CM_WAIT_CASE
-        default: wait_vmcnt<0>(); break;
-      }
+      default: wait_vmcnt<0>(); break;
     }
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (kt + AST - 1 < KT) issue_a(kt + AST - 1);
-    if (kt + AST - 1 + D < KT) issue_b(kt + AST - 1 + D);
+    issue_iter(kt);
     const char *slab_a = sA + (kt % AST) * A_SLAB;
     const char *slab_b = sB + (kt % BST) * B_SLAB;
     load_frags(slab_a, slab_b, 0, 0);
