@@ -91,6 +91,7 @@ def measure(args, workload, steps, warmup, with_naive, with_trace):
     buffers.check_inputs(plan_ag, x, w1, y1, ws1)
     buffers.check_inputs(plan_rs, h, w2, y2, ws2)
     compute = torch.cuda.Stream()
+    compute.wait_stream(torch.cuda.current_stream())  # inputs were written on the current stream
     comm = buffers.comm_streams(n_comm)
     flops_op = 2.0 * N * T * d * fN  # each op: N ranks x [T x d] . [d x f/N]
     flops_step = 2 * flops_op

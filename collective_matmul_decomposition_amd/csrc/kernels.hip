@@ -27,6 +27,7 @@ namespace collmm {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void *lds_ptr;
 typedef __attribute__((address_space(1))) void *glob_ptr;
 
@@ -105,8 +106,8 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int AST, int BST>
-__global__ __launch_bounds__(512) void gemm_jobs_kernel(const GemmParams p) {
+template <int BM, int BN, int WM, int WN, int BK, int AST, int BST, int NL, int LP>
+__global__ __launch_bounds__(512 + 64 * NL) void gemm_jobs_kernel(const GemmParams p) {
   // A (activations, shared by every tile of a job and mostly served from L2)
   // and B (weights, streamed from HBM once per launch) have separate LDS
   // rings of AST and BST slabs, so each stream gets its own prefetch depth.
@@ -119,10 +120,21 @@ __global__ __launch_bounds__(512) void gemm_jobs_kernel(const GemmParams p) {
   static_assert(WM * WN == 8, "eight waves");
   static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "tile shape");
   static_assert(BK == 32 || BK == 64, "slab depth");
-  static_assert(A_GROUPS % 8 == 0 && B_GROUPS % 8 == 0, "loads split evenly over the waves");
+  // NL = 0: the eight MFMA waves also issue the loads.  NL > 0: NL extra
+  // waves issue every load and the eight MFMA waves never wait on the vector
+  // memory pipe (a wave that issues a load behind a full address queue
+  // stalls, and with it the MFMAs queued behind the load).
+  constexpr int NLW = NL > 0 ? NL : 8;  // waves that issue loads
+  static_assert(NL == 0 || NL == 2 || NL == 4, "loader waves");
+  // LP = 0: loads go straight to LDS (global_load_lds).  LP = 1: the loader
+  // waves load into two register sets and store to LDS with ds_write (two
+  // LDS slabs per operand; the weights use non-temporal loads).
+  static_assert(LP == 0 || (NL > 0 && AST == 2 && BST == 2), "register-staged loads need loader waves and 2 slabs");
+  static_assert(A_GROUPS % NLW == 0 && B_GROUPS % NLW == 0, "loads split evenly over the waves");
   static_assert(AST >= 2 && BST >= 2 && AST <= 6 && BST <= 6, "stages");
   static_assert(AST * A_SLAB + BST * B_SLAB <= 160 * 1024, "LDS");
-  constexpr int LA = A_GROUPS / 8, LB = B_GROUPS / 8;  // loads per wave per slab
+  constexpr int LA = A_GROUPS / NLW, LB = B_GROUPS / NLW;  // loads per loading wave per slab
+  static_assert((LA + LB) * ((AST > BST ? AST : BST) - 1) < 64, "outstanding loads within vmcnt range");
 
   __shared__ __attribute__((aligned(1024))) char smem[AST * A_SLAB + BST * B_SLAB];
   char *const sA = smem;
@@ -141,37 +153,41 @@ __global__ __launch_bounds__(512) void gemm_jobs_kernel(const GemmParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
+  const bool loader = NL == 0 || wave >= 8;  // this wave issues loads
+  const int lw = NL == 0 ? wave : (wave >= 8 ? wave - 8 : 0);  // its index among the loading waves
 
-  // Direct-to-LDS addressing: load i of wave w fills the 1 KB group
-  // (8 i + w); lane l writes position l % CH of row l / CH of the group,
+  // Direct-to-LDS addressing: load i of loading wave w fills the 1 KB group
+  // (NLW i + w); lane l writes position l % CH of row l / CH of the group,
   // which holds the swizzled K-chunk.
-  const char *a_src[LA];
-  const char *b_src[LB];
+  // Byte offsets from the job's A and B base (each operand of a job spans
+  // less than 4 GiB; the planner rejects larger shapes).
+  uint32_t a_src[LA];
+  uint32_t b_src[LB];
 #pragma unroll
   for (int i = 0; i < LA; ++i) {
-    const int row = (i * 8 + wave) * RPG + lane / CH;
+    const int row = (i * NLW + lw) * RPG + lane / CH;
     const int chunk = (lane % CH) ^ ((row / RPB) % CH);
-    a_src[i] = Abase + ((size_t)min(tm0 + row, p.M - 1) * p.lda + chunk * 8) * 2;
+    a_src[i] = ((uint32_t)min(tm0 + row, p.M - 1) * (uint32_t)p.lda + chunk * 8) * 2;
   }
 #pragma unroll
   for (int i = 0; i < LB; ++i) {
-    const int row = (i * 8 + wave) * RPG + lane / CH;
+    const int row = (i * NLW + lw) * RPG + lane / CH;
     const int chunk = (lane % CH) ^ ((row / RPB) % CH);
-    b_src[i] = Bbase + ((size_t)min(tn0 + row, p.N - 1) * p.ldb + chunk * 8) * 2;
+    b_src[i] = ((uint32_t)min(tn0 + row, p.N - 1) * (uint32_t)p.ldb + chunk * 8) * 2;
   }
   auto issue_a = [&](int kt) {
     char *slab = sA + (kt % AST) * A_SLAB;
-    const size_t koff = (size_t)kt * BK * 2;
+    const uint32_t koff = (uint32_t)kt * BK * 2;
 #pragma unroll
     for (int i = 0; i < LA; ++i)
-      __builtin_amdgcn_global_load_lds((glob_ptr)(a_src[i] + koff), (lds_ptr)(slab + (i * 8 + wave) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((glob_ptr)(Abase + (a_src[i] + koff)), (lds_ptr)(slab + (i * NLW + lw) * 1024), 16, 0, 0);
   };
   auto issue_b = [&](int kt) {
     char *slab = sB + (kt % BST) * B_SLAB;
-    const size_t koff = (size_t)kt * BK * 2;
+    const uint32_t koff = (uint32_t)kt * BK * 2;
 #pragma unroll
     for (int i = 0; i < LB; ++i)
-      __builtin_amdgcn_global_load_lds((glob_ptr)(b_src[i] + koff), (lds_ptr)(slab + (i * 8 + wave) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((glob_ptr)(Bbase + (b_src[i] + koff)), (lds_ptr)(slab + (i * NLW + lw) * 1024), 16, 0, 0);
   };
 
   f32x16 acc[TM][TN];
@@ -191,8 +207,6 @@ __global__ __launch_bounds__(512) void gemm_jobs_kernel(const GemmParams p) {
     if (j + AST - 1 >= 0 && j + AST - 1 < KT) issue_a(j + AST - 1);
     if (j + BST - 1 >= 0 && j + BST - 1 < KT) issue_b(j + BST - 1);
   };
-#pragma unroll
-  for (int j = -LEAD; j < 0; ++j) issue_iter(j);
   // Loads issued after both of slab kt's loads, when iteration kt starts:
   // they may stay outstanding (loads complete in issue order).
   auto younger_than = [&](int kt) -> int {
@@ -228,20 +242,18 @@ __global__ __launch_bounds__(512) void gemm_jobs_kernel(const GemmParams p) {
     for (int j = 0; j < TN; ++j)
       fb[set][j] = *reinterpret_cast<const bf16x8 *>(slab_b + b_row[j] * ROWB + ((chunk ^ ((b_row[j] / RPB) % CH)) << 4));
   };
-  for (int kt = 0; kt < KT; ++kt) {
+  auto wait_slab = [&](int kt) {
     switch (younger_than(kt)) {
 #define CM_WAIT_CASE(n) case n: wait_vmcnt<n>(); break;
-      CM_WAIT_CASE(0) CM_WAIT_CASE(1) CM_WAIT_CASE(2) CM_WAIT_CASE(3) CM_WAIT_CASE(4) CM_WAIT_CASE(5)
-      CM_WAIT_CASE(6) CM_WAIT_CASE(7) CM_WAIT_CASE(8) CM_WAIT_CASE(9) CM_WAIT_CASE(10) CM_WAIT_CASE(11)
-      CM_WAIT_CASE(12) CM_WAIT_CASE(13) CM_WAIT_CASE(14) CM_WAIT_CASE(15) CM_WAIT_CASE(16) CM_WAIT_CASE(17)
-      CM_WAIT_CASE(18) CM_WAIT_CASE(19) CM_WAIT_CASE(20) CM_WAIT_CASE(21) CM_WAIT_CASE(22) CM_WAIT_CASE(23)
-      CM_WAIT_CASE(24)
+#define CM_WAIT_8(b) CM_WAIT_CASE(b) CM_WAIT_CASE(b + 1) CM_WAIT_CASE(b + 2) CM_WAIT_CASE(b + 3) \
+      CM_WAIT_CASE(b + 4) CM_WAIT_CASE(b + 5) CM_WAIT_CASE(b + 6) CM_WAIT_CASE(b + 7)
+      CM_WAIT_8(0) CM_WAIT_8(8) CM_WAIT_8(16) CM_WAIT_8(24) CM_WAIT_8(32) CM_WAIT_8(40) CM_WAIT_8(48) CM_WAIT_8(56)
+#undef CM_WAIT_8
 #undef CM_WAIT_CASE
       default: wait_vmcnt<0>(); break;
     }
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    issue_iter(kt);
+  };
+  auto compute_slab = [&](int kt) {
     const char *slab_a = sA + (kt % AST) * A_SLAB;
     const char *slab_b = sB + (kt % BST) * B_SLAB;
     load_frags(slab_a, slab_b, 0, 0);
@@ -253,6 +265,82 @@ __global__ __launch_bounds__(512) void gemm_jobs_kernel(const GemmParams p) {
 #pragma unroll
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][i], fb[ks & 1][j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // Barrier kt separates the reads of slab kt-1 (every MFMA wave is past
+  // them) from the loads issued after it into that slab's buffer, and makes
+  // slab kt, which every loading wave waited for before it, visible.
+  if (LP == 0 && loader) {
+#pragma unroll
+    for (int j = -LEAD; j < 0; ++j) issue_iter(j);
+  }
+  if (NL == 0) {
+    for (int kt = 0; kt < KT; ++kt) {
+      wait_slab(kt);
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      issue_iter(kt);
+      compute_slab(kt);
+    }
+  } else if (loader && LP == 0) {
+    for (int kt = 0; kt < KT; ++kt) {
+      wait_slab(kt);
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      issue_iter(kt);
+    }
+    return;
+  } else if (loader) {
+    // Slab j is loaded into register set j % 2 two iterations before it is
+    // stored to LDS slab j % 2 (during iteration j - 1, while slab j - 1 is
+    // multiplied); the loads of slab j + 2 reuse the set right after.
+    i32x4 ra[2][LA], rb[2][LB];
+    auto gload = [&](int kt, int set) {
+      if (kt < KT) {
+        const uint32_t koff = (uint32_t)kt * BK * 2;
+#pragma unroll
+        for (int i = 0; i < LA; ++i) ra[set][i] = *reinterpret_cast<const i32x4 *>(Abase + (a_src[i] + koff));
+#pragma unroll
+        for (int i = 0; i < LB; ++i)
+          rb[set][i] = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(Bbase + (b_src[i] + koff)));
+      }
+    };
+    auto lstore = [&](int kt, int set) {
+      if (kt < KT) {
+        char *slab_a = sA + (kt & 1) * A_SLAB + lane * 16;
+        char *slab_b = sB + (kt & 1) * B_SLAB + lane * 16;
+#pragma unroll
+        for (int i = 0; i < LA; ++i) *reinterpret_cast<i32x4 *>(slab_a + (i * NLW + lw) * 1024) = ra[set][i];
+#pragma unroll
+        for (int i = 0; i < LB; ++i) *reinterpret_cast<i32x4 *>(slab_b + (i * NLW + lw) * 1024) = rb[set][i];
+      }
+    };
+    gload(0, 0);
+    gload(1, 1);
+    lstore(0, 0);
+    gload(2, 0);
+    for (int kt = 0; kt < KT; kt += 2) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      lstore(kt + 1, 1);
+      gload(kt + 3, 1);
+      if (kt + 1 < KT) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        lstore(kt + 2, 0);
+        gload(kt + 4, 0);
+      }
+    }
+    return;
+  } else {
+    for (int kt = 0; kt < KT; ++kt) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      compute_slab(kt);
     }
   }
 
@@ -315,18 +403,25 @@ bool gemm_tile_supported(int tm, int tn) {
   return gemm_launch_config(p, tm, tn, &L);
 }
 
+template <int BM, int BN, int WM, int WN, int BK, int AST, int BST, int NL, int LP = 0>
+void pick_gemm(void **f, int *threads) {
+  *f = reinterpret_cast<void *>(&gemm_jobs_kernel<BM, BN, WM, WN, BK, AST, BST, NL, LP>);
+  *threads = 512 + 64 * NL;
+}
+
 bool gemm_launch_config(const GemmParams &p, int tm, int tn, KernelLaunch *out) {
   void *f = nullptr;
-  if (tm == 256 && tn == 256) f = reinterpret_cast<void *>(&gemm_jobs_kernel<256, 256, 2, 4, 64, 2, 3>);
-  else if (tm == 256 && tn == 192) f = reinterpret_cast<void *>(&gemm_jobs_kernel<256, 192, 4, 2, 64, 2, 4>);
-  else if (tm == 256 && tn == 128) f = reinterpret_cast<void *>(&gemm_jobs_kernel<256, 128, 4, 2, 64, 2, 5>);
-  else if (tm == 128 && tn == 256) f = reinterpret_cast<void *>(&gemm_jobs_kernel<128, 256, 2, 4, 64, 2, 3>);
-  else if (tm == 128 && tn == 128) f = reinterpret_cast<void *>(&gemm_jobs_kernel<128, 128, 2, 4, 64, 3, 4>);
-  else if (tm == 64 && tn == 256) f = reinterpret_cast<void *>(&gemm_jobs_kernel<64, 256, 2, 4, 64, 2, 3>);
+  int threads = 0;
+  if (tm == 256 && tn == 256) pick_gemm<256, 256, 2, 4, 64, 2, 3, 0>(&f, &threads);
+  else if (tm == 256 && tn == 192) pick_gemm<256, 192, 4, 2, 64, 2, 2, 4, 1>(&f, &threads);
+  else if (tm == 256 && tn == 128) pick_gemm<256, 128, 4, 2, 64, 2, 5, 0>(&f, &threads);
+  else if (tm == 128 && tn == 256) pick_gemm<128, 256, 2, 4, 64, 2, 3, 0>(&f, &threads);
+  else if (tm == 128 && tn == 128) pick_gemm<128, 128, 2, 4, 64, 3, 4, 0>(&f, &threads);
+  else if (tm == 64 && tn == 256) pick_gemm<64, 256, 2, 4, 64, 2, 3, 0>(&f, &threads);
   if (!f) return false;
   out->func = f;
   out->grid = dim3(p.n_jobs * p.tiles_per_job);
-  out->block = dim3(512);
+  out->block = dim3(threads);
   return true;
 }
 

@@ -152,6 +152,11 @@ cm_status validate_desc(const cm_plan_desc &d) {
   if (d.m < 1 || d.k < 64 || d.n < 64) { set_error("need m >= 1, k >= 64, n >= 64 (got m=%d k=%d n=%d)", d.m, d.k, d.n); return CM_ERR_SHAPE; }
   if (d.k % 64 || d.n % 64) { set_error("k (%d) and n (%d) must be multiples of 64", d.k, d.n); return CM_ERR_SHAPE; }
   if ((long long)d.n_ranks * d.m > (1 << 24)) { set_error("N*m too large"); return CM_ERR_SHAPE; }
+  if ((long long)d.n_ranks * d.m * d.k * 2 > 0xFFFFFFFFll || (long long)d.n * d.k * 2 > 0xFFFFFFFFll) {
+    set_error("an operand of one virtual rank exceeds 4 GiB (N*m*k*2 = %lld, n*k*2 = %lld bytes)",
+              (long long)d.n_ranks * d.m * d.k * 2, (long long)d.n * d.k * 2);
+    return CM_ERR_SHAPE;
+  }
   if (d.copy_gbps < 0 || d.mfma_tflops < 0 || d.launch_us < 0) { set_error("cost-model inputs must be >= 0"); return CM_ERR_INVALID_ARG; }
   if (d.exec_mode != CM_EXEC_GRAPH && d.exec_mode != CM_EXEC_EAGER) { set_error("unknown exec_mode %d", d.exec_mode); return CM_ERR_INVALID_ARG; }
   if ((d.tile_m || d.tile_n) && !tile_known(d.tile_m, d.tile_n)) {

@@ -149,9 +149,10 @@ typedef struct {
 } cm_plan;
 
 /*
- * Build a plan.  Fails with CM_ERR_SHAPE unless: N*m rows; k and n are
- * multiples of 64; AG: c divides m; RS: c divides n and n/c is a multiple
- * of 64; PIPE: same as RS.  Host only: makes no HIP call.
+ * Build a plan.  Fails with CM_ERR_SHAPE unless: N*m <= 2^24 rows; k and n
+ * are multiples of 64; one virtual rank's operands stay under 4 GiB
+ * (N*m*k*2 and n*k*2 bytes); AG: c divides m; RS: c divides n and n/c is a
+ * multiple of 64; PIPE: same as RS.  Host only: makes no HIP call.
  */
 cm_status cm_ring_plan(const cm_plan_desc *desc, cm_plan *out);
 
