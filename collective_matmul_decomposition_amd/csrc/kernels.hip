@@ -68,19 +68,35 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[TM][TN], const EpiA
     for (int j = 0; j < TN; ++j) {
       const int col = a.col0 + j * 32;
       const bool col_ok = col < a.N;
+      const int colc = min(col, a.N - 1);
+      // Eight elements at a time: their addends are read unconditionally
+      // from clamped (in-bounds) positions before any of them is written
+      // (C may be the buffer that holds in0), so the reads are in flight
+      // together; only the stores are predicated.
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = a.row0 + i * 32 + 8 * (e >> 2) + (e & 3);
-        if (col_ok && row < a.M) {
-          float v = acc[i][j][e];
-          const size_t ii = (size_t)row * a.ld_in + col;
-          if (H0) v += a.In0[ii];
-          if (H1) v += a.In1[ii];
-          const size_t oc = (size_t)row * a.ldc + col;
-          if (F32)
-            reinterpret_cast<float *>(a.C)[oc] = v;
-          else
-            reinterpret_cast<uint16_t *>(a.C)[oc] = (uint16_t)f32_to_bf16_rne(v);
+      for (int h = 0; h < 2; ++h) {
+        float add[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int e = h * 8 + q;
+          const int rowc = min(a.row0 + i * 32 + 8 * (e >> 2) + (e & 3), a.M - 1);
+          const size_t ii = (size_t)rowc * a.ld_in + colc;
+          add[q] = 0.f;
+          if (H0) add[q] = a.In0[ii];
+          if (H1) add[q] += a.In1[ii];
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int e = h * 8 + q;
+          const int row = a.row0 + i * 32 + 8 * (e >> 2) + (e & 3);
+          if (col_ok && row < a.M) {
+            const float v = (H0 || H1) ? acc[i][j][e] + add[q] : acc[i][j][e];
+            const size_t oc = (size_t)row * a.ldc + col;
+            if (F32)
+              reinterpret_cast<float *>(a.C)[oc] = v;
+            else
+              reinterpret_cast<uint16_t *>(a.C)[oc] = (uint16_t)f32_to_bf16_rne(v);
+          }
         }
       }
     }
@@ -106,7 +122,24 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int AST, int BST, int NL, int LP>
+// Wait until at most n (0..63) of this wave's vector-memory loads are
+// outstanding; the count is an immediate, hence the switch.
+__device__ __forceinline__ void wait_vmcnt_upto(int n) {
+  switch (n) {
+#define CM_WAIT_CASE(k) case k: wait_vmcnt<k>(); break;
+#define CM_WAIT_8(b) CM_WAIT_CASE(b) CM_WAIT_CASE(b + 1) CM_WAIT_CASE(b + 2) CM_WAIT_CASE(b + 3) \
+  CM_WAIT_CASE(b + 4) CM_WAIT_CASE(b + 5) CM_WAIT_CASE(b + 6) CM_WAIT_CASE(b + 7)
+    CM_WAIT_8(0) CM_WAIT_8(8) CM_WAIT_8(16) CM_WAIT_8(24) CM_WAIT_8(32) CM_WAIT_8(40) CM_WAIT_8(48) CM_WAIT_8(56)
+#undef CM_WAIT_8
+#undef CM_WAIT_CASE
+    default: wait_vmcnt<0>(); break;
+  }
+}
+
+// ADD: the launch has jobs that add in0/in1 in the epilogue.  Launches
+// without addends get their own instantiation, whose register allocation
+// is not sized for the addend reads.
+template <int BM, int BN, int WM, int WN, int BK, int AST, int BST, int NL, int LP, bool ADD>
 __global__ __launch_bounds__(512 + 64 * NL) void gemm_jobs_kernel(const GemmParams p) {
   // A (activations, shared by every tile of a job and mostly served from L2)
   // and B (weights, streamed from HBM once per launch) have separate LDS
@@ -126,10 +159,11 @@ __global__ __launch_bounds__(512 + 64 * NL) void gemm_jobs_kernel(const GemmPara
   // stalls, and with it the MFMAs queued behind the load).
   constexpr int NLW = NL > 0 ? NL : 8;  // waves that issue loads
   static_assert(NL == 0 || NL == 2 || NL == 4, "loader waves");
-  // LP = 0: loads go straight to LDS (global_load_lds).  LP = 1: the loader
-  // waves load into two register sets and store to LDS with ds_write (two
-  // LDS slabs per operand; the weights use non-temporal loads).
-  static_assert(LP == 0 || (NL > 0 && AST == 2 && BST == 2), "register-staged loads need loader waves and 2 slabs");
+  // LP = 0: loads go straight to LDS (global_load_lds).  LP >= 2: the
+  // loader waves load into LP register sets (LP slabs ahead) and store to
+  // a ring of AST = BST LDS slabs with ds_write, AST - 1 slabs ahead of use;
+  // the weights use non-temporal loads.
+  static_assert(LP == 0 || (LP >= 2 && NL > 0 && AST == BST), "register-staged loads need loader waves and equal slab rings");
   static_assert(A_GROUPS % NLW == 0 && B_GROUPS % NLW == 0, "loads split evenly over the waves");
   static_assert(AST >= 2 && BST >= 2 && AST <= 6 && BST <= 6, "stages");
   static_assert(AST * A_SLAB + BST * B_SLAB <= 160 * 1024, "LDS");
@@ -180,14 +214,14 @@ __global__ __launch_bounds__(512 + 64 * NL) void gemm_jobs_kernel(const GemmPara
     const uint32_t koff = (uint32_t)kt * BK * 2;
 #pragma unroll
     for (int i = 0; i < LA; ++i)
-      __builtin_amdgcn_global_load_lds((glob_ptr)(Abase + (a_src[i] + koff)), (lds_ptr)(slab + (i * NLW + lw) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((glob_ptr)((Abase + koff) + a_src[i]), (lds_ptr)(slab + (i * NLW + lw) * 1024), 16, 0, 0);
   };
   auto issue_b = [&](int kt) {
     char *slab = sB + (kt % BST) * B_SLAB;
     const uint32_t koff = (uint32_t)kt * BK * 2;
 #pragma unroll
     for (int i = 0; i < LB; ++i)
-      __builtin_amdgcn_global_load_lds((glob_ptr)(Bbase + (b_src[i] + koff)), (lds_ptr)(slab + (i * NLW + lw) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((glob_ptr)((Bbase + koff) + b_src[i]), (lds_ptr)(slab + (i * NLW + lw) * 1024), 16, 0, 0);
   };
 
   f32x16 acc[TM][TN];
@@ -242,17 +276,7 @@ __global__ __launch_bounds__(512 + 64 * NL) void gemm_jobs_kernel(const GemmPara
     for (int j = 0; j < TN; ++j)
       fb[set][j] = *reinterpret_cast<const bf16x8 *>(slab_b + b_row[j] * ROWB + ((chunk ^ ((b_row[j] / RPB) % CH)) << 4));
   };
-  auto wait_slab = [&](int kt) {
-    switch (younger_than(kt)) {
-#define CM_WAIT_CASE(n) case n: wait_vmcnt<n>(); break;
-#define CM_WAIT_8(b) CM_WAIT_CASE(b) CM_WAIT_CASE(b + 1) CM_WAIT_CASE(b + 2) CM_WAIT_CASE(b + 3) \
-      CM_WAIT_CASE(b + 4) CM_WAIT_CASE(b + 5) CM_WAIT_CASE(b + 6) CM_WAIT_CASE(b + 7)
-      CM_WAIT_8(0) CM_WAIT_8(8) CM_WAIT_8(16) CM_WAIT_8(24) CM_WAIT_8(32) CM_WAIT_8(40) CM_WAIT_8(48) CM_WAIT_8(56)
-#undef CM_WAIT_8
-#undef CM_WAIT_CASE
-      default: wait_vmcnt<0>(); break;
-    }
-  };
+  auto wait_slab = [&](int kt) { wait_vmcnt_upto(younger_than(kt)); };
   auto compute_slab = [&](int kt) {
     const char *slab_a = sA + (kt % AST) * A_SLAB;
     const char *slab_b = sB + (kt % BST) * B_SLAB;
@@ -292,46 +316,64 @@ __global__ __launch_bounds__(512 + 64 * NL) void gemm_jobs_kernel(const GemmPara
     }
     return;
   } else if (loader) {
-    // Slab j is loaded into register set j % 2 two iterations before it is
-    // stored to LDS slab j % 2 (during iteration j - 1, while slab j - 1 is
-    // multiplied); the loads of slab j + 2 reuse the set right after.
-    i32x4 ra[2][LA], rb[2][LB];
+    // Slab j is loaded into register set j % RS, and stored to LDS slab
+    // j % SB during iteration j - SB + 1 (SB - 1 slabs before it is
+    // multiplied, into the slab the MFMA waves finished in the previous
+    // iteration); its register set then takes the loads of slab j + RS.
+    // The loads are issued by inline asm with explicit waits: the compiler's
+    // own wait insertion, which cannot tell the loop-carried register sets
+    // apart, would drain every outstanding load before each store and leave
+    // only one slab in flight.  The loaded registers feed LDS stores only.
+    constexpr int RS = LP > 0 ? LP : 2, SB = AST;
+    static_assert(RS >= 2 && (LA + LB) * (RS - 1) < 64, "register sets");
+    i32x4 ra[RS][LA], rb[RS][LB];
     auto gload = [&](int kt, int set) {
       if (kt < KT) {
         const uint32_t koff = (uint32_t)kt * BK * 2;
+        const char *a = Abase + koff;
+        const char *b = Bbase + koff;
 #pragma unroll
-        for (int i = 0; i < LA; ++i) ra[set][i] = *reinterpret_cast<const i32x4 *>(Abase + (a_src[i] + koff));
+        for (int i = 0; i < LA; ++i)
+          asm volatile("global_load_dwordx4 %0, %1, %2" : "=v"(ra[set][i]) : "v"(a_src[i]), "s"(a) : "memory");
 #pragma unroll
         for (int i = 0; i < LB; ++i)
-          rb[set][i] = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(Bbase + (b_src[i] + koff)));
+          asm volatile("global_load_dwordx4 %0, %1, %2 nt" : "=v"(rb[set][i]) : "v"(b_src[i]), "s"(b) : "memory");
       }
     };
+    // Store slab j: first wait until only the loads of slabs j+1 .. j+RS-1
+    // (those that exist) are outstanding, then wait for the stores, which
+    // also frees the register set for new loads.
     auto lstore = [&](int kt, int set) {
       if (kt < KT) {
-        char *slab_a = sA + (kt & 1) * A_SLAB + lane * 16;
-        char *slab_b = sB + (kt & 1) * B_SLAB + lane * 16;
+        int younger = 0;
+#pragma unroll
+        for (int q = 1; q < RS; ++q) younger += (kt + q < KT) ? LA + LB : 0;
+        wait_vmcnt_upto(younger);
+        char *slab_a = sA + (kt % SB) * A_SLAB + lane * 16;
+        char *slab_b = sB + (kt % SB) * B_SLAB + lane * 16;
 #pragma unroll
         for (int i = 0; i < LA; ++i) *reinterpret_cast<i32x4 *>(slab_a + (i * NLW + lw) * 1024) = ra[set][i];
 #pragma unroll
         for (int i = 0; i < LB; ++i) *reinterpret_cast<i32x4 *>(slab_b + (i * NLW + lw) * 1024) = rb[set][i];
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       }
     };
-    gload(0, 0);
-    gload(1, 1);
-    lstore(0, 0);
-    gload(2, 0);
-    for (int kt = 0; kt < KT; kt += 2) {
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      lstore(kt + 1, 1);
-      gload(kt + 3, 1);
-      if (kt + 1 < KT) {
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        lstore(kt + 2, 0);
-        gload(kt + 4, 0);
+#pragma unroll
+    for (int j = 0; j < RS; ++j) gload(j, j);
+#pragma unroll
+    for (int j = 0; j < SB - 1; ++j) {
+      lstore(j, j % RS);
+      gload(j + RS, j % RS);
+    }
+    for (int kt = 0; kt < KT; kt += RS) {
+#pragma unroll
+      for (int u = 0; u < RS; ++u) {
+        if (kt + u < KT) {
+          __builtin_amdgcn_s_barrier();
+          asm volatile("" ::: "memory");
+          lstore(kt + u + SB - 1, (u + SB - 1) % RS);
+          gload(kt + u + SB - 1 + RS, (u + SB - 1) % RS);
+        }
       }
     }
     return;
@@ -357,6 +399,13 @@ __global__ __launch_bounds__(512 + 64 * NL) void gemm_jobs_kernel(const GemmPara
   ea.row0 = tm0 + wm * WTM + 4 * fgrp;
   ea.col0 = tn0 + wn * WTN + (lane & 31);
   const int mode = (p.c_f32 ? 1 : 0) | (((sel >> 6) & 1) << 1) | (((sel >> 7) & 1) << 2);
+  if (!ADD) {
+    if (mode & 1)
+      epilogue<TM, TN, true, false, false>(acc, ea);
+    else
+      epilogue<TM, TN, false, false, false>(acc, ea);
+    return;
+  }
   switch (mode) {
     case 0: epilogue<TM, TN, false, false, false>(acc, ea); break;
     case 1: epilogue<TM, TN, true, false, false>(acc, ea); break;
@@ -404,20 +453,23 @@ bool gemm_tile_supported(int tm, int tn) {
 }
 
 template <int BM, int BN, int WM, int WN, int BK, int AST, int BST, int NL, int LP = 0>
-void pick_gemm(void **f, int *threads) {
-  *f = reinterpret_cast<void *>(&gemm_jobs_kernel<BM, BN, WM, WN, BK, AST, BST, NL, LP>);
+void pick_gemm(bool add, void **f, int *threads) {
+  *f = add ? reinterpret_cast<void *>(&gemm_jobs_kernel<BM, BN, WM, WN, BK, AST, BST, NL, LP, true>)
+           : reinterpret_cast<void *>(&gemm_jobs_kernel<BM, BN, WM, WN, BK, AST, BST, NL, LP, false>);
   *threads = 512 + 64 * NL;
 }
 
 bool gemm_launch_config(const GemmParams &p, int tm, int tn, KernelLaunch *out) {
+  bool add = false;  // does any job read in0 or in1?
+  for (int j = 0; j < p.n_jobs && j < kMaxJobs; ++j) add = add || (p.sel[j] & 0xC0);
   void *f = nullptr;
   int threads = 0;
-  if (tm == 256 && tn == 256) pick_gemm<256, 256, 2, 4, 64, 2, 3, 0>(&f, &threads);
-  else if (tm == 256 && tn == 192) pick_gemm<256, 192, 4, 2, 64, 2, 2, 4, 1>(&f, &threads);
-  else if (tm == 256 && tn == 128) pick_gemm<256, 128, 4, 2, 64, 2, 5, 0>(&f, &threads);
-  else if (tm == 128 && tn == 256) pick_gemm<128, 256, 2, 4, 64, 2, 3, 0>(&f, &threads);
-  else if (tm == 128 && tn == 128) pick_gemm<128, 128, 2, 4, 64, 3, 4, 0>(&f, &threads);
-  else if (tm == 64 && tn == 256) pick_gemm<64, 256, 2, 4, 64, 2, 3, 0>(&f, &threads);
+  if (tm == 256 && tn == 256) pick_gemm<256, 256, 2, 4, 64, 2, 3, 0>(add, &f, &threads);
+  else if (tm == 256 && tn == 192) pick_gemm<256, 192, 4, 2, 64, 2, 2, 4, 2>(add, &f, &threads);
+  else if (tm == 256 && tn == 128) pick_gemm<256, 128, 4, 2, 64, 2, 5, 0>(add, &f, &threads);
+  else if (tm == 128 && tn == 256) pick_gemm<128, 256, 2, 4, 64, 2, 3, 0>(add, &f, &threads);
+  else if (tm == 128 && tn == 128) pick_gemm<128, 128, 2, 4, 64, 3, 4, 0>(add, &f, &threads);
+  else if (tm == 64 && tn == 256) pick_gemm<64, 256, 2, 4, 64, 2, 3, 0>(add, &f, &threads);
   if (!f) return false;
   out->func = f;
   out->grid = dim3(p.n_jobs * p.tiles_per_job);
