@@ -65,6 +65,26 @@ def algorithmic_bytes(op_rec, jobs, out_size):
     return total
 
 
+def profiled_traffic(workload, step_name):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary (profiles/gemm_step_<workload>.md: FETCH_SIZE and WRITE_SIZE
+    scaled by calibration kernels), or None when that summary was taken on
+    other kernel source than the one built now."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gemm_step_%s.md" % workload)
+    src = os.path.join(ROOT, "collective_matmul_decomposition_amd", "csrc", "kernels.hip")
+    try:
+        lines = open(path).read().splitlines()
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    kv = dict(l.split("=", 1) for l in lines if "=" in l and " " not in l)
+    if kv.get("kernel_source_sha256") != sha:
+        return None
+    v = kv.get("traffic_bytes_%s_step" % step_name)
+    return int(v) if v else None
+
+
 def measure(args, workload, steps, warmup, with_naive, with_trace):
     import torch
     from collective_matmul_decomposition_amd import _native as nat
@@ -176,6 +196,7 @@ def measure(args, workload, steps, warmup, with_naive, with_trace):
                      "intensity_flop_per_byte": round(intensity, 1), "ridge_flop_per_byte": round(ridge, 1),
                      "mfma_tflops": round(flops_launch / (avg_us * 1e-6) / 1e12, 1),
                      "hbm_gbps": round(abytes / (avg_us * 1e-6) / 1e9, 1)})
+        roof["traffic"] = profiled_traffic(workload, name)
         res["roofline"] = roof
         res["gemm_launches"] = {
             "%s %dx%dx%d x%d tile %dx%d" % (nm, r, c, dd, j, a, b): {
@@ -274,7 +295,7 @@ def main():
     ap.add_argument("--dir", default="uni", choices=["uni", "bi"])
     ap.add_argument("--rs-op", default="rs", choices=["rs", "rs_pipe"])
     ap.add_argument("--chunks-ag", type=int, default=0)
-    ap.add_argument("--chunks-rs", type=int, default=2, help="RS column chunks (0: cost model)")
+    ap.add_argument("--chunks-rs", type=int, default=1, help="RS column chunks (0: cost model)")
     ap.add_argument("--n-comm", type=int, default=1, help="comm streams (copy lanes) per op")
     ap.add_argument("--tile", default="0x0")
     ap.add_argument("--no-cpu-baseline", action="store_true")
