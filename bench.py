@@ -97,9 +97,9 @@ def measure(args, workload, steps, warmup, with_naive, with_trace):
     n_comm = args.n_comm
     tile = tuple(int(v) for v in args.tile.split("x"))
     plan_ag = nat.cm_ring_plan(op="ag", n_ranks=N, m=m, k=d, n=fN, dir=args.dir, chunks=args.chunks_ag,
-                               out_dtype="bf16", n_comm=n_comm, tile=tile)
+                               out_dtype="bf16", n_comm=n_comm, tile=tile, copy_engine=args.copy_engine)
     plan_rs = nat.cm_ring_plan(op=args.rs_op, n_ranks=N, m=m, k=fN, n=d, dir=args.dir, chunks=args.chunks_rs,
-                               out_dtype="bf16", n_comm=n_comm, tile=tile)
+                               out_dtype="bf16", n_comm=n_comm, tile=tile, copy_engine=args.copy_engine)
     log("%s plans: AG chunks=%d tile=%dx%d ws=%.0fMB | RS(%s) chunks=%d tile=%dx%d ws=%.0fMB | n_comm=%d" % (
         workload, plan_ag.chunks, plan_ag.tile_m, plan_ag.tile_n, plan_ag.ws_bytes / 1e6, args.rs_op,
         plan_rs.chunks, plan_rs.tile_m, plan_rs.tile_n, plan_rs.ws_bytes / 1e6, n_comm))
@@ -218,8 +218,10 @@ def measure(args, workload, steps, warmup, with_naive, with_trace):
         res["overlap"] = ov
 
     if with_naive:
-        pa = nat.cm_ring_plan(op="ag", n_ranks=N, m=m, k=d, n=fN, sched="naive", out_dtype="bf16", n_comm=n_comm)
-        pr = nat.cm_ring_plan(op="rs", n_ranks=N, m=m, k=fN, n=d, sched="naive", out_dtype="bf16", n_comm=n_comm)
+        pa = nat.cm_ring_plan(op="ag", n_ranks=N, m=m, k=d, n=fN, sched="naive", out_dtype="bf16", n_comm=n_comm,
+                              copy_engine=args.copy_engine)
+        pr = nat.cm_ring_plan(op="rs", n_ranks=N, m=m, k=fN, n=d, sched="naive", out_dtype="bf16", n_comm=n_comm,
+                              copy_engine=args.copy_engine)
         yn1, wsn1 = buffers.alloc_outputs(pa)
         yn2, wsn2 = buffers.alloc_outputs(pr)
 
@@ -239,6 +241,87 @@ def measure(args, workload, steps, warmup, with_naive, with_trace):
                         "speedup_of_decomposed": round(nwall * 1e3 / ms_per_step, 3)}
         del yn1, wsn1, yn2, wsn2
     return res
+
+
+def measure_op(op, N, m, k, n, chunks, ring, n_comm, reps, copy_engine="sdma"):
+    """One op alone (no step around it): decomposed time D from the wall clock
+    of `reps` graph replays, GEMM-busy G and hop-busy C from the trace of the
+    same replays, and the naive (all hops, then the monolithic GEMM) time."""
+    import torch
+    from collective_matmul_decomposition_amd import _native as nat
+    from collective_matmul_decomposition_amd import buffers
+    from collective_matmul_decomposition_amd import inputs as gen
+    mk = gen.ag_inputs_torch if op == "ag" else gen.rs_inputs_torch
+    x, w = mk(N, m, k, n, "normal", 0, "cuda")
+    compute = torch.cuda.Stream()
+    compute.wait_stream(torch.cuda.current_stream())
+    comm = buffers.comm_streams(n_comm)
+    fn = nat.cm_ag_gemm if op == "ag" else nat.cm_gemm_rs
+    flops = 2.0 * N * (N * m) * k * n
+    out = {"op": op, "N": N, "m": m, "k": k, "n": n, "ring": ring, "n_comm": n_comm, "copy_engine": copy_engine}
+    for sched in ("decomposed", "naive"):
+        plan = nat.cm_ring_plan(op=op, n_ranks=N, m=m, k=k, n=n, dir=ring, chunks=chunks, sched=sched,
+                                out_dtype="bf16", n_comm=n_comm, copy_engine=copy_engine)
+        y, ws = buffers.alloc_outputs(plan)
+        ops, _ = nat.cm_plan_program(plan)
+        cap = sum(1 for o in ops if o.kind in (nat.CM_OPK_GEMM, nat.CM_OPK_COPY, nat.CM_OPK_REDUCE))
+        traces = [nat.Trace(cap) for _ in range(reps)]
+        for tr in traces:  # builds (and warms) one graph per trace
+            fn(plan, x, w, y, ws, compute, comm, tr)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for tr in traces:
+            fn(plan, x, w, y, ws, compute, comm, tr)
+        torch.cuda.synchronize()
+        wall_us = (time.perf_counter() - t0) / reps * 1e6
+        Gs, Cs, Ts = [], [], []
+        for tr in traces:
+            spans, total = tr.read()
+            Gs.append(union_length([(q[4], q[5]) for q in spans if q[0] == nat.CM_OPK_GEMM]))
+            Cs.append(union_length([(q[4], q[5]) for q in spans if q[0] in (nat.CM_OPK_COPY, nat.CM_OPK_REDUCE)]))
+            Ts.append(total)
+            tr.close()
+        G, C, D = float(np.median(Gs)), float(np.median(Cs)), float(np.median(Ts))
+        if sched == "decomposed":
+            out.update({"chunks": plan.chunks, "tile": "%dx%d" % (plan.tile_m, plan.tile_n),
+                        "declined_by_cost_model": bool(plan.declined),
+                        "decomposed_us": round(D, 1), "wall_us": round(wall_us, 1), "gemm_busy_us": round(G, 1),
+                        "hop_busy_us": round(C, 1), "overlap_efficiency": round(D / max(G, C), 3),
+                        "hidden_fraction": round((G + C - D) / C, 3) if C > 0 else None,
+                        "tflops": round(flops / (D * 1e-6) / 1e12, 1)})
+        else:
+            out.update({"naive_us": round(D, 1), "monolithic_gemm_us": round(G, 1),
+                        "speedup_over_naive": round(D / out["decomposed_us"], 3)})
+        del y, ws
+    del x, w
+    torch.cuda.empty_cache()
+    return out
+
+
+def run_sweep(name, reps, copy_engine):
+    """The small-chunk regime grid (d = 2048, ffn 8192, 1024 tokens, N in
+    {2, 4, 8}, chunks in {1, 2, 4}, AG / RS / pipeline-chunk RS) or the four
+    GEMM + collective pairs of the SP transformer layer (N = 8, 4096 tokens,
+    d = 8192, ffn 28672); one JSON line per case."""
+    cases = []
+    if name == "c4":
+        T, d, f = 1024, 2048, 8192
+        for op in ("ag", "rs", "rs_pipe"):
+            for N in (2, 4, 8):
+                for c in (1, 2, 4):
+                    k, n = (d, f // N) if op == "ag" else (f // N, d)
+                    cases.append((op, N, T // N, k, n, c))
+    else:
+        N, m = 8, 512
+        cases = [("ag", N, m, 8192, 3072, 0), ("rs_pipe", N, m, 1024, 8192, 4), ("ag", N, m, 8192, 3584, 0),
+                 ("rs", N, m, 3584, 8192, 0)]
+    for op, N, m, k, n, c in cases:
+        r = measure_op(op, N, m, k, n, c, "uni", 1, reps, copy_engine)
+        r["sweep"] = name
+        log("%-4s %-7s N=%d c=%d [%dx%d].[%dx%d]^T: D %.1f us (G %.1f, C %.1f, eff %.2f, hidden %s) naive %.1f us -> x%.2f" % (
+            copy_engine, op, N, r["chunks"], m, k, n, k, r["decomposed_us"], r["gemm_busy_us"], r["hop_busy_us"],
+            r["overlap_efficiency"], r["hidden_fraction"], r["naive_us"], r["speedup_over_naive"]))
+        print(json.dumps(r), flush=True)
 
 
 def sampled_parity(res):
@@ -297,11 +380,15 @@ def main():
     ap.add_argument("--chunks-ag", type=int, default=0)
     ap.add_argument("--chunks-rs", type=int, default=1, help="RS column chunks (0: cost model)")
     ap.add_argument("--n-comm", type=int, default=1, help="comm streams (copy lanes) per op")
+    ap.add_argument("--copy-engine", default="sdma", choices=["sdma", "cu"], help="what moves the ring hops")
+    ap.add_argument("--no-alt-copy", action="store_true", help="skip the run with the other copy engine")
     ap.add_argument("--tile", default="0x0")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
     ap.add_argument("--no-naive", action="store_true")
     ap.add_argument("--no-trace", action="store_true", help="time without the per-launch events")
+    ap.add_argument("--sweep", choices=["c4", "c5"], help="instead of the step: the small-chunk grid (c4) or the "
+                    "layer's GEMM + collective pairs (c5), one JSON line per case")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -319,6 +406,10 @@ def main():
         sys.exit(1)
     nat.lib()
 
+    if args.sweep:
+        run_sweep(args.sweep, max(3, args.steps // 2), args.copy_engine)
+        return
+
     if args.calib_copy_mib:
         # plain kernels of known traffic, for scaling the FETCH_SIZE / WRITE_SIZE
         # counters: a fill that writes the buffer, then an fp32 -> bf16 copy
@@ -331,10 +422,21 @@ def main():
     res = measure(args, args.workload, args.steps, args.warmup, not args.no_naive, not args.no_trace)
     parity, arrays = sampled_parity(res)
     cpu = None if args.no_cpu_baseline else cpu_baseline(res, arrays, args.cpu_seconds)
+    del res["tensors"]
+    torch.cuda.empty_cache()
+    alt = None
+    if not args.no_alt_copy:
+        # the same step with the other engine moving the hops
+        alt_args = argparse.Namespace(**vars(args))
+        alt_args.copy_engine = "cu" if args.copy_engine == "sdma" else "sdma"
+        ra = measure(alt_args, args.workload, args.steps, args.warmup, False, not args.no_trace)
+        alt = {"copy_engine": alt_args.copy_engine, "value": round(ra["value"], 2), "unit": "TFLOP/s",
+               "ms_per_step": round(ra["ms_per_step"], 4), "overlap": ra.get("overlap"),
+               "gemm_launches": ra.get("gemm_launches")}
+        del ra
+        torch.cuda.empty_cache()
     secondary = None
     if args.secondary != "none" and args.secondary != args.workload:
-        del res["tensors"]
-        torch.cuda.empty_cache()
         s2 = measure(args, args.secondary, max(5, args.steps // 2), 2, not args.no_naive, not args.no_trace)
         secondary = {"workload": args.secondary, "value": round(s2["value"], 2), "unit": "TFLOP/s",
                      "ms_per_step": round(s2["ms_per_step"], 4),
@@ -356,7 +458,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "virtual_ranks": res["N"], "tokens": res["T"], "hidden": res["d"],
                    "ffn": res["f"], "ffn_per_rank": res["fN"], "ring": args.dir, "rs_variant": args.rs_op,
-                   "n_comm_streams": res["n_comm"], "chunks_ag": res["plan_ag"].chunks,
+                   "n_comm_streams": res["n_comm"], "copy_engine": args.copy_engine, "chunks_ag": res["plan_ag"].chunks,
                    "chunks_rs": res["plan_rs"].chunks,
                    "step": "AllGather->GEMM (fc1) then GEMM->ReduceScatter (fc2), decomposed, bf16 in / fp32 "
                            "accumulate / bf16 out"},
@@ -367,6 +469,7 @@ def main():
         "gemm_launches": res.get("gemm_launches"),
         "naive": res.get("naive"),
         "parity_sampled_err_over_bound": parity,
+        "alt_copy_engine": alt,
         "secondary": secondary,
     }
     print(json.dumps(out), flush=True)

@@ -20,6 +20,7 @@ CM_BF16, CM_F32 = range(2)
 CM_BUF_X, CM_BUF_W, CM_BUF_Y, CM_BUF_WS = range(4)
 CM_OPK_GEMM, CM_OPK_COPY, CM_OPK_RECORD, CM_OPK_WAIT, CM_OPK_REDUCE = range(5)
 CM_EXEC_GRAPH, CM_EXEC_EAGER = range(2)
+CM_COPY_SDMA, CM_COPY_CU = range(2)
 CM_MAX_RANKS, CM_MAX_CHUNKS, CM_MAX_COMM = 64, 16, 32
 
 EXPORTS = ["cm_ring_plan", "cm_workspace_size", "cm_plan_program", "cm_trace_create", "cm_trace_destroy",
@@ -31,7 +32,7 @@ class cm_plan_desc(ctypes.Structure):
                 ("n", ctypes.c_int), ("dir", ctypes.c_int), ("chunks", ctypes.c_int), ("sched", ctypes.c_int),
                 ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int), ("n_comm", ctypes.c_int),
                 ("tile_m", ctypes.c_int), ("tile_n", ctypes.c_int), ("exec_mode", ctypes.c_int),
-                ("copy_gbps", ctypes.c_double),
+                ("copy_engine", ctypes.c_int), ("copy_gbps", ctypes.c_double),
                 ("mfma_tflops", ctypes.c_double), ("launch_us", ctypes.c_double)]
 
 
@@ -132,18 +133,19 @@ _ENUMS = {
     "sched": {"decomposed": CM_SCHED_DECOMPOSED, "naive": CM_SCHED_NAIVE},
     "dtype": {"bf16": CM_BF16, "f32": CM_F32},
     "exec": {"graph": CM_EXEC_GRAPH, "eager": CM_EXEC_EAGER},
+    "copy": {"sdma": CM_COPY_SDMA, "cu": CM_COPY_CU},
 }
 
 
 def make_desc(op, n_ranks, m, k, n, dir="uni", chunks=0, sched="decomposed", out_dtype="bf16", n_comm=1,
-              tile=(0, 0), exec_mode="graph", copy_gbps=0.0, mfma_tflops=0.0, launch_us=0.0):
+              tile=(0, 0), exec_mode="graph", copy_engine="sdma", copy_gbps=0.0, mfma_tflops=0.0, launch_us=0.0):
     """A cm_plan_desc from keyword arguments (strings or enum values)."""
     def e(kind, v):
         return _ENUMS[kind][v] if isinstance(v, str) else int(v)
     return cm_plan_desc(op=e("op", op), n_ranks=n_ranks, m=m, k=k, n=n, dir=e("dir", dir), chunks=chunks,
                         sched=e("sched", sched), in_dtype=CM_BF16, out_dtype=e("dtype", out_dtype),
                         n_comm=n_comm, tile_m=tile[0], tile_n=tile[1], exec_mode=e("exec", exec_mode),
-                        copy_gbps=copy_gbps,
+                        copy_engine=e("copy", copy_engine), copy_gbps=copy_gbps,
                         mfma_tflops=mfma_tflops, launch_us=launch_us)
 
 

@@ -47,15 +47,16 @@ struct Compiled {
   Program prog;
   std::vector<Launch> launches;  // one per GEMM / REDUCE op, in op order
   std::vector<int> launch_of_op; // op index -> launches index (-1 if none)
+  hipMemcpyKind copy_kind = hipMemcpyDeviceToDeviceNoCU;  // ring hops: SDMA or the CU copy kernel
 };
 
 std::string plan_key(const cm_plan &p) {
   // Every field the program depends on (struct padding is not part of it).
   const cm_plan_desc &d = p.desc;
   char buf[512];
-  std::snprintf(buf, sizeof buf, "%d %d %d %d %d %d %d %d %d %d %d %d %d %d %a %a %a|%d %d %d %d %d %d %d %zu",
+  std::snprintf(buf, sizeof buf, "%d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %a %a %a|%d %d %d %d %d %d %d %zu",
                 d.op, d.n_ranks, d.m, d.k, d.n, d.dir, d.chunks, d.sched, d.in_dtype, d.out_dtype, d.n_comm, d.tile_m,
-                d.tile_n, d.exec_mode, d.copy_gbps, d.mfma_tflops,
+                d.tile_n, d.exec_mode, d.copy_engine, d.copy_gbps, d.mfma_tflops,
                 d.launch_us, p.chunks, p.n_steps, p.arc_cw, p.arc_ccw, p.tile_m, p.tile_n, p.n_events, p.ws_bytes);
   return buf;
 }
@@ -188,6 +189,7 @@ cm_status get_compiled(const cm_plan &pl, const Compiled **out) {
   if (cst != CM_OK) return cst;
   auto c = std::make_unique<Compiled>();
   build_program(canon, c->prog);
+  c->copy_kind = canon.desc.copy_engine == CM_COPY_CU ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToDeviceNoCU;
   c->launch_of_op.assign(c->prog.ops.size(), -1);
   for (size_t i = 0; i < c->prog.ops.size(); ++i) {
     const cm_op_rec &o = c->prog.ops[i];
@@ -326,7 +328,7 @@ cm_status enqueue(const Compiled *cp, const std::vector<hipEvent_t> &ev, char *c
       case CM_OPK_COPY: {
         int sp = span_begin(o);
         e = hipMemcpyAsync(base[o.dst_buf] + o.dst_off, base[o.src_buf] + o.src_off, o.bytes,
-                           hipMemcpyDeviceToDeviceNoCU, s);
+                           cp->copy_kind, s);
         if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (ring hop)");
         span_end(sp, o);
         break;
@@ -415,7 +417,7 @@ cm_status build_graph(const Compiled *cp, char *const base[4], int n_streams, cm
     hipGraphNode_t node;
     if (o.kind == CM_OPK_COPY) {
       e = hipGraphAddMemcpyNode1D(&node, graph, frontier[s].data(), frontier[s].size(), base[o.dst_buf] + o.dst_off,
-                                  base[o.src_buf] + o.src_off, o.bytes, hipMemcpyDeviceToDeviceNoCU);
+                                  base[o.src_buf] + o.src_off, o.bytes, cp->copy_kind);
       if (e != hipSuccess) return hip_fail(e, "hipGraphAddMemcpyNode1D (ring hop)");
     } else if (o.kind == CM_OPK_GEMM || o.kind == CM_OPK_REDUCE) {
       const Launch &L = cp->launches[cp->launch_of_op[i]];
@@ -488,7 +490,12 @@ cm_status run(const cm_plan *pl, bool want_ag, const void *x, const void *w, voi
   auto it = ts.graphs.find(key);
   hipError_t e;
   if (it == ts.graphs.end()) {
-    if (ts.graphs.size() >= kMaxGraphs) ts.graphs.clear();
+    if (ts.graphs.size() >= kMaxGraphs) {
+      // Evict every cached graph; a graph launched earlier may still be
+      // executing, so wait for the device before destroying them.
+      if ((e = hipDeviceSynchronize()) != hipSuccess) return hip_fail(e, "hipDeviceSynchronize (graph cache)");
+      ts.graphs.clear();
+    }
     auto g = std::make_unique<GraphEntry>();
     if ((st = build_graph(cp, base, n_comm + 1, trace, g.get())) != CM_OK) return st;
     it = ts.graphs.emplace(key, std::move(g)).first;
@@ -509,9 +516,15 @@ void forget_graphs_of(const cm_trace *t) {
   char tag[32];
   std::snprintf(tag, sizeof tag, " %p", (const void *)t);
   auto &g = tls().graphs;
+  auto ends_with_tag = [&](const std::string &k) {
+    return k.size() >= std::strlen(tag) && k.compare(k.size() - std::strlen(tag), std::string::npos, tag) == 0;
+  };
+  bool any = false;
+  for (const auto &kv : g) any = any || ends_with_tag(kv.first);
+  if (!any) return;
+  (void)hipDeviceSynchronize();  // a launch of one of these graphs may still be running
   for (auto it = g.begin(); it != g.end();) {
-    const std::string &k = it->first;
-    if (k.size() >= std::strlen(tag) && k.compare(k.size() - std::strlen(tag), std::string::npos, tag) == 0)
+    if (ends_with_tag(it->first))
       it = g.erase(it);
     else
       ++it;

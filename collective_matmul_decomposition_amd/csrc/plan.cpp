@@ -55,7 +55,8 @@ int mod(int a, int n) { return ((a % n) + n) % n; }
 // library (graph replay): the hop rate one comm lane sustains with large
 // copies, the step GEMM's rate at a full, well-shaped launch, and the fixed
 // cost of one graph node (kernel or copy).
-constexpr double kDefaultCopyGBps = 100.0;
+constexpr double kDefaultCopyGBps = 100.0;    // one SDMA lane
+constexpr double kDefaultCuCopyGBps = 1000.0; // the CU copy kernel
 constexpr double kDefaultMfmaTflops = 900.0;
 constexpr double kDefaultLaunchUs = 20.0;
 
@@ -159,6 +160,7 @@ cm_status validate_desc(const cm_plan_desc &d) {
   }
   if (d.copy_gbps < 0 || d.mfma_tflops < 0 || d.launch_us < 0) { set_error("cost-model inputs must be >= 0"); return CM_ERR_INVALID_ARG; }
   if (d.exec_mode != CM_EXEC_GRAPH && d.exec_mode != CM_EXEC_EAGER) { set_error("unknown exec_mode %d", d.exec_mode); return CM_ERR_INVALID_ARG; }
+  if (d.copy_engine != CM_COPY_SDMA && d.copy_engine != CM_COPY_CU) { set_error("unknown copy_engine %d", d.copy_engine); return CM_ERR_INVALID_ARG; }
   if ((d.tile_m || d.tile_n) && !tile_known(d.tile_m, d.tile_n)) {
     set_error("no GEMM tile %dx%d (choose 256x256, 256x192, 256x128, 128x256, 128x128, 64x256 or 0x0)", d.tile_m,
               d.tile_n);
@@ -232,7 +234,7 @@ Est estimate(const cm_plan_desc &d, int c) {
 cm_status plan(const cm_plan_desc *desc, cm_plan *out) {
   if (!desc || !out) { set_error("null argument"); return CM_ERR_INVALID_ARG; }
   cm_plan_desc d = *desc;
-  if (d.copy_gbps == 0) d.copy_gbps = kDefaultCopyGBps;
+  if (d.copy_gbps == 0) d.copy_gbps = d.copy_engine == CM_COPY_CU ? kDefaultCuCopyGBps : kDefaultCopyGBps;
   if (d.mfma_tflops == 0) d.mfma_tflops = kDefaultMfmaTflops;
   if (d.launch_us == 0) d.launch_us = kDefaultLaunchUs;
   cm_status st = validate_desc(d);

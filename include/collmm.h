@@ -92,17 +92,25 @@ typedef enum { CM_BF16 = 0, CM_F32 = 1 } cm_dtype;
 
 /*
  * CM_EXEC_GRAPH: the first call with a given plan, set of buffers and trace
- * builds the program as a HIP graph (kernel and SDMA memcpy nodes whose edges
+ * builds the program as a HIP graph (kernel and memcpy nodes whose edges
  * are the program's stream order and event waits); that call and every later
  * identical call launch the graph on the compute stream with one host call.
  * The comm streams are then not used (the graph's copy nodes run on the
- * copy engines directly).  CM_EXEC_EAGER: every call enqueues the program op
+ * engine that copy_engine names).  CM_EXEC_EAGER: every call enqueues the program op
  * by op on the compute and comm streams.  Both run the same operations with
  * the same ordering; the graph form avoids the host-side cost of enqueueing
  * SDMA copies behind cross-stream waits.  Up to 256 graphs are cached per
  * host thread.
  */
 typedef enum { CM_EXEC_GRAPH = 0, CM_EXEC_EAGER = 1 } cm_exec_mode;
+
+/*
+ * Which engine moves a ring hop.  CM_COPY_SDMA (the default): the system DMA
+ * copy engines (hipMemcpyDeviceToDeviceNoCU), which use no compute units.
+ * CM_COPY_CU: the runtime's copy kernel (hipMemcpyDeviceToDevice), which
+ * runs on compute units beside the GEMMs.  The two give identical results.
+ */
+typedef enum { CM_COPY_SDMA = 0, CM_COPY_CU = 1 } cm_copy_engine;
 
 #define CM_MAX_RANKS 64
 #define CM_MAX_CHUNKS 16
@@ -125,6 +133,7 @@ typedef struct {
   int tile_m;    /* GEMM block tile: 0 x 0 = choose per launch, else one of */
   int tile_n;    /* 256x256, 256x192, 256x128, 128x256, 128x128, 64x256 */
   int exec_mode; /* cm_exec_mode: how the calls enqueue the program */
+  int copy_engine; /* cm_copy_engine: what moves the ring hops */
   /* Cost-model inputs (0 = built-in defaults for MI355X). */
   double copy_gbps;      /* sustained hop bandwidth of ONE comm stream, GB/s */
   double mfma_tflops;    /* sustained bf16 GEMM rate, TFLOP/s */

@@ -43,9 +43,9 @@ def gpu_ready():
 
 
 def run_case(op, N, m, k, n, dist="int", out="f32", dir="uni", chunks=1, sched="decomposed", n_comm=1, seed=0,
-             repeat=1, tile=(0, 0), exec_mode="graph"):
+             repeat=1, tile=(0, 0), exec_mode="graph", copy_engine="sdma"):
     plan = nat.cm_ring_plan(op=op, n_ranks=N, m=m, k=k, n=n, dir=dir, chunks=chunks, sched=sched, out_dtype=out,
-                            n_comm=n_comm, tile=tile, exec_mode=exec_mode)
+                            n_comm=n_comm, tile=tile, exec_mode=exec_mode, copy_engine=copy_engine)
     if op == "ag":
         a, w = gen.ag_inputs(N, m, k, n, dist, seed)
     else:
@@ -97,11 +97,13 @@ for op in ("ag", "rs", "rs_pipe"):
                 TINY.append((op, dir, sched, chunks, dist, out))
 
 
-@pytest.mark.parametrize("exec_mode", ["graph", "eager"])
+@pytest.mark.parametrize("exec_mode,copy_engine", [("graph", "sdma"), ("eager", "sdma"), ("graph", "cu"),
+                                                   ("eager", "cu")])
 @pytest.mark.parametrize("op,dir,sched,chunks,dist,out", TINY)
-def test_tiny_config(op, dir, sched, chunks, dist, out, exec_mode):
-    say("tiny", op, dir, sched, chunks, dist, out, exec_mode)
-    _, a, w, (y,) = run_case(op, 4, 64, 256, 256, dist, out, dir, chunks, sched, n_comm=4, exec_mode=exec_mode)
+def test_tiny_config(op, dir, sched, chunks, dist, out, exec_mode, copy_engine):
+    say("tiny", op, dir, sched, chunks, dist, out, exec_mode, copy_engine)
+    _, a, w, (y,) = run_case(op, 4, 64, 256, 256, dist, out, dir, chunks, sched, n_comm=4, exec_mode=exec_mode,
+                             copy_engine=copy_engine)
     check(op, a, w, y, out, dist)
 
 
@@ -198,42 +200,112 @@ def test_trace_spans():
 
 
 FULL = [
+    # op, N, m, k, n, dir, n_comm, chunks (0 = cost model)
     # Llama-3-8B MLP: N = 8, 4096 tokens, d = 4096, ffn 14336 (f/N = 1792)
-    ("ag", 8, 512, 4096, 1792, "uni"),
-    ("rs", 8, 512, 1792, 4096, "uni"),
-    ("rs_pipe", 8, 512, 1792, 4096, "uni"),
+    ("ag", 8, 512, 4096, 1792, "uni", 8, 0),
+    ("rs", 8, 512, 1792, 4096, "uni", 8, 0),
+    ("rs_pipe", 8, 512, 1792, 4096, "uni", 8, 0),
+    ("ag", 8, 512, 4096, 1792, "uni", 1, 1),
+    ("rs", 8, 512, 1792, 4096, "uni", 1, 1),
     # GPT-3 175B MLP: N = 8, 2048 tokens, d = 12288, ffn 49152 (f/N = 6144)
-    ("ag", 8, 256, 12288, 6144, "uni"),
-    ("ag", 8, 256, 12288, 6144, "bi"),
-    ("rs", 8, 256, 6144, 12288, "uni"),
-    ("rs", 8, 256, 6144, 12288, "bi"),
+    ("ag", 8, 256, 12288, 6144, "uni", 8, 0),
+    ("ag", 8, 256, 12288, 6144, "bi", 16, 0),
+    ("rs", 8, 256, 6144, 12288, "uni", 8, 0),
+    ("rs", 8, 256, 6144, 12288, "bi", 16, 0),
+    # the benchmark's launch configuration: one comm lane, one chunk per op
+    ("ag", 8, 256, 12288, 6144, "uni", 1, 1),
+    ("rs", 8, 256, 6144, 12288, "uni", 1, 1),
+    ("rs", 8, 256, 6144, 12288, "uni", 1, 2),
 ]
+FULL_CU = [("ag", 8, 256, 12288, 6144, "uni", 1, 1), ("rs", 8, 256, 6144, 12288, "uni", 1, 1),
+           ("ag", 8, 512, 4096, 1792, "uni", 1, 1), ("rs", 8, 512, 1792, 4096, "uni", 1, 1)]
 
 
-@pytest.mark.parametrize("op,N,m,k,n,dir", FULL)
-def test_full_size_sampled(op, N, m, k, n, dir):
-    """Full-size shapes in the benchmark's launch configuration; sampled rows against the oracle."""
-    n_comm = 8 if dir == "uni" else 16
-    plan = nat.cm_ring_plan(op=op, n_ranks=N, m=m, k=k, n=n, dir=dir, out_dtype="bf16", n_comm=n_comm)
+def sampled_check(op, N, m, x_t, w_t, y, n_rows, seed=1, exact=False):
+    """Sampled output rows against the oracle: bitwise for integer inputs
+    with fp32 outputs (exact=True), else within the stated bound."""
+    a, w = gen.torch_bf16_to_bits(x_t), gen.torch_bf16_to_bits(w_t)
+    rng = np.random.default_rng(seed)
+    if op == "ag":
+        ranks = rng.integers(0, N, n_rows)
+        rows = rng.integers(0, N * m, n_rows)
+        ref, mag = oracle.ag_gemm_rows(a, w, ranks, rows, with_mag=True)
+        sel = (ranks, rows)
+    else:
+        owners = rng.integers(0, N, n_rows)
+        rows = rng.integers(0, m, n_rows)
+        ref, mag = oracle.gemm_rs_rows(a, w, owners, rows, with_mag=True)
+        sel = (owners, rows)
+    if y.dtype == torch.float32:
+        got = y.cpu().numpy()[sel].astype(np.float64)
+        if exact:
+            assert np.array_equal(got, ref), "max |err| %g" % np.abs(got - ref).max()
+            return
+        bound = 1e-5 * mag
+    else:
+        got = gen.bf16_bits_to_f32(gen.torch_bf16_to_bits(y)[sel]).astype(np.float64)
+        if exact:
+            assert np.array_equal(gen.torch_bf16_to_bits(y)[sel], oracle.round_bf16(ref))
+            return
+        bound = 1e-5 * mag + 2.0 ** -8 * np.abs(ref)
+    err = np.abs(got - ref)
+    assert (err <= bound).all(), "worst err/bound %g" % (err / np.maximum(bound, 1e-300)).max()
+
+
+@pytest.mark.parametrize("op,N,m,k,n,dir,n_comm,chunks,copy_engine",
+                         [f + ("sdma",) for f in FULL] + [f + ("cu",) for f in FULL_CU])
+def test_full_size_sampled(op, N, m, k, n, dir, n_comm, chunks, copy_engine):
+    """Full-size shapes, including the benchmark's launch configuration; sampled rows against the oracle."""
+    plan = nat.cm_ring_plan(op=op, n_ranks=N, m=m, k=k, n=n, dir=dir, chunks=chunks, out_dtype="bf16",
+                            n_comm=n_comm, copy_engine=copy_engine)
     mk = gen.ag_inputs_torch if op == "ag" else gen.rs_inputs_torch
     x_t, w_t = mk(N, m, k, n, "normal", 0, "cuda")
     y, ws = buffers.alloc_outputs(plan)
-    say("full", op, N, m, k, n, dir, "chunks", plan.chunks, "tile", plan.tile_m, plan.tile_n)
-    buffers.run(plan, x_t, w_t, y, ws)
+    say("full", op, N, m, k, n, dir, "n_comm", n_comm, "chunks", plan.chunks, "tile", plan.tile_m, plan.tile_n)
+    buffers.run(plan, x_t, w_t, y, ws, comm=buffers.comm_streams(n_comm))
     torch.cuda.synchronize()
-    a, w = gen.torch_bf16_to_bits(x_t), gen.torch_bf16_to_bits(w_t)
-    rng = np.random.default_rng(1)
-    yb = gen.torch_bf16_to_bits(y)
-    if op == "ag":
-        ranks = rng.integers(0, N, 12)
-        rows = rng.integers(0, N * m, 12)
-        ref, mag = oracle.ag_gemm_rows(a, w, ranks, rows, with_mag=True)
-        got = gen.bf16_bits_to_f32(yb[ranks, rows]).astype(np.float64)
-    else:
-        owners = rng.integers(0, N, 8)
-        rows = rng.integers(0, m, 8)
-        ref, mag = oracle.gemm_rs_rows(a, w, owners, rows, with_mag=True)
-        got = gen.bf16_bits_to_f32(yb[owners, rows]).astype(np.float64)
-    err = np.abs(got - ref)
-    bound = 1e-5 * mag + 2.0 ** -8 * np.abs(ref)
-    assert (err <= bound).all(), "worst err/bound %g" % (err / bound).max()
+    sampled_check(op, N, m, x_t, w_t, y, 12 if op == "ag" else 8)
+
+
+# The small-chunk regime sweep: d = 2048, ffn 8192, 1024 tokens, N in {2, 4, 8}
+# and chunks per shard in {1, 2, 4}, for AG, RS and the pipeline-chunk RS.
+C4 = [(op, N, c) for op in ("ag", "rs", "rs_pipe") for N in (2, 4, 8) for c in (1, 2, 4)]
+
+
+@pytest.mark.parametrize("op,N,c", C4)
+def test_small_chunk_sweep(op, N, c):
+    T, d, f = 1024, 2048, 8192
+    m = T // N
+    k, n = (d, f // N) if op == "ag" else (f // N, d)
+    plan = nat.cm_ring_plan(op=op, n_ranks=N, m=m, k=k, n=n, chunks=c, out_dtype="f32", n_comm=1)
+    say("c4", op, N, c, "tile", plan.tile_m, plan.tile_n)
+    for dist, seed in (("int", 3), ("normal", 4)):
+        if op == "ag":
+            a, w = gen.ag_inputs(N, m, k, n, dist, seed)
+        else:
+            a, w = gen.rs_inputs(N, m, k, n, dist, seed)
+        x_t, w_t = gen.to_torch_bf16(a, "cuda"), gen.to_torch_bf16(w, "cuda")
+        y, ws = buffers.alloc_outputs(plan)
+        buffers.run(plan, x_t, w_t, y, ws, comm=buffers.comm_streams(1))
+        torch.cuda.synchronize()
+        sampled_check(op, N, m, x_t, w_t, y, 16, seed=seed, exact=(dist == "int"))
+
+
+# The four GEMM + collective pairs of the SP transformer layer (N = 8, 4096
+# tokens, d = 8192, 64 heads, ffn 28672): AG->QKV (f/N = 3072 columns of the
+# fused QKV projection), out-proj->pipeline-chunk RS (K = 1024), AG->fc1
+# (3584), fc2->RS (K = 3584).
+C5 = [("ag", 8192, 3072, 0), ("rs_pipe", 1024, 8192, 4), ("ag", 8192, 3584, 0), ("rs", 3584, 8192, 0)]
+
+
+@pytest.mark.parametrize("op,k,n,chunks", C5)
+def test_layer_gemm_pairs(op, k, n, chunks):
+    N, m = 8, 512
+    plan = nat.cm_ring_plan(op=op, n_ranks=N, m=m, k=k, n=n, chunks=chunks, out_dtype="bf16", n_comm=1)
+    mk = gen.ag_inputs_torch if op == "ag" else gen.rs_inputs_torch
+    x_t, w_t = mk(N, m, k, n, "normal", 5, "cuda")
+    y, ws = buffers.alloc_outputs(plan)
+    say("c5", op, k, n, "chunks", plan.chunks, "tile", plan.tile_m, plan.tile_n)
+    buffers.run(plan, x_t, w_t, y, ws, comm=buffers.comm_streams(1))
+    torch.cuda.synchronize()
+    sampled_check(op, N, m, x_t, w_t, y, 12, seed=6)

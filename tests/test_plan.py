@@ -188,8 +188,13 @@ def _gpu_cases():
     for op, dir, chunks in g.MID:
         k, n = (1024, 768) if op == "ag" else (768, 1024)
         cases.append(dict(op=op, n_ranks=8, m=256, k=k, n=n, dir=dir, chunks=chunks, out_dtype="f32", n_comm=8))
-    for op, N, m, k, n, dir in g.FULL:
-        cases.append(dict(op=op, n_ranks=N, m=m, k=k, n=n, dir=dir, out_dtype="bf16", n_comm=8 if dir == "uni" else 16))
+    for op, N, m, k, n, dir, n_comm, chunks in g.FULL:
+        cases.append(dict(op=op, n_ranks=N, m=m, k=k, n=n, dir=dir, chunks=chunks, out_dtype="bf16", n_comm=n_comm))
+    for op, N, c in g.C4:
+        k, n = (2048, 8192 // N) if op == "ag" else (8192 // N, 2048)
+        cases.append(dict(op=op, n_ranks=N, m=1024 // N, k=k, n=n, chunks=c, out_dtype="f32", n_comm=1))
+    for op, k, n, chunks in g.C5:
+        cases.append(dict(op=op, n_ranks=8, m=512, k=k, n=n, chunks=chunks, out_dtype="bf16", n_comm=1))
     for tile in g.TILES:
         for op in ("ag", "rs"):
             for out in ("f32", "bf16"):
