@@ -50,6 +50,8 @@ def _bind(lib):
         f.argtypes = [ci, ci, ci, ci, u16p, u16p, ci, i32p, i32p, f64p, f64p_or_null]
     lib.orc_allreduce.restype = None
     lib.orc_allreduce.argtypes = [ci, ci, ci, ci, u16p, u16p, f64p]
+    lib.orc_gemm_rs_bf16_bucket_rows.restype = None
+    lib.orc_gemm_rs_bf16_bucket_rows.argtypes = [ci, ci, ci, ci, u16p, u16p, ci, ci, i32p, i32p, f64p, f64p_or_null, f64p_or_null]
     lib.orc_round_bf16.restype = None
     lib.orc_round_bf16.argtypes = [f64p, u16p, ctypes.c_size_t]
     return lib
@@ -128,6 +130,40 @@ def gemm_rs_rows(h, w, owners, rows, with_mag=False, lib=None):
     mag = np.empty_like(out) if with_mag else None
     lib.orc_gemm_rs_rows(N, m, k, n, h, w, len(rows), owners, rows, out, _ptr(mag))
     return (out, mag) if with_mag else out
+
+
+def gemm_rs_bf16_bucket_rows(h, w, owners, rows, dir="uni", with_mag=False, lib=None):
+    """GEMM -> ReduceScatter with the circulating bucket rounded to bf16 after
+    every addition (see oracle.c).  Returns out [len(rows), n] (unrounded
+    final sums), and with with_mag also mag (sum |a*w|) and rmag (sum of
+    |bucket| over every rounding)."""
+    lib = lib or load()
+    h, w = _u16(h), _u16(w)
+    N, T, k = h.shape
+    n = w.shape[1]
+    m = T // N
+    owners = np.ascontiguousarray(owners, np.int32)
+    rows = np.ascontiguousarray(rows, np.int32)
+    assert owners.shape == rows.shape and owners.ndim == 1
+    assert ((0 <= owners) & (owners < N)).all() and ((0 <= rows) & (rows < m)).all()
+    out = np.empty((len(rows), n), np.float64)
+    mag = np.empty_like(out) if with_mag else None
+    rmag = np.empty_like(out) if with_mag else None
+    lib.orc_gemm_rs_bf16_bucket_rows(N, m, k, n, h, w, 1 if dir == "bi" else 0, len(rows), owners, rows, out,
+                                     _ptr(mag), _ptr(rmag))
+    return (out, mag, rmag) if with_mag else out
+
+
+def gemm_rs_bf16_bucket(h, w, dir="uni", with_mag=False, lib=None):
+    """Every output row of the bf16-bucket GEMM -> ReduceScatter: [N][m][n]."""
+    N, T, _ = np.asarray(h).shape
+    m, n = T // N, np.asarray(w).shape[1]
+    owners = np.repeat(np.arange(N), m)
+    rows = np.tile(np.arange(m), N)
+    res = gemm_rs_bf16_bucket_rows(h, w, owners, rows, dir, with_mag, lib)
+    if with_mag:
+        return tuple(v.reshape(N, m, n) for v in res)
+    return res.reshape(N, m, n)
 
 
 def allreduce(h, w, lib=None):

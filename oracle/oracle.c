@@ -40,9 +40,16 @@
  *   - "mag" outputs, when not NULL, receive sum_k |a_ik| * |w_jk| over the
  *     same (full) contraction, which scales the floating-point error bound.
  *
+ *   GEMM -> ReduceScatter with a bf16 bucket (the same bucket hand-off, the
+ *   bucket stored in bf16 between hops): the definition above with the
+ *   bucket rounded to bf16 after every addition, in ring order.
+ *
  * Parity pins: see the tests (brute force on tiny shapes, closed forms,
  * N = 1 against a library matmul, the AllReduce invariant, planted
- * mistakes).  The bf16 rounding routine is pinned by hand-derived tie cases.
+ * mistakes).  The bf16 rounding routine is pinned by hand-derived tie cases;
+ * the bf16-bucket chain by a hand-derived fixture with rounding ties, a
+ * brute force in Python integers and its reduction to the fp32 definition
+ * where no rounding can act.
  */
 #include <math.h>
 #include <stdlib.h>
@@ -206,37 +213,105 @@ void orc_allreduce(int N, int m, int k, int n, const uint16_t *h, const uint16_t
 }
 
 /*
- * Round each double to the nearest bfloat16 value, ties to the value whose
- * last significand bit is zero (round-half-to-even), returning bit patterns.
- * bfloat16: 1 sign bit, 8 exponent bits (bias 127), 7 stored significand
- * bits; normal values carry 8 significant bits, so the spacing of values in
- * [2^e, 2^(e+1)) is 2^(e-7); below 2^-126 the spacing is fixed at 2^-133.
- * Magnitudes that round above the largest finite value become infinity.
- * Written from that definition (nearbyint rounds ties to even under the
- * default rounding mode), not from any bit-manipulation shortcut.
+ * Round a double to the nearest bfloat16 value, ties to the value whose last
+ * significand bit is zero (round-half-to-even).  bfloat16: 1 sign bit, 8
+ * exponent bits (bias 127), 7 stored significand bits; normal values carry 8
+ * significant bits, so the spacing of values in [2^e, 2^(e+1)) is 2^(e-7);
+ * below 2^-126 the spacing is fixed at 2^-133.  Magnitudes that round above
+ * the largest finite value become infinity.  Written from that definition
+ * (nearbyint rounds ties to even under the default rounding mode), not from
+ * any bit-manipulation shortcut.
  */
-void orc_round_bf16(const double *in, uint16_t *out, size_t count) {
+static double bf16_round(double v) {
   const double max_finite = ldexp(255.0, 127 - 7); /* (2 - 2^-7) * 2^127 */
+  if (v == 0.0 || isnan(v) || isinf(v)) return v;
+  double a = fabs(v);
+  int e;
+  frexp(a, &e); /* a = f * 2^e with f in [0.5, 1): a in [2^(e-1), 2^e) */
+  int exp2 = e - 1;
+  if (exp2 < -126) exp2 = -126; /* subnormal spacing */
+  double quantum = ldexp(1.0, exp2 - 7);
+  double q = nearbyint(a / quantum) * quantum;
+  if (q > max_finite) q = INFINITY;
+  return v < 0 ? -q : q;
+}
+
+/* The same rounding as bit patterns. */
+void orc_round_bf16(const double *in, uint16_t *out, size_t count) {
   for (size_t t = 0; t < count; ++t) {
-    double v = in[t];
-    double r;
-    if (v == 0.0 || isnan(v) || isinf(v)) {
-      r = v;
-    } else {
-      double a = fabs(v);
-      int e;
-      frexp(a, &e); /* a = f * 2^e with f in [0.5, 1): a in [2^(e-1), 2^e) */
-      int exp2 = e - 1;
-      if (exp2 < -126) exp2 = -126; /* subnormal spacing */
-      double quantum = ldexp(1.0, exp2 - 7);
-      double q = nearbyint(a / quantum) * quantum;
-      if (q > max_finite) q = INFINITY;
-      r = v < 0 ? -q : q;
-    }
+    double r = bf16_round(in[t]);
     float f = (float)r; /* exact: r is a bf16 value, representable in binary32 */
     uint32_t u;
     memcpy(&u, &f, sizeof u);
     if (isnan(r)) u = 0x7FC00000u;
     out[t] = (uint16_t)(u >> 16);
+  }
+}
+
+/*
+ * GEMM -> ReduceScatter with the circulating bucket held in bfloat16 between
+ * hops (half the bytes per hop of an fp32 bucket).  The bucket owned by q is
+ * the accumulator that travels the ring ("The idea" on the decomposition
+ * page; the bucket hand-off of section 4 of the Megatron page): each rank it
+ * visits adds its partial product Z_r[q*m + i, :] and sends it on, so the sum
+ * is stored, and here rounded to bf16, after every addition.  The owner adds
+ * its own partial last; that final sum is returned unrounded (the caller
+ * rounds to the output type).  Partial products are exact (fp64).
+ *   dir 0, one ring:  the bucket visits ranks q+1, q+2, ..., q-1 (mod N).
+ *   dir 1, both ring directions: two buckets, clockwise over ranks q-L, ...,
+ *     q-1 and counter-clockwise over ranks q+R, ..., q+1 (mod N), with
+ *     L = ceil((N-1)/2) and R = floor((N-1)/2); the owner adds its partial
+ *     and both arrivals (the realigning addition).
+ *   owner[s], row[s]: the output row Out_q[i] of sample s; out [ns][n].
+ *   mag [ns][n] or NULL: sum_k |a|*|w| over every rank's contraction.
+ *   rmag [ns][n] or NULL: the sum of |bucket| over every rounded bucket value
+ *     (each rounding moves the value by at most half a bf16 spacing).
+ */
+void orc_gemm_rs_bf16_bucket_rows(int N, int m, int k, int n, const uint16_t *h, const uint16_t *w,
+                                  int dir, int ns, const int *owner, const int *row, double *out,
+                                  double *mag, double *rmag) {
+  const size_t T = (size_t)N * m;
+  const int L = N / 2, R = (N - 1) / 2; /* L = ceil((N-1)/2) */
+#pragma omp parallel
+  {
+    double *z = (double *)malloc(sizeof(double) * 4 * (size_t)n);
+    double *zm = z + n, *b0 = z + 2 * (size_t)n, *b1 = z + 3 * (size_t)n;
+#pragma omp for schedule(dynamic)
+    for (int s = 0; s < ns; ++s) {
+      const int q = owner[s], i = row[s];
+      double *o = out + (size_t)s * n;
+      double *mg = mag ? mag + (size_t)s * n : NULL;
+      double *rm = rmag ? rmag + (size_t)s * n : NULL;
+      for (int j = 0; j < n; ++j) {
+        b0[j] = b1[j] = 0.0;
+        if (mg) mg[j] = 0.0;
+        if (rm) rm[j] = 0.0;
+      }
+      /* one bucket visiting `len` ranks first, first + step, ... */
+      for (int chain = 0; chain < (dir ? 2 : 1); ++chain) {
+        int first, len, step;
+        if (!dir) { first = q + 1; len = N - 1; step = 1; }
+        else if (chain == 0) { first = q - L; len = L; step = 1; }
+        else { first = q + R; len = R; step = -1; }
+        double *b = chain == 0 ? b0 : b1;
+        for (int t = 0; t < len; ++t) {
+          const int r = ((first + t * step) % N + N) % N;
+          row_times_weight(h + ((size_t)r * T + (size_t)q * m + i) * k, w + (size_t)r * n * k, k, n, z,
+                           mg ? zm : NULL);
+          for (int j = 0; j < n; ++j) {
+            b[j] = bf16_round(b[j] + z[j]);
+            if (rm) rm[j] += fabs(b[j]);
+            if (mg) mg[j] += zm[j];
+          }
+        }
+      }
+      row_times_weight(h + ((size_t)q * T + (size_t)q * m + i) * k, w + (size_t)q * n * k, k, n, z,
+                       mg ? zm : NULL);
+      for (int j = 0; j < n; ++j) {
+        o[j] = z[j] + b0[j] + b1[j];
+        if (mg) mg[j] += zm[j];
+      }
+    }
+    free(z);
   }
 }

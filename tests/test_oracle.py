@@ -202,8 +202,77 @@ def check_round_bf16(lib):
     assert np.array_equal(oracle.round_bf16(f.astype(np.float64), lib=lib), gen.f32_to_bf16_bits(f))
 
 
+def check_bf16_bucket_golden(lib):
+    g = json.load(open(os.path.join(GOLDEN, "bf16_bucket_n3.json")))
+    h, w = bits(g["h"]), bits(g["w"])
+    for dir, key in (("uni", "out_uni"), ("bi", "out_bi")):
+        out = oracle.gemm_rs_bf16_bucket(h, w, dir=dir, lib=lib)
+        assert np.array_equal(out, np.array(g[key], np.float64)), (dir, out)
+    assert np.array_equal(oracle.gemm_rs(h, w, lib=lib), np.array(g["out_fp32_bucket"], np.float64))
+
+
+def _brute_bf16_bucket(h, w, dir):
+    """Python-integer partials; the bucket rounded after every addition with the
+    input generator's float32 -> bf16 rounding (exact here: small integers)."""
+    N = len(h)
+    m = len(h[0]) // N
+    n = len(w[0])
+    L, R = -(-(N - 1) // 2), (N - 1) // 2
+
+    def z(r, q, i):
+        return [sum(a * b for a, b in zip(h[r][q * m + i], w[r][j])) for j in range(n)]
+
+    def rnd(v):
+        return [int(x) for x in vals(gen.f32_to_bf16_bits(np.asarray(v, np.float32)))]
+
+    out = []
+    for q in range(N):
+        rows = []
+        for i in range(m):
+            if dir == "uni":
+                chains = [[(q + t) % N for t in range(1, N)]]
+            else:
+                chains = [[(q - L + t) % N for t in range(L)], [(q + R - t) % N for t in range(R)]]
+            total = z(q, q, i)
+            for chain in chains:
+                b = [0] * n
+                for r in chain:
+                    b = rnd([x + y for x, y in zip(b, z(r, q, i))])
+                total = [x + y for x, y in zip(total, b)]
+            rows.append(total)
+        out.append(rows)
+    return out
+
+
+def check_bf16_bucket_brute_force(lib):
+    rng = np.random.default_rng(11)
+    # values large enough that almost every bucket addition rounds
+    for N, m, k, n in ((2, 1, 3, 2), (3, 2, 2, 3), (4, 1, 4, 2), (5, 2, 3, 2), (6, 1, 2, 3), (7, 1, 2, 4)):
+        hv = rng.integers(-60, 61, (N, N * m, k))
+        wv = rng.integers(-60, 61, (N, n, k))
+        for dir in ("uni", "bi"):
+            want = np.array(_brute_bf16_bucket(hv.tolist(), wv.tolist(), dir), np.float64)
+            got = oracle.gemm_rs_bf16_bucket(bits(hv), bits(wv), dir=dir, lib=lib)
+            assert np.array_equal(got, want), (N, m, k, n, dir)
+
+
+def check_bf16_bucket_reductions(lib):
+    """Where no rounding can act, the bf16 bucket is the fp32 definition: one
+    rank (no hops), and integer data whose partial sums stay within +-256."""
+    h, w = gen.rs_inputs(1, 4, 64, 8, "normal", 2)
+    assert np.array_equal(oracle.gemm_rs_bf16_bucket(h, w, lib=lib), oracle.gemm_rs(h, w, lib=lib))
+    rng = np.random.default_rng(5)
+    for N in (2, 3, 4, 7):
+        hv = rng.integers(-2, 3, (N, N * 2, 4))
+        wv = rng.integers(-2, 3, (N, 5, 4))
+        ref = oracle.gemm_rs(bits(hv), bits(wv), lib=lib)
+        for dir in ("uni", "bi"):
+            assert np.array_equal(oracle.gemm_rs_bf16_bucket(bits(hv), bits(wv), dir=dir, lib=lib), ref)
+
+
 ALL_CHECKS = [check_golden, check_brute_force, check_brute_force_fractions, check_n1_matmul,
-              check_closed_forms, check_allreduce_invariant, check_sampled_rows, check_round_bf16]
+              check_closed_forms, check_allreduce_invariant, check_sampled_rows, check_round_bf16,
+              check_bf16_bucket_golden, check_bf16_bucket_brute_force, check_bf16_bucket_reductions]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda c: c.__name__)
@@ -232,6 +301,11 @@ MUTANTS = {
     "reversed_shard_rows": ("int local = i % m;", "int local = m - 1 - i % m;"),
     "dropped_last_term": ("for (int kk = 0; kk < k; ++kk) acc +=", "for (int kk = 0; kk < k - 1; ++kk) acc +="),
     "round_ties_away": ("nearbyint(a / quantum)", "round(a / quantum)"),
+    "bucket_unrounded": ("b[j] = bf16_round(b[j] + z[j]);", "b[j] = b[j] + z[j];"),
+    "bucket_owner_first": ("if (!dir) { first = q + 1; len = N - 1; step = 1; }",
+                           "if (!dir) { first = q; len = N - 1; step = 1; }"),
+    "bucket_final_rounded": ("o[j] = z[j] + b0[j] + b1[j];", "o[j] = bf16_round(z[j] + b0[j] + b1[j]);"),
+    "bucket_ccw_wrong_way": ("else { first = q + R; len = R; step = -1; }", "else { first = q + 1; len = R; step = 1; }"),
 }
 
 
