@@ -99,7 +99,8 @@ def measure(args, workload, steps, warmup, with_naive, with_trace):
     plan_ag = nat.cm_ring_plan(op="ag", n_ranks=N, m=m, k=d, n=fN, dir=args.dir, chunks=args.chunks_ag,
                                out_dtype="bf16", n_comm=n_comm, tile=tile, copy_engine=args.copy_engine)
     plan_rs = nat.cm_ring_plan(op=args.rs_op, n_ranks=N, m=m, k=fN, n=d, dir=args.dir, chunks=args.chunks_rs,
-                               out_dtype="bf16", n_comm=n_comm, tile=tile, copy_engine=args.copy_engine)
+                               out_dtype="bf16", n_comm=n_comm, tile=tile, copy_engine=args.copy_engine,
+                               bucket=args.rs_bucket)
     log("%s plans: AG chunks=%d tile=%dx%d ws=%.0fMB | RS(%s) chunks=%d tile=%dx%d ws=%.0fMB | n_comm=%d" % (
         workload, plan_ag.chunks, plan_ag.tile_m, plan_ag.tile_n, plan_ag.ws_bytes / 1e6, args.rs_op,
         plan_rs.chunks, plan_rs.tile_m, plan_rs.tile_n, plan_rs.ws_bytes / 1e6, n_comm))
@@ -207,7 +208,7 @@ def measure(args, workload, steps, warmup, with_naive, with_trace):
         for name, plan in (("ag", plan_ag), ("rs", plan_rs)):
             arr = np.array(per_op[name])
             D, G, C = np.median(arr[:, 0]), np.median(arr[:, 1]), np.median(arr[:, 2])
-            elt = 2 if name == "ag" else 4
+            elt = 2 if name == "ag" or args.rs_bucket == "bf16" else 4
             ring_bytes = N * (N - 1) * m * d * elt
             ov[name] = {"decomposed_us": round(D, 1), "gemm_busy_us": round(G, 1), "hop_busy_us": round(C, 1),
                         "overlap_efficiency": round(D / max(G, C), 3),
@@ -324,7 +325,7 @@ def run_sweep(name, reps, copy_engine):
         print(json.dumps(r), flush=True)
 
 
-def sampled_parity(res):
+def sampled_parity(res, rs_bucket="f32"):
     import oracle
     from collective_matmul_decomposition_amd import inputs as gen
     x, w1, y1, h, w2, y2 = res["tensors"]
@@ -337,7 +338,11 @@ def sampled_parity(res):
     got = gen.bf16_bits_to_f32(gen.torch_bf16_to_bits(y1)[rk, rw]).astype(np.float64)
     worst_ag = float((np.abs(got - ref) / (1e-5 * mag + 2.0 ** -8 * np.abs(ref))).max())
     qo, qr = rng.integers(0, N, 4), rng.integers(0, m, 4)
-    ref, mag = oracle.gemm_rs_rows(ha, w2a, qo, qr, with_mag=True)
+    if rs_bucket == "bf16":
+        ref, mag, rmag = oracle.gemm_rs_bf16_bucket_rows(ha, w2a, qo, qr, with_mag=True)
+        mag = mag + 2.0 ** -7 / 1e-5 * rmag  # each bucket rounding: up to one bf16 spacing
+    else:
+        ref, mag = oracle.gemm_rs_rows(ha, w2a, qo, qr, with_mag=True)
     got = gen.bf16_bits_to_f32(gen.torch_bf16_to_bits(y2)[qo, qr]).astype(np.float64)
     worst_rs = float((np.abs(got - ref) / (1e-5 * mag + 2.0 ** -8 * np.abs(ref))).max())
     return {"ag": round(worst_ag, 4), "rs": round(worst_rs, 4)}, (xa, w1a, ha, w2a)
@@ -382,6 +387,10 @@ def main():
     ap.add_argument("--n-comm", type=int, default=1, help="comm streams (copy lanes) per op")
     ap.add_argument("--copy-engine", default="sdma", choices=["sdma", "cu"], help="what moves the ring hops")
     ap.add_argument("--no-alt-copy", action="store_true", help="skip the run with the other copy engine")
+    ap.add_argument("--rs-bucket", default="f32", choices=["f32", "bf16"],
+                    help="element type of the circulating RS bucket (bf16: half the hop bytes, outside the "
+                         "fp32-bucket error bound)")
+    ap.add_argument("--no-alt-bucket", action="store_true", help="skip the run with the other RS bucket type")
     ap.add_argument("--tile", default="0x0")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
@@ -420,7 +429,7 @@ def main():
         torch.cuda.synchronize()
         del a, b
     res = measure(args, args.workload, args.steps, args.warmup, not args.no_naive, not args.no_trace)
-    parity, arrays = sampled_parity(res)
+    parity, arrays = sampled_parity(res, args.rs_bucket if args.rs_op == "rs" else "f32")
     cpu = None if args.no_cpu_baseline else cpu_baseline(res, arrays, args.cpu_seconds)
     del res["tensors"]
     torch.cuda.empty_cache()
@@ -434,6 +443,15 @@ def main():
                "ms_per_step": round(ra["ms_per_step"], 4), "overlap": ra.get("overlap"),
                "gemm_launches": ra.get("gemm_launches")}
         del ra
+        torch.cuda.empty_cache()
+    alt_bucket = None
+    if not args.no_alt_bucket and args.rs_op == "rs":
+        alt_args = argparse.Namespace(**vars(args))
+        alt_args.rs_bucket = "bf16" if args.rs_bucket == "f32" else "f32"
+        rb = measure(alt_args, args.workload, args.steps, args.warmup, False, not args.no_trace)
+        alt_bucket = {"rs_bucket": alt_args.rs_bucket, "value": round(rb["value"], 2), "unit": "TFLOP/s",
+                      "ms_per_step": round(rb["ms_per_step"], 4), "overlap": rb.get("overlap")}
+        del rb
         torch.cuda.empty_cache()
     secondary = None
     if args.secondary != "none" and args.secondary != args.workload:
@@ -458,7 +476,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "virtual_ranks": res["N"], "tokens": res["T"], "hidden": res["d"],
                    "ffn": res["f"], "ffn_per_rank": res["fN"], "ring": args.dir, "rs_variant": args.rs_op,
-                   "n_comm_streams": res["n_comm"], "copy_engine": args.copy_engine, "chunks_ag": res["plan_ag"].chunks,
+                   "n_comm_streams": res["n_comm"], "copy_engine": args.copy_engine, "rs_bucket": args.rs_bucket,
+                   "chunks_ag": res["plan_ag"].chunks,
                    "chunks_rs": res["plan_rs"].chunks,
                    "step": "AllGather->GEMM (fc1) then GEMM->ReduceScatter (fc2), decomposed, bf16 in / fp32 "
                            "accumulate / bf16 out"},
@@ -470,6 +489,7 @@ def main():
         "naive": res.get("naive"),
         "parity_sampled_err_over_bound": parity,
         "alt_copy_engine": alt,
+        "alt_rs_bucket": alt_bucket,
         "secondary": secondary,
     }
     print(json.dumps(out), flush=True)

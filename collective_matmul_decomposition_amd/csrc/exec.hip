@@ -95,6 +95,7 @@ cm_status fill_params(const cm_op_rec &o, const cm_job_rec *jobs, Launch &L) {
   p.ldc = j0.ldc;
   p.ld_in = j0.ld_in;
   p.c_f32 = j0.c_dtype == CM_F32;
+  int add_dtype = -1;  // common element type of the addends of the launch
   auto off16 = [&](size_t off, uint32_t *out) -> bool {
     if (off % 16 || off / 16 > 0xFFFFFFFFull) return false;
     *out = (uint32_t)(off / 16);
@@ -114,6 +115,17 @@ cm_status fill_params(const cm_op_rec &o, const cm_job_rec *jobs, Launch &L) {
     }
     ok &= j.c_buf >= 0 && off16(j.c_off, &p.c_off[i]);
     sel |= (uint32_t)(j.c_buf & 3) << 4;
+    if (j.in0_buf >= 0 || j.in1_buf >= 0) {
+      if (add_dtype >= 0 && j.add_dtype != add_dtype) {
+        set_error("jobs of one launch differ in addend type");
+        return CM_ERR_SHAPE;
+      }
+      if (j.add_dtype != CM_F32 && (j.add_dtype != CM_BF16 || o.kind != CM_OPK_GEMM)) {
+        set_error("bad addend type %d", j.add_dtype);
+        return CM_ERR_SHAPE;
+      }
+      add_dtype = j.add_dtype;
+    }
     if (j.in0_buf >= 0) {
       ok &= j.in0_buf == CM_BUF_WS && off16(j.in0_off, &p.in0_off[i]);
       sel |= 1u << 6;
@@ -148,6 +160,7 @@ cm_status fill_params(const cm_op_rec &o, const cm_job_rec *jobs, Launch &L) {
       return CM_ERR_SHAPE;
     }
   }
+  p.add_bf16 = add_dtype == CM_BF16;
   return CM_OK;
 }
 

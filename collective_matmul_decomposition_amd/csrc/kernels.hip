@@ -53,14 +53,23 @@ __device__ __forceinline__ int logical_block() {
 
 struct EpiArgs {
   char *C;
-  const float *In0, *In1;
+  const void *In0, *In1;  // fp32, or bf16 (HB)
   int ldc, ld_in, M, N, row0, col0;
 };
 
 // Store one wave's accumulators: C = acc (+ in0) (+ in1), rounded to bf16
 // when the output is bf16.  Fully unrolled so the accumulators stay in
 // registers.
-template <int TM, int TN, bool F32, bool H0, bool H1>
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Addend element ii of in0 or in1: fp32, or bf16 when HB.
+template <bool HB>
+__device__ __forceinline__ float addend(const void *p, size_t ii) {
+  if (HB) return bf16_to_f32(reinterpret_cast<const uint16_t *>(p)[ii]);
+  return reinterpret_cast<const float *>(p)[ii];
+}
+
+template <int TM, int TN, bool F32, bool H0, bool H1, bool HB>
 __device__ __forceinline__ void epilogue(const f32x16 (&acc)[TM][TN], const EpiArgs &a) {
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -82,8 +91,8 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[TM][TN], const EpiA
           const int rowc = min(a.row0 + i * 32 + 8 * (e >> 2) + (e & 3), a.M - 1);
           const size_t ii = (size_t)rowc * a.ld_in + colc;
           add[q] = 0.f;
-          if (H0) add[q] = a.In0[ii];
-          if (H1) add[q] += a.In1[ii];
+          if (H0) add[q] = addend<HB>(a.In0, ii);
+          if (H1) add[q] += addend<HB>(a.In1, ii);
         }
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
@@ -133,6 +142,21 @@ __device__ __forceinline__ void wait_vmcnt_upto(int n) {
 #undef CM_WAIT_8
 #undef CM_WAIT_CASE
     default: wait_vmcnt<0>(); break;
+  }
+}
+
+// The epilogue variant for one job: mode bit 0 = fp32 output, 1 = in0, 2 = in1.
+template <int TM, int TN, bool HB>
+__device__ __forceinline__ void epilogue_mode(const f32x16 (&acc)[TM][TN], const EpiArgs &ea, int mode) {
+  switch (mode) {
+    case 0: epilogue<TM, TN, false, false, false, HB>(acc, ea); break;
+    case 1: epilogue<TM, TN, true, false, false, HB>(acc, ea); break;
+    case 2: epilogue<TM, TN, false, true, false, HB>(acc, ea); break;
+    case 3: epilogue<TM, TN, true, true, false, HB>(acc, ea); break;
+    case 6: epilogue<TM, TN, false, true, true, HB>(acc, ea); break;
+    case 7: epilogue<TM, TN, true, true, true, HB>(acc, ea); break;
+    case 4: epilogue<TM, TN, false, false, true, HB>(acc, ea); break;
+    default: epilogue<TM, TN, true, false, true, HB>(acc, ea); break;
   }
 }
 
@@ -390,8 +414,8 @@ __global__ __launch_bounds__(512 + 64 * NL) void gemm_jobs_kernel(const GemmPara
   // 8*(e/4) + 4*(lane/32) + e%4 and column lane%32.
   EpiArgs ea;
   ea.C = p.base[(sel >> 4) & 3] + (size_t)p.c_off[job] * 16;
-  ea.In0 = reinterpret_cast<const float *>(p.base[3] + (size_t)p.in0_off[job] * 16);
-  ea.In1 = reinterpret_cast<const float *>(p.base[3] + (size_t)p.in1_off[job] * 16);
+  ea.In0 = p.base[3] + (size_t)p.in0_off[job] * 16;
+  ea.In1 = p.base[3] + (size_t)p.in1_off[job] * 16;
   ea.ldc = p.ldc;
   ea.ld_in = p.ld_in;
   ea.M = p.M;
@@ -401,21 +425,15 @@ __global__ __launch_bounds__(512 + 64 * NL) void gemm_jobs_kernel(const GemmPara
   const int mode = (p.c_f32 ? 1 : 0) | (((sel >> 6) & 1) << 1) | (((sel >> 7) & 1) << 2);
   if (!ADD) {
     if (mode & 1)
-      epilogue<TM, TN, true, false, false>(acc, ea);
+      epilogue<TM, TN, true, false, false, false>(acc, ea);
     else
-      epilogue<TM, TN, false, false, false>(acc, ea);
+      epilogue<TM, TN, false, false, false, false>(acc, ea);
     return;
   }
-  switch (mode) {
-    case 0: epilogue<TM, TN, false, false, false>(acc, ea); break;
-    case 1: epilogue<TM, TN, true, false, false>(acc, ea); break;
-    case 2: epilogue<TM, TN, false, true, false>(acc, ea); break;
-    case 3: epilogue<TM, TN, true, true, false>(acc, ea); break;
-    case 6: epilogue<TM, TN, false, true, true>(acc, ea); break;
-    case 7: epilogue<TM, TN, true, true, true>(acc, ea); break;
-    case 4: epilogue<TM, TN, false, false, true>(acc, ea); break;
-    default: epilogue<TM, TN, true, false, true>(acc, ea); break;
-  }
+  if (p.add_bf16)
+    epilogue_mode<TM, TN, true>(acc, ea, mode);
+  else
+    epilogue_mode<TM, TN, false>(acc, ea, mode);
 }
 
 // C = in0 + in1 over rows x cols per job; 4 columns per thread.

@@ -112,7 +112,7 @@ const char *last_error() { return g_last_error.c_str(); }
 // AG decomposed: receive slots, chunk-major so that one chunk of a range of
 //   ranks is contiguous:  slot[dir][p][j][r][m/c][k] bf16.
 // AG naive: gathered activations G[r][T][k] bf16.
-// RS decomposed: buckets  bkt[dir][p][j][r][m][n/c] fp32.
+// RS decomposed: buckets  bkt[dir][p][j][r][m][n/c] fp32 (bf16 with bucket_bf16).
 // RS pipe / naive: partials P[r][j][T][n/c] fp32, then ring slots
 //   R[p][r][m][n/c] fp32.
 WsLayout ws_layout(const cm_plan &pl) {
@@ -129,7 +129,7 @@ WsLayout ws_layout(const cm_plan &pl) {
       L.total = ndir * L.slot_dir_bytes;
     }
   } else if (d.op == CM_OP_GEMM_RS && d.sched == CM_SCHED_DECOMPOSED) {
-    L.slot_dir_bytes = 2 * N * m * n * 4;  // c chunks of n/c columns
+    L.slot_dir_bytes = 2 * N * m * n * (d.bucket_bf16 ? 2 : 4);  // c chunks of n/c columns
     L.total = ndir * L.slot_dir_bytes;
   } else {  // PIPE, or RS naive (PIPE with one chunk)
     L.partial = 0;
@@ -161,6 +161,11 @@ cm_status validate_desc(const cm_plan_desc &d) {
   if (d.copy_gbps < 0 || d.mfma_tflops < 0 || d.launch_us < 0) { set_error("cost-model inputs must be >= 0"); return CM_ERR_INVALID_ARG; }
   if (d.exec_mode != CM_EXEC_GRAPH && d.exec_mode != CM_EXEC_EAGER) { set_error("unknown exec_mode %d", d.exec_mode); return CM_ERR_INVALID_ARG; }
   if (d.copy_engine != CM_COPY_SDMA && d.copy_engine != CM_COPY_CU) { set_error("unknown copy_engine %d", d.copy_engine); return CM_ERR_INVALID_ARG; }
+  if (d.bucket_bf16 != 0 && d.bucket_bf16 != 1) { set_error("bucket_bf16 must be 0 or 1"); return CM_ERR_INVALID_ARG; }
+  if (d.bucket_bf16 && !(d.op == CM_OP_GEMM_RS && d.sched == CM_SCHED_DECOMPOSED)) {
+    set_error("bf16 buckets exist only for the decomposed GEMM-RS");
+    return CM_ERR_UNSUPPORTED;
+  }
   if ((d.tile_m || d.tile_n) && !tile_known(d.tile_m, d.tile_n)) {
     set_error("no GEMM tile %dx%d (choose 256x256, 256x192, 256x128, 128x256, 128x128, 64x256 or 0x0)", d.tile_m,
               d.tile_n);
@@ -211,7 +216,7 @@ Est estimate(const cm_plan_desc &d, int c) {
     e.hidden = h <= g;
   } else if (d.op == CM_OP_GEMM_RS) {
     const double g = gemm_us(d, d.n_ranks * ndir, m, n / c, k);
-    const double h = hop_us(d, N * m * (n / c) * 4.0 * ndir, lanes, per_lane);
+    const double h = hop_us(d, N * m * (n / c) * (d.bucket_bf16 ? 2.0 : 4.0) * ndir, lanes, per_lane);
     const int steps = bi ? 1 + d.n_ranks / 2 : d.n_ranks;
     e.g = g; e.h = h;
     // GEMM(s+1, j) needs hop(s, j), which starts after GEMM(s, j): a step
@@ -398,6 +403,7 @@ struct Builder {
     cm_job_rec j;
     std::memset(&j, 0, sizeof j);
     j.a_buf = j.b_buf = j.c_buf = j.in0_buf = j.in1_buf = -1;
+    j.add_dtype = CM_F32;
     return j;
   }
   void gemm(const std::vector<cm_job_rec> &jobs, int rows, int cols, int depth) {
@@ -635,7 +641,8 @@ struct Builder {
     const bool bi = d.dir == CM_RING_BI;
     const int ndir = bi ? 2 : 1;
     const size_t nc = n / c;
-    const size_t blk = m * nc * 4;  // one rank's bucket chunk, fp32
+    const int bdt = d.bucket_bf16 ? CM_BF16 : CM_F32;  // bucket element type
+    const size_t blk = m * nc * (d.bucket_bf16 ? 2 : 4);  // one rank's bucket chunk
     const int osz = d.out_dtype == CM_F32 ? 4 : 2;
     auto bkt = [&](int dir, int par, int j, int r) -> size_t {
       return dir * L.slot_dir_bytes + ((((size_t)par * c + j) * N + r) * blk);
@@ -662,6 +669,7 @@ struct Builder {
           jb.a_buf = CM_BUF_X; jb.a_off = ((size_t)r * T + (size_t)bucket * m) * k * 2; jb.lda = (int)k;
           jb.b_buf = CM_BUF_W; jb.b_off = ((size_t)r * n + (size_t)j * nc) * k * 2; jb.ldb = (int)k;
           jb.ld_in = (int)nc;
+          jb.add_dtype = bdt;
           return jb;
         };
         for (int r = 0; r < N; ++r) {
@@ -680,13 +688,13 @@ struct Builder {
           int arc = bi ? Lc : N - 1;
           int q = mod(r + (arc - s), N);
           cm_job_rec jb = mk(r, 0, q);
-          jb.c_buf = CM_BUF_WS; jb.c_off = bkt(0, s % 2, j, r); jb.ldc = (int)nc; jb.c_dtype = CM_F32;
+          jb.c_buf = CM_BUF_WS; jb.c_off = bkt(0, s % 2, j, r); jb.ldc = (int)nc; jb.c_dtype = bdt;
           if (s > 0) { jb.in0_buf = CM_BUF_WS; jb.in0_off = jb.c_off; }
           jobs.push_back(jb);
           if (bi && s >= Lc - R) {
             int qq = mod(r - (Lc - s), N);
             cm_job_rec jc = mk(r, 1, qq);
-            jc.c_buf = CM_BUF_WS; jc.c_off = bkt(1, s % 2, j, r); jc.ldc = (int)nc; jc.c_dtype = CM_F32;
+            jc.c_buf = CM_BUF_WS; jc.c_off = bkt(1, s % 2, j, r); jc.ldc = (int)nc; jc.c_dtype = bdt;
             if (s > Lc - R) { jc.in0_buf = CM_BUF_WS; jc.in0_off = jc.c_off; }
             jobs.push_back(jc);
           }

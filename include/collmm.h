@@ -134,6 +134,11 @@ typedef struct {
   int tile_n;    /* 256x256, 256x192, 256x128, 128x256, 128x128, 64x256 */
   int exec_mode; /* cm_exec_mode: how the calls enqueue the program */
   int copy_engine; /* cm_copy_engine: what moves the ring hops */
+  int bucket_bf16; /* GEMM-RS (decomposed) only: 0 = the circulating bucket is
+                      fp32; 1 = it is stored and sent in bf16 (half the hop
+                      bytes), rounded to nearest-even after every addition,
+                      which adds up to half a bf16 spacing of error per hop
+                      (outside the fp32-bucket error bound) */
   /* Cost-model inputs (0 = built-in defaults for MI355X). */
   double copy_gbps;      /* sustained hop bandwidth of ONE comm stream, GB/s */
   double mfma_tflops;    /* sustained bf16 GEMM rate, TFLOP/s */
@@ -212,6 +217,7 @@ typedef struct {
   size_t a_off, b_off, c_off, in0_off, in1_off;
   int lda, ldb, ldc, ld_in;
   int c_dtype;
+  int add_dtype; /* element type of in0/in1: CM_F32, or CM_BF16 for bf16 buckets */
 } cm_job_rec;
 
 /*

@@ -150,9 +150,10 @@ class Sim:
             if o.kind == nat.CM_OPK_GEMM:
                 r |= {(j.a_buf, int(g)) for g in self._rows(j.a_buf, j.a_off, o.rows, j.lda * 2, o.depth * 2)}
                 r |= {(j.b_buf, int(g)) for g in self._rows(j.b_buf, j.b_off, o.cols, j.ldb * 2, o.depth * 2)}
+            asz = 2 if j.add_dtype == nat.CM_BF16 else 4
             for ib, io in ((j.in0_buf, j.in0_off), (j.in1_buf, j.in1_off)):
                 if ib >= 0:
-                    r |= {(ib, int(g)) for g in self._rows(ib, io, o.rows, j.ld_in * 4, o.cols * 4)}
+                    r |= {(ib, int(g)) for g in self._rows(ib, io, o.rows, j.ld_in * asz, o.cols * asz)}
             esz = 4 if j.c_dtype == nat.CM_F32 else 2
             w = {(j.c_buf, int(g)) for g in self._rows(j.c_buf, j.c_off, o.rows, j.ldc * esz, o.cols * esz)}
             reads.append(r)
@@ -197,10 +198,12 @@ class Sim:
                         A = self._bf16(j.a_buf, j.a_off, o.rows, o.depth, j.lda)
                         B = self._bf16(j.b_buf, j.b_off, o.cols, o.depth, j.ldb)
                         val = A @ B.T
+                    asz = 2 if j.add_dtype == nat.CM_BF16 else 4
                     for ib, io in ((j.in0_buf, j.in0_off), (j.in1_buf, j.in1_off)):
                         if ib >= 0:
-                            self.read(s, ib, self._rows(ib, io, o.rows, j.ld_in * 4, o.cols * 4))
-                            val = val + self._f32(ib, io, o.rows, o.cols, j.ld_in)
+                            self.read(s, ib, self._rows(ib, io, o.rows, j.ld_in * asz, o.cols * asz))
+                            add = self._bf16 if asz == 2 else self._f32
+                            val = val + add(ib, io, o.rows, o.cols, j.ld_in)
                     results.append((j, val))
                 for j, val in results:
                     esz = 4 if j.c_dtype == nat.CM_F32 else 2
@@ -251,10 +254,11 @@ def check_program_bounds(plan, sizes=None):
                     assert o.depth % 64 == 0
                     span(j.a_buf, j.a_off, o.rows, j.lda * 2, o.depth * 2)
                     span(j.b_buf, j.b_off, o.cols, j.ldb * 2, o.depth * 2)
+                asz = 2 if j.add_dtype == nat.CM_BF16 else 4
                 for ib, io in ((j.in0_buf, j.in0_off), (j.in1_buf, j.in1_off)):
                     if ib >= 0:
                         assert ib == nat.CM_BUF_WS
-                        span(ib, io, o.rows, j.ld_in * 4, o.cols * 4)
+                        span(ib, io, o.rows, j.ld_in * asz, o.cols * asz)
                 esz = 4 if j.c_dtype == nat.CM_F32 else 2
                 span(j.c_buf, j.c_off, o.rows, j.ldc * esz, o.cols * esz)
     return len(ops)

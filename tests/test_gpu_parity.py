@@ -309,3 +309,64 @@ def test_layer_gemm_pairs(op, k, n, chunks):
     buffers.run(plan, x_t, w_t, y, ws, comm=buffers.comm_streams(1))
     torch.cuda.synchronize()
     sampled_check(op, N, m, x_t, w_t, y, 12, seed=6)
+
+
+# GEMM -> ReduceScatter with the bucket held in bf16 between hops.  Integer
+# inputs: partial products and bucket sums are exact in fp32, so the GPU
+# rounds the same values the oracle rounds and the result is bitwise equal.
+# Float inputs: the GPU's fp32 partials differ from the exact ones by at most
+# 1e-5 * sum|a*w|, and each bucket rounding can then land on the neighbouring
+# bf16 value, at most one spacing (2^-7 of the value) away; the oracle's
+# rmag sums |bucket| over every rounding.
+BF16B = [
+    # N, m, k, n, dir, chunks, out
+    (4, 64, 256, 256, "uni", 1, "f32"),
+    (4, 64, 256, 256, "bi", 2, "f32"),
+    (5, 100, 128, 448, "bi", 1, "bf16"),
+    (3, 37, 192, 320, "uni", 5, "f32"),
+    (8, 256, 768, 1024, "uni", 2, "f32"),
+    (7, 64, 256, 512, "bi", 2, "bf16"),
+]
+
+
+@pytest.mark.parametrize("N,m,k,n,dir,chunks,out", BF16B)
+def test_bf16_bucket_rs(N, m, k, n, dir, chunks, out):
+    plan = nat.cm_ring_plan(op="rs", n_ranks=N, m=m, k=k, n=n, dir=dir, chunks=chunks, out_dtype=out,
+                            n_comm=2, bucket="bf16")
+    for dist in ("int", "normal"):
+        a, w = gen.rs_inputs(N, m, k, n, dist, 7)
+        x_t, w_t = gen.to_torch_bf16(a, "cuda"), gen.to_torch_bf16(w, "cuda")
+        y, ws = buffers.alloc_outputs(plan)
+        say("bf16 bucket", N, m, k, n, dir, chunks, out, dist)
+        buffers.run(plan, x_t, w_t, y, ws)
+        torch.cuda.synchronize()
+        ref, mag, rmag = oracle.gemm_rs_bf16_bucket(a, w, dir=dir, with_mag=True)
+        if out == "f32":
+            got = y.cpu().numpy().astype(np.float64)
+        else:
+            got = gen.bf16_bits_to_f32(gen.torch_bf16_to_bits(y)).astype(np.float64)
+        if dist == "int":
+            want = ref if out == "f32" else gen.bf16_bits_to_f32(oracle.round_bf16(ref)).astype(np.float64)
+            assert np.array_equal(got, want), "max |err| %g" % np.abs(got - want).max()
+        else:
+            bound = 1e-5 * mag + 2.0 ** -7 * rmag + (2.0 ** -8 * np.abs(ref) if out == "bf16" else 0)
+            err = np.abs(got - ref)
+            assert (err <= bound).all(), "worst err/bound %g" % (err / np.maximum(bound, 1e-300)).max()
+
+
+def test_bf16_bucket_rs_full_size_sampled():
+    """The GPT-3 MLP fc2 step with bf16 buckets (one lane, one chunk, as the benchmark runs it)."""
+    N, m, k, n = 8, 256, 6144, 12288
+    plan = nat.cm_ring_plan(op="rs", n_ranks=N, m=m, k=k, n=n, chunks=1, out_dtype="bf16", n_comm=1, bucket="bf16")
+    x_t, w_t = gen.rs_inputs_torch(N, m, k, n, "normal", 0, "cuda")
+    y, ws = buffers.alloc_outputs(plan)
+    say("bf16 bucket full")
+    buffers.run(plan, x_t, w_t, y, ws, comm=buffers.comm_streams(1))
+    torch.cuda.synchronize()
+    a, w = gen.torch_bf16_to_bits(x_t), gen.torch_bf16_to_bits(w_t)
+    rng = np.random.default_rng(3)
+    owners, rows = rng.integers(0, N, 8), rng.integers(0, m, 8)
+    ref, mag, rmag = oracle.gemm_rs_bf16_bucket_rows(a, w, owners, rows, with_mag=True)
+    got = gen.bf16_bits_to_f32(gen.torch_bf16_to_bits(y)[owners, rows]).astype(np.float64)
+    bound = 1e-5 * mag + 2.0 ** -7 * rmag + 2.0 ** -8 * np.abs(ref)
+    assert (np.abs(got - ref) <= bound).all()

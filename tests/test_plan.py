@@ -26,9 +26,9 @@ from ring_sim import Race, Sim, buffer_sizes
 
 
 def simulate(op, N, m, k, n, dir="uni", chunks=1, sched="decomposed", out="f32", n_comm=1, seed=0, dist="int",
-             data=None):
+             data=None, bucket="f32"):
     plan = nat.cm_ring_plan(op=op, n_ranks=N, m=m, k=k, n=n, dir=dir, chunks=chunks, sched=sched, out_dtype=out,
-                            n_comm=n_comm)
+                            n_comm=n_comm, bucket=bucket)
     if data is None:
         if op == "ag":
             a, w = gen.ag_inputs(N, m, k, n, dist, seed)
@@ -65,6 +65,37 @@ for N in (1, 2, 3, 4, 5, 8):
                                    ("rs", "uni", "naive", 1)]:
         for n_comm in sorted({1, 2, 3, N, 2 * N}):
             CASES.append((op, N, dir, sched, chunks, n_comm))
+
+
+BF16_BUCKET = [(N, dir, chunks, n_comm) for N in (1, 2, 3, 4, 5, 8) for dir in ("uni", "bi")
+               for chunks in (1, 2) for n_comm in sorted({1, N})]
+
+
+@pytest.mark.parametrize("N,dir,chunks,n_comm", BF16_BUCKET)
+def test_bf16_bucket_program_matches_oracle(N, dir, chunks, n_comm):
+    """The bf16-bucket RS program visits the ranks in the order the oracle's
+    definition does: with integer data large enough that nearly every bucket
+    addition rounds, the simulated result equals the oracle's bit for bit."""
+    m, k, n = 3, 64, 64 * chunks
+    rng = np.random.default_rng(100 + N)
+    hv = rng.integers(-40, 41, (N, N * m, k)).astype(np.float32)
+    wv = rng.integers(-40, 41, (N, n, k)).astype(np.float32)
+    data = (gen.f32_to_bf16_bits(hv), gen.f32_to_bf16_bits(wv))
+    plan, sim, a, w = simulate("rs", N, m, k, n, dir, chunks, "decomposed", "f32", n_comm, data=data, bucket="bf16")
+    f32_plan = nat.cm_ring_plan(op="rs", n_ranks=N, m=m, k=k, n=n, dir=dir, chunks=chunks, n_comm=n_comm)
+    assert 2 * plan.ws_bytes == f32_plan.ws_bytes  # half the bucket bytes
+    got = output(sim, plan)
+    ref = oracle.gemm_rs_bf16_bucket(a, w, dir=dir).reshape(-1)
+    assert np.array_equal(got, ref)
+    if N > 2:  # rounding acted: the fp32-bucket result differs
+        assert not np.array_equal(got, oracle.gemm_rs(a, w).reshape(-1))
+    assert (sim.writes[nat.CM_BUF_Y] == 1).all()
+
+
+def test_bf16_bucket_is_only_for_the_decomposed_rs():
+    for kw in (dict(op="ag"), dict(op="rs_pipe", chunks=2), dict(op="rs", sched="naive")):
+        st, _ = nat.cm_ring_plan_status(nat.make_desc(**dict(dict(n_ranks=4, m=8, k=64, n=128, bucket="bf16"), **kw)))
+        assert st == nat.CM_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("op,N,dir,sched,chunks,n_comm", CASES)
@@ -195,6 +226,10 @@ def _gpu_cases():
         cases.append(dict(op=op, n_ranks=N, m=1024 // N, k=k, n=n, chunks=c, out_dtype="f32", n_comm=1))
     for op, k, n, chunks in g.C5:
         cases.append(dict(op=op, n_ranks=8, m=512, k=k, n=n, chunks=chunks, out_dtype="bf16", n_comm=1))
+    for N, m, k, n, dir, chunks, out in g.BF16B:
+        cases.append(dict(op="rs", n_ranks=N, m=m, k=k, n=n, dir=dir, chunks=chunks, out_dtype=out, n_comm=2,
+                          bucket="bf16"))
+    cases.append(dict(op="rs", n_ranks=8, m=256, k=6144, n=12288, chunks=1, out_dtype="bf16", n_comm=1, bucket="bf16"))
     for tile in g.TILES:
         for op in ("ag", "rs"):
             for out in ("f32", "bf16"):
