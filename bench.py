@@ -380,7 +380,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gpt3-175b-mlp", choices=sorted(WORKLOADS))
     ap.add_argument("--secondary", default="llama3-8b-mlp", help="second workload reported beside (or 'none')")
-    ap.add_argument("--dir", default="uni", choices=["uni", "bi"])
+    ap.add_argument("--dir", default="uni", choices=["uni", "bi", "direct"])
     ap.add_argument("--rs-op", default="rs", choices=["rs", "rs_pipe"])
     ap.add_argument("--chunks-ag", type=int, default=0)
     ap.add_argument("--chunks-rs", type=int, default=1, help="RS column chunks (0: cost model)")

@@ -14,8 +14,8 @@ LIB_PATH = os.path.join(PKG, "libcollmm.so")
 CM_OK, CM_ERR_INVALID_ARG, CM_ERR_SHAPE, CM_ERR_ALIGN, CM_ERR_WORKSPACE, CM_ERR_UNSUPPORTED, CM_ERR_HIP, \
     CM_ERR_CAPACITY = range(8)
 CM_OP_AG_GEMM, CM_OP_GEMM_RS, CM_OP_GEMM_RS_PIPE = range(3)
-CM_RING_UNI, CM_RING_BI = range(2)
-CM_SCHED_DECOMPOSED, CM_SCHED_NAIVE = range(2)
+CM_RING_UNI, CM_RING_BI, CM_RING_DIRECT = range(3)
+CM_SCHED_DECOMPOSED, CM_SCHED_NAIVE, CM_SCHED_AUTO = range(3)
 CM_BF16, CM_F32 = range(2)
 CM_BUF_X, CM_BUF_W, CM_BUF_Y, CM_BUF_WS = range(4)
 CM_OPK_GEMM, CM_OPK_COPY, CM_OPK_RECORD, CM_OPK_WAIT, CM_OPK_REDUCE = range(5)
@@ -23,7 +23,7 @@ CM_EXEC_GRAPH, CM_EXEC_EAGER = range(2)
 CM_COPY_SDMA, CM_COPY_CU = range(2)
 CM_MAX_RANKS, CM_MAX_CHUNKS, CM_MAX_COMM = 64, 16, 32
 
-EXPORTS = ["cm_ring_plan", "cm_workspace_size", "cm_plan_program", "cm_trace_create", "cm_trace_destroy",
+EXPORTS = ["cm_ring_plan", "cm_pick_overlap", "cm_workspace_size", "cm_plan_program", "cm_trace_create", "cm_trace_destroy",
            "cm_trace_read", "cm_ag_gemm", "cm_gemm_rs", "cm_status_string", "cm_last_error", "cm_version"]
 
 
@@ -41,7 +41,8 @@ class cm_plan(ctypes.Structure):
                 ("arc_cw", ctypes.c_int), ("arc_ccw", ctypes.c_int), ("tile_m", ctypes.c_int),
                 ("tile_n", ctypes.c_int), ("declined", ctypes.c_int), ("n_ops", ctypes.c_int),
                 ("n_jobs", ctypes.c_int), ("n_events", ctypes.c_int), ("ws_bytes", ctypes.c_size_t),
-                ("est_gemm_us", ctypes.c_double), ("est_hop_us", ctypes.c_double)]
+                ("est_gemm_us", ctypes.c_double), ("est_hop_us", ctypes.c_double),
+                ("est_total_us", ctypes.c_double)]
 
 
 class cm_op_rec(ctypes.Structure):
@@ -86,6 +87,8 @@ def lib():
         vp, ci, cs = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
         L.cm_ring_plan.argtypes = [ctypes.POINTER(cm_plan_desc), ctypes.POINTER(cm_plan)]
         L.cm_workspace_size.argtypes = [ctypes.POINTER(cm_plan), ctypes.POINTER(cs)]
+        L.cm_pick_overlap.argtypes = [ctypes.POINTER(cm_plan_desc), ctypes.POINTER(cm_plan_desc), ctypes.POINTER(ci),
+                                      ctypes.POINTER(ctypes.c_double)]
         L.cm_plan_program.argtypes = [ctypes.POINTER(cm_plan), ctypes.POINTER(cm_op_rec), ci, ctypes.POINTER(ci),
                                       ctypes.POINTER(cm_job_rec), ci, ctypes.POINTER(ci)]
         L.cm_trace_create.argtypes = [ci, ctypes.POINTER(vp)]
@@ -129,8 +132,8 @@ def version():
 
 _ENUMS = {
     "op": {"ag": CM_OP_AG_GEMM, "rs": CM_OP_GEMM_RS, "rs_pipe": CM_OP_GEMM_RS_PIPE},
-    "dir": {"uni": CM_RING_UNI, "bi": CM_RING_BI},
-    "sched": {"decomposed": CM_SCHED_DECOMPOSED, "naive": CM_SCHED_NAIVE},
+    "dir": {"uni": CM_RING_UNI, "bi": CM_RING_BI, "direct": CM_RING_DIRECT},
+    "sched": {"decomposed": CM_SCHED_DECOMPOSED, "naive": CM_SCHED_NAIVE, "auto": CM_SCHED_AUTO},
     "dtype": {"bf16": CM_BF16, "f32": CM_F32},
     "exec": {"graph": CM_EXEC_GRAPH, "eager": CM_EXEC_EAGER},
     "copy": {"sdma": CM_COPY_SDMA, "cu": CM_COPY_CU},
@@ -158,6 +161,18 @@ def cm_ring_plan(desc=None, **kw):
     p = cm_plan()
     _check(lib().cm_ring_plan(ctypes.byref(desc), ctypes.byref(p)), "cm_ring_plan")
     return p
+
+
+def cm_pick_overlap(ag, rs):
+    """Which of two candidate collectives to decompose: (choice, (saving_ag_us, saving_rs_us)),
+    choice 0 = the AllGather, 1 = the ReduceScatter, -1 = neither.  ag / rs are
+    cm_plan_desc values or keyword dicts for make_desc."""
+    ag = ag if isinstance(ag, cm_plan_desc) else make_desc(**ag)
+    rs = rs if isinstance(rs, cm_plan_desc) else make_desc(**rs)
+    choice = ctypes.c_int()
+    save = (ctypes.c_double * 2)()
+    _check(lib().cm_pick_overlap(ctypes.byref(ag), ctypes.byref(rs), ctypes.byref(choice), save), "cm_pick_overlap")
+    return choice.value, (save[0], save[1])
 
 
 def cm_ring_plan_status(desc):

@@ -14,7 +14,8 @@ struct WsLayout {
   size_t gather = 0;          // AG naive: gathered activations
   size_t partial = 0;         // RS pipe / naive: partial products
   size_t partial_bytes = 0;
-  size_t ring = 0;            // RS pipe / naive: ring slots
+  size_t ring = 0;            // RS pipe / naive: ring slots; RS direct: receive slots
+  size_t acc = 0;             // RS direct: the owners' home accumulators
   size_t total = 0;
 };
 

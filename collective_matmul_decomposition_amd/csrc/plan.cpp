@@ -128,6 +128,13 @@ WsLayout ws_layout(const cm_plan &pl) {
       L.slot_dir_bytes = 2 * N * m * k * 2;
       L.total = ndir * L.slot_dir_bytes;
     }
+  } else if (d.op == CM_OP_GEMM_RS && d.sched == CM_SCHED_DECOMPOSED && d.dir == CM_RING_DIRECT) {
+    // send slots S[p][j][r][m][n/c], receive slots R[p][j][q][m][n/c],
+    // home accumulators A[j][q][m][n/c], all fp32
+    L.partial = 0;
+    L.ring = 2 * N * m * n * 4;
+    L.acc = 4 * N * m * n * 4;
+    L.total = 5 * N * m * n * 4;
   } else if (d.op == CM_OP_GEMM_RS && d.sched == CM_SCHED_DECOMPOSED) {
     L.slot_dir_bytes = 2 * N * m * n * (d.bucket_bf16 ? 2 : 4);  // c chunks of n/c columns
     L.total = ndir * L.slot_dir_bytes;
@@ -144,8 +151,8 @@ WsLayout ws_layout(const cm_plan &pl) {
 cm_status validate_desc(const cm_plan_desc &d) {
   if (d.op < CM_OP_AG_GEMM || d.op > CM_OP_GEMM_RS_PIPE) { set_error("unknown op %d", d.op); return CM_ERR_INVALID_ARG; }
   if (d.n_ranks < 1 || d.n_ranks > CM_MAX_RANKS) { set_error("n_ranks %d outside 1..%d", d.n_ranks, CM_MAX_RANKS); return CM_ERR_INVALID_ARG; }
-  if (d.dir != CM_RING_UNI && d.dir != CM_RING_BI) { set_error("unknown ring direction %d", d.dir); return CM_ERR_INVALID_ARG; }
-  if (d.sched != CM_SCHED_DECOMPOSED && d.sched != CM_SCHED_NAIVE) { set_error("unknown schedule %d", d.sched); return CM_ERR_INVALID_ARG; }
+  if (d.dir != CM_RING_UNI && d.dir != CM_RING_BI && d.dir != CM_RING_DIRECT) { set_error("unknown ring direction %d", d.dir); return CM_ERR_INVALID_ARG; }
+  if (d.sched != CM_SCHED_DECOMPOSED && d.sched != CM_SCHED_NAIVE && d.sched != CM_SCHED_AUTO) { set_error("unknown schedule %d", d.sched); return CM_ERR_INVALID_ARG; }
   if (d.n_comm < 1 || d.n_comm > CM_MAX_COMM) { set_error("n_comm %d outside 1..%d", d.n_comm, CM_MAX_COMM); return CM_ERR_INVALID_ARG; }
   if (d.in_dtype != CM_BF16) { set_error("only bf16 inputs are supported"); return CM_ERR_UNSUPPORTED; }
   if (d.out_dtype != CM_BF16 && d.out_dtype != CM_F32) { set_error("out dtype must be CM_BF16 or CM_F32"); return CM_ERR_UNSUPPORTED; }
@@ -162,8 +169,12 @@ cm_status validate_desc(const cm_plan_desc &d) {
   if (d.exec_mode != CM_EXEC_GRAPH && d.exec_mode != CM_EXEC_EAGER) { set_error("unknown exec_mode %d", d.exec_mode); return CM_ERR_INVALID_ARG; }
   if (d.copy_engine != CM_COPY_SDMA && d.copy_engine != CM_COPY_CU) { set_error("unknown copy_engine %d", d.copy_engine); return CM_ERR_INVALID_ARG; }
   if (d.bucket_bf16 != 0 && d.bucket_bf16 != 1) { set_error("bucket_bf16 must be 0 or 1"); return CM_ERR_INVALID_ARG; }
-  if (d.bucket_bf16 && !(d.op == CM_OP_GEMM_RS && d.sched == CM_SCHED_DECOMPOSED)) {
-    set_error("bf16 buckets exist only for the decomposed GEMM-RS");
+  if (d.bucket_bf16 && !(d.op == CM_OP_GEMM_RS && d.sched == CM_SCHED_DECOMPOSED && d.dir != CM_RING_DIRECT)) {
+    set_error("bf16 buckets exist only for the decomposed GEMM-RS on a ring");
+    return CM_ERR_UNSUPPORTED;
+  }
+  if (d.dir == CM_RING_DIRECT && d.op == CM_OP_GEMM_RS_PIPE) {
+    set_error("the pipeline-chunk ReduceScatter runs its own copy-and-add ring; no direct variant");
     return CM_ERR_UNSUPPORTED;
   }
   if ((d.tile_m || d.tile_n) && !tile_known(d.tile_m, d.tile_n)) {
@@ -234,6 +245,21 @@ Est estimate(const cm_plan_desc &d, int c) {
   return e;
 }
 
+// Predicted time of the naive schedule: AG gathers every shard (N - 1 hop
+// rounds) and then runs one GEMM over the gathered rows; RS runs the whole
+// GEMM and then a copy-and-add ring of N - 1 rounds.
+double estimate_naive(const cm_plan_desc &d) {
+  const double N = d.n_ranks, m = d.m, k = d.k, n = d.n;
+  if (d.n_ranks == 1) return gemm_us(d, 1, m, n, k);
+  const int per_lane = std::max(1, std::min(2, d.n_ranks / std::max(1, d.n_comm)));
+  if (d.op == CM_OP_AG_GEMM) {
+    const double round = hop_us(d, N * m * k * 2.0, d.n_ranks, per_lane);
+    return (N - 1) * round + gemm_us(d, d.n_ranks, N * m, n, k);
+  }
+  const double round = hop_us(d, N * m * n * 4.0, d.n_ranks, per_lane) + d.launch_us;  // copy + add
+  return gemm_us(d, d.n_ranks, N * m, n, k) + (N - 1) * round;
+}
+
 }  // namespace
 
 cm_status plan(const cm_plan_desc *desc, cm_plan *out) {
@@ -244,8 +270,24 @@ cm_status plan(const cm_plan_desc *desc, cm_plan *out) {
   if (d.launch_us == 0) d.launch_us = kDefaultLaunchUs;
   cm_status st = validate_desc(d);
   if (st != CM_OK) return st;
-  // A two-rank ring has one neighbour: the bidirectional ring is the uni ring.
-  if (d.n_ranks <= 2) d.dir = CM_RING_UNI;
+  // A two-rank ring has one neighbour: the bidirectional ring is the uni ring;
+  // one rank has no transfers at all.
+  if ((d.n_ranks <= 2 && d.dir == CM_RING_BI) || d.n_ranks == 1) d.dir = CM_RING_UNI;
+  // The decline gate: plan the decomposed op (best chunking) and compare its
+  // predicted time with the naive schedule's.
+  if (d.sched == CM_SCHED_AUTO) {
+    cm_plan_desc dd = d, dn = d;
+    dd.sched = CM_SCHED_DECOMPOSED;
+    dn.sched = CM_SCHED_NAIVE;
+    dn.chunks = 0;
+    cm_plan pd, pn;
+    if ((st = plan(&dd, &pd)) != CM_OK) return st;
+    if ((st = plan(&dn, &pn)) != CM_OK) return st;
+    const bool decline = d.n_ranks > 1 && estimate_naive(dn) < pd.est_total_us;
+    *out = decline ? pn : pd;
+    out->declined = decline ? 1 : 0;
+    return CM_OK;
+  }
   // The naive RS is the pipeline RS with one chunk: the whole GEMM, then the
   // whole ring reduce-scatter.
   if (d.sched == CM_SCHED_NAIVE) d.dir = CM_RING_UNI;
@@ -314,6 +356,7 @@ cm_status plan(const cm_plan_desc *desc, cm_plan *out) {
   Est e = estimate(d, c);
   p.est_gemm_us = e.g;
   p.est_hop_us = e.h;
+  p.est_total_us = d.sched == CM_SCHED_NAIVE ? estimate_naive(d) : e.total;
   p.declined = (N > 1 && !e.hidden) ? 1 : 0;
   int rows = d.op == CM_OP_AG_GEMM ? d.m / c : d.m;
   int cols = d.op == CM_OP_AG_GEMM ? d.n : d.n / c;
@@ -486,7 +529,24 @@ struct Builder {
   }
 
   // ------------------------------------------------------------ AG, decomposed
+  // AG direct: for consumer ranks [a, b) copy shard (r - s - 1) of chunk j
+  // from the owners' inputs into the ranks' slots (one copy per run of ranks
+  // whose sources are also contiguous: only with one chunk per shard).
+  void direct_fetch(int stream, int s, int j, int a, int b, size_t slot_base, size_t chunk_bytes) {
+    const size_t mc = m / c;
+    int r = a;
+    while (r < b) {
+      const int src = mod(r - s - 1, N);
+      int run = 1;
+      while (c == 1 && r + run < b && src + run < N) ++run;
+      copy(stream, CM_BUF_X, ((size_t)src * m + (size_t)j * mc) * k * 2, CM_BUF_WS, slot_base + (size_t)r * chunk_bytes,
+           chunk_bytes * run);
+      r += run;
+    }
+  }
+
   void ag_decomposed() {
+    const bool direct = d.dir == CM_RING_DIRECT;
     const int ndir = d.dir == CM_RING_BI ? 2 : 1;
     const size_t mc = m / c;
     const size_t chunk_bytes = mc * k * 2;             // one rank's chunk, bf16
@@ -511,6 +571,14 @@ struct Builder {
           ehop[s][j][dr].assign(G[dr].size(), -1);
           for (size_t gi = 0; gi < G[dr].size(); ++gi) {
             const Group &g = G[dr][gi];
+            if (direct) {
+              // owner -> consumer: rank r's slot s%2 takes shard (r - s - 1)
+              // from its owner's input; WAR: GEMM(s-1, j) read that slot
+              if (s >= 2) wait(g.stream, egemm[s - 1][j]);
+              direct_fetch(g.stream, s, j, g.a, g.b, slot_off(0, s % 2, j, 0), chunk_bytes);
+              ehop[s][j][dr][gi] = record(g.stream);
+              continue;
+            }
             // WAR: the destination slot (parity s%2) was read by GEMM(s-1, j)
             // and, as the source of hop(s-1, j), by the downstream ranks' copies
             if (s >= 2) {
@@ -721,6 +789,90 @@ struct Builder {
     exit_();
   }
 
+  // ------------------------------------------------------ RS, direct to owner
+  // Step s < N-1: every rank r computes its partial product for bucket
+  // q = r - s - 1 (the ring's order) into its send slot, copies it straight to
+  // owner q (into q's home accumulator at s = 0, else into q's receive slot),
+  // and the owners add the arrivals into their accumulators (one add launch
+  // per step on the first comm lane).  Step N-1: each owner's own partial
+  // plus its accumulator -> Out_q.  The sum is taken in the ring's order, so
+  // the result equals the one-way ring's bitwise.
+  void rs_direct() {
+    const size_t nc = n / c;
+    const size_t blk = m * nc * 4;
+    const int osz = d.out_dtype == CM_F32 ? 4 : 2;
+    auto S = [&](int par, int j, int r) -> size_t { return L.partial + (((size_t)par * c + j) * N + r) * blk; };
+    auto Rv = [&](int par, int j, int q) -> size_t { return L.ring + (((size_t)par * c + j) * N + q) * blk; };
+    auto A = [&](int j, int q) -> size_t { return L.acc + ((size_t)j * N + q) * blk; };
+    std::vector<Group> G = groups(0, 1);
+    const int red_stream = G[0].stream;
+    // events per (step, chunk): the GEMM, the hop groups, the add
+    std::vector<std::vector<int>> eg(N, std::vector<int>(c, -1)), ered(N, std::vector<int>(c, -1));
+    std::vector<std::vector<std::vector<int>>> ehop(N, std::vector<std::vector<int>>(c));
+    entry();
+    for (int s = 0; s < N; ++s) {
+      for (int j = 0; j < c; ++j) {
+        cur_step = s; cur_chunk = j;
+        std::vector<cm_job_rec> jobs;
+        const bool last = s == N - 1;
+        if (last && s >= 1) wait(0, N >= 3 ? ered[s - 1][j] : -1);
+        if (last && N == 2)
+          for (int e : ehop[0][j]) wait(0, e);  // the accumulator is hop(0)'s copy
+        // WAR: send slot s%2 was read by hop(s-2, j)
+        if (!last && s >= 2)
+          for (int e : ehop[s - 2][j]) wait(0, e);
+        for (int r = 0; r < N; ++r) {
+          const int q = last ? r : mod(r - s - 1, N);
+          cm_job_rec jb = job0();
+          jb.rank = r; jb.index = q;
+          jb.a_buf = CM_BUF_X; jb.a_off = ((size_t)r * T + (size_t)q * m) * k * 2; jb.lda = (int)k;
+          jb.b_buf = CM_BUF_W; jb.b_off = ((size_t)r * n + (size_t)j * nc) * k * 2; jb.ldb = (int)k;
+          jb.ld_in = (int)nc;
+          if (last) {
+            jb.c_buf = CM_BUF_Y; jb.c_off = ((size_t)r * m * n + (size_t)j * nc) * osz; jb.ldc = (int)n;
+            jb.c_dtype = d.out_dtype;
+            if (N > 1) { jb.in0_buf = CM_BUF_WS; jb.in0_off = A(j, r); }
+          } else {
+            jb.c_buf = CM_BUF_WS; jb.c_off = S(s % 2, j, r); jb.ldc = (int)nc; jb.c_dtype = CM_F32;
+          }
+          jobs.push_back(jb);
+        }
+        gemm(jobs, (int)m, (int)nc, (int)k);
+        eg[s][j] = record(0);
+        if (last) continue;
+        // hop(s, j): sender ranges [a, b) -> owners r - s - 1
+        std::vector<int> ecp;
+        for (const Group &g : G) {
+          wait(g.stream, eg[s][j]);  // RAW: the partials
+          // WAR: receive slot s%2 was read by add(s-2, j) (on the add lane)
+          if (s >= 2 && g.stream != red_stream) wait(g.stream, ered[s - 2][j]);
+          if (s == 0)
+            shifted_copy(g.stream, CM_BUF_WS, S(0, j, 0), CM_BUF_WS, A(j, 0), blk, g.a, g.b, -1);
+          else
+            shifted_copy(g.stream, CM_BUF_WS, S(s % 2, j, 0), CM_BUF_WS, Rv(s % 2, j, 0), blk, g.a, g.b, -(s + 1));
+          const int e = record(g.stream);
+          ehop[s][j].push_back(e);
+          if (g.stream != red_stream) ecp.push_back(e);
+        }
+        if (s == 0) continue;  // the first arrivals are copied into the accumulators
+        for (int e : ecp) wait(red_stream, e);
+        std::vector<cm_job_rec> rj;
+        for (int q = 0; q < N; ++q) {
+          cm_job_rec jb = job0();
+          jb.rank = q; jb.index = q;
+          jb.in0_buf = CM_BUF_WS; jb.in0_off = A(j, q);
+          jb.in1_buf = CM_BUF_WS; jb.in1_off = Rv(s % 2, j, q);
+          jb.ld_in = (int)nc;
+          jb.c_buf = CM_BUF_WS; jb.c_off = A(j, q); jb.ldc = (int)nc; jb.c_dtype = CM_F32;
+          rj.push_back(jb);
+        }
+        reduce(red_stream, rj, (int)m, (int)nc);
+        ered[s][j] = record(red_stream);
+      }
+    }
+    exit_();
+  }
+
   // ------------------------------------------------- RS, pipeline chunks / naive
   void rs_pipe() {
     const size_t nc = n / c;
@@ -806,7 +958,7 @@ void build_program(const cm_plan &p, Program &prog) {
   if (d.op == CM_OP_AG_GEMM) {
     if (d.sched == CM_SCHED_NAIVE) b.ag_naive(); else b.ag_decomposed();
   } else if (d.op == CM_OP_GEMM_RS && d.sched == CM_SCHED_DECOMPOSED) {
-    b.rs_decomposed();
+    if (d.dir == CM_RING_DIRECT) b.rs_direct(); else b.rs_decomposed();
   } else {
     b.rs_pipe();
   }
@@ -818,6 +970,30 @@ void build_program(const cm_plan &p, Program &prog) {
 extern "C" {
 
 cm_status cm_ring_plan(const cm_plan_desc *desc, cm_plan *out) { return collmm::plan(desc, out); }
+
+cm_status cm_pick_overlap(const cm_plan_desc *ag, const cm_plan_desc *rs, int *choice, double *saving_us) {
+  if (!ag || !rs || !choice) { collmm::set_error("null argument"); return CM_ERR_INVALID_ARG; }
+  if (ag->op != CM_OP_AG_GEMM || (rs->op != CM_OP_GEMM_RS && rs->op != CM_OP_GEMM_RS_PIPE)) {
+    collmm::set_error("cm_pick_overlap takes an AllGather-side and a ReduceScatter-side request");
+    return CM_ERR_INVALID_ARG;
+  }
+  double save[2];
+  const cm_plan_desc *cand[2] = {ag, rs};
+  for (int i = 0; i < 2; ++i) {
+    cm_plan_desc dd = *cand[i], dn = *cand[i];
+    dd.sched = CM_SCHED_DECOMPOSED;
+    dn.sched = CM_SCHED_NAIVE;
+    dn.chunks = 0;
+    cm_plan pd, pn;
+    cm_status st = collmm::plan(&dd, &pd);
+    if (st != CM_OK) return st;
+    if ((st = collmm::plan(&dn, &pn)) != CM_OK) return st;
+    save[i] = pn.est_total_us - pd.est_total_us;
+  }
+  *choice = (save[0] <= 0 && save[1] <= 0) ? -1 : (save[0] >= save[1] ? 0 : 1);
+  if (saving_us) { saving_us[0] = save[0]; saving_us[1] = save[1]; }
+  return CM_OK;
+}
 
 cm_status cm_workspace_size(const cm_plan *plan, size_t *bytes) {
   if (!plan || !bytes) { collmm::set_error("null argument"); return CM_ERR_INVALID_ARG; }

@@ -80,12 +80,27 @@ typedef enum {
   CM_OP_GEMM_RS_PIPE = 2 /* GEMM -> ReduceScatter, pipeline chunks */
 } cm_op;
 
-typedef enum { CM_RING_UNI = 0, CM_RING_BI = 1 } cm_ring_dir;
+/*
+ * CM_RING_DIRECT: no forwarding.  AllGather: at step s rank r fetches shard
+ * (r - s - 1) straight from its owner's input for step s + 1 (the shard
+ * order of the one-way ring, but every transfer is owner -> consumer).
+ * ReduceScatter: at step s rank r sends its partial product for bucket
+ * (r - s - 1) straight to the bucket's owner, which adds the arrivals in the
+ * ring's order into a home accumulator (with the library's add kernel on a
+ * comm stream) and adds its own partial last in its final GEMM.  On a fully
+ * connected fabric each transfer has a link of its own; on one GPU it moves
+ * the same bytes as the ring.  Results equal the one-way ring's bitwise.
+ */
+typedef enum { CM_RING_UNI = 0, CM_RING_BI = 1, CM_RING_DIRECT = 2 } cm_ring_dir;
 
 typedef enum {
   CM_SCHED_DECOMPOSED = 0, /* partial GEMMs overlapped with ring hops */
-  CM_SCHED_NAIVE = 1       /* the blocking baseline: the whole collective, then the whole GEMM
+  CM_SCHED_NAIVE = 1,      /* the blocking baseline: the whole collective, then the whole GEMM
                               (AG), or the whole GEMM, then the whole collective (RS) */
+  CM_SCHED_AUTO = 2        /* the cost model decides per op ("Knowing when to decline"):
+                              decomposed with the best chunking if it predicts a win over the
+                              naive schedule, else naive; plan.desc.sched holds the result and
+                              plan.declined is 1 when the rewrite was declined */
 } cm_sched;
 
 typedef enum { CM_BF16 = 0, CM_F32 = 1 } cm_dtype;
@@ -160,6 +175,7 @@ typedef struct {
   size_t ws_bytes;     /* workspace bytes the calls need */
   double est_gemm_us;  /* cost model: one step's GEMM time (all ranks, one chunk) */
   double est_hop_us;   /* cost model: one step's hop time (all ranks, one chunk) */
+  double est_total_us; /* cost model: the whole op */
 } cm_plan;
 
 /*
@@ -172,6 +188,23 @@ cm_status cm_ring_plan(const cm_plan_desc *desc, cm_plan *out);
 
 /* Workspace bytes a plan needs (same as plan->ws_bytes). */
 cm_status cm_workspace_size(const cm_plan *plan, size_t *bytes);
+
+/*
+ * Pick one of two collectives to decompose ("Knowing when to decline" on the
+ * decomposition page: the cost model "picks which of two candidate
+ * collectives to overlap when an Einsum offers both").  An einsum whose
+ * input is all-gathered and whose output is reduce-scattered can overlap only
+ * one of them with its partial products.  `ag` describes the AllGather-side
+ * candidate (op CM_OP_AG_GEMM) and `rs` the ReduceScatter-side candidate (op
+ * CM_OP_GEMM_RS or CM_OP_GEMM_RS_PIPE), each with the shapes the einsum would
+ * have in that form.  The cost model predicts each candidate's decomposed
+ * time (best chunking) and naive time; *choice receives 0 (decompose the
+ * AllGather), 1 (decompose the ReduceScatter) or -1 (neither is predicted to
+ * win), and saving_us[2] (may be NULL) the predicted savings, naive minus
+ * decomposed, of the two.  Host only.  Errors: CM_ERR_INVALID_ARG for null
+ * pointers or wrong ops, and every error of cm_ring_plan for either request.
+ */
+cm_status cm_pick_overlap(const cm_plan_desc *ag, const cm_plan_desc *rs, int *choice, double *saving_us);
 
 /*
  * The plan as a program: the exact sequence of operations the executor

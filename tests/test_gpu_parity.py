@@ -370,3 +370,55 @@ def test_bf16_bucket_rs_full_size_sampled():
     got = gen.bf16_bits_to_f32(gen.torch_bf16_to_bits(y)[owners, rows]).astype(np.float64)
     bound = 1e-5 * mag + 2.0 ** -7 * rmag + 2.0 ** -8 * np.abs(ref)
     assert (np.abs(got - ref) <= bound).all()
+
+
+# Direct-peer schedules: owner -> consumer transfers, the ring's order of
+# shards and of additions, so the results equal the one-way ring's bitwise.
+DIRECT = [
+    # op, N, m, k, n, chunks, n_comm
+    ("ag", 4, 64, 256, 256, 1, 1),
+    ("ag", 5, 100, 128, 448, 2, 3),
+    ("ag", 8, 256, 1024, 768, 1, 8),
+    ("rs", 4, 64, 256, 256, 1, 1),
+    ("rs", 5, 37, 192, 320, 5, 3),
+    ("rs", 8, 256, 768, 1024, 2, 8),
+    ("rs", 2, 19, 256, 640, 2, 2),
+]
+
+
+@pytest.mark.parametrize("op,N,m,k,n,chunks,n_comm", DIRECT)
+def test_direct_schedule_equals_ring(op, N, m, k, n, chunks, n_comm):
+    say("direct", op, N, m, k, n, chunks, n_comm)
+    _, a, w, (yi,) = run_case(op, N, m, k, n, "int", "f32", "direct", chunks, "decomposed", n_comm)
+    check(op, a, w, yi, "f32", "int")
+    _, _, _, (yd,) = run_case(op, N, m, k, n, "normal", "f32", "direct", chunks, "decomposed", n_comm, seed=9)
+    _, _, _, (yu,) = run_case(op, N, m, k, n, "normal", "f32", "uni", chunks, "decomposed", n_comm, seed=9)
+    assert torch.equal(yd, yu)
+
+
+@pytest.mark.parametrize("op", ["ag", "rs"])
+def test_direct_schedule_full_size_sampled(op):
+    N, m = 8, 256
+    k, n = (12288, 6144) if op == "ag" else (6144, 12288)
+    plan = nat.cm_ring_plan(op=op, n_ranks=N, m=m, k=k, n=n, dir="direct", chunks=1, out_dtype="bf16", n_comm=1)
+    mk = gen.ag_inputs_torch if op == "ag" else gen.rs_inputs_torch
+    x_t, w_t = mk(N, m, k, n, "normal", 0, "cuda")
+    y, ws = buffers.alloc_outputs(plan)
+    say("direct full", op)
+    buffers.run(plan, x_t, w_t, y, ws, comm=buffers.comm_streams(1))
+    torch.cuda.synchronize()
+    sampled_check(op, N, m, x_t, w_t, y, 8)
+
+
+@pytest.mark.parametrize("op", ["ag", "rs", "rs_pipe"])
+def test_auto_schedule(op):
+    """The decline gate's resolved plan (decomposed or naive) runs and matches the oracle."""
+    for kw in (dict(), dict(copy_gbps=1.0)):
+        plan = nat.cm_ring_plan(op=op, n_ranks=4, m=64, k=256, n=256, sched="auto", out_dtype="f32", n_comm=2, **kw)
+        a, w = (gen.ag_inputs if op == "ag" else gen.rs_inputs)(4, 64, 256, 256, "int", 1)
+        x_t, w_t = gen.to_torch_bf16(a, "cuda"), gen.to_torch_bf16(w, "cuda")
+        y, ws = buffers.alloc_outputs(plan)
+        say("auto", op, kw, "resolved", plan.desc.sched, "declined", plan.declined)
+        buffers.run(plan, x_t, w_t, y, ws)
+        torch.cuda.synchronize()
+        check(op, a, w, y, "f32", "int")

@@ -62,7 +62,9 @@ for N in (1, 2, 3, 4, 5, 8):
                                    ("rs", "uni", "decomposed", 1), ("rs", "uni", "decomposed", 2),
                                    ("rs", "bi", "decomposed", 2), ("rs", "bi", "decomposed", 1),
                                    ("rs_pipe", "uni", "decomposed", 2), ("rs_pipe", "uni", "decomposed", 4),
-                                   ("rs", "uni", "naive", 1)]:
+                                   ("rs", "uni", "naive", 1),
+                                   ("ag", "direct", "decomposed", 1), ("ag", "direct", "decomposed", 2),
+                                   ("rs", "direct", "decomposed", 1), ("rs", "direct", "decomposed", 2)]:
         for n_comm in sorted({1, 2, 3, N, 2 * N}):
             CASES.append((op, N, dir, sched, chunks, n_comm))
 
@@ -90,6 +92,71 @@ def test_bf16_bucket_program_matches_oracle(N, dir, chunks, n_comm):
     if N > 2:  # rounding acted: the fp32-bucket result differs
         assert not np.array_equal(got, oracle.gemm_rs(a, w).reshape(-1))
     assert (sim.writes[nat.CM_BUF_Y] == 1).all()
+
+
+def test_auto_schedule_declines_when_hops_cannot_hide():
+    """The decline gate of the decomposition page: the cost model keeps the
+    decomposed op where it predicts a win and falls back to the naive
+    schedule where the hops are longer than the compute."""
+    big = dict(n_ranks=8, m=256, k=12288, n=6144, n_comm=1)
+    p = nat.cm_ring_plan(op="ag", sched="auto", **big)
+    assert p.desc.sched == nat.CM_SCHED_DECOMPOSED and p.declined == 0
+    # thin compute, same hops: the rewrite is declined
+    thin = dict(n_ranks=8, m=256, k=12288, n=64, n_comm=1, copy_gbps=20.0)
+    p = nat.cm_ring_plan(op="ag", sched="auto", **thin)
+    assert p.desc.sched == nat.CM_SCHED_NAIVE and p.declined == 1
+    naive = nat.cm_ring_plan(op="ag", sched="naive", **thin)
+    dec = nat.cm_ring_plan(op="ag", sched="decomposed", **thin)
+    assert naive.est_total_us < dec.est_total_us
+    # the resolved plan runs like an explicit one
+    plan, sim, a, w = None, None, None, None
+    for op in ("ag", "rs"):
+        for kw in (dict(n_ranks=4, m=8, k=64, n=64, copy_gbps=1.0), dict(n_ranks=4, m=8, k=64, n=64)):
+            pl = nat.cm_ring_plan(op=op, sched="auto", **kw)
+            ref = nat.cm_ring_plan(op=op, sched=pl.desc.sched, chunks=pl.chunks, **kw)
+            assert (pl.n_ops, pl.n_jobs, pl.ws_bytes) == (ref.n_ops, ref.n_jobs, ref.ws_bytes)
+
+
+def test_direct_schedules_fetch_from_owners():
+    """AG direct: every hop copies from the user's input (owner -> consumer);
+    RS direct: every partial goes to its owner, whose adds follow the ring order."""
+    p = nat.cm_ring_plan(op="ag", n_ranks=6, m=8, k=64, n=64, dir="direct", n_comm=2)
+    ops, _ = nat.cm_plan_program(p)
+    copies = [o for o in ops if o.kind == nat.CM_OPK_COPY]
+    assert copies and all(o.src_buf == nat.CM_BUF_X and o.dst_buf == nat.CM_BUF_WS for o in copies)
+    assert sum(o.bytes for o in copies) == 6 * 5 * 8 * 64 * 2  # the ring AllGather volume
+    p = nat.cm_ring_plan(op="rs", n_ranks=6, m=8, k=64, n=128, dir="direct", n_comm=2)
+    ops, _ = nat.cm_plan_program(p)
+    copies = [o for o in ops if o.kind == nat.CM_OPK_COPY]
+    assert sum(o.bytes for o in copies) == 6 * 5 * 8 * 128 * 4  # the ring ReduceScatter volume
+    assert sum(1 for o in ops if o.kind == nat.CM_OPK_REDUCE) == p.chunks * (6 - 2)  # one add per step and chunk
+
+
+def test_pick_one_of_two_collectives():
+    """An einsum with a gathered input and a reduce-scattered output overlaps
+    only one of them: the cost model picks the candidate with the larger
+    predicted saving (naive minus decomposed time), or neither."""
+    # the AllGather side has shard hops and a wide GEMM to hide them; the
+    # ReduceScatter side moves 64-column buckets, with little to hide
+    ag = dict(op="ag", n_ranks=8, m=256, k=8192, n=8192, n_comm=1)
+    rs = dict(op="rs", n_ranks=8, m=256, k=8192, n=64, n_comm=1)
+    choice, (s_ag, s_rs) = nat.cm_pick_overlap(ag, rs)
+    assert choice == 0 and s_ag > 0 > s_rs
+    # the other way round
+    choice, (s_ag, s_rs) = nat.cm_pick_overlap(dict(ag, k=64, n=64), dict(rs, n=8192))
+    assert choice == 1 and s_rs > 0 > s_ag
+    # links too slow for either to hide: neither
+    choice, (s_ag, s_rs) = nat.cm_pick_overlap(dict(ag, copy_gbps=0.5, k=64, n=64),
+                                               dict(rs, copy_gbps=0.5, k=64, n=64))
+    assert choice == -1 and s_ag <= 0 and s_rs <= 0
+    # the savings are the gate's own estimates
+    for d in (ag, dict(rs, n=8192)):
+        dec = nat.cm_ring_plan(sched="decomposed", **d)
+        nai = nat.cm_ring_plan(sched="naive", **d)
+        _, sv = nat.cm_pick_overlap(d if d["op"] == "ag" else ag, d if d["op"] == "rs" else rs)
+        assert abs(sv[0 if d["op"] == "ag" else 1] - (nai.est_total_us - dec.est_total_us)) < 1e-6
+    with pytest.raises(nat.CMError):
+        nat.cm_pick_overlap(rs, ag)
 
 
 def test_bf16_bucket_is_only_for_the_decomposed_rs():
@@ -230,6 +297,13 @@ def _gpu_cases():
         cases.append(dict(op="rs", n_ranks=N, m=m, k=k, n=n, dir=dir, chunks=chunks, out_dtype=out, n_comm=2,
                           bucket="bf16"))
     cases.append(dict(op="rs", n_ranks=8, m=256, k=6144, n=12288, chunks=1, out_dtype="bf16", n_comm=1, bucket="bf16"))
+    for op, N, m, k, n, chunks, n_comm in g.DIRECT:
+        cases.append(dict(op=op, n_ranks=N, m=m, k=k, n=n, dir="direct", chunks=chunks, out_dtype="f32", n_comm=n_comm))
+    cases.append(dict(op="ag", n_ranks=8, m=256, k=12288, n=6144, dir="direct", chunks=1, out_dtype="bf16", n_comm=1))
+    cases.append(dict(op="rs", n_ranks=8, m=256, k=6144, n=12288, dir="direct", chunks=1, out_dtype="bf16", n_comm=1))
+    for op in ("ag", "rs", "rs_pipe"):
+        for kw in (dict(), dict(copy_gbps=1.0)):
+            cases.append(dict(op=op, n_ranks=4, m=64, k=256, n=256, sched="auto", out_dtype="f32", n_comm=2, **kw))
     for tile in g.TILES:
         for op in ("ag", "rs"):
             for out in ("f32", "bf16"):
