@@ -65,11 +65,20 @@ def algorithmic_bytes(op_rec, jobs, out_size):
     return total
 
 
-def profiled_traffic(workload, step_name):
+def addends_per_job(op_rec, jobs):
+    """How many fp32 addends (arrived buckets) each job of a GEMM launch reads."""
+    return max((j.in0_buf >= 0) + (j.in1_buf >= 0) for j in jobs[op_rec.first_job:op_rec.first_job + op_rec.n_jobs])
+
+
+def launch_label(name, nadd):
+    return "%s_add%d" % (name, nadd)
+
+
+def profiled_traffic(workload, label):
     """HBM bytes per launch of the dominant kernel from the committed counter
     summary (profiles/gemm_step_<workload>.md: FETCH_SIZE and WRITE_SIZE
     scaled by calibration kernels), or None when that summary was taken on
-    other kernel source than the one built now."""
+    other kernel source than the one built now or holds no such launch."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "gemm_step_%s.md" % workload)
     src = os.path.join(ROOT, "collective_matmul_decomposition_amd", "csrc", "kernels.hip")
@@ -81,8 +90,14 @@ def profiled_traffic(workload, step_name):
     kv = dict(l.split("=", 1) for l in lines if "=" in l and " " not in l)
     if kv.get("kernel_source_sha256") != sha:
         return None
-    v = kv.get("traffic_bytes_%s_step" % step_name)
+    v = kv.get("traffic_bytes_%s" % label)
     return int(v) if v else None
+
+
+def rs_hop(args):
+    """The RS hop kind a run uses: add-and-forward exists for the ring RS with an fp32 bucket only."""
+    ok = args.rs_op == "rs" and args.dir in ("uni", "bi") and args.rs_bucket == "f32"
+    return args.rs_hop if ok else "copy"
 
 
 def measure(args, workload, steps, warmup, with_naive, with_trace):
@@ -100,7 +115,7 @@ def measure(args, workload, steps, warmup, with_naive, with_trace):
                                out_dtype="bf16", n_comm=n_comm, tile=tile, copy_engine=args.copy_engine)
     plan_rs = nat.cm_ring_plan(op=args.rs_op, n_ranks=N, m=m, k=fN, n=d, dir=args.dir, chunks=args.chunks_rs,
                                out_dtype="bf16", n_comm=n_comm, tile=tile, copy_engine=args.copy_engine,
-                               bucket=args.rs_bucket)
+                               bucket=args.rs_bucket, hop=rs_hop(args))
     log("%s plans: AG chunks=%d tile=%dx%d ws=%.0fMB | RS(%s) chunks=%d tile=%dx%d ws=%.0fMB | n_comm=%d" % (
         workload, plan_ag.chunks, plan_ag.tile_m, plan_ag.tile_n, plan_ag.ws_bytes / 1e6, args.rs_op,
         plan_rs.chunks, plan_rs.tile_m, plan_rs.tile_n, plan_rs.ws_bytes / 1e6, n_comm))
@@ -161,7 +176,7 @@ def measure(args, workload, steps, warmup, with_naive, with_trace):
             for o in ops:
                 if o.kind == nat.CM_OPK_GEMM:
                     keys.append((name, o.rows, o.cols, o.depth, o.n_jobs, o.tile_m, o.tile_n,
-                                 algorithmic_bytes(o, jobs, 2)))
+                                 addends_per_job(o, jobs), algorithmic_bytes(o, jobs, 2)))
             return keys
 
         keys = {"ag": launch_keys(ops_ag, jobs_ag, "ag"), "rs": launch_keys(ops_rs, jobs_rs, "rs")}
@@ -176,7 +191,8 @@ def measure(args, workload, steps, warmup, with_naive, with_trace):
                 C = union_length([(s[4], s[5]) for s in spans if s[0] in (nat.CM_OPK_COPY, nat.CM_OPK_REDUCE)])
                 per_op[name].append((total, G, C))
         # the dominant kernel: the launch shape with the most total time
-        (name, rows, cols, depth, jobs, tm, tn, abytes), durs = max(gemm_stats.items(), key=lambda kv: sum(kv[1]))
+        (name, rows, cols, depth, jobs, tm, tn, nadd, abytes), durs = max(gemm_stats.items(),
+                                                                        key=lambda kv: sum(kv[1]))
         flops_launch = 2.0 * rows * cols * depth * jobs
         avg_us = float(np.mean(durs))
         intensity = flops_launch / abytes
@@ -190,20 +206,24 @@ def measure(args, workload, steps, warmup, with_naive, with_trace):
             roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                     "frac": round(achieved / PEAK_HBM_GBPS, 4)}
         roof.update({"traffic": None,
-                     "kernel": "gemm_jobs_kernel<%d,%d,...> (%s step: %d jobs of [%dx%d].[%dx%d]^T)" % (
-                         tm, tn, name.upper(), jobs, rows, depth, cols, depth),
+                     "kernel": "gemm_jobs_kernel<%d,%d,...> (%s step: %d jobs of [%dx%d].[%dx%d]^T%s)" % (
+                         tm, tn, name.upper(), jobs, rows, depth, cols, depth,
+                         ", + %d fp32 addend(s)" % nadd if nadd else ""),
+                     "launch": launch_label(name, nadd),
                      "avg_launch_us": round(avg_us, 2), "launches": len(durs),
                      "flops_per_launch": flops_launch, "algorithmic_bytes_per_launch": abytes,
                      "intensity_flop_per_byte": round(intensity, 1), "ridge_flop_per_byte": round(ridge, 1),
                      "mfma_tflops": round(flops_launch / (avg_us * 1e-6) / 1e12, 1),
                      "hbm_gbps": round(abytes / (avg_us * 1e-6) / 1e9, 1)})
-        roof["traffic"] = profiled_traffic(workload, name)
+        roof["traffic"] = profiled_traffic(workload, launch_label(name, nadd))
         res["roofline"] = roof
         res["gemm_launches"] = {
-            "%s %dx%dx%d x%d tile %dx%d" % (nm, r, c, dd, j, a, b): {
-                "avg_us": round(float(np.mean(dl)), 2), "count": len(dl),
-                "tflops": round(2.0 * r * c * dd * j / (np.mean(dl) * 1e-6) / 1e12, 1)}
-            for (nm, r, c, dd, j, a, b, _), dl in gemm_stats.items()}
+            "%s %dx%dx%d x%d tile %dx%d%s" % (nm, r, c, dd, j, a, b, " +%d addend" % na if na else ""): {
+                "launch": launch_label(nm, na), "avg_us": round(float(np.mean(dl)), 2), "count": len(dl),
+                "tflops": round(2.0 * r * c * dd * j / (np.mean(dl) * 1e-6) / 1e12, 1), "algorithmic_bytes": ab}
+            for (nm, r, c, dd, j, a, b, na, ab), dl in gemm_stats.items()}
+        # the GEMM launches of one step in program order (for splitting a profiler's trace)
+        res["step_launches"] = [launch_label(k[0], k[7]) for k in keys["ag"] + keys["rs"]]
         ov = {}
         for name, plan in (("ag", plan_ag), ("rs", plan_rs)):
             arr = np.array(per_op[name])
@@ -391,6 +411,10 @@ def main():
                     help="element type of the circulating RS bucket (bf16: half the hop bytes, outside the "
                          "fp32-bucket error bound)")
     ap.add_argument("--no-alt-bucket", action="store_true", help="skip the run with the other RS bucket type")
+    ap.add_argument("--no-alt-hop", action="store_true", help="skip the run with the other RS hop kind")
+    ap.add_argument("--rs-hop", default="add", choices=["copy", "add"],
+                    help="RS ring hop: a copy with the addition in the GEMM epilogue, or an add-and-forward "
+                         "launch that lets each step's GEMM start without waiting for the previous hop")
     ap.add_argument("--tile", default="0x0")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
@@ -449,9 +473,20 @@ def main():
         alt_args = argparse.Namespace(**vars(args))
         alt_args.rs_bucket = "bf16" if args.rs_bucket == "f32" else "f32"
         rb = measure(alt_args, args.workload, args.steps, args.warmup, False, not args.no_trace)
-        alt_bucket = {"rs_bucket": alt_args.rs_bucket, "value": round(rb["value"], 2), "unit": "TFLOP/s",
+        alt_bucket = {"rs_bucket": alt_args.rs_bucket, "rs_hop": rs_hop(alt_args), "value": round(rb["value"], 2),
+                      "unit": "TFLOP/s",
                       "ms_per_step": round(rb["ms_per_step"], 4), "overlap": rb.get("overlap")}
         del rb
+        torch.cuda.empty_cache()
+    alt_hop = None
+    if not args.no_alt_hop and rs_hop(args) == args.rs_hop:
+        alt_args = argparse.Namespace(**vars(args))
+        alt_args.rs_hop = "copy" if args.rs_hop == "add" else "add"
+        rh = measure(alt_args, args.workload, args.steps, args.warmup, False, not args.no_trace)
+        alt_hop = {"rs_hop": alt_args.rs_hop, "value": round(rh["value"], 2), "unit": "TFLOP/s",
+                   "ms_per_step": round(rh["ms_per_step"], 4), "overlap": rh.get("overlap"),
+                   "gemm_launches": rh.get("gemm_launches")}
+        del rh
         torch.cuda.empty_cache()
     secondary = None
     if args.secondary != "none" and args.secondary != args.workload:
@@ -477,6 +512,7 @@ def main():
         "config": {"workload": args.workload, "virtual_ranks": res["N"], "tokens": res["T"], "hidden": res["d"],
                    "ffn": res["f"], "ffn_per_rank": res["fN"], "ring": args.dir, "rs_variant": args.rs_op,
                    "n_comm_streams": res["n_comm"], "copy_engine": args.copy_engine, "rs_bucket": args.rs_bucket,
+                   "rs_hop": rs_hop(args),
                    "chunks_ag": res["plan_ag"].chunks,
                    "chunks_rs": res["plan_rs"].chunks,
                    "step": "AllGather->GEMM (fc1) then GEMM->ReduceScatter (fc2), decomposed, bf16 in / fp32 "
@@ -490,6 +526,8 @@ def main():
         "parity_sampled_err_over_bound": parity,
         "alt_copy_engine": alt,
         "alt_rs_bucket": alt_bucket,
+        "alt_rs_hop": alt_hop,
+        "step_launches": res.get("step_launches"),
         "secondary": secondary,
     }
     print(json.dumps(out), flush=True)

@@ -32,7 +32,8 @@ class cm_plan_desc(ctypes.Structure):
                 ("n", ctypes.c_int), ("dir", ctypes.c_int), ("chunks", ctypes.c_int), ("sched", ctypes.c_int),
                 ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int), ("n_comm", ctypes.c_int),
                 ("tile_m", ctypes.c_int), ("tile_n", ctypes.c_int), ("exec_mode", ctypes.c_int),
-                ("copy_engine", ctypes.c_int), ("bucket_bf16", ctypes.c_int), ("copy_gbps", ctypes.c_double),
+                ("copy_engine", ctypes.c_int), ("bucket_bf16", ctypes.c_int), ("hop_add", ctypes.c_int),
+                ("copy_gbps", ctypes.c_double),
                 ("mfma_tflops", ctypes.c_double), ("launch_us", ctypes.c_double)]
 
 
@@ -137,12 +138,13 @@ _ENUMS = {
     "dtype": {"bf16": CM_BF16, "f32": CM_F32},
     "exec": {"graph": CM_EXEC_GRAPH, "eager": CM_EXEC_EAGER},
     "copy": {"sdma": CM_COPY_SDMA, "cu": CM_COPY_CU},
+    "hop": {"copy": 0, "add": 1},
 }
 
 
 def make_desc(op, n_ranks, m, k, n, dir="uni", chunks=0, sched="decomposed", out_dtype="bf16", n_comm=1,
-              tile=(0, 0), exec_mode="graph", copy_engine="sdma", bucket="f32", copy_gbps=0.0, mfma_tflops=0.0,
-              launch_us=0.0):
+              tile=(0, 0), exec_mode="graph", copy_engine="sdma", bucket="f32", hop="copy", copy_gbps=0.0,
+              mfma_tflops=0.0, launch_us=0.0):
     """A cm_plan_desc from keyword arguments (strings or enum values)."""
     def e(kind, v):
         return _ENUMS[kind][v] if isinstance(v, str) else int(v)
@@ -150,7 +152,7 @@ def make_desc(op, n_ranks, m, k, n, dir="uni", chunks=0, sched="decomposed", out
                         sched=e("sched", sched), in_dtype=CM_BF16, out_dtype=e("dtype", out_dtype),
                         n_comm=n_comm, tile_m=tile[0], tile_n=tile[1], exec_mode=e("exec", exec_mode),
                         copy_engine=e("copy", copy_engine), bucket_bf16=1 if bucket == "bf16" else 0,
-                        copy_gbps=copy_gbps,
+                        hop_add=e("hop", hop), copy_gbps=copy_gbps,
                         mfma_tflops=mfma_tflops, launch_us=launch_us)
 
 

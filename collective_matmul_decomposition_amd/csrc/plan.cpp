@@ -57,6 +57,7 @@ int mod(int a, int n) { return ((a % n) + n) % n; }
 // cost of one graph node (kernel or copy).
 constexpr double kDefaultCopyGBps = 100.0;    // one SDMA lane
 constexpr double kDefaultCuCopyGBps = 1000.0; // the CU copy kernel
+constexpr double kDefaultCuAddGBps = 1500.0;  // the add-and-forward launch beside a GEMM (bytes read + written)
 constexpr double kDefaultMfmaTflops = 900.0;
 constexpr double kDefaultLaunchUs = 20.0;
 
@@ -112,7 +113,8 @@ const char *last_error() { return g_last_error.c_str(); }
 // AG decomposed: receive slots, chunk-major so that one chunk of a range of
 //   ranks is contiguous:  slot[dir][p][j][r][m/c][k] bf16.
 // AG naive: gathered activations G[r][T][k] bf16.
-// RS decomposed: buckets  bkt[dir][p][j][r][m][n/c] fp32 (bf16 with bucket_bf16).
+// RS decomposed: buckets  bkt[dir][p][j][r][m][n/c] fp32 (bf16 with bucket_bf16);
+//   with add-and-forward hops also partial slots of the same shape after them.
 // RS pipe / naive: partials P[r][j][T][n/c] fp32, then ring slots
 //   R[p][r][m][n/c] fp32.
 WsLayout ws_layout(const cm_plan &pl) {
@@ -138,6 +140,10 @@ WsLayout ws_layout(const cm_plan &pl) {
   } else if (d.op == CM_OP_GEMM_RS && d.sched == CM_SCHED_DECOMPOSED) {
     L.slot_dir_bytes = 2 * N * m * n * (d.bucket_bf16 ? 2 : 4);  // c chunks of n/c columns
     L.total = ndir * L.slot_dir_bytes;
+    if (d.hop_add) {  // + partial slots P[dir][p][j][r][m][n/c] fp32
+      L.partial = L.total;
+      L.total *= 2;
+    }
   } else {  // PIPE, or RS naive (PIPE with one chunk)
     L.partial = 0;
     L.partial_bytes = N > 1 ? N * T * n * 4 : 0;
@@ -171,6 +177,11 @@ cm_status validate_desc(const cm_plan_desc &d) {
   if (d.bucket_bf16 != 0 && d.bucket_bf16 != 1) { set_error("bucket_bf16 must be 0 or 1"); return CM_ERR_INVALID_ARG; }
   if (d.bucket_bf16 && !(d.op == CM_OP_GEMM_RS && d.sched == CM_SCHED_DECOMPOSED && d.dir != CM_RING_DIRECT)) {
     set_error("bf16 buckets exist only for the decomposed GEMM-RS on a ring");
+    return CM_ERR_UNSUPPORTED;
+  }
+  if (d.hop_add != 0 && d.hop_add != 1) { set_error("hop_add must be 0 or 1"); return CM_ERR_INVALID_ARG; }
+  if (d.hop_add && !(d.op == CM_OP_GEMM_RS && d.sched != CM_SCHED_NAIVE && d.dir != CM_RING_DIRECT && !d.bucket_bf16)) {
+    set_error("add-and-forward hops exist only for the decomposed GEMM-RS on a ring with an fp32 bucket");
     return CM_ERR_UNSUPPORTED;
   }
   if (d.dir == CM_RING_DIRECT && d.op == CM_OP_GEMM_RS_PIPE) {
@@ -224,6 +235,15 @@ Est estimate(const cm_plan_desc &d, int c) {
     e.g = g; e.h = h;
     // hop(s) runs beside GEMM(s); GEMM(s+1) needs hop(s)
     e.total = c * steps * std::max(g, h) + std::min(g, h);
+    e.hidden = h <= g;
+  } else if (d.op == CM_OP_GEMM_RS && d.hop_add) {
+    // add-and-forward: hop(s) (read partial, read bucket, write the next
+    // rank's slot) runs beside GEMM(s+1); only the last hop is exposed
+    const double g = gemm_us(d, d.n_ranks * ndir, m, n / c, k);
+    const double h = N * m * (n / c) * 4.0 * 3.0 * ndir / (kDefaultCuAddGBps * 1e9) * 1e6 + d.launch_us;
+    const int steps = bi ? 1 + d.n_ranks / 2 : d.n_ranks;
+    e.g = g; e.h = h;
+    e.total = c * steps * std::max(g, h) + h;
     e.hidden = h <= g;
   } else if (d.op == CM_OP_GEMM_RS) {
     const double g = gemm_us(d, d.n_ranks * ndir, m, n / c, k);
@@ -280,6 +300,7 @@ cm_status plan(const cm_plan_desc *desc, cm_plan *out) {
     dd.sched = CM_SCHED_DECOMPOSED;
     dn.sched = CM_SCHED_NAIVE;
     dn.chunks = 0;
+    dn.hop_add = 0;
     cm_plan pd, pn;
     if ((st = plan(&dd, &pd)) != CM_OK) return st;
     if ((st = plan(&dn, &pn)) != CM_OK) return st;
@@ -317,7 +338,7 @@ cm_status plan(const cm_plan_desc *desc, cm_plan *out) {
     const int cands[] = {1, 2, 3, 4, 6, 8};
     for (int cc : cands) {
       if (!chunk_ok(cc)) continue;
-      if (d.op == CM_OP_GEMM_RS && cc < 2 && d.n_ranks > 1) continue;
+      if (d.op == CM_OP_GEMM_RS && !d.hop_add && cc < 2 && d.n_ranks > 1) continue;
       if (d.op == CM_OP_AG_GEMM && d.m / cc < 32 && cc > 1) continue;
       Est e = estimate(d, cc);
       if (best < 0 || e.total < best_t * 0.95) { best = cc; best_t = e.total; }
@@ -706,6 +727,7 @@ struct Builder {
 
   // ------------------------------------------------------------ RS, decomposed
   void rs_decomposed() {
+    if (d.hop_add) { rs_hop_add(); return; }
     const bool bi = d.dir == CM_RING_BI;
     const int ndir = bi ? 2 : 1;
     const size_t nc = n / c;
@@ -784,6 +806,103 @@ struct Builder {
             ehop[j][dr].push_back(record(g.stream));
           }
         }
+      }
+    }
+    exit_();
+  }
+
+  // ------------------------------------------ RS, ring with add-and-forward hops
+  // The ring's order and sums of rs_decomposed with the addition moved out of
+  // the GEMM into the hop.  At a direction's first step the partial product is
+  // stored straight into the next rank's receive slot; at later steps it is
+  // stored into a partial slot, and one add launch on the first comm stream
+  // writes partial + arrived bucket into the next rank's receive slot (the
+  // copy and the addition in one pass over the bytes).  A step's GEMM waits
+  // only for its partial slot to be free (two per rank, alternating by
+  // parity), not for the previous hop.  The owner's last GEMM adds the
+  // arrived bucket(s) in its epilogue as in rs_decomposed.  fp32 addition
+  // commutes, so every sum equals the epilogue's bitwise.
+  void rs_hop_add() {
+    const bool bi = d.dir == CM_RING_BI;
+    const int ndir = bi ? 2 : 1;
+    const size_t nc = n / c;
+    const size_t blk = m * nc * 4;
+    const int osz = d.out_dtype == CM_F32 ? 4 : 2;
+    auto bkt = [&](int dir, int par, int j, int r) -> size_t {
+      return dir * L.slot_dir_bytes + ((((size_t)par * c + j) * N + r) * blk);
+    };
+    auto part = [&](int dir, int par, int j, int r) -> size_t {
+      return L.partial + dir * L.slot_dir_bytes + ((((size_t)par * c + j) * N + r) * blk);
+    };
+    const int Lc = p.arc_cw, R = p.arc_ccw;
+    const int last = bi ? Lc : N - 1;
+    const int arc = bi ? Lc : N - 1;
+    // a direction contributes at steps [first, last): clockwise from 0,
+    // counter-clockwise from Lc - R (bi only)
+    const int first[2] = {0, Lc - R};
+    const int red = 1;  // the add launches run on the first comm stream
+    std::vector<std::vector<int>> ered(last + 1, std::vector<int>(c, -1));
+    entry();
+    for (int s = 0; s <= last; ++s) {
+      for (int j = 0; j < c; ++j) {
+        cur_step = s; cur_chunk = j;
+        if (s == last) {
+          if (s >= 1) wait(0, ered[s - 1][j]);  // RAW: the arrived buckets
+        } else if (s >= 2) {
+          wait(0, ered[s - 2][j]);  // WAR: partial slot s%2 was read by add(s-2, j)
+        }
+        std::vector<cm_job_rec> jobs;
+        auto mk = [&](int r, int dr, int bucket) {
+          cm_job_rec jb = job0();
+          jb.rank = r; jb.dir = dr; jb.index = bucket;
+          jb.a_buf = CM_BUF_X; jb.a_off = ((size_t)r * T + (size_t)bucket * m) * k * 2; jb.lda = (int)k;
+          jb.b_buf = CM_BUF_W; jb.b_off = ((size_t)r * n + (size_t)j * nc) * k * 2; jb.ldb = (int)k;
+          jb.ld_in = (int)nc;
+          return jb;
+        };
+        for (int r = 0; r < N; ++r) {
+          if (s == last) {
+            cm_job_rec jb = mk(r, 0, r);
+            jb.c_buf = CM_BUF_Y; jb.c_off = ((size_t)r * m * n + (size_t)j * nc) * osz; jb.ldc = (int)n;
+            jb.c_dtype = d.out_dtype;
+            if (N > 1) { jb.in0_buf = CM_BUF_WS; jb.in0_off = bkt(0, s % 2, j, r); }
+            if (bi && R >= 1) { jb.in1_buf = CM_BUF_WS; jb.in1_off = bkt(1, s % 2, j, r); }
+            jobs.push_back(jb);
+            continue;
+          }
+          for (int dr = 0; dr < ndir; ++dr) {
+            if (s < first[dr]) continue;
+            const int shift = dr == 0 ? 1 : -1;
+            const int q = dr == 0 ? mod(r + (arc - s), N) : mod(r - (Lc - s), N);
+            cm_job_rec jb = mk(r, dr, q);
+            jb.c_buf = CM_BUF_WS; jb.ldc = (int)nc; jb.c_dtype = CM_F32;
+            jb.c_off = s == first[dr] ? bkt(dr, (s + 1) % 2, j, mod(r + shift, N)) : part(dr, s % 2, j, r);
+            jobs.push_back(jb);
+          }
+        }
+        gemm(jobs, (int)m, (int)nc, (int)k);
+        const int eg = record(0);
+        if (s == last) continue;
+        std::vector<cm_job_rec> rj;
+        for (int dr = 0; dr < ndir; ++dr) {
+          if (s <= first[dr]) continue;
+          const int shift = dr == 0 ? 1 : -1;
+          for (int r = 0; r < N; ++r) {
+            cm_job_rec jb = job0();
+            jb.rank = r; jb.dir = dr;
+            jb.index = dr == 0 ? mod(r + (arc - s), N) : mod(r - (Lc - s), N);
+            jb.in0_buf = CM_BUF_WS; jb.in0_off = part(dr, s % 2, j, r);
+            jb.in1_buf = CM_BUF_WS; jb.in1_off = bkt(dr, s % 2, j, r);
+            jb.ld_in = (int)nc;
+            jb.c_buf = CM_BUF_WS; jb.c_off = bkt(dr, (s + 1) % 2, j, mod(r + shift, N)); jb.ldc = (int)nc;
+            jb.c_dtype = CM_F32;
+            rj.push_back(jb);
+          }
+        }
+        if (rj.empty()) continue;  // every direction's first step: the GEMM stored straight into the slots
+        wait(red, eg);  // RAW: the partials (and, through the compute stream, earlier direct stores)
+        reduce(red, rj, (int)m, (int)nc);
+        ered[s][j] = record(red);
       }
     }
     exit_();
@@ -984,6 +1103,7 @@ cm_status cm_pick_overlap(const cm_plan_desc *ag, const cm_plan_desc *rs, int *c
     dd.sched = CM_SCHED_DECOMPOSED;
     dn.sched = CM_SCHED_NAIVE;
     dn.chunks = 0;
+    dn.hop_add = 0;
     cm_plan pd, pn;
     cm_status st = collmm::plan(&dd, &pd);
     if (st != CM_OK) return st;

@@ -154,6 +154,16 @@ typedef struct {
                       bytes), rounded to nearest-even after every addition,
                       which adds up to half a bf16 spacing of error per hop
                       (outside the fp32-bucket error bound) */
+  int hop_add;     /* GEMM-RS (decomposed, uni or bi ring, fp32 bucket) only:
+                      0 = each step's GEMM adds the arrived bucket in its
+                      epilogue (read-add-write) and the hop is a copy, so a
+                      step's GEMM waits for the previous hop; 1 = each step's
+                      GEMM stores its partial product and the hop is an
+                      add-and-forward launch on compute units (on the first
+                      comm stream) that writes partial + arrived bucket into
+                      the next rank's receive slot, so a step's GEMM waits for
+                      nothing but a free partial slot.  The owner's last GEMM
+                      still adds in its epilogue.  Bitwise the same result. */
   /* Cost-model inputs (0 = built-in defaults for MI355X). */
   double copy_gbps;      /* sustained hop bandwidth of ONE comm stream, GB/s */
   double mfma_tflops;    /* sustained bf16 GEMM rate, TFLOP/s */

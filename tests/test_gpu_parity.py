@@ -43,9 +43,9 @@ def gpu_ready():
 
 
 def run_case(op, N, m, k, n, dist="int", out="f32", dir="uni", chunks=1, sched="decomposed", n_comm=1, seed=0,
-             repeat=1, tile=(0, 0), exec_mode="graph", copy_engine="sdma"):
+             repeat=1, tile=(0, 0), exec_mode="graph", copy_engine="sdma", hop="copy"):
     plan = nat.cm_ring_plan(op=op, n_ranks=N, m=m, k=k, n=n, dir=dir, chunks=chunks, sched=sched, out_dtype=out,
-                            n_comm=n_comm, tile=tile, exec_mode=exec_mode, copy_engine=copy_engine)
+                            n_comm=n_comm, tile=tile, exec_mode=exec_mode, copy_engine=copy_engine, hop=hop)
     if op == "ag":
         a, w = gen.ag_inputs(N, m, k, n, dist, seed)
     else:
@@ -422,3 +422,51 @@ def test_auto_schedule(op):
         buffers.run(plan, x_t, w_t, y, ws)
         torch.cuda.synchronize()
         check(op, a, w, y, "f32", "int")
+
+
+HOP_ADD = [
+    # N, m, k, n, dir, chunks, n_comm
+    (2, 19, 256, 640, "uni", 2, 1),
+    (3, 64, 256, 256, "bi", 1, 2),
+    (4, 64, 256, 256, "uni", 1, 1),
+    (5, 37, 192, 320, "bi", 5, 3),
+    (8, 256, 768, 1024, "uni", 2, 1),
+    (8, 256, 768, 1024, "bi", 1, 2),
+]
+
+
+@pytest.mark.parametrize("N,m,k,n,dir,chunks,n_comm", HOP_ADD)
+def test_hop_add_equals_epilogue_ring(N, m, k, n, dir, chunks, n_comm):
+    """Add-and-forward hops: the oracle's bound on integers, and bitwise the
+    sums of the ring that adds in the GEMM epilogue on real-valued data."""
+    say("hop add", N, m, k, n, dir, chunks, n_comm)
+    for out in ("f32", "bf16"):
+        _, a, w, (yi,) = run_case("rs", N, m, k, n, "int", out, dir, chunks, "decomposed", n_comm, hop="add")
+        check("rs", a, w, yi, out, "int")
+    for exec_mode in ("graph", "eager"):
+        _, _, _, (ya,) = run_case("rs", N, m, k, n, "normal", "f32", dir, chunks, "decomposed", n_comm, seed=9,
+                                  exec_mode=exec_mode, hop="add")
+        _, _, _, (yc,) = run_case("rs", N, m, k, n, "normal", "f32", dir, chunks, "decomposed", n_comm, seed=9,
+                                  exec_mode=exec_mode)
+        assert torch.equal(ya, yc)
+
+
+@pytest.mark.parametrize("dir", ["uni", "bi"])
+def test_hop_add_full_size_sampled(dir):
+    """GPT-3 MLP fc2 shape (8 ranks, [256 x 6144] . [6144 x 12288] per step),
+    add-and-forward hops, bf16 out: sampled rows against the oracle, and the
+    whole output bitwise equal to the epilogue-add ring's."""
+    N, m, k, n = 8, 256, 6144, 12288
+    x_t, w_t = gen.rs_inputs_torch(N, m, k, n, "normal", 0, "cuda")
+    ys = []
+    for hop in ("add", "copy"):
+        plan = nat.cm_ring_plan(op="rs", n_ranks=N, m=m, k=k, n=n, dir=dir, chunks=1, out_dtype="bf16", n_comm=1,
+                                hop=hop)
+        y, ws = buffers.alloc_outputs(plan)
+        say("hop full", dir, hop)
+        buffers.run(plan, x_t, w_t, y, ws, comm=buffers.comm_streams(1))
+        torch.cuda.synchronize()
+        ys.append(y)
+        del ws
+    sampled_check("rs", N, m, x_t, w_t, ys[0], 8)
+    assert torch.equal(ys[0], ys[1])

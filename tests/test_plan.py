@@ -26,9 +26,9 @@ from ring_sim import Race, Sim, buffer_sizes
 
 
 def simulate(op, N, m, k, n, dir="uni", chunks=1, sched="decomposed", out="f32", n_comm=1, seed=0, dist="int",
-             data=None, bucket="f32"):
+             data=None, bucket="f32", hop="copy"):
     plan = nat.cm_ring_plan(op=op, n_ranks=N, m=m, k=k, n=n, dir=dir, chunks=chunks, sched=sched, out_dtype=out,
-                            n_comm=n_comm, bucket=bucket)
+                            n_comm=n_comm, bucket=bucket, hop=hop)
     if data is None:
         if op == "ag":
             a, w = gen.ag_inputs(N, m, k, n, dist, seed)
@@ -92,6 +92,57 @@ def test_bf16_bucket_program_matches_oracle(N, dir, chunks, n_comm):
     if N > 2:  # rounding acted: the fp32-bucket result differs
         assert not np.array_equal(got, oracle.gemm_rs(a, w).reshape(-1))
     assert (sim.writes[nat.CM_BUF_Y] == 1).all()
+
+
+HOP_ADD = [(N, dir, chunks, n_comm) for N in (1, 2, 3, 4, 5, 8) for dir in ("uni", "bi")
+           for chunks in (1, 2) for n_comm in sorted({1, 2, N})]
+
+
+@pytest.mark.parametrize("N,dir,chunks,n_comm", HOP_ADD)
+def test_hop_add_program_matches_oracle_and_the_epilogue_ring(N, dir, chunks, n_comm):
+    """Add-and-forward hops: exact on integers against the oracle, race-free,
+    every output written once, and no copies (the adds are the hops).  That
+    the GPU sums equal the epilogue-add ring's bitwise is a GPU test: this
+    simulation adds in float64."""
+    m, k, n = 3, 64, 64 * chunks
+    for out in ("f32", "bf16"):
+        plan, sim, a, w = simulate("rs", N, m, k, n, dir, chunks, "decomposed", out, n_comm, hop="add")
+        assert np.array_equal(output(sim, plan), expect("rs", a, w, out))
+        assert (sim.writes[nat.CM_BUF_Y] == 1).all()
+    ops, _ = nat.cm_plan_program(nat.cm_ring_plan(op="rs", n_ranks=N, m=m, k=k, n=n, dir=dir, chunks=chunks,
+                                                  n_comm=n_comm, hop="add"))
+    assert not any(o.kind == nat.CM_OPK_COPY for o in ops)
+
+
+@pytest.mark.parametrize("N", [3, 4, 8])
+def test_hop_add_gemms_do_not_wait_for_the_previous_hop(N):
+    """With add-and-forward hops the GEMM of step s waits only for the add of
+    step s - 2 (its partial slot's last reader), never for hop(s - 1); the
+    owner's last GEMM waits for the last add."""
+    plan = nat.cm_ring_plan(op="rs", n_ranks=N, m=8, k=64, n=128, chunks=1, n_comm=1, hop="add")
+    ops, _ = nat.cm_plan_program(plan)
+    recorded_at = {}
+    for o in ops:
+        if o.kind == nat.CM_OPK_RECORD and o.stream != 0:
+            recorded_at[o.event] = o.step
+    for o in ops:
+        if o.kind == nat.CM_OPK_WAIT and o.stream == 0 and 0 <= o.step < N - 1:
+            assert recorded_at[o.event] <= o.step - 2, (o.step, recorded_at[o.event])
+    last_waits = [recorded_at[o.event] for o in ops if o.kind == nat.CM_OPK_WAIT and o.stream == 0
+                  and o.step == N - 1]
+    assert last_waits == [N - 2]
+
+
+def test_hop_add_is_only_for_the_ring_rs():
+    base = dict(n_ranks=4, m=8, k=64, n=128, hop="add")
+    for kw in (dict(op="ag"), dict(op="rs_pipe", chunks=2), dict(op="rs", sched="naive"), dict(op="rs", dir="direct"),
+               dict(op="rs", bucket="bf16")):
+        st, _ = nat.cm_ring_plan_status(nat.make_desc(**dict(base, **kw)))
+        assert st == nat.CM_ERR_UNSUPPORTED, kw
+    st, _ = nat.cm_ring_plan_status(nat.make_desc(op="rs", n_ranks=4, m=8, k=64, n=128, hop=2))
+    assert st == nat.CM_ERR_INVALID_ARG
+    p = nat.cm_ring_plan(op="rs", n_ranks=4, m=8, k=64, n=128, sched="auto", hop="add", copy_gbps=1.0)
+    assert p.desc.sched in (nat.CM_SCHED_DECOMPOSED, nat.CM_SCHED_NAIVE)
 
 
 def test_auto_schedule_declines_when_hops_cannot_hide():
@@ -234,14 +285,16 @@ def _drop_op(sim, index):
     return sim
 
 
-@pytest.mark.parametrize("op,dir,chunks", [("ag", "uni", 1), ("ag", "bi", 2), ("rs", "uni", 2), ("rs", "bi", 2),
-                                           ("rs_pipe", "uni", 2), ("ag", "uni", 2)])
-def test_dropped_dependency_is_caught(op, dir, chunks):
+@pytest.mark.parametrize("op,dir,chunks,hop", [("ag", "uni", 1, "copy"), ("ag", "bi", 2, "copy"),
+                                               ("rs", "uni", 2, "copy"), ("rs", "bi", 2, "copy"),
+                                               ("rs_pipe", "uni", 2, "copy"), ("ag", "uni", 2, "copy"),
+                                               ("rs", "uni", 1, "add"), ("rs", "bi", 2, "add")])
+def test_dropped_dependency_is_caught(op, dir, chunks, hop):
     """Negative control: removing any one wait that orders a hop against a GEMM makes a race."""
     N, m, k = 4, 4 * chunks, 64
     n = 64 * chunks
     plan = nat.cm_ring_plan(op=op, n_ranks=N, m=m if op == "ag" else 3, k=k, n=n if op != "ag" else 64, dir=dir,
-                            chunks=chunks, n_comm=2)
+                            chunks=chunks, n_comm=2, hop=hop)
     sizes = buffer_sizes(plan)
     if op == "ag":
         a, w = gen.ag_inputs(N, plan.desc.m, k, plan.desc.n, "int", 0)
@@ -301,6 +354,13 @@ def _gpu_cases():
         cases.append(dict(op=op, n_ranks=N, m=m, k=k, n=n, dir="direct", chunks=chunks, out_dtype="f32", n_comm=n_comm))
     cases.append(dict(op="ag", n_ranks=8, m=256, k=12288, n=6144, dir="direct", chunks=1, out_dtype="bf16", n_comm=1))
     cases.append(dict(op="rs", n_ranks=8, m=256, k=6144, n=12288, dir="direct", chunks=1, out_dtype="bf16", n_comm=1))
+    for N, m, k, n, dir, chunks, n_comm in g.HOP_ADD:
+        for out in ("f32", "bf16"):
+            cases.append(dict(op="rs", n_ranks=N, m=m, k=k, n=n, dir=dir, chunks=chunks, out_dtype=out,
+                              n_comm=n_comm, hop="add"))
+    for dir in ("uni", "bi"):
+        cases.append(dict(op="rs", n_ranks=8, m=256, k=6144, n=12288, dir=dir, chunks=1, out_dtype="bf16", n_comm=1,
+                          hop="add"))
     for op in ("ag", "rs", "rs_pipe"):
         for kw in (dict(), dict(copy_gbps=1.0)):
             cases.append(dict(op=op, n_ranks=4, m=64, k=256, n=256, sched="auto", out_dtype="f32", n_comm=2, **kw))
