@@ -12,6 +12,15 @@ and stores them as bfloat16.  Shapes follow the library's layout:
                         w [N, n, k]     (row-parallel weight shards, stored
                                          one output feature per row)
 
+The transformer layer around the two ops (layer_inputs) adds the attention
+and MLP weights of one sequence-parallel layer:
+
+    x [N, m, d], wqkv [N, 3*H*D, d], wo [N, d, H*D], w1 [N, f/N, d],
+    w2 [N, d, f/N]   (H heads of D dimensions per rank)
+
+and the stand-alone attention and LayerNorm inputs (attention_inputs:
+qkv [N, T, 3*H*D]; layernorm_inputs: fp32 rows).
+
 Distributions: "normal" draws activations from N(0, 1) and weights from
 N(0, 0.02^2); "int" draws every element uniformly from {-3, ..., 3}, which
 bf16 holds exactly and whose products and sums stay exact in fp32.
@@ -115,3 +124,59 @@ def rs_inputs_torch(N, m, k, n, dist="normal", seed=0, device="cuda"):
     g.manual_seed(seed * 4 + 3)
     w = _torch_draw((N, n, k), dist, WEIGHT_STD, g, device)
     return h, w
+
+
+def _layer_streams(seed):
+    # independent of the (X, W1, H, W2) streams above
+    return [np.random.Generator(np.random.PCG64(s)) for s in np.random.SeedSequence([seed, 5]).spawn(5)]
+
+
+def layer_inputs(N, m, d, heads, head_dim, f_per_rank, dist="normal", seed=0):
+    """(x, wqkv, wo, w1, w2) of one sequence-parallel layer as bf16 bit
+    patterns (numpy, CPU): activations N(0,1), weights N(0, 0.02^2)."""
+    g = _layer_streams(seed)
+    HD = heads * head_dim
+    x = f32_to_bf16_bits(_draw(g[0], (N, m, d), dist, ACT_STD))
+    wqkv = f32_to_bf16_bits(_draw(g[1], (N, 3 * HD, d), dist, WEIGHT_STD))
+    wo = f32_to_bf16_bits(_draw(g[2], (N, d, HD), dist, WEIGHT_STD))
+    w1 = f32_to_bf16_bits(_draw(g[3], (N, f_per_rank, d), dist, WEIGHT_STD))
+    w2 = f32_to_bf16_bits(_draw(g[4], (N, d, f_per_rank), dist, WEIGHT_STD))
+    return x, wqkv, wo, w1, w2
+
+
+def layer_inputs_torch(N, m, d, heads, head_dim, f_per_rank, dist="normal", seed=0, device="cuda"):
+    """The same tensors drawn on `device` (torch.bfloat16), for full sizes."""
+    import torch
+    g = torch.Generator(device=device)
+    HD = heads * head_dim
+    shapes = [((N, m, d), ACT_STD), ((N, 3 * HD, d), WEIGHT_STD), ((N, d, HD), WEIGHT_STD),
+              ((N, f_per_rank, d), WEIGHT_STD), ((N, d, f_per_rank), WEIGHT_STD)]
+    out = []
+    for i, (shape, std) in enumerate(shapes):
+        g.manual_seed(seed * 8 + 100 + i)
+        out.append(_torch_draw(shape, dist, std, g, device))
+    return tuple(out)
+
+
+def attention_inputs(N, T, heads, head_dim, std=1.8, seed=0):
+    """qkv [N, T, 3*heads*head_dim] bf16 bits, N(0, std^2) (std 1.8 is the
+    spread of a projection of N(0,1) activations by N(0, 0.02^2) weights over
+    d = 8192: sqrt(8192) * 0.02 = 1.81)."""
+    gen = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 6])))
+    return f32_to_bf16_bits(_draw(gen, (N, T, 3 * heads * head_dim), "normal", std))
+
+
+def attention_inputs_torch(N, T, heads, head_dim, std=1.8, seed=0, device="cuda"):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed * 8 + 110)
+    return _torch_draw((N, T, 3 * heads * head_dim), "normal", std, g, device)
+
+
+def layernorm_inputs(rows, cols, seed=0):
+    """fp32 rows x[i] = mu_i + s_i * z with z ~ N(0,1), per-row offsets
+    mu_i ~ N(0, 2^2) and spreads s_i uniform in [0.25, 4] (numpy float32)."""
+    gen = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 7])))
+    mu = gen.standard_normal((rows, 1), dtype=np.float32) * np.float32(2.0)
+    sd = gen.uniform(0.25, 4.0, (rows, 1)).astype(np.float32)
+    return (mu + sd * gen.standard_normal((rows, cols), dtype=np.float32)).astype(np.float32)

@@ -9,6 +9,8 @@ arrays of bf16 bit patterns; outputs are float64.  Shapes:
     ag_gemm:  x [N, m, k], w [N, n, k]    -> y   [N, N*m, n]
     gemm_rs:  h [N, N*m, k], w [N, n, k]  -> out [N, m, n]
     allreduce: same inputs as gemm_rs     -> ar  [N*m, n]
+and the sequence-parallel transformer layer around them (attention,
+LayerNorm, GELU and the chained layer, sp_layer_rows).
 """
 import ctypes
 import os
@@ -54,6 +56,12 @@ def _bind(lib):
     lib.orc_gemm_rs_bf16_bucket_rows.argtypes = [ci, ci, ci, ci, u16p, u16p, ci, ci, i32p, i32p, f64p, f64p_or_null, f64p_or_null]
     lib.orc_round_bf16.restype = None
     lib.orc_round_bf16.argtypes = [f64p, u16p, ctypes.c_size_t]
+    lib.orc_attention_rows.restype = None
+    lib.orc_attention_rows.argtypes = [ci, ci, ci, ci, ci, u16p, ci, i32p, i32p, i32p, f64p, f64p_or_null]
+    lib.orc_layernorm.restype = None
+    lib.orc_layernorm.argtypes = [ci, ci, f64p, ctypes.c_double, f64p_or_null, f64p_or_null, f64p]
+    lib.orc_gelu.restype = None
+    lib.orc_gelu.argtypes = [f64p, f64p, ctypes.c_size_t]
     return lib
 
 
@@ -184,3 +192,128 @@ def round_bf16(values, lib=None):
     out = np.empty(v.shape, np.uint16)
     lib.orc_round_bf16(v.reshape(-1), out.reshape(-1), v.size)
     return out
+
+
+# ---------------------------------------------------------------- the layer
+def bf16_to_f64(bits):
+    """bf16 bit patterns -> float64 (exact: a bf16 value is a binary32 value)."""
+    b = np.ascontiguousarray(bits, np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def attention_rows(qkv, heads, ranks, head_idx, rows, causal=True, with_mag=False, lib=None):
+    """Attention output rows (see oracle.c): qkv [N, T, 3*heads*D] bf16 bits;
+    sample s is query row rows[s] of head head_idx[s] of rank ranks[s].
+    Returns out [ns, D] (and mag [ns, D])."""
+    lib = lib or load()
+    qkv = _u16(qkv)
+    N, T, c3 = qkv.shape
+    assert c3 % (3 * heads) == 0
+    D = c3 // (3 * heads)
+    ranks = np.ascontiguousarray(ranks, np.int32)
+    head_idx = np.ascontiguousarray(head_idx, np.int32)
+    rows = np.ascontiguousarray(rows, np.int32)
+    assert ranks.shape == head_idx.shape == rows.shape and ranks.ndim == 1
+    assert ((0 <= ranks) & (ranks < N)).all() and ((0 <= head_idx) & (head_idx < heads)).all()
+    assert ((0 <= rows) & (rows < T)).all()
+    out = np.empty((len(rows), D), np.float64)
+    mag = np.empty_like(out) if with_mag else None
+    lib.orc_attention_rows(N, T, heads, D, 1 if causal else 0, qkv, len(rows), ranks, head_idx, rows, out, _ptr(mag))
+    return (out, mag) if with_mag else out
+
+
+def attention(qkv, heads, causal=True, with_mag=False, lib=None):
+    """Every output row: [N, T, heads*D] (head h in columns h*D..)."""
+    N, T, c3 = np.asarray(qkv).shape
+    D = c3 // (3 * heads)
+    rank_g, row_g, head_g = np.meshgrid(np.arange(N), np.arange(T), np.arange(heads), indexing="ij")
+    res = attention_rows(qkv, heads, rank_g.ravel(), head_g.ravel(), row_g.ravel(), causal, with_mag, lib)
+    shape = (N, T, heads * D)
+    if with_mag:
+        return tuple(v.reshape(shape) for v in res)
+    return res.reshape(shape)
+
+
+def layernorm(x, eps=1e-5, gamma=None, beta=None, lib=None):
+    """LayerNorm over the last axis of float64 x (any leading shape)."""
+    lib = lib or load()
+    x = np.ascontiguousarray(x, np.float64)
+    cols = x.shape[-1]
+    rows = x.size // cols
+    g = None if gamma is None else np.ascontiguousarray(gamma, np.float64)
+    b = None if beta is None else np.ascontiguousarray(beta, np.float64)
+    assert g is None or g.shape == (cols,)
+    assert b is None or b.shape == (cols,)
+    y = np.empty_like(x)
+    lib.orc_layernorm(rows, cols, x.reshape(rows, cols), float(eps), _ptr(g), _ptr(b), y.reshape(rows, cols))
+    return y
+
+
+def gelu(x, lib=None):
+    """GELU (erf form) of float64 values, elementwise."""
+    lib = lib or load()
+    x = np.ascontiguousarray(x, np.float64)
+    y = np.empty_like(x)
+    lib.orc_gelu(x.reshape(-1), y.reshape(-1), x.size)
+    return y
+
+
+def sp_layer_rows(x, wqkv, wo, w1, w2, heads, tokens, eps=1e-5, causal=True, lib=None):
+    """The sequence-parallel transformer-layer forward at selected tokens.
+
+    Inputs (bf16 bit patterns, the library's layouts):
+        x     [N, m, d]          sequence shards (T = N*m tokens)
+        wqkv  [N, 3*heads*D, d]  rank r's query/key/value projection (heads
+                                 r*heads .. of the layer), one output per row
+        wo    [N, d, heads*D]    rank r's slice of the output projection
+        w1    [N, f/N, d]        rank r's fc1 columns
+        w2    [N, d, f/N]        rank r's fc2 rows
+    Chain (each stage the monolithic definition; values that the layer
+    stores as bf16 between stages are rounded to bf16, nearest-even):
+        QKV_r  = bf16(concat(x) . wqkv_r^T)                 AllGather -> GEMM
+        A_r    = bf16(attention(QKV_r))                     per head
+        P      = sum_r A_r . wo_r^T                         GEMM -> ReduceScatter
+        L      = bf16(LayerNorm(P))                         on the shard
+        F_r    = bf16(gelu(concat(L) . w1_r^T))             AllGather -> GEMM
+        Out    = sum_r F_r . w2_r^T                         GEMM -> ReduceScatter
+    tokens: global token indices g (owner g // m, row g % m of Out_owner).
+    Returns a dict of float64 arrays, one row per token: "out" [ns, d], "mag"
+    (sum_r sum_k |F_r| |w2_r| of the last contraction), and the stages
+    "attn" [N, ns, heads*D] (unrounded), "proj" [ns, d], "ln" [ns, d]
+    (rounded values) and "fc1" [N, ns, f/N] (rounded values)."""
+    lib = lib or load()
+    x, wqkv, wo, w1, w2 = (_u16(a) for a in (x, wqkv, wo, w1, w2))
+    N, m, d = x.shape
+    T = N * m
+    HD = wqkv.shape[1] // 3
+    assert wqkv.shape == (N, 3 * HD, d) and HD % heads == 0
+    assert wo.shape == (N, d, HD)
+    fN = w1.shape[1]
+    assert w1.shape == (N, fN, d) and w2.shape == (N, d, fN)
+    tokens = np.ascontiguousarray(tokens, np.int64)
+    assert tokens.ndim == 1 and ((0 <= tokens) & (tokens < T)).all()
+    ns = len(tokens)
+    rows_needed = int(tokens.max()) + 1 if causal else T
+    xf = bf16_to_f64(x).reshape(T, d)
+    qkv = np.empty((N, rows_needed, 3 * HD), np.uint16)
+    for r in range(N):
+        qkv[r] = round_bf16(xf[:rows_needed] @ bf16_to_f64(wqkv[r]).T, lib)
+    rr = np.repeat(np.arange(N), ns * heads)
+    tt = np.tile(np.repeat(tokens, heads), N)
+    hh = np.tile(np.arange(heads), N * ns)
+    attn = attention_rows(qkv, heads, rr, hh, tt, causal, False, lib).reshape(N, ns, HD)
+    attn_b = bf16_to_f64(round_bf16(attn, lib))
+    proj = np.zeros((ns, d))
+    for r in range(N):
+        proj += attn_b[r] @ bf16_to_f64(wo[r]).T
+    ln = bf16_to_f64(round_bf16(layernorm(proj, eps, lib=lib), lib))
+    fc1 = np.empty((N, ns, fN))
+    for r in range(N):
+        fc1[r] = bf16_to_f64(round_bf16(gelu(ln @ bf16_to_f64(w1[r]).T, lib), lib))
+    out = np.zeros((ns, d))
+    mag = np.zeros((ns, d))
+    for r in range(N):
+        w2r = bf16_to_f64(w2[r])
+        out += fc1[r] @ w2r.T
+        mag += np.abs(fc1[r]) @ np.abs(w2r).T
+    return {"out": out, "mag": mag, "attn": attn, "proj": proj, "ln": ln, "fc1": fc1}

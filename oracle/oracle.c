@@ -44,6 +44,10 @@
  *   bucket stored in bf16 between hops): the definition above with the
  *   bucket rounded to bf16 after every addition, in ring order.
  *
+ *   The transformer layer around them (attention, LayerNorm, GELU): see the
+ *   section at the end of this file; the chained layer is composed in
+ *   oracle/__init__.py.
+ *
  * Parity pins: see the tests (brute force on tiny shapes, closed forms,
  * N = 1 against a library matmul, the AllReduce invariant, planted
  * mistakes).  The bf16 rounding routine is pinned by hand-derived tie cases;
@@ -314,4 +318,105 @@ void orc_gemm_rs_bf16_bucket_rows(int N, int m, int k, int n, const uint16_t *h,
     }
     free(z);
   }
+}
+
+/* ------------------------------------------------------------------------
+ * The sequence-parallel transformer layer around the collective matmuls
+ * (attention between the AllGather->QKV projection and the output projection's
+ * ReduceScatter; LayerNorm on the sequence shard between that ReduceScatter and
+ * the next AllGather, the "do per-token work on the small shard" point of the
+ * all-reduce paragraph of "Tensor Parallelism > Communication Patterns"; the
+ * MLP activation between fc1 and fc2).  The pages name these stages but give
+ * no formulas for them; the definitions below are the textbook ones:
+ *
+ *   attention (one head, query row t):
+ *       s_j   = (q_t . k_j) / sqrt(D)     for j <= t (causal) or all j
+ *       p_j   = exp(s_j - max_j s_j)
+ *       out_t = sum_j p_j v_j / sum_j p_j
+ *   LayerNorm (one row x of length n):
+ *       mu = sum x / n,  var = sum (x - mu)^2 / n   (population variance)
+ *       y  = (x - mu) / sqrt(var + eps) * gamma + beta
+ *   GELU (exact form): gelu(x) = x * Phi(x) = 0.5 * x * (1 + erf(x / sqrt 2))
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Attention at selected (rank, head, query row) triples.
+ *   qkv  [N][T][3*H*D] bf16: rank r's projection output; columns h*D.. hold
+ *        the query of head h, H*D + h*D.. its key, 2*H*D + h*D.. its value
+ *   out  [ns][D]: the head's output row
+ *   mag  [ns][D] or NULL: sum_j p_j |v_jd| / sum_j p_j (the error scale of the
+ *        weighted sum)
+ */
+void orc_attention_rows(int N, int T, int H, int D, int causal, const uint16_t *qkv, int ns,
+                        const int *rank, const int *head, const int *row, double *out, double *mag) {
+  (void)N;
+  const size_t ld = (size_t)3 * H * D;
+  const double scale = 1.0 / sqrt((double)D);
+#pragma omp parallel
+  {
+    double *s = (double *)malloc(sizeof(double) * (size_t)T);
+#pragma omp for schedule(dynamic)
+    for (int t = 0; t < ns; ++t) {
+      const int r = rank[t], h = head[t], i = row[t];
+      const uint16_t *base = qkv + (size_t)r * T * ld;
+      const uint16_t *q = base + (size_t)i * ld + (size_t)h * D;
+      const int nk = causal ? i + 1 : T;
+      double mx = -INFINITY;
+      for (int j = 0; j < nk; ++j) {
+        const uint16_t *kj = base + (size_t)j * ld + (size_t)H * D + (size_t)h * D;
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d) dot += bf16_value(q[d]) * bf16_value(kj[d]);
+        s[j] = dot * scale;
+        if (s[j] > mx) mx = s[j];
+      }
+      double z = 0.0;
+      for (int j = 0; j < nk; ++j) {
+        s[j] = exp(s[j] - mx);
+        z += s[j];
+      }
+      double *o = out + (size_t)t * D;
+      double *mg = mag ? mag + (size_t)t * D : NULL;
+      for (int d = 0; d < D; ++d) {
+        double acc = 0.0, accabs = 0.0;
+        for (int j = 0; j < nk; ++j) {
+          const double v = bf16_value(base[(size_t)j * ld + (size_t)2 * H * D + (size_t)h * D + d]);
+          acc += s[j] * v;
+          accabs += s[j] * fabs(v);
+        }
+        o[d] = acc / z;
+        if (mg) mg[d] = accabs / z;
+      }
+    }
+    free(s);
+  }
+}
+
+/*
+ * LayerNorm of every row of x [rows][cols] (fp64 values) into y; gamma and
+ * beta [cols] or NULL (1 and 0).
+ */
+void orc_layernorm(int rows, int cols, const double *x, double eps, const double *gamma,
+                   const double *beta, double *y) {
+#pragma omp parallel for schedule(static)
+  for (int i = 0; i < rows; ++i) {
+    const double *xi = x + (size_t)i * cols;
+    double *yi = y + (size_t)i * cols;
+    double sum = 0.0;
+    for (int j = 0; j < cols; ++j) sum += xi[j];
+    const double mu = sum / cols;
+    double ss = 0.0;
+    for (int j = 0; j < cols; ++j) ss += (xi[j] - mu) * (xi[j] - mu);
+    const double inv = 1.0 / sqrt(ss / cols + eps);
+    for (int j = 0; j < cols; ++j) {
+      double v = (xi[j] - mu) * inv;
+      if (gamma) v *= gamma[j];
+      if (beta) v += beta[j];
+      yi[j] = v;
+    }
+  }
+}
+
+/* GELU, exact (erf) form, elementwise. */
+void orc_gelu(const double *x, double *y, size_t count) {
+  for (size_t t = 0; t < count; ++t) y[t] = 0.5 * x[t] * (1.0 + erf(x[t] / sqrt(2.0)));
 }
