@@ -21,10 +21,12 @@ CM_BUF_X, CM_BUF_W, CM_BUF_Y, CM_BUF_WS = range(4)
 CM_OPK_GEMM, CM_OPK_COPY, CM_OPK_RECORD, CM_OPK_WAIT, CM_OPK_REDUCE = range(5)
 CM_EXEC_GRAPH, CM_EXEC_EAGER = range(2)
 CM_COPY_SDMA, CM_COPY_CU = range(2)
+CM_ACT_NONE, CM_ACT_GELU = range(2)
 CM_MAX_RANKS, CM_MAX_CHUNKS, CM_MAX_COMM = 64, 16, 32
 
 EXPORTS = ["cm_ring_plan", "cm_pick_overlap", "cm_workspace_size", "cm_plan_program", "cm_trace_create", "cm_trace_destroy",
-           "cm_trace_read", "cm_ag_gemm", "cm_gemm_rs", "cm_status_string", "cm_last_error", "cm_version"]
+           "cm_trace_read", "cm_ag_gemm", "cm_gemm_rs", "cm_attention", "cm_layernorm", "cm_plan_layer",
+           "cm_layer_forward", "cm_status_string", "cm_last_error", "cm_version"]
 
 
 class cm_plan_desc(ctypes.Structure):
@@ -34,7 +36,7 @@ class cm_plan_desc(ctypes.Structure):
                 ("tile_m", ctypes.c_int), ("tile_n", ctypes.c_int), ("exec_mode", ctypes.c_int),
                 ("copy_engine", ctypes.c_int), ("bucket_bf16", ctypes.c_int), ("hop_add", ctypes.c_int),
                 ("copy_gbps", ctypes.c_double),
-                ("mfma_tflops", ctypes.c_double), ("launch_us", ctypes.c_double)]
+                ("mfma_tflops", ctypes.c_double), ("launch_us", ctypes.c_double), ("act", ctypes.c_int)]
 
 
 class cm_plan(ctypes.Structure):
@@ -51,7 +53,8 @@ class cm_op_rec(ctypes.Structure):
                 ("chunk", ctypes.c_int), ("first_job", ctypes.c_int), ("n_jobs", ctypes.c_int),
                 ("rows", ctypes.c_int), ("cols", ctypes.c_int), ("depth", ctypes.c_int), ("tile_m", ctypes.c_int),
                 ("tile_n", ctypes.c_int), ("src_buf", ctypes.c_int), ("dst_buf", ctypes.c_int),
-                ("src_off", ctypes.c_size_t), ("dst_off", ctypes.c_size_t), ("bytes", ctypes.c_size_t)]
+                ("src_off", ctypes.c_size_t), ("dst_off", ctypes.c_size_t), ("bytes", ctypes.c_size_t),
+                ("act", ctypes.c_int)]
 
 
 class cm_job_rec(ctypes.Structure):
@@ -66,6 +69,17 @@ class cm_job_rec(ctypes.Structure):
 class cm_span(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int), ("stream", ctypes.c_int), ("step", ctypes.c_int), ("chunk", ctypes.c_int),
                 ("start_us", ctypes.c_double), ("end_us", ctypes.c_double)]
+
+
+class cm_layer_desc(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_int) for f in ("n_ranks", "m", "d", "heads", "head_dim", "ffn", "dir", "n_comm",
+                                            "copy_engine", "exec_mode", "ag_chunks", "rs_chunks", "proj_chunks",
+                                            "out_dtype")] + [("ln_eps", ctypes.c_float)]
+
+
+class cm_layer_plan(ctypes.Structure):
+    _fields_ = [("desc", cm_layer_desc), ("qkv", cm_plan), ("proj", cm_plan), ("fc1", cm_plan), ("fc2", cm_plan)] + \
+        [(f, ctypes.c_size_t) for f in ("off_qkv", "off_attn", "off_proj", "off_ln", "off_fc1", "off_ops", "ws_bytes")]
 
 
 class CMError(RuntimeError):
@@ -97,6 +111,11 @@ def lib():
         L.cm_trace_read.argtypes = [vp, ctypes.POINTER(cm_span), ci, ctypes.POINTER(ci), ctypes.POINTER(ctypes.c_double)]
         for f in (L.cm_ag_gemm, L.cm_gemm_rs):
             f.argtypes = [ctypes.POINTER(cm_plan), vp, vp, vp, vp, cs, vp, ctypes.POINTER(vp), ci, vp]
+        L.cm_attention.argtypes = [vp, vp, ci, ci, ci, ci, ci, vp]
+        L.cm_layernorm.argtypes = [vp, vp, ci, ci, ctypes.c_float, vp, vp, vp]
+        L.cm_plan_layer.argtypes = [ctypes.POINTER(cm_layer_desc), ctypes.POINTER(cm_layer_plan)]
+        L.cm_layer_forward.argtypes = [ctypes.POINTER(cm_layer_plan), vp, vp, vp, vp, vp, vp, vp, cs, vp,
+                                       ctypes.POINTER(vp), ci]
         for name in EXPORTS:
             if name in ("cm_status_string", "cm_last_error", "cm_version"):
                 continue
@@ -139,12 +158,13 @@ _ENUMS = {
     "exec": {"graph": CM_EXEC_GRAPH, "eager": CM_EXEC_EAGER},
     "copy": {"sdma": CM_COPY_SDMA, "cu": CM_COPY_CU},
     "hop": {"copy": 0, "add": 1},
+    "act": {"none": CM_ACT_NONE, "gelu": CM_ACT_GELU},
 }
 
 
 def make_desc(op, n_ranks, m, k, n, dir="uni", chunks=0, sched="decomposed", out_dtype="bf16", n_comm=1,
               tile=(0, 0), exec_mode="graph", copy_engine="sdma", bucket="f32", hop="copy", copy_gbps=0.0,
-              mfma_tflops=0.0, launch_us=0.0):
+              mfma_tflops=0.0, launch_us=0.0, act="none"):
     """A cm_plan_desc from keyword arguments (strings or enum values)."""
     def e(kind, v):
         return _ENUMS[kind][v] if isinstance(v, str) else int(v)
@@ -153,7 +173,7 @@ def make_desc(op, n_ranks, m, k, n, dir="uni", chunks=0, sched="decomposed", out
                         n_comm=n_comm, tile_m=tile[0], tile_n=tile[1], exec_mode=e("exec", exec_mode),
                         copy_engine=e("copy", copy_engine), bucket_bf16=1 if bucket == "bf16" else 0,
                         hop_add=e("hop", hop), copy_gbps=copy_gbps,
-                        mfma_tflops=mfma_tflops, launch_us=launch_us)
+                        mfma_tflops=mfma_tflops, launch_us=launch_us, act=e("act", act))
 
 
 def cm_ring_plan(desc=None, **kw):
@@ -264,3 +284,59 @@ def cm_ag_gemm(plan, x, w, y, ws, compute, comm, trace=None, ws_bytes=None):
 def cm_gemm_rs(plan, x, w, y, ws, compute, comm, trace=None, ws_bytes=None):
     """GEMM -> ReduceScatter through the C ABI (tensors or raw device pointers)."""
     _call(lib().cm_gemm_rs, "cm_gemm_rs", plan, x, w, y, ws, ws_bytes, compute, comm, trace)
+
+
+# ------------------------------------------------------------ the layer
+def cm_attention(qkv, o, n_ranks, T, heads, head_dim=128, causal=True, stream=None):
+    """Attention of every head of every virtual rank (tensors or device pointers)."""
+    _check(lib().cm_attention(_ptr(qkv), _ptr(o), n_ranks, T, heads, head_dim, 1 if causal else 0, _stream(stream)),
+           "cm_attention")
+
+
+def cm_attention_status(qkv, o, n_ranks, T, heads, head_dim=128, causal=1, stream=None):
+    """Status code of cm_attention without raising (for error-path tests)."""
+    return lib().cm_attention(_ptr(qkv), _ptr(o), n_ranks, T, heads, head_dim, causal, _stream(stream))
+
+
+def cm_layernorm(x, y, rows, cols, eps=1e-5, gamma=None, beta=None, stream=None):
+    """LayerNorm of fp32 rows into bf16."""
+    _check(lib().cm_layernorm(_ptr(x), _ptr(y), rows, cols, eps, _ptr(gamma), _ptr(beta), _stream(stream)),
+           "cm_layernorm")
+
+
+def cm_layernorm_status(x, y, rows, cols, eps=1e-5, gamma=None, beta=None, stream=None):
+    return lib().cm_layernorm(_ptr(x), _ptr(y), rows, cols, eps, _ptr(gamma), _ptr(beta), _stream(stream))
+
+
+def make_layer_desc(n_ranks, m, d, heads, ffn, head_dim=128, dir="uni", n_comm=1, copy_engine="sdma",
+                    exec_mode="graph", ag_chunks=0, rs_chunks=0, proj_chunks=0, out_dtype="f32", ln_eps=0.0):
+    def e(kind, v):
+        return _ENUMS[kind][v] if isinstance(v, str) else int(v)
+    return cm_layer_desc(n_ranks=n_ranks, m=m, d=d, heads=heads, head_dim=head_dim, ffn=ffn, dir=e("dir", dir),
+                         n_comm=n_comm, copy_engine=e("copy", copy_engine), exec_mode=e("exec", exec_mode),
+                         ag_chunks=ag_chunks, rs_chunks=rs_chunks, proj_chunks=proj_chunks,
+                         out_dtype=e("dtype", out_dtype), ln_eps=ln_eps)
+
+
+def cm_plan_layer(desc=None, **kw):
+    """cm_plan_layer(desc) or cm_plan_layer(n_ranks=..., ...) -> cm_layer_plan."""
+    if desc is None:
+        desc = make_layer_desc(**kw)
+    p = cm_layer_plan()
+    _check(lib().cm_plan_layer(ctypes.byref(desc), ctypes.byref(p)), "cm_plan_layer")
+    return p
+
+
+def cm_plan_layer_status(desc):
+    p = cm_layer_plan()
+    return lib().cm_plan_layer(ctypes.byref(desc), ctypes.byref(p)), p
+
+
+def cm_layer_forward(plan, x, wqkv, wo, w1, w2, out, ws, compute, comm, ws_bytes=None):
+    """The layer forward through the C ABI."""
+    comm = list(comm or [])
+    arr = (ctypes.c_void_p * max(1, len(comm)))(*[_stream(s) for s in comm])
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(lib().cm_layer_forward(ctypes.byref(plan), _ptr(x), _ptr(wqkv), _ptr(wo), _ptr(w1), _ptr(w2), _ptr(out),
+                                  _ptr(ws), ws_bytes, _stream(compute), arr, len(comm)), "cm_layer_forward")

@@ -54,10 +54,10 @@ std::string plan_key(const cm_plan &p) {
   // Every field the program depends on (struct padding is not part of it).
   const cm_plan_desc &d = p.desc;
   char buf[512];
-  std::snprintf(buf, sizeof buf, "%d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %a %a %a|%d %d %d %d %d %d %d %zu",
+  std::snprintf(buf, sizeof buf, "%d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %a %a %a %d|%d %d %d %d %d %d %d %zu",
                 d.op, d.n_ranks, d.m, d.k, d.n, d.dir, d.chunks, d.sched, d.in_dtype, d.out_dtype, d.n_comm, d.tile_m,
                 d.tile_n, d.exec_mode, d.copy_engine, d.bucket_bf16, d.hop_add, d.copy_gbps, d.mfma_tflops,
-                d.launch_us, p.chunks, p.n_steps, p.arc_cw, p.arc_ccw, p.tile_m, p.tile_n, p.n_events, p.ws_bytes);
+                d.launch_us, d.act, p.chunks, p.n_steps, p.arc_cw, p.arc_ccw, p.tile_m, p.tile_n, p.n_events, p.ws_bytes);
   return buf;
 }
 
@@ -161,6 +161,13 @@ cm_status fill_params(const cm_op_rec &o, const cm_job_rec *jobs, Launch &L) {
     }
   }
   p.add_bf16 = add_dtype == CM_BF16;
+  if (o.kind == CM_OPK_GEMM && o.act != CM_ACT_NONE) {
+    if (o.act != CM_ACT_GELU || add_dtype >= 0) {
+      set_error("an epilogue activation needs a launch without addends");
+      return CM_ERR_UNSUPPORTED;
+    }
+    p.act = o.act;
+  }
   return CM_OK;
 }
 

@@ -19,6 +19,7 @@ struct GemmParams {
   int lda, ldb, ldc, ld_in;  // row strides in elements
   int c_f32;                 // 1: C is fp32, 0: C is bf16 (round to nearest even)
   int add_bf16;              // 1: the addends in0/in1 are bf16, 0: fp32
+  int act;                   // epilogue activation of launches without addends: 0 none, 1 GELU (erf form)
   int n_jobs;
   int tiles_m;               // row tiles per job
   int tiles_per_job;

@@ -4,7 +4,9 @@
 //      C[i][j] = sum_kk A[i][kk] * B[j][kk] (+ in0[i][j]) (+ in1[i][j]),
 //    A, B bf16 with K contiguous, fp32 accumulation on the matrix cores
 //    (v_mfma_f32_32x32x16_bf16).  The epilogue covers the three uses in the
-//    schedules: a plain store at a row offset of Y (the slice update of the
+//    schedules (and, for launches without addends, an optional GELU applied
+//    before the store: the MLP activation fused into the AllGather->fc1
+//    slice update): a plain store at a row offset of Y (the slice update of the
 //    AllGather loop), a read-add-write into the fp32 bucket that circulates in
 //    the ReduceScatter loop, and the owner's final add of one or two arriving
 //    buckets with rounding to the output type (the realigning addition of
@@ -69,7 +71,10 @@ __device__ __forceinline__ float addend(const void *p, size_t ii) {
   return reinterpret_cast<const float *>(p)[ii];
 }
 
-template <int TM, int TN, bool F32, bool H0, bool H1, bool HB>
+// GELU, erf form: x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2)), in fp32.
+__device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.f + erff(x * 0.70710678118654752f)); }
+
+template <int TM, int TN, bool F32, bool H0, bool H1, bool HB, bool GELU = false>
 __device__ __forceinline__ void epilogue(const f32x16 (&acc)[TM][TN], const EpiArgs &a) {
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -99,7 +104,8 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[TM][TN], const EpiA
           const int e = h * 8 + q;
           const int row = a.row0 + i * 32 + 8 * (e >> 2) + (e & 3);
           if (col_ok && row < a.M) {
-            const float v = (H0 || H1) ? acc[i][j][e] + add[q] : acc[i][j][e];
+            float v = (H0 || H1) ? acc[i][j][e] + add[q] : acc[i][j][e];
+            if (GELU) v = gelu_erf(v);
             const size_t oc = (size_t)row * a.ldc + col;
             if (F32)
               reinterpret_cast<float *>(a.C)[oc] = v;
@@ -424,10 +430,16 @@ __global__ __launch_bounds__(512 + 64 * NL) void gemm_jobs_kernel(const GemmPara
   ea.col0 = tn0 + wn * WTN + (lane & 31);
   const int mode = (p.c_f32 ? 1 : 0) | (((sel >> 6) & 1) << 1) | (((sel >> 7) & 1) << 2);
   if (!ADD) {
-    if (mode & 1)
+    if (p.act == 1) {
+      if (mode & 1)
+        epilogue<TM, TN, true, false, false, false, true>(acc, ea);
+      else
+        epilogue<TM, TN, false, false, false, false, true>(acc, ea);
+    } else if (mode & 1) {
       epilogue<TM, TN, true, false, false, false>(acc, ea);
-    else
+    } else {
       epilogue<TM, TN, false, false, false, false>(acc, ea);
+    }
     return;
   }
   if (p.add_bf16)

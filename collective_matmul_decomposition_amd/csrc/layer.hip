@@ -1,0 +1,527 @@
+// The sequence-parallel transformer layer around the two decomposed
+// collective matmuls: the stages between them (causal attention, LayerNorm on
+// the sequence shard) and the layer forward that chains
+//
+//   AllGather -> QKV projection      (cm_ag_gemm, decomposed)
+//   attention, every rank's heads    (attn_fwd_kernel)
+//   output projection -> ReduceScatter (cm_gemm_rs, pipeline chunks)
+//   LayerNorm on the [m x d] shard   (layernorm_kernel)
+//   AllGather -> fc1, GELU fused     (cm_ag_gemm, decomposed)
+//   fc2 -> ReduceScatter             (cm_gemm_rs, decomposed)
+//
+// The Megatron page's sequence parallelism places the LayerNorm on the
+// sequence-sharded activation between the ReduceScatter of one block and the
+// AllGather of the next; "Tensor Parallelism > Communication Patterns" notes
+// the same point, between the two halves of an all-reduce.  The pages give no
+// formulas for attention, LayerNorm or the activation: the kernels compute the
+// textbook definitions (scaled dot-product attention with a causal mask,
+// population-variance LayerNorm, GELU in its erf form).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cmath>
+#include <cstring>
+
+#include "collmm.h"
+#include "internal.h"
+
+namespace collmm {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return 0x7FC0u;  // NaN
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ float bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// ------------------------------------------------------------------ attention
+//
+// One workgroup: 128 query rows of one head of one virtual rank; 4 waves of
+// 32 query rows each.  Keys and values stream through LDS in blocks of 64.
+// The scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16,
+// keys as rows), so that every lane of a wave owns one query: the running
+// maximum, the exponentials and the running sum stay in the lane (plus one
+// exchange with the lane 32 away, which holds the other half of the block's
+// keys for the same query).  The output is accumulated transposed as well,
+// O^T += V^T P^T: the probabilities are the B operand straight from the
+// score registers (rounded to bf16), and V is written to LDS transposed.
+// Within a 16-key MFMA step lane group g supplies keys {4g..4g+3, 8+4g..8+4g+3}
+// of P and of V^T alike; the contraction only needs the two operands to agree.
+// The probabilities' bf16 values feed both the numerator and the running sum,
+// so every output row is a convex combination of the value rows.
+constexpr int kAttnD = 128;   // head dimension
+constexpr int kAttnBQ = 128;  // query rows per workgroup
+constexpr int kAttnBK = 64;   // keys per block
+
+struct AttnParams {
+  const uint16_t *qkv;  // [N][T][3*H*D]
+  uint16_t *o;          // [N][T][H*D]
+  int T, H;
+  int ld_qkv, ld_o;     // row strides in elements
+  int causal;
+  int qblocks;          // ceil(T / 128)
+  float scale_log2;     // log2(e) / sqrt(D)
+};
+
+__device__ __forceinline__ int attn_logical_block() {
+  // block b runs on XCD b % 8: give each XCD a contiguous range of logical
+  // blocks, so the query blocks of one head (which share its keys and values)
+  // meet in one L2
+  const int G = gridDim.x, b = blockIdx.x;
+  const int per = G >> 3;
+  return b < per * 8 ? (b & 7) * per + (b >> 3) : b;
+}
+
+__global__ __launch_bounds__(256) void attn_fwd_kernel(const AttnParams p) {
+  // K block [64 keys][128 dims]: 256-byte rows of 16 chunks of 16 bytes,
+  // chunk c of key row r stored at position c ^ (r % 16).
+  __shared__ __attribute__((aligned(16))) char sK[kAttnBK * kAttnD * 2];
+  // V^T block [128 dims][64 keys]: 128-byte rows of 16 units of 4 keys,
+  // unit u of dim row r stored at position u ^ ((r / 2) % 16).
+  __shared__ __attribute__((aligned(16))) char sV[kAttnD * kAttnBK * 2];
+
+  const int lb = attn_logical_block();
+  const int bh = lb / p.qblocks;
+  const int qb = p.qblocks - 1 - (lb - bh * p.qblocks);  // long (late) query blocks first
+  const int rank = bh / p.H, head = bh - rank * p.H;
+  const uint16_t *base = p.qkv + (size_t)rank * p.T * p.ld_qkv;
+  const int qcol = head * kAttnD, kcol = (p.H + head) * kAttnD, vcol = (2 * p.H + head) * kAttnD;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int q0 = qb * kAttnBQ + wave * 32;  // the wave's first query
+  const int my_q = q0 + l32;                // the lane's query
+
+  // B operand of S^T = K Q^T: lane (query l32, group g) holds
+  // Q[my_q][16 ks + 8 g .. + 8] for the 8 MFMA steps over D = 128.
+  bf16x8 qf[8];
+  {
+    const uint16_t *qrow = base + (size_t)min(my_q, p.T - 1) * p.ld_qkv + qcol + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = *reinterpret_cast<const bf16x8 *>(qrow + 16 * ks);
+  }
+
+  f32x16 oacc[4];  // O^T tiles: dims 32 dt .. 32 dt + 31 x this wave's queries
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[dt][e] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int kv_end = p.causal ? min(p.T, (qb + 1) * kAttnBQ) : p.T;
+  const int nblk = (kv_end + kAttnBK - 1) / kAttnBK;
+  const int dg = tid & 15, kgp = tid >> 4;  // V staging: dims 8 dg .. 8 dg + 7 of keys 4 kgp .. 4 kgp + 3
+
+  for (int j = 0; j < nblk; ++j) {
+    const int k0 = j * kAttnBK;
+    __syncthreads();  // every wave is done with the previous block
+    // K block: 1024 chunks of 16 bytes, 4 per thread, rows read whole
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i, key = c >> 4, ch = c & 15;
+      const uint4 v = *reinterpret_cast<const uint4 *>(base + (size_t)min(k0 + key, p.T - 1) * p.ld_qkv + kcol + 8 * ch);
+      *reinterpret_cast<uint4 *>(sK + key * 256 + ((ch ^ (key & 15)) << 4)) = v;
+    }
+    // V block, transposed: this thread's 4 keys x 8 dims
+    {
+      uint32_t w[4][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 v =
+            *reinterpret_cast<const uint4 *>(base + (size_t)min(k0 + 4 * kgp + i, p.T - 1) * p.ld_qkv + vcol + 8 * dg);
+        w[i][0] = v.x; w[i][1] = v.y; w[i][2] = v.z; w[i][3] = v.w;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int sh = (e & 1) * 16;
+        uint2 pk;
+        pk.x = ((w[0][e >> 1] >> sh) & 0xFFFFu) | (((w[1][e >> 1] >> sh) & 0xFFFFu) << 16);
+        pk.y = ((w[2][e >> 1] >> sh) & 0xFFFFu) | (((w[3][e >> 1] >> sh) & 0xFFFFu) << 16);
+        const int dim = 8 * dg + e;
+        *reinterpret_cast<uint2 *>(sV + dim * 128 + ((kgp ^ ((dim >> 1) & 15)) << 3)) = pk;
+      }
+    }
+    __syncthreads();
+    if (p.causal && k0 > q0 + 31) continue;  // every key of the block is after every query of the wave
+
+    // S^T = K Q^T for keys k0 .. k0 + 63 (two 32-key tiles)
+    f32x16 s[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[t][e] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int key = t * 32 + l32, ch = 2 * ks + g;
+        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(sK + key * 256 + ((ch ^ (key & 15)) << 4));
+        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[t], 0, 0, 0);
+      }
+    }
+    // online softmax: element e of tile t is key k0 + 32 t + 8 (e / 4) + 4 g + e % 4
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = k0 + t * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+        const bool ok = key < p.T && (!p.causal || key <= my_q);
+        const float v = ok ? s[t][e] * p.scale_log2 : -INFINITY;
+        s[t][e] = v;
+        mloc = fmaxf(mloc, v);
+      }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    const float m_new = fmaxf(m_run, mloc);
+    const float msub = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = exp2f(m_run - msub);  // 0 on the first block (m_run = -inf)
+    float lsum = 0.f;
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const uint32_t b = bf16_bits_rne(exp2f(s[t][e] - msub));
+        lsum += bits_to_f32(b);
+        pf[t][e >> 3][e & 7] = __builtin_bit_cast(__bf16, (uint16_t)b);
+      }
+    lsum += __shfl_xor(lsum, 32);
+    l_run = l_run * alpha + lsum;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
+
+    // O^T += V^T P^T over the block's 64 keys (four 16-key steps)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int u0 = t * 8 + h * 4 + g;  // units of keys 32 t + 16 h + 4 g .. +3 and 8 keys later
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const int dim = dt * 32 + l32, sw = (dim >> 1) & 15;
+          const uint2 lo = *reinterpret_cast<const uint2 *>(sV + dim * 128 + ((u0 ^ sw) << 3));
+          const uint2 hi = *reinterpret_cast<const uint2 *>(sV + dim * 128 + (((u0 + 2) ^ sw) << 3));
+          const uint4 both = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, both);
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t][h], oacc[dt], 0, 0, 0);
+        }
+      }
+  }
+
+  if (my_q >= p.T) return;
+  const float inv = 1.f / l_run;
+  uint16_t *orow = p.o + ((size_t)rank * p.T + my_q) * p.ld_o + head * kAttnD;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int eg = 0; eg < 4; ++eg) {
+      // elements 4 eg .. 4 eg + 3: dims 32 dt + 8 eg + 4 g .. +3
+      uint2 pk;
+      pk.x = bf16_bits_rne(oacc[dt][4 * eg + 0] * inv) | (bf16_bits_rne(oacc[dt][4 * eg + 1] * inv) << 16);
+      pk.y = bf16_bits_rne(oacc[dt][4 * eg + 2] * inv) | (bf16_bits_rne(oacc[dt][4 * eg + 3] * inv) << 16);
+      *reinterpret_cast<uint2 *>(orow + dt * 32 + 8 * eg + 4 * g) = pk;
+    }
+}
+
+// ------------------------------------------------------------------ LayerNorm
+//
+// One workgroup of 256 threads per row; the row (fp32) stays in registers,
+// VPT float4 per thread: the mean, then the variance about it (two passes over
+// registers, fp32), then y = (x - mean) / sqrt(var + eps) * gamma + beta,
+// rounded to bf16.
+__device__ __forceinline__ float block_sum_256(float v, float *red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();  // red is reused by consecutive sums
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+template <int VPT>
+__global__ __launch_bounds__(256) void layernorm_kernel(const float *x, uint16_t *y, int cols, float eps,
+                                                         const float *gamma, const float *beta) {
+  __shared__ float red[4];
+  const size_t row = blockIdx.x;
+  const float *xr = x + row * cols;
+  uint16_t *yr = y + row * cols;
+  const int c4 = cols >> 2;
+  float4 v[VPT];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int idx = threadIdx.x + 256 * i;
+    v[i] = idx < c4 ? reinterpret_cast<const float4 *>(xr)[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
+    s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+  }
+  const float mean = block_sum_256(s, red) / cols;
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    if (threadIdx.x + 256 * i < c4) {
+      const float a = v[i].x - mean, b = v[i].y - mean, c = v[i].z - mean, d = v[i].w - mean;
+      ss += (a * a + b * b) + (c * c + d * d);
+    }
+  }
+  const float rstd = 1.f / sqrtf(block_sum_256(ss, red) / cols + eps);
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int idx = threadIdx.x + 256 * i;
+    if (idx >= c4) continue;
+    float o[4] = {(v[i].x - mean) * rstd, (v[i].y - mean) * rstd, (v[i].z - mean) * rstd, (v[i].w - mean) * rstd};
+    if (gamma) {
+      const float4 gm = reinterpret_cast<const float4 *>(gamma)[idx];
+      o[0] *= gm.x; o[1] *= gm.y; o[2] *= gm.z; o[3] *= gm.w;
+    }
+    if (beta) {
+      const float4 bt = reinterpret_cast<const float4 *>(beta)[idx];
+      o[0] += bt.x; o[1] += bt.y; o[2] += bt.z; o[3] += bt.w;
+    }
+    uint2 pk;
+    pk.x = bf16_bits_rne(o[0]) | (bf16_bits_rne(o[1]) << 16);
+    pk.y = bf16_bits_rne(o[2]) | (bf16_bits_rne(o[3]) << 16);
+    reinterpret_cast<uint2 *>(yr)[idx] = pk;
+  }
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+cm_status hip_fail(hipError_t e, const char *what) {
+  set_error("%s: %s", what, hipGetErrorString(e));
+  return CM_ERR_HIP;
+}
+
+cm_status gfx950_current(void) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  hipDeviceProp_t prop;
+  if ((e = hipGetDeviceProperties(&prop, dev)) != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+    set_error("device %d is %s; this library is built for gfx950 only", dev, prop.gcnArchName);
+    return CM_ERR_UNSUPPORTED;
+  }
+  return CM_OK;
+}
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Field-wise equality (struct padding is not part of a plan).
+bool same_desc(const cm_plan_desc &a, const cm_plan_desc &b) {
+  return a.op == b.op && a.n_ranks == b.n_ranks && a.m == b.m && a.k == b.k && a.n == b.n && a.dir == b.dir &&
+         a.chunks == b.chunks && a.sched == b.sched && a.in_dtype == b.in_dtype && a.out_dtype == b.out_dtype &&
+         a.n_comm == b.n_comm && a.tile_m == b.tile_m && a.tile_n == b.tile_n && a.exec_mode == b.exec_mode &&
+         a.copy_engine == b.copy_engine && a.bucket_bf16 == b.bucket_bf16 && a.hop_add == b.hop_add &&
+         a.copy_gbps == b.copy_gbps && a.mfma_tflops == b.mfma_tflops && a.launch_us == b.launch_us && a.act == b.act;
+}
+bool same_plan(const cm_plan &a, const cm_plan &b) {
+  return same_desc(a.desc, b.desc) && a.chunks == b.chunks && a.n_steps == b.n_steps && a.arc_cw == b.arc_cw &&
+         a.arc_ccw == b.arc_ccw && a.tile_m == b.tile_m && a.tile_n == b.tile_n && a.n_ops == b.n_ops &&
+         a.n_jobs == b.n_jobs && a.n_events == b.n_events && a.ws_bytes == b.ws_bytes;
+}
+bool same_layer(const cm_layer_plan &a, const cm_layer_plan &b) {
+  const cm_layer_desc &x = a.desc, &y = b.desc;
+  return x.n_ranks == y.n_ranks && x.m == y.m && x.d == y.d && x.heads == y.heads && x.head_dim == y.head_dim &&
+         x.ffn == y.ffn && x.dir == y.dir && x.n_comm == y.n_comm && x.copy_engine == y.copy_engine &&
+         x.exec_mode == y.exec_mode && x.ag_chunks == y.ag_chunks && x.rs_chunks == y.rs_chunks &&
+         x.proj_chunks == y.proj_chunks && x.out_dtype == y.out_dtype && x.ln_eps == y.ln_eps &&
+         same_plan(a.qkv, b.qkv) && same_plan(a.proj, b.proj) && same_plan(a.fc1, b.fc1) && same_plan(a.fc2, b.fc2) &&
+         a.off_qkv == b.off_qkv && a.off_attn == b.off_attn && a.off_proj == b.off_proj && a.off_ln == b.off_ln &&
+         a.off_fc1 == b.off_fc1 && a.off_ops == b.off_ops && a.ws_bytes == b.ws_bytes;
+}
+
+}  // namespace
+
+cm_status attention_check(int n_ranks, int T, int heads, int head_dim, int causal) {
+  if (n_ranks < 1 || n_ranks > CM_MAX_RANKS || T < 1 || heads < 1 || (causal != 0 && causal != 1)) {
+    set_error("attention: need 1 <= n_ranks <= %d, T >= 1, heads >= 1, causal 0 or 1", CM_MAX_RANKS);
+    return CM_ERR_INVALID_ARG;
+  }
+  if (head_dim != kAttnD) {
+    set_error("attention: head_dim must be %d (got %d)", kAttnD, head_dim);
+    return CM_ERR_UNSUPPORTED;
+  }
+  const long long blocks = (long long)n_ranks * heads * ((T + kAttnBQ - 1) / kAttnBQ);
+  if (blocks > (1ll << 30) || (long long)T * 3 * heads * kAttnD * 2 * n_ranks > (1ll << 46)) {
+    set_error("attention: problem too large");
+    return CM_ERR_SHAPE;
+  }
+  return CM_OK;
+}
+
+cm_status layernorm_check(int rows, int cols) {
+  if (rows < 1 || cols < 4 || cols % 4 || cols > 16384) {
+    set_error("layernorm: need rows >= 1 and 4 <= cols <= 16384 with cols a multiple of 4 (got %d x %d)", rows, cols);
+    return CM_ERR_SHAPE;
+  }
+  if (rows > (1 << 30)) {
+    set_error("layernorm: too many rows");
+    return CM_ERR_SHAPE;
+  }
+  return CM_OK;
+}
+
+}  // namespace collmm
+
+using namespace collmm;
+
+extern "C" {
+
+cm_status cm_attention(const void *qkv, void *o, int n_ranks, int T, int heads, int head_dim, int causal,
+                       void *stream) {
+  cm_status st = attention_check(n_ranks, T, heads, head_dim, causal);
+  if (st != CM_OK) return st;
+  if (!qkv || !o) { set_error("attention: null qkv or o"); return CM_ERR_INVALID_ARG; }
+  if (!aligned16(qkv) || !aligned16(o)) { set_error("attention: qkv and o must be 16-byte aligned"); return CM_ERR_ALIGN; }
+  if ((st = gfx950_current()) != CM_OK) return st;
+  AttnParams p;
+  p.qkv = static_cast<const uint16_t *>(qkv);
+  p.o = static_cast<uint16_t *>(o);
+  p.T = T;
+  p.H = heads;
+  p.ld_qkv = 3 * heads * kAttnD;
+  p.ld_o = heads * kAttnD;
+  p.causal = causal;
+  p.qblocks = (T + kAttnBQ - 1) / kAttnBQ;
+  p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)kAttnD));
+  const unsigned blocks = (unsigned)(n_ranks * heads * p.qblocks);
+  hipLaunchKernelGGL(attn_fwd_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return CM_OK;
+}
+
+cm_status cm_layernorm(const void *x, void *y, int rows, int cols, float eps, const void *gamma, const void *beta,
+                       void *stream) {
+  cm_status st = layernorm_check(rows, cols);
+  if (st != CM_OK) return st;
+  if (!x || !y) { set_error("layernorm: null x or y"); return CM_ERR_INVALID_ARG; }
+  if (!(eps >= 0.f) || std::isinf(eps)) { set_error("layernorm: eps must be finite and >= 0"); return CM_ERR_INVALID_ARG; }
+  if (!aligned16(x) || !aligned16(y) || (gamma && !aligned16(gamma)) || (beta && !aligned16(beta))) {
+    set_error("layernorm: x, y, gamma and beta must be 16-byte aligned");
+    return CM_ERR_ALIGN;
+  }
+  if ((st = gfx950_current()) != CM_OK) return st;
+  const float *xf = static_cast<const float *>(x);
+  uint16_t *yb = static_cast<uint16_t *>(y);
+  const float *gm = static_cast<const float *>(gamma), *bt = static_cast<const float *>(beta);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int vpt = (cols / 4 + 255) / 256;
+  if (vpt <= 1) hipLaunchKernelGGL(layernorm_kernel<1>, dim3(rows), dim3(256), 0, s, xf, yb, cols, eps, gm, bt);
+  else if (vpt <= 2) hipLaunchKernelGGL(layernorm_kernel<2>, dim3(rows), dim3(256), 0, s, xf, yb, cols, eps, gm, bt);
+  else if (vpt <= 4) hipLaunchKernelGGL(layernorm_kernel<4>, dim3(rows), dim3(256), 0, s, xf, yb, cols, eps, gm, bt);
+  else if (vpt <= 8) hipLaunchKernelGGL(layernorm_kernel<8>, dim3(rows), dim3(256), 0, s, xf, yb, cols, eps, gm, bt);
+  else hipLaunchKernelGGL(layernorm_kernel<16>, dim3(rows), dim3(256), 0, s, xf, yb, cols, eps, gm, bt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "layernorm launch");
+  return CM_OK;
+}
+
+// ------------------------------------------------------------------ the layer
+cm_status cm_plan_layer(const cm_layer_desc *desc, cm_layer_plan *out) {
+  if (!desc || !out) { set_error("null argument"); return CM_ERR_INVALID_ARG; }
+  cm_layer_desc d = *desc;
+  if (d.proj_chunks == 0) d.proj_chunks = 4;  // the pipeline-chunk ReduceScatter's default of four
+  if (d.ln_eps == 0.f) d.ln_eps = 1e-5f;
+  if (!(d.ln_eps > 0.f) || std::isinf(d.ln_eps)) { set_error("ln_eps must be finite and > 0"); return CM_ERR_INVALID_ARG; }
+  if (d.out_dtype != CM_F32 && d.out_dtype != CM_BF16) { set_error("out_dtype must be CM_F32 or CM_BF16"); return CM_ERR_UNSUPPORTED; }
+  cm_status st = attention_check(d.n_ranks, d.n_ranks * d.m, d.heads, d.head_dim, 1);
+  if (st != CM_OK) return st;
+  if ((st = layernorm_check(d.n_ranks * d.m, d.d)) != CM_OK) return st;
+  cm_layer_plan p;
+  std::memset(&p, 0, sizeof p);
+  p.desc = d;
+  const int N = d.n_ranks, HD = d.heads * d.head_dim;
+  auto mk = [&](int op, int k, int n, int chunks, int out_dtype, int act, int hop_add) {
+    cm_plan_desc q;
+    std::memset(&q, 0, sizeof q);
+    q.op = op;
+    q.n_ranks = N;
+    q.m = d.m;
+    q.k = k;
+    q.n = n;
+    q.dir = d.dir;
+    q.chunks = chunks;
+    q.sched = CM_SCHED_DECOMPOSED;
+    q.in_dtype = CM_BF16;
+    q.out_dtype = out_dtype;
+    q.n_comm = d.n_comm;
+    q.exec_mode = d.exec_mode;
+    q.copy_engine = d.copy_engine;
+    q.act = act;
+    q.hop_add = hop_add;
+    return q;
+  };
+  const int rs_hop_add = d.dir == CM_RING_DIRECT ? 0 : 1;
+  cm_plan_desc dq = mk(CM_OP_AG_GEMM, d.d, 3 * HD, d.ag_chunks, CM_BF16, CM_ACT_NONE, 0);
+  cm_plan_desc dp = mk(CM_OP_GEMM_RS_PIPE, HD, d.d, d.proj_chunks, CM_F32, CM_ACT_NONE, 0);
+  dp.dir = CM_RING_UNI;  // the pipeline-chunk ReduceScatter runs its own one-way copy-and-add ring
+  cm_plan_desc d1 = mk(CM_OP_AG_GEMM, d.d, d.ffn, d.ag_chunks, CM_BF16, CM_ACT_GELU, 0);
+  cm_plan_desc d2 = mk(CM_OP_GEMM_RS, d.ffn, d.d, d.rs_chunks, d.out_dtype, CM_ACT_NONE, rs_hop_add);
+  if ((st = plan(&dq, &p.qkv)) != CM_OK) return st;
+  if ((st = plan(&dp, &p.proj)) != CM_OK) return st;
+  if ((st = plan(&d1, &p.fc1)) != CM_OK) return st;
+  if ((st = plan(&d2, &p.fc2)) != CM_OK) return st;
+  // workspace: the intermediates, then one region the four collective
+  // matmuls share (they run one after another on the same streams)
+  const size_t T = (size_t)N * d.m, A = 256;
+  size_t off = 0;
+  p.off_qkv = off; off = round_up(off + (size_t)N * T * 3 * HD * 2, A);
+  p.off_attn = off; off = round_up(off + (size_t)N * T * HD * 2, A);
+  p.off_proj = off; off = round_up(off + (size_t)N * d.m * d.d * 4, A);
+  p.off_ln = off; off = round_up(off + (size_t)N * d.m * d.d * 2, A);
+  p.off_fc1 = off; off = round_up(off + (size_t)N * T * d.ffn * 2, A);
+  p.off_ops = off;
+  size_t ops = p.qkv.ws_bytes;
+  if (p.proj.ws_bytes > ops) ops = p.proj.ws_bytes;
+  if (p.fc1.ws_bytes > ops) ops = p.fc1.ws_bytes;
+  if (p.fc2.ws_bytes > ops) ops = p.fc2.ws_bytes;
+  p.ws_bytes = off + ops;
+  *out = p;
+  return CM_OK;
+}
+
+cm_status cm_layer_forward(const cm_layer_plan *pl, const void *x, const void *wqkv, const void *wo, const void *w1,
+                           const void *w2, void *out, void *ws, size_t ws_bytes, void *compute, void *const *comm,
+                           int n_comm) {
+  if (!pl) { set_error("null plan"); return CM_ERR_INVALID_ARG; }
+  cm_layer_plan canon;
+  cm_status st = cm_plan_layer(&pl->desc, &canon);
+  if (st != CM_OK) return st;
+  if (!same_layer(canon, *pl)) {
+    set_error("layer plan does not match what cm_plan_layer produces for its request");
+    return CM_ERR_INVALID_ARG;
+  }
+  if (!x || !wqkv || !wo || !w1 || !w2 || !out || !ws) { set_error("null buffer"); return CM_ERR_INVALID_ARG; }
+  if (!aligned16(x) || !aligned16(wqkv) || !aligned16(wo) || !aligned16(w1) || !aligned16(w2) || !aligned16(out) ||
+      !aligned16(ws)) {
+    set_error("buffers must be 16-byte aligned");
+    return CM_ERR_ALIGN;
+  }
+  if (ws_bytes < pl->ws_bytes) {
+    set_error("workspace of %zu bytes, layer plan needs %zu", ws_bytes, pl->ws_bytes);
+    return CM_ERR_WORKSPACE;
+  }
+  const cm_layer_desc &d = pl->desc;
+  char *w = static_cast<char *>(ws);
+  char *qkv = w + pl->off_qkv, *attn = w + pl->off_attn, *proj = w + pl->off_proj, *ln = w + pl->off_ln,
+       *fc1 = w + pl->off_fc1, *opws = w + pl->off_ops;
+  const size_t opbytes = ws_bytes - pl->off_ops;
+  if ((st = cm_ag_gemm(&pl->qkv, x, wqkv, qkv, opws, opbytes, compute, comm, n_comm, nullptr)) != CM_OK) return st;
+  if ((st = cm_attention(qkv, attn, d.n_ranks, d.n_ranks * d.m, d.heads, d.head_dim, 1, compute)) != CM_OK) return st;
+  if ((st = cm_gemm_rs(&pl->proj, attn, wo, proj, opws, opbytes, compute, comm, n_comm, nullptr)) != CM_OK) return st;
+  if ((st = cm_layernorm(proj, ln, d.n_ranks * d.m, d.d, d.ln_eps, nullptr, nullptr, compute)) != CM_OK) return st;
+  if ((st = cm_ag_gemm(&pl->fc1, ln, w1, fc1, opws, opbytes, compute, comm, n_comm, nullptr)) != CM_OK) return st;
+  return cm_gemm_rs(&pl->fc2, fc1, w2, out, opws, opbytes, compute, comm, n_comm, nullptr);
+}
+
+}  // extern "C"

@@ -188,6 +188,11 @@ cm_status validate_desc(const cm_plan_desc &d) {
     set_error("the pipeline-chunk ReduceScatter runs its own copy-and-add ring; no direct variant");
     return CM_ERR_UNSUPPORTED;
   }
+  if (d.act != CM_ACT_NONE && d.act != CM_ACT_GELU) { set_error("unknown activation %d", d.act); return CM_ERR_INVALID_ARG; }
+  if (d.act != CM_ACT_NONE && d.op != CM_OP_AG_GEMM) {
+    set_error("an epilogue activation exists only for AllGather->GEMM");
+    return CM_ERR_UNSUPPORTED;
+  }
   if ((d.tile_m || d.tile_n) && !tile_known(d.tile_m, d.tile_n)) {
     set_error("no GEMM tile %dx%d (choose 256x256, 256x192, 256x128, 128x256, 128x128, 64x256 or 0x0)", d.tile_m,
               d.tile_n);
@@ -473,6 +478,7 @@ struct Builder {
   void gemm(const std::vector<cm_job_rec> &jobs, int rows, int cols, int depth) {
     if (jobs.empty()) return;
     cm_op_rec o = base(CM_OPK_GEMM, 0);
+    o.act = d.op == CM_OP_AG_GEMM ? d.act : CM_ACT_NONE;
     o.first_job = (int)prog.jobs.size();
     o.n_jobs = (int)jobs.size();
     o.rows = rows; o.cols = cols; o.depth = depth;

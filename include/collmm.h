@@ -105,6 +105,11 @@ typedef enum {
 
 typedef enum { CM_BF16 = 0, CM_F32 = 1 } cm_dtype;
 
+/* Epilogue activation: none, or GELU in its erf form, x * Phi(x) =
+ * 0.5 * x * (1 + erf(x / sqrt(2))), evaluated in fp32 before the rounding to
+ * the output type. */
+typedef enum { CM_ACT_NONE = 0, CM_ACT_GELU = 1 } cm_act;
+
 /*
  * CM_EXEC_GRAPH: the first call with a given plan, set of buffers and trace
  * builds the program as a HIP graph (kernel and memcpy nodes whose edges
@@ -168,6 +173,9 @@ typedef struct {
   double copy_gbps;      /* sustained hop bandwidth of ONE comm stream, GB/s */
   double mfma_tflops;    /* sustained bf16 GEMM rate, TFLOP/s */
   double launch_us;      /* fixed cost per step launch / hop, microseconds */
+  int act;               /* AllGather->GEMM only: cm_act applied to every output
+                            element before it is stored (the MLP activation fused
+                            into the slice update); CM_ACT_NONE for the other ops */
 } cm_plan_desc;
 
 /* The resolved schedule.  Plain data: no heap, nothing to destroy. */
@@ -243,6 +251,7 @@ typedef struct {
   int tile_m, tile_n;    /* GEMM: block tile the launch uses */
   int src_buf, dst_buf;  /* COPY */
   size_t src_off, dst_off, bytes;
+  int act;               /* GEMM: cm_act of the epilogue (launches without addends only) */
 } cm_op_rec;
 
 /*
@@ -321,6 +330,104 @@ cm_status cm_ag_gemm(const cm_plan *plan, const void *x, const void *w, void *y,
 cm_status cm_gemm_rs(const cm_plan *plan, const void *x, const void *w, void *y, void *ws,
                      size_t ws_bytes, void *compute, void *const *comm, int n_comm,
                      cm_trace *trace);
+
+/* ------------------------------------------------------------------------
+ * The sequence-parallel transformer layer around the two collective matmuls.
+ *
+ * The Megatron page's sequence parallelism keeps per-token work (LayerNorm,
+ * dropout) on the sequence-sharded activation between the ReduceScatter that
+ * ends one tensor-parallel block and the AllGather that starts the next;
+ * "Tensor Parallelism > Communication Patterns" places LayerNorm in the same
+ * gap between the two halves of an all-reduce.  The pages give no formulas
+ * for the layer's other stages; these entry points compute the textbook
+ * definitions.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Causal (or full) scaled dot-product attention of every head of every
+ * virtual rank, softmax(Q K^T / sqrt(D)) V, bf16 in and out, fp32 scores,
+ * probabilities rounded to bf16 for the value product and the normaliser.
+ *   qkv  [n_ranks][T][3*heads*head_dim] bf16: columns h*D.. hold head h's
+ *        query, heads*D + h*D.. its key, 2*heads*D + h*D.. its value (the
+ *        QKV projection's output in this library's layout)
+ *   o    [n_ranks][T][heads*head_dim] bf16: head h in columns h*D..
+ *   causal 1: query t attends to keys 0..t; 0: to every key
+ *   stream the stream to enqueue on (hipStream_t as void*; NULL = default)
+ * head_dim must be 128 (CM_ERR_UNSUPPORTED otherwise).  Asynchronous.
+ * Errors: CM_ERR_INVALID_ARG (null pointer, bad count), CM_ERR_ALIGN
+ * (pointers not 16-byte aligned), CM_ERR_SHAPE (too large), CM_ERR_HIP.
+ */
+cm_status cm_attention(const void *qkv, void *o, int n_ranks, int T, int heads, int head_dim, int causal,
+                       void *stream);
+
+/*
+ * LayerNorm of every row: y = (x - mean) / sqrt(var + eps) * gamma + beta,
+ * with the population variance; x fp32 [rows][cols], y bf16 [rows][cols]
+ * (nearest-even), gamma and beta fp32 [cols] or NULL (1 and 0).  cols must be
+ * a multiple of 4 in 4..16384.  Asynchronous on `stream`.  Errors:
+ * CM_ERR_SHAPE, CM_ERR_INVALID_ARG (null x or y, eps < 0 or not finite),
+ * CM_ERR_ALIGN, CM_ERR_HIP.
+ */
+cm_status cm_layernorm(const void *x, void *y, int rows, int cols, float eps, const void *gamma, const void *beta,
+                       void *stream);
+
+/* One sequence-parallel transformer layer (forward), N virtual ranks. */
+typedef struct {
+  int n_ranks;     /* N */
+  int m;           /* tokens per sequence shard; T = N*m */
+  int d;           /* hidden size */
+  int heads;       /* attention heads per rank (the layer has N*heads) */
+  int head_dim;    /* 128 */
+  int ffn;         /* MLP width per rank (f/N) */
+  int dir;         /* cm_ring_dir of the QKV, fc1 and fc2 collective matmuls (the
+                      output projection's pipeline-chunk ReduceScatter is a one-way ring) */
+  int n_comm;      /* comm streams the call passes */
+  int copy_engine; /* cm_copy_engine */
+  int exec_mode;   /* cm_exec_mode */
+  int ag_chunks;   /* chunks of both AllGather->GEMMs (0 = cost model) */
+  int rs_chunks;   /* chunks of the fc2 ReduceScatter (0 = cost model) */
+  int proj_chunks; /* pipeline chunks of the output projection's ReduceScatter (0 = 4) */
+  int out_dtype;   /* CM_BF16 or CM_F32: the layer output */
+  float ln_eps;    /* LayerNorm epsilon (0 = 1e-5) */
+} cm_layer_desc;
+
+/* The resolved layer: plain data, nothing to destroy. */
+typedef struct {
+  cm_layer_desc desc; /* the request with defaults filled in */
+  cm_plan qkv;        /* AllGather -> QKV projection (k = d, n = 3*heads*D), bf16 out */
+  cm_plan proj;       /* output projection -> pipeline-chunk ReduceScatter (k = heads*D, n = d), fp32 out */
+  cm_plan fc1;        /* AllGather -> fc1 (k = d, n = ffn) with GELU, bf16 out */
+  cm_plan fc2;        /* fc2 -> ReduceScatter (k = ffn, n = d), add-and-forward hops on a ring */
+  size_t off_qkv, off_attn, off_proj, off_ln, off_fc1, off_ops; /* workspace regions (bytes) */
+  size_t ws_bytes;    /* workspace the call needs */
+} cm_layer_plan;
+
+/*
+ * Plan a layer.  Host only.  Errors: those of cm_ring_plan for any of the four
+ * collective matmuls, of cm_attention (head_dim) and of cm_layernorm (d).
+ */
+cm_status cm_plan_layer(const cm_layer_desc *desc, cm_layer_plan *out);
+
+/*
+ * The layer forward (all inputs bf16, row-major, rank r = block r):
+ *   x    [N][m][d]             the sequence shards entering the layer
+ *   wqkv [N][3*heads*D][d]     rank r's query, key and value projections (its
+ *                              heads r*heads..), one output feature per row
+ *   wo   [N][d][heads*D]       rank r's slice of the output projection
+ *   w1   [N][ffn][d]           rank r's fc1 columns
+ *   w2   [N][d][ffn]           rank r's fc2 rows
+ *   out  [N][m][d]             the shards leaving the layer (desc.out_dtype)
+ *   ws   workspace of ws_bytes >= plan->ws_bytes; after the call it holds the
+ *        intermediates at the plan's offsets: QKV [N][T][3*heads*D] bf16,
+ *        attention [N][T][heads*D] bf16, projection [N][m][d] fp32, LayerNorm
+ *        [N][m][d] bf16, fc1 (after GELU) [N][T][ffn] bf16
+ * Chain: x -> AG->QKV -> attention (causal) -> out-proj->RS (pipeline chunks)
+ * -> LayerNorm (gamma 1, beta 0) -> AG->fc1 (+GELU) -> fc2->RS.  No residual
+ * connections.  Streams, ordering and errors as for cm_ag_gemm; asynchronous.
+ */
+cm_status cm_layer_forward(const cm_layer_plan *plan, const void *x, const void *wqkv, const void *wo,
+                           const void *w1, const void *w2, void *out, void *ws, size_t ws_bytes, void *compute,
+                           void *const *comm, int n_comm);
 
 const char *cm_status_string(cm_status s);
 /* Detail of the last failing call on this thread ("" if none). */

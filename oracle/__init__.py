@@ -279,7 +279,9 @@ def sp_layer_rows(x, wqkv, wo, w1, w2, heads, tokens, eps=1e-5, causal=True, lib
     tokens: global token indices g (owner g // m, row g % m of Out_owner).
     Returns a dict of float64 arrays, one row per token: "out" [ns, d], "mag"
     (sum_r sum_k |F_r| |w2_r| of the last contraction), and the stages
-    "attn" [N, ns, heads*D] (unrounded), "proj" [ns, d], "ln" [ns, d]
+    "qkv" [N, R, 3*heads*D] (rounded values of the rows 0..R-1 the sample
+    needs: R = max(tokens) + 1 when causal, else T), "attn" [N, ns, heads*D]
+    (unrounded), "proj" [ns, d], "ln" [ns, d]
     (rounded values) and "fc1" [N, ns, f/N] (rounded values)."""
     lib = lib or load()
     x, wqkv, wo, w1, w2 = (_u16(a) for a in (x, wqkv, wo, w1, w2))
@@ -316,4 +318,4 @@ def sp_layer_rows(x, wqkv, wo, w1, w2, heads, tokens, eps=1e-5, causal=True, lib
         w2r = bf16_to_f64(w2[r])
         out += fc1[r] @ w2r.T
         mag += np.abs(fc1[r]) @ np.abs(w2r).T
-    return {"out": out, "mag": mag, "attn": attn, "proj": proj, "ln": ln, "fc1": fc1}
+    return {"out": out, "mag": mag, "qkv": bf16_to_f64(qkv), "attn": attn, "proj": proj, "ln": ln, "fc1": fc1}

@@ -21,12 +21,15 @@ it, stream 0 reads the output and overwrites the inputs and the workspace
 (the caller synchronises only the compute stream, then reuses buffers).  The arithmetic is exact float64 on small integers, with
 fp32 / bf16 stores.
 """
+import math
+
 import numpy as np
 
 from collective_matmul_decomposition_amd import _native as nat
 from collective_matmul_decomposition_amd.inputs import f32_to_bf16_bits
 
 G = 16  # granule bytes
+_erf = np.vectorize(math.erf, otypes=[np.float64])
 
 
 class Race(AssertionError):
@@ -204,6 +207,8 @@ class Sim:
                             self.read(s, ib, self._rows(ib, io, o.rows, j.ld_in * asz, o.cols * asz))
                             add = self._bf16 if asz == 2 else self._f32
                             val = val + add(ib, io, o.rows, o.cols, j.ld_in)
+                    if o.kind == nat.CM_OPK_GEMM and o.act == nat.CM_ACT_GELU:
+                        val = 0.5 * val * (1.0 + _erf(val / np.sqrt(2.0)))
                     results.append((j, val))
                 for j, val in results:
                     esz = 4 if j.c_dtype == nat.CM_F32 else 2

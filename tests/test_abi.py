@@ -34,8 +34,8 @@ def test_struct_sizes_match_the_header():
 #include <stdio.h>
 #include "collmm.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu\n", sizeof(cm_plan_desc), sizeof(cm_plan), sizeof(cm_op_rec), sizeof(cm_job_rec),
-         sizeof(cm_span));
+  printf("%zu %zu %zu %zu %zu %zu %zu\n", sizeof(cm_plan_desc), sizeof(cm_plan), sizeof(cm_op_rec), sizeof(cm_job_rec),
+         sizeof(cm_span), sizeof(cm_layer_desc), sizeof(cm_layer_plan));
   return 0;
 }
 '''
@@ -46,7 +46,8 @@ int main(void) {
         subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
         sizes = [int(v) for v in subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()]
     assert sizes == [ctypes.sizeof(nat.cm_plan_desc), ctypes.sizeof(nat.cm_plan), ctypes.sizeof(nat.cm_op_rec),
-                     ctypes.sizeof(nat.cm_job_rec), ctypes.sizeof(nat.cm_span)]
+                     ctypes.sizeof(nat.cm_job_rec), ctypes.sizeof(nat.cm_span), ctypes.sizeof(nat.cm_layer_desc),
+                     ctypes.sizeof(nat.cm_layer_plan)]
 
 
 def status_of(**kw):
