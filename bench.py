@@ -345,6 +345,98 @@ def run_sweep(name, reps, copy_engine):
         print(json.dumps(r), flush=True)
 
 
+LAYER = dict(N=8, T=4096, d=8192, heads=64, head_dim=128, ffn=28672)  # the full SP layer (4096 tokens, d 8192)
+
+
+def measure_layer(args, steps, warmup):
+    """The sequence-parallel transformer-layer forward on N = 8 virtual ranks
+    (AG->QKV, causal attention, out-proj->pipeline-chunk RS, LayerNorm on the
+    shard, AG->fc1+GELU, fc2->RS): whole-layer wall time over `steps` calls,
+    then each stage alone between events on the compute stream."""
+    import torch
+    from collective_matmul_decomposition_amd import _native as nat
+    from collective_matmul_decomposition_amd import buffers
+    from collective_matmul_decomposition_amd import inputs as gen
+    L = LAYER
+    N, T, d, D, f = L["N"], L["T"], L["d"], L["head_dim"], L["ffn"]
+    m, H, fN = T // N, L["heads"] // N, f // N
+    HD = H * D
+    ring = args.dir if args.dir != "bi" else "uni"
+    plan = nat.cm_plan_layer(n_ranks=N, m=m, d=d, heads=H, ffn=fN, dir=ring, n_comm=args.n_comm,
+                             copy_engine=args.copy_engine, ag_chunks=1, rs_chunks=1, proj_chunks=0)
+    x, wqkv, wo, w1, w2 = gen.layer_inputs_torch(N, m, d, H, D, fN, "normal", 0, "cuda")
+    out = torch.empty((N, m, d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(plan.ws_bytes, dtype=torch.uint8, device="cuda")
+    compute = torch.cuda.Stream()
+    compute.wait_stream(torch.cuda.current_stream())
+    comm = buffers.comm_streams(args.n_comm)
+    for _ in range(warmup):
+        nat.cm_layer_forward(plan, x, wqkv, wo, w1, w2, out, ws, compute, comm)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        nat.cm_layer_forward(plan, x, wqkv, wo, w1, w2, out, ws, compute, comm)
+    torch.cuda.synchronize()
+    layer_ms = (time.perf_counter() - t0) * 1e3 / steps
+    gemm_fl = {"qkv": 2.0 * N * T * d * 3 * HD, "proj": 2.0 * N * T * HD * d, "fc1": 2.0 * N * T * d * fN,
+               "fc2": 2.0 * N * T * fN * d}
+    attn_fl = 2.0 * N * H * D * T * (T + 1)  # causal: q.k and p.v over the T(T+1)/2 visible pairs
+    total_fl = sum(gemm_fl.values()) + attn_fl
+    # each stage alone, between events on the compute stream (the same calls
+    # cm_layer_forward makes, on the same workspace regions)
+    base = ws.data_ptr()
+    reg = {k: base + getattr(plan, "off_" + k) for k in ("qkv", "attn", "proj", "ln", "fc1", "ops")}
+    opbytes = plan.ws_bytes - plan.off_ops
+    stages = [
+        ("qkv", lambda: nat.cm_ag_gemm(plan.qkv, x, wqkv, reg["qkv"], reg["ops"], compute, comm, ws_bytes=opbytes)),
+        ("attention", lambda: nat.cm_attention(reg["qkv"], reg["attn"], N, T, H, D, True, compute)),
+        ("proj", lambda: nat.cm_gemm_rs(plan.proj, reg["attn"], wo, reg["proj"], reg["ops"], compute, comm,
+                                        ws_bytes=opbytes)),
+        ("layernorm", lambda: nat.cm_layernorm(reg["proj"], reg["ln"], N * m, d, plan.desc.ln_eps, None, None,
+                                               compute)),
+        ("fc1", lambda: nat.cm_ag_gemm(plan.fc1, reg["ln"], w1, reg["fc1"], reg["ops"], compute, comm,
+                                       ws_bytes=opbytes)),
+        ("fc2", lambda: nat.cm_gemm_rs(plan.fc2, reg["fc1"], w2, out, reg["ops"], compute, comm, ws_bytes=opbytes)),
+    ]
+    reps = max(3, steps)
+    times = {}
+    for name, fn in stages:
+        fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record(compute)
+            fn()
+            b.record(compute)
+        torch.cuda.synchronize()
+        times[name] = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3  # us
+    st = {}
+    for name in ("qkv", "proj", "fc1", "fc2"):
+        st[name] = {"us": round(times[name], 1), "tflops": round(gemm_fl[name] / (times[name] * 1e-6) / 1e12, 1)}
+    attn_t = times["attention"]
+    st["attention"] = {"us": round(attn_t, 1), "tflops": round(attn_fl / (attn_t * 1e-6) / 1e12, 1),
+                       "roofline": {"bound": "mfma", "achieved": round(attn_fl / (attn_t * 1e-6) / 1e12, 1),
+                                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                    "frac": round(attn_fl / (attn_t * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                                    "flops": attn_fl}}
+    ln_bytes = N * m * d * (4 + 2)  # fp32 in, bf16 out
+    ln_t = times["layernorm"]
+    st["layernorm"] = {"us": round(ln_t, 1),
+                       "roofline": {"bound": "hbm", "achieved": round(ln_bytes / (ln_t * 1e-6) / 1e9, 1),
+                                    "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                    "frac": round(ln_bytes / (ln_t * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+                                    "bytes": ln_bytes}}
+    log("layer: %.3f ms, %.1f TFLOP/s; %s" % (layer_ms, total_fl / (layer_ms * 1e-3) / 1e12,
+                                             ", ".join("%s %.0f us" % (k, v) for k, v in times.items())))
+    res = {"workload": "sp-layer-fwd (N=8, 4096 tokens, d=8192, 64 heads x 128, ffn 28672)",
+           "ms": round(layer_ms, 4), "tflops": round(total_fl / (layer_ms * 1e-3) / 1e12, 1),
+           "pct_of_bf16_peak": round(100 * total_fl / (layer_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+           "flops": total_fl, "ring": ring, "proj_chunks": plan.proj.chunks, "stages": st,
+           "stage_sum_ms": round(sum(times.values()) / 1e3, 4)}
+    del x, wqkv, wo, w1, w2, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def sampled_parity(res, rs_bucket="f32"):
     import oracle
     from collective_matmul_decomposition_amd import inputs as gen
@@ -419,6 +511,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
     ap.add_argument("--no-naive", action="store_true")
+    ap.add_argument("--no-layer", action="store_true", help="skip the sequence-parallel layer forward")
     ap.add_argument("--no-trace", action="store_true", help="time without the per-launch events")
     ap.add_argument("--sweep", choices=["c4", "c5"], help="instead of the step: the small-chunk grid (c4) or the "
                     "layer's GEMM + collective pairs (c5), one JSON line per case")
@@ -496,6 +589,8 @@ def main():
                      "pct_of_bf16_peak": round(100 * s2["value"] / PEAK_BF16_TFLOPS, 2),
                      "roofline": s2.get("roofline"), "overlap": s2.get("overlap"), "naive": s2.get("naive")}
 
+    layer = None if args.no_layer else measure_layer(args, max(5, args.steps // 2), 2)
+
     out = {
         "metric": "AG-GEMM / GEMM-RS TFLOP/s + % bf16 MFMA peak + overlap efficiency, 1 GPU",
         "value": round(res["value"], 2),
@@ -529,6 +624,7 @@ def main():
         "alt_rs_hop": alt_hop,
         "step_launches": res.get("step_launches"),
         "secondary": secondary,
+        "layer": layer,
     }
     print(json.dumps(out), flush=True)
 

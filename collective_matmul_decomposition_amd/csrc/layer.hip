@@ -463,7 +463,7 @@ cm_status cm_plan_layer(const cm_layer_desc *desc, cm_layer_plan *out) {
   };
   const int rs_hop_add = d.dir == CM_RING_DIRECT ? 0 : 1;
   cm_plan_desc dq = mk(CM_OP_AG_GEMM, d.d, 3 * HD, d.ag_chunks, CM_BF16, CM_ACT_NONE, 0);
-  cm_plan_desc dp = mk(CM_OP_GEMM_RS_PIPE, HD, d.d, d.proj_chunks, CM_F32, CM_ACT_NONE, 0);
+  cm_plan_desc dp = mk(CM_OP_GEMM_RS_PIPE, HD, d.d, d.proj_chunks, CM_F32, CM_ACT_NONE, 1);
   dp.dir = CM_RING_UNI;  // the pipeline-chunk ReduceScatter runs its own one-way copy-and-add ring
   cm_plan_desc d1 = mk(CM_OP_AG_GEMM, d.d, d.ffn, d.ag_chunks, CM_BF16, CM_ACT_GELU, 0);
   cm_plan_desc d2 = mk(CM_OP_GEMM_RS, d.ffn, d.d, d.rs_chunks, d.out_dtype, CM_ACT_NONE, rs_hop_add);

@@ -73,6 +73,7 @@ constexpr TileCand kTiles[] = {
     {256, 256, 1.00}, {256, 192, 0.90}, {256, 128, 0.88}, {128, 256, 0.88}, {128, 128, 0.75}, {64, 256, 0.65},
 };
 constexpr int kCUs = 256;
+constexpr int kJobCap = 128;  // jobs one launch can hold (the kernels' parameter block)
 
 bool tile_known(int tm, int tn) {
   for (const TileCand &t : kTiles)
@@ -116,7 +117,8 @@ const char *last_error() { return g_last_error.c_str(); }
 // RS decomposed: buckets  bkt[dir][p][j][r][m][n/c] fp32 (bf16 with bucket_bf16);
 //   with add-and-forward hops also partial slots of the same shape after them.
 // RS pipe / naive: partials P[r][j][T][n/c] fp32, then ring slots
-//   R[p][r][m][n/c] fp32.
+//   R[p][r][m][n/c] fp32; with add-and-forward hops the ring slots are per
+//   chunk, R[j][p][r][m][n/c].
 WsLayout ws_layout(const cm_plan &pl) {
   const cm_plan_desc &d = pl.desc;
   const size_t N = d.n_ranks, m = d.m, k = d.k, n = d.n, c = pl.chunks, T = N * m;
@@ -144,6 +146,11 @@ WsLayout ws_layout(const cm_plan &pl) {
       L.partial = L.total;
       L.total *= 2;
     }
+  } else if (d.hop_add) {  // PIPE / RS naive with add-and-forward hops: ring slots per chunk
+    L.partial = 0;
+    L.partial_bytes = N > 1 ? N * T * n * 4 : 0;
+    L.ring = L.partial_bytes;
+    L.total = L.partial_bytes + (N > 1 ? 2 * N * m * n * 4 : 0);
   } else {  // PIPE, or RS naive (PIPE with one chunk)
     L.partial = 0;
     L.partial_bytes = N > 1 ? N * T * n * 4 : 0;
@@ -180,8 +187,9 @@ cm_status validate_desc(const cm_plan_desc &d) {
     return CM_ERR_UNSUPPORTED;
   }
   if (d.hop_add != 0 && d.hop_add != 1) { set_error("hop_add must be 0 or 1"); return CM_ERR_INVALID_ARG; }
-  if (d.hop_add && !(d.op == CM_OP_GEMM_RS && d.sched != CM_SCHED_NAIVE && d.dir != CM_RING_DIRECT && !d.bucket_bf16)) {
-    set_error("add-and-forward hops exist only for the decomposed GEMM-RS on a ring with an fp32 bucket");
+  if (d.hop_add && !((d.op == CM_OP_GEMM_RS || d.op == CM_OP_GEMM_RS_PIPE) && d.dir != CM_RING_DIRECT &&
+                     !d.bucket_bf16)) {
+    set_error("add-and-forward hops exist only for a GEMM-RS on a ring with an fp32 bucket");
     return CM_ERR_UNSUPPORTED;
   }
   if (d.dir == CM_RING_DIRECT && d.op == CM_OP_GEMM_RS_PIPE) {
@@ -259,6 +267,15 @@ Est estimate(const cm_plan_desc &d, int c) {
     // takes the longer of c GEMM chunks and one chunk's GEMM + hop.
     e.total = steps * std::max(c * g, g + h);
     e.hidden = c >= 2 && h <= (c - 1) * g;
+  } else if (d.hop_add) {
+    // pipeline chunks with add-and-forward hops: N - 1 add launches per
+    // chunk (each reads a partial and a bucket and writes the next slot)
+    const double g = gemm_us(d, d.n_ranks * d.n_ranks, m, n / c, k);
+    const double h = N * m * (n / c) * 4.0 * 3.0 / (kDefaultCuAddGBps * 1e9) * 1e6 + d.launch_us;
+    const double ring = (N - 1) * h;
+    e.g = g; e.h = h;
+    e.total = std::max(c * g + ring, g + c * ring);
+    e.hidden = ring <= g;
   } else {
     const double g = gemm_us(d, d.n_ranks, N * m, n / c, k);
     const double h = hop_us(d, N * m * (n / c) * 4.0, d.n_ranks, per_lane) + d.launch_us;  // copy + add
@@ -998,8 +1015,77 @@ struct Builder {
     exit_();
   }
 
+  // ------------------------------- RS, pipeline chunks with add-and-forward hops
+  // Chunk j's GEMM computes every rank's partial for every bucket as one job
+  // per (rank, bucket); the job of rank r for bucket r - 1, which starts that
+  // bucket's trip around the ring, stores straight into rank r + 1's ring
+  // slot (the first hop).  Then N - 1 add launches on the first comm stream:
+  // at hop t rank r adds its partial for bucket q = r - 1 - t to the bucket
+  // that arrived and writes the sum into rank r + 1's slot; at t = N - 1 the
+  // owner (r = q) writes Out_q.  Every chunk has its own slots, so chunk
+  // j + 1's GEMM runs beside chunk j's adds and waits for none of them.  The
+  // additions are those of the copy-and-add ring, in the same order.
+  void rs_pipe_add() {
+    const size_t nc = n / c;
+    const int osz = d.out_dtype == CM_F32 ? 4 : 2;
+    const size_t blk = m * nc * 4;
+    auto part = [&](int r, int j, int q) -> size_t { return L.partial + (((size_t)r * c + j) * N + q) * blk; };
+    auto ring = [&](int j, int par, int r) -> size_t { return L.ring + (((size_t)j * 2 + par) * N + r) * blk; };
+    const int red = 1;
+    const int per_launch = std::max(1, kJobCap / N);  // ranks per GEMM launch (N jobs each)
+    entry();
+    for (int j = 0; j < c; ++j) {
+      cur_step = 0; cur_chunk = j;
+      for (int a = 0; a < N; a += per_launch) {
+        std::vector<cm_job_rec> jobs;
+        for (int r = a; r < std::min(N, a + per_launch); ++r) {
+          for (int q = 0; q < N; ++q) {
+            cm_job_rec jb = job0();
+            jb.rank = r; jb.index = q;
+            jb.a_buf = CM_BUF_X; jb.a_off = ((size_t)r * T + (size_t)q * m) * k * 2; jb.lda = (int)k;
+            jb.b_buf = CM_BUF_W; jb.b_off = ((size_t)r * n + (size_t)j * nc) * k * 2; jb.ldb = (int)k;
+            jb.ld_in = (int)nc;
+            if (N == 1) {
+              jb.c_buf = CM_BUF_Y; jb.c_off = (size_t)j * nc * osz; jb.ldc = (int)n; jb.c_dtype = d.out_dtype;
+            } else {
+              jb.c_buf = CM_BUF_WS; jb.ldc = (int)nc; jb.c_dtype = CM_F32;
+              jb.c_off = q == mod(r - 1, N) ? ring(j, 0, mod(r + 1, N)) : part(r, j, q);
+            }
+            jobs.push_back(jb);
+          }
+        }
+        gemm(jobs, (int)m, (int)nc, (int)k);
+      }
+      if (N == 1) continue;
+      const int eg = record(0);
+      wait(red, eg);  // RAW: the partials and the first hop's slots
+      for (int t = 1; t < N; ++t) {
+        cur_step = t;
+        std::vector<cm_job_rec> rj;
+        for (int r = 0; r < N; ++r) {
+          const int q = mod(r - 1 - t, N);
+          cm_job_rec jb = job0();
+          jb.rank = r; jb.index = q;
+          jb.in0_buf = CM_BUF_WS; jb.in0_off = ring(j, (t - 1) % 2, r);
+          jb.in1_buf = CM_BUF_WS; jb.in1_off = part(r, j, q);
+          jb.ld_in = (int)nc;
+          if (t == N - 1) {
+            jb.c_buf = CM_BUF_Y; jb.c_off = ((size_t)r * m * n + (size_t)j * nc) * osz; jb.ldc = (int)n;
+            jb.c_dtype = d.out_dtype;
+          } else {
+            jb.c_buf = CM_BUF_WS; jb.c_off = ring(j, t % 2, mod(r + 1, N)); jb.ldc = (int)nc; jb.c_dtype = CM_F32;
+          }
+          rj.push_back(jb);
+        }
+        reduce(red, rj, (int)m, (int)nc);
+      }
+    }
+    exit_();
+  }
+
   // ------------------------------------------------- RS, pipeline chunks / naive
   void rs_pipe() {
+    if (d.hop_add) { rs_pipe_add(); return; }
     const size_t nc = n / c;
     const int osz = d.out_dtype == CM_F32 ? 4 : 2;
     const size_t part_rank = (size_t)c * T * nc * 4;           // P[r]

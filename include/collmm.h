@@ -159,16 +159,22 @@ typedef struct {
                       bytes), rounded to nearest-even after every addition,
                       which adds up to half a bf16 spacing of error per hop
                       (outside the fp32-bucket error bound) */
-  int hop_add;     /* GEMM-RS (decomposed, uni or bi ring, fp32 bucket) only:
-                      0 = each step's GEMM adds the arrived bucket in its
-                      epilogue (read-add-write) and the hop is a copy, so a
-                      step's GEMM waits for the previous hop; 1 = each step's
-                      GEMM stores its partial product and the hop is an
-                      add-and-forward launch on compute units (on the first
-                      comm stream) that writes partial + arrived bucket into
-                      the next rank's receive slot, so a step's GEMM waits for
-                      nothing but a free partial slot.  The owner's last GEMM
-                      still adds in its epilogue.  Bitwise the same result. */
+  int hop_add;     /* GEMM-RS on a uni or bi ring with an fp32 bucket only.
+                      Decomposed CM_OP_GEMM_RS: 0 = each step's GEMM adds the
+                      arrived bucket in its epilogue (read-add-write) and the
+                      hop is a copy, so a step's GEMM waits for the previous
+                      hop; 1 = each step's GEMM stores its partial product and
+                      the hop is an add-and-forward launch on compute units (on
+                      the first comm stream) that writes partial + arrived
+                      bucket into the next rank's receive slot, so a step's
+                      GEMM waits for nothing but a free partial slot; the
+                      owner's last GEMM still adds in its epilogue.
+                      CM_OP_GEMM_RS_PIPE and the naive GEMM-RS: 0 = each ring
+                      hop is a copy followed by an add launch; 1 = the chunk's
+                      GEMM starts every bucket by storing into the next rank's
+                      slot and each further hop is one add-and-forward launch
+                      (ring slots per chunk, so a chunk's GEMM never waits for
+                      an earlier chunk's ring).  Bitwise the same result. */
   /* Cost-model inputs (0 = built-in defaults for MI355X). */
   double copy_gbps;      /* sustained hop bandwidth of ONE comm stream, GB/s */
   double mfma_tflops;    /* sustained bf16 GEMM rate, TFLOP/s */
@@ -395,7 +401,8 @@ typedef struct {
 typedef struct {
   cm_layer_desc desc; /* the request with defaults filled in */
   cm_plan qkv;        /* AllGather -> QKV projection (k = d, n = 3*heads*D), bf16 out */
-  cm_plan proj;       /* output projection -> pipeline-chunk ReduceScatter (k = heads*D, n = d), fp32 out */
+  cm_plan proj;       /* output projection -> pipeline-chunk ReduceScatter (k = heads*D, n = d), fp32 out,
+                         add-and-forward hops */
   cm_plan fc1;        /* AllGather -> fc1 (k = d, n = ffn) with GELU, bf16 out */
   cm_plan fc2;        /* fc2 -> ReduceScatter (k = ffn, n = d), add-and-forward hops on a ring */
   size_t off_qkv, off_attn, off_proj, off_ln, off_fc1, off_ops; /* workspace regions (bytes) */

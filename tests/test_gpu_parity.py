@@ -451,6 +451,53 @@ def test_hop_add_equals_epilogue_ring(N, m, k, n, dir, chunks, n_comm):
         assert torch.equal(ya, yc)
 
 
+PIPE_ADD = [
+    # op, N, m, k, n, chunks, n_comm, sched
+    ("rs_pipe", 2, 19, 256, 640, 2, 1, "decomposed"),
+    ("rs_pipe", 3, 64, 256, 256, 4, 2, "decomposed"),
+    ("rs_pipe", 5, 37, 192, 320, 5, 3, "decomposed"),
+    ("rs_pipe", 8, 256, 768, 1024, 4, 1, "decomposed"),
+    ("rs", 4, 64, 256, 256, 1, 1, "naive"),
+    ("rs_pipe", 1, 50, 64, 128, 2, 1, "decomposed"),
+]
+
+
+@pytest.mark.parametrize("op,N,m,k,n,chunks,n_comm,sched", PIPE_ADD)
+def test_pipe_hop_add_equals_copy_ring(op, N, m, k, n, chunks, n_comm, sched):
+    """Pipeline-chunk (and naive) ReduceScatter with add-and-forward hops:
+    exact on integers, and bitwise the sums of the copy-and-add ring."""
+    say("pipe hop add", op, N, m, k, n, chunks, n_comm, sched)
+    for out in ("f32", "bf16"):
+        _, a, w, (yi,) = run_case(op, N, m, k, n, "int", out, "uni", chunks, sched, n_comm, hop="add")
+        check("rs", a, w, yi, out, "int")
+    for exec_mode in ("graph", "eager"):
+        _, a, w, (ya,) = run_case(op, N, m, k, n, "normal", "f32", "uni", chunks, sched, n_comm, seed=9,
+                                  exec_mode=exec_mode, hop="add")
+        check("rs", a, w, ya, "f32", "normal")
+        _, _, _, (yc,) = run_case(op, N, m, k, n, "normal", "f32", "uni", chunks, sched, n_comm, seed=9,
+                                  exec_mode=exec_mode)
+        assert torch.equal(ya, yc)
+
+
+def test_pipe_hop_add_layer_shape_sampled():
+    """The layer's output projection: 8 ranks, [4096 x 1024] . [1024 x 8192]
+    per rank in 4 pipeline chunks, add-and-forward hops, fp32 out: sampled
+    rows against the oracle, the whole output bitwise equal to the copy ring's."""
+    N, m, k, n = 8, 512, 1024, 8192
+    x_t, w_t = gen.rs_inputs_torch(N, m, k, n, "normal", 0, "cuda")
+    ys = []
+    for hop in ("add", "copy"):
+        plan = nat.cm_ring_plan(op="rs_pipe", n_ranks=N, m=m, k=k, n=n, chunks=4, out_dtype="f32", n_comm=1, hop=hop)
+        y, ws = buffers.alloc_outputs(plan)
+        say("pipe hop full", hop)
+        buffers.run(plan, x_t, w_t, y, ws, comm=buffers.comm_streams(1))
+        torch.cuda.synchronize()
+        ys.append(y)
+        del ws
+    sampled_check("rs", N, m, x_t, w_t, ys[0], 8)
+    assert torch.equal(ys[0], ys[1])
+
+
 @pytest.mark.parametrize("dir", ["uni", "bi"])
 def test_hop_add_full_size_sampled(dir):
     """GPT-3 MLP fc2 shape (8 ranks, [256 x 6144] . [6144 x 12288] per step),

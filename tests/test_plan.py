@@ -133,10 +133,38 @@ def test_hop_add_gemms_do_not_wait_for_the_previous_hop(N):
     assert last_waits == [N - 2]
 
 
+PIPE_ADD = [(N, chunks, n_comm, sched) for N in (1, 2, 3, 4, 5, 8) for chunks in (1, 2, 4)
+            for n_comm in sorted({1, 2, N}) for sched in ("decomposed", "naive") if sched == "decomposed" or chunks == 1]
+
+
+@pytest.mark.parametrize("N,chunks,n_comm,sched", PIPE_ADD)
+def test_pipe_hop_add_program_matches_oracle(N, chunks, n_comm, sched):
+    """Pipeline-chunk (and naive) ReduceScatter with add-and-forward hops:
+    exact on integers against the oracle, race-free, each output written once,
+    no copies, and no GEMM waits for a comm stream (every chunk has its own
+    ring slots)."""
+    m, k, n = 3, 64, 64 * chunks
+    op = "rs_pipe" if sched == "decomposed" else "rs"
+    for out in ("f32", "bf16"):
+        plan, sim, a, w = simulate(op, N, m, k, n, "uni", chunks, sched, out, n_comm, hop="add")
+        assert np.array_equal(output(sim, plan), expect("rs", a, w, out))
+        assert (sim.writes[nat.CM_BUF_Y] == 1).all()
+    ops, _ = nat.cm_plan_program(plan)
+    assert not any(o.kind == nat.CM_OPK_COPY for o in ops)
+    assert not any(o.kind == nat.CM_OPK_WAIT and o.stream == 0 and o.step >= 0 for o in ops)
+
+
+def test_pipe_hop_add_splits_large_launches():
+    # N = 16: 256 (rank, bucket) jobs per chunk in launches of at most 128
+    plan, sim, a, w = simulate("rs_pipe", 16, 2, 64, 128, "uni", 2, "decomposed", "f32", 1, hop="add")
+    assert np.array_equal(output(sim, plan), expect("rs", a, w, "f32"))
+    ops, _ = nat.cm_plan_program(plan)
+    assert max(o.n_jobs for o in ops if o.kind == nat.CM_OPK_GEMM) <= 128
+
+
 def test_hop_add_is_only_for_the_ring_rs():
     base = dict(n_ranks=4, m=8, k=64, n=128, hop="add")
-    for kw in (dict(op="ag"), dict(op="rs_pipe", chunks=2), dict(op="rs", sched="naive"), dict(op="rs", dir="direct"),
-               dict(op="rs", bucket="bf16")):
+    for kw in (dict(op="ag"), dict(op="rs", dir="direct"), dict(op="rs", bucket="bf16")):
         st, _ = nat.cm_ring_plan_status(nat.make_desc(**dict(base, **kw)))
         assert st == nat.CM_ERR_UNSUPPORTED, kw
     st, _ = nat.cm_ring_plan_status(nat.make_desc(op="rs", n_ranks=4, m=8, k=64, n=128, hop=2))
@@ -288,7 +316,8 @@ def _drop_op(sim, index):
 @pytest.mark.parametrize("op,dir,chunks,hop", [("ag", "uni", 1, "copy"), ("ag", "bi", 2, "copy"),
                                                ("rs", "uni", 2, "copy"), ("rs", "bi", 2, "copy"),
                                                ("rs_pipe", "uni", 2, "copy"), ("ag", "uni", 2, "copy"),
-                                               ("rs", "uni", 1, "add"), ("rs", "bi", 2, "add")])
+                                               ("rs", "uni", 1, "add"), ("rs", "bi", 2, "add"),
+                                               ("rs_pipe", "uni", 2, "add")])
 def test_dropped_dependency_is_caught(op, dir, chunks, hop):
     """Negative control: removing any one wait that orders a hop against a GEMM makes a race."""
     N, m, k = 4, 4 * chunks, 64
@@ -361,6 +390,12 @@ def _gpu_cases():
     for dir in ("uni", "bi"):
         cases.append(dict(op="rs", n_ranks=8, m=256, k=6144, n=12288, dir=dir, chunks=1, out_dtype="bf16", n_comm=1,
                           hop="add"))
+    for op, N, m, k, n, chunks, n_comm, sched in g.PIPE_ADD:
+        for out in ("f32", "bf16"):
+            cases.append(dict(op=op, n_ranks=N, m=m, k=k, n=n, chunks=chunks, out_dtype=out, n_comm=n_comm,
+                              sched=sched, hop="add"))
+    for hop in ("add", "copy"):
+        cases.append(dict(op="rs_pipe", n_ranks=8, m=512, k=1024, n=8192, chunks=4, out_dtype="f32", n_comm=1, hop=hop))
     for op in ("ag", "rs", "rs_pipe"):
         for kw in (dict(), dict(copy_gbps=1.0)):
             cases.append(dict(op=op, n_ranks=4, m=64, k=256, n=256, sched="auto", out_dtype="f32", n_comm=2, **kw))
