@@ -170,7 +170,7 @@ __device__ __forceinline__ void epilogue_mode(const f32x16 (&acc)[TM][TN], const
 // without addends get their own instantiation, whose register allocation
 // is not sized for the addend reads.
 template <int BM, int BN, int WM, int WN, int BK, int AST, int BST, int NL, int LP, bool ADD>
-__global__ __launch_bounds__(512 + 64 * NL) void gemm_jobs_kernel(const GemmParams p) {
+__global__ __launch_bounds__(64 * (WM * WN) + 64 * NL) void gemm_jobs_kernel(const GemmParams p) {
   // A (activations, shared by every tile of a job and mostly served from L2)
   // and B (weights, streamed from HBM once per launch) have separate LDS
   // rings of AST and BST slabs, so each stream gets its own prefetch depth.
@@ -180,14 +180,15 @@ __global__ __launch_bounds__(512 + 64 * NL) void gemm_jobs_kernel(const GemmPara
   constexpr int ROWB = 2 * BK, CH = BK / 8, RPG = 1024 / ROWB, RPB = 256 / ROWB;
   constexpr int A_GROUPS = BM / RPG, B_GROUPS = BN / RPG;  // 1 KB load groups per slab
   constexpr int A_SLAB = BM * ROWB, B_SLAB = BN * ROWB;
-  static_assert(WM * WN == 8, "eight waves");
+  constexpr int MW = WM * WN;  // MFMA waves: 8 (two per SIMD) or 4 (one per SIMD, larger wave tiles)
+  static_assert(MW == 8 || MW == 4, "four or eight MFMA waves");
   static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "tile shape");
   static_assert(BK == 32 || BK == 64, "slab depth");
   // NL = 0: the eight MFMA waves also issue the loads.  NL > 0: NL extra
   // waves issue every load and the eight MFMA waves never wait on the vector
   // memory pipe (a wave that issues a load behind a full address queue
   // stalls, and with it the MFMAs queued behind the load).
-  constexpr int NLW = NL > 0 ? NL : 8;  // waves that issue loads
+  constexpr int NLW = NL > 0 ? NL : MW;  // waves that issue loads
   static_assert(NL == 0 || NL == 2 || NL == 4, "loader waves");
   // LP = 0: loads go straight to LDS (global_load_lds).  LP >= 2: the
   // loader waves load into LP register sets (LP slabs ahead) and store to
@@ -217,8 +218,8 @@ __global__ __launch_bounds__(512 + 64 * NL) void gemm_jobs_kernel(const GemmPara
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
-  const bool loader = NL == 0 || wave >= 8;  // this wave issues loads
-  const int lw = NL == 0 ? wave : (wave >= 8 ? wave - 8 : 0);  // its index among the loading waves
+  const bool loader = NL == 0 || wave >= MW;  // this wave issues loads
+  const int lw = NL == 0 ? wave : (wave >= MW ? wave - MW : 0);  // its index among the loading waves
 
   // Direct-to-LDS addressing: load i of loading wave w fills the 1 KB group
   // (NLW i + w); lane l writes position l % CH of row l / CH of the group,
@@ -486,7 +487,7 @@ template <int BM, int BN, int WM, int WN, int BK, int AST, int BST, int NL, int 
 void pick_gemm(bool add, void **f, int *threads) {
   *f = add ? reinterpret_cast<void *>(&gemm_jobs_kernel<BM, BN, WM, WN, BK, AST, BST, NL, LP, true>)
            : reinterpret_cast<void *>(&gemm_jobs_kernel<BM, BN, WM, WN, BK, AST, BST, NL, LP, false>);
-  *threads = 512 + 64 * NL;
+  *threads = 64 * (WM * WN) + 64 * NL;
 }
 
 bool gemm_launch_config(const GemmParams &p, int tm, int tn, KernelLaunch *out) {
