@@ -180,3 +180,32 @@ def layernorm_inputs(rows, cols, seed=0):
     mu = gen.standard_normal((rows, 1), dtype=np.float32) * np.float32(2.0)
     sd = gen.uniform(0.25, 4.0, (rows, 1)).astype(np.float32)
     return (mu + sd * gen.standard_normal((rows, cols), dtype=np.float32)).astype(np.float32)
+
+
+def backward_inputs(kind, N, m, k, n, dist="normal", seed=0):
+    """Inputs of the backward of a collective matmul as bf16 bit patterns:
+    kind "col" (AllGather -> GEMM): x [N, m, k], w [N, n, k], dy [N, N*m, n];
+    kind "row" (GEMM -> ReduceScatter): h [N, N*m, k], w [N, n, k],
+    dout [N, m, n].  Activations N(0,1), weights N(0, 0.02^2), upstream
+    gradients N(0,1) (a scale-free stand-in: the ops are linear in them)."""
+    g = [np.random.Generator(np.random.PCG64(s)) for s in np.random.SeedSequence([seed, 9]).spawn(3)]
+    if kind == "col":
+        shapes = ((N, m, k), (N, n, k), (N, N * m, n))
+    else:
+        shapes = ((N, N * m, k), (N, n, k), (N, m, n))
+    stds = (ACT_STD, WEIGHT_STD, ACT_STD)
+    return tuple(f32_to_bf16_bits(_draw(g[i], shapes[i], dist, stds[i])) for i in range(3))
+
+
+def backward_inputs_torch(kind, N, m, k, n, dist="normal", seed=0, device="cuda"):
+    import torch
+    gen_ = torch.Generator(device=device)
+    if kind == "col":
+        shapes = ((N, m, k), (N, n, k), (N, N * m, n))
+    else:
+        shapes = ((N, N * m, k), (N, n, k), (N, m, n))
+    out = []
+    for i, (shape, std) in enumerate(zip(shapes, (ACT_STD, WEIGHT_STD, ACT_STD))):
+        gen_.manual_seed(seed * 8 + 120 + i + (3 if kind == "row" else 0))
+        out.append(_torch_draw(shape, dist, std, gen_, device))
+    return tuple(out)

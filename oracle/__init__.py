@@ -9,8 +9,9 @@ arrays of bf16 bit patterns; outputs are float64.  Shapes:
     ag_gemm:  x [N, m, k], w [N, n, k]    -> y   [N, N*m, n]
     gemm_rs:  h [N, N*m, k], w [N, n, k]  -> out [N, m, n]
     allreduce: same inputs as gemm_rs     -> ar  [N*m, n]
-and the sequence-parallel transformer layer around them (attention,
-LayerNorm, GELU and the chained layer, sp_layer_rows).
+the sequence-parallel transformer layer around them (attention,
+LayerNorm, GELU and the chained layer, sp_layer_rows), and the backward pass
+of both collective matmuls (col_backward, row_backward).
 """
 import ctypes
 import os
@@ -62,6 +63,10 @@ def _bind(lib):
     lib.orc_layernorm.argtypes = [ci, ci, f64p, ctypes.c_double, f64p_or_null, f64p_or_null, f64p]
     lib.orc_gelu.restype = None
     lib.orc_gelu.argtypes = [f64p, f64p, ctypes.c_size_t]
+    for name in ("orc_col_backward", "orc_row_backward"):
+        f = getattr(lib, name)
+        f.restype = None
+        f.argtypes = [ci, ci, ci, ci, u16p, u16p, u16p, f64p, f64p, f64p_or_null, f64p_or_null]
     return lib
 
 
@@ -319,3 +324,37 @@ def sp_layer_rows(x, wqkv, wo, w1, w2, heads, tokens, eps=1e-5, causal=True, lib
         out += fc1[r] @ w2r.T
         mag += np.abs(fc1[r]) @ np.abs(w2r).T
     return {"out": out, "mag": mag, "qkv": bf16_to_f64(qkv), "attn": attn, "proj": proj, "ln": ln, "fc1": fc1}
+
+
+# ---------------------------------------------------------------- backward
+def col_backward(x, w, dy, with_mag=False, lib=None):
+    """Backward of AllGather -> GEMM (see oracle.c): x [N, m, k], w [N, n, k],
+    dy [N, N*m, n] -> dx [N, m, k], dw [N, n, k] (and their mags)."""
+    lib = lib or load()
+    x, w, dy = _u16(x), _u16(w), _u16(dy)
+    N, m, k = x.shape
+    n = w.shape[1]
+    assert w.shape == (N, n, k) and dy.shape == (N, N * m, n)
+    dx = np.empty((N, m, k))
+    dw = np.empty((N, n, k))
+    mx = np.empty_like(dx) if with_mag else None
+    mw = np.empty_like(dw) if with_mag else None
+    lib.orc_col_backward(N, m, k, n, x, w, dy, dx, dw, _ptr(mx), _ptr(mw))
+    return (dx, dw, mx, mw) if with_mag else (dx, dw)
+
+
+def row_backward(h, w, dout, with_mag=False, lib=None):
+    """Backward of GEMM -> ReduceScatter: h [N, N*m, k], w [N, n, k],
+    dout [N, m, n] -> dh [N, N*m, k], dw [N, n, k] (and their mags)."""
+    lib = lib or load()
+    h, w, dout = _u16(h), _u16(w), _u16(dout)
+    N, T, k = h.shape
+    n = w.shape[1]
+    m = T // N
+    assert w.shape == (N, n, k) and dout.shape == (N, m, n)
+    dh = np.empty((N, T, k))
+    dw = np.empty((N, n, k))
+    mh = np.empty_like(dh) if with_mag else None
+    mw = np.empty_like(dw) if with_mag else None
+    lib.orc_row_backward(N, m, k, n, h, w, dout, dh, dw, _ptr(mh), _ptr(mw))
+    return (dh, dw, mh, mw) if with_mag else (dh, dw)

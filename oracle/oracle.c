@@ -420,3 +420,102 @@ void orc_layernorm(int rows, int cols, const double *x, double eps, const double
 void orc_gelu(const double *x, double *y, size_t count) {
   for (size_t t = 0; t < count; ++t) y[t] = 0.5 * x[t] * (1.0 + erf(x[t] / sqrt(2.0)));
 }
+
+/* ------------------------------------------------------------------------
+ * The backward pass of the two collective matmuls.  "Tensor Parallelism >
+ * Communication Patterns" states that the backward communication pattern is
+ * the dual of the forward one: the gradient of an AllGather->GEMM's input is
+ * reduce-scattered, the gradient of a GEMM->ReduceScatter's input is
+ * all-gathered.  With the forward definitions above:
+ *
+ *   column-parallel (forward Y_r = Xfull . W_r^T), given dY_r [T][n]:
+ *       dX_q  = sum_r (dY_r . W_r)[q*m:(q+1)*m, :]      [m][k], ranks in order
+ *       dW_r  = dY_r^T . Xfull                            [n][k]
+ *   row-parallel (forward Out_q = sum_r (H_r . W_r^T)[q rows]), given dOut_q [m][n]:
+ *       dH_r  = dOutfull . W_r                            [T][k], dOutfull = concat_q dOut_q
+ *       dW_r  = dOutfull^T . H_r                          [n][k]
+ *
+ * These are the gradients of the scalar sum_r <dY_r, Y_r> (resp.
+ * sum_q <dOut_q, Out_q>) with respect to X (resp. H) and W_r.  fp64, summed in
+ * increasing index order; mag outputs (or NULL) receive the same sums of
+ * absolute values.
+ * ------------------------------------------------------------------------ */
+
+/* out[i][j] = sum_t a[t*lda + i] * b[t*ldb + j] over t < T (a contraction over
+ * the leading index of both operands), i < ni, j < nj. */
+static void at_b(const uint16_t *a, int lda, const uint16_t *b, int ldb, int T, int ni, int nj, double *out,
+                 double *mag) {
+#pragma omp parallel for schedule(static)
+  for (int i = 0; i < ni; ++i)
+    for (int j = 0; j < nj; ++j) {
+      double acc = 0.0, accabs = 0.0;
+      for (int t = 0; t < T; ++t) {
+        const double p = bf16_value(a[(size_t)t * lda + i]) * bf16_value(b[(size_t)t * ldb + j]);
+        acc += p;
+        accabs += fabs(p);
+      }
+      out[(size_t)i * nj + j] = acc;
+      if (mag) mag[(size_t)i * nj + j] = accabs;
+    }
+}
+
+/* out[t][j] = sum_c a[t][c] * w[c][j] (w stored [nc][nj], its leading index
+ * contracted), t < rows. */
+static void a_w(const uint16_t *a, const uint16_t *w, int rows, int nc, int nj, double *out, double *mag) {
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < rows; ++t)
+    for (int j = 0; j < nj; ++j) {
+      double acc = 0.0, accabs = 0.0;
+      for (int c = 0; c < nc; ++c) {
+        const double p = bf16_value(a[(size_t)t * nc + c]) * bf16_value(w[(size_t)c * nj + j]);
+        acc += p;
+        accabs += fabs(p);
+      }
+      out[(size_t)t * nj + j] = acc;
+      if (mag) mag[(size_t)t * nj + j] = accabs;
+    }
+}
+
+/*
+ * Column-parallel backward.
+ *   x  [N][m][k], w [N][n][k], dy [N][N*m][n]   (bf16)
+ *   dx [N][m][k], dw [N][n][k]                  (fp64; mags or NULL)
+ */
+void orc_col_backward(int N, int m, int k, int n, const uint16_t *x, const uint16_t *w, const uint16_t *dy,
+                      double *dx, double *dw, double *dx_mag, double *dw_mag) {
+  const size_t T = (size_t)N * m;
+  double *part = (double *)malloc(sizeof(double) * T * k);
+  double *pmag = dx_mag ? (double *)malloc(sizeof(double) * T * k) : NULL;
+  for (size_t i = 0; i < (size_t)N * m * k; ++i) {
+    dx[i] = 0.0;
+    if (dx_mag) dx_mag[i] = 0.0;
+  }
+  for (int r = 0; r < N; ++r) {
+    /* dY_r . W_r over all T rows, then each owner q takes rows q*m.. */
+    a_w(dy + (size_t)r * T * n, w + (size_t)r * n * k, (int)T, n, k, part, pmag);
+    for (size_t i = 0; i < T * k; ++i) {
+      dx[i] += part[i]; /* dx [N][m][k] is the row-major [T][k] of the owners' blocks */
+      if (dx_mag) dx_mag[i] += pmag[i];
+    }
+    /* dW_r = dY_r^T . Xfull (Xfull rows = x read as [T][k]) */
+    at_b(dy + (size_t)r * T * n, n, x, k, (int)T, n, k, dw + (size_t)r * n * k, dw_mag ? dw_mag + (size_t)r * n * k : NULL);
+  }
+  free(part);
+  free(pmag);
+}
+
+/*
+ * Row-parallel backward.
+ *   h [N][N*m][k], w [N][n][k], dout [N][m][n]  (bf16)
+ *   dh [N][N*m][k], dw [N][n][k]                (fp64; mags or NULL)
+ */
+void orc_row_backward(int N, int m, int k, int n, const uint16_t *h, const uint16_t *w, const uint16_t *dout,
+                      double *dh, double *dw, double *dh_mag, double *dw_mag) {
+  const size_t T = (size_t)N * m;
+  for (int r = 0; r < N; ++r) {
+    /* dH_r = dOutfull . W_r (dOutfull rows = dout read as [T][n]) */
+    a_w(dout, w + (size_t)r * n * k, (int)T, n, k, dh + (size_t)r * T * k, dh_mag ? dh_mag + (size_t)r * T * k : NULL);
+    /* dW_r = dOutfull^T . H_r */
+    at_b(dout, n, h + (size_t)r * T * k, k, (int)T, n, k, dw + (size_t)r * n * k, dw_mag ? dw_mag + (size_t)r * n * k : NULL);
+  }
+}
