@@ -13,7 +13,8 @@ LIB_PATH = os.path.join(PKG, "libcollmm.so")
 # enums (collmm.h)
 CM_OK, CM_ERR_INVALID_ARG, CM_ERR_SHAPE, CM_ERR_ALIGN, CM_ERR_WORKSPACE, CM_ERR_UNSUPPORTED, CM_ERR_HIP, \
     CM_ERR_CAPACITY = range(8)
-CM_OP_AG_GEMM, CM_OP_GEMM_RS, CM_OP_GEMM_RS_PIPE = range(3)
+CM_OP_AG_GEMM, CM_OP_GEMM_RS, CM_OP_GEMM_RS_PIPE, CM_OP_ALLGATHER = range(4)
+CM_BWD_COL, CM_BWD_ROW = range(2)
 CM_RING_UNI, CM_RING_BI, CM_RING_DIRECT = range(3)
 CM_SCHED_DECOMPOSED, CM_SCHED_NAIVE, CM_SCHED_AUTO = range(3)
 CM_BF16, CM_F32 = range(2)
@@ -26,7 +27,8 @@ CM_MAX_RANKS, CM_MAX_CHUNKS, CM_MAX_COMM = 64, 16, 32
 
 EXPORTS = ["cm_ring_plan", "cm_pick_overlap", "cm_workspace_size", "cm_plan_program", "cm_trace_create", "cm_trace_destroy",
            "cm_trace_read", "cm_ag_gemm", "cm_gemm_rs", "cm_attention", "cm_layernorm", "cm_plan_layer",
-           "cm_layer_forward", "cm_status_string", "cm_last_error", "cm_version"]
+           "cm_layer_forward", "cm_allgather", "cm_transpose", "cm_gemm", "cm_plan_backward", "cm_linear_backward",
+           "cm_status_string", "cm_last_error", "cm_version"]
 
 
 class cm_plan_desc(ctypes.Structure):
@@ -82,6 +84,16 @@ class cm_layer_plan(ctypes.Structure):
         [(f, ctypes.c_size_t) for f in ("off_qkv", "off_attn", "off_proj", "off_ln", "off_fc1", "off_ops", "ws_bytes")]
 
 
+class cm_bwd_desc(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_int) for f in ("kind", "n_ranks", "m", "k", "n", "dir", "chunks", "n_comm", "bulk",
+                                            "dx_dtype", "dw_dtype", "exec_mode", "copy_engine")]
+
+
+class cm_bwd_plan(ctypes.Structure):
+    _fields_ = [("desc", cm_bwd_desc), ("dgrad", cm_plan), ("gather", cm_plan)] + \
+        [(f, ctypes.c_size_t) for f in ("off_wt", "off_g", "off_gt", "off_ot", "off_ops", "ws_bytes")]
+
+
 class CMError(RuntimeError):
     def __init__(self, status, where, detail):
         self.status = status
@@ -114,6 +126,13 @@ def lib():
         L.cm_attention.argtypes = [vp, vp, ci, ci, ci, ci, ci, vp]
         L.cm_layernorm.argtypes = [vp, vp, ci, ci, ctypes.c_float, vp, vp, vp]
         L.cm_plan_layer.argtypes = [ctypes.POINTER(cm_layer_desc), ctypes.POINTER(cm_layer_plan)]
+        L.cm_allgather.argtypes = [ctypes.POINTER(cm_plan), vp, vp, vp, ctypes.POINTER(vp), ci, vp]
+        L.cm_transpose.argtypes = [vp, vp, ci, ci, ci, ci, vp]
+        ll = ctypes.c_longlong
+        L.cm_gemm.argtypes = [ci, ci, ci, ci, vp, ci, ll, vp, ci, ll, vp, ci, ll, ci, vp]
+        L.cm_plan_backward.argtypes = [ctypes.POINTER(cm_bwd_desc), ctypes.POINTER(cm_bwd_plan)]
+        L.cm_linear_backward.argtypes = [ctypes.POINTER(cm_bwd_plan), vp, vp, vp, vp, vp, vp, vp, cs, vp,
+                                         ctypes.POINTER(vp), ci]
         L.cm_layer_forward.argtypes = [ctypes.POINTER(cm_layer_plan), vp, vp, vp, vp, vp, vp, vp, cs, vp,
                                        ctypes.POINTER(vp), ci]
         for name in EXPORTS:
@@ -151,7 +170,8 @@ def version():
 
 
 _ENUMS = {
-    "op": {"ag": CM_OP_AG_GEMM, "rs": CM_OP_GEMM_RS, "rs_pipe": CM_OP_GEMM_RS_PIPE},
+    "op": {"ag": CM_OP_AG_GEMM, "rs": CM_OP_GEMM_RS, "rs_pipe": CM_OP_GEMM_RS_PIPE, "allgather": CM_OP_ALLGATHER},
+    "bwd": {"col": CM_BWD_COL, "row": CM_BWD_ROW},
     "dir": {"uni": CM_RING_UNI, "bi": CM_RING_BI, "direct": CM_RING_DIRECT},
     "sched": {"decomposed": CM_SCHED_DECOMPOSED, "naive": CM_SCHED_NAIVE, "auto": CM_SCHED_AUTO},
     "dtype": {"bf16": CM_BF16, "f32": CM_F32},
@@ -340,3 +360,68 @@ def cm_layer_forward(plan, x, wqkv, wo, w1, w2, out, ws, compute, comm, ws_bytes
         ws_bytes = ws.numel() * ws.element_size()
     _check(lib().cm_layer_forward(ctypes.byref(plan), _ptr(x), _ptr(wqkv), _ptr(wo), _ptr(w1), _ptr(w2), _ptr(out),
                                   _ptr(ws), ws_bytes, _stream(compute), arr, len(comm)), "cm_layer_forward")
+
+
+# ------------------------------------------------------------ backward
+def cm_allgather(plan, x, y, compute, comm, trace=None):
+    """AllGather of the shards x [N, m, k] into y [N, N*m, k] through the C ABI."""
+    comm = list(comm or [])
+    arr = (ctypes.c_void_p * max(1, len(comm)))(*[_stream(s) for s in comm])
+    _check(lib().cm_allgather(ctypes.byref(plan), _ptr(x), _ptr(y), _stream(compute), arr, len(comm),
+                              trace.handle if trace is not None else None), "cm_allgather")
+
+
+def cm_transpose(src, dst, batch, rows, cols, ld_dst=None, stream=None):
+    _check(lib().cm_transpose(_ptr(src), _ptr(dst), batch, rows, cols, rows if ld_dst is None else ld_dst,
+                              _stream(stream)), "cm_transpose")
+
+
+def cm_transpose_status(src, dst, batch, rows, cols, ld_dst, stream=None):
+    return lib().cm_transpose(_ptr(src), _ptr(dst), batch, rows, cols, ld_dst, _stream(stream))
+
+
+def cm_gemm(batch, M, N, K, a, lda, stride_a, b, ldb, stride_b, c, ldc, stride_c, out_dtype="f32", stream=None):
+    """C_b = A_b . B_b^T for b < batch (bf16 in, fp32 accumulate)."""
+    od = _ENUMS["dtype"][out_dtype] if isinstance(out_dtype, str) else int(out_dtype)
+    _check(lib().cm_gemm(batch, M, N, K, _ptr(a), lda, stride_a, _ptr(b), ldb, stride_b, _ptr(c), ldc, stride_c, od,
+                         _stream(stream)), "cm_gemm")
+
+
+def cm_gemm_status(batch, M, N, K, a, lda, stride_a, b, ldb, stride_b, c, ldc, stride_c, out_dtype=CM_F32, stream=None):
+    return lib().cm_gemm(batch, M, N, K, _ptr(a), lda, stride_a, _ptr(b), ldb, stride_b, _ptr(c), ldc, stride_c,
+                         out_dtype, _stream(stream))
+
+
+def make_bwd_desc(kind, n_ranks, m, k, n, dir="uni", chunks=0, n_comm=1, bulk=True, dx_dtype="f32", dw_dtype="f32",
+                  exec_mode="graph", copy_engine="sdma"):
+    def e(cat, v):
+        return _ENUMS[cat][v] if isinstance(v, str) else int(v)
+    return cm_bwd_desc(kind=e("bwd", kind), n_ranks=n_ranks, m=m, k=k, n=n, dir=e("dir", dir), chunks=chunks,
+                       n_comm=n_comm, bulk=1 if bulk else 0, dx_dtype=e("dtype", dx_dtype),
+                       dw_dtype=e("dtype", dw_dtype), exec_mode=e("exec", exec_mode),
+                       copy_engine=e("copy", copy_engine))
+
+
+def cm_plan_backward(desc=None, **kw):
+    if desc is None:
+        desc = make_bwd_desc(**kw)
+    p = cm_bwd_plan()
+    _check(lib().cm_plan_backward(ctypes.byref(desc), ctypes.byref(p)), "cm_plan_backward")
+    return p
+
+
+def cm_plan_backward_status(desc):
+    p = cm_bwd_plan()
+    return lib().cm_plan_backward(ctypes.byref(desc), ctypes.byref(p)), p
+
+
+def cm_linear_backward(plan, act, w, wt, grad, dact, dw, ws, compute, comm, ws_bytes=None):
+    """Backward of a collective matmul: comm = the input gradient's n_comm
+    streams, then the bulk stream, then the bulk AllGather's copy lane."""
+    comm = list(comm or [])
+    arr = (ctypes.c_void_p * max(1, len(comm)))(*[_stream(s) for s in comm])
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(lib().cm_linear_backward(ctypes.byref(plan), _ptr(act), _ptr(w), _ptr(wt), _ptr(grad), _ptr(dact),
+                                    _ptr(dw), _ptr(ws), ws_bytes, _stream(compute), arr, len(comm)),
+           "cm_linear_backward")

@@ -267,15 +267,21 @@ cm_status event_pool(int dev, int n, std::vector<hipEvent_t> **out) {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-cm_status validate_call(const cm_plan *pl, bool want_ag, const void *x, const void *w, void *y, void *ws,
+// Which entry point a call came through.
+enum Entry { kEntryAG = 0, kEntryRS = 1, kEntryGather = 2 };
+
+cm_status validate_call(const cm_plan *pl, Entry want, const void *x, const void *w, void *y, void *ws,
                         size_t ws_bytes, void *compute, void *const *comm, int n_comm) {
   if (!pl) { set_error("null plan"); return CM_ERR_INVALID_ARG; }
   cm_status st = validate_desc(pl->desc);
   if (st != CM_OK) return st;
-  const bool is_ag = pl->desc.op == CM_OP_AG_GEMM;
-  if (is_ag != want_ag) {
-    set_error(want_ag ? "cm_ag_gemm needs a plan with op CM_OP_AG_GEMM"
-                      : "cm_gemm_rs needs a plan with op CM_OP_GEMM_RS or CM_OP_GEMM_RS_PIPE");
+  const int op = pl->desc.op;
+  const Entry is = op == CM_OP_AG_GEMM ? kEntryAG : op == CM_OP_ALLGATHER ? kEntryGather : kEntryRS;
+  const bool is_ag = is != kEntryRS;  // row-chunked (or unchunked) ops
+  if (is != want) {
+    set_error(want == kEntryAG   ? "cm_ag_gemm needs a plan with op CM_OP_AG_GEMM"
+              : want == kEntryRS ? "cm_gemm_rs needs a plan with op CM_OP_GEMM_RS or CM_OP_GEMM_RS_PIPE"
+                                 : "cm_allgather needs a plan with op CM_OP_ALLGATHER");
     return CM_ERR_INVALID_ARG;
   }
   if (pl->chunks < 1 || pl->chunks > CM_MAX_CHUNKS) { set_error("plan has invalid chunk count"); return CM_ERR_INVALID_ARG; }
@@ -485,9 +491,9 @@ std::string graph_key(const cm_plan &pl, char *const base[4], const cm_trace *tr
   return plan_key(pl) + buf;
 }
 
-cm_status run(const cm_plan *pl, bool want_ag, const void *x, const void *w, void *y, void *ws, size_t ws_bytes,
+cm_status run(const cm_plan *pl, Entry want, const void *x, const void *w, void *y, void *ws, size_t ws_bytes,
               void *compute, void *const *comm, int n_comm, cm_trace *trace) {
-  cm_status st = validate_call(pl, want_ag, x, w, y, ws, ws_bytes, compute, comm, n_comm);
+  cm_status st = validate_call(pl, want, x, w, y, ws, ws_bytes, compute, comm, n_comm);
   if (st != CM_OK) return st;
   int dev;
   if ((st = check_device(&dev)) != CM_OK) return st;
@@ -557,12 +563,18 @@ extern "C" {
 
 cm_status cm_ag_gemm(const cm_plan *plan, const void *x, const void *w, void *y, void *ws, size_t ws_bytes,
                      void *compute, void *const *comm, int n_comm, cm_trace *trace) {
-  return collmm::run(plan, true, x, w, y, ws, ws_bytes, compute, comm, n_comm, trace);
+  return collmm::run(plan, collmm::kEntryAG, x, w, y, ws, ws_bytes, compute, comm, n_comm, trace);
 }
 
 cm_status cm_gemm_rs(const cm_plan *plan, const void *x, const void *w, void *y, void *ws, size_t ws_bytes,
                      void *compute, void *const *comm, int n_comm, cm_trace *trace) {
-  return collmm::run(plan, false, x, w, y, ws, ws_bytes, compute, comm, n_comm, trace);
+  return collmm::run(plan, collmm::kEntryRS, x, w, y, ws, ws_bytes, compute, comm, n_comm, trace);
+}
+
+cm_status cm_allgather(const cm_plan *plan, const void *x, void *y, void *compute, void *const *comm, int n_comm,
+                       cm_trace *trace) {
+  // the program reads only x and writes only y; x stands in for the unused weight pointer
+  return collmm::run(plan, collmm::kEntryGather, x, x, y, y, 0, compute, comm, n_comm, trace);
 }
 
 cm_status cm_trace_create(int capacity, cm_trace **out) {

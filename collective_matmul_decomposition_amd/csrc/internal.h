@@ -26,6 +26,8 @@ struct Program {
 };
 
 void set_error(const char *fmt, ...);
+// The compiled GEMM block tile that fits `jobs` jobs of rows x cols outputs best.
+double choose_gemm_tile(int rows, int cols, int jobs, int *tm, int *tn);
 const char *last_error();
 cm_status validate_desc(const cm_plan_desc &d);
 cm_status plan(const cm_plan_desc *desc, cm_plan *out);

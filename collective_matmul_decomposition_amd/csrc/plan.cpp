@@ -99,6 +99,8 @@ double choose_tile(int rows, int cols, int jobs, int *tm, int *tn) {
 
 }  // namespace
 
+double choose_gemm_tile(int rows, int cols, int jobs, int *tm, int *tn) { return choose_tile(rows, cols, jobs, tm, tn); }
+
 void set_error(const char *fmt, ...) {
   char buf[512];
   va_list ap;
@@ -124,7 +126,9 @@ WsLayout ws_layout(const cm_plan &pl) {
   const size_t N = d.n_ranks, m = d.m, k = d.k, n = d.n, c = pl.chunks, T = N * m;
   WsLayout L{};
   const int ndir = d.dir == CM_RING_BI ? 2 : 1;
-  if (d.op == CM_OP_AG_GEMM) {
+  if (d.op == CM_OP_ALLGATHER) {
+    L.total = 0;
+  } else if (d.op == CM_OP_AG_GEMM) {
     if (d.sched == CM_SCHED_NAIVE) {
       L.gather = 0;
       L.total = N * T * k * 2;
@@ -162,7 +166,23 @@ WsLayout ws_layout(const cm_plan &pl) {
 
 // ---------------------------------------------------------------- validation
 cm_status validate_desc(const cm_plan_desc &d) {
-  if (d.op < CM_OP_AG_GEMM || d.op > CM_OP_GEMM_RS_PIPE) { set_error("unknown op %d", d.op); return CM_ERR_INVALID_ARG; }
+  if (d.op < CM_OP_AG_GEMM || d.op > CM_OP_ALLGATHER) { set_error("unknown op %d", d.op); return CM_ERR_INVALID_ARG; }
+  if (d.op == CM_OP_ALLGATHER) {
+    if (d.n_ranks < 1 || d.n_ranks > CM_MAX_RANKS) { set_error("n_ranks %d outside 1..%d", d.n_ranks, CM_MAX_RANKS); return CM_ERR_INVALID_ARG; }
+    if (d.n_comm < 1 || d.n_comm > CM_MAX_COMM) { set_error("n_comm %d outside 1..%d", d.n_comm, CM_MAX_COMM); return CM_ERR_INVALID_ARG; }
+    if (d.m < 1 || d.k < 8 || d.k % 8) { set_error("AllGather: need m >= 1 and k a multiple of 8 (got m=%d k=%d)", d.m, d.k); return CM_ERR_SHAPE; }
+    if ((long long)d.n_ranks * d.m > (1 << 24)) { set_error("N*m too large"); return CM_ERR_SHAPE; }
+    if (d.n != 0 || d.dir != CM_RING_UNI || d.sched != CM_SCHED_DECOMPOSED || d.chunks > 1 || d.act || d.hop_add ||
+        d.bucket_bf16 || d.tile_m || d.tile_n) {
+      set_error("AllGather: n must be 0 and dir, sched, chunks, act, hop_add, bucket_bf16 and tile left at their defaults");
+      return CM_ERR_INVALID_ARG;
+    }
+    if (d.in_dtype != CM_BF16) { set_error("only bf16 inputs are supported"); return CM_ERR_UNSUPPORTED; }
+    if (d.exec_mode != CM_EXEC_GRAPH && d.exec_mode != CM_EXEC_EAGER) { set_error("unknown exec_mode %d", d.exec_mode); return CM_ERR_INVALID_ARG; }
+    if (d.copy_engine != CM_COPY_SDMA && d.copy_engine != CM_COPY_CU) { set_error("unknown copy_engine %d", d.copy_engine); return CM_ERR_INVALID_ARG; }
+    if (d.copy_gbps < 0 || d.mfma_tflops < 0 || d.launch_us < 0) { set_error("cost-model inputs must be >= 0"); return CM_ERR_INVALID_ARG; }
+    return CM_OK;
+  }
   if (d.n_ranks < 1 || d.n_ranks > CM_MAX_RANKS) { set_error("n_ranks %d outside 1..%d", d.n_ranks, CM_MAX_RANKS); return CM_ERR_INVALID_ARG; }
   if (d.dir != CM_RING_UNI && d.dir != CM_RING_BI && d.dir != CM_RING_DIRECT) { set_error("unknown ring direction %d", d.dir); return CM_ERR_INVALID_ARG; }
   if (d.sched != CM_SCHED_DECOMPOSED && d.sched != CM_SCHED_NAIVE && d.sched != CM_SCHED_AUTO) { set_error("unknown schedule %d", d.sched); return CM_ERR_INVALID_ARG; }
@@ -312,6 +332,25 @@ cm_status plan(const cm_plan_desc *desc, cm_plan *out) {
   if (d.launch_us == 0) d.launch_us = kDefaultLaunchUs;
   cm_status st = validate_desc(d);
   if (st != CM_OK) return st;
+  if (d.op == CM_OP_ALLGATHER) {
+    cm_plan p;
+    std::memset(&p, 0, sizeof p);
+    p.desc = d;
+    p.chunks = 1;
+    p.n_steps = 1;
+    p.arc_cw = d.n_ranks - 1;
+    const int per_lane = std::max(1, std::min(2, d.n_ranks / std::max(1, d.n_comm)));
+    p.est_hop_us = hop_us(d, (double)d.n_ranks * d.m * d.k * 2.0, d.n_ranks, per_lane);
+    p.est_total_us = (d.n_ranks - 1) * p.est_hop_us;
+    p.ws_bytes = 0;
+    Program prog;
+    build_program(p, prog);
+    p.n_ops = (int)prog.ops.size();
+    p.n_jobs = (int)prog.jobs.size();
+    p.n_events = prog.n_events;
+    *out = p;
+    return CM_OK;
+  }
   // A two-rank ring has one neighbour: the bidirectional ring is the uni ring;
   // one rank has no transfers at all.
   if ((d.n_ranks <= 2 && d.dir == CM_RING_BI) || d.n_ranks == 1) d.dir = CM_RING_UNI;
@@ -692,17 +731,19 @@ struct Builder {
   }
 
   // --------------------------------------------------------------- AG, naive
-  void ag_naive() {
+  // The ring AllGather of the shards x[r] into every rank's gathered buffer
+  // (dst_buf + r * T * k * 2, shard q at row q * m), N - 1 rounds of copies on
+  // the comm streams; the compute stream then waits for all of it.
+  void gather_ring(int dst_buf, size_t dst_base) {
     const size_t shard_bytes = m * k * 2;
     const size_t rank_bytes = T * k * 2;  // G[r]
     std::vector<Group> G = groups(0, 1);
-    entry();
     cur_step = 0; cur_chunk = 0;
     std::vector<int> prev(G.size(), -1), cur(G.size(), -1);
     // every rank's own shard into its gathered buffer (the collective's local part)
     for (size_t gi = 0; gi < G.size(); ++gi)
       for (int r = G[gi].a; r < G[gi].b; ++r)
-        copy(G[gi].stream, CM_BUF_X, (size_t)r * shard_bytes, CM_BUF_WS, (size_t)r * rank_bytes + (size_t)r * shard_bytes,
+        copy(G[gi].stream, CM_BUF_X, (size_t)r * shard_bytes, dst_buf, dst_base + (size_t)r * rank_bytes + (size_t)r * shard_bytes,
              shard_bytes);
     for (int h = 0; h < N - 1; ++h) {
       cur_step = h;
@@ -717,23 +758,37 @@ struct Builder {
           int shard = mod(r - h, N);
           int dst = mod(r + 1, N);
           if (h == 0)
-            copy(g.stream, CM_BUF_X, (size_t)r * shard_bytes, CM_BUF_WS, (size_t)dst * rank_bytes + shard * shard_bytes,
+            copy(g.stream, CM_BUF_X, (size_t)r * shard_bytes, dst_buf, dst_base + (size_t)dst * rank_bytes + shard * shard_bytes,
                  shard_bytes);
           else
-            copy(g.stream, CM_BUF_WS, (size_t)r * rank_bytes + shard * shard_bytes, CM_BUF_WS,
-                 (size_t)dst * rank_bytes + shard * shard_bytes, shard_bytes);
+            copy(g.stream, dst_buf, dst_base + (size_t)r * rank_bytes + shard * shard_bytes, dst_buf,
+                 dst_base + (size_t)dst * rank_bytes + shard * shard_bytes, shard_bytes);
         }
         cur[gi] = record(g.stream);
       }
       prev = cur;
     }
     cur_step = N - 1;
-    // the whole gathered activation is needed before the GEMM
+    // the whole gathered activation is needed before what follows
     for (size_t gi = 0; gi < G.size(); ++gi) {
       int e = prev[gi];
       if (e < 0) e = record(G[gi].stream);  // N == 1: only the local copies
       wait(0, e);
     }
+  }
+
+  // AllGather alone (the bulk collective of the backward pass): y[r] = the
+  // gathered sequence for every rank r.
+  void allgather() {
+    entry();
+    gather_ring(CM_BUF_Y, 0);
+    exit_();
+  }
+
+  void ag_naive() {
+    const size_t rank_bytes = T * k * 2;  // G[r]
+    entry();
+    gather_ring(CM_BUF_WS, 0);
     std::vector<cm_job_rec> jobs;
     for (int r = 0; r < N; ++r) {
       cm_job_rec jb = job0();
@@ -1166,7 +1221,9 @@ void build_program(const cm_plan &p, Program &prog) {
   prog.n_events = 0;
   Builder b(p, prog);
   const cm_plan_desc &d = p.desc;
-  if (d.op == CM_OP_AG_GEMM) {
+  if (d.op == CM_OP_ALLGATHER) {
+    b.allgather();
+  } else if (d.op == CM_OP_AG_GEMM) {
     if (d.sched == CM_SCHED_NAIVE) b.ag_naive(); else b.ag_decomposed();
   } else if (d.op == CM_OP_GEMM_RS && d.sched == CM_SCHED_DECOMPOSED) {
     if (d.dir == CM_RING_DIRECT) b.rs_direct(); else b.rs_decomposed();

@@ -75,9 +75,13 @@ typedef enum {
 } cm_status;
 
 typedef enum {
-  CM_OP_AG_GEMM = 0,     /* AllGather -> GEMM */
-  CM_OP_GEMM_RS = 1,     /* GEMM -> ReduceScatter, circulating bucket */
-  CM_OP_GEMM_RS_PIPE = 2 /* GEMM -> ReduceScatter, pipeline chunks */
+  CM_OP_AG_GEMM = 0,      /* AllGather -> GEMM */
+  CM_OP_GEMM_RS = 1,      /* GEMM -> ReduceScatter, circulating bucket */
+  CM_OP_GEMM_RS_PIPE = 2, /* GEMM -> ReduceScatter, pipeline chunks */
+  CM_OP_ALLGATHER = 3     /* the AllGather alone (cm_allgather): k = row length in
+                             bf16 elements (a multiple of 8), n = 0; dir, sched,
+                             chunks, act, hop_add, bucket_bf16 and tile at their
+                             defaults */
 } cm_op;
 
 /*
@@ -435,6 +439,104 @@ cm_status cm_plan_layer(const cm_layer_desc *desc, cm_layer_plan *out);
 cm_status cm_layer_forward(const cm_layer_plan *plan, const void *x, const void *wqkv, const void *wo,
                            const void *w1, const void *w2, void *out, void *ws, size_t ws_bytes, void *compute,
                            void *const *comm, int n_comm);
+
+/* ------------------------------------------------------------------------
+ * The backward pass of the two collective matmuls, with bulk overlap.
+ *
+ * "Tensor Parallelism > Communication Patterns": the backward communication
+ * pattern is the dual of the forward one.  Megatron page, section 7 ("Bulk
+ * Overlap"): an AllGather that only the weight gradient needs can run on a
+ * communication stream while the input-gradient GEMM runs on the compute
+ * stream, into buffers the compute stream leaves alone until an event.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * AllGather alone: y[r] = concat_q x[q] for every virtual rank r, by N - 1
+ * ring hops of copies (the plan's copy engine).  plan from cm_ring_plan with op
+ * CM_OP_ALLGATHER; x [N][m][k] bf16, y [N][N*m][k] bf16 (16-byte aligned).
+ * Streams, ordering and errors as for cm_ag_gemm (no workspace).
+ */
+cm_status cm_allgather(const cm_plan *plan, const void *x, void *y, void *compute, void *const *comm, int n_comm,
+                       cm_trace *trace);
+
+/*
+ * Batched bf16 transpose: dst[b][c][r] = src[b][r][c] (r < rows, c < cols) and
+ * dst[b][c][r] = 0 for rows <= r < ld_dst, b < batch; src [batch][rows][cols],
+ * dst [batch][cols][ld_dst].  Asynchronous on `stream`.  Errors: CM_ERR_SHAPE
+ * (batch outside 1..65535, rows or cols < 1, ld_dst < rows), CM_ERR_INVALID_ARG,
+ * CM_ERR_ALIGN (odd addresses), CM_ERR_HIP.
+ */
+cm_status cm_transpose(const void *src, void *dst, int batch, int rows, int cols, int ld_dst, void *stream);
+
+/*
+ * Batched GEMM on the library's MFMA kernel: for b < batch,
+ *   C_b[i][j] = sum_kk A_b[i][kk] * B_b[j][kk]   (i < M, j < N, kk < K)
+ * A_b = a + b * stride_a (bf16, row stride lda), B_b = b + b * stride_b (bf16,
+ * row stride ldb), C_b = c + b * stride_c (out_dtype, row stride ldc); strides
+ * in elements.  fp32 accumulation; bf16 outputs rounded to nearest even.  K a
+ * multiple of 64; lda, ldb, stride_a and stride_b multiples of 8; stride_c a
+ * multiple of 4 (fp32) or 8 (bf16); 16-byte aligned pointers.
+ * Asynchronous.  Errors: CM_ERR_SHAPE, CM_ERR_INVALID_ARG, CM_ERR_ALIGN,
+ * CM_ERR_UNSUPPORTED, CM_ERR_HIP.
+ */
+cm_status cm_gemm(int batch, int M, int N, int K, const void *a, int lda, long long stride_a, const void *b, int ldb,
+                  long long stride_b, void *c, int ldc, long long stride_c, int out_dtype, void *stream);
+
+typedef enum {
+  CM_BWD_COL = 0, /* the forward was AllGather -> GEMM (column-parallel):
+                     dX = ReduceScatter_r(dY_r . W_r), dW_r = dY_r^T . Xfull */
+  CM_BWD_ROW = 1  /* the forward was GEMM -> ReduceScatter (row-parallel):
+                     dH_r = AllGather(dOut) . W_r, dW_r = AllGather(dOut)^T . H_r */
+} cm_bwd_kind;
+
+typedef struct {
+  int kind;         /* cm_bwd_kind */
+  int n_ranks, m, k, n; /* the forward's shapes: W_r [n][k]; T = N*m tokens */
+  int dir;          /* cm_ring_dir of the input gradient's collective matmul */
+  int chunks;       /* its chunks (0 = cost model) */
+  int n_comm;       /* its comm streams */
+  int bulk;         /* 1: the weight gradient's AllGather (and transposes) run on
+                       the bulk stream beside the input gradient; 0: in the
+                       compute stream's order, before it */
+  int dx_dtype;     /* CM_F32 or CM_BF16: the input gradient */
+  int dw_dtype;     /* CM_F32 or CM_BF16: the weight gradient */
+  int exec_mode;    /* cm_exec_mode */
+  int copy_engine;  /* cm_copy_engine */
+} cm_bwd_desc;
+
+typedef struct {
+  cm_bwd_desc desc;
+  cm_plan dgrad;    /* COL: GEMM -> ReduceScatter (k' = n, n' = k, add-and-forward
+                       hops on a ring); ROW: AllGather -> GEMM (k' = n, n' = k) */
+  cm_plan gather;   /* the bulk AllGather (COL: of x, rows of k; ROW: of dOut, rows of n) */
+  size_t off_wt;    /* workspace: W_r^T [N][k][n] (made unless the caller passes it) */
+  size_t off_g;     /* the gathered operand [N][T][k or n] */
+  size_t off_gt;    /* its transpose [N][k or n][Tp], Tp = T rounded up to 64 (zero padded) */
+  size_t off_ot;    /* COL: dY_r^T [N][n][Tp]; ROW: H_r^T [N][k][Tp] */
+  size_t off_ops;   /* the input gradient's workspace */
+  size_t ws_bytes;
+} cm_bwd_plan;
+
+/* Plan a backward.  Host only.  Errors: those of cm_ring_plan for the input
+ * gradient's collective matmul and for the AllGather, CM_ERR_INVALID_ARG,
+ * CM_ERR_UNSUPPORTED (gradient dtypes), CM_ERR_SHAPE. */
+cm_status cm_plan_backward(const cm_bwd_desc *desc, cm_bwd_plan *out);
+
+/*
+ * The backward (all inputs bf16, rank r = block r):
+ *   COL: act = x [N][m][k], grad = dY [N][T][n] -> dact = dX [N][m][k]
+ *   ROW: act = H [N][T][k], grad = dOut [N][m][n] -> dact = dH [N][T][k]
+ *   w [N][n][k] the forward weights; wt [N][k][n] their transpose or NULL (then
+ *   the call transposes w into the workspace); dw [N][n][k] (desc.dw_dtype).
+ * comm: the plan's n_comm streams for the input gradient's hops, then the bulk
+ * stream, then the bulk AllGather's copy lane (n_comm + 2 distinct streams).
+ * The call orders everything against `compute`: the bulk stream starts after
+ * the work already on `compute`, and the weight gradient waits for the bulk
+ * stream.  Asynchronous; errors as for cm_ag_gemm.
+ */
+cm_status cm_linear_backward(const cm_bwd_plan *plan, const void *act, const void *w, const void *wt,
+                             const void *grad, void *dact, void *dw, void *ws, size_t ws_bytes, void *compute,
+                             void *const *comm, int n_comm);
 
 const char *cm_status_string(cm_status s);
 /* Detail of the last failing call on this thread ("" if none). */

@@ -358,3 +358,42 @@ def row_backward(h, w, dout, with_mag=False, lib=None):
     mw = np.empty_like(dw) if with_mag else None
     lib.orc_row_backward(N, m, k, n, h, w, dout, dh, dw, _ptr(mh), _ptr(mw))
     return (dh, dw, mh, mw) if with_mag else (dh, dw)
+
+
+def col_backward_rows(x, w, dy, dx_owners, dx_rows, dw_ranks, dw_rows, lib=None):
+    """Sampled column-parallel backward: dX_q rows (owner q, row i) through
+    the duality dX = GEMM->ReduceScatter(dY, W^T) (gemm_rs_rows), and dW_r
+    rows f = dY_r[:, f]^T . Xfull (numpy float64).  Returns (dx [s, k], dx_mag,
+    dw [s', k], dw_mag)."""
+    x, w, dy = _u16(x), _u16(w), _u16(dy)
+    N, m, k = x.shape
+    wt = np.ascontiguousarray(np.transpose(w, (0, 2, 1)))
+    dx, dx_mag = gemm_rs_rows(dy, wt, dx_owners, dx_rows, with_mag=True, lib=lib)
+    X = bf16_to_f64(x).reshape(N * m, k)
+    dw = np.empty((len(dw_rows), k))
+    dw_mag = np.empty_like(dw)
+    for s, (r, f) in enumerate(zip(dw_ranks, dw_rows)):
+        g = bf16_to_f64(dy[r][:, f])
+        dw[s] = g @ X
+        dw_mag[s] = np.abs(g) @ np.abs(X)
+    return dx, dx_mag, dw, dw_mag
+
+
+def row_backward_rows(h, w, dout, dh_ranks, dh_rows, dw_ranks, dw_rows, lib=None):
+    """Sampled row-parallel backward: dH_r rows t through the duality
+    dH = AllGather->GEMM(dOut, W^T) (ag_gemm_rows), and dW_r rows j =
+    dOutfull[:, j]^T . H_r (numpy float64).  Returns (dh [s, k], dh_mag,
+    dw [s', k], dw_mag)."""
+    h, w, dout = _u16(h), _u16(w), _u16(dout)
+    N, T, k = h.shape
+    n = w.shape[1]
+    wt = np.ascontiguousarray(np.transpose(w, (0, 2, 1)))
+    dh, dh_mag = ag_gemm_rows(dout, wt, dh_ranks, dh_rows, with_mag=True, lib=lib)
+    G = bf16_to_f64(dout).reshape(T, n)
+    dw = np.empty((len(dw_rows), k))
+    dw_mag = np.empty_like(dw)
+    for s, (r, j) in enumerate(zip(dw_ranks, dw_rows)):
+        Hr = bf16_to_f64(h[r])
+        dw[s] = G[:, j] @ Hr
+        dw_mag[s] = np.abs(G[:, j]) @ np.abs(Hr)
+    return dh, dh_mag, dw, dw_mag

@@ -232,6 +232,8 @@ def buffer_sizes(plan):
     N, m, k, n = d.n_ranks, d.m, d.k, d.n
     T = N * m
     osz = 4 if d.out_dtype == nat.CM_F32 else 2
+    if d.op == nat.CM_OP_ALLGATHER:
+        return [N * m * k * 2, 0, N * T * k * 2, plan.ws_bytes]
     if d.op == nat.CM_OP_AG_GEMM:
         return [N * m * k * 2, N * n * k * 2, N * T * n * osz, plan.ws_bytes]
     return [N * T * k * 2, N * n * k * 2, N * m * n * osz, plan.ws_bytes]

@@ -34,8 +34,9 @@ def test_struct_sizes_match_the_header():
 #include <stdio.h>
 #include "collmm.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu\n", sizeof(cm_plan_desc), sizeof(cm_plan), sizeof(cm_op_rec), sizeof(cm_job_rec),
-         sizeof(cm_span), sizeof(cm_layer_desc), sizeof(cm_layer_plan));
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(cm_plan_desc), sizeof(cm_plan), sizeof(cm_op_rec),
+         sizeof(cm_job_rec), sizeof(cm_span), sizeof(cm_layer_desc), sizeof(cm_layer_plan), sizeof(cm_bwd_desc),
+         sizeof(cm_bwd_plan));
   return 0;
 }
 '''
@@ -47,7 +48,7 @@ int main(void) {
         sizes = [int(v) for v in subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()]
     assert sizes == [ctypes.sizeof(nat.cm_plan_desc), ctypes.sizeof(nat.cm_plan), ctypes.sizeof(nat.cm_op_rec),
                      ctypes.sizeof(nat.cm_job_rec), ctypes.sizeof(nat.cm_span), ctypes.sizeof(nat.cm_layer_desc),
-                     ctypes.sizeof(nat.cm_layer_plan)]
+                     ctypes.sizeof(nat.cm_layer_plan), ctypes.sizeof(nat.cm_bwd_desc), ctypes.sizeof(nat.cm_bwd_plan)]
 
 
 def status_of(**kw):

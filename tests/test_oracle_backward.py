@@ -127,3 +127,18 @@ def test_backward_planted_mistake_is_caught(name, tmp_path):
         except (AssertionError, IndexError, ValueError):
             failed.append(check.__name__)
     assert failed, "planted mistake %r passed every pin" % name
+
+
+def test_sampled_backward_equals_full():
+    x, w, dy = gen.backward_inputs("col", 3, 5, 64, 128, "normal", 11)
+    dx, dw, mx, mw = oracle.col_backward(x, w, dy, with_mag=True)
+    qo, qr, wr, wf = np.array([0, 2, 1]), np.array([4, 0, 2]), np.array([2, 0]), np.array([127, 3])
+    sx, smx, sw, smw = oracle.col_backward_rows(x, w, dy, qo, qr, wr, wf)
+    assert np.allclose(sx, dx[qo, qr], rtol=1e-12, atol=1e-12) and np.allclose(smx, mx[qo, qr], rtol=1e-12)
+    assert np.allclose(sw, dw[wr, wf], rtol=1e-12, atol=1e-12) and np.allclose(smw, mw[wr, wf], rtol=1e-12)
+    h, w, dout = gen.backward_inputs("row", 3, 5, 64, 128, "normal", 12)
+    dh, dw, mh, mw = oracle.row_backward(h, w, dout, with_mag=True)
+    hr, ht = np.array([1, 0, 2]), np.array([14, 0, 7])
+    sh, smh, sw, smw = oracle.row_backward_rows(h, w, dout, hr, ht, wr, wf)
+    assert np.allclose(sh, dh[hr, ht], rtol=1e-12, atol=1e-12) and np.allclose(smh, mh[hr, ht], rtol=1e-12)
+    assert np.allclose(sw, dw[wr, wf], rtol=1e-12, atol=1e-12) and np.allclose(smw, mw[wr, wf], rtol=1e-12)
