@@ -437,6 +437,60 @@ def measure_layer(args, steps, warmup):
     return res
 
 
+def measure_backward(args, workload, steps, warmup):
+    """The backward of the workload's two linears (fc1: column-parallel, the
+    forward was AllGather->GEMM; fc2: row-parallel, the forward was
+    GEMM->ReduceScatter), bf16 gradients: wall time per call with the weight
+    gradient's AllGather on the bulk stream (bulk overlap) and in the serial
+    order, and with the transposed weights passed in."""
+    import torch
+    from collective_matmul_decomposition_amd import _native as nat
+    from collective_matmul_decomposition_amd import buffers
+    from collective_matmul_decomposition_amd import inputs as gen
+    wl = WORKLOADS[workload]
+    N, T, d, f = wl["N"], wl["T"], wl["d"], wl["f"]
+    m, fN = T // N, f // N
+    compute = torch.cuda.Stream()
+    compute.wait_stream(torch.cuda.current_stream())
+    comm = buffers.comm_streams(3)
+    out = {"workload": workload}
+    for kind, k, n in (("col", d, fN), ("row", fN, d)):
+        act, w, grad = gen.backward_inputs_torch(kind, N, m, k, n, "normal", 0, "cuda")
+        wt = w.transpose(1, 2).contiguous()
+        dact = torch.empty((N, m, k) if kind == "col" else (N, T, k), dtype=torch.bfloat16, device="cuda")
+        dw = torch.empty((N, n, k), dtype=torch.bfloat16, device="cuda")
+        flops = 2 * 2.0 * N * T * n * k  # input gradient + weight gradient
+        r = {}
+        for label, bulk, wtp in (("bulk", True, None), ("serial", False, None), ("bulk_wt_given", True, wt)):
+            plan = nat.cm_plan_backward(kind=kind, n_ranks=N, m=m, k=k, n=n, chunks=1, n_comm=1, bulk=bulk,
+                                        dx_dtype="bf16", dw_dtype="bf16", copy_engine=args.copy_engine)
+            ws = torch.empty(plan.ws_bytes, dtype=torch.uint8, device="cuda")
+            call = lambda: nat.cm_linear_backward(plan, act, w, wtp, grad, dact, dw, ws, compute, comm)
+            for _ in range(warmup):
+                call()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                call()
+            torch.cuda.synchronize()
+            us = (time.perf_counter() - t0) / steps * 1e6
+            r[label + "_us"] = round(us, 1)
+            if label == "bulk":
+                r["tflops"] = round(flops / (us * 1e-6) / 1e12, 1)
+            del ws
+        r["bulk_speedup_over_serial"] = round(r["serial_us"] / r["bulk_us"], 3)
+        r["flops"] = flops
+        out["fc1_col" if kind == "col" else "fc2_row"] = r
+        log("backward %s: bulk %.0f us (%.0f TFLOP/s), serial %.0f us, W^T given %.0f us" % (
+            kind, r["bulk_us"], r["tflops"], r["serial_us"], r["bulk_wt_given_us"]))
+        del act, w, grad, wt, dact, dw
+        torch.cuda.empty_cache()
+    tot = out["fc1_col"]["bulk_us"] + out["fc2_row"]["bulk_us"]
+    out["mlp_backward_ms"] = round(tot / 1e3, 4)
+    out["mlp_backward_tflops"] = round((out["fc1_col"]["flops"] + out["fc2_row"]["flops"]) / (tot * 1e-6) / 1e12, 1)
+    return out
+
+
 def sampled_parity(res, rs_bucket="f32"):
     import oracle
     from collective_matmul_decomposition_amd import inputs as gen
@@ -512,6 +566,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
     ap.add_argument("--no-naive", action="store_true")
     ap.add_argument("--no-layer", action="store_true", help="skip the sequence-parallel layer forward")
+    ap.add_argument("--no-backward", action="store_true", help="skip the MLP backward (bulk overlap)")
     ap.add_argument("--no-trace", action="store_true", help="time without the per-launch events")
     ap.add_argument("--sweep", choices=["c4", "c5"], help="instead of the step: the small-chunk grid (c4) or the "
                     "layer's GEMM + collective pairs (c5), one JSON line per case")
@@ -590,6 +645,7 @@ def main():
                      "roofline": s2.get("roofline"), "overlap": s2.get("overlap"), "naive": s2.get("naive")}
 
     layer = None if args.no_layer else measure_layer(args, max(5, args.steps // 2), 2)
+    backward = None if args.no_backward else measure_backward(args, args.workload, max(5, args.steps // 2), 2)
 
     out = {
         "metric": "AG-GEMM / GEMM-RS TFLOP/s + % bf16 MFMA peak + overlap efficiency, 1 GPU",
@@ -625,6 +681,7 @@ def main():
         "step_launches": res.get("step_launches"),
         "secondary": secondary,
         "layer": layer,
+        "backward": backward,
     }
     print(json.dumps(out), flush=True)
 
