@@ -597,9 +597,12 @@ def main():
         # kernel that reads it once (and writes half as many bytes)
         nbytes = args.calib_copy_mib << 20
         a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        # a second fill of the same size evicts `a` from the last-level cache,
+        # so the copy below reads all of it from HBM
+        flush = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(2.0)
         b = a.to(torch.bfloat16)
         torch.cuda.synchronize()
-        del a, b
+        del a, b, flush
     res = measure(args, args.workload, args.steps, args.warmup, not args.no_naive, not args.no_trace)
     parity, arrays = sampled_parity(res, args.rs_bucket if args.rs_op == "rs" else "f32")
     cpu = None if args.no_cpu_baseline else cpu_baseline(res, arrays, args.cpu_seconds)
