@@ -53,7 +53,10 @@ __device__ __forceinline__ float bits_to_f32(uint32_t b16) { return __uint_as_fl
 // Within a 16-key MFMA step lane group g supplies keys {4g..4g+3, 8+4g..8+4g+3}
 // of P and of V^T alike; the contraction only needs the two operands to agree.
 // The probabilities' bf16 values feed both the numerator and the running sum,
-// so every output row is a convex combination of the value rows.
+// so every output row is a convex combination of the value rows.  The kernel
+// is held to two waves per SIMD (accumulators in VGPRs, no AGPR moves); blocks
+// entirely below the causal diagonal skip the mask, and the rescale of the
+// output is skipped when no lane's running maximum moved.
 constexpr int kAttnD = 128;   // head dimension
 constexpr int kAttnBQ = 128;  // query rows per workgroup
 constexpr int kAttnBK = 64;   // keys per block
@@ -77,7 +80,44 @@ __device__ __forceinline__ int attn_logical_block() {
   return b < per * 8 ? (b & 7) * per + (b >> 3) : b;
 }
 
-__global__ __launch_bounds__(256) void attn_fwd_kernel(const AttnParams p) {
+// One block of keys and values, staged through registers: K rows whole (1024
+// chunks of 16 bytes, 4 per thread), V as 4 keys x 8 dims per thread.
+__device__ __forceinline__ void attn_load_kv(const uint16_t *base, int ld, int kcol, int vcol, int T, int k0,
+                                             int tid, uint4 (&kr)[4], uint4 (&vr)[4]) {
+  const int dg = tid & 15, kgp = tid >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int key = (tid + 256 * i) >> 4, ch = (tid + 256 * i) & 15;
+    kr[i] = *reinterpret_cast<const uint4 *>(base + (size_t)min(k0 + key, T - 1) * ld + kcol + 8 * ch);
+    vr[i] = *reinterpret_cast<const uint4 *>(base + (size_t)min(k0 + 4 * kgp + i, T - 1) * ld + vcol + 8 * dg);
+  }
+}
+
+// K into its swizzled LDS rows; V transposed into V^T units of 4 keys.
+__device__ __forceinline__ void attn_store_kv(char *sK, char *sV, int tid, const uint4 (&kr)[4], const uint4 (&vr)[4]) {
+  const int dg = tid & 15, kgp = tid >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int key = (tid + 256 * i) >> 4, ch = (tid + 256 * i) & 15;
+    *reinterpret_cast<uint4 *>(sK + key * 256 + ((ch ^ (key & 15)) << 4)) = kr[i];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int sh = (e & 1) * 16;
+    auto word = [&](int i) -> uint32_t {
+      const uint4 &v = vr[i];
+      const uint32_t w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
+      return (w >> sh) & 0xFFFFu;
+    };
+    uint2 pk;
+    pk.x = word(0) | (word(1) << 16);
+    pk.y = word(2) | (word(3) << 16);
+    const int dim = 8 * dg + e;
+    *reinterpret_cast<uint2 *>(sV + dim * 128 + ((kgp ^ ((dim >> 1) & 15)) << 3)) = pk;
+  }
+}
+
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
   // K block [64 keys][128 dims]: 256-byte rows of 16 chunks of 16 bytes,
   // chunk c of key row r stored at position c ^ (r % 16).
   __shared__ __attribute__((aligned(16))) char sK[kAttnBK * kAttnD * 2];
@@ -115,37 +155,15 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const AttnParams p) {
 
   const int kv_end = p.causal ? min(p.T, (qb + 1) * kAttnBQ) : p.T;
   const int nblk = (kv_end + kAttnBK - 1) / kAttnBK;
-  const int dg = tid & 15, kgp = tid >> 4;  // V staging: dims 8 dg .. 8 dg + 7 of keys 4 kgp .. 4 kgp + 3
 
+  // (loading the next block into registers during this block's MFMAs was
+  // measured slower: the extra registers cost more than the hidden latency)
+  uint4 kreg[4], vreg[4];
   for (int j = 0; j < nblk; ++j) {
     const int k0 = j * kAttnBK;
     __syncthreads();  // every wave is done with the previous block
-    // K block: 1024 chunks of 16 bytes, 4 per thread, rows read whole
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i, key = c >> 4, ch = c & 15;
-      const uint4 v = *reinterpret_cast<const uint4 *>(base + (size_t)min(k0 + key, p.T - 1) * p.ld_qkv + kcol + 8 * ch);
-      *reinterpret_cast<uint4 *>(sK + key * 256 + ((ch ^ (key & 15)) << 4)) = v;
-    }
-    // V block, transposed: this thread's 4 keys x 8 dims
-    {
-      uint32_t w[4][4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 v =
-            *reinterpret_cast<const uint4 *>(base + (size_t)min(k0 + 4 * kgp + i, p.T - 1) * p.ld_qkv + vcol + 8 * dg);
-        w[i][0] = v.x; w[i][1] = v.y; w[i][2] = v.z; w[i][3] = v.w;
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sh = (e & 1) * 16;
-        uint2 pk;
-        pk.x = ((w[0][e >> 1] >> sh) & 0xFFFFu) | (((w[1][e >> 1] >> sh) & 0xFFFFu) << 16);
-        pk.y = ((w[2][e >> 1] >> sh) & 0xFFFFu) | (((w[3][e >> 1] >> sh) & 0xFFFFu) << 16);
-        const int dim = 8 * dg + e;
-        *reinterpret_cast<uint2 *>(sV + dim * 128 + ((kgp ^ ((dim >> 1) & 15)) << 3)) = pk;
-      }
-    }
+    attn_load_kv(base, p.ld_qkv, kcol, vcol, p.T, k0, tid, kreg, vreg);
+    attn_store_kv(sK, sV, tid, kreg, vreg);
     __syncthreads();
     if (p.causal && k0 > q0 + 31) continue;  // every key of the block is after every query of the wave
 
@@ -165,14 +183,18 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const AttnParams p) {
       }
     }
     // online softmax: element e of tile t is key k0 + 32 t + 8 (e / 4) + 4 g + e % 4
+    // the mask is needed only where a key can lie after a query of the wave or past the sequence
+    const bool masked = (p.causal && k0 + kAttnBK - 1 > q0) || k0 + kAttnBK > p.T;
     float mloc = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int key = k0 + t * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
-        const bool ok = key < p.T && (!p.causal || key <= my_q);
-        const float v = ok ? s[t][e] * p.scale_log2 : -INFINITY;
+        float v = s[t][e] * p.scale_log2;
+        if (masked) {
+          const int key = k0 + t * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+          if (key >= p.T || (p.causal && key > my_q)) v = -INFINITY;
+        }
         s[t][e] = v;
         mloc = fmaxf(mloc, v);
       }
@@ -186,17 +208,19 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const AttnParams p) {
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const uint32_t b = bf16_bits_rne(exp2f(s[t][e] - msub));
-        lsum += bits_to_f32(b);
-        pf[t][e >> 3][e & 7] = __builtin_bit_cast(__bf16, (uint16_t)b);
+        const __bf16 pb = (__bf16)exp2f(s[t][e] - msub);  // nearest even
+        lsum += (float)pb;
+        pf[t][e >> 3][e & 7] = pb;
       }
     lsum += __shfl_xor(lsum, 32);
     l_run = l_run * alpha + lsum;
     m_run = m_new;
+    if (__any(alpha != 1.f)) {  // no lane's running maximum moved: nothing to rescale
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
+        for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
+    }
 
     // O^T += V^T P^T over the block's 64 keys (four 16-key steps)
 #pragma unroll
@@ -219,15 +243,16 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const AttnParams p) {
   if (my_q >= p.T) return;
   const float inv = 1.f / l_run;
   uint16_t *orow = p.o + ((size_t)rank * p.T + my_q) * p.ld_o + head * kAttnD;
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int eg = 0; eg < 4; ++eg) {
-      // elements 4 eg .. 4 eg + 3: dims 32 dt + 8 eg + 4 g .. +3
-      uint2 pk;
-      pk.x = bf16_bits_rne(oacc[dt][4 * eg + 0] * inv) | (bf16_bits_rne(oacc[dt][4 * eg + 1] * inv) << 16);
-      pk.y = bf16_bits_rne(oacc[dt][4 * eg + 2] * inv) | (bf16_bits_rne(oacc[dt][4 * eg + 3] * inv) << 16);
-      *reinterpret_cast<uint2 *>(orow + dt * 32 + 8 * eg + 4 * g) = pk;
+      // elements 4 eg .. 4 eg + 3: dims 32 dt + 8 eg + 4 g .. +3, rounded to nearest even
+      bf16x4 o4;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o4[q] = (__bf16)(oacc[dt][4 * eg + q] * inv);
+      *reinterpret_cast<bf16x4 *>(orow + dt * 32 + 8 * eg + 4 * g) = o4;
     }
 }
 
