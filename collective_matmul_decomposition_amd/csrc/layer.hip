@@ -59,7 +59,8 @@ __device__ __forceinline__ float bits_to_f32(uint32_t b16) { return __uint_as_fl
 // output is skipped when no lane's running maximum moved.
 constexpr int kAttnD = 128;   // head dimension
 constexpr int kAttnBQ = 128;  // query rows per workgroup
-constexpr int kAttnBK = 64;   // keys per block
+constexpr int kAttnBK = 64;   // keys per block (one softmax update)
+constexpr int kAttnSub = 2;   // blocks staged through LDS per pair of barriers
 
 struct AttnParams {
   const uint16_t *qkv;  // [N][T][3*H*D]
@@ -120,10 +121,10 @@ __device__ __forceinline__ void attn_store_kv(char *sK, char *sV, int tid, const
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
   // K block [64 keys][128 dims]: 256-byte rows of 16 chunks of 16 bytes,
   // chunk c of key row r stored at position c ^ (r % 16).
-  __shared__ __attribute__((aligned(16))) char sK[kAttnBK * kAttnD * 2];
+  __shared__ __attribute__((aligned(16))) char sK[kAttnSub * kAttnBK * kAttnD * 2];
   // V^T block [128 dims][64 keys]: 128-byte rows of 16 units of 4 keys,
   // unit u of dim row r stored at position u ^ ((r / 2) % 16).
-  __shared__ __attribute__((aligned(16))) char sV[kAttnD * kAttnBK * 2];
+  __shared__ __attribute__((aligned(16))) char sV[kAttnSub * kAttnD * kAttnBK * 2];
 
   const int lb = attn_logical_block();
   const int bh = lb / p.qblocks;
@@ -159,13 +160,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
   // (loading the next block into registers during this block's MFMAs was
   // measured slower: the extra registers cost more than the hidden latency)
   uint4 kreg[4], vreg[4];
-  for (int j = 0; j < nblk; ++j) {
-    const int k0 = j * kAttnBK;
-    __syncthreads();  // every wave is done with the previous block
-    attn_load_kv(base, p.ld_qkv, kcol, vcol, p.T, k0, tid, kreg, vreg);
-    attn_store_kv(sK, sV, tid, kreg, vreg);
+  for (int jj = 0; jj < nblk; jj += kAttnSub) {
+    __syncthreads();  // every wave is done with the previous blocks
+#pragma unroll
+    for (int sb = 0; sb < kAttnSub; ++sb) {
+      if (jj + sb < nblk) {
+        attn_load_kv(base, p.ld_qkv, kcol, vcol, p.T, (jj + sb) * kAttnBK, tid, kreg, vreg);
+        attn_store_kv(sK + sb * kAttnBK * 256, sV + sb * kAttnD * kAttnBK * 2, tid, kreg, vreg);
+      }
+    }
     __syncthreads();
-    if (p.causal && k0 > q0 + 31) continue;  // every key of the block is after every query of the wave
+#pragma unroll
+  for (int sb = 0; sb < kAttnSub; ++sb) {
+    const int j = jj + sb;
+    const int k0 = j * kAttnBK;
+    if (j >= nblk || (p.causal && k0 > q0 + 31)) break;  // every later key is after every query of the wave
+    const char *sKb = sK + sb * kAttnBK * 256;
+    const char *sVb = sV + sb * kAttnD * kAttnBK * 2;
 
     // S^T = K Q^T for keys k0 .. k0 + 63 (two 32-key tiles)
     f32x16 s[2];
@@ -178,7 +189,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int key = t * 32 + l32, ch = 2 * ks + g;
-        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(sK + key * 256 + ((ch ^ (key & 15)) << 4));
+        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(sKb + key * 256 + ((ch ^ (key & 15)) << 4));
         s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[t], 0, 0, 0);
       }
     }
@@ -231,13 +242,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
           const int dim = dt * 32 + l32, sw = (dim >> 1) & 15;
-          const uint2 lo = *reinterpret_cast<const uint2 *>(sV + dim * 128 + ((u0 ^ sw) << 3));
-          const uint2 hi = *reinterpret_cast<const uint2 *>(sV + dim * 128 + (((u0 + 2) ^ sw) << 3));
+          const uint2 lo = *reinterpret_cast<const uint2 *>(sVb + dim * 128 + ((u0 ^ sw) << 3));
+          const uint2 hi = *reinterpret_cast<const uint2 *>(sVb + dim * 128 + (((u0 + 2) ^ sw) << 3));
           const uint4 both = make_uint4(lo.x, lo.y, hi.x, hi.y);
           const bf16x8 vf = __builtin_bit_cast(bf16x8, both);
           oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t][h], oacc[dt], 0, 0, 0);
         }
       }
+  }
   }
 
   if (my_q >= p.T) return;
