@@ -38,7 +38,8 @@ class cm_plan_desc(ctypes.Structure):
                 ("tile_m", ctypes.c_int), ("tile_n", ctypes.c_int), ("exec_mode", ctypes.c_int),
                 ("copy_engine", ctypes.c_int), ("bucket_bf16", ctypes.c_int), ("hop_add", ctypes.c_int),
                 ("copy_gbps", ctypes.c_double),
-                ("mfma_tflops", ctypes.c_double), ("launch_us", ctypes.c_double), ("act", ctypes.c_int)]
+                ("mfma_tflops", ctypes.c_double), ("launch_us", ctypes.c_double), ("act", ctypes.c_int),
+                ("share", ctypes.c_int), ("split_k", ctypes.c_int)]
 
 
 class cm_plan(ctypes.Structure):
@@ -47,7 +48,7 @@ class cm_plan(ctypes.Structure):
                 ("tile_n", ctypes.c_int), ("declined", ctypes.c_int), ("n_ops", ctypes.c_int),
                 ("n_jobs", ctypes.c_int), ("n_events", ctypes.c_int), ("ws_bytes", ctypes.c_size_t),
                 ("est_gemm_us", ctypes.c_double), ("est_hop_us", ctypes.c_double),
-                ("est_total_us", ctypes.c_double)]
+                ("est_total_us", ctypes.c_double), ("split", ctypes.c_int)]
 
 
 class cm_op_rec(ctypes.Structure):
@@ -184,8 +185,9 @@ _ENUMS = {
 
 def make_desc(op, n_ranks, m, k, n, dir="uni", chunks=0, sched="decomposed", out_dtype="bf16", n_comm=1,
               tile=(0, 0), exec_mode="graph", copy_engine="sdma", bucket="f32", hop="copy", copy_gbps=0.0,
-              mfma_tflops=0.0, launch_us=0.0, act="none"):
-    """A cm_plan_desc from keyword arguments (strings or enum values)."""
+              mfma_tflops=0.0, launch_us=0.0, act="none", share=0, split_k=0):
+    """A cm_plan_desc from keyword arguments (strings or enum values).  share=1:
+    one rank's share (virtual rank 0's steps at real shape, split-K GEMMs)."""
     def e(kind, v):
         return _ENUMS[kind][v] if isinstance(v, str) else int(v)
     return cm_plan_desc(op=e("op", op), n_ranks=n_ranks, m=m, k=k, n=n, dir=e("dir", dir), chunks=chunks,
@@ -193,7 +195,8 @@ def make_desc(op, n_ranks, m, k, n, dir="uni", chunks=0, sched="decomposed", out
                         n_comm=n_comm, tile_m=tile[0], tile_n=tile[1], exec_mode=e("exec", exec_mode),
                         copy_engine=e("copy", copy_engine), bucket_bf16=1 if bucket == "bf16" else 0,
                         hop_add=e("hop", hop), copy_gbps=copy_gbps,
-                        mfma_tflops=mfma_tflops, launch_us=launch_us, act=e("act", act))
+                        mfma_tflops=mfma_tflops, launch_us=launch_us, act=e("act", act), share=int(share),
+                        split_k=int(split_k))
 
 
 def cm_ring_plan(desc=None, **kw):

@@ -3,6 +3,9 @@
 Sizes follow the layouts of include/collmm.h:
     AllGather->GEMM   x [N, m, k] bf16, w [N, n, k] bf16, y [N, N*m, n]
     GEMM->ReduceScatter x [N, N*m, k] bf16, w [N, n, k] bf16, y [N, m, n]
+and for one rank's share (plan.desc.share = 1) rank 0's blocks:
+    AllGather->GEMM   x [N, m, k] (all shards), w [1, n, k], y [1, N*m, n]
+    GEMM->ReduceScatter x [1, N*m, k], w [1, n, k], y [1, m, n]
 plus the plan's workspace (plan.ws_bytes, at least one byte so it has an
 address).
 """
@@ -13,9 +16,10 @@ def shapes(plan):
     d = plan.desc
     N, m, k, n = d.n_ranks, d.m, d.k, d.n
     T = N * m
+    R = 1 if d.share else N  # ranks whose weights and outputs the call touches
     if d.op == nat.CM_OP_AG_GEMM:
-        return {"x": (N, m, k), "w": (N, n, k), "y": (N, T, n)}
-    return {"x": (N, T, k), "w": (N, n, k), "y": (N, m, n)}
+        return {"x": (N, m, k), "w": (R, n, k), "y": (R, T, n)}
+    return {"x": (R, T, k), "w": (R, n, k), "y": (R, m, n)}
 
 
 def alloc_outputs(plan, device="cuda"):

@@ -54,10 +54,12 @@ std::string plan_key(const cm_plan &p) {
   // Every field the program depends on (struct padding is not part of it).
   const cm_plan_desc &d = p.desc;
   char buf[512];
-  std::snprintf(buf, sizeof buf, "%d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %a %a %a %d|%d %d %d %d %d %d %d %zu",
+  std::snprintf(buf, sizeof buf,
+                "%d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %a %a %a %d %d %d|%d %d %d %d %d %d %d %zu %d",
                 d.op, d.n_ranks, d.m, d.k, d.n, d.dir, d.chunks, d.sched, d.in_dtype, d.out_dtype, d.n_comm, d.tile_m,
                 d.tile_n, d.exec_mode, d.copy_engine, d.bucket_bf16, d.hop_add, d.copy_gbps, d.mfma_tflops,
-                d.launch_us, d.act, p.chunks, p.n_steps, p.arc_cw, p.arc_ccw, p.tile_m, p.tile_n, p.n_events, p.ws_bytes);
+                d.launch_us, d.act, d.share, d.split_k, p.chunks, p.n_steps, p.arc_cw, p.arc_ccw, p.tile_m, p.tile_n,
+                p.n_events, p.ws_bytes, p.split);
   return buf;
 }
 
@@ -71,7 +73,7 @@ cm_status canonical_plan(const cm_plan &pl, cm_plan *canon) {
   if (canon->chunks != pl.chunks || canon->n_steps != pl.n_steps || canon->arc_cw != pl.arc_cw ||
       canon->arc_ccw != pl.arc_ccw || canon->tile_m != pl.tile_m || canon->tile_n != pl.tile_n ||
       canon->ws_bytes != pl.ws_bytes || canon->n_ops != pl.n_ops || canon->n_jobs != pl.n_jobs ||
-      canon->n_events != pl.n_events || canon->desc.dir != pl.desc.dir) {
+      canon->n_events != pl.n_events || canon->desc.dir != pl.desc.dir || canon->split != pl.split) {
     set_error("plan does not match what cm_ring_plan produces for its request");
     return CM_ERR_INVALID_ARG;
   }
@@ -134,7 +136,7 @@ cm_status fill_params(const cm_op_rec &o, const cm_job_rec *jobs, Launch &L) {
       ok &= j.in1_buf == CM_BUF_WS && off16(j.in1_off, &p.in1_off[i]);
       sel |= 1u << 7;
     }
-    if (o.kind == CM_OPK_REDUCE) ok &= j.in0_buf >= 0 && j.in1_buf >= 0;
+    if (o.kind == CM_OPK_REDUCE) ok &= j.in0_buf >= 0 && (j.in1_buf >= 0 || o.depth >= 1);
     if (!ok) {
       set_error("job %d of a launch has an unaligned, out-of-range or missing operand", i);
       return CM_ERR_SHAPE;
@@ -159,6 +161,15 @@ cm_status fill_params(const cm_op_rec &o, const cm_job_rec *jobs, Launch &L) {
       set_error("reduce columns must be multiples of 4");
       return CM_ERR_SHAPE;
     }
+    if (o.depth < 0 || o.depth > 64) {
+      set_error("a reduce sums 1..64 blocks (got %d)", o.depth);
+      return CM_ERR_SHAPE;
+    }
+    if (o.act != CM_ACT_NONE && o.act != CM_ACT_GELU) {
+      set_error("unknown activation %d", o.act);
+      return CM_ERR_UNSUPPORTED;
+    }
+    p.act = o.act;
   }
   p.add_bf16 = add_dtype == CM_BF16;
   if (o.kind == CM_OPK_GEMM && o.act != CM_ACT_NONE) {

@@ -12,7 +12,9 @@
 //    buckets with rounding to the output type (the realigning addition of
 //    the bidirectional ring).
 //  * reduce_jobs: C = in0 + in1 elementwise (the add of the pipeline-chunk
-//    ReduceScatter ring), fp32 in, fp32 or bf16 out.
+//    ReduceScatter ring and of the add-and-forward hops), or the sum of S
+//    fp32 blocks (+ in1, then optionally GELU): the split-K partials of one
+//    rank's step GEMM; fp32 in, fp32 or bf16 out.
 //
 // Block tile BM x BN x 64, 512 threads = 8 waves; operands are staged
 // through two LDS buffers by direct-to-LDS loads (the next K-slab is in
@@ -449,27 +451,45 @@ __global__ __launch_bounds__(64 * (WM * WN) + 64 * NL) void gemm_jobs_kernel(con
     epilogue_mode<TM, TN, false>(acc, ea, mode);
 }
 
-// C = in0 + in1 over rows x cols per job; 4 columns per thread.
+// C = act(B_0 + B_1 + ... + B_{S-1} (+ in1)) over rows x cols per job, added
+// in that order in fp32, where B_s is the fp32 block of rows x ld_in at
+// in0 + s * rows * ld_in and S = max(1, K); 4 columns per thread.  PAIR: the
+// launch is C = in0 + in1 for every job (S = 1, in1 present, no activation):
+// the ring's add-and-forward, in its own instantiation.
+template <bool PAIR>
 __global__ __launch_bounds__(256) void reduce_jobs_kernel(const GemmParams p) {
   const int job = blockIdx.y;
   const uint32_t sel = p.sel[job];
   const float *In0 = reinterpret_cast<const float *>(p.base[3] + (size_t)p.in0_off[job] * 16);
   const float *In1 = reinterpret_cast<const float *>(p.base[3] + (size_t)p.in1_off[job] * 16);
   char *Cbase = p.base[(sel >> 4) & 3] + (size_t)p.c_off[job] * 16;
+  const bool has1 = PAIR || ((sel >> 7) & 1);
+  const int S = PAIR ? 1 : (p.K > 1 ? p.K : 1);
+  const size_t bstride = (size_t)p.M * p.ld_in;
   const int cols4 = p.N >> 2;
   const long total = (long)p.M * cols4;
   for (long t = (long)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (long)gridDim.x * blockDim.x) {
     const int row = (int)(t / cols4), c4 = (int)(t - (long)row * cols4) * 4;
-    const float4 a = *reinterpret_cast<const float4 *>(In0 + (size_t)row * p.ld_in + c4);
-    const float4 b = *reinterpret_cast<const float4 *>(In1 + (size_t)row * p.ld_in + c4);
-    const float4 s = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+    const size_t ii = (size_t)row * p.ld_in + c4;
+    float4 v = *reinterpret_cast<const float4 *>(In0 + ii);
+    if (!PAIR) {
+      for (int b = 1; b < S; ++b) {
+        const float4 a = *reinterpret_cast<const float4 *>(In0 + (size_t)b * bstride + ii);
+        v = make_float4(v.x + a.x, v.y + a.y, v.z + a.z, v.w + a.w);
+      }
+    }
+    if (has1) {
+      const float4 a = *reinterpret_cast<const float4 *>(In1 + ii);
+      v = make_float4(v.x + a.x, v.y + a.y, v.z + a.z, v.w + a.w);
+    }
+    if (!PAIR && p.act == 1) v = make_float4(gelu_erf(v.x), gelu_erf(v.y), gelu_erf(v.z), gelu_erf(v.w));
     const size_t oc = (size_t)row * p.ldc + c4;
     if (p.c_f32) {
-      *reinterpret_cast<float4 *>(reinterpret_cast<float *>(Cbase) + oc) = s;
+      *reinterpret_cast<float4 *>(reinterpret_cast<float *>(Cbase) + oc) = v;
     } else {
       uint2 o;
-      o.x = f32_to_bf16_rne(s.x) | (f32_to_bf16_rne(s.y) << 16);
-      o.y = f32_to_bf16_rne(s.z) | (f32_to_bf16_rne(s.w) << 16);
+      o.x = f32_to_bf16_rne(v.x) | (f32_to_bf16_rne(v.y) << 16);
+      o.y = f32_to_bf16_rne(v.z) | (f32_to_bf16_rne(v.w) << 16);
       *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(Cbase) + oc) = o;
     }
   }
@@ -513,7 +533,9 @@ void reduce_launch_config(const GemmParams &p, KernelLaunch *out) {
   int bx = (int)((per_job + 255) / 256);
   if (bx > 1024) bx = 1024;
   if (bx < 1) bx = 1;
-  out->func = reinterpret_cast<void *>(&reduce_jobs_kernel);
+  bool pair = p.K <= 1 && p.act == 0;  // every job: in0 + in1
+  for (int j = 0; j < p.n_jobs && j < kMaxJobs; ++j) pair = pair && ((p.sel[j] >> 7) & 1);
+  out->func = pair ? reinterpret_cast<void *>(&reduce_jobs_kernel<true>) : reinterpret_cast<void *>(&reduce_jobs_kernel<false>);
   out->grid = dim3(bx, p.n_jobs);
   out->block = dim3(256);
 }

@@ -60,6 +60,7 @@ constexpr double kDefaultCuCopyGBps = 1000.0; // the CU copy kernel
 constexpr double kDefaultCuAddGBps = 1500.0;  // the add-and-forward launch beside a GEMM (bytes read + written)
 constexpr double kDefaultMfmaTflops = 900.0;
 constexpr double kDefaultLaunchUs = 20.0;
+constexpr double kDefaultHbmGBps = 5000.0;    // an HBM-bound launch (bytes read + written)
 
 bool is_pow2_chunk(int c) { return c == 1 || c == 2 || c == 4 || c == 8 || c == 16; }
 
@@ -126,7 +127,20 @@ WsLayout ws_layout(const cm_plan &pl) {
   const size_t N = d.n_ranks, m = d.m, k = d.k, n = d.n, c = pl.chunks, T = N * m;
   WsLayout L{};
   const int ndir = d.dir == CM_RING_BI ? 2 : 1;
-  if (d.op == CM_OP_ALLGATHER) {
+  if (d.share) {
+    const size_t S = pl.split;
+    if (d.op == CM_OP_AG_GEMM) {  // receive slots [2][m][k] bf16, partials [S][m][n] fp32
+      L.ring = 0;
+      L.partial = 2 * m * k * 2;
+    } else {  // peer [N-1][m][n] at 0, receive slots [2][m][n] at ring, sent [N-1][m][n] at acc,
+              // partials [S][m][n] at partial; fp32
+      L.ring = (N - 1) * m * n * 4;
+      L.acc = L.ring + 2 * m * n * 4;
+      L.partial = L.acc + (N - 1) * m * n * 4;
+    }
+    L.partial_bytes = S * m * n * 4;
+    L.total = L.partial + L.partial_bytes;
+  } else if (d.op == CM_OP_ALLGATHER) {
     L.total = 0;
   } else if (d.op == CM_OP_AG_GEMM) {
     if (d.sched == CM_SCHED_NAIVE) {
@@ -221,6 +235,21 @@ cm_status validate_desc(const cm_plan_desc &d) {
     set_error("an epilogue activation exists only for AllGather->GEMM");
     return CM_ERR_UNSUPPORTED;
   }
+  if (d.share != 0 && d.share != 1) { set_error("share must be 0 or 1"); return CM_ERR_INVALID_ARG; }
+  if (d.split_k < 0 || d.split_k > 16) { set_error("split_k %d outside 0..16", d.split_k); return CM_ERR_INVALID_ARG; }
+  if (!d.share && d.split_k) { set_error("split_k applies to one rank's share (share = 1) only"); return CM_ERR_INVALID_ARG; }
+  if (d.share) {
+    if (!(d.op == CM_OP_AG_GEMM || d.op == CM_OP_GEMM_RS) || d.dir != CM_RING_UNI || d.sched != CM_SCHED_DECOMPOSED ||
+        d.chunks > 1 || d.hop_add || d.bucket_bf16) {
+      set_error("one rank's share: AllGather->GEMM or decomposed GEMM->ReduceScatter on a one-way ring, one chunk, "
+                "copy hops, fp32 bucket");
+      return CM_ERR_UNSUPPORTED;
+    }
+    if (d.split_k && (d.k / 64) % d.split_k) {
+      set_error("split_k %d must divide k/64 = %d", d.split_k, d.k / 64);
+      return CM_ERR_SHAPE;
+    }
+  }
   if ((d.tile_m || d.tile_n) && !tile_known(d.tile_m, d.tile_n)) {
     set_error("no GEMM tile %dx%d (choose 256x256, 256x192, 256x128, 128x256, 128x128, 64x256 or 0x0)", d.tile_m,
               d.tile_n);
@@ -307,6 +336,34 @@ Est estimate(const cm_plan_desc &d, int c) {
   return e;
 }
 
+// One rank's share: the K slices S of a step's GEMM ([m x k] . [k x n]) and
+// the predicted time of one step (the split GEMM at the tile's expected
+// rate, plus the partials written and summed at an HBM-bound rate).
+// Candidates: divisors of k/64 up to 16 that leave each slice at least 8
+// slabs of 64 (S = 1 always); a requested split_k is taken as it is.
+double share_step_us(const cm_plan_desc &d, int S, int *tm, int *tn) {
+  const double m = d.m, n = d.n, k = d.k;
+  const double score = choose_tile(d.m, d.n, S, tm, tn);
+  if (d.tile_m) { *tm = d.tile_m; *tn = d.tile_n; }
+  const double g = 2.0 * m * n * k / (d.mfma_tflops * 1e12 * score) * 1e6;
+  const double bytes = 2.0 * S * m * n * 4 + m * n * (d.op == CM_OP_GEMM_RS ? 12.0 : (d.out_dtype == CM_F32 ? 4 : 2));
+  return g + bytes / (kDefaultHbmGBps * 1e9) * 1e6 + 2 * d.launch_us;
+}
+int share_split(const cm_plan_desc &d, int *tm, int *tn) {
+  if (d.split_k) { (void)share_step_us(d, d.split_k, tm, tn); return d.split_k; }
+  const int KT = d.k / 64;
+  int best = 1;
+  double best_t = share_step_us(d, 1, tm, tn);
+  for (int S = 2; S <= 16; ++S) {
+    if (KT % S || KT / S < 8) continue;
+    int a, b;
+    const double t = share_step_us(d, S, &a, &b);
+    if (t < best_t) { best = S; best_t = t; }
+  }
+  (void)share_step_us(d, best, tm, tn);
+  return best;
+}
+
 // Predicted time of the naive schedule: AG gathers every shard (N - 1 hop
 // rounds) and then runs one GEMM over the gathered rows; RS runs the whole
 // GEMM and then a copy-and-add ring of N - 1 rounds.
@@ -343,6 +400,29 @@ cm_status plan(const cm_plan_desc *desc, cm_plan *out) {
     p.est_hop_us = hop_us(d, (double)d.n_ranks * d.m * d.k * 2.0, d.n_ranks, per_lane);
     p.est_total_us = (d.n_ranks - 1) * p.est_hop_us;
     p.ws_bytes = 0;
+    Program prog;
+    build_program(p, prog);
+    p.n_ops = (int)prog.ops.size();
+    p.n_jobs = (int)prog.jobs.size();
+    p.n_events = prog.n_events;
+    *out = p;
+    return CM_OK;
+  }
+  if (d.share) {
+    cm_plan p;
+    std::memset(&p, 0, sizeof p);
+    p.desc = d;
+    p.chunks = 1;
+    p.n_steps = d.n_ranks;
+    p.arc_cw = d.n_ranks - 1;
+    p.split = share_split(d, &p.tile_m, &p.tile_n);
+    const double g = share_step_us(d, p.split, &p.tile_m, &p.tile_n);
+    const double hop_bytes = (double)d.m * (d.op == CM_OP_AG_GEMM ? d.k * 2.0 : d.n * 4.0);
+    p.est_gemm_us = g;
+    p.est_hop_us = hop_bytes / (d.copy_gbps * 1e9) * 1e6 + d.launch_us;
+    p.est_total_us = d.n_ranks * std::max(g, p.est_hop_us) + std::min(g, p.est_hop_us);
+    p.declined = (d.n_ranks > 1 && p.est_hop_us > g) ? 1 : 0;
+    p.ws_bytes = ws_layout(p).total;
     Program prog;
     build_program(p, prog);
     p.n_ops = (int)prog.ops.size();
@@ -544,12 +624,13 @@ struct Builder {
     prog.ops.push_back(o);
     tick(0);
   }
-  void reduce(int stream, const std::vector<cm_job_rec> &jobs, int rows, int cols) {
+  void reduce(int stream, const std::vector<cm_job_rec> &jobs, int rows, int cols, int blocks = 0,
+              int act = CM_ACT_NONE) {
     if (jobs.empty()) return;
     cm_op_rec o = base(CM_OPK_REDUCE, stream);
     o.first_job = (int)prog.jobs.size();
     o.n_jobs = (int)jobs.size();
-    o.rows = rows; o.cols = cols;
+    o.rows = rows; o.cols = cols; o.depth = blocks; o.act = act;
     prog.jobs.insert(prog.jobs.end(), jobs.begin(), jobs.end());
     prog.ops.push_back(o);
     tick(stream);
@@ -1138,6 +1219,99 @@ struct Builder {
     exit_();
   }
 
+  // ------------------------------------------------------ one rank's share
+  // Virtual rank 0's steps on a one-way ring.  Step s: S split-K GEMM jobs
+  // (slice i: columns [i*k/S, (i+1)*k/S) of A and B) write the partials
+  // P[i] (fp32, [m][n]); one reduce launch adds them in slice order and
+  // stores the step's result.  Buffers that stand for the ring neighbour
+  // feed the hops.
+  void share_gemm(int a_buf, size_t a_off, int lda, size_t b_off) {
+    const int S = p.split;
+    const size_t ks = k / S;
+    std::vector<cm_job_rec> jobs;
+    for (int i = 0; i < S; ++i) {
+      cm_job_rec jb = job0();
+      jb.rank = 0; jb.index = i;
+      jb.a_buf = a_buf; jb.a_off = a_off + (size_t)i * ks * 2; jb.lda = lda;
+      jb.b_buf = CM_BUF_W; jb.b_off = b_off + (size_t)i * ks * 2; jb.ldb = (int)k;
+      jb.c_buf = CM_BUF_WS; jb.c_off = L.partial + (size_t)i * m * n * 4; jb.ldc = (int)n; jb.c_dtype = CM_F32;
+      jobs.push_back(jb);
+    }
+    cm_op_rec o = base(CM_OPK_GEMM, 0);
+    o.act = CM_ACT_NONE;
+    o.first_job = (int)prog.jobs.size();
+    o.n_jobs = S;
+    o.rows = (int)m; o.cols = (int)n; o.depth = (int)ks;
+    o.tile_m = p.tile_m; o.tile_n = p.tile_n;
+    prog.jobs.insert(prog.jobs.end(), jobs.begin(), jobs.end());
+    prog.ops.push_back(o);
+    tick(0);
+  }
+  void share_sum(int in1_off_valid, size_t in1_off, int c_buf, size_t c_off, int ldc, int c_dtype, int act) {
+    cm_job_rec jb = job0();
+    jb.rank = 0;
+    jb.in0_buf = CM_BUF_WS; jb.in0_off = L.partial;
+    if (in1_off_valid) { jb.in1_buf = CM_BUF_WS; jb.in1_off = in1_off; }
+    jb.ld_in = (int)n;
+    jb.c_buf = c_buf; jb.c_off = c_off; jb.ldc = ldc; jb.c_dtype = c_dtype;
+    reduce(0, {jb}, (int)m, (int)n, p.split, act);
+  }
+
+  void ag_share() {
+    const size_t slot_bytes = m * k * 2;
+    const int osz = d.out_dtype == CM_F32 ? 4 : 2;
+    std::vector<int> ehop(N, -1), egemm(N, -1);
+    entry();
+    for (int s = 0; s < N; ++s) {
+      cur_step = s;
+      if (s + 1 < N) {
+        // hop s: the neighbour's shard (N - s - 1) arrives in slot (s + 1) % 2;
+        // WAR: GEMM(s - 1) read that slot (step 0 reads rank 0's own shard
+        // from x, so slot 0 is free for hop 1)
+        if (s >= 2) wait(1, egemm[s - 1]);
+        copy(1, CM_BUF_X, (size_t)mod(-s - 1, N) * m * k * 2, CM_BUF_WS, (size_t)((s + 1) % 2) * slot_bytes, slot_bytes);
+        ehop[s] = record(1);
+      }
+      if (s >= 1) wait(0, ehop[s - 1]);  // RAW: the shard this step multiplies
+      const int c = mod(-s, N);
+      if (s == 0)
+        share_gemm(CM_BUF_X, 0, (int)k, 0);
+      else
+        share_gemm(CM_BUF_WS, (size_t)(s % 2) * slot_bytes, (int)k, 0);
+      egemm[s] = record(0);
+      share_sum(0, 0, CM_BUF_Y, (size_t)c * m * n * osz, (int)n, d.out_dtype, d.act);
+    }
+    exit_();
+  }
+
+  void rs_share() {
+    const size_t blk = m * n * 4;
+    auto peer = [&](int s) -> size_t { return (size_t)s * blk; };  // the neighbour's bucket for step s + 1
+    auto slot = [&](int par) -> size_t { return L.ring + (size_t)par * blk; };
+    auto sent = [&](int s) -> size_t { return L.acc + (size_t)s * blk; };
+    std::vector<int> ehop(N, -1), esum(N, -1);
+    entry();
+    for (int s = 0; s < N; ++s) {
+      cur_step = s;
+      if (s + 1 < N) {
+        // hop s: the bucket for step s + 1 arrives in slot (s + 1) % 2;
+        // WAR: the sum of step s - 1 read that slot (step 0's sum reads none)
+        if (s >= 2) wait(1, esum[s - 1]);
+        copy(1, CM_BUF_WS, peer(s), CM_BUF_WS, slot((s + 1) % 2), blk);
+        ehop[s] = record(1);
+      }
+      const int b = mod(-1 - s, N);
+      share_gemm(CM_BUF_X, (size_t)b * m * k * 2, (int)k, 0);
+      if (s >= 1) wait(0, ehop[s - 1]);  // RAW: the arrived bucket
+      if (s + 1 < N)
+        share_sum(s >= 1, slot(s % 2), CM_BUF_WS, sent(s), (int)n, CM_F32, CM_ACT_NONE);
+      else
+        share_sum(s >= 1, slot(s % 2), CM_BUF_Y, 0, (int)n, d.out_dtype, CM_ACT_NONE);
+      esum[s] = record(0);
+    }
+    exit_();
+  }
+
   // ------------------------------------------------- RS, pipeline chunks / naive
   void rs_pipe() {
     if (d.hop_add) { rs_pipe_add(); return; }
@@ -1221,7 +1395,9 @@ void build_program(const cm_plan &p, Program &prog) {
   prog.n_events = 0;
   Builder b(p, prog);
   const cm_plan_desc &d = p.desc;
-  if (d.op == CM_OP_ALLGATHER) {
+  if (d.share) {
+    if (d.op == CM_OP_AG_GEMM) b.ag_share(); else b.rs_share();
+  } else if (d.op == CM_OP_ALLGATHER) {
     b.allgather();
   } else if (d.op == CM_OP_AG_GEMM) {
     if (d.sched == CM_SCHED_NAIVE) b.ag_naive(); else b.ag_decomposed();

@@ -19,7 +19,9 @@ and MLP weights of one sequence-parallel layer:
     w2 [N, d, f/N]   (H heads of D dimensions per rank)
 
 and the stand-alone attention and LayerNorm inputs (attention_inputs:
-qkv [N, T, 3*H*D]; layernorm_inputs: fp32 rows).
+qkv [N, T, 3*H*D]; layernorm_inputs: fp32 rows), and the fp32 buckets that
+stand for the ring neighbour in one rank's share of the ReduceScatter
+(peer_buckets: [N-1, m, n]).
 
 Distributions: "normal" draws activations from N(0, 1) and weights from
 N(0, 0.02^2); "int" draws every element uniformly from {-3, ..., 3}, which
@@ -209,3 +211,18 @@ def backward_inputs_torch(kind, N, m, k, n, dist="normal", seed=0, device="cuda"
         gen_.manual_seed(seed * 8 + 120 + i + (3 if kind == "row" else 0))
         out.append(_torch_draw(shape, dist, std, gen_, device))
     return tuple(out)
+
+
+def peer_buckets(N, m, n, dist="normal", seed=0):
+    """The buckets a ring neighbour sends to rank 0 in one rank's share of the
+    ReduceScatter: fp32 [N-1, m, n].  "int": uniform over {-3, ..., 3} x 8
+    (partial sums of integer products); "normal": N(0, 0.5^2), about the size of
+    a partial product of the N(0, 1) x N(0, 0.02^2) inputs at k of a few
+    hundred."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 7])))
+    shape = (max(0, N - 1), m, n)
+    if dist == "int":
+        return (g.integers(INT_LO, INT_HI + 1, size=shape) * 8).astype(np.float32)
+    if dist == "normal":
+        return (g.standard_normal(size=shape, dtype=np.float32) * np.float32(0.5)).astype(np.float32)
+    raise ValueError("dist must be 'normal' or 'int', got %r" % (dist,))

@@ -186,6 +186,14 @@ typedef struct {
   int act;               /* AllGather->GEMM only: cm_act applied to every output
                             element before it is stored (the MLP activation fused
                             into the slice update); CM_ACT_NONE for the other ops */
+  int share;             /* 0 = every virtual rank's work (the N-rank group on one
+                            GPU); 1 = one rank's share: only virtual rank 0's
+                            steps, at their real shapes, as one GPU of the group
+                            would run them (see "One rank's share" below) */
+  int split_k;           /* share = 1 only: number of K slices each step's GEMM is
+                            split into (0 = choose: enough slices for the step's
+                            tiles to fill the chip, at least 8 slabs of 64 each);
+                            must divide k/64, at most 16 */
 } cm_plan_desc;
 
 /* The resolved schedule.  Plain data: no heap, nothing to destroy. */
@@ -204,7 +212,44 @@ typedef struct {
   double est_gemm_us;  /* cost model: one step's GEMM time (all ranks, one chunk) */
   double est_hop_us;   /* cost model: one step's hop time (all ranks, one chunk) */
   double est_total_us; /* cost model: the whole op */
+  int split;           /* share = 1: the K slices per step GEMM (S); else 0 */
 } cm_plan;
+
+/*
+ * One rank's share (cm_plan_desc.share = 1; AllGather->GEMM and the
+ * decomposed GEMM->ReduceScatter on a one-way ring, one chunk, fp32 bucket,
+ * copy hops).  On a real group each GPU runs only its own rank's steps; this
+ * program runs virtual rank 0's, at the real per-rank shapes, and brings in
+ * what its ring neighbour would send from buffers that stand for that
+ * neighbour.  One step's GEMM of one rank has too few output tiles to fill
+ * the chip (the GPT-3 fc1 step: 32 tiles of 256x192 for 256 compute units),
+ * so it is split along K into S slices (cm_plan.split) that write fp32
+ * partial products to the workspace, and one reduce launch adds the S
+ * partials in slice order (and, for the ReduceScatter, the arrived bucket)
+ * and stores the step's result.  Per step the GPU moves what rank 0's HBM
+ * would: the step GEMM's operands, the partials, and one hop copy of the
+ * shard (or bucket) that arrives.
+ *
+ *   AllGather->GEMM: x = [N][m][k] (the N shards; the ones of ranks 1..N-1
+ *   stand for the peers'), w = rank 0's weights [n][k] (the first block of a
+ *   [N][n][k] array is what is read), y = rank 0's output [N*m][n]:
+ *   y[c*m .. c*m+m) = act(X_c . W_0^T) for every shard c.  Step s multiplies
+ *   shard (N - s) mod N; hop s copies shard (N - s - 1) mod N from x into the
+ *   receive slot of step s + 1.
+ *   Workspace: receive slots [2][m][k] bf16, then partials [S][m][n] fp32.
+ *
+ *   GEMM->ReduceScatter: h = rank 0's activations [N*m][k], w = rank 0's
+ *   weights [n][k] (first block), out = rank 0's result [m][n].  Step s adds
+ *   rank 0's contribution H_0[b*m .. b*m+m) . W_0^T for bucket
+ *   b = (N - 1 - s) mod N to the bucket that arrived (none at s = 0) and
+ *   sends it on; at s = N - 1 (b = 0, the home bucket) the sum is rank 0's
+ *   output.  The arriving buckets are the caller's: the workspace starts
+ *   with peer[N-1][m][n] fp32, peer[s - 1] being the bucket the neighbour
+ *   sends for step s; hop s - 1 copies it into a receive slot.  The buckets
+ *   rank 0 sends are stored in sent[N-1][m][n] fp32 (sent[s] = step s's sum,
+ *   s < N - 1).  Workspace: peer, receive slots [2][m][n], sent, partials
+ *   [S][m][n], all fp32, in that order.
+ */
 
 /*
  * Build a plan.  Fails with CM_ERR_SHAPE unless: N*m <= 2^24 rows; k and n
@@ -257,19 +302,23 @@ typedef struct {
   int chunk;     /* chunk index */
   int first_job; /* GEMM / REDUCE */
   int n_jobs;
-  int rows, cols, depth; /* GEMM: M, N, K of every job; REDUCE: rows, cols */
+  int rows, cols, depth; /* GEMM: M, N, K of every job; REDUCE: rows, cols and
+                            the number S of fp32 blocks summed from in0 (0 = 1) */
   int tile_m, tile_n;    /* GEMM: block tile the launch uses */
   int src_buf, dst_buf;  /* COPY */
   size_t src_off, dst_off, bytes;
-  int act;               /* GEMM: cm_act of the epilogue (launches without addends only) */
+  int act;               /* GEMM: cm_act of the epilogue (launches without addends
+                            only); REDUCE: cm_act applied to the sum */
 } cm_op_rec;
 
 /*
  * One job of a GEMM op:  C[i][j] = sum_kk A[i][kk] * B[j][kk] + in0[i][j] + in1[i][j]
  * for i < rows, j < cols, kk < depth.  A, B bf16; in0/in1 fp32, each optional
  * (buf -1 = absent; in0 may alias C: read-add-write); C in c_dtype.
- * lda/ldb/ldc/ld_in are row strides in elements.  For a REDUCE op:
- * C = in0 + in1 (both fp32, both present).  `rank`, `dir` and `index` (the
+ * lda/ldb/ldc/ld_in are row strides in elements.  For a REDUCE op with
+ * S = max(1, depth): C = act(B_0 + B_1 + ... + B_{S-1} (+ in1)), added in that
+ * order, where B_s is the fp32 block of rows x ld_in elements at in0 +
+ * s * rows * ld_in (in0 present, in1 optional, both fp32).  `rank`, `dir` and `index` (the
  * shard or bucket the job works on) label the job for tests; the executor
  * does not use them.
  */

@@ -154,9 +154,8 @@ class Sim:
                 r |= {(j.a_buf, int(g)) for g in self._rows(j.a_buf, j.a_off, o.rows, j.lda * 2, o.depth * 2)}
                 r |= {(j.b_buf, int(g)) for g in self._rows(j.b_buf, j.b_off, o.cols, j.ldb * 2, o.depth * 2)}
             asz = 2 if j.add_dtype == nat.CM_BF16 else 4
-            for ib, io in ((j.in0_buf, j.in0_off), (j.in1_buf, j.in1_off)):
-                if ib >= 0:
-                    r |= {(ib, int(g)) for g in self._rows(ib, io, o.rows, j.ld_in * asz, o.cols * asz)}
+            for ib, io, nb in _addends(o, j):
+                r |= {(ib, int(g)) for g in self._rows(ib, io, o.rows * nb, j.ld_in * asz, o.cols * asz)}
             esz = 4 if j.c_dtype == nat.CM_F32 else 2
             w = {(j.c_buf, int(g)) for g in self._rows(j.c_buf, j.c_off, o.rows, j.ldc * esz, o.cols * esz)}
             reads.append(r)
@@ -202,12 +201,12 @@ class Sim:
                         B = self._bf16(j.b_buf, j.b_off, o.cols, o.depth, j.ldb)
                         val = A @ B.T
                     asz = 2 if j.add_dtype == nat.CM_BF16 else 4
-                    for ib, io in ((j.in0_buf, j.in0_off), (j.in1_buf, j.in1_off)):
-                        if ib >= 0:
-                            self.read(s, ib, self._rows(ib, io, o.rows, j.ld_in * asz, o.cols * asz))
-                            add = self._bf16 if asz == 2 else self._f32
-                            val = val + add(ib, io, o.rows, o.cols, j.ld_in)
-                    if o.kind == nat.CM_OPK_GEMM and o.act == nat.CM_ACT_GELU:
+                    for ib, io, nb in _addends(o, j):
+                        self.read(s, ib, self._rows(ib, io, o.rows * nb, j.ld_in * asz, o.cols * asz))
+                        add = self._bf16 if asz == 2 else self._f32
+                        for t in range(nb):  # a reduce's blocks, in order
+                            val = val + add(ib, io + t * o.rows * j.ld_in * asz, o.rows, o.cols, j.ld_in)
+                    if o.act == nat.CM_ACT_GELU:
                         val = 0.5 * val * (1.0 + _erf(val / np.sqrt(2.0)))
                     results.append((j, val))
                 for j, val in results:
@@ -226,12 +225,27 @@ class Sim:
         return self
 
 
+def _addends(o, j):
+    """(buffer, offset, blocks) of a job's addends: a reduce sums max(1, depth)
+    consecutive blocks from in0."""
+    out = []
+    if j.in0_buf >= 0:
+        out.append((j.in0_buf, j.in0_off, max(1, o.depth) if o.kind == nat.CM_OPK_REDUCE else 1))
+    if j.in1_buf >= 0:
+        out.append((j.in1_buf, j.in1_off, 1))
+    return out
+
+
 def buffer_sizes(plan):
     """Byte sizes of X, W, Y and the workspace for a plan (the documented layouts)."""
     d = plan.desc
     N, m, k, n = d.n_ranks, d.m, d.k, d.n
     T = N * m
     osz = 4 if d.out_dtype == nat.CM_F32 else 2
+    if d.share:  # one rank's share: rank 0's weights and output only
+        if d.op == nat.CM_OP_AG_GEMM:
+            return [N * m * k * 2, n * k * 2, T * n * osz, plan.ws_bytes]
+        return [T * k * 2, n * k * 2, m * n * osz, plan.ws_bytes]
     if d.op == nat.CM_OP_ALLGATHER:
         return [N * m * k * 2, 0, N * T * k * 2, plan.ws_bytes]
     if d.op == nat.CM_OP_AG_GEMM:
@@ -262,10 +276,9 @@ def check_program_bounds(plan, sizes=None):
                     span(j.a_buf, j.a_off, o.rows, j.lda * 2, o.depth * 2)
                     span(j.b_buf, j.b_off, o.cols, j.ldb * 2, o.depth * 2)
                 asz = 2 if j.add_dtype == nat.CM_BF16 else 4
-                for ib, io in ((j.in0_buf, j.in0_off), (j.in1_buf, j.in1_off)):
-                    if ib >= 0:
-                        assert ib == nat.CM_BUF_WS
-                        span(ib, io, o.rows, j.ld_in * asz, o.cols * asz)
+                for ib, io, nb in _addends(o, j):
+                    assert ib == nat.CM_BUF_WS
+                    span(ib, io, o.rows * nb, j.ld_in * asz, o.cols * asz)
                 esz = 4 if j.c_dtype == nat.CM_F32 else 2
                 span(j.c_buf, j.c_off, o.rows, j.ldc * esz, o.cols * esz)
     return len(ops)
