@@ -319,6 +319,124 @@ def measure_op(op, N, m, k, n, chunks, ring, n_comm, reps, copy_engine="sdma"):
     return out
 
 
+def measure_share(workload, reps):
+    """One rank's share of the step: virtual rank 0's fc1 (AllGather->GEMM)
+    and fc2 (GEMM->ReduceScatter) ring steps at their real shapes, as one GPU
+    of the N-GPU group runs them.  Each step's GEMM is split along K (S
+    slices, the planner's choice) and one reduce launch sums the partials; the
+    hops bring in the neighbour's shard / bucket (N(0, 0.5^2) buckets for
+    fc2).  Op time D: wall clock of `reps` graph replays without the trace,
+    with the hops on the SDMA engines and on compute units (the faster is
+    reported); compute-only time: the same split step GEMM + reduce with no
+    ring (a one-rank plan), times N; per-launch times from a traced run."""
+    import torch
+    from collective_matmul_decomposition_amd import _native as nat
+    from collective_matmul_decomposition_amd import buffers
+    from collective_matmul_decomposition_amd import inputs as gen
+    W = WORKLOADS[workload]
+    N, T, d, f = W["N"], W["T"], W["d"], W["f"]
+    m, fN = T // N, f // N
+    out = {"workload": workload, "rank": 0, "virtual_ranks": N,
+           "what": "virtual rank 0's ring steps at real shape (one GPU's share of the N-rank group); split-K step "
+                   "GEMMs + one reduce launch per step; hops bring in the neighbour's shard / bucket"}
+    total_flops, total_us = 0.0, 0.0
+    compute = torch.cuda.Stream()
+    compute.wait_stream(torch.cuda.current_stream())
+
+    def wall(fn, plan, x, w, y, ws, comm, n):
+        # best of three batches of n calls (one op is about half a millisecond)
+        for _ in range(3):
+            fn(plan, x, w, y, ws, compute, comm, None)
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(3):
+            t0 = time.perf_counter()
+            for _ in range(n):
+                fn(plan, x, w, y, ws, compute, comm, None)
+            torch.cuda.synchronize()
+            t = (time.perf_counter() - t0) / n * 1e6
+            best = t if best is None else min(best, t)
+        return best
+
+    for name, op, k, n in (("fc1", "ag", d, fN), ("fc2", "rs", fN, d)):
+        if op == "ag":
+            x, w = gen.ag_inputs_torch(N, m, k, n, "normal", 0, "cuda")
+        else:
+            x, w = gen.rs_inputs_torch(N, m, k, n, "normal", 0, "cuda")
+            x = x[:1].contiguous()
+        w = w[:1].contiguous()
+        fn = nat.cm_ag_gemm if op == "ag" else nat.cm_gemm_rs
+        comm = buffers.comm_streams(1)
+        D = {}
+        for ce in ("sdma", "cu"):
+            plan = nat.cm_ring_plan(op=op, n_ranks=N, m=m, k=k, n=n, share=1, out_dtype="bf16", n_comm=1,
+                                    copy_engine=ce)
+            y, ws = buffers.alloc_outputs(plan)
+            if op == "rs":
+                peer = gen.peer_buckets(N, m, n, "normal", 0)
+                ws[:peer.nbytes].copy_(torch.from_numpy(peer.view(np.uint8).reshape(-1)))
+            D[ce] = wall(fn, plan, x, w, y, ws, comm, reps)
+            del y, ws
+        best = min(D, key=D.get)
+        # compute only: one rank, one step, the same split
+        p1 = nat.cm_ring_plan(op=op, n_ranks=1, m=m, k=k, n=n, share=1, out_dtype="bf16", split_k=plan.split)
+        y1, ws1 = buffers.alloc_outputs(p1)
+        x1 = x[:1] if op == "ag" else x[:, :m].contiguous()
+        g_only = N * wall(fn, p1, x1, w, y1, ws1, comm, 4 * reps)
+        del y1, ws1, x1
+        # per-launch breakdown (the trace's timing events slow the op down)
+        plan = nat.cm_ring_plan(op=op, n_ranks=N, m=m, k=k, n=n, share=1, out_dtype="bf16", n_comm=1, copy_engine=best)
+        y, ws = buffers.alloc_outputs(plan)
+        ops, _ = nat.cm_plan_program(plan)
+        cap = sum(1 for o in ops if o.kind in (nat.CM_OPK_GEMM, nat.CM_OPK_COPY, nat.CM_OPK_REDUCE))
+        traces = [nat.Trace(cap) for _ in range(reps)]
+        for _ in range(2):
+            for tr in traces:
+                fn(plan, x, w, y, ws, compute, comm, tr)
+            torch.cuda.synchronize()
+        g_each, r_each, c_each = [], [], []
+        for tr in traces:
+            spans, _total = tr.read()
+            g_each += [q[5] - q[4] for q in spans if q[0] == nat.CM_OPK_GEMM]
+            r_each += [q[5] - q[4] for q in spans if q[0] == nat.CM_OPK_REDUCE]
+            c_each += [q[5] - q[4] for q in spans if q[0] == nat.CM_OPK_COPY]
+            tr.close()
+        g_us, r_us = float(np.median(g_each)), float(np.median(r_each))
+        c_us = float(np.median(c_each)) if c_each else 0.0
+        C = c_us * (N - 1)
+        Db = D[best]
+        flops = 2.0 * N * m * k * n  # rank 0's work in one op
+        hop_bytes = m * k * 2 if op == "ag" else m * n * 4
+        out[name] = {
+            "op": op, "step_gemm": "[%dx%d].[%dx%d]" % (m, k, k, n), "split_k": plan.split,
+            "tile": "%dx%d" % (plan.tile_m, plan.tile_n),
+            "workgroups_per_step": plan.split * (-(-m // plan.tile_m)) * (-(-n // plan.tile_n)),
+            "op_us": round(Db, 1), "op_us_sdma_hops": round(D["sdma"], 1), "op_us_cu_hops": round(D["cu"], 1),
+            "hops_on": best, "tflops": round(flops / (Db * 1e-6) / 1e12, 1),
+            "pct_of_bf16_peak": round(100 * flops / (Db * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "compute_only_us": round(g_only, 1),
+            "gemm_us_per_step": round(g_us, 1), "gemm_tflops": round(2.0 * m * k * n / (g_us * 1e-6) / 1e12, 1),
+            "reduce_us_per_step": round(r_us, 1),
+            "hop_us_per_step": round(c_us, 1) if c_each else None,
+            "hop_GBps": round(hop_bytes / (c_us * 1e-6) / 1e9, 1) if c_each else None,
+            "overlap_efficiency": round(Db / max(g_only, C), 3),
+            "hidden_fraction": round((g_only + C - Db) / C, 3) if C > 0 else None,
+            "weight_shard_MB": round(n * k * 2 / 1e6, 1),
+        }
+        total_flops += flops
+        total_us += Db
+        log("share %s: %s split %d tile %s: op %.1f us (hops on %s; sdma %.1f, cu %.1f) -> %.1f TFLOP/s; compute "
+            "only %.1f us; GEMM %.1f us/step = %.1f TFLOP/s, reduce %.1f us/step, hop %.1f us/step, hidden %s" % (
+                name, out[name]["step_gemm"], plan.split, out[name]["tile"], Db, best, D["sdma"], D["cu"],
+                out[name]["tflops"], g_only, g_us, out[name]["gemm_tflops"], r_us, c_us, out[name]["hidden_fraction"]))
+        del x, w, y, ws
+        torch.cuda.empty_cache()
+    out["step_us"] = round(total_us, 1)
+    out["tflops"] = round(total_flops / (total_us * 1e-6) / 1e12, 1)
+    out["pct_of_bf16_peak"] = round(100 * out["tflops"] / PEAK_BF16_TFLOPS, 2)
+    return out
+
+
 def run_sweep(name, reps, copy_engine):
     """The small-chunk regime grid (d = 2048, ffn 8192, 1024 tokens, N in
     {2, 4, 8}, chunks in {1, 2, 4}, AG / RS / pipeline-chunk RS) or the four
@@ -566,6 +684,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
     ap.add_argument("--no-naive", action="store_true")
     ap.add_argument("--no-layer", action="store_true", help="skip the sequence-parallel layer forward")
+    ap.add_argument("--no-share", action="store_true", help="skip one rank's share (rank 0's steps at real shape)")
     ap.add_argument("--no-backward", action="store_true", help="skip the MLP backward (bulk overlap)")
     ap.add_argument("--no-trace", action="store_true", help="time without the per-launch events")
     ap.add_argument("--sweep", choices=["c4", "c5"], help="instead of the step: the small-chunk grid (c4) or the "
@@ -647,6 +766,7 @@ def main():
                      "pct_of_bf16_peak": round(100 * s2["value"] / PEAK_BF16_TFLOPS, 2),
                      "roofline": s2.get("roofline"), "overlap": s2.get("overlap"), "naive": s2.get("naive")}
 
+    share = None if args.no_share else measure_share(args.workload, max(10, args.steps))
     layer = None if args.no_layer else measure_layer(args, max(5, args.steps // 2), 2)
     backward = None if args.no_backward else measure_backward(args, args.workload, max(5, args.steps // 2), 2)
 
@@ -683,6 +803,7 @@ def main():
         "alt_rs_hop": alt_hop,
         "step_launches": res.get("step_launches"),
         "secondary": secondary,
+        "one_rank_share": share,
         "layer": layer,
         "backward": backward,
     }
