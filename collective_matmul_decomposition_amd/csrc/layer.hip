@@ -192,36 +192,52 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
         s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[t], 0, 0, 0);
       }
     }
-    // online softmax: element e of tile t is key k0 + 32 t + 8 (e / 4) + 4 g + e % 4
-    // the mask is needed only where a key can lie after a query of the wave or past the sequence
+    // online softmax: element e of tile t is key k0 + 32 t + 8 (e / 4) + 4 g + e % 4.
+    // The mask is needed only where a key can lie after a query of the wave or
+    // past the sequence; a key is kept while its offset 32 t + 8 (e / 4) + e % 4
+    // is at most `lim` (one comparison with a per-lane limit, no branch).
     const bool masked = (p.causal && k0 + kAttnBK - 1 > q0) || k0 + kAttnBK > p.T;
+    if (masked) {
+      const int lim = (p.causal ? min(my_q, p.T - 1) : p.T - 1) - k0 - 4 * g;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (32 * t + 8 * (e >> 2) + (e & 3) > lim) s[t][e] = -INFINITY;
+    }
+    // the maximum of the raw scores: the scale is positive, and rounding is
+    // monotone, so scaling the maximum gives the maximum of the scaled scores
     float mloc = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float v = s[t][e] * p.scale_log2;
-        if (masked) {
-          const int key = k0 + t * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
-          if (key >= p.T || (p.causal && key > my_q)) v = -INFINITY;
-        }
-        s[t][e] = v;
-        mloc = fmaxf(mloc, v);
-      }
+      for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, s[t][e]);
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);
+    const float m_new = fmaxf(m_run, mloc * p.scale_log2);
     const float msub = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - msub);  // 0 on the first block (m_run = -inf)
-    float lsum = 0.f;
+    // exponentials with the hardware's base-2 exponential (v_exp_f32; results
+    // below 2^-126 may flush to zero, far inside the error bound), the scale
+    // and the subtraction of the maximum in one fused multiply-add
+    const float alpha = __builtin_amdgcn_exp2f(m_run - msub);  // 0 on the first block (m_run = -inf)
     bf16x8 pf[2][2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const __bf16 pb = (__bf16)exp2f(s[t][e] - msub);  // nearest even
-        lsum += (float)pb;
-        pf[t][e >> 3][e & 7] = pb;
-      }
+      for (int e = 0; e < 16; ++e)
+        pf[t][e >> 3][e & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[t][e], p.scale_log2, -msub));  // nearest even
+    // the running sum adds the same bf16 values, two at a time (dot product with ones)
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float lsum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const bf16x2 pr = {pf[t][h][2 * q], pf[t][h][2 * q + 1]};
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
+        }
     lsum += __shfl_xor(lsum, 32);
     l_run = l_run * alpha + lsum;
     m_run = m_new;
