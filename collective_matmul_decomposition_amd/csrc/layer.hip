@@ -93,6 +93,17 @@ __device__ __forceinline__ void attn_load_kv(const uint16_t *base, int ld, int k
   }
 }
 
+// Byte offset, within its 128-byte V^T row, of the 8-byte unit u (keys
+// 4u .. 4u + 3) of dim row `dim`.  The units that one 16-key MFMA step reads
+// together, u and u + 2 with u % 4 < 2, share a 16-byte chunk
+// (u / 4 * 2 + u % 2) in that order; chunks are XOR-swizzled by dim / 2 mod 8,
+// so the 16 rows that a 16-lane phase of the operand read touches cover the
+// 64 banks once.
+__device__ __forceinline__ int attn_vt_unit(int dim, int u) {
+  const int chunk = ((u >> 2) << 1) | (u & 1), half = (u >> 1) & 1;
+  return ((chunk ^ ((dim >> 1) & 7)) << 4) | (half << 3);
+}
+
 // K into its swizzled LDS rows; V transposed into V^T units of 4 keys.
 __device__ __forceinline__ void attn_store_kv(char *sK, char *sV, int tid, const uint4 (&kr)[4], const uint4 (&vr)[4]) {
   const int dg = tid & 15, kgp = tid >> 4;
@@ -113,7 +124,7 @@ __device__ __forceinline__ void attn_store_kv(char *sK, char *sV, int tid, const
     pk.x = word(0) | (word(1) << 16);
     pk.y = word(2) | (word(3) << 16);
     const int dim = 8 * dg + e;
-    *reinterpret_cast<uint2 *>(sV + dim * 128 + ((kgp ^ ((dim >> 1) & 15)) << 3)) = pk;
+    *reinterpret_cast<uint2 *>(sV + dim * 128 + attn_vt_unit(dim, kgp)) = pk;
   }
 }
 
@@ -122,7 +133,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
   // chunk c of key row r stored at position c ^ (r % 16).
   __shared__ __attribute__((aligned(16))) char sK[kAttnSub * kAttnBK * kAttnD * 2];
   // V^T block [128 dims][64 keys]: 128-byte rows of 16 units of 4 keys,
-  // unit u of dim row r stored at position u ^ ((r / 2) % 16).
+  // placed by attn_vt_unit.
   __shared__ __attribute__((aligned(16))) char sV[kAttnSub * kAttnD * kAttnBK * 2];
 
   const int lb = attn_logical_block();
@@ -219,25 +230,30 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
     // below 2^-126 may flush to zero, far inside the error bound), the scale
     // and the subtraction of the maximum in one fused multiply-add
     const float alpha = __builtin_amdgcn_exp2f(m_run - msub);  // 0 on the first block (m_run = -inf)
-    bf16x8 pf[2][2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        pf[t][e >> 3][e & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[t][e], p.scale_log2, -msub));  // nearest even
-    // the running sum adds the same bf16 values, two at a time (dot product with ones)
+    // elements e, e + 1 are converted together (nearest even) into one register
+    // of the B operand; the running sum adds the same bf16 values, two at a
+    // time (a dot product with ones)
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    bf16x8 pf[2][2];
     float lsum = 0.f;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h) {
+        uint32_t w[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const bf16x2 pr = {pf[t][h][2 * q], pf[t][h][2 * q + 1]};
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
+          const int e = 8 * h + 2 * q;
+          const f32x2 x = {__builtin_amdgcn_exp2f(__builtin_fmaf(s[t][e], p.scale_log2, -msub)),
+                           __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][e + 1], p.scale_log2, -msub))};
+          const bf16x2 b = __builtin_convertvector(x, bf16x2);
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(b, ones, lsum, false);
+          w[q] = __builtin_bit_cast(uint32_t, b);
         }
+        pf[t][h] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+      }
     lsum += __shfl_xor(lsum, 32);
     l_run = l_run * alpha + lsum;
     m_run = m_new;
@@ -256,11 +272,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
         const int u0 = t * 8 + h * 4 + g;  // units of keys 32 t + 16 h + 4 g .. +3 and 8 keys later
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          const int dim = dt * 32 + l32, sw = (dim >> 1) & 15;
-          const uint2 lo = *reinterpret_cast<const uint2 *>(sVb + dim * 128 + ((u0 ^ sw) << 3));
-          const uint2 hi = *reinterpret_cast<const uint2 *>(sVb + dim * 128 + (((u0 + 2) ^ sw) << 3));
-          const uint4 both = make_uint4(lo.x, lo.y, hi.x, hi.y);
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, both);
+          const int dim = dt * 32 + l32;
+          // units u0 and u0 + 2, one 16-byte chunk
+          const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(sVb + dim * 128 + attn_vt_unit(dim, u0));
           oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t][h], oacc[dt], 0, 0, 0);
         }
       }
