@@ -131,6 +131,33 @@ def test_ragged_shapes(op, N, m, k, n, dir, chunks, n_comm):
         check(op, a, w, y, out, dist)
 
 
+# The limits: 64 virtual ranks (CM_MAX_RANKS) with one to three rows per shard,
+# on every schedule (so launches of 64 and 128 jobs, and the pipeline's 4096
+# jobs split over launches), and the maximum of 16 chunks.
+EXTREME = [
+    # op, N, m, k, n, dir, chunks, n_comm, hop
+    ("ag", 64, 1, 64, 64, "uni", 1, 4, "copy"),
+    ("ag", 64, 2, 64, 128, "bi", 2, 8, "copy"),
+    ("rs", 64, 3, 64, 64, "uni", 1, 4, "copy"),
+    ("rs", 64, 1, 64, 64, "bi", 1, 8, "copy"),
+    ("rs", 64, 2, 64, 64, "uni", 1, 4, "add"),
+    ("rs_pipe", 64, 2, 64, 128, "uni", 2, 4, "copy"),
+    ("ag", 64, 1, 64, 64, "direct", 1, 4, "copy"),
+    ("rs", 64, 1, 64, 64, "direct", 1, 4, "copy"),
+    ("ag", 4, 32, 64, 64, "uni", 16, 2, "copy"),
+    ("rs", 3, 8, 64, 1024, "uni", 16, 2, "copy"),
+    ("rs", 3, 8, 64, 1024, "bi", 16, 3, "add"),
+]
+
+
+@pytest.mark.parametrize("op,N,m,k,n,dir,chunks,n_comm,hop", EXTREME)
+def test_extreme_shapes(op, N, m, k, n, dir, chunks, n_comm, hop):
+    say("extreme", op, N, m, k, n, dir, chunks, n_comm, hop)
+    for dist, out in (("int", "f32"), ("normal", "bf16")):
+        _, a, w, (y,) = run_case(op, N, m, k, n, dist, out, dir, chunks, "decomposed", n_comm, hop=hop)
+        check(op, a, w, y, out, dist)
+
+
 MID = [("ag", "uni", 1), ("ag", "bi", 2), ("rs", "uni", 2), ("rs", "bi", 4), ("rs_pipe", "uni", 4)]
 
 

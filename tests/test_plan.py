@@ -404,7 +404,26 @@ def _gpu_cases():
             for out in ("f32", "bf16"):
                 cases.append(dict(op=op, n_ranks=3, m=300, k=192, n=320 if op == "ag" else 640, n_comm=2,
                                   chunks=1 if op == "ag" else 2, out_dtype=out, tile=tile))
+    for op, N, m, k, n, dir, chunks, n_comm, hop in g.EXTREME:
+        for out in ("f32", "bf16"):
+            cases.append(dict(op=op, n_ranks=N, m=m, k=k, n=n, dir=dir, chunks=chunks, out_dtype=out, n_comm=n_comm,
+                              hop=hop))
     return cases
+
+
+@pytest.mark.parametrize("case", range(11))
+def test_extreme_programs_simulate(case):
+    """The limits the GPU tests run (64 virtual ranks with 1-3 rows per shard on every
+    schedule; 16 chunks), executed on the CPU with the race check: equal to the oracle."""
+    import test_gpu_parity as g
+    op, N, m, k, n, dir, chunks, n_comm, hop = g.EXTREME[case]
+    plan = nat.cm_ring_plan(op=op, n_ranks=N, m=m, k=k, n=n, dir=dir, chunks=chunks, out_dtype="f32", n_comm=n_comm,
+                            hop=hop)
+    a, w = (gen.ag_inputs if op == "ag" else gen.rs_inputs)(N, m, k, n, "int", 0)
+    sim = Sim(plan, buffer_sizes(plan), {nat.CM_BUF_X: a, nat.CM_BUF_W: w}).run()
+    ref = oracle.ag_gemm(a, w) if op == "ag" else oracle.gemm_rs(a, w)
+    got = sim.buf[nat.CM_BUF_Y].view(np.float32).reshape(ref.shape).astype(np.float64)
+    assert np.array_equal(got, ref)
 
 
 def test_gpu_test_programs_stay_in_bounds():
