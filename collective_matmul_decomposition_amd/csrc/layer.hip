@@ -29,6 +29,8 @@ namespace collmm {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void *attn_lds_ptr;
+typedef __attribute__((address_space(1))) void *attn_glob_ptr;
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
@@ -59,7 +61,6 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
 constexpr int kAttnD = 128;   // head dimension
 constexpr int kAttnBQ = 128;  // query rows per workgroup
 constexpr int kAttnBK = 64;   // keys per block (one softmax update)
-constexpr int kAttnSub = 2;   // blocks staged through LDS per pair of barriers
 
 struct AttnParams {
   const uint16_t *qkv;  // [N][T][3*H*D]
@@ -80,17 +81,37 @@ __device__ __forceinline__ int attn_logical_block() {
   return b < per * 8 ? (b & 7) * per + (b >> 3) : b;
 }
 
-// One block of keys and values, staged through registers: K rows whole (1024
-// chunks of 16 bytes, 4 per thread), V as 4 keys x 8 dims per thread.
-__device__ __forceinline__ void attn_load_kv(const uint16_t *base, int ld, int kcol, int vcol, int T, int k0,
-                                             int tid, uint4 (&kr)[4], uint4 (&vr)[4]) {
-  const int dg = tid & 15, kgp = tid >> 4;
+// Workgroup barrier without a memory fence: this wave's LDS stores are
+// complete, then s_barrier.  (__syncthreads() would also wait for every
+// outstanding global load, including the next block's prefetch.)
+__device__ __forceinline__ void attn_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One block of keys straight into its LDS buffer (global_load_lds: lane l of
+// a wave's load lands at the wave's 1 KB base + 16 l, no registers): load i of
+// wave w fills keys 4 (4 i + w) .. +3; lane l writes position l % 16 of key
+// row l / 16, which holds the row's chunk (l % 16) ^ (key % 16).  Rows past the
+// sequence read the last key (their scores are masked).
+__device__ __forceinline__ void attn_load_k(const uint16_t *base, int ld, int kcol, int T, int k0, int wave, int lane,
+                                            char *sKbuf) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int key = (tid + 256 * i) >> 4, ch = (tid + 256 * i) & 15;
-    kr[i] = *reinterpret_cast<const uint4 *>(base + (size_t)min(k0 + key, T - 1) * ld + kcol + 8 * ch);
-    vr[i] = *reinterpret_cast<const uint4 *>(base + (size_t)min(k0 + 4 * kgp + i, T - 1) * ld + vcol + 8 * dg);
+    const int grp = 4 * i + wave, key = 4 * grp + (lane >> 4), ch = (lane & 15) ^ (key & 15);
+    const uint16_t *src = base + (size_t)min(k0 + key, T - 1) * ld + kcol + 8 * ch;
+    __builtin_amdgcn_global_load_lds((attn_glob_ptr)src, (attn_lds_ptr)(sKbuf + grp * 1024), 16, 0, 0);
   }
+}
+
+// One block of values into registers: 4 keys x 8 dims per thread.
+__device__ __forceinline__ void attn_load_v(const uint16_t *base, int ld, int vcol, int T, int k0, int tid,
+                                            uint4 (&vr)[4]) {
+  const int dg = tid & 15, kgp = tid >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    vr[i] = *reinterpret_cast<const uint4 *>(base + (size_t)min(k0 + 4 * kgp + i, T - 1) * ld + vcol + 8 * dg);
 }
 
 // Byte offset, within its 128-byte V^T row, of the 8-byte unit u (keys
@@ -104,14 +125,9 @@ __device__ __forceinline__ int attn_vt_unit(int dim, int u) {
   return ((chunk ^ ((dim >> 1) & 7)) << 4) | (half << 3);
 }
 
-// K into its swizzled LDS rows; V transposed into V^T units of 4 keys.
-__device__ __forceinline__ void attn_store_kv(char *sK, char *sV, int tid, const uint4 (&kr)[4], const uint4 (&vr)[4]) {
+// V transposed into V^T units of 4 keys.
+__device__ __forceinline__ void attn_store_v(char *sV, int tid, const uint4 (&vr)[4]) {
   const int dg = tid & 15, kgp = tid >> 4;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int key = (tid + 256 * i) >> 4, ch = (tid + 256 * i) & 15;
-    *reinterpret_cast<uint4 *>(sK + key * 256 + ((ch ^ (key & 15)) << 4)) = kr[i];
-  }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int sh = (e & 1) * 16;
@@ -131,10 +147,13 @@ __device__ __forceinline__ void attn_store_kv(char *sK, char *sV, int tid, const
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
   // K block [64 keys][128 dims]: 256-byte rows of 16 chunks of 16 bytes,
   // chunk c of key row r stored at position c ^ (r % 16).
-  __shared__ __attribute__((aligned(16))) char sK[kAttnSub * kAttnBK * kAttnD * 2];
+  // Two K buffers, separate objects so that the compiler can tell the next
+  // block's loads into one from this block's reads of the other.
+  __shared__ __attribute__((aligned(1024))) char sK0[kAttnBK * kAttnD * 2];
+  __shared__ __attribute__((aligned(1024))) char sK1[kAttnBK * kAttnD * 2];
   // V^T block [128 dims][64 keys]: 128-byte rows of 16 units of 4 keys,
   // placed by attn_vt_unit.
-  __shared__ __attribute__((aligned(16))) char sV[kAttnSub * kAttnD * kAttnBK * 2];
+  __shared__ __attribute__((aligned(16))) char sV[kAttnD * kAttnBK * 2];
 
   const int lb = attn_logical_block();
   const int bh = lb / p.qblocks;
@@ -167,26 +186,25 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
   const int kv_end = p.causal ? min(p.T, (qb + 1) * kAttnBQ) : p.T;
   const int nblk = (kv_end + kAttnBK - 1) / kAttnBK;
 
-  // (loading the next block into registers during this block's MFMAs was
-  // measured slower: the extra registers cost more than the hidden latency)
-  uint4 kreg[4], vreg[4];
-  for (int jj = 0; jj < nblk; jj += kAttnSub) {
-    __syncthreads();  // every wave is done with the previous blocks
-#pragma unroll
-    for (int sb = 0; sb < kAttnSub; ++sb) {
-      if (jj + sb < nblk) {
-        attn_load_kv(base, p.ld_qkv, kcol, vcol, p.T, (jj + sb) * kAttnBK, tid, kreg, vreg);
-        attn_store_kv(sK + sb * kAttnBK * 256, sV + sb * kAttnD * kAttnBK * 2, tid, kreg, vreg);
-      }
-    }
-    __syncthreads();
-#pragma unroll
-  for (int sb = 0; sb < kAttnSub; ++sb) {
-    const int j = jj + sb;
+  // Block j + 1's keys stream into the other K buffer, and its values into
+  // registers, while block j is multiplied.  The wait for the values (which
+  // the compiler places before their LDS store) also covers the keys, which
+  // were issued before them: vector-memory loads complete in order.
+  uint4 vreg[4];
+  attn_load_k(base, p.ld_qkv, kcol, p.T, 0, wave, lane, sK0);
+  attn_load_v(base, p.ld_qkv, vcol, p.T, 0, tid, vreg);
+  // one block: its keys in sKb, the next block's keys stream into sKn
+  auto block = [&](const int j, const char *sKb, char *sKn) __attribute__((always_inline)) {
     const int k0 = j * kAttnBK;
-    if (j >= nblk || (p.causal && k0 > q0 + 31)) break;  // every later key is after every query of the wave
-    const char *sKb = sK + sb * kAttnBK * 256;
-    const char *sVb = sV + sb * kAttnD * kAttnBK * 2;
+    attn_barrier();  // every wave is done with block j - 1 (V^T and the other K buffer)
+    attn_store_v(sV, tid, vreg);  // the compiler waits for vreg here: block j's keys are in LDS too
+    if (j + 1 < nblk) {
+      attn_load_k(base, p.ld_qkv, kcol, p.T, k0 + kAttnBK, wave, lane, sKn);
+      attn_load_v(base, p.ld_qkv, vcol, p.T, k0 + kAttnBK, tid, vreg);
+    }
+    attn_barrier();  // block j's keys and values are in LDS, for every wave
+    if (p.causal && k0 > q0 + 31) return;  // every key of the block is after every query of the wave
+    const char *sVb = sV;
 
     // S^T = K Q^T for keys k0 .. k0 + 63 (two 32-key tiles)
     f32x16 s[2];
@@ -278,7 +296,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
           oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t][h], oacc[dt], 0, 0, 0);
         }
       }
-  }
+  };
+  for (int j = 0; j < nblk; j += 2) {
+    block(j, sK0, sK1);
+    if (j + 1 < nblk) block(j + 1, sK1, sK0);
   }
 
   if (my_q >= p.T) return;
