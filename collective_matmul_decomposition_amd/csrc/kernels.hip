@@ -455,7 +455,11 @@ __global__ __launch_bounds__(64 * (WM * WN) + 64 * NL) void gemm_jobs_kernel(con
 // in that order in fp32, where B_s is the fp32 block of rows x ld_in at
 // in0 + s * rows * ld_in and S = max(1, K); 4 columns per thread.  PAIR: the
 // launch is C = in0 + in1 for every job (S = 1, in1 present, no activation):
-// the ring's add-and-forward, in its own instantiation.
+// the ring's add-and-forward, in its own instantiation, with non-temporal
+// loads and stores (it streams beside the step GEMMs; measured 4% faster GEMM
+// launches on the GPT-3 fc2 ring than with cached accesses).
+typedef float f32x4nt __attribute__((ext_vector_type(4)));  // for the non-temporal builtins
+
 template <bool PAIR>
 __global__ __launch_bounds__(256) void reduce_jobs_kernel(const GemmParams p) {
   const int job = blockIdx.y;
@@ -471,7 +475,13 @@ __global__ __launch_bounds__(256) void reduce_jobs_kernel(const GemmParams p) {
   for (long t = (long)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (long)gridDim.x * blockDim.x) {
     const int row = (int)(t / cols4), c4 = (int)(t - (long)row * cols4) * 4;
     const size_t ii = (size_t)row * p.ld_in + c4;
-    float4 v = *reinterpret_cast<const float4 *>(In0 + ii);
+    float4 v;
+    if (PAIR) {
+      const f32x4nt x = __builtin_nontemporal_load(reinterpret_cast<const f32x4nt *>(In0 + ii));
+      v = make_float4(x[0], x[1], x[2], x[3]);
+    } else {
+      v = *reinterpret_cast<const float4 *>(In0 + ii);
+    }
     if (!PAIR) {
       for (int b = 1; b < S; ++b) {
         const float4 a = *reinterpret_cast<const float4 *>(In0 + (size_t)b * bstride + ii);
@@ -479,13 +489,22 @@ __global__ __launch_bounds__(256) void reduce_jobs_kernel(const GemmParams p) {
       }
     }
     if (has1) {
-      const float4 a = *reinterpret_cast<const float4 *>(In1 + ii);
+      float4 a;
+      if (PAIR) {
+        const f32x4nt x = __builtin_nontemporal_load(reinterpret_cast<const f32x4nt *>(In1 + ii));
+        a = make_float4(x[0], x[1], x[2], x[3]);
+      } else {
+        a = *reinterpret_cast<const float4 *>(In1 + ii);
+      }
       v = make_float4(v.x + a.x, v.y + a.y, v.z + a.z, v.w + a.w);
     }
     if (!PAIR && p.act == 1) v = make_float4(gelu_erf(v.x), gelu_erf(v.y), gelu_erf(v.z), gelu_erf(v.w));
     const size_t oc = (size_t)row * p.ldc + c4;
     if (p.c_f32) {
-      *reinterpret_cast<float4 *>(reinterpret_cast<float *>(Cbase) + oc) = v;
+      if (PAIR)
+        __builtin_nontemporal_store((f32x4nt){v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4nt *>(reinterpret_cast<float *>(Cbase) + oc));
+      else
+        *reinterpret_cast<float4 *>(reinterpret_cast<float *>(Cbase) + oc) = v;
     } else {
       uint2 o;
       o.x = f32_to_bf16_rne(v.x) | (f32_to_bf16_rne(v.y) << 16);
