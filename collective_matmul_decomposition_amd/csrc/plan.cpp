@@ -287,7 +287,7 @@ Est estimate(const cm_plan_desc &d, int c) {
   const int ndir = bi ? 2 : 1;
   const int lanes = d.n_ranks * ndir;
   // copies per lane per step: a lane moves a contiguous range of ranks in one
-  // or two copies (AG step 0 copies rank by rank)
+  // or two copies (AG step 0 with several chunks per shard copies rank by rank)
   const int per_lane = std::max(1, std::min(2, (int)(lanes / std::max(1, d.n_comm))));
   Est e{};
   if (d.op == CM_OP_AG_GEMM) {
@@ -759,7 +759,11 @@ struct Builder {
                 if (up != (int)gi) { wait(g.stream, ehop[s - 1][j][dr][up]); }
               }
             }
-            if (s == 0) {
+            if (s == 0 && c == 1) {
+              // from the user's shards, which are laid out like the slots: a run of
+              // ranks is one copy (two at the ring's wrap)
+              shifted_copy(g.stream, CM_BUF_X, 0, CM_BUF_WS, slot_off(dr, 0, 0, 0), chunk_bytes, g.a, g.b, shift);
+            } else if (s == 0) {
               // from the user's shards: rank r's chunk j rows
               for (int r = g.a; r < g.b; ++r)
                 copy(g.stream, CM_BUF_X, ((size_t)r * m + (size_t)j * mc) * k * 2, CM_BUF_WS,
