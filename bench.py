@@ -765,6 +765,17 @@ def main():
                      "ms_per_step": round(s2["ms_per_step"], 4),
                      "pct_of_bf16_peak": round(100 * s2["value"] / PEAK_BF16_TFLOPS, 2),
                      "roofline": s2.get("roofline"), "overlap": s2.get("overlap"), "naive": s2.get("naive")}
+        del s2
+        torch.cuda.empty_cache()
+        if not args.no_alt_copy:
+            # the same step with the other engine moving the hops (at these small hops it matters)
+            alt_args = argparse.Namespace(**vars(args))
+            alt_args.copy_engine = "cu" if args.copy_engine == "sdma" else "sdma"
+            s3 = measure(alt_args, args.secondary, max(5, args.steps // 2), 2, False, not args.no_trace)
+            secondary["alt_copy_engine"] = {"copy_engine": alt_args.copy_engine, "value": round(s3["value"], 2),
+                                            "ms_per_step": round(s3["ms_per_step"], 4), "overlap": s3.get("overlap")}
+            del s3
+            torch.cuda.empty_cache()
 
     share = None if args.no_share else measure_share(args.workload, max(10, args.steps))
     layer = None if args.no_layer else measure_layer(args, max(5, args.steps // 2), 2)
