@@ -11,8 +11,12 @@ Prints ONE JSON line:
   roofline     the dominant kernel (the batched step GEMM) against the bf16
                dense MFMA peak, from HIP events around every launch of it on
                the compute stream during the timed steps
-  overlap      decomposed time over max(GEMM time, hop time) and the fraction
-               of hop time hidden under GEMMs, per op, from the same events
+  overlap      per op: decomposed time over max(GEMM-only, copy-only) time.
+               GEMM-only: the monolithic GEMM alone (the naive schedule's);
+               copy-only: the smaller of the naive collective alone and the
+               decomposed hops' busy time.  Also the GEMM and hop busy times
+               inside the decomposed run and the fraction of hop time hidden
+               under GEMMs, from the same events
   cpu_baseline the CPU oracle timed on a bounded sample of the same workload
 
 Inputs are seeded synthetic tensors (activations N(0,1), weights
@@ -260,6 +264,42 @@ def measure(args, workload, steps, warmup, with_naive, with_trace):
         nwall = (time.perf_counter() - t0) / ns
         res["naive"] = {"ms_per_step": round(nwall * 1e3, 3), "tflops": round(flops_step / nwall / 1e12, 1),
                         "speedup_of_decomposed": round(nwall * 1e3 / ms_per_step, 3)}
+        if with_trace and "overlap" in res:
+            # GEMM-only and copy-only times: the naive schedule runs the
+            # monolithic GEMM and the collective one after the other, so each
+            # runs alone; the overlap efficiency is the decomposed time over
+            # the larger of the two
+            caps = [sum(1 for o in nat.cm_plan_program(p)[0]
+                        if o.kind in (nat.CM_OPK_GEMM, nat.CM_OPK_COPY, nat.CM_OPK_REDUCE)) for p in (pa, pr)]
+            ntr = [(nat.Trace(caps[0]), nat.Trace(caps[1])) for _ in range(3)]
+            for _ in range(2):
+                for ta, tb in ntr:
+                    nat.cm_ag_gemm(pa, x, w1, yn1, wsn1, compute, comm, ta)
+                    nat.cm_gemm_rs(pr, h, w2, yn2, wsn2, compute, comm, tb)
+                torch.cuda.synchronize()
+            alone = {"ag": [], "rs": []}
+            for ta, tb in ntr:
+                for name, tr in (("ag", ta), ("rs", tb)):
+                    spans, _total = tr.read()
+                    alone[name].append((union_length([(q[4], q[5]) for q in spans if q[0] == nat.CM_OPK_GEMM]),
+                                        union_length([(q[4], q[5]) for q in spans
+                                                      if q[0] in (nat.CM_OPK_COPY, nat.CM_OPK_REDUCE)])))
+                    tr.close()
+            for name, ov in res["overlap"].items():
+                Ga, Cn = (float(np.median([a[i] for a in alone[name]])) for i in (0, 1))
+                D = ov["decomposed_us"]
+                # copy-only: the naive collective alone, or the decomposed
+                # ring's own hops, whose busy time beside the GEMMs bounds
+                # theirs alone from above; the smaller of the two
+                Ca = min(Cn, ov["hop_busy_us"])
+                ov["overlap_efficiency_busy"] = ov["overlap_efficiency"]
+                ov.update({"gemm_only_us": round(Ga, 1), "naive_collective_us": round(Cn, 1),
+                           "copy_only_us": round(Ca, 1), "overlap_efficiency": round(D / max(Ga, Ca), 3),
+                           "bound_by": "gemm" if Ga >= Ca else "copy"})
+                log("%s: decomposed %.1f us; GEMM-only %.1f us, copy-only %.1f us (naive collective %.1f) -> "
+                    "efficiency %.3f (in-run busy: GEMM %.1f, hops %.1f -> %.3f)" % (
+                        name, D, Ga, Ca, Cn, ov["overlap_efficiency"], ov["gemm_busy_us"], ov["hop_busy_us"],
+                        ov["overlap_efficiency_busy"]))
         del yn1, wsn1, yn2, wsn2
     return res
 
@@ -311,8 +351,16 @@ def measure_op(op, N, m, k, n, chunks, ring, n_comm, reps, copy_engine="sdma"):
                         "hidden_fraction": round((G + C - D) / C, 3) if C > 0 else None,
                         "tflops": round(flops / (D * 1e-6) / 1e12, 1)})
         else:
+            # the naive schedule runs the monolithic GEMM and the collective
+            # one after the other: its GEMM time is the GEMM-only time; the
+            # copy-only time is the smaller of its collective's time and the
+            # decomposed hops' busy time (an upper bound on those hops alone)
             out.update({"naive_us": round(D, 1), "monolithic_gemm_us": round(G, 1),
-                        "speedup_over_naive": round(D / out["decomposed_us"], 3)})
+                        "speedup_over_naive": round(D / out["decomposed_us"], 3),
+                        "gemm_only_us": round(G, 1), "naive_collective_us": round(C, 1),
+                        "copy_only_us": round(min(C, out["hop_busy_us"]), 1),
+                        "overlap_efficiency_busy": out["overlap_efficiency"],
+                        "overlap_efficiency": round(out["decomposed_us"] / max(G, min(C, out["hop_busy_us"])), 3)})
         del y, ws
     del x, w
     torch.cuda.empty_cache()

@@ -728,88 +728,102 @@ struct Builder {
     for (int s = 0; s < p.n_steps; ++s) {
       for (int j = 0; j < c; ++j) {
         cur_step = s; cur_chunk = j;
-        // hops of step s: forward what this step multiplies
-        for (int dr = 0; dr < ndir; ++dr) {
-          if (s >= arcs[dr]) continue;
-          const int shift = dr == 0 ? 1 : -1;
-          ehop[s][j][dr].assign(G[dr].size(), -1);
-          for (size_t gi = 0; gi < G[dr].size(); ++gi) {
-            const Group &g = G[dr][gi];
-            if (direct) {
-              // owner -> consumer: rank r's slot s%2 takes shard (r - s - 1)
-              // from its owner's input; WAR: GEMM(s-1, j) read that slot
-              if (s >= 2) wait(g.stream, egemm[s - 1][j]);
-              direct_fetch(g.stream, s, j, g.a, g.b, slot_off(0, s % 2, j, 0), chunk_bytes);
+        auto hops = [&]() {
+          // hops of step s: forward what this step multiplies
+          for (int dr = 0; dr < ndir; ++dr) {
+            if (s >= arcs[dr]) continue;
+            const int shift = dr == 0 ? 1 : -1;
+            ehop[s][j][dr].assign(G[dr].size(), -1);
+            for (size_t gi = 0; gi < G[dr].size(); ++gi) {
+              const Group &g = G[dr][gi];
+              if (direct) {
+                // owner -> consumer: rank r's slot s%2 takes shard (r - s - 1)
+                // from its owner's input; WAR: GEMM(s-1, j) read that slot
+                if (s >= 2) wait(g.stream, egemm[s - 1][j]);
+                direct_fetch(g.stream, s, j, g.a, g.b, slot_off(0, s % 2, j, 0), chunk_bytes);
+                ehop[s][j][dr][gi] = record(g.stream);
+                continue;
+              }
+              // WAR: the destination slot (parity s%2) was read by GEMM(s-1, j)
+              // and, as the source of hop(s-1, j), by the downstream ranks' copies
+              if (s >= 2) {
+                wait(g.stream, egemm[s - 1][j]);
+                for (int r = g.a; r < g.b; ++r) {
+                  int down = group_of(G[dr], mod(r + shift, N));
+                  if (down != (int)gi) wait(g.stream, ehop[s - 1][j][dr][down]);
+                }
+              }
+              // RAW: the source slot was filled by hop(s-1, j) from the upstream ranks
+              if (s >= 1) {
+                for (int r = g.a; r < g.b; ++r) {
+                  int up = group_of(G[dr], mod(r - shift, N));
+                  if (up != (int)gi) { wait(g.stream, ehop[s - 1][j][dr][up]); }
+                }
+              }
+              if (s == 0 && c == 1) {
+                // from the user's shards, which are laid out like the slots: a run of
+                // ranks is one copy (two at the ring's wrap)
+                shifted_copy(g.stream, CM_BUF_X, 0, CM_BUF_WS, slot_off(dr, 0, 0, 0), chunk_bytes, g.a, g.b, shift);
+              } else if (s == 0) {
+                // from the user's shards: rank r's chunk j rows
+                for (int r = g.a; r < g.b; ++r)
+                  copy(g.stream, CM_BUF_X, ((size_t)r * m + (size_t)j * mc) * k * 2, CM_BUF_WS,
+                       slot_off(dr, 0, j, mod(r + shift, N)), chunk_bytes);
+              } else {
+                shifted_copy(g.stream, CM_BUF_WS, slot_off(dr, (s - 1) % 2, j, 0), CM_BUF_WS,
+                             slot_off(dr, s % 2, j, 0), chunk_bytes, g.a, g.b, shift);
+              }
               ehop[s][j][dr][gi] = record(g.stream);
-              continue;
             }
-            // WAR: the destination slot (parity s%2) was read by GEMM(s-1, j)
-            // and, as the source of hop(s-1, j), by the downstream ranks' copies
-            if (s >= 2) {
-              wait(g.stream, egemm[s - 1][j]);
-              for (int r = g.a; r < g.b; ++r) {
-                int down = group_of(G[dr], mod(r + shift, N));
-                if (down != (int)gi) wait(g.stream, ehop[s - 1][j][dr][down]);
-              }
-            }
-            // RAW: the source slot was filled by hop(s-1, j) from the upstream ranks
-            if (s >= 1) {
-              for (int r = g.a; r < g.b; ++r) {
-                int up = group_of(G[dr], mod(r - shift, N));
-                if (up != (int)gi) { wait(g.stream, ehop[s - 1][j][dr][up]); }
-              }
-            }
-            if (s == 0 && c == 1) {
-              // from the user's shards, which are laid out like the slots: a run of
-              // ranks is one copy (two at the ring's wrap)
-              shifted_copy(g.stream, CM_BUF_X, 0, CM_BUF_WS, slot_off(dr, 0, 0, 0), chunk_bytes, g.a, g.b, shift);
-            } else if (s == 0) {
-              // from the user's shards: rank r's chunk j rows
-              for (int r = g.a; r < g.b; ++r)
-                copy(g.stream, CM_BUF_X, ((size_t)r * m + (size_t)j * mc) * k * 2, CM_BUF_WS,
-                     slot_off(dr, 0, j, mod(r + shift, N)), chunk_bytes);
-            } else {
-              shifted_copy(g.stream, CM_BUF_WS, slot_off(dr, (s - 1) % 2, j, 0), CM_BUF_WS,
-                           slot_off(dr, s % 2, j, 0), chunk_bytes, g.a, g.b, shift);
-            }
-            ehop[s][j][dr][gi] = record(g.stream);
           }
-        }
-        // GEMM(s, j) needs hop(s-1, j)
-        if (s >= 1)
-          for (int dr = 0; dr < ndir; ++dr)
-            if (s - 1 < arcs[dr])
-              for (int e : ehop[s - 1][j][dr]) wait(0, e);
-        std::vector<cm_job_rec> jobs;
-        for (int dr = 0; dr < ndir; ++dr) {
-          if (s > 0 && s > arcs[dr]) continue;
-          if (s == 0 && dr > 0) continue;
-          for (int r = 0; r < N; ++r) {
-            cm_job_rec jb = job0();
-            jb.rank = r;
-            jb.dir = dr;
-            int shard = s == 0 ? r : (dr == 0 ? mod(r - s, N) : mod(r + s, N));
-            jb.index = shard;
-            if (s == 0) {
-              jb.a_buf = CM_BUF_X;
-              jb.a_off = ((size_t)r * m + (size_t)j * mc) * k * 2;
-            } else {
-              jb.a_buf = CM_BUF_WS;
-              jb.a_off = slot_off(dr, (s - 1) % 2, j, r);
+        };
+        auto step_gemm = [&]() {
+          // GEMM(s, j) needs hop(s-1, j)
+          if (s >= 1)
+            for (int dr = 0; dr < ndir; ++dr)
+              if (s - 1 < arcs[dr])
+                for (int e : ehop[s - 1][j][dr]) wait(0, e);
+          std::vector<cm_job_rec> jobs;
+          for (int dr = 0; dr < ndir; ++dr) {
+            if (s > 0 && s > arcs[dr]) continue;
+            if (s == 0 && dr > 0) continue;
+            for (int r = 0; r < N; ++r) {
+              cm_job_rec jb = job0();
+              jb.rank = r;
+              jb.dir = dr;
+              int shard = s == 0 ? r : (dr == 0 ? mod(r - s, N) : mod(r + s, N));
+              jb.index = shard;
+              if (s == 0) {
+                jb.a_buf = CM_BUF_X;
+                jb.a_off = ((size_t)r * m + (size_t)j * mc) * k * 2;
+              } else {
+                jb.a_buf = CM_BUF_WS;
+                jb.a_off = slot_off(dr, (s - 1) % 2, j, r);
+              }
+              jb.lda = (int)k;
+              jb.b_buf = CM_BUF_W;
+              jb.b_off = (size_t)r * n * k * 2;
+              jb.ldb = (int)k;
+              jb.c_buf = CM_BUF_Y;
+              jb.c_dtype = d.out_dtype;
+              jb.c_off = ((size_t)r * T + (size_t)shard * m + (size_t)j * mc) * n * (d.out_dtype == CM_F32 ? 4 : 2);
+              jb.ldc = (int)n;
+              jobs.push_back(jb);
             }
-            jb.lda = (int)k;
-            jb.b_buf = CM_BUF_W;
-            jb.b_off = (size_t)r * n * k * 2;
-            jb.ldb = (int)k;
-            jb.c_buf = CM_BUF_Y;
-            jb.c_dtype = d.out_dtype;
-            jb.c_off = ((size_t)r * T + (size_t)shard * m + (size_t)j * mc) * n * (d.out_dtype == CM_F32 ? 4 : 2);
-            jb.ldc = (int)n;
-            jobs.push_back(jb);
           }
+          gemm(jobs, (int)mc, (int)n, (int)k);
+          egemm[s][j] = record(0);
+        };
+        // Step 0's GEMM reads only the user's own shards. It is emitted before
+        // the step's hops so that a graph dispatches it first: emitted after
+        // them, it started 60-120 us late, behind the copies' dispatch
+        if (s == 0) {
+          step_gemm();
+          hops();
+        } else {
+          hops();
+          step_gemm();
         }
-        gemm(jobs, (int)mc, (int)n, (int)k);
-        egemm[s][j] = record(0);
       }
     }
     exit_();
@@ -1266,8 +1280,17 @@ struct Builder {
     const int osz = d.out_dtype == CM_F32 ? 4 : 2;
     std::vector<int> ehop(N, -1), egemm(N, -1);
     entry();
+    // Each step's GEMM is emitted before the step's hop (which it does not
+    // depend on), so that a graph dispatches the GEMM first.
     for (int s = 0; s < N; ++s) {
       cur_step = s;
+      if (s >= 1) wait(0, ehop[s - 1]);  // RAW: the shard this step multiplies
+      const int c = mod(-s, N);
+      if (s == 0)
+        share_gemm(CM_BUF_X, 0, (int)k, 0);
+      else
+        share_gemm(CM_BUF_WS, (size_t)(s % 2) * slot_bytes, (int)k, 0);
+      egemm[s] = record(0);
       if (s + 1 < N) {
         // hop s: the neighbour's shard (N - s - 1) arrives in slot (s + 1) % 2;
         // WAR: GEMM(s - 1) read that slot (step 0 reads rank 0's own shard
@@ -1276,13 +1299,6 @@ struct Builder {
         copy(1, CM_BUF_X, (size_t)mod(-s - 1, N) * m * k * 2, CM_BUF_WS, (size_t)((s + 1) % 2) * slot_bytes, slot_bytes);
         ehop[s] = record(1);
       }
-      if (s >= 1) wait(0, ehop[s - 1]);  // RAW: the shard this step multiplies
-      const int c = mod(-s, N);
-      if (s == 0)
-        share_gemm(CM_BUF_X, 0, (int)k, 0);
-      else
-        share_gemm(CM_BUF_WS, (size_t)(s % 2) * slot_bytes, (int)k, 0);
-      egemm[s] = record(0);
       share_sum(0, 0, CM_BUF_Y, (size_t)c * m * n * osz, (int)n, d.out_dtype, d.act);
     }
     exit_();
@@ -1295,8 +1311,12 @@ struct Builder {
     auto sent = [&](int s) -> size_t { return L.acc + (size_t)s * blk; };
     std::vector<int> ehop(N, -1), esum(N, -1);
     entry();
+    // Each step's GEMM is emitted before the step's hop (which it does not
+    // depend on), so that a graph dispatches the GEMM first.
     for (int s = 0; s < N; ++s) {
       cur_step = s;
+      const int b = mod(-1 - s, N);
+      share_gemm(CM_BUF_X, (size_t)b * m * k * 2, (int)k, 0);
       if (s + 1 < N) {
         // hop s: the bucket for step s + 1 arrives in slot (s + 1) % 2;
         // WAR: the sum of step s - 1 read that slot (step 0's sum reads none)
@@ -1304,8 +1324,6 @@ struct Builder {
         copy(1, CM_BUF_WS, peer(s), CM_BUF_WS, slot((s + 1) % 2), blk);
         ehop[s] = record(1);
       }
-      const int b = mod(-1 - s, N);
-      share_gemm(CM_BUF_X, (size_t)b * m * k * 2, (int)k, 0);
       if (s >= 1) wait(0, ehop[s - 1]);  // RAW: the arrived bucket
       if (s + 1 < N)
         share_sum(s >= 1, slot(s % 2), CM_BUF_WS, sent(s), (int)n, CM_F32, CM_ACT_NONE);
