@@ -133,6 +133,33 @@ def test_hop_add_gemms_do_not_wait_for_the_previous_hop(N):
     assert last_waits == [N - 2]
 
 
+@pytest.mark.parametrize("dir,chunks,n_comm", [("uni", 1, 1), ("uni", 2, 2), ("bi", 1, 2), ("direct", 1, 1)])
+def test_ag_step0_gemm_is_emitted_before_the_hops(dir, chunks, n_comm):
+    """A graph dispatches nodes in program order: step 0's GEMM, which reads
+    only the ranks' own shards, comes before step 0's hop copies of the same
+    chunk (emitted after them, it started behind the copies)."""
+    plan = nat.cm_ring_plan(op="ag", n_ranks=4, m=16, k=64, n=64, dir=dir, chunks=chunks, n_comm=n_comm)
+    ops, jobs = nat.cm_plan_program(plan)
+    for j in range(plan.chunks):
+        idx = [i for i, o in enumerate(ops) if o.step == 0 and o.chunk == j and o.kind in (nat.CM_OPK_GEMM,
+                                                                                          nat.CM_OPK_COPY)]
+        kinds = [ops[i].kind for i in idx]
+        assert kinds[0] == nat.CM_OPK_GEMM and nat.CM_OPK_COPY in kinds, kinds
+        g = ops[idx[0]]
+        assert all(jb.a_buf == nat.CM_BUF_X for jb in jobs[g.first_job:g.first_job + g.n_jobs])
+
+
+@pytest.mark.parametrize("op", ["ag", "rs"])
+def test_share_step_gemm_is_emitted_before_its_hop(op):
+    """One rank's share: every step's GEMM precedes that step's hop in program
+    order (the hop does not depend on it)."""
+    plan = nat.cm_ring_plan(op=op, n_ranks=5, m=16, k=256, n=64, share=1, split_k=2)
+    ops, _ = nat.cm_plan_program(plan)
+    for s in range(4):
+        first = [o.kind for o in ops if o.step == s and o.kind in (nat.CM_OPK_GEMM, nat.CM_OPK_COPY)]
+        assert first == [nat.CM_OPK_GEMM, nat.CM_OPK_COPY], (s, first)
+
+
 PIPE_ADD = [(N, chunks, n_comm, sched) for N in (1, 2, 3, 4, 5, 8) for chunks in (1, 2, 4)
             for n_comm in sorted({1, 2, N}) for sched in ("decomposed", "naive") if sched == "decomposed" or chunks == 1]
 
