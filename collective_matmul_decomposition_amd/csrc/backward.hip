@@ -324,6 +324,20 @@ cm_status cm_linear_backward(const cm_bwd_plan *pl, const void *act, const void 
     if ((e = hipEventRecord(ev[0], S)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     if ((e = hipStreamWaitEvent(B, ev[0], 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
   }
+  // the input gradient: the dual collective matmul with W_r^T [k][n].  It is
+  // enqueued before the weight gradient's operands, which it does not depend
+  // on, so that its first GEMM is dispatched ahead of their copies.
+  const void *wtp = wt;
+  if (!wtp) {
+    if ((e = launch_transpose(w, wt_ws, N, n, k, n, S)) != hipSuccess) return hip_fail(e, "transpose");
+    wtp = wt_ws;
+  }
+  if (col)
+    st = cm_gemm_rs(&pl->dgrad, grad, wtp, dact, ops, opbytes, compute, comm, d.n_comm, nullptr);
+  else
+    st = cm_ag_gemm(&pl->dgrad, grad, wtp, dact, ops, opbytes, compute, comm, d.n_comm, nullptr);
+  if (st != CM_OK) return st;
+
   // COL: dY_r^T [n][Tp]; ROW: H_r^T [k][Tp]
   const void *other = col ? grad : act;
   const int orows = T, ocols = col ? n : k;
@@ -336,18 +350,6 @@ cm_status cm_linear_backward(const cm_bwd_plan *pl, const void *act, const void 
   if (d.bulk) {
     if ((e = hipEventRecord(ev[1], B)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   }
-
-  // the input gradient: the dual collective matmul with W_r^T [k][n]
-  const void *wtp = wt;
-  if (!wtp) {
-    if ((e = launch_transpose(w, wt_ws, N, n, k, n, S)) != hipSuccess) return hip_fail(e, "transpose");
-    wtp = wt_ws;
-  }
-  if (col)
-    st = cm_gemm_rs(&pl->dgrad, grad, wtp, dact, ops, opbytes, compute, comm, d.n_comm, nullptr);
-  else
-    st = cm_ag_gemm(&pl->dgrad, grad, wtp, dact, ops, opbytes, compute, comm, d.n_comm, nullptr);
-  if (st != CM_OK) return st;
 
   // the weight gradient: dW_r [n][k] = (gathered or dY)^T-major operands, K = tokens
   if (d.bulk && (e = hipStreamWaitEvent(S, ev[1], 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
