@@ -251,7 +251,11 @@ cm_status cm_plan_backward(const cm_bwd_desc *desc, cm_bwd_plan *out) {
   a.op = CM_OP_ALLGATHER;
   a.n_ranks = d.n_ranks; a.m = d.m; a.k = d.kind == CM_BWD_COL ? d.k : d.n; a.n = 0;
   a.dir = CM_RING_UNI; a.sched = CM_SCHED_DECOMPOSED; a.in_dtype = CM_BF16; a.out_dtype = CM_BF16;
-  a.n_comm = 1; a.exec_mode = d.exec_mode; a.copy_engine = d.copy_engine;
+  // The gather's copies are one rank's shard each (the gathered arrays are
+  // per rank), which the CU copy kernel moves several times faster than the
+  // SDMA engines; off the SDMA engines it also leaves them to the input
+  // gradient's ring hops.  So it always uses the copy kernel.
+  a.n_comm = 1; a.exec_mode = d.exec_mode; a.copy_engine = CM_COPY_CU;
   if ((st = plan(&a, &p.gather)) != CM_OK) return st;
   if (Tp > 0x7FFFFFFFll || Tp * d.n * 2 > 0xFFFFFFFFll || Tp * d.k * 2 > 0xFFFFFFFFll) {
     set_error("backward: a rank's gathered operand exceeds 4 GiB");

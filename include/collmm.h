@@ -550,7 +550,8 @@ typedef struct {
   int dx_dtype;     /* CM_F32 or CM_BF16: the input gradient */
   int dw_dtype;     /* CM_F32 or CM_BF16: the weight gradient */
   int exec_mode;    /* cm_exec_mode */
-  int copy_engine;  /* cm_copy_engine */
+  int copy_engine;  /* cm_copy_engine of the input gradient's ring hops; the
+                       weight gradient's AllGather always uses CM_COPY_CU */
 } cm_bwd_desc;
 
 typedef struct {

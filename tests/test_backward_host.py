@@ -55,6 +55,12 @@ def test_backward_plans():
         assert p.off_ops >= end and p.ws_bytes == p.off_ops + p.dgrad.ws_bytes
         check_program_bounds(p.dgrad)
         check_program_bounds(p.gather)
+        # the ring hops use the requested engine; the per-rank copies of the
+        # weight gradient's gather always use the copy kernel
+        for ce in ("sdma", "cu"):
+            q = nat.cm_plan_backward(kind=kind, n_ranks=4, m=64, k=256, n=128, copy_engine=ce)
+            assert q.dgrad.desc.copy_engine == nat._ENUMS["copy"][ce]
+            assert q.gather.desc.copy_engine == nat.CM_COPY_CU
     # ragged token count: the weight gradient's operands are padded to 64 tokens
     p = nat.cm_plan_backward(kind="col", n_ranks=3, m=7, k=64, n=128)
     assert p.off_ot - p.off_gt >= 3 * 64 * 64 * 2
