@@ -23,6 +23,7 @@ CM_OPK_GEMM, CM_OPK_COPY, CM_OPK_RECORD, CM_OPK_WAIT, CM_OPK_REDUCE = range(5)
 CM_EXEC_GRAPH, CM_EXEC_EAGER = range(2)
 CM_COPY_SDMA, CM_COPY_CU = range(2)
 CM_ACT_NONE, CM_ACT_GELU = range(2)
+CM_SKIP_NONE, CM_SKIP_HOPS, CM_SKIP_GEMMS = range(3)
 CM_MAX_RANKS, CM_MAX_CHUNKS, CM_MAX_COMM = 64, 16, 32
 
 EXPORTS = ["cm_ring_plan", "cm_pick_overlap", "cm_workspace_size", "cm_plan_program", "cm_trace_create", "cm_trace_destroy",
@@ -39,7 +40,7 @@ class cm_plan_desc(ctypes.Structure):
                 ("copy_engine", ctypes.c_int), ("bucket_bf16", ctypes.c_int), ("hop_add", ctypes.c_int),
                 ("copy_gbps", ctypes.c_double),
                 ("mfma_tflops", ctypes.c_double), ("launch_us", ctypes.c_double), ("act", ctypes.c_int),
-                ("share", ctypes.c_int), ("split_k", ctypes.c_int)]
+                ("share", ctypes.c_int), ("split_k", ctypes.c_int), ("skip", ctypes.c_int)]
 
 
 class cm_plan(ctypes.Structure):
@@ -180,14 +181,17 @@ _ENUMS = {
     "copy": {"sdma": CM_COPY_SDMA, "cu": CM_COPY_CU},
     "hop": {"copy": 0, "add": 1},
     "act": {"none": CM_ACT_NONE, "gelu": CM_ACT_GELU},
+    "skip": {"none": CM_SKIP_NONE, "hops": CM_SKIP_HOPS, "gemms": CM_SKIP_GEMMS},
 }
 
 
 def make_desc(op, n_ranks, m, k, n, dir="uni", chunks=0, sched="decomposed", out_dtype="bf16", n_comm=1,
               tile=(0, 0), exec_mode="graph", copy_engine="sdma", bucket="f32", hop="copy", copy_gbps=0.0,
-              mfma_tflops=0.0, launch_us=0.0, act="none", share=0, split_k=0):
+              mfma_tflops=0.0, launch_us=0.0, act="none", share=0, split_k=0, skip="none"):
     """A cm_plan_desc from keyword arguments (strings or enum values).  share=1:
-    one rank's share (virtual rank 0's steps at real shape, split-K GEMMs)."""
+    one rank's share (virtual rank 0's steps at real shape, split-K GEMMs).
+    skip="hops" / "gemms": a timing-only mode that runs the program with its hops
+    (or its compute-stream launches) replaced by empty operations."""
     def e(kind, v):
         return _ENUMS[kind][v] if isinstance(v, str) else int(v)
     return cm_plan_desc(op=e("op", op), n_ranks=n_ranks, m=m, k=k, n=n, dir=e("dir", dir), chunks=chunks,
@@ -196,7 +200,7 @@ def make_desc(op, n_ranks, m, k, n, dir="uni", chunks=0, sched="decomposed", out
                         copy_engine=e("copy", copy_engine), bucket_bf16=1 if bucket == "bf16" else 0,
                         hop_add=e("hop", hop), copy_gbps=copy_gbps,
                         mfma_tflops=mfma_tflops, launch_us=launch_us, act=e("act", act), share=int(share),
-                        split_k=int(split_k))
+                        split_k=int(split_k), skip=e("skip", skip))
 
 
 def cm_ring_plan(desc=None, **kw):
@@ -252,6 +256,56 @@ def _ptr(t):
     return t.data_ptr()
 
 
+_BF16, _F32 = "bfloat16", "float32"
+
+
+def _dtype_name(dt):
+    return _BF16 if dt == CM_BF16 else _F32
+
+
+def _expect(t, name, elems, dtype):
+    """Host-side check of one tensor argument before a launch: on the GPU,
+    contiguous, of element type `dtype` ("bfloat16" / "float32"), and holding at
+    least `elems` elements (so the kernels stay inside it).  Raw integer device
+    pointers are passed through unchecked."""
+    if t is None or isinstance(t, int):
+        return
+    if getattr(t, "device", None) is None or t.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if str(t.dtype).split(".")[-1] != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.numel() < elems:
+        raise ValueError("%s holds %d elements, the plan needs %d" % (name, t.numel(), elems))
+
+
+def _expect_bytes(t, name, nbytes):
+    if t is None or isinstance(t, int):
+        return
+    if getattr(t, "device", None) is None or t.device.type != "cuda" or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous GPU tensor" % name)
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError("%s holds %d bytes, the plan needs %d" % (name, t.numel() * t.element_size(), nbytes))
+
+
+def _check_plan_tensors(plan, x, w, y, ws):
+    """The layouts of include/collmm.h for cm_ag_gemm / cm_gemm_rs."""
+    d = plan.desc
+    N, m, k, n = d.n_ranks, d.m, d.k, d.n
+    T = N * m
+    R = 1 if d.share else N
+    if d.op == CM_OP_AG_GEMM:
+        xe, ye = N * m * k, R * T * n
+    else:
+        xe, ye = R * T * k, R * m * n
+    _expect(x, "x", xe, _BF16)
+    _expect(w, "w", R * n * k, _BF16)
+    _expect(y, "y", ye, _dtype_name(d.out_dtype))
+    if ws is not None:
+        _expect_bytes(ws, "ws", plan.ws_bytes)
+
+
 def _stream(s):
     if s is None:
         return None
@@ -290,6 +344,7 @@ class Trace:
 
 
 def _call(fn, name, plan, x, w, y, ws, ws_bytes, compute, comm, trace):
+    _check_plan_tensors(plan, x, w, y, ws)
     comm = list(comm or [])
     arr = (ctypes.c_void_p * max(1, len(comm)))(*[_stream(s) for s in comm])
     if ws_bytes is None:
@@ -357,6 +412,13 @@ def cm_plan_layer_status(desc):
 
 def cm_layer_forward(plan, x, wqkv, wo, w1, w2, out, ws, compute, comm, ws_bytes=None):
     """The layer forward through the C ABI."""
+    d = plan.desc
+    N, m, dm, H, D, F = d.n_ranks, d.m, d.d, d.heads, d.head_dim, d.ffn
+    for t, nm, e in ((x, "x", N * m * dm), (wqkv, "wqkv", N * 3 * H * D * dm), (wo, "wo", N * dm * H * D),
+                     (w1, "w1", N * F * dm), (w2, "w2", N * dm * F)):
+        _expect(t, nm, e, _BF16)
+    _expect(out, "out", N * m * dm, _dtype_name(d.out_dtype))
+    _expect_bytes(ws, "ws", plan.ws_bytes)
     comm = list(comm or [])
     arr = (ctypes.c_void_p * max(1, len(comm)))(*[_stream(s) for s in comm])
     if ws_bytes is None:
@@ -368,6 +430,9 @@ def cm_layer_forward(plan, x, wqkv, wo, w1, w2, out, ws, compute, comm, ws_bytes
 # ------------------------------------------------------------ backward
 def cm_allgather(plan, x, y, compute, comm, trace=None):
     """AllGather of the shards x [N, m, k] into y [N, N*m, k] through the C ABI."""
+    d = plan.desc
+    _expect(x, "x", d.n_ranks * d.m * d.k, _BF16)
+    _expect(y, "y", d.n_ranks * d.n_ranks * d.m * d.k, _BF16)
     comm = list(comm or [])
     arr = (ctypes.c_void_p * max(1, len(comm)))(*[_stream(s) for s in comm])
     _check(lib().cm_allgather(ctypes.byref(plan), _ptr(x), _ptr(y), _stream(compute), arr, len(comm),
@@ -421,6 +486,17 @@ def cm_plan_backward_status(desc):
 def cm_linear_backward(plan, act, w, wt, grad, dact, dw, ws, compute, comm, ws_bytes=None):
     """Backward of a collective matmul: comm = the input gradient's n_comm
     streams, then the bulk stream, then the bulk AllGather's copy lane."""
+    d = plan.desc
+    N, m, k, n = d.n_ranks, d.m, d.k, d.n
+    T = N * m
+    col = d.kind == CM_BWD_COL
+    _expect(act, "act", N * (m if col else T) * k, _BF16)
+    _expect(grad, "grad", N * (T if col else m) * n, _BF16)
+    _expect(w, "w", N * n * k, _BF16)
+    _expect(wt, "wt", N * k * n, _BF16)
+    _expect(dact, "dact", N * (m if col else T) * k, _dtype_name(d.dx_dtype))
+    _expect(dw, "dw", N * n * k, _dtype_name(d.dw_dtype))
+    _expect_bytes(ws, "ws", plan.ws_bytes)
     comm = list(comm or [])
     arr = (ctypes.c_void_p * max(1, len(comm)))(*[_stream(s) for s in comm])
     if ws_bytes is None:

@@ -178,7 +178,7 @@ bool same_plan_desc(const cm_plan_desc &a, const cm_plan_desc &b) {
          a.n_comm == b.n_comm && a.tile_m == b.tile_m && a.tile_n == b.tile_n && a.exec_mode == b.exec_mode &&
          a.copy_engine == b.copy_engine && a.bucket_bf16 == b.bucket_bf16 && a.hop_add == b.hop_add &&
          a.copy_gbps == b.copy_gbps && a.mfma_tflops == b.mfma_tflops && a.launch_us == b.launch_us && a.act == b.act &&
-         a.share == b.share && a.split_k == b.split_k;
+         a.share == b.share && a.split_k == b.split_k && a.skip == b.skip;
 }
 bool same_sched(const cm_plan &a, const cm_plan &b) {
   return same_plan_desc(a.desc, b.desc) && a.chunks == b.chunks && a.n_steps == b.n_steps && a.arc_cw == b.arc_cw &&
@@ -310,6 +310,7 @@ cm_status cm_linear_backward(const cm_bwd_plan *pl, const void *act, const void 
       if (comm[i] == comm[j]) { set_error("comm streams %d and %d are the same stream", j, i); return CM_ERR_INVALID_ARG; }
   }
   if ((st = gfx950_current()) != CM_OK) return st;
+  if ((st = refuse_capture(compute, comm, n_comm)) != CM_OK) return st;
   hipEvent_t *ev;
   if ((st = bulk_events(&ev)) != CM_OK) return st;
 

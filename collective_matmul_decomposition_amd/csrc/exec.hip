@@ -14,6 +14,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <cstring>
+#include <list>
 #include <memory>
 #include <mutex>
 #include <string>
@@ -48,6 +49,15 @@ struct Compiled {
   std::vector<Launch> launches;  // one per GEMM / REDUCE op, in op order
   std::vector<int> launch_of_op; // op index -> launches index (-1 if none)
   hipMemcpyKind copy_kind = hipMemcpyDeviceToDeviceNoCU;  // ring hops: SDMA or the CU copy kernel
+  int skip = CM_SKIP_NONE;       // measurement mode: which operations become empty
+  // Is program operation `o` skipped in this plan's measurement mode?  Hops are
+  // the copies and the launches on comm streams; the compute stream's launches
+  // are the GEMMs (and split-K reduces).
+  bool skipped(const cm_op_rec &o) const {
+    if (skip == CM_SKIP_HOPS) return o.kind == CM_OPK_COPY || (o.kind == CM_OPK_REDUCE && o.stream != 0);
+    if (skip == CM_SKIP_GEMMS) return (o.kind == CM_OPK_GEMM || o.kind == CM_OPK_REDUCE) && o.stream == 0;
+    return false;
+  }
 };
 
 std::string plan_key(const cm_plan &p) {
@@ -55,10 +65,10 @@ std::string plan_key(const cm_plan &p) {
   const cm_plan_desc &d = p.desc;
   char buf[512];
   std::snprintf(buf, sizeof buf,
-                "%d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %a %a %a %d %d %d|%d %d %d %d %d %d %d %zu %d",
+                "%d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %a %a %a %d %d %d %d|%d %d %d %d %d %d %d %zu %d",
                 d.op, d.n_ranks, d.m, d.k, d.n, d.dir, d.chunks, d.sched, d.in_dtype, d.out_dtype, d.n_comm, d.tile_m,
                 d.tile_n, d.exec_mode, d.copy_engine, d.bucket_bf16, d.hop_add, d.copy_gbps, d.mfma_tflops,
-                d.launch_us, d.act, d.share, d.split_k, p.chunks, p.n_steps, p.arc_cw, p.arc_ccw, p.tile_m, p.tile_n,
+                d.launch_us, d.act, d.share, d.split_k, d.skip, p.chunks, p.n_steps, p.arc_cw, p.arc_ccw, p.tile_m, p.tile_n,
                 p.n_events, p.ws_bytes, p.split);
   return buf;
 }
@@ -185,9 +195,16 @@ cm_status fill_params(const cm_op_rec &o, const cm_job_rec *jobs, Launch &L) {
 struct GraphEntry {
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
+  hipEvent_t done = nullptr;   // recorded on the compute stream after every launch of the graph
+  const cm_trace *trace = nullptr;
   std::vector<cm_span> spans;  // trace metadata captured with the graph
   bool overflow = false;
+  // Destroying the graph waits only for its own last launch.
   ~GraphEntry() {
+    if (done) {
+      (void)hipEventSynchronize(done);
+      (void)hipEventDestroy(done);
+    }
     if (exec) (void)hipGraphExecDestroy(exec);
     if (graph) (void)hipGraphDestroy(graph);
   }
@@ -195,8 +212,25 @@ struct GraphEntry {
 
 constexpr size_t kMaxGraphs = 256;
 
+// Instantiated graphs, shared by every host thread of the process and
+// evicted least-recently-used first, one at a time.  A graph is keyed by the
+// plan, the buffers and the trace it was built for.
+struct GraphCache {
+  std::mutex mu;
+  std::list<std::string> lru;  // front = most recently used
+  struct Slot {
+    std::unique_ptr<GraphEntry> g;
+    std::list<std::string>::iterator pos;
+  };
+  std::unordered_map<std::string, Slot> map;
+};
+
+GraphCache &graph_cache() {
+  static GraphCache *c = new GraphCache;  // never destroyed: graphs may outlive static destruction order
+  return *c;
+}
+
 struct ThreadState {
-  std::unordered_map<std::string, std::unique_ptr<GraphEntry>> graphs;
   std::unordered_map<std::string, std::unique_ptr<Compiled>> programs;
   std::unordered_map<int, std::vector<hipEvent_t>> events;  // per device
   std::unordered_map<int, int> arch_ok;                     // per device: 1 ok, 0 not gfx950
@@ -221,6 +255,7 @@ cm_status get_compiled(const cm_plan &pl, const Compiled **out) {
   auto c = std::make_unique<Compiled>();
   build_program(canon, c->prog);
   c->copy_kind = canon.desc.copy_engine == CM_COPY_CU ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToDeviceNoCU;
+  c->skip = canon.desc.skip;
   c->launch_of_op.assign(c->prog.ops.size(), -1);
   for (size_t i = 0; i < c->prog.ops.size(); ++i) {
     const cm_op_rec &o = c->prog.ops[i];
@@ -323,8 +358,9 @@ cm_status validate_call(const cm_plan *pl, Entry want, const void *x, const void
   return CM_OK;
 }
 
-// Enqueue the program's operations on the streams (eagerly, or into a
-// graph when the compute stream is capturing).
+// Enqueue the program's operations on the streams, one HIP call each
+// (eager mode).  Calls made while a stream is being captured are refused
+// before this point (refuse_capture).
 cm_status enqueue(const Compiled *cp, const std::vector<hipEvent_t> &ev, char *const base[4],
                   const hipStream_t *streams, cm_trace *trace) {
   hipError_t e;
@@ -364,6 +400,10 @@ cm_status enqueue(const Compiled *cp, const std::vector<hipEvent_t> &ev, char *c
         break;
       case CM_OPK_COPY: {
         int sp = span_begin(o);
+        if (cp->skipped(o)) {
+          span_end(sp, o);
+          break;
+        }
         e = hipMemcpyAsync(base[o.dst_buf] + o.dst_off, base[o.src_buf] + o.src_off, o.bytes,
                            cp->copy_kind, s);
         if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (ring hop)");
@@ -375,6 +415,10 @@ cm_status enqueue(const Compiled *cp, const std::vector<hipEvent_t> &ev, char *c
         GemmParams p = cp->launches[cp->launch_of_op[i]].p;
         for (int b = 0; b < 4; ++b) p.base[b] = base[b];
         int sp = span_begin(o);
+        if (cp->skipped(o)) {
+          span_end(sp, o);
+          break;
+        }
         if (o.kind == CM_OPK_GEMM) {
           const Launch &L = cp->launches[cp->launch_of_op[i]];
           e = launch_gemm(p, L.tm, L.tn, s);
@@ -452,7 +496,11 @@ cm_status build_graph(const Compiled *cp, char *const base[4], int n_streams, cm
       }
     }
     hipGraphNode_t node;
-    if (o.kind == CM_OPK_COPY) {
+    if (cp->skipped(o)) {
+      // the operation's place in the ordering stays; its work does not
+      e = hipGraphAddEmptyNode(&node, graph, frontier[s].data(), frontier[s].size());
+      if (e != hipSuccess) return hip_fail(e, "hipGraphAddEmptyNode");
+    } else if (o.kind == CM_OPK_COPY) {
       e = hipGraphAddMemcpyNode1D(&node, graph, frontier[s].data(), frontier[s].size(), base[o.dst_buf] + o.dst_off,
                                   base[o.src_buf] + o.src_off, o.bytes, cp->copy_kind);
       if (e != hipSuccess) return hip_fail(e, "hipGraphAddMemcpyNode1D (ring hop)");
@@ -509,6 +557,7 @@ cm_status run(const cm_plan *pl, Entry want, const void *x, const void *w, void 
   int dev;
   if ((st = check_device(&dev)) != CM_OK) return st;
   if (trace && trace->device != dev) { set_error("trace was created on another device"); return CM_ERR_INVALID_ARG; }
+  if ((st = refuse_capture(compute, comm, n_comm)) != CM_OK) return st;
   const Compiled *cp;
   if ((st = get_compiled(*pl, &cp)) != CM_OK) return st;
   std::vector<hipEvent_t> *evp;
@@ -522,50 +571,81 @@ cm_status run(const cm_plan *pl, Entry want, const void *x, const void *w, void 
 
   if (pl->desc.exec_mode == CM_EXEC_EAGER) return enqueue(cp, *evp, base, streams, trace);
 
-  ThreadState &ts = tls();
   std::string key = graph_key(*pl, base, trace);
-  auto it = ts.graphs.find(key);
+  GraphCache &gc = graph_cache();
+  std::lock_guard<std::mutex> lock(gc.mu);
+  auto it = gc.map.find(key);
   hipError_t e;
-  if (it == ts.graphs.end()) {
-    if (ts.graphs.size() >= kMaxGraphs) {
-      // Evict every cached graph; a graph launched earlier may still be
-      // executing, so wait for the device before destroying them.
-      if ((e = hipDeviceSynchronize()) != hipSuccess) return hip_fail(e, "hipDeviceSynchronize (graph cache)");
-      ts.graphs.clear();
+  if (it == gc.map.end()) {
+    if (gc.map.size() >= kMaxGraphs) {
+      // evict the least recently used graph (its destructor waits for its last launch)
+      auto victim = gc.map.find(gc.lru.back());
+      gc.lru.pop_back();
+      if (victim != gc.map.end()) gc.map.erase(victim);
     }
     auto g = std::make_unique<GraphEntry>();
+    if ((e = hipEventCreateWithFlags(&g->done, hipEventDisableTiming)) != hipSuccess)
+      return hip_fail(e, "hipEventCreateWithFlags (graph)");
+    g->trace = trace;
     if ((st = build_graph(cp, base, n_comm + 1, trace, g.get())) != CM_OK) return st;
-    it = ts.graphs.emplace(key, std::move(g)).first;
+    gc.lru.push_front(key);
+    GraphCache::Slot slot;
+    slot.g = std::move(g);
+    slot.pos = gc.lru.begin();
+    it = gc.map.emplace(key, std::move(slot)).first;
+  } else {
+    gc.lru.splice(gc.lru.begin(), gc.lru, it->second.pos);
   }
+  GraphEntry *ge = it->second.g.get();
   if (trace) {
-    trace->spans = it->second->spans;
+    trace->spans = ge->spans;
     trace->used = (int)trace->spans.size();
-    trace->overflow = it->second->overflow;
+    trace->overflow = ge->overflow;
   }
-  if ((e = hipGraphLaunch(it->second->exec, streams[0])) != hipSuccess) return hip_fail(e, "hipGraphLaunch");
+  if ((e = hipGraphLaunch(ge->exec, streams[0])) != hipSuccess) return hip_fail(e, "hipGraphLaunch");
+  if ((e = hipEventRecord(ge->done, streams[0])) != hipSuccess) return hip_fail(e, "hipEventRecord (graph)");
   return CM_OK;
 }
 
 }  // namespace
 
-// Graphs that record a trace's events must not outlive the trace.
+// Graphs that record a trace's events must not outlive the trace: drop them
+// in every thread's view (the cache is process-wide), each after its last
+// launch has finished.
 void forget_graphs_of(const cm_trace *t) {
-  char tag[32];
-  std::snprintf(tag, sizeof tag, " %p", (const void *)t);
-  auto &g = tls().graphs;
-  auto ends_with_tag = [&](const std::string &k) {
-    return k.size() >= std::strlen(tag) && k.compare(k.size() - std::strlen(tag), std::string::npos, tag) == 0;
-  };
-  bool any = false;
-  for (const auto &kv : g) any = any || ends_with_tag(kv.first);
-  if (!any) return;
-  (void)hipDeviceSynchronize();  // a launch of one of these graphs may still be running
-  for (auto it = g.begin(); it != g.end();) {
-    if (ends_with_tag(it->first))
-      it = g.erase(it);
-    else
+  GraphCache &gc = graph_cache();
+  std::lock_guard<std::mutex> lock(gc.mu);
+  for (auto it = gc.map.begin(); it != gc.map.end();) {
+    if (it->second.g->trace == t) {
+      gc.lru.erase(it->second.pos);
+      it = gc.map.erase(it);
+    } else {
       ++it;
+    }
   }
+}
+
+// Calls made while the compute stream or a comm stream is being captured
+// into a graph are refused: the programs are multi-stream, and the library
+// builds its own graphs node by node instead of through stream capture.
+cm_status refuse_capture(void *compute, void *const *comm, int n_comm) {
+  auto capturing = [](void *s, bool *out) -> cm_status {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(static_cast<hipStream_t>(s), &cs);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+    *out = cs != hipStreamCaptureStatusNone;
+    return CM_OK;
+  };
+  bool cap = false;
+  cm_status st = capturing(compute, &cap);
+  for (int i = 0; st == CM_OK && !cap && comm && i < n_comm; ++i) st = capturing(comm[i], &cap);
+  if (st != CM_OK) return st;
+  if (cap) {
+    set_error("a stream passed to the call is being captured into a graph; stream capture is not supported "
+              "(the library builds and caches its own graphs)");
+    return CM_ERR_UNSUPPORTED;
+  }
+  return CM_OK;
 }
 
 }  // namespace collmm

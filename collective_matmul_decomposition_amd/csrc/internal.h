@@ -33,5 +33,8 @@ cm_status validate_desc(const cm_plan_desc &d);
 cm_status plan(const cm_plan_desc *desc, cm_plan *out);
 WsLayout ws_layout(const cm_plan &p);
 void build_program(const cm_plan &p, Program &prog);
+// CM_ERR_UNSUPPORTED if the compute stream or a comm stream is being
+// captured into a graph (executor; streams are hipStream_t passed as void*).
+cm_status refuse_capture(void *compute, void *const *comm, int n_comm);
 
 }  // namespace collmm

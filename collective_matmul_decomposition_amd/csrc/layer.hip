@@ -409,7 +409,7 @@ bool same_desc(const cm_plan_desc &a, const cm_plan_desc &b) {
          a.n_comm == b.n_comm && a.tile_m == b.tile_m && a.tile_n == b.tile_n && a.exec_mode == b.exec_mode &&
          a.copy_engine == b.copy_engine && a.bucket_bf16 == b.bucket_bf16 && a.hop_add == b.hop_add &&
          a.copy_gbps == b.copy_gbps && a.mfma_tflops == b.mfma_tflops && a.launch_us == b.launch_us && a.act == b.act &&
-         a.share == b.share && a.split_k == b.split_k;
+         a.share == b.share && a.split_k == b.split_k && a.skip == b.skip;
 }
 bool same_plan(const cm_plan &a, const cm_plan &b) {
   return same_desc(a.desc, b.desc) && a.chunks == b.chunks && a.n_steps == b.n_steps && a.arc_cw == b.arc_cw &&
@@ -599,6 +599,7 @@ cm_status cm_layer_forward(const cm_layer_plan *pl, const void *x, const void *w
     set_error("workspace of %zu bytes, layer plan needs %zu", ws_bytes, pl->ws_bytes);
     return CM_ERR_WORKSPACE;
   }
+  if ((st = refuse_capture(compute, comm, n_comm)) != CM_OK) return st;
   const cm_layer_desc &d = pl->desc;
   char *w = static_cast<char *>(ws);
   char *qkv = w + pl->off_qkv, *attn = w + pl->off_attn, *proj = w + pl->off_proj, *ln = w + pl->off_ln,

@@ -136,6 +136,22 @@ typedef enum { CM_EXEC_GRAPH = 0, CM_EXEC_EAGER = 1 } cm_exec_mode;
  */
 typedef enum { CM_COPY_SDMA = 0, CM_COPY_CU = 1 } cm_copy_engine;
 
+/*
+ * Measurement modes: what a trace of the parts alone needs in order to set the
+ * decomposed time against them ("Hiding Tensor-Parallel Collectives", section 9:
+ * a step is judged against its compute and its communication, each timed on
+ * its own).  The program is unchanged -- the same launches, copies and
+ * ordering edges -- but one class of its operations is replaced by an empty
+ * operation:
+ *   CM_SKIP_HOPS   every hop is skipped (copies, and the add launches that run
+ *                  on comm streams): the op's GEMM time alone, "G";
+ *   CM_SKIP_GEMMS  every launch on the compute stream is skipped (the partial
+ *                  GEMMs and split-K reduces): the op's hop time alone, "C".
+ * The outputs of a call in either mode are meaningless (not computed); the
+ * mode is for timing only.  CM_SKIP_NONE runs the operation.
+ */
+typedef enum { CM_SKIP_NONE = 0, CM_SKIP_HOPS = 1, CM_SKIP_GEMMS = 2 } cm_skip;
+
 #define CM_MAX_RANKS 64
 #define CM_MAX_CHUNKS 16
 #define CM_MAX_COMM 32
@@ -153,7 +169,10 @@ typedef struct {
   int sched;     /* cm_sched */
   int in_dtype;  /* CM_BF16 */
   int out_dtype; /* CM_F32 or CM_BF16 */
-  int n_comm;    /* number of comm streams the calls will pass, 1..CM_MAX_COMM */
+  int n_comm;    /* number of comm streams the calls will pass, 1..CM_MAX_COMM;
+                    a program puts hops on at most three of them (with the
+                    compute stream, the four hardware queues a process has by
+                    default) */
   int tile_m;    /* GEMM block tile: 0 x 0 = choose per launch, else one of */
   int tile_n;    /* 256x256, 256x192, 256x128, 128x256, 128x128, 64x256 */
   int exec_mode; /* cm_exec_mode: how the calls enqueue the program */
@@ -194,6 +213,7 @@ typedef struct {
                             split into (0 = choose: enough slices for the step's
                             tiles to fill the chip, at least 8 slabs of 64 each);
                             must divide k/64, at most 16 */
+  int skip;              /* cm_skip: a measurement mode (0 = normal) */
 } cm_plan_desc;
 
 /* The resolved schedule.  Plain data: no heap, nothing to destroy. */
@@ -264,8 +284,8 @@ cm_status cm_workspace_size(const cm_plan *plan, size_t *bytes);
 
 /*
  * Pick one of two collectives to decompose ("Knowing when to decline" on the
- * decomposition page: the cost model "picks which of two candidate
- * collectives to overlap when an Einsum offers both").  An einsum whose
+ * decomposition page: when an einsum could overlap either of two collectives,
+ * the cost model chooses between them).  An einsum whose
  * input is all-gathered and whose output is reduce-scattered can overlap only
  * one of them with its partial products.  `ag` describes the AllGather-side
  * candidate (op CM_OP_AG_GEMM) and `rs` the ReduceScatter-side candidate (op

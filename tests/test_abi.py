@@ -146,3 +146,49 @@ def test_trace_argument_checks():
     h = ctypes.c_void_p()
     assert lib.cm_trace_create(0, ctypes.byref(h)) == nat.CM_ERR_INVALID_ARG
     assert lib.cm_trace_destroy(None) == nat.CM_OK
+
+
+class _FakeTensor:
+    """Stands in for a torch tensor on the GPU (the checks run before any call)."""
+
+    def __init__(self, numel, dtype="bfloat16", contiguous=True, device="cuda"):
+        self._n, self.dtype, self._c = numel, "torch." + dtype, contiguous
+        self.device = type("D", (), {"type": device})()
+
+    def numel(self):
+        return self._n
+
+    def element_size(self):
+        return {"bfloat16": 2, "float16": 2, "float32": 4, "uint8": 1}[self.dtype.split(".")[-1]]
+
+    def is_contiguous(self):
+        return self._c
+
+    def data_ptr(self):
+        raise AssertionError("the library must not be called")
+
+
+@pytest.mark.parametrize("bad", ["x_small", "w_dtype", "y_small", "y_dtype", "ws_small", "noncontig", "cpu"])
+def test_binding_rejects_bad_tensors_before_calling(bad):
+    """Tensor arguments are checked against the plan's layout on the host, so a
+    buffer that is too small becomes a Python error, not out-of-bounds writes."""
+    N, m, k, n = 4, 16, 64, 128
+    plan = nat.cm_ring_plan(op="ag", n_ranks=N, m=m, k=k, n=n, out_dtype="f32")
+    args = dict(x=_FakeTensor(N * m * k), w=_FakeTensor(N * n * k), y=_FakeTensor(N * N * m * n, "float32"),
+                ws=_FakeTensor(max(1, plan.ws_bytes), "uint8"))
+    if bad == "x_small":
+        args["x"] = _FakeTensor(N * m * k - 1)
+    elif bad == "w_dtype":
+        args["w"] = _FakeTensor(N * n * k, "float16")
+    elif bad == "y_small":
+        args["y"] = _FakeTensor(N * N * m * n - 8, "float32")
+    elif bad == "y_dtype":
+        args["y"] = _FakeTensor(N * N * m * n, "bfloat16")
+    elif bad == "ws_small":
+        args["ws"] = _FakeTensor(plan.ws_bytes - 1, "uint8")
+    elif bad == "noncontig":
+        args["x"] = _FakeTensor(N * m * k, contiguous=False)
+    elif bad == "cpu":
+        args["w"] = _FakeTensor(N * n * k, device="cpu")
+    with pytest.raises(ValueError):
+        nat.cm_ag_gemm(plan, args["x"], args["w"], args["y"], args["ws"], None, [])

@@ -459,3 +459,49 @@ def test_gpu_test_programs_stay_in_bounds():
     for kw in _gpu_cases():
         plan = nat.cm_ring_plan(**kw)
         check_program_bounds(plan)
+
+
+# ------------------------------------------------------------ measurement modes and lanes
+@pytest.mark.parametrize("op,dir,hop", [("ag", "uni", "copy"), ("ag", "bi", "copy"), ("rs", "uni", "add"),
+                                        ("rs", "bi", "copy"), ("rs_pipe", "uni", "add")])
+@pytest.mark.parametrize("skip", ["hops", "gemms"])
+def test_skip_modes_keep_the_program(op, dir, hop, skip):
+    """The G-alone / C-alone modes run the same program (same launches, copies
+    and ordering edges); the executor only empties one class of operations."""
+    kw = dict(op=op, n_ranks=5, m=32, k=128, n=256, dir=dir, chunks=2, out_dtype="f32", n_comm=2,
+              hop=hop if op != "ag" else "copy")
+    base = nat.cm_ring_plan(**kw)
+    meas = nat.cm_ring_plan(skip=skip, **kw)
+    assert meas.desc.skip == nat._ENUMS["skip"][skip]
+    ops0, jobs0 = nat.cm_plan_program(base)
+    ops1, jobs1 = nat.cm_plan_program(meas)
+    key = lambda o: (o.kind, o.stream, o.event, o.step, o.chunk, o.first_job, o.n_jobs, o.rows, o.cols, o.depth,
+                     o.src_buf, o.dst_buf, o.src_off, o.dst_off, o.bytes)
+    assert [key(o) for o in ops0] == [key(o) for o in ops1]
+    assert (base.n_ops, base.n_jobs, base.n_events, base.ws_bytes) == (meas.n_ops, meas.n_jobs, meas.n_events,
+                                                                      meas.ws_bytes)
+    # each mode empties something, and not everything
+    hops = [o for o in ops1 if o.kind == nat.CM_OPK_COPY or (o.kind == nat.CM_OPK_REDUCE and o.stream != 0)]
+    gemms = [o for o in ops1 if o.kind in (nat.CM_OPK_GEMM, nat.CM_OPK_REDUCE) and o.stream == 0]
+    assert hops and gemms
+
+
+def test_unknown_skip_mode_is_rejected():
+    st, _ = nat.cm_ring_plan_status(nat.make_desc("ag", 4, 16, 64, 64, skip=3))
+    assert st == nat.CM_ERR_INVALID_ARG
+    st, _ = nat.cm_ring_plan_status(nat.make_desc("allgather", 4, 16, 64, 0, skip=-1))
+    assert st == nat.CM_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("op,dir", [("ag", "uni"), ("ag", "bi"), ("rs", "uni"), ("rs", "bi"), ("rs", "direct"),
+                                    ("rs_pipe", "uni")])
+@pytest.mark.parametrize("n_comm", [4, 8, 16])
+def test_programs_use_at_most_three_comm_lanes(op, dir, n_comm):
+    """A process has four hardware queues by default: the compute stream plus at
+    most three comm lanes run side by side.  Streams beyond three are accepted
+    and left idle, and the program still equals the oracle."""
+    plan, sim, a, w = simulate(op, 8, 16, 128, 256, dir=dir, chunks=2, n_comm=n_comm)
+    ops, _ = nat.cm_plan_program(plan)
+    work = {o.stream for o in ops if o.kind in (nat.CM_OPK_COPY, nat.CM_OPK_REDUCE, nat.CM_OPK_GEMM)}
+    assert max(work) <= 3
+    assert np.array_equal(output(sim, plan), expect("ag" if op == "ag" else "rs", a, w, "f32"))
