@@ -29,7 +29,8 @@ CM_MAX_RANKS, CM_MAX_CHUNKS, CM_MAX_COMM = 64, 16, 32
 EXPORTS = ["cm_ring_plan", "cm_pick_overlap", "cm_workspace_size", "cm_plan_program", "cm_trace_create", "cm_trace_destroy",
            "cm_trace_read", "cm_ag_gemm", "cm_gemm_rs", "cm_attention", "cm_layernorm", "cm_plan_layer",
            "cm_layer_forward", "cm_allgather", "cm_transpose", "cm_gemm", "cm_plan_backward", "cm_linear_backward",
-           "cm_status_string", "cm_last_error", "cm_version"]
+           "cm_gemm_rs_noalloc", "cm_status_string", "cm_last_error", "cm_version"]
+CM_NOALLOC_WS_BYTES = 256 << 20
 
 
 class cm_plan_desc(ctypes.Structure):
@@ -125,6 +126,7 @@ def lib():
         L.cm_trace_read.argtypes = [vp, ctypes.POINTER(cm_span), ci, ctypes.POINTER(ci), ctypes.POINTER(ctypes.c_double)]
         for f in (L.cm_ag_gemm, L.cm_gemm_rs):
             f.argtypes = [ctypes.POINTER(cm_plan), vp, vp, vp, vp, cs, vp, ctypes.POINTER(vp), ci, vp]
+        L.cm_gemm_rs_noalloc.argtypes = [ctypes.POINTER(cm_plan), vp, vp, vp, vp, ctypes.POINTER(vp), ci]
         L.cm_attention.argtypes = [vp, vp, ci, ci, ci, ci, ci, vp]
         L.cm_layernorm.argtypes = [vp, vp, ci, ci, ctypes.c_float, vp, vp, vp]
         L.cm_plan_layer.argtypes = [ctypes.POINTER(cm_layer_desc), ctypes.POINTER(cm_layer_plan)]
@@ -362,6 +364,22 @@ def cm_ag_gemm(plan, x, w, y, ws, compute, comm, trace=None, ws_bytes=None):
 def cm_gemm_rs(plan, x, w, y, ws, compute, comm, trace=None, ws_bytes=None):
     """GEMM -> ReduceScatter through the C ABI (tensors or raw device pointers)."""
     _call(lib().cm_gemm_rs, "cm_gemm_rs", plan, x, w, y, ws, ws_bytes, compute, comm, trace)
+
+
+def cm_gemm_rs_noalloc(plan, x, w, y, compute, comm):
+    """GEMM -> ReduceScatter with the library's static workspace (no allocation)."""
+    _check_plan_tensors(plan, x, w, y, None)
+    comm = list(comm or [])
+    arr = (ctypes.c_void_p * max(1, len(comm)))(*[_stream(s) for s in comm])
+    _check(lib().cm_gemm_rs_noalloc(ctypes.byref(plan), _ptr(x), _ptr(w), _ptr(y), _stream(compute), arr, len(comm)),
+           "cm_gemm_rs_noalloc")
+
+
+def cm_gemm_rs_noalloc_status(plan, x=None, w=None, y=None, compute=None, comm=None):
+    """Status code of cm_gemm_rs_noalloc without raising (for error-path tests)."""
+    comm = list(comm or [])
+    arr = (ctypes.c_void_p * max(1, len(comm)))(*[_stream(s) for s in comm])
+    return lib().cm_gemm_rs_noalloc(ctypes.byref(plan), _ptr(x), _ptr(w), _ptr(y), _stream(compute), arr, len(comm))
 
 
 # ------------------------------------------------------------ the layer

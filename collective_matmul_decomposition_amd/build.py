@@ -21,7 +21,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 instructions are disabled for all device code (no v_pk_*_f32).
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I" + INCLUDE, "-I" + CSRC]
 DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-SOURCES = [("plan.cpp", False), ("exec.hip", True), ("kernels.hip", True), ("layer.hip", True), ("backward.hip", True)]
+SOURCES = [("plan.cpp", False), ("exec.hip", True), ("kernels.hip", True), ("layer.hip", True), ("backward.hip", True),
+           ("noalloc.hip", True)]
 
 
 def _compile(src, is_hip):

@@ -608,6 +608,27 @@ cm_status cm_linear_backward(const cm_bwd_plan *plan, const void *act, const voi
                              const void *grad, void *dact, void *dw, void *ws, size_t ws_bytes, void *compute,
                              void *const *comm, int n_comm);
 
+/*
+ * For callers that cannot allocate device memory (code a caller captures into
+ * a graph, tight serving loops, harnesses that forbid hipMalloc): cm_gemm_rs
+ * with its workspace taken from a static array the library holds on each GPU
+ * (CM_NOALLOC_WS_BYTES bytes, allocated when the library's code object is
+ * loaded on that GPU and held until the process ends), instead of the
+ * caller's `ws`.  Arguments, layouts, ordering and results are those of
+ * cm_gemm_rs; the program is always enqueued op by op (exec_mode is taken as
+ * CM_EXEC_EAGER, since instantiating a graph may allocate) and no trace is
+ * recorded.  Nothing in the array has to start at zero: every program writes
+ * each bucket and partial slot before it reads it.  The call allocates no
+ * memory (no hipMalloc, no hipFree).  All calls on one GPU share that GPU's
+ * array: two calls whose work overlaps in time on one GPU (on different
+ * streams, or from different threads) race on it.
+ * Errors: those of cm_gemm_rs; CM_ERR_WORKSPACE if plan->ws_bytes exceeds
+ * CM_NOALLOC_WS_BYTES.
+ */
+#define CM_NOALLOC_WS_BYTES ((size_t)256 << 20)
+cm_status cm_gemm_rs_noalloc(const cm_plan *plan, const void *x, const void *w, void *y, void *compute,
+                             void *const *comm, int n_comm);
+
 const char *cm_status_string(cm_status s);
 /* Detail of the last failing call on this thread ("" if none). */
 const char *cm_last_error(void);
