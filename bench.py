@@ -115,11 +115,16 @@ def measure(args, workload, steps, warmup, with_naive, with_trace):
     m, fN = T // N, f // N
     n_comm = args.n_comm
     tile = tuple(int(v) for v in args.tile.split("x"))
-    plan_ag = nat.cm_ring_plan(op="ag", n_ranks=N, m=m, k=d, n=fN, dir=args.dir, chunks=args.chunks_ag,
-                               out_dtype="bf16", n_comm=n_comm, tile=tile, copy_engine=args.copy_engine)
-    plan_rs = nat.cm_ring_plan(op=args.rs_op, n_ranks=N, m=m, k=fN, n=d, dir=args.dir, chunks=args.chunks_rs,
-                               out_dtype="bf16", n_comm=n_comm, tile=tile, copy_engine=args.copy_engine,
-                               bucket=args.rs_bucket, hop=rs_hop(args))
+
+    def make_plans(skip="none"):
+        pa = nat.cm_ring_plan(op="ag", n_ranks=N, m=m, k=d, n=fN, dir=args.dir, chunks=args.chunks_ag,
+                              out_dtype="bf16", n_comm=n_comm, tile=tile, copy_engine=args.copy_engine, skip=skip)
+        pr = nat.cm_ring_plan(op=args.rs_op, n_ranks=N, m=m, k=fN, n=d, dir=args.dir, chunks=args.chunks_rs,
+                              out_dtype="bf16", n_comm=n_comm, tile=tile, copy_engine=args.copy_engine,
+                              bucket=args.rs_bucket, hop=rs_hop(args), skip=skip)
+        return pa, pr
+
+    plan_ag, plan_rs = make_plans()
     log("%s plans: AG chunks=%d tile=%dx%d ws=%.0fMB | RS(%s) chunks=%d tile=%dx%d ws=%.0fMB | n_comm=%d" % (
         workload, plan_ag.chunks, plan_ag.tile_m, plan_ag.tile_n, plan_ag.ws_bytes / 1e6, args.rs_op,
         plan_rs.chunks, plan_rs.tile_m, plan_rs.tile_n, plan_rs.ws_bytes / 1e6, n_comm))
@@ -235,12 +240,47 @@ def measure(args, workload, steps, warmup, with_naive, with_trace):
             elt = 2 if name == "ag" or args.rs_bucket == "bf16" else 4
             ring_bytes = N * (N - 1) * m * d * elt
             ov[name] = {"decomposed_us": round(D, 1), "gemm_busy_us": round(G, 1), "hop_busy_us": round(C, 1),
-                        "overlap_efficiency": round(D / max(G, C), 3),
-                        "hidden_fraction": round((G + C - D) / C, 3) if C > 0 else None,
+                        "overlap_efficiency_inrun": round(D / max(G, C), 3),
+                        "hidden_fraction_inrun": round((G + C - D) / C, 3) if C > 0 else None,
                         "tflops": round(flops_op / (D * 1e-6) / 1e12, 1), "ring_bytes": ring_bytes,
                         "hop_GBps": round(ring_bytes / (C * 1e-6) / 1e9, 1) if C > 0 else None,
                         "chunks": plan.chunks}
         res["overlap"] = ov
+
+        # G and C alone: the same programs (same launches, copies and edges)
+        # with the hops, or the compute-stream launches, replaced by empty
+        # operations, timed per op inside alternating AG/RS steps as D is
+        alone = {"ag": {}, "rs": {}}
+        reps = max(5, steps // 2)
+        for skip in ("hops", "gemms"):
+            pa, pr = make_plans(skip)
+            tr = [(nat.Trace(cap_ag), nat.Trace(cap_rs)) for _ in range(reps)]
+            for _ in range(2):  # the first round builds each trace's graphs
+                for ta, tb in tr:
+                    step(ta, tb, pa, pr)
+                torch.cuda.synchronize()
+            for name, i in (("ag", 0), ("rs", 1)):
+                alone[name][skip] = float(np.median([t[i].read()[1] for t in tr]))
+            for ta, tb in tr:
+                ta.close()
+                tb.close()
+        for name, plan in (("ag", plan_ag), ("rs", plan_rs)):
+            o = ov[name]
+            D, Ga, Ca = o["decomposed_us"], alone[name]["hops"], alone[name]["gemms"]
+            elt = 2 if name == "ag" or args.rs_bucket == "bf16" else 4
+            # overlap efficiency = D / max(GEMM-only, copy-only); hidden
+            # fraction = (G + C - D) / C, with G and C the op's parts alone
+            o.update({"gemm_alone_us": round(Ga, 1), "copy_alone_us": round(Ca, 1),
+                      "bound_by": "gemm" if Ga >= Ca else "copy",
+                      "overlap_efficiency": round(D / max(Ga, Ca), 3),
+                      "hidden_fraction": round((Ga + Ca - D) / Ca, 3) if Ca > 0 else None,
+                      # each hop byte is read and written once in HBM
+                      "hop_GBps_alone": round(o["ring_bytes"] / (Ca * 1e-6) / 1e9, 1) if Ca > 0 else None,
+                      "hop_hbm_frac_alone": round(2 * o["ring_bytes"] / (Ca * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)
+                      if Ca > 0 else None})
+            log("%s alone: G %.1f us (hops skipped), C %.1f us (GEMMs skipped), D %.1f us -> D/max(G,C) %.3f, "
+                "hidden (G+C-D)/C %.3f" % (name, Ga, Ca, D, o["overlap_efficiency"],
+                                            o["hidden_fraction"] or 0.0))
 
     if with_naive:
         pa = nat.cm_ring_plan(op="ag", n_ranks=N, m=m, k=d, n=fN, sched="naive", out_dtype="bf16", n_comm=n_comm,
@@ -316,14 +356,15 @@ def measure(args, workload, steps, warmup, with_naive, with_trace):
                 # ring's own hops, whose busy time beside the GEMMs bounds
                 # theirs alone from above; the smaller of the two
                 Ca = min(Cn, ov["hop_busy_us"])
-                ov["overlap_efficiency_busy"] = ov["overlap_efficiency"]
-                ov.update({"gemm_only_us": round(Ga, 1), "naive_collective_us": round(Cn, 1),
-                           "copy_only_us": round(Ca, 1), "overlap_efficiency": round(D / max(Ga, Ca), 3),
-                           "bound_by": "gemm" if Ga >= Ca else "copy"})
-                log("%s: decomposed %.1f us; GEMM-only %.1f us, copy-only %.1f us (naive collective %.1f) -> "
+                ov.update({"monolithic_gemm_us": round(Ga, 1), "naive_collective_us": round(Cn, 1),
+                           "overlap_efficiency_vs_naive": round(D / max(Ga, Ca), 3)})
+                if "gemm_alone_us" in ov:
+                    # the cost of cutting the GEMM into per-step partial GEMMs: G / M
+                    ov["g_over_m"] = round(ov["gemm_alone_us"] / Ga, 3)
+                log("%s: decomposed %.1f us; monolithic GEMM %.1f us, copy-only %.1f us (naive collective %.1f) -> "
                     "efficiency %.3f (in-run busy: GEMM %.1f, hops %.1f -> %.3f)" % (
-                        name, D, Ga, Ca, Cn, ov["overlap_efficiency"], ov["gemm_busy_us"], ov["hop_busy_us"],
-                        ov["overlap_efficiency_busy"]))
+                        name, D, Ga, Ca, Cn, ov["overlap_efficiency_vs_naive"], ov["gemm_busy_us"], ov["hop_busy_us"],
+                        ov["overlap_efficiency_inrun"]))
         del yn1, wsn1, yn2, wsn2
     return res
 
@@ -704,9 +745,24 @@ def sampled_parity(res, rs_bucket="f32"):
     return {"ag": round(worst_ag, 4), "rs": round(worst_rs, 4)}, (xa, w1a, ha, w2a)
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(res, arrays, seconds):
+    """The oracle timed on the host's cores on a row sample of the step; then
+    the same rows (with the |a||b| magnitudes, untimed) are checked against
+    the GPU's step output."""
     import oracle
+    from collective_matmul_decomposition_amd import inputs as gen
     xa, w1a, ha, w2a = arrays
+    x, w1, y1, h, w2, y2 = res["tensors"]
     N, T, m, d, fN = res["N"], res["T"], res["m"], res["d"], res["fN"]
     rng = np.random.default_rng(1)
     cores = oracle.threads()
@@ -714,19 +770,34 @@ def cpu_baseline(res, arrays, seconds):
     oracle.ag_gemm_rows(xa, w1a, np.zeros(cores, np.int32), np.arange(cores, dtype=np.int32))
     per_row = (time.perf_counter() - t0) / cores
     rows_ag = int(max(cores, min(N * T, seconds / max(per_row, 1e-9))))
-    sel = rng.choice(N * T, rows_ag, replace=False)
+    sel_ag = rng.choice(N * T, rows_ag, replace=False)
+    ra, rr = (sel_ag // T).astype(np.int32), (sel_ag % T).astype(np.int32)
     t0 = time.perf_counter()
-    oracle.ag_gemm_rows(xa, w1a, (sel // T).astype(np.int32), (sel % T).astype(np.int32))
+    ref_ag = oracle.ag_gemm_rows(xa, w1a, ra, rr)
     t_ag = time.perf_counter() - t0
     rows_rs = max(cores, rows_ag // N)
     sel = rng.choice(N * m, min(rows_rs, N * m), replace=False)
+    qo, qr = (sel // m).astype(np.int32), (sel % m).astype(np.int32)
     t0 = time.perf_counter()
-    oracle.gemm_rs_rows(ha, w2a, (sel // m).astype(np.int32), (sel % m).astype(np.int32))
+    ref_rs = oracle.gemm_rs_rows(ha, w2a, qo, qr)
     t_rs = time.perf_counter() - t0
     fl = 2.0 * rows_ag * d * fN + 2.0 * len(sel) * N * fN * d
+    # parity of the same rows: |gpu - oracle| <= 1e-5 * sum|a||b| + 2^-8 |oracle| (bf16 outputs)
+    _, mag_ag = oracle.ag_gemm_rows(xa, w1a, ra, rr, with_mag=True)
+    _, mag_rs = oracle.gemm_rs_rows(ha, w2a, qo, qr, with_mag=True)
+    got_ag = gen.bf16_bits_to_f32(gen.torch_bf16_to_bits(y1)[ra, rr]).astype(np.float64)
+    got_rs = gen.bf16_bits_to_f32(gen.torch_bf16_to_bits(y2)[qo, qr]).astype(np.float64)
+    w_ag = float((np.abs(got_ag - ref_ag) / (1e-5 * mag_ag + 2.0 ** -8 * np.abs(ref_ag))).max())
+    w_rs = float((np.abs(got_rs - ref_rs) / (1e-5 * mag_rs + 2.0 ** -8 * np.abs(ref_rs))).max())
+    log("cpu baseline: %d AG + %d RS rows in %.1f s on %d cores; their parity err/bound: AG %.4f, RS %.4f" % (
+        rows_ag, len(sel), t_ag + t_rs, cores, w_ag, w_rs))
     return {"value": round(fl / (t_ag + t_rs) / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": "%d of %d AG output rows and %d of %d RS output rows of the step (fp64, all %d rank "
-                      "contributions each), %.1f s" % (rows_ag, N * T, len(sel), N * m, N, t_ag + t_rs)}
+                      "contributions each), %.1f s" % (rows_ag, N * T, len(sel), N * m, N, t_ag + t_rs),
+            "parity": {"ag_rows": rows_ag, "rs_rows": int(len(sel)), "max_err_over_bound_ag": round(w_ag, 4),
+                       "max_err_over_bound_rs": round(w_rs, 4),
+                       "passed": bool(w_ag <= 1.0 and w_rs <= 1.0)}}
 
 
 def main():
@@ -755,6 +826,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
     ap.add_argument("--no-naive", action="store_true")
+    ap.add_argument("--no-bi", action="store_true", help="skip the run on the bidirectional ring")
     ap.add_argument("--no-layer", action="store_true", help="skip the sequence-parallel layer forward")
     ap.add_argument("--no-share", action="store_true", help="skip one rank's share (rank 0's steps at real shape)")
     ap.add_argument("--no-backward", action="store_true", help="skip the MLP backward (bulk overlap)")
@@ -830,6 +902,17 @@ def main():
                    "gemm_launches": rh.get("gemm_launches")}
         del rh
         torch.cuda.empty_cache()
+    bi = None
+    if not args.no_bi and args.dir != "bi":
+        # the same step on the bidirectional ring
+        bi_args = argparse.Namespace(**vars(args))
+        bi_args.dir = "bi"
+        rb = measure(bi_args, args.workload, args.steps, args.warmup, False, not args.no_trace)
+        bi = {"ring": "bi", "value": round(rb["value"], 2), "unit": "TFLOP/s", "ms_per_step": round(rb["ms_per_step"], 4),
+              "pct_of_bf16_peak": round(100 * rb["value"] / PEAK_BF16_TFLOPS, 2), "overlap": rb.get("overlap"),
+              "gemm_launches": rb.get("gemm_launches")}
+        del rb
+        torch.cuda.empty_cache()
     secondary = None
     if args.secondary != "none" and args.secondary != args.workload:
         s2 = measure(args, args.secondary, max(5, args.steps // 2), 2, not args.no_naive, not args.no_trace)
@@ -881,6 +964,7 @@ def main():
         "gemm_launches": res.get("gemm_launches"),
         "naive": res.get("naive"),
         "parity_sampled_err_over_bound": parity,
+        "bi": bi,
         "alt_copy_engine": alt,
         "alt_rs_bucket": alt_bucket,
         "alt_rs_hop": alt_hop,

@@ -1,4 +1,5 @@
-"""Dataflow check of inline-asm vector loads in gfx950 assembly.
+"""Dataflow check of inline-asm vector loads in gfx950 assembly (run by the
+build on every compile of the GEMM kernels, and by the tests).
 
 The GEMM's loader waves issue `global_load_dwordx4` through inline asm and
 wait for them with explicit `s_waitcnt vmcnt(n)`.  The compiler takes an asm
@@ -146,3 +147,24 @@ def analyse(lines):
                     changed = True
     n = sum(1 for b in order for t, a in blocks[b] if a and t.startswith("global_load"))
     return n, sorted(bad)
+
+
+def check_loader_asm(asm_text, expected_functions=2):
+    """Raise RuntimeError unless every function with inline-asm loads leaves
+    their registers alone until a wait drains them, and exactly
+    `expected_functions` functions issue such loads (the register-staged GEMM
+    instantiations).  Returns the number of functions checked."""
+    checked, problems = 0, []
+    for name, lines in functions(asm_text).items():
+        n, bad = analyse(lines)
+        if n == 0:
+            continue
+        checked += 1
+        if bad:
+            problems.append("%s: %d instructions touch in-flight load registers, e.g. %s" % (name, len(bad), bad[:3]))
+    if problems:
+        raise RuntimeError("loader register hazard in the GEMM kernels:\n" + "\n".join(problems))
+    if checked != expected_functions:
+        raise RuntimeError("expected %d GEMM instantiations with asm-issued loads, found %d" %
+                           (expected_functions, checked))
+    return checked

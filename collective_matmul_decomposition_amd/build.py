@@ -39,10 +39,29 @@ def _compile(src, is_hip):
     return obj
 
 
+def check_loader_asm(src=None, out=None):
+    """Compile the GEMM kernels (src: kernels.hip by default) to gfx950
+    assembly with the build flags and prove that the loader waves' inline-asm
+    load registers are not read, copied, spilled or reused before the wait
+    that drains them (asm_check).  Raises RuntimeError otherwise."""
+    from . import asm_check
+    src = src or os.path.join(CSRC, "kernels.hip")
+    out = out or os.path.join(OBJDIR, "kernels.s")
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    cmd = [HIPCC, *COMMON, *DEVICE, "--cuda-device-only", "-S", src, "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("assembly listing failed: %s\n%s" % (" ".join(cmd), r.stderr))
+    with open(out) as f:
+        return asm_check.check_loader_asm(f.read())
+
+
 def build(verbose=False):
     os.makedirs(OBJDIR, exist_ok=True)
-    with ThreadPoolExecutor(len(SOURCES)) as ex:
+    with ThreadPoolExecutor(len(SOURCES) + 1) as ex:
+        asm = ex.submit(check_loader_asm)
         objs = list(ex.map(lambda s: _compile(*s), SOURCES))
+        asm.result()  # raises if the loader's in-flight registers are touched
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", *DEVICE, *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -15,9 +15,8 @@ import subprocess
 
 import pytest
 
+from collective_matmul_decomposition_amd import asm_check as asm_flow
 from collective_matmul_decomposition_amd import build as B
-
-import asm_flow
 
 
 @pytest.fixture(scope="module")
@@ -29,6 +28,22 @@ def kernels_asm(tmp_path_factory):
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
     return open(out).read()
+
+
+def test_build_check_fails_on_a_planted_read(tmp_path):
+    """The same check runs in build(): a source mutant whose loader reads a
+    register of a load that may still be in flight makes it fail."""
+    if not os.path.exists(B.HIPCC) and shutil.which("hipcc") is None:
+        pytest.skip("hipcc not available")
+    src = open(os.path.join(B.CSRC, "kernels.hip")).read()
+    anchor = "    for (int j = 0; j < RS; ++j) gload(j, j);\n"
+    assert anchor in src
+    planted = anchor + ("    { int sink; asm volatile(\"v_mov_b32 %0, %1\" : \"=v\"(sink) : \"v\"(ra[0][0][0]));\n"
+                        "      asm volatile(\"\" :: \"v\"(sink)); }\n")
+    mutant = tmp_path / "kernels.hip"
+    mutant.write_text(src.replace(anchor, planted))
+    with pytest.raises(RuntimeError, match="in-flight"):
+        B.check_loader_asm(str(mutant), str(tmp_path / "kernels.s"))
 
 
 def test_loader_registers_untouched_until_waited(kernels_asm):
