@@ -259,6 +259,7 @@ def _ptr(t):
 
 
 _BF16, _F32 = "bfloat16", "float32"
+_BITS_OF = {_BF16: (_BF16, "int16", "uint16"), _F32: (_F32, "int32", "uint32")}
 
 
 def _dtype_name(dt):
@@ -276,7 +277,8 @@ def _expect(t, name, elems, dtype):
         raise ValueError("%s must be a GPU tensor" % name)
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
-    if str(t.dtype).split(".")[-1] != dtype:
+    # the element type, or an integer type of the same width holding its bit patterns
+    if str(t.dtype).split(".")[-1] not in _BITS_OF[dtype]:
         raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
     if t.numel() < elems:
         raise ValueError("%s holds %d elements, the plan needs %d" % (name, t.numel(), elems))
