@@ -195,16 +195,12 @@ cm_status fill_params(const cm_op_rec &o, const cm_job_rec *jobs, Launch &L) {
 struct GraphEntry {
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
-  hipEvent_t done = nullptr;   // recorded on the compute stream after every launch of the graph
   const cm_trace *trace = nullptr;
   std::vector<cm_span> spans;  // trace metadata captured with the graph
   bool overflow = false;
-  // Destroying the graph waits only for its own last launch.
+  // The owner makes sure no launch of the graph is still running (see
+  // drop_graphs).
   ~GraphEntry() {
-    if (done) {
-      (void)hipEventSynchronize(done);
-      (void)hipEventDestroy(done);
-    }
     if (exec) (void)hipGraphExecDestroy(exec);
     if (graph) (void)hipGraphDestroy(graph);
   }
@@ -212,9 +208,12 @@ struct GraphEntry {
 
 constexpr size_t kMaxGraphs = 256;
 
-// Instantiated graphs, shared by every host thread of the process and
-// evicted least-recently-used first, one at a time.  A graph is keyed by the
-// plan, the buffers and the trace it was built for.
+// Instantiated graphs, shared by every host thread of the process and kept in
+// least-recently-used order.  A graph is keyed by the plan, the buffers and the
+// trace it was built for.  A launched graph may still be running when it is
+// dropped, and the only handle on its completion is the caller's stream, which
+// the caller may have destroyed by then; so dropping graphs first waits for the
+// device, and a full cache drops its least recently used quarter at once.
 struct GraphCache {
   std::mutex mu;
   std::list<std::string> lru;  // front = most recently used
@@ -578,14 +577,13 @@ cm_status run(const cm_plan *pl, Entry want, const void *x, const void *w, void 
   hipError_t e;
   if (it == gc.map.end()) {
     if (gc.map.size() >= kMaxGraphs) {
-      // evict the least recently used graph (its destructor waits for its last launch)
-      auto victim = gc.map.find(gc.lru.back());
-      gc.lru.pop_back();
-      if (victim != gc.map.end()) gc.map.erase(victim);
+      if ((e = hipDeviceSynchronize()) != hipSuccess) return hip_fail(e, "hipDeviceSynchronize (graph cache)");
+      for (size_t i = 0; i < kMaxGraphs / 4 && !gc.lru.empty(); ++i) {
+        gc.map.erase(gc.lru.back());
+        gc.lru.pop_back();
+      }
     }
     auto g = std::make_unique<GraphEntry>();
-    if ((e = hipEventCreateWithFlags(&g->done, hipEventDisableTiming)) != hipSuccess)
-      return hip_fail(e, "hipEventCreateWithFlags (graph)");
     g->trace = trace;
     if ((st = build_graph(cp, base, n_comm + 1, trace, g.get())) != CM_OK) return st;
     gc.lru.push_front(key);
@@ -603,18 +601,21 @@ cm_status run(const cm_plan *pl, Entry want, const void *x, const void *w, void 
     trace->overflow = ge->overflow;
   }
   if ((e = hipGraphLaunch(ge->exec, streams[0])) != hipSuccess) return hip_fail(e, "hipGraphLaunch");
-  if ((e = hipEventRecord(ge->done, streams[0])) != hipSuccess) return hip_fail(e, "hipEventRecord (graph)");
   return CM_OK;
 }
 
 }  // namespace
 
 // Graphs that record a trace's events must not outlive the trace: drop them
-// in every thread's view (the cache is process-wide), each after its last
-// launch has finished.
+// in every thread's view (the cache is process-wide), after the device has
+// finished any launch of them.
 void forget_graphs_of(const cm_trace *t) {
   GraphCache &gc = graph_cache();
   std::lock_guard<std::mutex> lock(gc.mu);
+  bool any = false;
+  for (const auto &kv : gc.map) any = any || kv.second.g->trace == t;
+  if (!any) return;
+  (void)hipDeviceSynchronize();
   for (auto it = gc.map.begin(); it != gc.map.end();) {
     if (it->second.g->trace == t) {
       gc.lru.erase(it->second.pos);
