@@ -252,18 +252,28 @@ def measure(args, workload, steps, warmup, with_naive, with_trace):
         # operations, timed per op inside alternating AG/RS steps as D is
         alone = {"ag": {}, "rs": {}}
         reps = max(5, steps // 2)
+        # their own outputs and workspaces: a call in a measurement mode leaves
+        # meaningless values, and y1 / y2 hold the step's results for the checks
+        ys1, wss1 = buffers.alloc_outputs(plan_ag)
+        ys2, wss2 = buffers.alloc_outputs(plan_rs)
+
+        def step_alone(ta, tb, pa, pr):
+            nat.cm_ag_gemm(pa, x, w1, ys1, wss1, compute, comm, ta)
+            nat.cm_gemm_rs(pr, h, w2, ys2, wss2, compute, comm, tb)
+
         for skip in ("hops", "gemms"):
             pa, pr = make_plans(skip)
             tr = [(nat.Trace(cap_ag), nat.Trace(cap_rs)) for _ in range(reps)]
             for _ in range(2):  # the first round builds each trace's graphs
                 for ta, tb in tr:
-                    step(ta, tb, pa, pr)
+                    step_alone(ta, tb, pa, pr)
                 torch.cuda.synchronize()
             for name, i in (("ag", 0), ("rs", 1)):
                 alone[name][skip] = float(np.median([t[i].read()[1] for t in tr]))
             for ta, tb in tr:
                 ta.close()
                 tb.close()
+        del ys1, wss1, ys2, wss2
         for name, plan in (("ag", plan_ag), ("rs", plan_rs)):
             o = ov[name]
             D, Ga, Ca = o["decomposed_us"], alone[name]["hops"], alone[name]["gemms"]
