@@ -41,7 +41,8 @@ class cm_plan_desc(ctypes.Structure):
                 ("copy_engine", ctypes.c_int), ("bucket_bf16", ctypes.c_int), ("hop_add", ctypes.c_int),
                 ("copy_gbps", ctypes.c_double),
                 ("mfma_tflops", ctypes.c_double), ("launch_us", ctypes.c_double), ("act", ctypes.c_int),
-                ("share", ctypes.c_int), ("split_k", ctypes.c_int), ("skip", ctypes.c_int)]
+                ("share", ctypes.c_int), ("split_k", ctypes.c_int), ("skip", ctypes.c_int),
+                ("stress", ctypes.c_int)]
 
 
 class cm_plan(ctypes.Structure):
@@ -189,7 +190,7 @@ _ENUMS = {
 
 def make_desc(op, n_ranks, m, k, n, dir="uni", chunks=0, sched="decomposed", out_dtype="bf16", n_comm=1,
               tile=(0, 0), exec_mode="graph", copy_engine="sdma", bucket="f32", hop="copy", copy_gbps=0.0,
-              mfma_tflops=0.0, launch_us=0.0, act="none", share=0, split_k=0, skip="none"):
+              mfma_tflops=0.0, launch_us=0.0, act="none", share=0, split_k=0, skip="none", stress=0):
     """A cm_plan_desc from keyword arguments (strings or enum values).  share=1:
     one rank's share (virtual rank 0's steps at real shape, split-K GEMMs).
     skip="hops" / "gemms": a timing-only mode that runs the program with its hops
@@ -202,7 +203,7 @@ def make_desc(op, n_ranks, m, k, n, dir="uni", chunks=0, sched="decomposed", out
                         copy_engine=e("copy", copy_engine), bucket_bf16=1 if bucket == "bf16" else 0,
                         hop_add=e("hop", hop), copy_gbps=copy_gbps,
                         mfma_tflops=mfma_tflops, launch_us=launch_us, act=e("act", act), share=int(share),
-                        split_k=int(split_k), skip=e("skip", skip))
+                        split_k=int(split_k), skip=e("skip", skip), stress=int(stress))
 
 
 def cm_ring_plan(desc=None, **kw):

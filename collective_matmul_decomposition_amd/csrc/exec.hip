@@ -50,6 +50,7 @@ struct Compiled {
   std::vector<int> launch_of_op; // op index -> launches index (-1 if none)
   hipMemcpyKind copy_kind = hipMemcpyDeviceToDeviceNoCU;  // ring hops: SDMA or the CU copy kernel
   int skip = CM_SKIP_NONE;       // measurement mode: which operations become empty
+  int stress = 0;                // test mode seed (eager only): delays and poisoned destinations
   // Is program operation `o` skipped in this plan's measurement mode?  Hops are
   // the copies and the launches on comm streams; the compute stream's launches
   // are the GEMMs (and split-K reduces).
@@ -68,7 +69,7 @@ std::string plan_key(const cm_plan &p) {
                 "%d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %a %a %a %d %d %d %d|%d %d %d %d %d %d %d %zu %d",
                 d.op, d.n_ranks, d.m, d.k, d.n, d.dir, d.chunks, d.sched, d.in_dtype, d.out_dtype, d.n_comm, d.tile_m,
                 d.tile_n, d.exec_mode, d.copy_engine, d.bucket_bf16, d.hop_add, d.copy_gbps, d.mfma_tflops,
-                d.launch_us, d.act, d.share, d.split_k, d.skip, p.chunks, p.n_steps, p.arc_cw, p.arc_ccw, p.tile_m, p.tile_n,
+                d.launch_us, d.act, d.share, d.split_k, d.skip * 1000003 + d.stress, p.chunks, p.n_steps, p.arc_cw, p.arc_ccw, p.tile_m, p.tile_n,
                 p.n_events, p.ws_bytes, p.split);
   return buf;
 }
@@ -255,6 +256,7 @@ cm_status get_compiled(const cm_plan &pl, const Compiled **out) {
   build_program(canon, c->prog);
   c->copy_kind = canon.desc.copy_engine == CM_COPY_CU ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToDeviceNoCU;
   c->skip = canon.desc.skip;
+  c->stress = canon.desc.stress;
   c->launch_of_op.assign(c->prog.ops.size(), -1);
   for (size_t i = 0; i < c->prog.ops.size(); ++i) {
     const cm_op_rec &o = c->prog.ops[i];
@@ -357,6 +359,35 @@ cm_status validate_call(const cm_plan *pl, Entry want, const void *x, const void
   return CM_OK;
 }
 
+// The stress mode (a test of the program's ordering): before operation `i`,
+// maybe a sleep on its stream (chosen by a hash of the seed and `i`), then a
+// fill with 0xFF bytes of every workspace region the operation is about to
+// write (not the ones it also reads: an epilogue that adds into its output).
+// Correct waits make both invisible in the results.
+cm_status stress_before(const Compiled *cp, const cm_op_rec &o, uint32_t i, char *const base[4], hipStream_t s) {
+  uint32_t h = (uint32_t)cp->stress * 0x9E3779B1u ^ (i + 1) * 0x85EBCA77u;
+  h ^= h >> 15;
+  h *= 0xC2B2AE3Du;
+  h ^= h >> 13;
+  hipError_t e;
+  if ((h & 3) == 0 && (e = launch_sleep((int)((h >> 8) & 7), s)) != hipSuccess) return hip_fail(e, "stress sleep");
+  if (o.kind == CM_OPK_COPY) {
+    if (o.dst_buf == CM_BUF_WS && (e = launch_fill_ff(base[CM_BUF_WS] + o.dst_off, 1, (long)o.bytes, (long)o.bytes, s)) != hipSuccess)
+      return hip_fail(e, "stress fill");
+    return CM_OK;
+  }
+  if (cp->skipped(o)) return CM_OK;
+  for (int j = o.first_job; j < o.first_job + o.n_jobs; ++j) {
+    const cm_job_rec &jb = cp->prog.jobs[j];
+    if (jb.c_buf != CM_BUF_WS) continue;
+    if ((jb.in0_buf == CM_BUF_WS && jb.in0_off == jb.c_off) || (jb.in1_buf == CM_BUF_WS && jb.in1_off == jb.c_off)) continue;
+    const long esz = jb.c_dtype == CM_F32 ? 4 : 2;
+    if ((e = launch_fill_ff(base[CM_BUF_WS] + jb.c_off, o.rows, o.cols * esz, (long)jb.ldc * esz, s)) != hipSuccess)
+      return hip_fail(e, "stress fill");
+  }
+  return CM_OK;
+}
+
 // Enqueue the program's operations on the streams, one HIP call each
 // (eager mode).  Calls made while a stream is being captured are refused
 // before this point (refuse_capture).
@@ -390,6 +421,10 @@ cm_status enqueue(const Compiled *cp, const std::vector<hipEvent_t> &ev, char *c
   for (size_t i = 0; i < ops.size(); ++i) {
     const cm_op_rec &o = ops[i];
     hipStream_t s = streams[o.stream];
+    if (cp->stress && o.kind != CM_OPK_RECORD && o.kind != CM_OPK_WAIT) {
+      cm_status st = stress_before(cp, o, (uint32_t)i, base, s);
+      if (st != CM_OK) return st;
+    }
     switch (o.kind) {
       case CM_OPK_RECORD:
         if ((e = hipEventRecord(ev[o.event], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");

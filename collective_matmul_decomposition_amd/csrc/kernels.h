@@ -38,5 +38,10 @@ bool gemm_launch_config(const GemmParams &p, int tm, int tn, KernelLaunch *out);
 void reduce_launch_config(const GemmParams &p, KernelLaunch *out);
 hipError_t launch_gemm(const GemmParams &p, int tm, int tn, hipStream_t s);
 hipError_t launch_reduce(const GemmParams &p, hipStream_t s);
+// Test support (the executor's stress mode): a kernel that sleeps for about
+// units * 8 us, and a fill of `rows` rows of `row_bytes` bytes, `ld_bytes`
+// apart, with 0xFF bytes (row_bytes and ld_bytes multiples of 4).
+hipError_t launch_sleep(int units, hipStream_t s);
+hipError_t launch_fill_ff(char *p, long rows, long row_bytes, long ld_bytes, hipStream_t s);
 
 }  // namespace collmm

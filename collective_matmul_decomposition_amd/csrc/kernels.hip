@@ -514,7 +514,36 @@ __global__ __launch_bounds__(256) void reduce_jobs_kernel(const GemmParams p) {
   }
 }
 
+// Sleep for about units * 8 us (one wave; s_sleep 127 is 8128 clocks).
+__global__ void sleep_kernel(int units) {
+  for (int i = 0; i < units * 2; ++i) __builtin_amdgcn_s_sleep(127);
+}
+
+// rows x row_bytes bytes, ld_bytes apart, set to 0xFF (4 bytes per thread).
+__global__ void fill_ff_kernel(char *p, long rows, long row_words, long ld_bytes) {
+  const long total = rows * row_words;
+  for (long t = (long)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (long)gridDim.x * blockDim.x) {
+    const long r = t / row_words, w = t - r * row_words;
+    reinterpret_cast<uint32_t *>(p + r * ld_bytes)[w] = 0xFFFFFFFFu;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_sleep(int units, hipStream_t s) {
+  void *args[] = {&units};
+  return hipLaunchKernel(reinterpret_cast<void *>(&sleep_kernel), dim3(1), dim3(64), args, 0, s);
+}
+
+hipError_t launch_fill_ff(char *p, long rows, long row_bytes, long ld_bytes, hipStream_t s) {
+  const long words = rows * (row_bytes / 4);
+  if (words <= 0) return hipSuccess;
+  long blocks = (words + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  long row_words = row_bytes / 4;
+  void *args[] = {&p, &rows, &row_words, &ld_bytes};
+  return hipLaunchKernel(reinterpret_cast<void *>(&fill_ff_kernel), dim3((unsigned)blocks), dim3(256), args, 0, s);
+}
 
 bool gemm_tile_supported(int tm, int tn) {
   KernelLaunch L;

@@ -251,6 +251,10 @@ cm_status validate_desc(const cm_plan_desc &d) {
     set_error("unknown skip mode %d", d.skip);
     return CM_ERR_INVALID_ARG;
   }
+  if (d.stress && d.exec_mode != CM_EXEC_EAGER) {
+    set_error("the stress mode runs in the eager executor only");
+    return CM_ERR_UNSUPPORTED;
+  }
   if (!d.share && d.split_k) { set_error("split_k applies to one rank's share (share = 1) only"); return CM_ERR_INVALID_ARG; }
   if (d.share) {
     if (!(d.op == CM_OP_AG_GEMM || d.op == CM_OP_GEMM_RS) || d.dir != CM_RING_UNI || d.sched != CM_SCHED_DECOMPOSED ||

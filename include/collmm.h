@@ -214,6 +214,17 @@ typedef struct {
                             tiles to fill the chip, at least 8 slabs of 64 each);
                             must divide k/64, at most 16 */
   int skip;              /* cm_skip: a measurement mode (0 = normal) */
+  int stress;            /* 0 = off.  Otherwise a test mode of the eager executor
+                            (exec_mode must be CM_EXEC_EAGER), seeded by this
+                            value: before some operations (chosen by a hash of the
+                            seed and the operation's index) a kernel that sleeps
+                            up to ~60 us is enqueued on that operation's stream,
+                            and every copy or launch that writes a workspace
+                            region is preceded, on its stream, by a fill of that
+                            region with 0xFF bytes (NaN in fp32 and bf16).  With
+                            the program's ordering right, the results equal those
+                            of a run without stress bit for bit; a missing wait
+                            shows up as changed or NaN outputs. */
 } cm_plan_desc;
 
 /* The resolved schedule.  Plain data: no heap, nothing to destroy. */

@@ -505,3 +505,13 @@ def test_programs_use_at_most_three_comm_lanes(op, dir, n_comm):
     work = {o.stream for o in ops if o.kind in (nat.CM_OPK_COPY, nat.CM_OPK_REDUCE, nat.CM_OPK_GEMM)}
     assert max(work) <= 3
     assert np.array_equal(output(sim, plan), expect("ag" if op == "ag" else "rs", a, w, "f32"))
+
+
+def test_stress_mode_is_eager_only():
+    """The race-stress test mode exists in the eager executor only; it does not
+    change the program."""
+    st, _ = nat.cm_ring_plan_status(nat.make_desc("ag", 4, 64, 256, 256, stress=1))
+    assert st == nat.CM_ERR_UNSUPPORTED
+    a = nat.cm_ring_plan(op="rs", n_ranks=4, m=64, k=256, n=256, chunks=2, exec_mode="eager", stress=7)
+    b = nat.cm_ring_plan(op="rs", n_ranks=4, m=64, k=256, n=256, chunks=2, exec_mode="eager")
+    assert (a.n_ops, a.n_jobs, a.n_events, a.ws_bytes) == (b.n_ops, b.n_jobs, b.n_events, b.ws_bytes)
