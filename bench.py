@@ -124,7 +124,7 @@ def measure(args, workload, steps, warmup, with_naive, with_trace):
                               bucket=args.rs_bucket, hop=rs_hop(args), skip=skip)
         return pa, pr
 
-    plan_ag, plan_rs = make_plans()
+    plan_ag, plan_rs = make_plans(args.skip)
     log("%s plans: AG chunks=%d tile=%dx%d ws=%.0fMB | RS(%s) chunks=%d tile=%dx%d ws=%.0fMB | n_comm=%d" % (
         workload, plan_ag.chunks, plan_ag.tile_m, plan_ag.tile_n, plan_ag.ws_bytes / 1e6, args.rs_op,
         plan_rs.chunks, plan_rs.tile_m, plan_rs.tile_n, plan_rs.ws_bytes / 1e6, n_comm))
@@ -252,45 +252,46 @@ def measure(args, workload, steps, warmup, with_naive, with_trace):
         # operations, timed per op inside alternating AG/RS steps as D is
         alone = {"ag": {}, "rs": {}}
         reps = max(5, steps // 2)
-        # their own outputs and workspaces: a call in a measurement mode leaves
-        # meaningless values, and y1 / y2 hold the step's results for the checks
-        ys1, wss1 = buffers.alloc_outputs(plan_ag)
-        ys2, wss2 = buffers.alloc_outputs(plan_rs)
+        if not (args.no_alone or args.skip != "none"):
+            # their own outputs and workspaces: a call in a measurement mode leaves
+            # meaningless values, and y1 / y2 hold the step's results for the checks
+            ys1, wss1 = buffers.alloc_outputs(plan_ag)
+            ys2, wss2 = buffers.alloc_outputs(plan_rs)
 
-        def step_alone(ta, tb, pa, pr):
-            nat.cm_ag_gemm(pa, x, w1, ys1, wss1, compute, comm, ta)
-            nat.cm_gemm_rs(pr, h, w2, ys2, wss2, compute, comm, tb)
+            def step_alone(ta, tb, pa, pr):
+                nat.cm_ag_gemm(pa, x, w1, ys1, wss1, compute, comm, ta)
+                nat.cm_gemm_rs(pr, h, w2, ys2, wss2, compute, comm, tb)
 
-        for skip in ("hops", "gemms"):
-            pa, pr = make_plans(skip)
-            tr = [(nat.Trace(cap_ag), nat.Trace(cap_rs)) for _ in range(reps)]
-            for _ in range(2):  # the first round builds each trace's graphs
+            for skip in ("hops", "gemms"):
+                pa, pr = make_plans(skip)
+                tr = [(nat.Trace(cap_ag), nat.Trace(cap_rs)) for _ in range(reps)]
+                for _ in range(2):  # the first round builds each trace's graphs
+                    for ta, tb in tr:
+                        step_alone(ta, tb, pa, pr)
+                    torch.cuda.synchronize()
+                for name, i in (("ag", 0), ("rs", 1)):
+                    alone[name][skip] = float(np.median([t[i].read()[1] for t in tr]))
                 for ta, tb in tr:
-                    step_alone(ta, tb, pa, pr)
-                torch.cuda.synchronize()
-            for name, i in (("ag", 0), ("rs", 1)):
-                alone[name][skip] = float(np.median([t[i].read()[1] for t in tr]))
-            for ta, tb in tr:
-                ta.close()
-                tb.close()
-        del ys1, wss1, ys2, wss2
-        for name, plan in (("ag", plan_ag), ("rs", plan_rs)):
-            o = ov[name]
-            D, Ga, Ca = o["decomposed_us"], alone[name]["hops"], alone[name]["gemms"]
-            elt = 2 if name == "ag" or args.rs_bucket == "bf16" else 4
-            # overlap efficiency = D / max(GEMM-only, copy-only); hidden
-            # fraction = (G + C - D) / C, with G and C the op's parts alone
-            o.update({"gemm_alone_us": round(Ga, 1), "copy_alone_us": round(Ca, 1),
-                      "bound_by": "gemm" if Ga >= Ca else "copy",
-                      "overlap_efficiency": round(D / max(Ga, Ca), 3),
-                      "hidden_fraction": round((Ga + Ca - D) / Ca, 3) if Ca > 0 else None,
-                      # each hop byte is read and written once in HBM
-                      "hop_GBps_alone": round(o["ring_bytes"] / (Ca * 1e-6) / 1e9, 1) if Ca > 0 else None,
-                      "hop_hbm_frac_alone": round(2 * o["ring_bytes"] / (Ca * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)
-                      if Ca > 0 else None})
-            log("%s alone: G %.1f us (hops skipped), C %.1f us (GEMMs skipped), D %.1f us -> D/max(G,C) %.3f, "
-                "hidden (G+C-D)/C %.3f" % (name, Ga, Ca, D, o["overlap_efficiency"],
-                                            o["hidden_fraction"] or 0.0))
+                    ta.close()
+                    tb.close()
+            del ys1, wss1, ys2, wss2
+            for name, plan in (("ag", plan_ag), ("rs", plan_rs)):
+                o = ov[name]
+                D, Ga, Ca = o["decomposed_us"], alone[name]["hops"], alone[name]["gemms"]
+                elt = 2 if name == "ag" or args.rs_bucket == "bf16" else 4
+                # overlap efficiency = D / max(GEMM-only, copy-only); hidden
+                # fraction = (G + C - D) / C, with G and C the op's parts alone
+                o.update({"gemm_alone_us": round(Ga, 1), "copy_alone_us": round(Ca, 1),
+                          "bound_by": "gemm" if Ga >= Ca else "copy",
+                          "overlap_efficiency": round(D / max(Ga, Ca), 3),
+                          "hidden_fraction": round((Ga + Ca - D) / Ca, 3) if Ca > 0 else None,
+                          # each hop byte is read and written once in HBM
+                          "hop_GBps_alone": round(o["ring_bytes"] / (Ca * 1e-6) / 1e9, 1) if Ca > 0 else None,
+                          "hop_hbm_frac_alone": round(2 * o["ring_bytes"] / (Ca * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)
+                          if Ca > 0 else None})
+                log("%s alone: G %.1f us (hops skipped), C %.1f us (GEMMs skipped), D %.1f us -> D/max(G,C) %.3f, "
+                    "hidden (G+C-D)/C %.3f" % (name, Ga, Ca, D, o["overlap_efficiency"],
+                                                o["hidden_fraction"] or 0.0))
 
     if with_naive:
         pa = nat.cm_ring_plan(op="ag", n_ranks=N, m=m, k=d, n=fN, sched="naive", out_dtype="bf16", n_comm=n_comm,
@@ -837,6 +838,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
     ap.add_argument("--no-naive", action="store_true")
     ap.add_argument("--no-bi", action="store_true", help="skip the run on the bidirectional ring")
+    ap.add_argument("--no-alone", action="store_true", help="skip timing G and C alone (the measurement modes)")
+    ap.add_argument("--skip", default="none", choices=["none", "hops", "gemms"],
+                    help="time the step itself in a measurement mode (hops or GEMMs replaced by empty "
+                         "operations; for profiling the GEMM launches alone)")
     ap.add_argument("--no-layer", action="store_true", help="skip the sequence-parallel layer forward")
     ap.add_argument("--no-share", action="store_true", help="skip one rank's share (rank 0's steps at real shape)")
     ap.add_argument("--no-backward", action="store_true", help="skip the MLP backward (bulk overlap)")
@@ -877,8 +882,10 @@ def main():
         torch.cuda.synchronize()
         del a, b, flush
     res = measure(args, args.workload, args.steps, args.warmup, not args.no_naive, not args.no_trace)
-    parity, arrays = sampled_parity(res, args.rs_bucket if args.rs_op == "rs" else "f32")
-    cpu = None if args.no_cpu_baseline else cpu_baseline(res, arrays, args.cpu_seconds)
+    parity, cpu = None, None
+    if args.skip == "none":  # in a measurement mode the outputs are not computed
+        parity, arrays = sampled_parity(res, args.rs_bucket if args.rs_op == "rs" else "f32")
+        cpu = None if args.no_cpu_baseline else cpu_baseline(res, arrays, args.cpu_seconds)
     del res["tensors"]
     torch.cuda.empty_cache()
     alt = None
@@ -962,7 +969,7 @@ def main():
         "config": {"workload": args.workload, "virtual_ranks": res["N"], "tokens": res["T"], "hidden": res["d"],
                    "ffn": res["f"], "ffn_per_rank": res["fN"], "ring": args.dir, "rs_variant": args.rs_op,
                    "n_comm_streams": res["n_comm"], "copy_engine": args.copy_engine, "rs_bucket": args.rs_bucket,
-                   "rs_hop": rs_hop(args),
+                   "rs_hop": rs_hop(args), "measurement_mode": args.skip,
                    "chunks_ag": res["plan_ag"].chunks,
                    "chunks_rs": res["plan_rs"].chunks,
                    "step": "AllGather->GEMM (fc1) then GEMM->ReduceScatter (fc2), decomposed, bf16 in / fp32 "
