@@ -91,7 +91,7 @@ def profiled_traffic(workload, label):
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     except OSError:
         return None
-    kv = dict(l.split("=", 1) for l in lines if "=" in l and " " not in l)
+    kv = dict(l.strip().split("=", 1) for l in lines if "=" in l and " " not in l.strip())
     if kv.get("kernel_source_sha256") != sha:
         return None
     v = kv.get("traffic_bytes_%s" % label)
