@@ -60,10 +60,12 @@ def union_length(intervals):
 
 
 def algorithmic_bytes(op_rec, jobs, out_size):
-    """Bytes a GEMM launch must move at least once: A, B, C, and the fp32 addends."""
+    """Bytes a GEMM launch must move at least once: A, B (once per run of
+    b_share jobs that read the same weights), C, and the fp32 addends."""
     total = 0
+    share = max(1, op_rec.b_share)
     for j in jobs[op_rec.first_job:op_rec.first_job + op_rec.n_jobs]:
-        total += op_rec.rows * op_rec.depth * 2 + op_rec.cols * op_rec.depth * 2
+        total += op_rec.rows * op_rec.depth * 2 + op_rec.cols * op_rec.depth * 2 // share
         total += op_rec.rows * op_rec.cols * (4 if j.c_dtype == 1 else 2)
         total += op_rec.rows * op_rec.cols * 4 * ((j.in0_buf >= 0) + (j.in1_buf >= 0))
     return total
@@ -74,8 +76,9 @@ def addends_per_job(op_rec, jobs):
     return max((j.in0_buf >= 0) + (j.in1_buf >= 0) for j in jobs[op_rec.first_job:op_rec.first_job + op_rec.n_jobs])
 
 
-def launch_label(name, nadd):
-    return "%s_add%d" % (name, nadd)
+def launch_label(name, jobs, nadd):
+    """A GEMM launch shape's name: op, jobs per launch, fp32 addends per job."""
+    return "%s%d_add%d" % (name, jobs, nadd)
 
 
 def profiled_traffic(workload, label):
@@ -118,16 +121,19 @@ def measure(args, workload, steps, warmup, with_naive, with_trace):
 
     def make_plans(skip="none"):
         pa = nat.cm_ring_plan(op="ag", n_ranks=N, m=m, k=d, n=fN, dir=args.dir, chunks=args.chunks_ag,
-                              out_dtype="bf16", n_comm=n_comm, tile=tile, copy_engine=args.copy_engine, skip=skip)
+                              out_dtype="bf16", n_comm=n_comm, tile=tile, copy_engine=args.copy_engine, skip=skip,
+                              group=args.group)
         pr = nat.cm_ring_plan(op=args.rs_op, n_ranks=N, m=m, k=fN, n=d, dir=args.dir, chunks=args.chunks_rs,
                               out_dtype="bf16", n_comm=n_comm, tile=tile, copy_engine=args.copy_engine,
-                              bucket=args.rs_bucket, hop=rs_hop(args), skip=skip)
+                              bucket=args.rs_bucket, hop=rs_hop(args), skip=skip, group=args.group)
         return pa, pr
 
     plan_ag, plan_rs = make_plans(args.skip)
-    log("%s plans: AG chunks=%d tile=%dx%d ws=%.0fMB | RS(%s) chunks=%d tile=%dx%d ws=%.0fMB | n_comm=%d" % (
-        workload, plan_ag.chunks, plan_ag.tile_m, plan_ag.tile_n, plan_ag.ws_bytes / 1e6, args.rs_op,
-        plan_rs.chunks, plan_rs.tile_m, plan_rs.tile_n, plan_rs.ws_bytes / 1e6, n_comm))
+    log("%s plans: AG chunks=%d tile=%dx%d ws=%.0fMB launches %s | RS(%s) chunks=%d tile=%dx%d ws=%.0fMB "
+        "launches %s | n_comm=%d" % (
+            workload, plan_ag.chunks, plan_ag.tile_m, plan_ag.tile_n, plan_ag.ws_bytes / 1e6,
+            list(plan_ag.group_len[:plan_ag.n_launches]), args.rs_op, plan_rs.chunks, plan_rs.tile_m, plan_rs.tile_n,
+            plan_rs.ws_bytes / 1e6, list(plan_rs.group_len[:plan_rs.n_launches]), n_comm))
 
     x, w1 = gen.ag_inputs_torch(N, m, d, fN, "normal", 0, "cuda")
     h, w2 = gen.rs_inputs_torch(N, m, fN, d, "normal", 0, "cuda")
@@ -218,21 +224,21 @@ def measure(args, workload, steps, warmup, with_naive, with_trace):
                      "kernel": "gemm_jobs_kernel<%d,%d,...> (%s step: %d jobs of [%dx%d].[%dx%d]^T%s)" % (
                          tm, tn, name.upper(), jobs, rows, depth, cols, depth,
                          ", + %d fp32 addend(s)" % nadd if nadd else ""),
-                     "launch": launch_label(name, nadd),
+                     "launch": launch_label(name, jobs, nadd),
                      "avg_launch_us": round(avg_us, 2), "launches": len(durs),
                      "flops_per_launch": flops_launch, "algorithmic_bytes_per_launch": abytes,
                      "intensity_flop_per_byte": round(intensity, 1), "ridge_flop_per_byte": round(ridge, 1),
                      "mfma_tflops": round(flops_launch / (avg_us * 1e-6) / 1e12, 1),
                      "hbm_gbps": round(abytes / (avg_us * 1e-6) / 1e9, 1)})
-        roof["traffic"] = profiled_traffic(workload, launch_label(name, nadd))
+        roof["traffic"] = profiled_traffic(workload, launch_label(name, jobs, nadd))
         res["roofline"] = roof
         res["gemm_launches"] = {
             "%s %dx%dx%d x%d tile %dx%d%s" % (nm, r, c, dd, j, a, b, " +%d addend" % na if na else ""): {
-                "launch": launch_label(nm, na), "avg_us": round(float(np.mean(dl)), 2), "count": len(dl),
+                "launch": launch_label(nm, j, na), "avg_us": round(float(np.mean(dl)), 2), "count": len(dl),
                 "tflops": round(2.0 * r * c * dd * j / (np.mean(dl) * 1e-6) / 1e12, 1), "algorithmic_bytes": ab}
             for (nm, r, c, dd, j, a, b, na, ab), dl in gemm_stats.items()}
         # the GEMM launches of one step in program order (for splitting a profiler's trace)
-        res["step_launches"] = [launch_label(k[0], k[7]) for k in keys["ag"] + keys["rs"]]
+        res["step_launches"] = [launch_label(k[0], k[4], k[7]) for k in keys["ag"] + keys["rs"]]
         ov = {}
         for name, plan in (("ag", plan_ag), ("rs", plan_rs)):
             arr = np.array(per_op[name])
@@ -834,6 +840,8 @@ def main():
                     help="RS ring hop: a copy with the addition in the GEMM epilogue, or an add-and-forward "
                          "launch that lets each step's GEMM start without waiting for the previous hop")
     ap.add_argument("--tile", default="0x0")
+    ap.add_argument("--group", type=int, default=0,
+                    help="steps per GEMM launch (0: cost model, 1: one step per launch, g: at most g)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
     ap.add_argument("--no-naive", action="store_true")
@@ -972,6 +980,8 @@ def main():
                    "rs_hop": rs_hop(args), "measurement_mode": args.skip,
                    "chunks_ag": res["plan_ag"].chunks,
                    "chunks_rs": res["plan_rs"].chunks,
+                   "steps_per_launch_ag": list(res["plan_ag"].group_len[:res["plan_ag"].n_launches]),
+                   "steps_per_launch_rs": list(res["plan_rs"].group_len[:res["plan_rs"].n_launches]),
                    "step": "AllGather->GEMM (fc1) then GEMM->ReduceScatter (fc2), decomposed, bf16 in / fp32 "
                            "accumulate / bf16 out"},
         "pct_of_bf16_peak": round(100 * res["value"] / PEAK_BF16_TFLOPS, 2),

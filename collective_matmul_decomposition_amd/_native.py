@@ -42,7 +42,7 @@ class cm_plan_desc(ctypes.Structure):
                 ("copy_gbps", ctypes.c_double),
                 ("mfma_tflops", ctypes.c_double), ("launch_us", ctypes.c_double), ("act", ctypes.c_int),
                 ("share", ctypes.c_int), ("split_k", ctypes.c_int), ("skip", ctypes.c_int),
-                ("stress", ctypes.c_int)]
+                ("stress", ctypes.c_int), ("group", ctypes.c_int)]
 
 
 class cm_plan(ctypes.Structure):
@@ -51,7 +51,8 @@ class cm_plan(ctypes.Structure):
                 ("tile_n", ctypes.c_int), ("declined", ctypes.c_int), ("n_ops", ctypes.c_int),
                 ("n_jobs", ctypes.c_int), ("n_events", ctypes.c_int), ("ws_bytes", ctypes.c_size_t),
                 ("est_gemm_us", ctypes.c_double), ("est_hop_us", ctypes.c_double),
-                ("est_total_us", ctypes.c_double), ("split", ctypes.c_int)]
+                ("est_total_us", ctypes.c_double), ("split", ctypes.c_int), ("n_launches", ctypes.c_int),
+                ("group_len", ctypes.c_int * 64), ("slots", ctypes.c_int)]
 
 
 class cm_op_rec(ctypes.Structure):
@@ -60,7 +61,7 @@ class cm_op_rec(ctypes.Structure):
                 ("rows", ctypes.c_int), ("cols", ctypes.c_int), ("depth", ctypes.c_int), ("tile_m", ctypes.c_int),
                 ("tile_n", ctypes.c_int), ("src_buf", ctypes.c_int), ("dst_buf", ctypes.c_int),
                 ("src_off", ctypes.c_size_t), ("dst_off", ctypes.c_size_t), ("bytes", ctypes.c_size_t),
-                ("act", ctypes.c_int)]
+                ("act", ctypes.c_int), ("b_share", ctypes.c_int)]
 
 
 class cm_job_rec(ctypes.Structure):
@@ -190,8 +191,9 @@ _ENUMS = {
 
 def make_desc(op, n_ranks, m, k, n, dir="uni", chunks=0, sched="decomposed", out_dtype="bf16", n_comm=1,
               tile=(0, 0), exec_mode="graph", copy_engine="sdma", bucket="f32", hop="copy", copy_gbps=0.0,
-              mfma_tflops=0.0, launch_us=0.0, act="none", share=0, split_k=0, skip="none", stress=0):
-    """A cm_plan_desc from keyword arguments (strings or enum values).  share=1:
+              mfma_tflops=0.0, launch_us=0.0, act="none", share=0, split_k=0, skip="none", stress=0, group=0):
+    """A cm_plan_desc from keyword arguments (strings or enum values).  group: steps
+    per GEMM launch (0 = cost model, 1 = one step per launch, g = at most g).  share=1:
     one rank's share (virtual rank 0's steps at real shape, split-K GEMMs).
     skip="hops" / "gemms": a timing-only mode that runs the program with its hops
     (or its compute-stream launches) replaced by empty operations."""
@@ -203,7 +205,7 @@ def make_desc(op, n_ranks, m, k, n, dir="uni", chunks=0, sched="decomposed", out
                         copy_engine=e("copy", copy_engine), bucket_bf16=1 if bucket == "bf16" else 0,
                         hop_add=e("hop", hop), copy_gbps=copy_gbps,
                         mfma_tflops=mfma_tflops, launch_us=launch_us, act=e("act", act), share=int(share),
-                        split_k=int(split_k), skip=e("skip", skip), stress=int(stress))
+                        split_k=int(split_k), skip=e("skip", skip), stress=int(stress), group=int(group))
 
 
 def cm_ring_plan(desc=None, **kw):

@@ -39,11 +39,12 @@ def _compile(src, is_hip):
     return obj
 
 
-def check_loader_asm(src=None, out=None):
+def check_loader_asm(src=None, out=None, expected_functions=0):
     """Compile the GEMM kernels (src: kernels.hip by default) to gfx950
-    assembly with the build flags and prove that the loader waves' inline-asm
-    load registers are not read, copied, spilled or reused before the wait
-    that drains them (asm_check).  Raises RuntimeError otherwise."""
+    assembly with the build flags and check their inline-asm vector loads
+    (asm_check): the kernels issue every load through builtins, so none may
+    appear (expected_functions = 0); any that does must leave its registers
+    alone until a wait drains it.  Raises RuntimeError otherwise."""
     from . import asm_check
     src = src or os.path.join(CSRC, "kernels.hip")
     out = out or os.path.join(OBJDIR, "kernels.s")
@@ -53,7 +54,7 @@ def check_loader_asm(src=None, out=None):
     if r.returncode != 0:
         raise RuntimeError("assembly listing failed: %s\n%s" % (" ".join(cmd), r.stderr))
     with open(out) as f:
-        return asm_check.check_loader_asm(f.read())
+        return asm_check.check_loader_asm(f.read(), expected_functions)
 
 
 def build(verbose=False):

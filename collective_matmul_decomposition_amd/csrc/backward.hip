@@ -178,12 +178,15 @@ bool same_plan_desc(const cm_plan_desc &a, const cm_plan_desc &b) {
          a.n_comm == b.n_comm && a.tile_m == b.tile_m && a.tile_n == b.tile_n && a.exec_mode == b.exec_mode &&
          a.copy_engine == b.copy_engine && a.bucket_bf16 == b.bucket_bf16 && a.hop_add == b.hop_add &&
          a.copy_gbps == b.copy_gbps && a.mfma_tflops == b.mfma_tflops && a.launch_us == b.launch_us && a.act == b.act &&
-         a.share == b.share && a.split_k == b.split_k && a.skip == b.skip && a.stress == b.stress;
+         a.share == b.share && a.split_k == b.split_k && a.skip == b.skip && a.stress == b.stress &&
+         a.group == b.group;
 }
 bool same_sched(const cm_plan &a, const cm_plan &b) {
   return same_plan_desc(a.desc, b.desc) && a.chunks == b.chunks && a.n_steps == b.n_steps && a.arc_cw == b.arc_cw &&
          a.arc_ccw == b.arc_ccw && a.tile_m == b.tile_m && a.tile_n == b.tile_n && a.n_ops == b.n_ops &&
-         a.n_jobs == b.n_jobs && a.n_events == b.n_events && a.ws_bytes == b.ws_bytes && a.split == b.split;
+         a.n_jobs == b.n_jobs && a.n_events == b.n_events && a.ws_bytes == b.ws_bytes && a.split == b.split &&
+         a.n_launches == b.n_launches && a.slots == b.slots &&
+         std::memcmp(a.group_len, b.group_len, sizeof a.group_len) == 0;
 }
 
 }  // namespace

@@ -66,12 +66,14 @@ std::string plan_key(const cm_plan &p) {
   const cm_plan_desc &d = p.desc;
   char buf[512];
   std::snprintf(buf, sizeof buf,
-                "%d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %a %a %a %d %d %d %d|%d %d %d %d %d %d %d %zu %d",
+                "%d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %a %a %a %d %d %d %d %d|%d %d %d %d %d %d %d %zu %d %d %d|",
                 d.op, d.n_ranks, d.m, d.k, d.n, d.dir, d.chunks, d.sched, d.in_dtype, d.out_dtype, d.n_comm, d.tile_m,
                 d.tile_n, d.exec_mode, d.copy_engine, d.bucket_bf16, d.hop_add, d.copy_gbps, d.mfma_tflops,
-                d.launch_us, d.act, d.share, d.split_k, d.skip * 1000003 + d.stress, p.chunks, p.n_steps, p.arc_cw, p.arc_ccw, p.tile_m, p.tile_n,
-                p.n_events, p.ws_bytes, p.split);
-  return buf;
+                d.launch_us, d.act, d.share, d.split_k, d.skip * 1000003 + d.stress, d.group, p.chunks, p.n_steps, p.arc_cw,
+                p.arc_ccw, p.tile_m, p.tile_n, p.n_events, p.ws_bytes, p.split, p.n_launches, p.slots);
+  std::string key = buf;
+  for (int i = 0; i < p.n_launches && i < CM_MAX_RANKS; ++i) key += std::to_string(p.group_len[i]) + ",";
+  return key;
 }
 
 // The caller's plan must be one that cm_ring_plan produced: re-derive it from
@@ -84,7 +86,9 @@ cm_status canonical_plan(const cm_plan &pl, cm_plan *canon) {
   if (canon->chunks != pl.chunks || canon->n_steps != pl.n_steps || canon->arc_cw != pl.arc_cw ||
       canon->arc_ccw != pl.arc_ccw || canon->tile_m != pl.tile_m || canon->tile_n != pl.tile_n ||
       canon->ws_bytes != pl.ws_bytes || canon->n_ops != pl.n_ops || canon->n_jobs != pl.n_jobs ||
-      canon->n_events != pl.n_events || canon->desc.dir != pl.desc.dir || canon->split != pl.split) {
+      canon->n_events != pl.n_events || canon->desc.dir != pl.desc.dir || canon->split != pl.split ||
+      canon->n_launches != pl.n_launches || canon->slots != pl.slots ||
+      std::memcmp(canon->group_len, pl.group_len, sizeof pl.group_len) != 0) {
     set_error("plan does not match what cm_ring_plan produces for its request");
     return CM_ERR_INVALID_ARG;
   }
@@ -102,6 +106,14 @@ cm_status fill_params(const cm_op_rec &o, const cm_job_rec *jobs, Launch &L) {
   p.N = o.cols;
   p.K = o.depth;
   p.n_jobs = o.n_jobs;
+  if (o.kind == CM_OPK_GEMM) {
+    // the kernel maps blocks to whole runs of b_share jobs
+    if (o.b_share < 0 || (o.b_share > 1 && o.n_jobs % o.b_share)) {
+      set_error("a launch of %d jobs cannot be cut into runs of %d", o.n_jobs, o.b_share);
+      return CM_ERR_SHAPE;
+    }
+    p.jobs_per_b = o.b_share > 1 ? o.b_share : 1;
+  }
   const cm_job_rec &j0 = jobs[0];
   p.lda = j0.lda;
   p.ldb = j0.ldb;

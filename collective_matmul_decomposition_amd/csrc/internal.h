@@ -11,6 +11,7 @@ namespace collmm {
 // Byte offsets of the workspace regions a plan uses.
 struct WsLayout {
   size_t slot_dir_bytes = 0;  // AG / RS decomposed: bytes of one direction's slots
+  size_t part_dir_bytes = 0;  // RS add-and-forward: bytes of one direction's partial slots
   size_t gather = 0;          // AG naive: gathered activations
   size_t partial = 0;         // RS pipe / naive: partial products
   size_t partial_bytes = 0;

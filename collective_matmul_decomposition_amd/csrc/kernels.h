@@ -23,6 +23,9 @@ struct GemmParams {
   int n_jobs;
   int tiles_m;               // row tiles per job
   int tiles_per_job;
+  int jobs_per_b;            // >= 1: consecutive jobs that read the same B (one
+                             // rank's grouped steps); their tiles of one B column
+                             // run next to each other so B is read once from HBM
   uint32_t a_off[kMaxJobs], b_off[kMaxJobs], c_off[kMaxJobs], in0_off[kMaxJobs], in1_off[kMaxJobs];
   uint8_t sel[kMaxJobs];
 };

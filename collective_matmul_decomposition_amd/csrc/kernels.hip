@@ -16,9 +16,12 @@
 //    fp32 blocks (+ in1, then optionally GELU): the split-K partials of one
 //    rank's step GEMM; fp32 in, fp32 or bf16 out.
 //
-// Block tile BM x BN x 64, 512 threads = 8 waves; operands are staged
-// through two LDS buffers by direct-to-LDS buffer loads (the next K-slab is in
-// flight while the current one is multiplied).  LDS rows are 128 bytes (64
+// Block tile BM x BN x 64, 8 MFMA waves (two per SIMD); operands are staged
+// through rings of LDS slabs by direct-to-LDS buffer loads (the next K-slabs
+// are in flight while the current one is multiplied).  The two largest tiles
+// add 4 loader waves that issue every load, so the MFMA waves never wait on
+// the vector-memory pipe, and give the weights (B, streamed from HBM) a
+// deeper ring than the activations (A, mostly L2 hits).  LDS rows are 128 bytes (64
 // bf16) with the 16-byte K-chunks XOR-swizzled by row so that the MFMA
 // operand reads spread over the banks.  Blocks are numbered so that each of
 // the 8 XCDs (which own separate L2 caches) works on whole jobs.
@@ -176,7 +179,7 @@ __device__ __forceinline__ void epilogue_mode(const f32x16 (&acc)[TM][TN], const
 // ADD: the launch has jobs that add in0/in1 in the epilogue.  Launches
 // without addends get their own instantiation, whose register allocation
 // is not sized for the addend reads.
-template <int BM, int BN, int WM, int WN, int BK, int AST, int BST, int NL, int LP, bool ADD>
+template <int BM, int BN, int WM, int WN, int BK, int AST, int BST, int NL, bool ADD>
 __global__ __launch_bounds__(64 * (WM * WN) + 64 * NL) void gemm_jobs_kernel(const GemmParams p) {
   // A (activations, shared by every tile of a job and mostly served from L2)
   // and B (weights, streamed from HBM once per launch) have separate LDS
@@ -197,11 +200,6 @@ __global__ __launch_bounds__(64 * (WM * WN) + 64 * NL) void gemm_jobs_kernel(con
   // stalls, and with it the MFMAs queued behind the load).
   constexpr int NLW = NL > 0 ? NL : MW;  // waves that issue loads
   static_assert(NL == 0 || NL == 2 || NL == 4, "loader waves");
-  // LP = 0: loads go straight to LDS (global_load_lds).  LP >= 2: the
-  // loader waves load into LP register sets (LP slabs ahead) and store to
-  // a ring of AST = BST LDS slabs with ds_write, AST - 1 slabs ahead of use;
-  // the weights use non-temporal loads.
-  static_assert(LP == 0 || (LP >= 2 && NL > 0 && AST == BST), "register-staged loads need loader waves and equal slab rings");
   static_assert(A_GROUPS % NLW == 0 && B_GROUPS % NLW == 0, "loads split evenly over the waves");
   static_assert(AST >= 2 && BST >= 2 && AST <= 6 && BST <= 6, "stages");
   static_assert(AST * A_SLAB + BST * B_SLAB <= 160 * 1024, "LDS");
@@ -213,8 +211,23 @@ __global__ __launch_bounds__(64 * (WM * WN) + 64 * NL) void gemm_jobs_kernel(con
   char *const sB = smem + AST * A_SLAB;
 
   const int lb = logical_block();
-  const int job = lb / p.tiles_per_job;
-  const int tile = lb - job * p.tiles_per_job;
+  // Jobs come in groups of jobs_per_b that share B.  Within a group the
+  // blocks run B column by B column, and for each column every job's row
+  // tiles in turn, so the group's tiles that read one B panel are dispatched
+  // together and the panel is fetched from HBM once.
+  int job, tile;
+  {
+    const int jpb = p.jobs_per_b > 1 ? p.jobs_per_b : 1;
+    const int gt = p.tiles_per_job * jpb;
+    const int grp = lb / gt;
+    int r = lb - grp * gt;
+    const int per_col = jpb * p.tiles_m;
+    const int col = r / per_col;
+    r -= col * per_col;
+    const int jj = r / p.tiles_m;
+    job = grp * jpb + jj;
+    tile = col * p.tiles_m + (r - jj * p.tiles_m);
+  }
   const int tm0 = (tile % p.tiles_m) * BM;
   const int tn0 = (tile / p.tiles_m) * BN;
   const uint32_t sel = p.sel[job];
@@ -337,7 +350,7 @@ __global__ __launch_bounds__(64 * (WM * WN) + 64 * NL) void gemm_jobs_kernel(con
   // Barrier kt separates the reads of slab kt-1 (every MFMA wave is past
   // them) from the loads issued after it into that slab's buffer, and makes
   // slab kt, which every loading wave waited for before it, visible.
-  if (LP == 0 && loader) {
+  if (loader) {
 #pragma unroll
     for (int j = -LEAD; j < 0; ++j) issue_iter(j);
   }
@@ -349,74 +362,12 @@ __global__ __launch_bounds__(64 * (WM * WN) + 64 * NL) void gemm_jobs_kernel(con
       issue_iter(kt);
       compute_slab(kt);
     }
-  } else if (loader && LP == 0) {
+  } else if (loader) {
     for (int kt = 0; kt < KT; ++kt) {
       wait_slab(kt);
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       issue_iter(kt);
-    }
-    return;
-  } else if (loader) {
-    // Slab j is loaded into register set j % RS, and stored to LDS slab
-    // j % SB during iteration j - SB + 1 (SB - 1 slabs before it is
-    // multiplied, into the slab the MFMA waves finished in the previous
-    // iteration); its register set then takes the loads of slab j + RS.
-    // The loads are issued by inline asm with explicit waits: the compiler's
-    // own wait insertion, which cannot tell the loop-carried register sets
-    // apart, would drain every outstanding load before each store and leave
-    // only one slab in flight.  The loaded registers feed LDS stores only.
-    constexpr int RS = LP > 0 ? LP : 2, SB = AST;
-    static_assert(RS >= 2 && (LA + LB) * (RS - 1) < 64, "register sets");
-    i32x4 ra[RS][LA], rb[RS][LB];
-    auto gload = [&](int kt, int set) {
-      if (kt < KT) {
-        const uint32_t koff = (uint32_t)kt * BK * 2;
-        const char *a = Abase + koff;
-        const char *b = Bbase + koff;
-#pragma unroll
-        for (int i = 0; i < LA; ++i)
-          asm volatile("global_load_dwordx4 %0, %1, %2" : "=v"(ra[set][i]) : "v"(a_src[i]), "s"(a) : "memory");
-#pragma unroll
-        for (int i = 0; i < LB; ++i)
-          asm volatile("global_load_dwordx4 %0, %1, %2 nt" : "=v"(rb[set][i]) : "v"(b_src[i]), "s"(b) : "memory");
-      }
-    };
-    // Store slab j: first wait until only the loads of slabs j+1 .. j+RS-1
-    // (those that exist) are outstanding, then wait for the stores, which
-    // also frees the register set for new loads.
-    auto lstore = [&](int kt, int set) {
-      if (kt < KT) {
-        int younger = 0;
-#pragma unroll
-        for (int q = 1; q < RS; ++q) younger += (kt + q < KT) ? LA + LB : 0;
-        wait_vmcnt_upto(younger);
-        char *slab_a = sA + (kt % SB) * A_SLAB + lane * 16;
-        char *slab_b = sB + (kt % SB) * B_SLAB + lane * 16;
-#pragma unroll
-        for (int i = 0; i < LA; ++i) *reinterpret_cast<i32x4 *>(slab_a + (i * NLW + lw) * 1024) = ra[set][i];
-#pragma unroll
-        for (int i = 0; i < LB; ++i) *reinterpret_cast<i32x4 *>(slab_b + (i * NLW + lw) * 1024) = rb[set][i];
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      }
-    };
-#pragma unroll
-    for (int j = 0; j < RS; ++j) gload(j, j);
-#pragma unroll
-    for (int j = 0; j < SB - 1; ++j) {
-      lstore(j, j % RS);
-      gload(j + RS, j % RS);
-    }
-    for (int kt = 0; kt < KT; kt += RS) {
-#pragma unroll
-      for (int u = 0; u < RS; ++u) {
-        if (kt + u < KT) {
-          __builtin_amdgcn_s_barrier();
-          asm volatile("" ::: "memory");
-          lstore(kt + u + SB - 1, (u + SB - 1) % RS);
-          gload(kt + u + SB - 1 + RS, (u + SB - 1) % RS);
-        }
-      }
     }
     return;
   } else {
@@ -560,10 +511,10 @@ bool gemm_tile_supported(int tm, int tn) {
   return gemm_launch_config(p, tm, tn, &L);
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int AST, int BST, int NL, int LP = 0>
+template <int BM, int BN, int WM, int WN, int BK, int AST, int BST, int NL>
 void pick_gemm(bool add, void **f, int *threads) {
-  *f = add ? reinterpret_cast<void *>(&gemm_jobs_kernel<BM, BN, WM, WN, BK, AST, BST, NL, LP, true>)
-           : reinterpret_cast<void *>(&gemm_jobs_kernel<BM, BN, WM, WN, BK, AST, BST, NL, LP, false>);
+  *f = add ? reinterpret_cast<void *>(&gemm_jobs_kernel<BM, BN, WM, WN, BK, AST, BST, NL, true>)
+           : reinterpret_cast<void *>(&gemm_jobs_kernel<BM, BN, WM, WN, BK, AST, BST, NL, false>);
   *threads = 64 * (WM * WN) + 64 * NL;
 }
 
@@ -572,8 +523,8 @@ bool gemm_launch_config(const GemmParams &p, int tm, int tn, KernelLaunch *out) 
   for (int j = 0; j < p.n_jobs && j < kMaxJobs; ++j) add = add || (p.sel[j] & 0xC0);
   void *f = nullptr;
   int threads = 0;
-  if (tm == 256 && tn == 256) pick_gemm<256, 256, 2, 4, 64, 2, 3, 0>(add, &f, &threads);
-  else if (tm == 256 && tn == 192) pick_gemm<256, 192, 4, 2, 64, 2, 2, 4, 2>(add, &f, &threads);
+  if (tm == 256 && tn == 256) pick_gemm<256, 256, 2, 4, 64, 2, 3, 4>(add, &f, &threads);
+  else if (tm == 256 && tn == 192) pick_gemm<256, 192, 4, 2, 64, 2, 4, 4>(add, &f, &threads);
   else if (tm == 256 && tn == 128) pick_gemm<256, 128, 4, 2, 64, 2, 5, 0>(add, &f, &threads);
   else if (tm == 128 && tn == 256) pick_gemm<128, 256, 2, 4, 64, 2, 3, 0>(add, &f, &threads);
   else if (tm == 128 && tn == 128) pick_gemm<128, 128, 2, 4, 64, 3, 4, 0>(add, &f, &threads);

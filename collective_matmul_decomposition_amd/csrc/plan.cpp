@@ -37,6 +37,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <functional>
 #include <string>
 #include <vector>
 
@@ -121,10 +122,12 @@ const char *last_error() { return g_last_error.c_str(); }
 
 // ------------------------------------------------------------ workspace map
 // AG decomposed: receive slots, chunk-major so that one chunk of a range of
-//   ranks is contiguous:  slot[dir][p][j][r][m/c][k] bf16.
+//   ranks is contiguous:  slot[dir][p][j][r][m/c][k] bf16, p < plan.slots (2,
+//   alternating by step, or one per hop when steps are grouped per launch).
 // AG naive: gathered activations G[r][T][k] bf16.
-// RS decomposed: buckets  bkt[dir][p][j][r][m][n/c] fp32 (bf16 with bucket_bf16);
-//   with add-and-forward hops also partial slots of the same shape after them.
+// RS decomposed: buckets  bkt[dir][p][j][r][m][n/c] fp32 (bf16 with bucket_bf16),
+//   p < 2; with add-and-forward hops also partial slots
+//   part[dir][q][j][r][m][n/c] fp32 after them, q < plan.slots.
 // RS pipe / naive: partials P[r][j][T][n/c] fp32, then ring slots
 //   R[p][r][m][n/c] fp32; with add-and-forward hops the ring slots are per
 //   chunk, R[j][p][r][m][n/c].
@@ -153,7 +156,7 @@ WsLayout ws_layout(const cm_plan &pl) {
       L.gather = 0;
       L.total = N * T * k * 2;
     } else {
-      L.slot_dir_bytes = 2 * N * m * k * 2;
+      L.slot_dir_bytes = (size_t)std::max(2, pl.slots) * N * m * k * 2;
       L.total = ndir * L.slot_dir_bytes;
     }
   } else if (d.op == CM_OP_GEMM_RS && d.sched == CM_SCHED_DECOMPOSED && d.dir == CM_RING_DIRECT) {
@@ -166,9 +169,10 @@ WsLayout ws_layout(const cm_plan &pl) {
   } else if (d.op == CM_OP_GEMM_RS && d.sched == CM_SCHED_DECOMPOSED) {
     L.slot_dir_bytes = 2 * N * m * n * (d.bucket_bf16 ? 2 : 4);  // c chunks of n/c columns
     L.total = ndir * L.slot_dir_bytes;
-    if (d.hop_add) {  // + partial slots P[dir][p][j][r][m][n/c] fp32
+    if (d.hop_add) {  // + partial slots part[dir][q][j][r][m][n/c] fp32
       L.partial = L.total;
-      L.total *= 2;
+      L.part_dir_bytes = (size_t)std::max(2, pl.slots) * N * m * n * 4;
+      L.total += ndir * L.part_dir_bytes;
     }
   } else if (d.hop_add) {  // PIPE / RS naive with add-and-forward hops: ring slots per chunk
     L.partial = 0;
@@ -256,6 +260,7 @@ cm_status validate_desc(const cm_plan_desc &d) {
     return CM_ERR_UNSUPPORTED;
   }
   if (!d.share && d.split_k) { set_error("split_k applies to one rank's share (share = 1) only"); return CM_ERR_INVALID_ARG; }
+  if (d.group < 0 || d.group > CM_MAX_RANKS) { set_error("group %d outside 0..%d", d.group, CM_MAX_RANKS); return CM_ERR_INVALID_ARG; }
   if (d.share) {
     if (!(d.op == CM_OP_AG_GEMM || d.op == CM_OP_GEMM_RS) || d.dir != CM_RING_UNI || d.sched != CM_SCHED_DECOMPOSED ||
         d.chunks > 1 || d.hop_add || d.bucket_bf16) {
@@ -395,6 +400,138 @@ double estimate_naive(const cm_plan_desc &d) {
   }
   const double round = hop_us(d, N * m * n * 4.0, d.n_ranks, per_lane) + d.launch_us;  // copy + add
   return gemm_us(d, d.n_ranks, N * m, n, k) + (N - 1) * round;
+}
+
+// ------------------------------------------------- steps grouped per launch
+// A launch that multiplies g steps of every rank reads each rank's weights
+// once.  Its time is modelled as the part of the weight stream that the MFMA
+// work does not hide plus the MFMA work at the compute-bound rate of the
+// chosen tile (measured on MI355X for the GPT-3 MLP step launches: about
+// 60 us of unhidden weight stream per 1.2 GB of weights, and 1.55 PFLOP/s
+// scaled by the tile's efficiency).
+constexpr double kGroupComputeTflops = 1550.0;
+constexpr double kWeightUnhiddenGBps = 20000.0;
+constexpr int kMaxGroupAuto = 4;
+// Hop and add rates beside the step GEMMs, measured in the same runs (GPT-3
+// MLP: a 50 MB AllGather hop step by SDMA takes about 150 us, by the CU copy
+// kernel about 75 us; an add-and-forward step of 302 MB about 110 us).  They
+// steer only the grouping choice, which depends on nothing else of the
+// request's cost-model inputs, so that re-planning a plan's own request
+// reproduces it.
+constexpr double kGroupSdmaGBps = 400.0, kGroupSdmaCopyUs = 25.0;
+constexpr double kGroupCuCopyGBps = 800.0, kGroupCuCopyUs = 10.0;
+constexpr double kGroupAddGBps = 2750.0;
+
+double group_launch_us(const cm_plan_desc &d, int jobs, int share, double rows, double cols, double depth) {
+  int tm, tn;
+  const double eff = choose_tile((int)rows, (int)cols, jobs, &tm, &tn);
+  const double flops = 2.0 * jobs * rows * cols * depth;
+  const double wbytes = (double)jobs / std::max(1, share) * cols * depth * 2.0;
+  return d.launch_us + wbytes / (kWeightUnhiddenGBps * 1e9) * 1e6 + flops / (kGroupComputeTflops * 1e12 * eff) * 1e6;
+}
+
+// Jobs per rank of step s: AG step 0 multiplies the own shard only; a later
+// step one shard per direction whose arc reaches it.  RS (add-and-forward):
+// the owner's step one job, others one per direction that has started.
+int step_dirs(const cm_plan &p, int s) {
+  const cm_plan_desc &d = p.desc;
+  const bool bi = d.dir == CM_RING_BI;
+  if (d.op == CM_OP_AG_GEMM) {
+    if (s == 0) return 1;
+    return (s <= p.arc_cw ? 1 : 0) + (bi && s <= p.arc_ccw ? 1 : 0);
+  }
+  const int last = bi ? p.arc_cw : d.n_ranks - 1;
+  if (s == last) return 1;
+  return 1 + (bi && s >= p.arc_cw - p.arc_ccw ? 1 : 0);
+}
+
+// Predicted time of the op with the given launch partition (group lengths in
+// step order), by a timeline: AllGather hops run back to back on the comm
+// lane(s) and a launch starts when the previous one has ended and the hop
+// that brings its last step's shard has arrived; ReduceScatter launches run
+// back to back, each step's add-and-forward follows its launch and the
+// previous add, and the owner's final launch waits for the last add.
+double group_timeline(const cm_plan &p, const std::vector<int> &len) {
+  const cm_plan_desc &d = p.desc;
+  const int N = d.n_ranks;
+  const bool bi = d.dir == CM_RING_BI;
+  const int lanes = std::min(d.n_comm, kMaxLanes);
+  double t = 0;
+  int s = 0;
+  if (d.op == CM_OP_AG_GEMM) {
+    const int per_lane = std::max(1, std::min(2, N / std::max(1, lanes)));
+    const bool sdma = d.copy_engine == CM_COPY_SDMA;
+    const double gbps = sdma ? kGroupSdmaGBps : kGroupCuCopyGBps;
+    const double lat = sdma ? kGroupSdmaCopyUs : kGroupCuCopyUs;
+    // one hop step of one direction (its lanes in parallel); both directions
+    // share the lane unless there are two
+    const double bytes = (double)N * d.m * d.k * 2.0 / std::max(1, std::min(lanes, N));
+    const double hop = (bytes / (gbps * 1e9) * 1e6 + per_lane * lat) * (bi && lanes < 2 ? 2.0 : 1.0);
+    for (int g : len) {
+      const int b = s + g - 1;
+      int jpr = 0;
+      for (int q = s; q <= b; ++q) jpr += step_dirs(p, q);
+      const double ready = b >= 1 ? std::min(b, p.arc_cw) * hop : 0.0;
+      t = std::max(t, ready) + group_launch_us(d, N * jpr, jpr, d.m, d.n, d.k);
+      s = b + 1;
+    }
+    return t;
+  }
+  const int last = bi ? p.arc_cw : N - 1;
+  const double add1 = (double)N * d.m * d.n * 4.0 * 3.0 / (kGroupAddGBps * 1e9) * 1e6;
+  double adds = 0;
+  for (int g : len) {
+    const int b = s + g - 1;
+    int jpr = 0;
+    for (int q = s; q <= b; ++q) jpr += step_dirs(p, q);
+    if (b == last) t = std::max(t, adds);
+    t += group_launch_us(d, N * jpr, jpr, d.m, d.n, d.k);
+    for (int q = s; q <= b && q < last; ++q)
+      if (q >= 1) adds = std::max(adds, t) + (step_dirs(p, q) - (bi && q == p.arc_cw - p.arc_ccw ? 1 : 0)) * add1 + d.launch_us;
+    s = b + 1;
+  }
+  return t;
+}
+
+// Choose the launch partition: every composition of the steps into groups of
+// at most gmax (the ReduceScatter's owner step alone at the end), or, beyond
+// 16 steps, equal groups (AllGather: the first step alone, so its hops start
+// at once).  The shortest predicted time wins; ties keep fewer launches.
+double choose_groups(const cm_plan &p, int gmax, std::vector<int> *best) {
+  const cm_plan_desc &d = p.desc;
+  const bool rs = d.op != CM_OP_AG_GEMM;
+  const int S = p.n_steps - (rs ? 1 : 0);  // steps free to group
+  double best_t = -1;
+  auto consider = [&](std::vector<int> len) {
+    if (rs) len.push_back(1);
+    const double t = group_timeline(p, len);
+    if (best_t < 0 || t < best_t - 1e-6 || (t < best_t + 1e-6 && len.size() < best->size())) {
+      best_t = t;
+      *best = len;
+    }
+  };
+  if (S <= 16) {
+    std::vector<int> cur;
+    // depth-first over compositions of S with parts <= gmax
+    std::function<void(int)> rec = [&](int rem) {
+      if (rem == 0) { consider(cur); return; }
+      for (int g = 1; g <= std::min(gmax, rem); ++g) {
+        cur.push_back(g);
+        rec(rem - g);
+        cur.pop_back();
+      }
+    };
+    rec(S);
+  } else {
+    for (int g = 1; g <= gmax; ++g) {
+      std::vector<int> len;
+      int rem = S;
+      if (!rs && g > 1) { len.push_back(1); --rem; }
+      while (rem > 0) { len.push_back(std::min(g, rem)); rem -= len.back(); }
+      consider(len);
+    }
+  }
+  return best_t;
 }
 
 }  // namespace
@@ -537,6 +674,30 @@ cm_status plan(const cm_plan_desc *desc, cm_plan *out) {
   p.est_gemm_us = e.g;
   p.est_hop_us = e.h;
   p.est_total_us = d.sched == CM_SCHED_NAIVE ? estimate_naive(d) : e.total;
+  // Launches per chunk: one per step, or consecutive steps grouped.
+  if (d.sched == CM_SCHED_DECOMPOSED && d.op != CM_OP_GEMM_RS_PIPE) {
+    p.n_launches = p.n_steps;
+    for (int i = 0; i < p.n_steps && i < CM_MAX_RANKS; ++i) p.group_len[i] = 1;
+    p.slots = 2;
+    const bool groupable = N > 1 && c == 1 && (d.dir == CM_RING_UNI || bi) &&
+                           (d.op == CM_OP_AG_GEMM || (d.op == CM_OP_GEMM_RS && d.hop_add));
+    if (groupable && d.group != 1) {
+      const int ndir = bi ? 2 : 1;
+      int gmax = d.group == 0 ? kMaxGroupAuto : d.group;
+      gmax = std::min(gmax, std::max(1, kJobCap / (N * ndir)));
+      gmax = std::min(gmax, p.n_steps);
+      std::vector<int> ones(p.n_steps, 1), best;
+      const double t1 = group_timeline(p, ones);
+      const double tb = choose_groups(p, gmax, &best);
+      if (best.size() < ones.size()) {
+        p.n_launches = (int)best.size();
+        for (int i = 0; i < CM_MAX_RANKS; ++i) p.group_len[i] = i < p.n_launches ? best[i] : 0;
+        p.slots = d.op == CM_OP_AG_GEMM ? std::max(2, p.arc_cw) : std::max(2, p.n_steps);
+        // the grouped model's gain applied to the per-step estimate
+        if (t1 > 0) p.est_total_us *= tb / t1;
+      }
+    }
+  }
   p.declined = (N > 1 && !e.hidden) ? 1 : 0;
   int rows = d.op == CM_OP_AG_GEMM ? d.m / c : d.m;
   int cols = d.op == CM_OP_AG_GEMM ? d.n : d.n / c;
@@ -629,9 +790,10 @@ struct Builder {
     j.add_dtype = CM_F32;
     return j;
   }
-  void gemm(const std::vector<cm_job_rec> &jobs, int rows, int cols, int depth) {
+  void gemm(const std::vector<cm_job_rec> &jobs, int rows, int cols, int depth, int b_share = 1) {
     if (jobs.empty()) return;
     cm_op_rec o = base(CM_OPK_GEMM, 0);
+    o.b_share = b_share;
     o.act = d.op == CM_OP_AG_GEMM ? d.act : CM_ACT_NONE;
     o.first_job = (int)prog.jobs.size();
     o.n_jobs = (int)jobs.size();
@@ -729,6 +891,7 @@ struct Builder {
   }
 
   void ag_decomposed() {
+    if (grouped()) { ag_grouped(); return; }
     const bool direct = d.dir == CM_RING_DIRECT;
     const int ndir = d.dir == CM_RING_BI ? 2 : 1;
     const size_t mc = m / c;
@@ -844,6 +1007,223 @@ struct Builder {
           step_gemm();
         }
       }
+    }
+    exit_();
+  }
+
+  bool grouped() const {
+    for (int i = 0; i < p.n_launches && i < CM_MAX_RANKS; ++i)
+      if (p.group_len[i] > 1) return true;
+    return false;
+  }
+
+  // ---------------------------------------------- AG, steps grouped per launch
+  // One chunk per shard; launch i multiplies steps [a, b] of every rank (one
+  // job per rank, step and direction, rank-major so that a rank's jobs, which
+  // read the same weights, are adjacent: b_share).  Every hop has a receive
+  // slot of its own (slot s holds what hop s brought: the shard of step s + 1),
+  // so no copy waits for a reader.  Emission order: the hops a launch needs,
+  // the launch, then the hops the next launch needs (they run beside it).
+  void ag_grouped() {
+    const int ndir = d.dir == CM_RING_BI ? 2 : 1;
+    const int P = std::max(2, p.slots);
+    const size_t chunk_bytes = m * k * 2;
+    auto slot_off = [&](int dir, int q, int r) -> size_t {
+      return dir * L.slot_dir_bytes + (((size_t)q * N + r) * chunk_bytes);
+    };
+    std::vector<std::vector<Group>> G(ndir);
+    for (int dr = 0; dr < ndir; ++dr) G[dr] = groups(dr, ndir);
+    const int arcs[2] = {p.arc_cw, p.arc_ccw};
+    const int max_arc = std::max(p.arc_cw, ndir == 2 ? p.arc_ccw : 0);
+    std::vector<std::vector<std::vector<int>>> ehop(p.n_steps, std::vector<std::vector<int>>(ndir));
+    std::vector<int> egemm(p.n_steps, -1);
+    entry();
+    int emitted = 0;  // hops 0 .. emitted-1 are in the program
+    auto emit_hop = [&](int s) {
+      cur_step = s; cur_chunk = 0;
+      for (int dr = 0; dr < ndir; ++dr) {
+        if (s >= arcs[dr]) continue;
+        const int shift = dr == 0 ? 1 : -1;
+        ehop[s][dr].assign(G[dr].size(), -1);
+        for (size_t gi = 0; gi < G[dr].size(); ++gi) {
+          const Group &g = G[dr][gi];
+          // WAR: slot s % P last held hop(s - P)'s shard, read by the launch of
+          // step s - P + 1 and, as the source of hop(s - P + 1), by the
+          // downstream ranks' copies
+          if (s >= P) {
+            wait(g.stream, egemm[s - P + 1]);
+            for (int r = g.a; r < g.b; ++r) {
+              int down = group_of(G[dr], mod(r + shift, N));
+              if (down != (int)gi) wait(g.stream, ehop[s - P + 1][dr][down]);
+            }
+          }
+          // RAW: the source slot was filled by hop(s-1) from the upstream ranks
+          if (s >= 1)
+            for (int r = g.a; r < g.b; ++r) {
+              int up = group_of(G[dr], mod(r - shift, N));
+              if (up != (int)gi) wait(g.stream, ehop[s - 1][dr][up]);
+            }
+          if (s == 0)
+            shifted_copy(g.stream, CM_BUF_X, 0, CM_BUF_WS, slot_off(dr, 0, 0), chunk_bytes, g.a, g.b, shift);
+          else
+            shifted_copy(g.stream, CM_BUF_WS, slot_off(dr, (s - 1) % P, 0), CM_BUF_WS, slot_off(dr, s % P, 0),
+                         chunk_bytes, g.a, g.b, shift);
+          ehop[s][dr][gi] = record(g.stream);
+        }
+      }
+    };
+    int a = 0;
+    for (int li = 0; li < p.n_launches; ++li) {
+      const int b = a + p.group_len[li] - 1;
+      while (emitted < std::min(b, max_arc)) emit_hop(emitted++);
+      cur_step = a; cur_chunk = 0;
+      // RAW: every step's shard arrived with hop(step - 1); the latest hops
+      // first, so the waits that they already imply are left out
+      for (int s = b; s >= std::max(a, 1); --s)
+        for (int dr = 0; dr < ndir; ++dr)
+          if (s - 1 < arcs[dr])
+            for (int e : ehop[s - 1][dr]) wait(0, e);
+      std::vector<cm_job_rec> jobs;
+      int per_rank = 0;
+      for (int r = 0; r < N; ++r) {
+        int cnt = 0;
+        for (int s = a; s <= b; ++s)
+          for (int dr = 0; dr < ndir; ++dr) {
+            if (s > 0 && s > arcs[dr]) continue;
+            if (s == 0 && dr > 0) continue;
+            cm_job_rec jb = job0();
+            jb.rank = r;
+            jb.dir = dr;
+            const int shard = s == 0 ? r : (dr == 0 ? mod(r - s, N) : mod(r + s, N));
+            jb.index = shard;
+            if (s == 0) {
+              jb.a_buf = CM_BUF_X;
+              jb.a_off = (size_t)r * m * k * 2;
+            } else {
+              jb.a_buf = CM_BUF_WS;
+              jb.a_off = slot_off(dr, (s - 1) % P, r);
+            }
+            jb.lda = (int)k;
+            jb.b_buf = CM_BUF_W;
+            jb.b_off = (size_t)r * n * k * 2;
+            jb.ldb = (int)k;
+            jb.c_buf = CM_BUF_Y;
+            jb.c_dtype = d.out_dtype;
+            jb.c_off = ((size_t)r * T + (size_t)shard * m) * n * (d.out_dtype == CM_F32 ? 4 : 2);
+            jb.ldc = (int)n;
+            jobs.push_back(jb);
+            ++cnt;
+          }
+        per_rank = cnt;
+      }
+      gemm(jobs, (int)m, (int)n, (int)k, per_rank);
+      const int e = record(0);
+      for (int s = a; s <= b; ++s) egemm[s] = e;
+      const int next_b = li + 1 < p.n_launches ? b + p.group_len[li + 1] : max_arc;
+      while (emitted < std::min(next_b, max_arc)) emit_hop(emitted++);
+      a = b + 1;
+    }
+    exit_();
+  }
+
+  // ------------------------- RS with add-and-forward hops, steps grouped
+  // One chunk.  Launch i computes the partial products of steps [a, b] of
+  // every rank (rank-major, b_share jobs per rank); every step has a partial
+  // slot of its own.  A direction's first step stores straight into the next
+  // rank's bucket slot; each later step's add-and-forward (partial + arrived
+  // bucket -> the next rank's slot) follows its launch on the first comm
+  // stream, in step order.  The owner's step is the last launch, alone: it
+  // waits for the last add and adds the arrived bucket(s) in its epilogue.
+  void rs_hop_add_grouped() {
+    const bool bi = d.dir == CM_RING_BI;
+    const int ndir = bi ? 2 : 1;
+    const int Pp = std::max(2, p.slots);
+    const size_t blk = m * n * 4;
+    const int osz = d.out_dtype == CM_F32 ? 4 : 2;
+    auto bkt = [&](int dir, int par, int r) -> size_t { return dir * L.slot_dir_bytes + (((size_t)par * N + r) * blk); };
+    auto part = [&](int dir, int q, int r) -> size_t {
+      return L.partial + dir * L.part_dir_bytes + (((size_t)q * N + r) * blk);
+    };
+    const int Lc = p.arc_cw, R = p.arc_ccw;
+    const int last = bi ? Lc : N - 1;
+    const int arc = bi ? Lc : N - 1;
+    const int first[2] = {0, Lc - R};
+    const int red = 1;
+    std::vector<int> ered(last + 1, -1);
+    entry();
+    int a = 0;
+    for (int li = 0; li < p.n_launches; ++li) {
+      const int b = a + p.group_len[li] - 1;
+      cur_step = a; cur_chunk = 0;
+      if (b == last) {
+        if (last >= 1) wait(0, ered[last - 1]);  // RAW: the arrived buckets
+      } else {
+        for (int s = b; s >= a; --s)
+          if (s >= Pp) wait(0, ered[s - Pp]);  // WAR: partial slot s % Pp was read by add(s - Pp)
+      }
+      std::vector<cm_job_rec> jobs;
+      int per_rank = 0;
+      for (int r = 0; r < N; ++r) {
+        int cnt = 0;
+        for (int s = a; s <= b; ++s) {
+          auto mk = [&](int dr, int bucket) {
+            cm_job_rec jb = job0();
+            jb.rank = r; jb.dir = dr; jb.index = bucket;
+            jb.a_buf = CM_BUF_X; jb.a_off = ((size_t)r * T + (size_t)bucket * m) * k * 2; jb.lda = (int)k;
+            jb.b_buf = CM_BUF_W; jb.b_off = (size_t)r * n * k * 2; jb.ldb = (int)k;
+            jb.ld_in = (int)n;
+            return jb;
+          };
+          if (s == last) {
+            cm_job_rec jb = mk(0, r);
+            jb.c_buf = CM_BUF_Y; jb.c_off = (size_t)r * m * n * osz; jb.ldc = (int)n;
+            jb.c_dtype = d.out_dtype;
+            if (N > 1) { jb.in0_buf = CM_BUF_WS; jb.in0_off = bkt(0, s % 2, r); }
+            if (bi && R >= 1) { jb.in1_buf = CM_BUF_WS; jb.in1_off = bkt(1, s % 2, r); }
+            jobs.push_back(jb);
+            ++cnt;
+            continue;
+          }
+          for (int dr = 0; dr < ndir; ++dr) {
+            if (s < first[dr]) continue;
+            const int shift = dr == 0 ? 1 : -1;
+            const int q = dr == 0 ? mod(r + (arc - s), N) : mod(r - (Lc - s), N);
+            cm_job_rec jb = mk(dr, q);
+            jb.c_buf = CM_BUF_WS; jb.ldc = (int)n; jb.c_dtype = CM_F32;
+            jb.c_off = s == first[dr] ? bkt(dr, (s + 1) % 2, mod(r + shift, N)) : part(dr, s % Pp, r);
+            jobs.push_back(jb);
+            ++cnt;
+          }
+        }
+        per_rank = cnt;
+      }
+      gemm(jobs, (int)m, (int)n, (int)k, per_rank);
+      const int eg = record(0);
+      if (b == last) break;
+      for (int s = a; s <= b; ++s) {
+        cur_step = s;
+        std::vector<cm_job_rec> rj;
+        for (int dr = 0; dr < ndir; ++dr) {
+          if (s <= first[dr]) continue;
+          const int shift = dr == 0 ? 1 : -1;
+          for (int r = 0; r < N; ++r) {
+            cm_job_rec jb = job0();
+            jb.rank = r; jb.dir = dr;
+            jb.index = dr == 0 ? mod(r + (arc - s), N) : mod(r - (Lc - s), N);
+            jb.in0_buf = CM_BUF_WS; jb.in0_off = part(dr, s % Pp, r);
+            jb.in1_buf = CM_BUF_WS; jb.in1_off = bkt(dr, s % 2, r);
+            jb.ld_in = (int)n;
+            jb.c_buf = CM_BUF_WS; jb.c_off = bkt(dr, (s + 1) % 2, mod(r + shift, N)); jb.ldc = (int)n;
+            jb.c_dtype = CM_F32;
+            rj.push_back(jb);
+          }
+        }
+        if (rj.empty()) continue;  // every direction's first step stored straight into the slots
+        wait(red, eg);  // RAW: the partials (and, through the compute stream, earlier direct stores)
+        reduce(red, rj, (int)m, (int)n);
+        ered[s] = record(red);
+      }
+      a = b + 1;
     }
     exit_();
   }
@@ -1019,6 +1399,7 @@ struct Builder {
   // arrived bucket(s) in its epilogue as in rs_decomposed.  fp32 addition
   // commutes, so every sum equals the epilogue's bitwise.
   void rs_hop_add() {
+    if (grouped()) { rs_hop_add_grouped(); return; }
     const bool bi = d.dir == CM_RING_BI;
     const int ndir = bi ? 2 : 1;
     const size_t nc = n / c;
@@ -1028,7 +1409,7 @@ struct Builder {
       return dir * L.slot_dir_bytes + ((((size_t)par * c + j) * N + r) * blk);
     };
     auto part = [&](int dir, int par, int j, int r) -> size_t {
-      return L.partial + dir * L.slot_dir_bytes + ((((size_t)par * c + j) * N + r) * blk);
+      return L.partial + dir * L.part_dir_bytes + ((((size_t)par * c + j) * N + r) * blk);
     };
     const int Lc = p.arc_cw, R = p.arc_ccw;
     const int last = bi ? Lc : N - 1;

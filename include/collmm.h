@@ -225,6 +225,18 @@ typedef struct {
                             the program's ordering right, the results equal those
                             of a run without stress bit for bit; a missing wait
                             shows up as changed or NaN outputs. */
+  int group;             /* steps per GEMM launch, for the decomposed AllGather->GEMM
+                            and the add-and-forward GEMM->ReduceScatter (hop_add = 1)
+                            on a uni- or bidirectional ring with one chunk: 0 = the
+                            cost model picks how consecutive steps are grouped (at
+                            most 4 per launch), 1 = one step per launch, g >= 2 = at
+                            most g.  A launch multiplies every rank's shards (or
+                            bucket rows) of its steps, so each rank's weights are
+                            streamed once per launch instead of once per step; a
+                            step still uses only shards that have arrived, and the
+                            ReduceScatter owner's final step is always a launch of
+                            its own.  Other ops and chunkings use one step per
+                            launch. */
 } cm_plan_desc;
 
 /* The resolved schedule.  Plain data: no heap, nothing to destroy. */
@@ -244,6 +256,13 @@ typedef struct {
   double est_hop_us;   /* cost model: one step's hop time (all ranks, one chunk) */
   double est_total_us; /* cost model: the whole op */
   int split;           /* share = 1: the K slices per step GEMM (S); else 0 */
+  int n_launches;      /* decomposed ring ops: GEMM launches per chunk (n_steps when
+                          every launch is one step); else 0 */
+  int group_len[CM_MAX_RANKS]; /* steps of each of those launches, in order */
+  int slots;           /* receive slots per rank and direction (AllGather) or
+                          partial-product slots (add-and-forward ReduceScatter):
+                          2, alternating by step, or one per step when steps are
+                          grouped (no slot is then written twice) */
 } cm_plan;
 
 /*
@@ -283,7 +302,16 @@ typedef struct {
  */
 
 /*
- * Build a plan.  Fails with CM_ERR_SHAPE unless: N*m <= 2^24 rows; k and n
+ * Build a plan: the ring schedule of one decomposed collective matmul, i.e.
+ * which shard (AllGather) or bucket (ReduceScatter) every virtual rank
+ * multiplies at every step, which hop moves it next, the chunk count and the
+ * GEMM tile.  Defined by the per-step order of "The idea" on the
+ * decomposition page (each partial uses only shards that have arrived; the
+ * accumulator circulates and reaches its home last), the ring hops of
+ * sections 3 and 5 of the Megatron page, the chunk count as a tuning knob
+ * (section 6 there) and the peak-rate cost model that may decline to
+ * decompose ("Knowing when to decline").
+ * Fails with CM_ERR_SHAPE unless: N*m <= 2^24 rows; k and n
  * are multiples of 64; one virtual rank's operands stay under 4 GiB
  * (N*m*k*2 and n*k*2 bytes); AG: c divides m; RS: c divides n and n/c is a
  * multiple of 64; PIPE: same as RS.  Host only: makes no HIP call.
@@ -340,6 +368,10 @@ typedef struct {
   size_t src_off, dst_off, bytes;
   int act;               /* GEMM: cm_act of the epilogue (launches without addends
                             only); REDUCE: cm_act applied to the sum */
+  int b_share;           /* GEMM: jobs come in runs of b_share consecutive jobs that
+                            read the same B (one rank's grouped steps); the kernel
+                            runs a run's tiles of one B column together.  n_jobs is
+                            a multiple of it; 1 = no sharing */
 } cm_op_rec;
 
 /*
@@ -397,6 +429,9 @@ cm_status cm_trace_read(cm_trace *trace, cm_span *spans, int cap, int *n_spans, 
  * AllGather -> GEMM (see "Layouts").  Decomposed schedule: at step s rank r
  * multiplies the shard it holds into rows of Y_r belonging to that shard
  * (the slice update), while the same shard is copied to the next rank.
+ * Defined by section 3 of the Megatron page (P2P AllGather overlap) and the
+ * AllGather->Einsum loop of "The idea" on the decomposition page (a partial
+ * einsum per arrived shard, written into its slice of the result).
  *   plan     from cm_ring_plan with op CM_OP_AG_GEMM
  *   x, w, y  device pointers, 16-byte aligned
  *   ws       device workspace of ws_bytes >= plan->ws_bytes (receive slots)
@@ -415,7 +450,11 @@ cm_status cm_ag_gemm(const cm_plan *plan, const void *x, const void *w, void *y,
  * writes Out_q.  CM_OP_GEMM_RS_PIPE: the output columns are split into c
  * chunks; each chunk's full partial products are computed in one launch and
  * reduce-scattered around the ring (copy + add) while the next chunk
- * computes.  Arguments as for cm_ag_gemm; x holds H.
+ * computes.  Defined by section 5 of the Megatron page (P2P ReduceScatter
+ * overlap) with the Einsum->ReduceScatter loop of "The idea" on the
+ * decomposition page (the circulating accumulator), and by section 6 of the
+ * Megatron page for the pipeline-chunk variant.  Arguments as for
+ * cm_ag_gemm; x holds H.
  */
 cm_status cm_gemm_rs(const cm_plan *plan, const void *x, const void *w, void *y, void *ws,
                      size_t ws_bytes, void *compute, void *const *comm, int n_comm,

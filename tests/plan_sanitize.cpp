@@ -120,6 +120,12 @@ int main(int argc, char **argv) {
     d.act = variant == 3 && op == CM_OP_AG_GEMM ? CM_ACT_GELU : CM_ACT_NONE;
     d.skip = (variant + N) % 3;
     check(d);
+    // steps grouped per launch (AllGather, add-and-forward ReduceScatter)
+    for (int g : {1, 2, 3, 4}) {
+      d.group = g;
+      if (op <= CM_OP_GEMM_RS && (it + g) % 3 == 0) check(d);
+    }
+    d.group = 0;
     if (op <= CM_OP_GEMM_RS && dir == 0 && sched == 0 && chunks <= 1 && !hop) {
       d.share = 1;
       d.chunks = 0;
@@ -141,6 +147,7 @@ int main(int argc, char **argv) {
     bad.dir = v % 4;
     bad.chunks = v;
     bad.n_comm = v % 40;
+    bad.group = v;
     check(bad);
   }
   cm_plan_desc ag{}, rs{};

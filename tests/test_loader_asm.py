@@ -1,13 +1,11 @@
-"""The GEMM loader's asynchronously written registers, checked in the gfx950
+"""Inline-asm vector loads in the GEMM kernels, checked in the gfx950
 assembly that the build flags produce (CPU only: hipcc cross-compiles).
 
-The loader waves of the register-staged GEMM instantiations issue their
-global loads as inline asm and store each register set to LDS after an
-explicit partial `s_waitcnt vmcnt`.  This is only correct while the compiler
-leaves those registers alone until the wait; `asm_flow` proves that for the
-code as built, and fails if a compiler or code change copies, spills or
-reuses one of them while its load may be in flight.  The wait counts
-themselves are checked against the issue order in `test_wait_counts`.
+The kernels issue every load through compiler builtins, whose waits the
+compiler inserts itself.  A load written as inline asm with an explicit
+`s_waitcnt vmcnt` is only correct while the compiler leaves its destination
+registers alone until the wait; `asm_flow` checks that by dataflow, and the
+build requires that no such load exists at all.
 """
 import os
 import shutil
@@ -30,23 +28,23 @@ def kernels_asm(tmp_path_factory):
     return open(out).read()
 
 
-def test_build_check_fails_on_a_planted_read(tmp_path):
-    """The same check runs in build(): a source mutant whose loader reads a
-    register of a load that may still be in flight makes it fail."""
+def test_build_check_fails_on_a_planted_asm_load(tmp_path):
+    """The same check runs in build(): a source mutant that issues a load
+    through inline asm makes it fail."""
     if not os.path.exists(B.HIPCC) and shutil.which("hipcc") is None:
         pytest.skip("hipcc not available")
     src = open(os.path.join(B.CSRC, "kernels.hip")).read()
-    anchor = "    for (int j = 0; j < RS; ++j) gload(j, j);\n"
+    anchor = "  f32x16 acc[TM][TN];\n"
     assert anchor in src
-    planted = anchor + ("    { int sink; asm volatile(\"v_mov_b32 %0, %1\" : \"=v\"(sink) : \"v\"(ra[0][0][0]));\n"
-                        "      asm volatile(\"\" :: \"v\"(sink)); }\n")
+    planted = ("  { i32x4 v; asm volatile(\"global_load_dwordx4 %0, %1, off\\n s_waitcnt vmcnt(0)\" : \"=v\"(v) : \"v\"(Abase) : \"memory\");\n"
+               "    asm volatile(\"\" :: \"v\"(v)); }\n") + anchor
     mutant = tmp_path / "kernels.hip"
-    mutant.write_text(src.replace(anchor, planted))
-    with pytest.raises(RuntimeError, match="in-flight"):
+    mutant.write_text(src.replace(anchor, planted, 1))
+    with pytest.raises(RuntimeError, match="GEMM"):
         B.check_loader_asm(str(mutant), str(tmp_path / "kernels.s"))
 
 
-def test_loader_registers_untouched_until_waited(kernels_asm):
+def test_kernels_have_no_asm_loads(kernels_asm):
     checked = 0
     for name, lines in asm_flow.functions(kernels_asm).items():
         n, bad = asm_flow.analyse(lines)
@@ -54,8 +52,7 @@ def test_loader_registers_untouched_until_waited(kernels_asm):
             continue
         checked += 1
         assert not bad, "%s: %d instructions touch in-flight load registers, e.g. %s" % (name, len(bad), bad[:5])
-    # the register-staged 256x192 tile, with and without epilogue addends
-    assert checked == 2
+    assert checked == 0
 
 
 # A planted mistake on hand-written assembly: the analysis must flag a copy of
@@ -109,37 +106,3 @@ def test_branch_paths_merge():
 """
     (lines,) = asm_flow.functions(asm).values()
     assert asm_flow.analyse(lines)[1] == ["v_mov_b32_e32 v6, v3"]
-
-
-def test_wait_counts():
-    """The loader stores slab j after a wait that leaves outstanding exactly
-    the loads issued after slab j's: those of slabs j+1 .. j+RS-1 (the ones
-    that exist).  Simulated over the issue order (RS register sets, SB LDS
-    slabs, LA + LB loads per slab) for short and long K loops."""
-    for RS in (2, 3, 4):
-        for SB in (2, 3):
-            for KT in range(1, 12):
-                L = 14
-                issued = []  # slab of each load, in issue order
-
-                def gload(s):
-                    if s < KT:
-                        issued.extend([s] * L)
-
-                def lstore(s):
-                    if s >= KT:
-                        return
-                    younger = sum(L for q in range(1, RS) if s + q < KT)  # the kernel's count
-                    last = max(i for i, x in enumerate(issued) if x == s)
-                    assert len(issued) - 1 - last == younger, (RS, SB, KT, s)
-                    # slab s's register set (s mod RS) has not yet been reloaded
-                    assert s + RS not in issued
-
-                for j in range(RS):
-                    gload(j)
-                for j in range(SB - 1):
-                    lstore(j)
-                    gload(j + RS)
-                for kt in range(KT):
-                    lstore(kt + SB - 1)
-                    gload(kt + SB - 1 + RS)

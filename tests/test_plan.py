@@ -26,9 +26,9 @@ from ring_sim import Race, Sim, buffer_sizes
 
 
 def simulate(op, N, m, k, n, dir="uni", chunks=1, sched="decomposed", out="f32", n_comm=1, seed=0, dist="int",
-             data=None, bucket="f32", hop="copy"):
+             data=None, bucket="f32", hop="copy", group=0):
     plan = nat.cm_ring_plan(op=op, n_ranks=N, m=m, k=k, n=n, dir=dir, chunks=chunks, sched=sched, out_dtype=out,
-                            n_comm=n_comm, bucket=bucket, hop=hop)
+                            n_comm=n_comm, bucket=bucket, hop=hop, group=group)
     if data is None:
         if op == "ag":
             a, w = gen.ag_inputs(N, m, k, n, dist, seed)
@@ -138,7 +138,7 @@ def test_ag_step0_gemm_is_emitted_before_the_hops(dir, chunks, n_comm):
     """A graph dispatches nodes in program order: step 0's GEMM, which reads
     only the ranks' own shards, comes before step 0's hop copies of the same
     chunk (emitted after them, it started behind the copies)."""
-    plan = nat.cm_ring_plan(op="ag", n_ranks=4, m=16, k=64, n=64, dir=dir, chunks=chunks, n_comm=n_comm)
+    plan = nat.cm_ring_plan(op="ag", n_ranks=4, m=16, k=64, n=64, dir=dir, chunks=chunks, n_comm=n_comm, group=1)
     ops, jobs = nat.cm_plan_program(plan)
     for j in range(plan.chunks):
         idx = [i for i, o in enumerate(ops) if o.step == 0 and o.chunk == j and o.kind in (nat.CM_OPK_GEMM,
@@ -515,3 +515,119 @@ def test_stress_mode_is_eager_only():
     a = nat.cm_ring_plan(op="rs", n_ranks=4, m=64, k=256, n=256, chunks=2, exec_mode="eager", stress=7)
     b = nat.cm_ring_plan(op="rs", n_ranks=4, m=64, k=256, n=256, chunks=2, exec_mode="eager")
     assert (a.n_ops, a.n_jobs, a.n_events, a.ws_bytes) == (b.n_ops, b.n_jobs, b.n_events, b.ws_bytes)
+
+
+# ---------------------------------------------------------------- grouped launches
+GROUPED = [(op, N, dir, g, n_comm) for op in ("ag", "rs") for N in (2, 3, 4, 5, 8) for dir in ("uni", "bi")
+           for g in (2, 3, 4) for n_comm in sorted({1, 2, N})]
+
+
+def _partition(plan):
+    return list(plan.group_len[:plan.n_launches])
+
+
+@pytest.mark.parametrize("op,N,dir,g,n_comm", GROUPED)
+def test_grouped_launches_match_oracle(op, N, dir, g, n_comm):
+    """Steps grouped per launch (at most g): exact on integers against the
+    oracle, race-free, every output written once; the launch partition
+    covers every step once, the ReduceScatter's owner step is a launch of its
+    own, and each launch's jobs come in runs of b_share that read the same
+    weights."""
+    m, k, n = 3, 64, 64
+    hop = "add" if op == "rs" else "copy"
+    for out in ("f32", "bf16"):
+        plan, sim, a, w = simulate(op, N, m, k, n, dir, 1, "decomposed", out, n_comm, hop=hop, group=g)
+        assert np.array_equal(output(sim, plan), expect(op, a, w, out))
+        assert (sim.writes[nat.CM_BUF_Y] == 1).all()
+    part = _partition(plan)
+    assert sum(part) == plan.n_steps and all(1 <= x <= g for x in part)
+    if op == "rs":
+        assert part[-1] == 1
+    ops, jobs = nat.cm_plan_program(plan)
+    gemms = [o for o in ops if o.kind == nat.CM_OPK_GEMM]
+    assert len(gemms) == plan.n_launches
+    for o in gemms:
+        assert o.b_share >= 1 and o.n_jobs % o.b_share == 0 and o.n_jobs <= 128
+        js = jobs[o.first_job:o.first_job + o.n_jobs]
+        for i in range(0, o.n_jobs, o.b_share):
+            run = js[i:i + o.b_share]
+            assert len({(j.b_buf, j.b_off, j.rank) for j in run}) == 1
+    if any(x > 1 for x in part):
+        assert plan.slots == (max(2, plan.arc_cw) if op == "ag" else max(2, plan.n_steps))
+
+
+@pytest.mark.parametrize("op,N", [("ag", 8), ("rs", 8)])
+def test_group_one_is_the_step_program(op, N):
+    """group = 1 is the one-step-per-launch program; every group setting
+    multiplies the same shards into the same outputs."""
+    hop = "add" if op == "rs" else "copy"
+    kw = dict(op=op, n_ranks=N, m=4, k=64, n=64, chunks=1, n_comm=1, hop=hop)
+    p1 = nat.cm_ring_plan(group=1, **kw)
+    assert _partition(p1) == [1] * p1.n_steps and p1.slots == 2
+    ops1, jobs1 = nat.cm_plan_program(p1)
+    assert all(o.b_share == 1 for o in ops1 if o.kind == nat.CM_OPK_GEMM)
+    key = lambda j: (j.rank, j.dir, j.index, j.c_buf)
+    for g in (2, 3, 4):
+        pg = nat.cm_ring_plan(group=g, **kw)
+        _, jobsg = nat.cm_plan_program(pg)
+        gem1 = sorted(key(j) for j in jobs1 if j.a_buf >= 0)
+        gemg = sorted(key(j) for j in jobsg if j.a_buf >= 0)
+        assert gem1 == gemg
+
+
+@pytest.mark.parametrize("op,dir", [("ag", "uni"), ("ag", "bi"), ("rs", "uni"), ("rs", "bi")])
+def test_grouped_dropped_dependency_is_caught(op, dir):
+    """Negative control for grouped launches: removing any one in-schedule wait makes a race."""
+    N, m, k, n = 5, 3, 64, 64
+    hop = "add" if op == "rs" else "copy"
+    plan = nat.cm_ring_plan(op=op, n_ranks=N, m=m, k=k, n=n, dir=dir, chunks=1, n_comm=2, hop=hop, group=2)
+    assert any(x > 1 for x in _partition(plan))
+    sizes = buffer_sizes(plan)
+    a, w = (gen.ag_inputs if op == "ag" else gen.rs_inputs)(N, m, k, n, "int", 0)
+    base = Sim(plan, sizes, {nat.CM_BUF_X: a, nat.CM_BUF_W: w})
+    waits = [i for i, o in enumerate(base.ops) if o.kind == nat.CM_OPK_WAIT and o.step >= 0]
+    assert waits
+    caught = 0
+    for i in waits:
+        sim = _drop_op(Sim(plan, sizes, {nat.CM_BUF_X: a, nat.CM_BUF_W: w}), i)
+        try:
+            sim.run()
+        except Race:
+            caught += 1
+    assert caught == len(waits), "%d of %d dropped waits went unnoticed" % (len(waits) - caught, len(waits))
+
+
+def test_auto_groups_the_gpt3_step():
+    """At the GPT-3 MLP shape the cost model groups steps (each rank's 151 MB
+    of weights is then streamed once per launch instead of once per step)."""
+    ag = nat.cm_ring_plan(op="ag", n_ranks=8, m=256, k=12288, n=6144, chunks=1, n_comm=1)
+    rs = nat.cm_ring_plan(op="rs", n_ranks=8, m=256, k=6144, n=12288, chunks=1, n_comm=1, hop="add")
+    for p in (ag, rs):
+        assert p.n_launches < p.n_steps and sum(_partition(p)) == p.n_steps
+    assert _partition(rs)[-1] == 1
+
+
+REPLAN = [dict(op=op, n_ranks=N, m=m, k=k, n=n, dir=dir, n_comm=nc, hop=hop, group=g, copy_gbps=cg)
+          for op, hop in (("ag", "copy"), ("rs", "add"), ("rs", "copy"), ("rs_pipe", "add"))
+          for N, m, k, n in ((8, 256, 12288, 6144), (8, 512, 4096, 1792), (4, 16, 64, 64), (5, 3, 64, 128))
+          for dir in ("uni", "bi") for nc in (1, 2) for g in (0, 2) for cg in (0.0, 333.0)
+          if not (op == "rs_pipe" and dir == "bi")]
+
+
+@pytest.mark.parametrize("kw", REPLAN)
+def test_replanning_a_plans_request_reproduces_it(kw):
+    """The executors re-derive a caller's plan from its own request (with its
+    chunk count) and refuse a mismatch; planning must therefore be a fixed
+    point: the filled-in request plans to the same schedule."""
+    if kw["op"] == "ag":
+        kw = dict(kw, n=kw["n"], k=kw["k"])
+    else:
+        kw = dict(kw, k=kw["n"] if kw["op"] == "ag" else kw["k"])
+    p = nat.cm_ring_plan(**kw)
+    d = nat.cm_plan_desc.from_buffer_copy(p.desc)
+    d.chunks = p.chunks
+    q = nat.cm_ring_plan(desc=d)
+    for f in ("chunks", "n_steps", "arc_cw", "arc_ccw", "tile_m", "tile_n", "n_ops", "n_jobs", "n_events",
+              "ws_bytes", "split", "n_launches", "slots"):
+        assert getattr(p, f) == getattr(q, f), f
+    assert list(p.group_len) == list(q.group_len)
