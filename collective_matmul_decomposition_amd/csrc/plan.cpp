@@ -127,10 +127,18 @@ const char *last_error() { return g_last_error.c_str(); }
 // AG naive: gathered activations G[r][T][k] bf16.
 // RS decomposed: buckets  bkt[dir][p][j][r][m][n/c] fp32 (bf16 with bucket_bf16),
 //   p < 2; with add-and-forward hops also partial slots
-//   part[dir][q][j][r][m][n/c] fp32 after them, q < plan.slots.
+//   part[dir][q][j][r][m][n/c] fp32 after them, q < plan.slots, and, when steps
+//   are grouped per launch, the owners' arrived buckets arr[r][dir][m][n] fp32.
 // RS pipe / naive: partials P[r][j][T][n/c] fp32, then ring slots
 //   R[p][r][m][n/c] fp32; with add-and-forward hops the ring slots are per
 //   chunk, R[j][p][r][m][n/c].
+// Whether the plan groups steps per launch (some launch covers several steps).
+bool steps_grouped(const cm_plan &pl) {
+  for (int i = 0; i < pl.n_launches && i < CM_MAX_RANKS; ++i)
+    if (pl.group_len[i] > 1) return true;
+  return false;
+}
+
 WsLayout ws_layout(const cm_plan &pl) {
   const cm_plan_desc &d = pl.desc;
   const size_t N = d.n_ranks, m = d.m, k = d.k, n = d.n, c = pl.chunks, T = N * m;
@@ -173,6 +181,10 @@ WsLayout ws_layout(const cm_plan &pl) {
       L.partial = L.total;
       L.part_dir_bytes = (size_t)std::max(2, pl.slots) * N * m * n * 4;
       L.total += ndir * L.part_dir_bytes;
+      if (steps_grouped(pl)) {  // + the owners' arrivals arr[r][dir][m][n] fp32
+        L.acc = L.total;
+        L.total += N * ndir * m * n * 4;
+      }
     }
   } else if (d.hop_add) {  // PIPE / RS naive with add-and-forward hops: ring slots per chunk
     L.partial = 0;
@@ -479,31 +491,38 @@ double group_timeline(const cm_plan &p, const std::vector<int> &len) {
   }
   const int last = bi ? p.arc_cw : N - 1;
   const double add1 = (double)N * d.m * d.n * 4.0 * 3.0 / (kGroupAddGBps * 1e9) * 1e6;
+  // grouped: the owner's partial is an ordinary step and a final add writes
+  // Out (reads the arrivals and the own partial, writes the output)
+  bool final_add = false;
+  for (int g : len) final_add = final_add || g > 1;
+  const int ndir = bi ? 2 : 1;
+  const double out_b = d.out_dtype == CM_F32 ? 4.0 : 2.0;
+  const double fin = (double)N * d.m * d.n * (4.0 * ndir + 4.0 + out_b) / (kGroupAddGBps * 1e9) * 1e6 + d.launch_us;
   double adds = 0;
   for (int g : len) {
     const int b = s + g - 1;
     int jpr = 0;
     for (int q = s; q <= b; ++q) jpr += step_dirs(p, q);
-    if (b == last) t = std::max(t, adds);
+    if (!final_add && b == last) t = std::max(t, adds);  // the owner's epilogue adds the arrivals
     t += group_launch_us(d, N * jpr, jpr, d.m, d.n, d.k);
     for (int q = s; q <= b && q < last; ++q)
       if (q >= 1) adds = std::max(adds, t) + (step_dirs(p, q) - (bi && q == p.arc_cw - p.arc_ccw ? 1 : 0)) * add1 + d.launch_us;
     s = b + 1;
   }
+  if (final_add) t = std::max(t, adds) + fin;
   return t;
 }
 
 // Choose the launch partition: every composition of the steps into groups of
-// at most gmax (the ReduceScatter's owner step alone at the end), or, beyond
-// 16 steps, equal groups (AllGather: the first step alone, so its hops start
-// at once).  The shortest predicted time wins; ties keep fewer launches.
+// at most gmax, or, beyond 16 steps, equal groups (AllGather: the first step
+// alone, so its hops start at once).  The shortest predicted time wins; ties
+// keep fewer launches.
 double choose_groups(const cm_plan &p, int gmax, std::vector<int> *best) {
   const cm_plan_desc &d = p.desc;
   const bool rs = d.op != CM_OP_AG_GEMM;
-  const int S = p.n_steps - (rs ? 1 : 0);  // steps free to group
+  const int S = p.n_steps;
   double best_t = -1;
-  auto consider = [&](std::vector<int> len) {
-    if (rs) len.push_back(1);
+  auto consider = [&](const std::vector<int> &len) {
     const double t = group_timeline(p, len);
     if (best_t < 0 || t < best_t - 1e-6 || (t < best_t + 1e-6 && len.size() < best->size())) {
       best_t = t;
@@ -1011,11 +1030,7 @@ struct Builder {
     exit_();
   }
 
-  bool grouped() const {
-    for (int i = 0; i < p.n_launches && i < CM_MAX_RANKS; ++i)
-      if (p.group_len[i] > 1) return true;
-    return false;
-  }
+  bool grouped() const { return steps_grouped(p); }
 
   // ---------------------------------------------- AG, steps grouped per launch
   // One chunk per shard; launch i multiplies steps [a, b] of every rank (one
@@ -1128,39 +1143,42 @@ struct Builder {
 
   // ------------------------- RS with add-and-forward hops, steps grouped
   // One chunk.  Launch i computes the partial products of steps [a, b] of
-  // every rank (rank-major, b_share jobs per rank); every step has a partial
-  // slot of its own.  A direction's first step stores straight into the next
+  // every rank (rank-major, b_share jobs per rank), each into a partial slot
+  // of its own; the owner's own partial (step `last`) is an ordinary step of
+  // the last launch.  A direction's first step stores straight into the next
   // rank's bucket slot; each later step's add-and-forward (partial + arrived
   // bucket -> the next rank's slot) follows its launch on the first comm
-  // stream, in step order.  The owner's step is the last launch, alone: it
-  // waits for the last add and adds the arrived bucket(s) in its epilogue.
+  // stream, in step order, and the adds of step last - 1 deliver into the
+  // owners' arrival blocks arr[q][dir].  A final add on the same stream then
+  // writes Out_q = (sum of arr[q][dir] over the directions) + own partial,
+  // the realigning addition of the bidirectional ring, in the same fp32
+  // order as an owner's epilogue would add them.
   void rs_hop_add_grouped() {
     const bool bi = d.dir == CM_RING_BI;
     const int ndir = bi ? 2 : 1;
     const int Pp = std::max(2, p.slots);
     const size_t blk = m * n * 4;
-    const int osz = d.out_dtype == CM_F32 ? 4 : 2;
     auto bkt = [&](int dir, int par, int r) -> size_t { return dir * L.slot_dir_bytes + (((size_t)par * N + r) * blk); };
     auto part = [&](int dir, int q, int r) -> size_t {
       return L.partial + dir * L.part_dir_bytes + (((size_t)q * N + r) * blk);
     };
+    auto arr = [&](int dir, int r) -> size_t { return L.acc + ((size_t)r * ndir + dir) * blk; };
     const int Lc = p.arc_cw, R = p.arc_ccw;
     const int last = bi ? Lc : N - 1;
     const int arc = bi ? Lc : N - 1;
     const int first[2] = {0, Lc - R};
     const int red = 1;
-    std::vector<int> ered(last + 1, -1);
+    // where the bucket that step s + 1 adds to is written (by step s's add, or
+    // by a direction's first GEMM): a bucket slot, or the owner's arrival block
+    auto dest = [&](int dr, int s, int r_to) -> size_t { return s + 1 == last ? arr(dr, r_to) : bkt(dr, (s + 1) % 2, r_to); };
+    int e_last_add = -1;
     entry();
     int a = 0;
     for (int li = 0; li < p.n_launches; ++li) {
       const int b = a + p.group_len[li] - 1;
       cur_step = a; cur_chunk = 0;
-      if (b == last) {
-        if (last >= 1) wait(0, ered[last - 1]);  // RAW: the arrived buckets
-      } else {
-        for (int s = b; s >= a; --s)
-          if (s >= Pp) wait(0, ered[s - Pp]);  // WAR: partial slot s % Pp was read by add(s - Pp)
-      }
+      for (int s = b; s >= a; --s)
+        if (s >= Pp) wait(0, e_last_add);  // WAR: a reused partial slot (only with fewer slots than steps)
       std::vector<cm_job_rec> jobs;
       int per_rank = 0;
       for (int r = 0; r < N; ++r) {
@@ -1172,14 +1190,12 @@ struct Builder {
             jb.a_buf = CM_BUF_X; jb.a_off = ((size_t)r * T + (size_t)bucket * m) * k * 2; jb.lda = (int)k;
             jb.b_buf = CM_BUF_W; jb.b_off = (size_t)r * n * k * 2; jb.ldb = (int)k;
             jb.ld_in = (int)n;
+            jb.c_buf = CM_BUF_WS; jb.ldc = (int)n; jb.c_dtype = CM_F32;
             return jb;
           };
-          if (s == last) {
+          if (s == last) {  // the owner's own share
             cm_job_rec jb = mk(0, r);
-            jb.c_buf = CM_BUF_Y; jb.c_off = (size_t)r * m * n * osz; jb.ldc = (int)n;
-            jb.c_dtype = d.out_dtype;
-            if (N > 1) { jb.in0_buf = CM_BUF_WS; jb.in0_off = bkt(0, s % 2, r); }
-            if (bi && R >= 1) { jb.in1_buf = CM_BUF_WS; jb.in1_off = bkt(1, s % 2, r); }
+            jb.c_off = part(0, s % Pp, r);
             jobs.push_back(jb);
             ++cnt;
             continue;
@@ -1189,8 +1205,7 @@ struct Builder {
             const int shift = dr == 0 ? 1 : -1;
             const int q = dr == 0 ? mod(r + (arc - s), N) : mod(r - (Lc - s), N);
             cm_job_rec jb = mk(dr, q);
-            jb.c_buf = CM_BUF_WS; jb.ldc = (int)n; jb.c_dtype = CM_F32;
-            jb.c_off = s == first[dr] ? bkt(dr, (s + 1) % 2, mod(r + shift, N)) : part(dr, s % Pp, r);
+            jb.c_off = s == first[dr] ? dest(dr, s, mod(r + shift, N)) : part(dr, s % Pp, r);
             jobs.push_back(jb);
             ++cnt;
           }
@@ -1199,8 +1214,7 @@ struct Builder {
       }
       gemm(jobs, (int)m, (int)n, (int)k, per_rank);
       const int eg = record(0);
-      if (b == last) break;
-      for (int s = a; s <= b; ++s) {
+      for (int s = a; s <= b && s < last; ++s) {
         cur_step = s;
         std::vector<cm_job_rec> rj;
         for (int dr = 0; dr < ndir; ++dr) {
@@ -1213,7 +1227,7 @@ struct Builder {
             jb.in0_buf = CM_BUF_WS; jb.in0_off = part(dr, s % Pp, r);
             jb.in1_buf = CM_BUF_WS; jb.in1_off = bkt(dr, s % 2, r);
             jb.ld_in = (int)n;
-            jb.c_buf = CM_BUF_WS; jb.c_off = bkt(dr, (s + 1) % 2, mod(r + shift, N)); jb.ldc = (int)n;
+            jb.c_buf = CM_BUF_WS; jb.c_off = dest(dr, s, mod(r + shift, N)); jb.ldc = (int)n;
             jb.c_dtype = CM_F32;
             rj.push_back(jb);
           }
@@ -1221,7 +1235,24 @@ struct Builder {
         if (rj.empty()) continue;  // every direction's first step stored straight into the slots
         wait(red, eg);  // RAW: the partials (and, through the compute stream, earlier direct stores)
         reduce(red, rj, (int)m, (int)n);
-        ered[s] = record(red);
+        e_last_add = record(red);
+      }
+      if (b == last) {
+        // the owners' final add: arr[q][0..ndir) + own partial -> Out_q
+        cur_step = last;
+        wait(red, eg);  // RAW: the own partials and any direct stores into arr
+        std::vector<cm_job_rec> fj;
+        for (int r = 0; r < N; ++r) {
+          cm_job_rec jb = job0();
+          jb.rank = r; jb.index = r;
+          jb.in0_buf = CM_BUF_WS; jb.in0_off = arr(0, r);
+          jb.in1_buf = CM_BUF_WS; jb.in1_off = part(0, last % Pp, r);
+          jb.ld_in = (int)n;
+          jb.c_buf = CM_BUF_Y; jb.c_off = (size_t)r * m * n * (d.out_dtype == CM_F32 ? 4 : 2); jb.ldc = (int)n;
+          jb.c_dtype = d.out_dtype;
+          fj.push_back(jb);
+        }
+        reduce(red, fj, (int)m, (int)n, ndir);
       }
       a = b + 1;
     }

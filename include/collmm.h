@@ -233,10 +233,12 @@ typedef struct {
                             most g.  A launch multiplies every rank's shards (or
                             bucket rows) of its steps, so each rank's weights are
                             streamed once per launch instead of once per step; a
-                            step still uses only shards that have arrived, and the
-                            ReduceScatter owner's final step is always a launch of
-                            its own.  Other ops and chunkings use one step per
-                            launch. */
+                            step still uses only shards that have arrived.  A
+                            grouped ReduceScatter computes the owner's own partial
+                            like any other step's and writes Out with a final add
+                            (arrived bucket(s) + own partial, in the fp32 order of
+                            the owner's epilogue) on the first comm stream.  Other
+                            ops and chunkings use one step per launch. */
 } cm_plan_desc;
 
 /* The resolved schedule.  Plain data: no heap, nothing to destroy. */
