@@ -423,7 +423,12 @@ double estimate_naive(const cm_plan_desc &d) {
 // scaled by the tile's efficiency).
 constexpr double kGroupComputeTflops = 1550.0;
 constexpr double kWeightUnhiddenGBps = 20000.0;
-constexpr int kMaxGroupAuto = 4;
+// At most three steps per launch when the model chooses: four steps of a rank
+// on the 256x256 tile read 1.3-1.4x the weight bytes from HBM (the tiles that
+// share a weight column drift further apart than L2 holds), which the model
+// does not see; measured on the GPT-3 MLP step, 4.86 ms with at most three
+// against 4.93 ms with at most four.
+constexpr int kMaxGroupAuto = 3;
 // Hop and add rates beside the step GEMMs, measured in the same runs (GPT-3
 // MLP: a 50 MB AllGather hop step by SDMA takes about 150 us, by the CU copy
 // kernel about 75 us; an add-and-forward step of 302 MB about 110 us).  They
@@ -514,9 +519,12 @@ double group_timeline(const cm_plan &p, const std::vector<int> &len) {
 }
 
 // Choose the launch partition: every composition of the steps into groups of
-// at most gmax, or, beyond 16 steps, equal groups (AllGather: the first step
-// alone, so its hops start at once).  The shortest predicted time wins; ties
-// keep fewer launches.
+// at most gmax, or, beyond 16 steps, equal groups.  An AllGather's first
+// launch is step 0 alone: it multiplies only the ranks' own shards, so the
+// GEMMs start at once while the first hops are in flight (measured on the
+// GPT-3 MLP: [1, 2, 2, 3] runs the op in 2251 us against 2354 us for
+// [2, 2, 4], whose first launch waits for a hop).  The shortest predicted
+// time wins; ties keep fewer launches.
 double choose_groups(const cm_plan &p, int gmax, std::vector<int> *best) {
   const cm_plan_desc &d = p.desc;
   const bool rs = d.op != CM_OP_AG_GEMM;
@@ -534,7 +542,8 @@ double choose_groups(const cm_plan &p, int gmax, std::vector<int> *best) {
     // depth-first over compositions of S with parts <= gmax
     std::function<void(int)> rec = [&](int rem) {
       if (rem == 0) { consider(cur); return; }
-      for (int g = 1; g <= std::min(gmax, rem); ++g) {
+      const int gtop = (!rs && cur.empty()) ? 1 : gmax;  // AllGather: step 0 alone
+      for (int g = 1; g <= std::min(gtop, rem); ++g) {
         cur.push_back(g);
         rec(rem - g);
         cur.pop_back();
