@@ -128,7 +128,7 @@ const char *last_error() { return g_last_error.c_str(); }
 // RS decomposed: buckets  bkt[dir][p][j][r][m][n/c] fp32 (bf16 with bucket_bf16),
 //   p < 2; with add-and-forward hops also partial slots
 //   part[dir][q][j][r][m][n/c] fp32 after them, q < plan.slots, and, when steps
-//   are grouped per launch, the owners' arrived buckets arr[r][dir][m][n] fp32.
+//   are grouped per launch, the owners' arrival blocks arr[r][2][m][n] fp32.
 // RS pipe / naive: partials P[r][j][T][n/c] fp32, then ring slots
 //   R[p][r][m][n/c] fp32; with add-and-forward hops the ring slots are per
 //   chunk, R[j][p][r][m][n/c].
@@ -181,9 +181,9 @@ WsLayout ws_layout(const cm_plan &pl) {
       L.partial = L.total;
       L.part_dir_bytes = (size_t)std::max(2, pl.slots) * N * m * n * 4;
       L.total += ndir * L.part_dir_bytes;
-      if (steps_grouped(pl)) {  // + the owners' arrivals arr[r][dir][m][n] fp32
+      if (steps_grouped(pl)) {  // + the owners' arrivals arr[r][2][m][n] fp32
         L.acc = L.total;
-        L.total += N * ndir * m * n * 4;
+        L.total += N * 2 * m * n * 4;
       }
     }
   } else if (d.hop_add) {  // PIPE / RS naive with add-and-forward hops: ring slots per chunk
@@ -502,7 +502,10 @@ double group_timeline(const cm_plan &p, const std::vector<int> &len) {
   for (int g : len) final_add = final_add || g > 1;
   const int ndir = bi ? 2 : 1;
   const double out_b = d.out_dtype == CM_F32 ? 4.0 : 2.0;
-  const double fin = (double)N * d.m * d.n * (4.0 * ndir + 4.0 + out_b) / (kGroupAddGBps * 1e9) * 1e6 + d.launch_us;
+  // one-way ring, N >= 3: the last add-and-forward is part of the final add
+  const bool fused = final_add && !bi && last >= 2;
+  const double fin = (double)N * d.m * d.n * (4.0 * (fused ? 2 : ndir) + 4.0 + out_b) / (kGroupAddGBps * 1e9) * 1e6 +
+                     d.launch_us;
   double adds = 0;
   for (int g : len) {
     const int b = s + g - 1;
@@ -510,7 +513,7 @@ double group_timeline(const cm_plan &p, const std::vector<int> &len) {
     for (int q = s; q <= b; ++q) jpr += step_dirs(p, q);
     if (!final_add && b == last) t = std::max(t, adds);  // the owner's epilogue adds the arrivals
     t += group_launch_us(d, N * jpr, jpr, d.m, d.n, d.k);
-    for (int q = s; q <= b && q < last; ++q)
+    for (int q = s; q <= b && q < last - (fused ? 1 : 0); ++q)
       if (q >= 1) adds = std::max(adds, t) + (step_dirs(p, q) - (bi && q == p.arc_cw - p.arc_ccw ? 1 : 0)) * add1 + d.launch_us;
     s = b + 1;
   }
@@ -1171,15 +1174,24 @@ struct Builder {
     auto part = [&](int dir, int q, int r) -> size_t {
       return L.partial + dir * L.part_dir_bytes + (((size_t)q * N + r) * blk);
     };
-    auto arr = [&](int dir, int r) -> size_t { return L.acc + ((size_t)r * ndir + dir) * blk; };
+    auto arr = [&](int dir, int r) -> size_t { return L.acc + ((size_t)r * 2 + dir) * blk; };
     const int Lc = p.arc_cw, R = p.arc_ccw;
     const int last = bi ? Lc : N - 1;
     const int arc = bi ? Lc : N - 1;
     const int first[2] = {0, Lc - R};
     const int red = 1;
+    // One-way ring with N >= 3: the add of step last - 1 and the owner's add
+    // are one launch.  Rank r's arrival pair arr[r] holds the bucket that
+    // reaches r at step last - 1 and r's own partial for it; the final add
+    // writes Out_{r+1} = (arr[r][0] + arr[r][1]) + own partial of r + 1, the
+    // fp32 additions of the ring in their order.
+    const bool fused = !bi && last - 1 > first[0];
     // where the bucket that step s + 1 adds to is written (by step s's add, or
-    // by a direction's first GEMM): a bucket slot, or the owner's arrival block
-    auto dest = [&](int dr, int s, int r_to) -> size_t { return s + 1 == last ? arr(dr, r_to) : bkt(dr, (s + 1) % 2, r_to); };
+    // by a direction's first GEMM): a bucket slot, or an arrival block
+    auto dest = [&](int dr, int s, int r_to) -> size_t {
+      if (fused) return s + 1 == last - 1 ? arr(0, r_to) : bkt(dr, (s + 1) % 2, r_to);
+      return s + 1 == last ? arr(dr, r_to) : bkt(dr, (s + 1) % 2, r_to);
+    };
     int e_last_add = -1;
     entry();
     int a = 0;
@@ -1215,6 +1227,7 @@ struct Builder {
             const int q = dr == 0 ? mod(r + (arc - s), N) : mod(r - (Lc - s), N);
             cm_job_rec jb = mk(dr, q);
             jb.c_off = s == first[dr] ? dest(dr, s, mod(r + shift, N)) : part(dr, s % Pp, r);
+            if (fused && s == last - 1) jb.c_off = arr(1, r);
             jobs.push_back(jb);
             ++cnt;
           }
@@ -1223,7 +1236,7 @@ struct Builder {
       }
       gemm(jobs, (int)m, (int)n, (int)k, per_rank);
       const int eg = record(0);
-      for (int s = a; s <= b && s < last; ++s) {
+      for (int s = a; s <= b && s < last - (fused ? 1 : 0); ++s) {
         cur_step = s;
         std::vector<cm_job_rec> rj;
         for (int dr = 0; dr < ndir; ++dr) {
@@ -1247,21 +1260,22 @@ struct Builder {
         e_last_add = record(red);
       }
       if (b == last) {
-        // the owners' final add: arr[q][0..ndir) + own partial -> Out_q
+        // the owners' final add: arr[q][0..ndir) + own partial -> Out_q (fused:
+        // arr[q - 1][0..2) + own partial)
         cur_step = last;
         wait(red, eg);  // RAW: the own partials and any direct stores into arr
         std::vector<cm_job_rec> fj;
         for (int r = 0; r < N; ++r) {
           cm_job_rec jb = job0();
           jb.rank = r; jb.index = r;
-          jb.in0_buf = CM_BUF_WS; jb.in0_off = arr(0, r);
+          jb.in0_buf = CM_BUF_WS; jb.in0_off = fused ? arr(0, mod(r - 1, N)) : arr(0, r);
           jb.in1_buf = CM_BUF_WS; jb.in1_off = part(0, last % Pp, r);
           jb.ld_in = (int)n;
           jb.c_buf = CM_BUF_Y; jb.c_off = (size_t)r * m * n * (d.out_dtype == CM_F32 ? 4 : 2); jb.ldc = (int)n;
           jb.c_dtype = d.out_dtype;
           fj.push_back(jb);
         }
-        reduce(red, fj, (int)m, (int)n, ndir);
+        reduce(red, fj, (int)m, (int)n, fused ? 2 : ndir);
       }
       a = b + 1;
     }
