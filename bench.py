@@ -846,6 +846,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
     ap.add_argument("--no-naive", action="store_true")
     ap.add_argument("--no-bi", action="store_true", help="skip the run on the bidirectional ring")
+    ap.add_argument("--bi-n-comm", type=int, default=2, help="comm streams of the bidirectional-ring run")
     ap.add_argument("--no-alone", action="store_true", help="skip timing G and C alone (the measurement modes)")
     ap.add_argument("--skip", default="none", choices=["none", "hops", "gemms"],
                     help="time the step itself in a measurement mode (hops or GEMMs replaced by empty "
@@ -932,8 +933,12 @@ def main():
         # the same step on the bidirectional ring
         bi_args = argparse.Namespace(**vars(args))
         bi_args.dir = "bi"
+        bi_args.n_comm = args.bi_n_comm  # one comm lane (copy engine queue) per direction
         rb = measure(bi_args, args.workload, args.steps, args.warmup, False, not args.no_trace)
-        bi = {"ring": "bi", "value": round(rb["value"], 2), "unit": "TFLOP/s", "ms_per_step": round(rb["ms_per_step"], 4),
+        bi = {"ring": "bi", "n_comm_streams": bi_args.n_comm, "value": round(rb["value"], 2), "unit": "TFLOP/s",
+              "ms_per_step": round(rb["ms_per_step"], 4),
+              "steps_per_launch_ag": list(rb["plan_ag"].group_len[:rb["plan_ag"].n_launches]),
+              "steps_per_launch_rs": list(rb["plan_rs"].group_len[:rb["plan_rs"].n_launches]),
               "pct_of_bf16_peak": round(100 * rb["value"] / PEAK_BF16_TFLOPS, 2), "overlap": rb.get("overlap"),
               "gemm_launches": rb.get("gemm_launches")}
         del rb
