@@ -846,7 +846,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
     ap.add_argument("--no-naive", action="store_true")
     ap.add_argument("--no-bi", action="store_true", help="skip the run on the bidirectional ring")
-    ap.add_argument("--bi-n-comm", type=int, default=2, help="comm streams of the bidirectional-ring run")
+    ap.add_argument("--bi-n-comm", type=int, default=1,
+                    help="comm streams of the bidirectional-ring run (2: one per direction; measured slower)")
     ap.add_argument("--no-alone", action="store_true", help="skip timing G and C alone (the measurement modes)")
     ap.add_argument("--skip", default="none", choices=["none", "hops", "gemms"],
                     help="time the step itself in a measurement mode (hops or GEMMs replaced by empty "
@@ -854,6 +855,7 @@ def main():
     ap.add_argument("--no-layer", action="store_true", help="skip the sequence-parallel layer forward")
     ap.add_argument("--no-share", action="store_true", help="skip one rank's share (rank 0's steps at real shape)")
     ap.add_argument("--no-backward", action="store_true", help="skip the MLP backward (bulk overlap)")
+    ap.add_argument("--no-c4", action="store_true", help="skip the small-chunk grid (d 2048, N 2/4/8, chunks 1/2/4)")
     ap.add_argument("--no-trace", action="store_true", help="time without the per-launch events")
     ap.add_argument("--sweep", choices=["c4", "c5"], help="instead of the step: the small-chunk grid (c4) or the "
                     "layer's GEMM + collective pairs (c5), one JSON line per case")
@@ -965,6 +967,23 @@ def main():
     share = None if args.no_share else measure_share(args.workload, max(10, args.steps))
     layer = None if args.no_layer else measure_layer(args, max(5, args.steps // 2), 2)
     backward = None if args.no_backward else measure_backward(args, args.workload, max(5, args.steps // 2), 2)
+    c4 = None
+    if not args.no_c4:
+        # the small-chunk regime grid (d = 2048, ffn 8192, 1024 tokens, N in {2, 4, 8}, chunks in {1, 2, 4}):
+        # where per-chunk GEMMs are too small to hide the hops and the launch overhead
+        c4 = []
+        T4, d4, f4 = 1024, 2048, 8192
+        for op in ("ag", "rs", "rs_pipe"):
+            for N4 in (2, 4, 8):
+                for c in (1, 2, 4):
+                    k4, n4 = (d4, f4 // N4) if op == "ag" else (f4 // N4, d4)
+                    r = measure_op(op, N4, T4 // N4, k4, n4, c, "uni", 1, 3, args.copy_engine)
+                    c4.append({key: r[key] for key in ("op", "N", "chunks", "decomposed_us", "gemm_busy_us",
+                                                       "hop_busy_us", "hidden_fraction", "naive_us",
+                                                       "speedup_over_naive", "declined_by_cost_model")})
+        log("c4 sweep: %s" % "; ".join("%s N=%d c=%d D %.0f naive x%.2f" % (
+            r["op"], r["N"], r["chunks"], r["decomposed_us"], r["speedup_over_naive"]) for r in c4))
+        torch.cuda.empty_cache()
 
     out = {
         "metric": "AG-GEMM / GEMM-RS TFLOP/s + % bf16 MFMA peak + overlap efficiency, 1 GPU",
@@ -1005,6 +1024,7 @@ def main():
         "one_rank_share": share,
         "layer": layer,
         "backward": backward,
+        "c4_sweep": c4,
     }
     print(json.dumps(out), flush=True)
 
