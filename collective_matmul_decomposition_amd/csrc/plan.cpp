@@ -423,12 +423,14 @@ double estimate_naive(const cm_plan_desc &d) {
 // scaled by the tile's efficiency).
 constexpr double kGroupComputeTflops = 1550.0;
 constexpr double kWeightUnhiddenGBps = 20000.0;
-// At most three steps per launch when the model chooses: four steps of a rank
-// on the 256x256 tile read 1.3-1.4x the weight bytes from HBM (the tiles that
-// share a weight column drift further apart than L2 holds), which the model
-// does not see; measured on the GPT-3 MLP step, 4.86 ms with at most three
-// against 4.93 ms with at most four.
-constexpr int kMaxGroupAuto = 3;
+// Steps per launch when the model chooses: at most three for the AllGather,
+// four for the ReduceScatter.  Four AllGather steps of a rank on the 256x256
+// tile read 1.3-1.4x the weight bytes from HBM (the tiles that share a weight
+// column drift further apart than L2 holds), which the model does not see:
+// measured on the GPT-3 MLP, the AllGather took 2251 us as [1, 2, 2, 3]
+// against 2354 us as [2, 2, 4]; the ReduceScatter 2368-2382 us as [4, 2, 2]
+// against 2530-2539 us as [2, 2, 2, 2].
+constexpr int kMaxGroupAutoAG = 3, kMaxGroupAutoRS = 4;
 // Hop and add rates beside the step GEMMs, measured in the same runs (GPT-3
 // MLP: a 50 MB AllGather hop step by SDMA takes about 150 us, by the CU copy
 // kernel about 75 us; an add-and-forward step of 302 MB about 110 us).  They
@@ -714,7 +716,7 @@ cm_status plan(const cm_plan_desc *desc, cm_plan *out) {
                            (d.op == CM_OP_AG_GEMM || (d.op == CM_OP_GEMM_RS && d.hop_add));
     if (groupable && d.group != 1) {
       const int ndir = bi ? 2 : 1;
-      int gmax = d.group == 0 ? kMaxGroupAuto : d.group;
+      int gmax = d.group != 0 ? d.group : (d.op == CM_OP_AG_GEMM ? kMaxGroupAutoAG : kMaxGroupAutoRS);
       gmax = std::min(gmax, std::max(1, kJobCap / (N * ndir)));
       gmax = std::min(gmax, p.n_steps);
       std::vector<int> ones(p.n_steps, 1), best;

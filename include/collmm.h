@@ -229,7 +229,8 @@ typedef struct {
                             and the add-and-forward GEMM->ReduceScatter (hop_add = 1)
                             on a uni- or bidirectional ring with one chunk: 0 = the
                             cost model picks how consecutive steps are grouped (at
-                            most 3 per launch), 1 = one step per launch, g >= 2 = at
+                            most 3 per launch for the AllGather, 4 for the
+                            ReduceScatter), 1 = one step per launch, g >= 2 = at
                             most g.  A launch multiplies every rank's shards (or
                             bucket rows) of its steps, so each rank's weights are
                             streamed once per launch instead of once per step; a
