@@ -208,6 +208,7 @@ def measure(args, workload, steps, warmup, with_naive, with_trace):
         # the dominant kernel: the launch shape with the most total time
         (name, rows, cols, depth, jobs, tm, tn, nadd, abytes), durs = max(gemm_stats.items(),
                                                                         key=lambda kv: sum(kv[1]))
+        dom_key = (name, rows, cols, depth, jobs, tm, tn, nadd, abytes)
         flops_launch = 2.0 * rows * cols * depth * jobs
         avg_us = float(np.mean(durs))
         intensity = flops_launch / abytes
@@ -253,6 +254,7 @@ def measure(args, workload, steps, warmup, with_naive, with_trace):
                         "chunks": plan.chunks}
         res["overlap"] = ov
 
+        gemm_alone_stats = {}  # launch shape -> durations with the hops skipped
         # G and C alone: the same programs (same launches, copies and edges)
         # with the hops, or the compute-stream launches, replaced by empty
         # operations, timed per op inside alternating AG/RS steps as D is
@@ -277,10 +279,36 @@ def measure(args, workload, steps, warmup, with_naive, with_trace):
                     torch.cuda.synchronize()
                 for name, i in (("ag", 0), ("rs", 1)):
                     alone[name][skip] = float(np.median([t[i].read()[1] for t in tr]))
+                if skip == "hops":
+                    # each launch's duration with the GEMMs alone (same programs, hops empty)
+                    for name, i in (("ag", 0), ("rs", 1)):
+                        for t in tr:
+                            g = [q for q in t[i].read()[0] if q[0] == nat.CM_OPK_GEMM]
+                            for key, q in zip(keys[name], g):
+                                gemm_alone_stats.setdefault(key, []).append(q[5] - q[4])
                 for ta, tb in tr:
                     ta.close()
                     tb.close()
             del ys1, wss1, ys2, wss2
+            # the dominant launch's roofline with the GEMMs alone: no hop (SDMA copy or
+            # add kernel) shares the device, which is what a profiler reproduces exactly
+            da = gemm_alone_stats.get(dom_key)
+            flops_launch = 2.0 * dom_key[1] * dom_key[2] * dom_key[3] * dom_key[4]
+            abytes = dom_key[8]
+            if da:
+                avg_a = float(np.mean(da))
+                ra = dict(roof)
+                if ra["bound"] == "mfma":
+                    ra["achieved"] = round(flops_launch / (avg_a * 1e-6) / 1e12, 1)
+                else:
+                    ra["achieved"] = round(abytes / (avg_a * 1e-6) / 1e9, 1)
+                ra["frac"] = round(ra["achieved"] / ra["peak"], 4)
+                ra["avg_launch_us"] = round(avg_a, 2)
+                ra["launches"] = len(da)
+                ra["mfma_tflops"] = round(flops_launch / (avg_a * 1e-6) / 1e12, 1)
+                ra["hbm_gbps"] = round(abytes / (avg_a * 1e-6) / 1e9, 1)
+                ra["measured"] = "GEMM-alone measurement mode (hops skipped, same programs)"
+                res["roofline_gemm_alone"] = ra
             for name, plan in (("ag", plan_ag), ("rs", plan_rs)):
                 o = ov[name]
                 D, Ga, Ca = o["decomposed_us"], alone[name]["hops"], alone[name]["gemms"]
@@ -1010,6 +1038,7 @@ def main():
                            "accumulate / bf16 out"},
         "pct_of_bf16_peak": round(100 * res["value"] / PEAK_BF16_TFLOPS, 2),
         "roofline": res.get("roofline"),
+        "roofline_gemm_alone": res.get("roofline_gemm_alone"),
         "cpu_baseline": cpu,
         "overlap": res.get("overlap"),
         "gemm_launches": res.get("gemm_launches"),
