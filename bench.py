@@ -639,7 +639,9 @@ def measure_layer(args, steps, warmup):
     HD = H * D
     ring = args.dir if args.dir != "bi" else "uni"
     plan = nat.cm_plan_layer(n_ranks=N, m=m, d=d, heads=H, ffn=fN, dir=ring, n_comm=args.n_comm,
-                             copy_engine=args.copy_engine, ag_chunks=1, rs_chunks=1, proj_chunks=0)
+                             copy_engine=args.layer_copy_engine, ag_chunks=1, rs_chunks=1, proj_chunks=0)
+    engines = {s: ("cu" if getattr(plan, s).desc.copy_engine == nat.CM_COPY_CU else "sdma")
+               for s in ("qkv", "proj", "fc1", "fc2")}
     x, wqkv, wo, w1, w2 = gen.layer_inputs_torch(N, m, d, H, D, fN, "normal", 0, "cuda")
     out = torch.empty((N, m, d), dtype=torch.float32, device="cuda")
     ws = torch.empty(plan.ws_bytes, dtype=torch.uint8, device="cuda")
@@ -706,7 +708,8 @@ def measure_layer(args, steps, warmup):
     res = {"workload": "sp-layer-fwd (N=8, 4096 tokens, d=8192, 64 heads x 128, ffn 28672)",
            "ms": round(layer_ms, 4), "tflops": round(total_fl / (layer_ms * 1e-3) / 1e12, 1),
            "pct_of_bf16_peak": round(100 * total_fl / (layer_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
-           "flops": total_fl, "ring": ring, "proj_chunks": plan.proj.chunks, "stages": st,
+           "flops": total_fl, "ring": ring, "proj_chunks": plan.proj.chunks,
+           "copy_engine": args.layer_copy_engine, "hops_on": engines, "stages": st,
            "stage_sum_ms": round(sum(times.values()) / 1e3, 4)}
     del x, wqkv, wo, w1, w2, out, ws
     torch.cuda.empty_cache()
@@ -857,7 +860,9 @@ def main():
     ap.add_argument("--chunks-ag", type=int, default=0)
     ap.add_argument("--chunks-rs", type=int, default=1, help="RS column chunks (0: cost model)")
     ap.add_argument("--n-comm", type=int, default=1, help="comm streams (copy lanes) per op")
-    ap.add_argument("--copy-engine", default="sdma", choices=["sdma", "cu"], help="what moves the ring hops")
+    ap.add_argument("--copy-engine", default="sdma", choices=["sdma", "cu", "auto"], help="what moves the ring hops")
+    ap.add_argument("--layer-copy-engine", default="auto", choices=["sdma", "cu", "auto"],
+                    help="what moves the layer's ring hops (auto: the planner chooses per stage)")
     ap.add_argument("--no-alt-copy", action="store_true", help="skip the run with the other copy engine")
     ap.add_argument("--rs-bucket", default="f32", choices=["f32", "bf16"],
                     help="element type of the circulating RS bucket (bf16: half the hop bytes, outside the "

@@ -21,7 +21,7 @@ CM_BF16, CM_F32 = range(2)
 CM_BUF_X, CM_BUF_W, CM_BUF_Y, CM_BUF_WS = range(4)
 CM_OPK_GEMM, CM_OPK_COPY, CM_OPK_RECORD, CM_OPK_WAIT, CM_OPK_REDUCE = range(5)
 CM_EXEC_GRAPH, CM_EXEC_EAGER = range(2)
-CM_COPY_SDMA, CM_COPY_CU = range(2)
+CM_COPY_SDMA, CM_COPY_CU, CM_COPY_AUTO = range(3)
 CM_ACT_NONE, CM_ACT_GELU = range(2)
 CM_SKIP_NONE, CM_SKIP_HOPS, CM_SKIP_GEMMS = range(3)
 CM_MAX_RANKS, CM_MAX_CHUNKS, CM_MAX_COMM = 64, 16, 32
@@ -182,7 +182,7 @@ _ENUMS = {
     "sched": {"decomposed": CM_SCHED_DECOMPOSED, "naive": CM_SCHED_NAIVE, "auto": CM_SCHED_AUTO},
     "dtype": {"bf16": CM_BF16, "f32": CM_F32},
     "exec": {"graph": CM_EXEC_GRAPH, "eager": CM_EXEC_EAGER},
-    "copy": {"sdma": CM_COPY_SDMA, "cu": CM_COPY_CU},
+    "copy": {"sdma": CM_COPY_SDMA, "cu": CM_COPY_CU, "auto": CM_COPY_AUTO},
     "hop": {"copy": 0, "add": 1},
     "act": {"none": CM_ACT_NONE, "gelu": CM_ACT_GELU},
     "skip": {"none": CM_SKIP_NONE, "hops": CM_SKIP_HOPS, "gemms": CM_SKIP_GEMMS},

@@ -567,10 +567,52 @@ double choose_groups(const cm_plan &p, int gmax, std::vector<int> *best) {
   return best_t;
 }
 
+// Engine choice (CM_COPY_AUTO): a planned op's predicted time plus what its
+// hops take from the GEMMs.  SDMA copies only contend for HBM: on the GPT-3
+// MLP AllGather, 352 MB of hops slowed the step GEMMs by about 83 us, the
+// hop bytes read and written at about 8.5 TB/s.  The CU copy kernel also
+// occupies compute units: about 0.3 of its time alone showed up in the op
+// (GPT-3 MLP AllGather; the SP layer's AllGather->QKV and AllGather->fc1,
+// where the SDMA hop chain outlasts the GEMMs and the CU copies won by
+// 100-380 us).  Grouped-capable ring ops are timed by their launch timeline;
+// the rest by the plan's estimate.
+constexpr double kSdmaContendGBps = 8500.0, kCuCopyExposed = 0.3;
+constexpr double kAutoCuMargin = 0.97;  // the copy kernel must win by 3%
+
+double engine_cost(const cm_plan &p) {
+  const cm_plan_desc &d = p.desc;
+  if (d.op == CM_OP_ALLGATHER) return p.est_total_us;  // no GEMM to take from
+  const int N = d.n_ranks;
+  double t = p.est_total_us;
+  if (N > 1 && p.chunks == 1 && (d.dir == CM_RING_UNI || d.dir == CM_RING_BI) && d.sched == CM_SCHED_DECOMPOSED &&
+      (d.op == CM_OP_AG_GEMM || (d.op == CM_OP_GEMM_RS && d.hop_add)) && p.n_launches >= 1) {
+    std::vector<int> len(p.group_len, p.group_len + std::min(p.n_launches, (int)CM_MAX_RANKS));
+    t = group_timeline(p, len);
+  }
+  double bytes = 0;  // what the hops copy (add-and-forward hops copy nothing)
+  if (d.op == CM_OP_AG_GEMM)
+    bytes = (double)(N - 1) * N * d.m * d.k * 2.0;
+  else if (!d.hop_add)
+    bytes = (double)(N - 1) * N * d.m * d.n * (d.bucket_bf16 ? 2.0 : 4.0);
+  if (d.copy_engine == CM_COPY_SDMA) return t + 2.0 * bytes / (kSdmaContendGBps * 1e9) * 1e6;
+  return t + kCuCopyExposed * (bytes / (kGroupCuCopyGBps * 1e9) * 1e6 + (bytes > 0 ? (N - 1) * kGroupCuCopyUs : 0.0));
+}
+
 }  // namespace
 
 cm_status plan(const cm_plan_desc *desc, cm_plan *out) {
   if (!desc || !out) { set_error("null argument"); return CM_ERR_INVALID_ARG; }
+  if (desc->copy_engine == CM_COPY_AUTO) {
+    cm_plan_desc ds = *desc, dc = *desc;
+    ds.copy_engine = CM_COPY_SDMA;
+    dc.copy_engine = CM_COPY_CU;
+    cm_plan ps, pc;
+    cm_status st = plan(&ds, &ps);
+    if (st != CM_OK) return st;
+    if ((st = plan(&dc, &pc)) != CM_OK) return st;
+    *out = engine_cost(pc) < kAutoCuMargin * engine_cost(ps) ? pc : ps;
+    return CM_OK;
+  }
   cm_plan_desc d = *desc;
   if (d.copy_gbps == 0) d.copy_gbps = d.copy_engine == CM_COPY_CU ? kDefaultCuCopyGBps : kDefaultCopyGBps;
   if (d.mfma_tflops == 0) d.mfma_tflops = kDefaultMfmaTflops;

@@ -133,8 +133,14 @@ typedef enum { CM_EXEC_GRAPH = 0, CM_EXEC_EAGER = 1 } cm_exec_mode;
  * copy engines (hipMemcpyDeviceToDeviceNoCU), which use no compute units.
  * CM_COPY_CU: the runtime's copy kernel (hipMemcpyDeviceToDevice), which
  * runs on compute units beside the GEMMs.  The two give identical results.
+ * CM_COPY_AUTO (a request only): the planner plans the op with each engine
+ * and keeps the one its cost model predicts faster, charging each for what
+ * its hops take from the GEMMs (HBM bandwidth for SDMA; HBM bandwidth and
+ * compute units for the copy kernel); a near tie keeps SDMA.  The returned
+ * plan's desc.copy_engine holds the engine chosen, so re-planning it gives
+ * the same plan.
  */
-typedef enum { CM_COPY_SDMA = 0, CM_COPY_CU = 1 } cm_copy_engine;
+typedef enum { CM_COPY_SDMA = 0, CM_COPY_CU = 1, CM_COPY_AUTO = 2 } cm_copy_engine;
 
 /*
  * Measurement modes: what a trace of the parts alone needs in order to set the

@@ -77,7 +77,7 @@ def status_of(**kw):
     (dict(out_dtype=5), nat.CM_ERR_UNSUPPORTED),
     (dict(tile=(96, 96)), nat.CM_ERR_UNSUPPORTED),
     (dict(exec_mode=4), nat.CM_ERR_INVALID_ARG),
-    (dict(copy_engine=2), nat.CM_ERR_INVALID_ARG),
+    (dict(copy_engine=3), nat.CM_ERR_INVALID_ARG),
 ])
 def test_plan_validation(kw, expect):
     assert status_of(**kw) == expect

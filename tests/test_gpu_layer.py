@@ -341,6 +341,22 @@ def test_layer_repeatable_and_bf16_out():
     assert np.array_equal(gen.torch_bf16_to_bits(c), gen.torch_bf16_to_bits(a.to(torch.bfloat16)))
 
 
+def test_layer_copy_engines_agree():
+    """The planner's engine choice (auto) and either engine forced give the
+    same layer output bit for bit: a hop copies the same bytes whichever
+    engine moves it."""
+    N, m, d, heads, ffn = 4, 128, 512, 2, 1024
+    bits, ts = layer_buffers(N, m, d, heads, ffn, seed=9)
+    outs = {}
+    for ce in ("auto", "sdma", "cu"):
+        plan = nat.cm_plan_layer(n_ranks=N, m=m, d=d, heads=heads, ffn=ffn, n_comm=1, ag_chunks=1, rs_chunks=1,
+                                 copy_engine=ce)
+        say("layer copy engine", ce, [getattr(plan, s).desc.copy_engine for s in ("qkv", "proj", "fc1", "fc2")])
+        (outs[ce],), _ = run_layer(plan, ts, N, m, d)
+    for ce in ("sdma", "cu"):
+        assert torch.equal(outs[ce].view(torch.int32), outs["auto"].view(torch.int32)), ce
+
+
 def test_layer_full_size_sampled():
     # the full sequence-parallel layer: N = 8, 4096 tokens, d = 8192, 64 heads
     # (8 per rank), ffn 28672 (3584 per rank); the configuration the bench times

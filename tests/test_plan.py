@@ -635,3 +635,49 @@ def test_replanning_a_plans_request_reproduces_it(kw):
               "ws_bytes", "split", "n_launches", "slots"):
         assert getattr(p, f) == getattr(q, f), f
     assert list(p.group_len) == list(q.group_len)
+
+
+ENGINE_CASES = [
+    # GPT-3 MLP fc1: seven 50 MB SDMA hop steps hide under the step GEMMs
+    (dict(op="ag", n_ranks=8, m=256, k=12288, n=6144), "sdma"),
+    # add-and-forward hops copy nothing: the engines tie and SDMA is kept
+    (dict(op="rs", n_ranks=8, m=256, k=6144, n=12288, hop="add"), "sdma"),
+    # SP layer AllGather->QKV and ->fc1: the SDMA hop chain (67 MB a step) outlasts the GEMMs
+    (dict(op="ag", n_ranks=8, m=512, k=8192, n=3072), "cu"),
+    (dict(op="ag", n_ranks=8, m=512, k=8192, n=3584), "cu"),
+]
+
+
+def _plan_fields(p):
+    return ([getattr(p, f) for f in ("chunks", "n_steps", "arc_cw", "arc_ccw", "tile_m", "tile_n", "n_ops", "n_jobs",
+                                    "n_events", "ws_bytes", "split", "n_launches", "slots", "est_total_us")]
+            + list(p.group_len))
+
+
+@pytest.mark.parametrize("kw,engine", ENGINE_CASES)
+def test_auto_copy_engine_picks_and_is_a_fixed_point(kw, engine):
+    """copy_engine=auto plans the request with each engine and keeps one; the
+    plan is the explicit engine's plan, its request names that engine, and
+    re-planning that request reproduces it."""
+    p = nat.cm_ring_plan(chunks=1, n_comm=1, copy_engine="auto", **kw)
+    assert p.desc.copy_engine == nat._ENUMS["copy"][engine]
+    q = nat.cm_ring_plan(chunks=1, n_comm=1, copy_engine=engine, **kw)
+    assert _plan_fields(p) == _plan_fields(q)
+    d = nat.cm_plan_desc.from_buffer_copy(p.desc)
+    r = nat.cm_ring_plan(desc=d)
+    assert _plan_fields(r) == _plan_fields(p) and r.desc.copy_engine == p.desc.copy_engine
+
+
+def test_auto_copy_engine_in_the_layer_plan():
+    """The SP layer's stages resolve the engine one by one: the AllGather
+    stages whose SDMA hops would outlast the GEMMs take the copy kernel, the
+    add-and-forward ReduceScatters keep SDMA; re-planning the layer's request
+    gives the same stage plans."""
+    lp = nat.cm_plan_layer(n_ranks=8, m=512, d=8192, heads=8, ffn=3584, n_comm=1, copy_engine="auto",
+                           ag_chunks=1, rs_chunks=1)
+    eng = {s: getattr(lp, s).desc.copy_engine for s in ("qkv", "proj", "fc1", "fc2")}
+    assert eng == {"qkv": nat.CM_COPY_CU, "proj": nat.CM_COPY_SDMA, "fc1": nat.CM_COPY_CU, "fc2": nat.CM_COPY_SDMA}
+    assert lp.desc.copy_engine == nat.CM_COPY_AUTO
+    again = nat.cm_plan_layer(desc=nat.cm_layer_desc.from_buffer_copy(lp.desc))
+    for s in ("qkv", "proj", "fc1", "fc2"):
+        assert _plan_fields(getattr(again, s)) == _plan_fields(getattr(lp, s))
