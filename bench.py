@@ -129,11 +129,13 @@ def measure(args, workload, steps, warmup, with_naive, with_trace):
         return pa, pr
 
     plan_ag, plan_rs = make_plans(args.skip)
+    # the engine each op's hops run on (the planner's choice when the request says auto)
+    hops_on = {k: "cu" if p.desc.copy_engine == nat.CM_COPY_CU else "sdma" for k, p in (("ag", plan_ag), ("rs", plan_rs))}
     log("%s plans: AG chunks=%d tile=%dx%d ws=%.0fMB launches %s | RS(%s) chunks=%d tile=%dx%d ws=%.0fMB "
-        "launches %s | n_comm=%d" % (
+        "launches %s | n_comm=%d | hops on %s" % (
             workload, plan_ag.chunks, plan_ag.tile_m, plan_ag.tile_n, plan_ag.ws_bytes / 1e6,
             list(plan_ag.group_len[:plan_ag.n_launches]), args.rs_op, plan_rs.chunks, plan_rs.tile_m, plan_rs.tile_n,
-            plan_rs.ws_bytes / 1e6, list(plan_rs.group_len[:plan_rs.n_launches]), n_comm))
+            plan_rs.ws_bytes / 1e6, list(plan_rs.group_len[:plan_rs.n_launches]), n_comm, hops_on))
 
     x, w1 = gen.ag_inputs_torch(N, m, d, fN, "normal", 0, "cuda")
     h, w2 = gen.rs_inputs_torch(N, m, fN, d, "normal", 0, "cuda")
@@ -179,7 +181,7 @@ def measure(args, workload, steps, warmup, with_naive, with_trace):
     value = flops_step / (wall / steps) / 1e12
     log("%s timed: %.3f ms/step, %.1f TFLOP/s" % (workload, ms_per_step, value))
     res = {"value": value, "ms_per_step": ms_per_step, "N": N, "T": T, "d": d, "f": f, "fN": fN, "m": m,
-           "plan_ag": plan_ag, "plan_rs": plan_rs, "n_comm": n_comm,
+           "plan_ag": plan_ag, "plan_rs": plan_rs, "n_comm": n_comm, "hops_on": hops_on,
            "tensors": (x, w1, y1, h, w2, y2)}
 
     if with_trace:
@@ -328,10 +330,12 @@ def measure(args, workload, steps, warmup, with_naive, with_trace):
                                                 o["hidden_fraction"] or 0.0))
 
     if with_naive:
+        # the naive schedule with the engine the decomposed AllGather uses, then with the other one
+        first = hops_on["ag"]
         pa = nat.cm_ring_plan(op="ag", n_ranks=N, m=m, k=d, n=fN, sched="naive", out_dtype="bf16", n_comm=n_comm,
-                              copy_engine=args.copy_engine)
+                              copy_engine=first)
         pr = nat.cm_ring_plan(op="rs", n_ranks=N, m=m, k=fN, n=d, sched="naive", out_dtype="bf16", n_comm=n_comm,
-                              copy_engine=args.copy_engine)
+                              copy_engine=first)
         yn1, wsn1 = buffers.alloc_outputs(pa)
         yn2, wsn2 = buffers.alloc_outputs(pr)
 
@@ -348,10 +352,10 @@ def measure(args, workload, steps, warmup, with_naive, with_trace):
         torch.cuda.synchronize()
         nwall = (time.perf_counter() - t0) / ns
         res["naive"] = {"ms_per_step": round(nwall * 1e3, 3), "tflops": round(flops_step / nwall / 1e12, 1),
-                        "speedup_of_decomposed": round(nwall * 1e3 / ms_per_step, 3), "copy_engine": args.copy_engine}
+                        "speedup_of_decomposed": round(nwall * 1e3 / ms_per_step, 3), "copy_engine": first}
         # the same naive schedule with the other engine: its collective moves one
         # rank's shard per copy, where the engines differ most
-        other = "cu" if args.copy_engine == "sdma" else "sdma"
+        other = "cu" if first == "sdma" else "sdma"
         pa2 = nat.cm_ring_plan(op="ag", n_ranks=N, m=m, k=d, n=fN, sched="naive", out_dtype="bf16", n_comm=n_comm,
                                copy_engine=other)
         pr2 = nat.cm_ring_plan(op="rs", n_ranks=N, m=m, k=fN, n=d, sched="naive", out_dtype="bf16", n_comm=n_comm,
@@ -372,7 +376,7 @@ def measure(args, workload, steps, warmup, with_naive, with_trace):
                                              "speedup_of_decomposed": round(owall * 1e3 / ms_per_step, 3)}
         res["naive"]["speedup_over_faster_naive"] = round(min(nwall, owall) * 1e3 / ms_per_step, 3)
         log("naive: %.3f ms (%s), %.3f ms (%s) -> decomposed is x%.2f faster than the faster one" % (
-            nwall * 1e3, args.copy_engine, owall * 1e3, other, res["naive"]["speedup_over_faster_naive"]))
+            nwall * 1e3, first, owall * 1e3, other, res["naive"]["speedup_over_faster_naive"]))
         if with_trace and "overlap" in res:
             # GEMM-only and copy-only times: the naive schedule runs the
             # monolithic GEMM and the collective one after the other, so each
@@ -434,6 +438,7 @@ def measure_op(op, N, m, k, n, chunks, ring, n_comm, reps, copy_engine="sdma"):
         plan = nat.cm_ring_plan(op=op, n_ranks=N, m=m, k=k, n=n, dir=ring, chunks=chunks, sched=sched,
                                 out_dtype="bf16", n_comm=n_comm, copy_engine=copy_engine)
         y, ws = buffers.alloc_outputs(plan)
+        out["hops_on_" + sched] = "cu" if plan.desc.copy_engine == nat.CM_COPY_CU else "sdma"
         ops, _ = nat.cm_plan_program(plan)
         cap = sum(1 for o in ops if o.kind in (nat.CM_OPK_GEMM, nat.CM_OPK_COPY, nat.CM_OPK_REDUCE))
         traces = [nat.Trace(cap) for _ in range(reps)]
@@ -860,7 +865,8 @@ def main():
     ap.add_argument("--chunks-ag", type=int, default=0)
     ap.add_argument("--chunks-rs", type=int, default=1, help="RS column chunks (0: cost model)")
     ap.add_argument("--n-comm", type=int, default=1, help="comm streams (copy lanes) per op")
-    ap.add_argument("--copy-engine", default="sdma", choices=["sdma", "cu", "auto"], help="what moves the ring hops")
+    ap.add_argument("--copy-engine", default="auto", choices=["sdma", "cu", "auto"],
+                    help="what moves the ring hops (auto: the planner chooses per op)")
     ap.add_argument("--layer-copy-engine", default="auto", choices=["sdma", "cu", "auto"],
                     help="what moves the layer's ring hops (auto: the planner chooses per stage)")
     ap.add_argument("--no-alt-copy", action="store_true", help="skip the run with the other copy engine")
@@ -936,7 +942,7 @@ def main():
     if not args.no_alt_copy:
         # the same step with the other engine moving the hops
         alt_args = argparse.Namespace(**vars(args))
-        alt_args.copy_engine = "cu" if args.copy_engine == "sdma" else "sdma"
+        alt_args.copy_engine = "cu" if res["hops_on"]["ag"] == "sdma" else "sdma"
         ra = measure(alt_args, args.workload, args.steps, args.warmup, False, not args.no_trace)
         alt = {"copy_engine": alt_args.copy_engine, "value": round(ra["value"], 2), "unit": "TFLOP/s",
                "ms_per_step": round(ra["ms_per_step"], 4), "overlap": ra.get("overlap"),
@@ -971,7 +977,7 @@ def main():
         bi_args.n_comm = args.bi_n_comm  # one comm lane (copy engine queue) per direction
         rb = measure(bi_args, args.workload, args.steps, args.warmup, False, not args.no_trace)
         bi = {"ring": "bi", "n_comm_streams": bi_args.n_comm, "value": round(rb["value"], 2), "unit": "TFLOP/s",
-              "ms_per_step": round(rb["ms_per_step"], 4),
+              "ms_per_step": round(rb["ms_per_step"], 4), "hops_on": rb["hops_on"],
               "steps_per_launch_ag": list(rb["plan_ag"].group_len[:rb["plan_ag"].n_launches]),
               "steps_per_launch_rs": list(rb["plan_rs"].group_len[:rb["plan_rs"].n_launches]),
               "pct_of_bf16_peak": round(100 * rb["value"] / PEAK_BF16_TFLOPS, 2), "overlap": rb.get("overlap"),
@@ -982,7 +988,7 @@ def main():
     if args.secondary != "none" and args.secondary != args.workload:
         s2 = measure(args, args.secondary, max(5, args.steps // 2), 2, not args.no_naive, not args.no_trace)
         secondary = {"workload": args.secondary, "value": round(s2["value"], 2), "unit": "TFLOP/s",
-                     "ms_per_step": round(s2["ms_per_step"], 4),
+                     "ms_per_step": round(s2["ms_per_step"], 4), "hops_on": s2["hops_on"],
                      "pct_of_bf16_peak": round(100 * s2["value"] / PEAK_BF16_TFLOPS, 2),
                      "roofline": s2.get("roofline"), "overlap": s2.get("overlap"), "naive": s2.get("naive")}
         del s2
@@ -990,7 +996,7 @@ def main():
         if not args.no_alt_copy:
             # the same step with the other engine moving the hops (at these small hops it matters)
             alt_args = argparse.Namespace(**vars(args))
-            alt_args.copy_engine = "cu" if args.copy_engine == "sdma" else "sdma"
+            alt_args.copy_engine = "cu" if secondary["hops_on"]["ag"] == "sdma" else "sdma"
             s3 = measure(alt_args, args.secondary, max(5, args.steps // 2), 2, False, not args.no_trace)
             secondary["alt_copy_engine"] = {"copy_engine": alt_args.copy_engine, "value": round(s3["value"], 2),
                                             "ms_per_step": round(s3["ms_per_step"], 4), "overlap": s3.get("overlap")}
@@ -1033,7 +1039,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "virtual_ranks": res["N"], "tokens": res["T"], "hidden": res["d"],
                    "ffn": res["f"], "ffn_per_rank": res["fN"], "ring": args.dir, "rs_variant": args.rs_op,
-                   "n_comm_streams": res["n_comm"], "copy_engine": args.copy_engine, "rs_bucket": args.rs_bucket,
+                   "n_comm_streams": res["n_comm"], "copy_engine": args.copy_engine, "hops_on": res["hops_on"], "rs_bucket": args.rs_bucket,
                    "rs_hop": rs_hop(args), "measurement_mode": args.skip,
                    "chunks_ag": res["plan_ag"].chunks,
                    "chunks_rs": res["plan_rs"].chunks,
