@@ -52,6 +52,43 @@ __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t *src, uin
   }
 }
 
+// The same transpose with 16-byte accesses on both sides, for cols and
+// ld_dst multiples of 8 and 16-byte aligned buffers: each thread reads 8
+// consecutive elements of a src row into the LDS tile, then gathers 8
+// consecutive rows of one column from the tile and writes them as one
+// 16-byte store along the dst row.  The tile's rows are padded by one dword
+// so that the column gathers of a wave fall into different banks.
+__global__ __launch_bounds__(256) void transpose16_kernel(const uint16_t *src, uint16_t *dst, int rows, int cols,
+                                                           int ld_dst, size_t src_batch, size_t dst_batch) {
+  __shared__ uint16_t tile[64][66];
+  const uint16_t *s = src + blockIdx.z * src_batch;
+  uint16_t *d = dst + blockIdx.z * dst_batch;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int t = threadIdx.x, q = t & 7, u = t >> 3;  // q: 8-element chunk, u: row (load) or column (store)
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rr = u + 32 * i, r = r0 + rr, c = c0 + 8 * q;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (r < rows && c < cols) v = *reinterpret_cast<const uint4 *>(s + (size_t)r * cols + c);
+    uint32_t *row = reinterpret_cast<uint32_t *>(&tile[rr][8 * q]);
+    row[0] = v.x;
+    row[1] = v.y;
+    row[2] = v.z;
+    row[3] = v.w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int cc = u + 32 * i, c = c0 + cc, r = r0 + 8 * q;
+    if (c < cols && r < ld_dst) {
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] = (uint32_t)tile[8 * q + 2 * j][cc] | ((uint32_t)tile[8 * q + 2 * j + 1][cc] << 16);
+      *reinterpret_cast<uint4 *>(d + (size_t)c * ld_dst + r) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 cm_status hip_fail(hipError_t e, const char *what) {
@@ -73,8 +110,15 @@ cm_status check_transpose(int batch, int rows, int cols, int ld_dst) {
 
 hipError_t launch_transpose(const void *src, void *dst, int batch, int rows, int cols, int ld_dst, hipStream_t s) {
   dim3 grid((cols + 63) / 64, (ld_dst + 63) / 64, batch);
-  hipLaunchKernelGGL(transpose_kernel, grid, dim3(256), 0, s, static_cast<const uint16_t *>(src),
-                     static_cast<uint16_t *>(dst), rows, cols, ld_dst, (size_t)rows * cols, (size_t)cols * ld_dst);
+  const bool vec = cols % 8 == 0 && ld_dst % 8 == 0 && aligned16(src) && aligned16(dst);
+  const uint16_t *sp = static_cast<const uint16_t *>(src);
+  uint16_t *dp = static_cast<uint16_t *>(dst);
+  if (vec)
+    hipLaunchKernelGGL(transpose16_kernel, grid, dim3(256), 0, s, sp, dp, rows, cols, ld_dst, (size_t)rows * cols,
+                       (size_t)cols * ld_dst);
+  else
+    hipLaunchKernelGGL(transpose_kernel, grid, dim3(256), 0, s, sp, dp, rows, cols, ld_dst, (size_t)rows * cols,
+                       (size_t)cols * ld_dst);
   return hipGetLastError();
 }
 

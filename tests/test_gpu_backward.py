@@ -61,7 +61,10 @@ def check(got_t, ref, mag, dtype, dist):
             assert (err <= bound).all(), "worst err/bound %g" % (err / np.maximum(bound, 1e-300)).max()
 
 
-@pytest.mark.parametrize("batch,rows,cols,ld", [(1, 1, 1, 1), (3, 70, 130, 128), (2, 64, 64, 64), (5, 33, 200, 100)])
+@pytest.mark.parametrize("batch,rows,cols,ld", [(1, 1, 1, 1), (3, 70, 130, 128), (2, 64, 64, 64), (5, 33, 200, 100),
+                                                # 16-byte path (cols and ld multiples of 8): ragged tiles, padding,
+                                                # a dst tile of padding only
+                                                (3, 70, 136, 72), (2, 100, 200, 104), (1, 8, 8, 8), (1, 5, 16, 136)])
 def test_transpose(batch, rows, cols, ld):
     say("transpose", batch, rows, cols, ld)
     src = torch.randint(-30000, 30000, (batch, rows, cols), dtype=torch.int16, device="cuda")
