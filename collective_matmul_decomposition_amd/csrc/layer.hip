@@ -56,11 +56,13 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
 // The probabilities' bf16 values feed both the numerator and the running sum,
 // so every output row is a convex combination of the value rows.  The kernel
 // is held to two waves per SIMD (accumulators in VGPRs, no AGPR moves); blocks
-// entirely below the causal diagonal skip the mask, and the rescale of the
-// output is skipped when no lane's running maximum moved.
+// entirely below the causal diagonal skip the mask, and the output is
+// rescaled only when some lane's running maximum outgrows the reference of
+// the exponentials by more than a fixed headroom (lazy rescaling).
 constexpr int kAttnD = 128;   // head dimension
 constexpr int kAttnBQ = 128;  // query rows per workgroup
 constexpr int kAttnBK = 64;   // keys per block (one softmax update)
+constexpr float kAttnLazy = 8.f;  // headroom of the lazy rescale, base 2
 
 struct AttnParams {
   const uint16_t *qkv;  // [N][T][3*H*D]
@@ -105,10 +107,14 @@ __device__ __forceinline__ void attn_load_k(const uint16_t *base, int ld, int kc
   }
 }
 
-// One block of values into registers: 4 keys x 8 dims per thread.
+// One block of values into registers: 4 keys x 8 dims per thread.  Thread t
+// takes keys 4 (t % 16) .. +3 and dims 8 (t / 16) .. +7, so that the 16 lanes
+// that store to LDS together (attn_store_v) write the 16 units of one V^T row:
+// 128 contiguous bytes, every bank once (with the dims spread over the lanes
+// instead, the 16 lanes hit two 16-byte chunks, an 8-way bank conflict).
 __device__ __forceinline__ void attn_load_v(const uint16_t *base, int ld, int vcol, int T, int k0, int tid,
                                             uint4 (&vr)[4]) {
-  const int dg = tid & 15, kgp = tid >> 4;
+  const int dg = tid >> 4, kgp = tid & 15;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     vr[i] = *reinterpret_cast<const uint4 *>(base + (size_t)min(k0 + 4 * kgp + i, T - 1) * ld + vcol + 8 * dg);
@@ -127,7 +133,7 @@ __device__ __forceinline__ int attn_vt_unit(int dim, int u) {
 
 // V transposed into V^T units of 4 keys.
 __device__ __forceinline__ void attn_store_v(char *sV, int tid, const uint4 (&vr)[4]) {
-  const int dg = tid & 15, kgp = tid >> 4;
+  const int dg = tid >> 4, kgp = tid & 15;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int sh = (e & 1) * 16;
@@ -206,21 +212,42 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
     if (p.causal && k0 > q0 + 31) return;  // every key of the block is after every query of the wave
     const char *sVb = sV;
 
-    // S^T = K Q^T for keys k0 .. k0 + 63 (two 32-key tiles)
+    // S^T = K Q^T for keys k0 .. k0 + 63 (two 32-key tiles).  The key
+    // fragments of step ks + 1 are read from LDS while step ks multiplies.
     f32x16 s[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[t][e] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    bf16x8 kf[2][2];
+    auto load_kf = [&](int ks, int set) __attribute__((always_inline)) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int key = t * 32 + l32, ch = 2 * ks + g;
-        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(sKb + key * 256 + ((ch ^ (key & 15)) << 4));
-        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[t], 0, 0, 0);
+        kf[set][t] = *reinterpret_cast<const bf16x8 *>(sKb + key * 256 + ((ch ^ (key & 15)) << 4));
       }
+    };
+    load_kf(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      if (ks + 1 < 8) load_kf(ks + 1, (ks + 1) & 1);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks & 1][t], qf[ks], s[t], 0, 0, 0);
     }
+    // V^T fragments of the first 16-key step of O^T += V^T P^T: they do not
+    // depend on the softmax, so their reads are in flight during it.  Step
+    // q = 2 t + h covers keys 32 t + 16 h .. + 15; lane group g supplies the
+    // units u0 = 8 t + 4 h + g and u0 + 2 (one 16-byte chunk).
+    bf16x8 vf[2][4];
+    auto load_vf = [&](int q, int set) __attribute__((always_inline)) {
+      const int u0 = (q >> 1) * 8 + (q & 1) * 4 + g;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const int dim = dt * 32 + l32;
+        vf[set][dt] = *reinterpret_cast<const bf16x8 *>(sVb + dim * 128 + attn_vt_unit(dim, u0));
+      }
+    };
+    load_vf(0, 0);
     // online softmax: element e of tile t is key k0 + 32 t + 8 (e / 4) + 4 g + e % 4.
     // The mask is needed only where a key can lie after a query of the wave or
     // past the sequence; a key is kept while its offset 32 t + 8 (e / 4) + e % 4
@@ -242,12 +269,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, s[t][e]);
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc * p.scale_log2);
+    // Lazy rescaling: the reference point of the exponentials (m_run) moves
+    // only when some lane's maximum has grown past it by more than
+    // kAttnLazy (base 2); until then the probabilities are taken against the
+    // older, smaller reference and stay below 2^kAttnLazy.  Numerator and
+    // normaliser share the reference, so it cancels in O = (P V) / l.
+    const float m_cand = fmaxf(m_run, mloc * p.scale_log2);
+    const bool grow = __any(!(m_cand <= m_run + kAttnLazy));
+    const float m_new = grow ? m_cand : m_run;
     const float msub = m_new == -INFINITY ? 0.f : m_new;
     // exponentials with the hardware's base-2 exponential (v_exp_f32; results
     // below 2^-126 may flush to zero, far inside the error bound), the scale
-    // and the subtraction of the maximum in one fused multiply-add
-    const float alpha = __builtin_amdgcn_exp2f(m_run - msub);  // 0 on the first block (m_run = -inf)
+    // and the subtraction of the reference in one fused multiply-add
+    const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - msub) : 1.f;  // 0 on the first block
     // elements e, e + 1 are converted together (nearest even) into one register
     // of the B operand; the running sum adds the same bf16 values, two at a
     // time (a dot product with ones)
@@ -275,27 +309,22 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
     lsum += __shfl_xor(lsum, 32);
     l_run = l_run * alpha + lsum;
     m_run = m_new;
-    if (__any(alpha != 1.f)) {  // no lane's running maximum moved: nothing to rescale
+    if (grow) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
     }
 
-    // O^T += V^T P^T over the block's 64 keys (four 16-key steps)
+    // O^T += V^T P^T over the block's 64 keys (four 16-key steps), the next
+    // step's V^T fragments read while this one multiplies
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int q = 0; q < 4; ++q) {
+      if (q + 1 < 4) load_vf(q + 1, (q + 1) & 1);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int u0 = t * 8 + h * 4 + g;  // units of keys 32 t + 16 h + 4 g .. +3 and 8 keys later
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const int dim = dt * 32 + l32;
-          // units u0 and u0 + 2, one 16-byte chunk
-          const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(sVb + dim * 128 + attn_vt_unit(dim, u0));
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t][h], oacc[dt], 0, 0, 0);
-        }
-      }
+      for (int dt = 0; dt < 4; ++dt)
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[q & 1][dt], pf[q >> 1][q & 1], oacc[dt], 0, 0, 0);
+    }
   };
   for (int j = 0; j < nblk; j += 2) {
     block(j, sK0, sK1);
