@@ -30,7 +30,6 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void *attn_lds_ptr;
-typedef __attribute__((address_space(1))) void *attn_glob_ptr;
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
@@ -92,18 +91,21 @@ __device__ __forceinline__ void attn_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// One block of keys straight into its LDS buffer (global_load_lds: lane l of
-// a wave's load lands at the wave's 1 KB base + 16 l, no registers): load i of
-// wave w fills keys 4 (4 i + w) .. +3; lane l writes position l % 16 of key
+// One block of keys straight into its LDS buffer (a buffer load into LDS:
+// lane l of a wave's load lands at the wave's 1 KB base + 16 l, no
+// registers; as a buffer load the compiler counts it on the vector-memory
+// counter only, so its waits for this wave's own LDS reads stay exact): load i
+// of wave w fills keys 4 (4 i + w) .. +3; lane l writes position l % 16 of key
 // row l / 16, which holds the row's chunk (l % 16) ^ (key % 16).  Rows past the
-// sequence read the last key (their scores are masked).
-__device__ __forceinline__ void attn_load_k(const uint16_t *base, int ld, int kcol, int T, int k0, int wave, int lane,
-                                            char *sKbuf) {
+// sequence read the last key (their scores are masked).  Offsets are bytes
+// from the rank's QKV base (the rank's QKV spans less than 4 GiB).
+__device__ __forceinline__ void attn_load_k(__amdgpu_buffer_rsrc_t r, int ld, int kcol, int T, int k0, int wave,
+                                            int lane, char *sKbuf) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int grp = 4 * i + wave, key = 4 * grp + (lane >> 4), ch = (lane & 15) ^ (key & 15);
-    const uint16_t *src = base + (size_t)min(k0 + key, T - 1) * ld + kcol + 8 * ch;
-    __builtin_amdgcn_global_load_lds((attn_glob_ptr)src, (attn_lds_ptr)(sKbuf + grp * 1024), 16, 0, 0);
+    const uint32_t off = ((uint32_t)min(k0 + key, T - 1) * (uint32_t)ld + (uint32_t)(kcol + 8 * ch)) * 2u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (attn_lds_ptr)(sKbuf + grp * 1024), 16, off, 0, 0, 0);
   }
 }
 
@@ -197,7 +199,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
   // the compiler places before their LDS store) also covers the keys, which
   // were issued before them: vector-memory loads complete in order.
   uint4 vreg[4];
-  attn_load_k(base, p.ld_qkv, kcol, p.T, 0, wave, lane, sK0);
+  const __amdgpu_buffer_rsrc_t rqkv =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base), (short)0, -1, 0x00020000);
+  attn_load_k(rqkv, p.ld_qkv, kcol, p.T, 0, wave, lane, sK0);
   attn_load_v(base, p.ld_qkv, vcol, p.T, 0, tid, vreg);
   // one block: its keys in sKb, the next block's keys stream into sKn
   auto block = [&](const int j, const char *sKb, char *sKn) __attribute__((always_inline)) {
@@ -205,7 +209,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
     attn_barrier();  // every wave is done with block j - 1 (V^T and the other K buffer)
     attn_store_v(sV, tid, vreg);  // the compiler waits for vreg here: block j's keys are in LDS too
     if (j + 1 < nblk) {
-      attn_load_k(base, p.ld_qkv, kcol, p.T, k0 + kAttnBK, wave, lane, sKn);
+      attn_load_k(rqkv, p.ld_qkv, kcol, p.T, k0 + kAttnBK, wave, lane, sKn);
       attn_load_v(base, p.ld_qkv, vcol, p.T, k0 + kAttnBK, tid, vreg);
     }
     attn_barrier();  // block j's keys and values are in LDS, for every wave
@@ -233,6 +237,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
       if (ks + 1 < 8) load_kf(ks + 1, (ks + 1) & 1);
 #pragma unroll
       for (int t = 0; t < 2; ++t) s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks & 1][t], qf[ks], s[t], 0, 0, 0);
+    }
+    // keep that order through scheduling: reads of step ks + 1, then the MFMAs of step ks
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      if (ks + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
     // V^T fragments of the first 16-key step of O^T += V^T P^T: they do not
     // depend on the softmax, so their reads are in flight during it.  Step
@@ -324,6 +335,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[q & 1][dt], pf[q >> 1][q & 1], oacc[dt], 0, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (q + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
     }
   };
   for (int j = 0; j < nblk; j += 2) {
@@ -471,7 +487,8 @@ cm_status attention_check(int n_ranks, int T, int heads, int head_dim, int causa
     return CM_ERR_UNSUPPORTED;
   }
   const long long blocks = (long long)n_ranks * heads * ((T + kAttnBQ - 1) / kAttnBQ);
-  if (blocks > (1ll << 30) || (long long)T * 3 * heads * kAttnD * 2 * n_ranks > (1ll << 46)) {
+  // one rank's QKV rows are addressed by 32-bit byte offsets
+  if (blocks > (1ll << 30) || (long long)T * 3 * heads * kAttnD * 2 > 0xFFFFFFFFll) {
     set_error("attention: problem too large");
     return CM_ERR_SHAPE;
   }
