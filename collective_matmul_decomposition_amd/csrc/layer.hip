@@ -73,6 +73,16 @@ struct AttnParams {
   float scale_log2;     // log2(e) / sqrt(D)
 };
 
+// Combine a lane's value with the one of the lane 32 away (the other half of
+// the same query's keys): v_permlane32_swap exchanges the wave's two halves
+// between two registers, so each lane holds both values, lower half's first;
+// both lanes of a pair get the same bits.  max when `mx`, else the sum.
+__device__ __forceinline__ float half_pair(float v, bool mx) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float lo = __uint_as_float(r[0]), hi = __uint_as_float(r[1]);
+  return mx ? fmaxf(lo, hi) : lo + hi;
+}
+
 __device__ __forceinline__ int attn_logical_block() {
   // block b runs on XCD b % 8: give each XCD a contiguous range of logical
   // blocks, so the query blocks of one head (which share its keys and values)
@@ -274,12 +284,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
     }
     // the maximum of the raw scores: the scale is positive, and rounding is
     // monotone, so scaling the maximum gives the maximum of the scaled scores
-    float mloc = -INFINITY;
+    // (four independent chains, then the lane 32 away through a lane swap)
+    float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, s[t][e]);
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+      for (int e = 0; e < 16; ++e) m4[e & 3] = fmaxf(m4[e & 3], s[t][e]);
+    float mloc = half_pair(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])), true);
     // Lazy rescaling: the reference point of the exponentials (m_run) moves
     // only when some lane's maximum has grown past it by more than
     // kAttnLazy (base 2); until then the probabilities are taken against the
@@ -317,7 +328,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
         }
         pf[t][h] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
       }
-    lsum += __shfl_xor(lsum, 32);
+    lsum = half_pair(lsum, false);
     l_run = l_run * alpha + lsum;
     m_run = m_new;
     if (grow) {
