@@ -101,22 +101,31 @@ __device__ __forceinline__ void attn_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Keys and values are read by buffer loads from the rank's QKV rows: byte
+// offsets from the rank's base, which the buffer's size (T rows) bounds, so
+// that rows past the sequence read as zeros (the hardware's range check; their
+// scores are masked, and their zero values meet zero probabilities).  Each
+// thread's offsets within a block are fixed; a block adds k0 rows.
+//
 // One block of keys straight into its LDS buffer (a buffer load into LDS:
 // lane l of a wave's load lands at the wave's 1 KB base + 16 l, no
 // registers; as a buffer load the compiler counts it on the vector-memory
 // counter only, so its waits for this wave's own LDS reads stay exact): load i
 // of wave w fills keys 4 (4 i + w) .. +3; lane l writes position l % 16 of key
-// row l / 16, which holds the row's chunk (l % 16) ^ (key % 16).  Rows past the
-// sequence read the last key (their scores are masked).  Offsets are bytes
-// from the rank's QKV base (the rank's QKV spans less than 4 GiB).
-__device__ __forceinline__ void attn_load_k(__amdgpu_buffer_rsrc_t r, int ld, int kcol, int T, int k0, int wave,
-                                            int lane, char *sKbuf) {
+// row l / 16, which holds the row's chunk (l % 16) ^ (key % 16).
+__device__ __forceinline__ void attn_k_offsets(int ld, int kcol, int wave, int lane, uint32_t (&ko)[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int grp = 4 * i + wave, key = 4 * grp + (lane >> 4), ch = (lane & 15) ^ (key & 15);
-    const uint32_t off = ((uint32_t)min(k0 + key, T - 1) * (uint32_t)ld + (uint32_t)(kcol + 8 * ch)) * 2u;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (attn_lds_ptr)(sKbuf + grp * 1024), 16, off, 0, 0, 0);
+    ko[i] = ((uint32_t)key * (uint32_t)ld + (uint32_t)(kcol + 8 * ch)) * 2u;
   }
+}
+__device__ __forceinline__ void attn_load_k(__amdgpu_buffer_rsrc_t r, const uint32_t (&ko)[4], uint32_t kbytes,
+                                            int wave, char *sKbuf) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (attn_lds_ptr)(sKbuf + (4 * i + wave) * 1024), 16, ko[i] + kbytes, 0,
+                                             0, 0);
 }
 
 // One block of values into registers: 4 keys x 8 dims per thread.  Thread t
@@ -124,12 +133,19 @@ __device__ __forceinline__ void attn_load_k(__amdgpu_buffer_rsrc_t r, int ld, in
 // that store to LDS together (attn_store_v) write the 16 units of one V^T row:
 // 128 contiguous bytes, every bank once (with the dims spread over the lanes
 // instead, the 16 lanes hit two 16-byte chunks, an 8-way bank conflict).
-__device__ __forceinline__ void attn_load_v(const uint16_t *base, int ld, int vcol, int T, int k0, int tid,
-                                            uint4 (&vr)[4]) {
+__device__ __forceinline__ void attn_v_offsets(int ld, int vcol, int tid, uint32_t (&vo)[4]) {
   const int dg = tid >> 4, kgp = tid & 15;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    vr[i] = *reinterpret_cast<const uint4 *>(base + (size_t)min(k0 + 4 * kgp + i, T - 1) * ld + vcol + 8 * dg);
+  for (int i = 0; i < 4; ++i) vo[i] = ((uint32_t)(4 * kgp + i) * (uint32_t)ld + (uint32_t)(vcol + 8 * dg)) * 2u;
+}
+__device__ __forceinline__ void attn_load_v(__amdgpu_buffer_rsrc_t r, const uint32_t (&vo)[4], uint32_t kbytes,
+                                            uint4 (&vr)[4]) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, vo[i] + kbytes, 0, 0);
+    vr[i] = make_uint4(v[0], v[1], v[2], v[3]);
+  }
 }
 
 // Byte offset, within its 128-byte V^T row, of the 8-byte unit u (keys
@@ -143,20 +159,22 @@ __device__ __forceinline__ int attn_vt_unit(int dim, int u) {
   return ((chunk ^ ((dim >> 1) & 7)) << 4) | (half << 3);
 }
 
-// V transposed into V^T units of 4 keys.
+// V transposed into V^T units of 4 keys.  Unit e (dim 8 dg + e) takes the
+// 16-bit half e % 2 of register word e / 2 of the four keys' loads, two keys
+// per 32-bit word with one byte permute (v_perm_b32: selector bytes 0-3 pick
+// bytes of the second operand, 4-7 of the first).
 __device__ __forceinline__ void attn_store_v(char *sV, int tid, const uint4 (&vr)[4]) {
   const int dg = tid >> 4, kgp = tid & 15;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const int sh = (e & 1) * 16;
-    auto word = [&](int i) -> uint32_t {
+    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+    auto comp = [&](int i) -> uint32_t {
       const uint4 &v = vr[i];
-      const uint32_t w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
-      return (w >> sh) & 0xFFFFu;
+      return (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
     };
     uint2 pk;
-    pk.x = word(0) | (word(1) << 16);
-    pk.y = word(2) | (word(3) << 16);
+    pk.x = __builtin_amdgcn_perm(comp(1), comp(0), sel);
+    pk.y = __builtin_amdgcn_perm(comp(3), comp(2), sel);
     const int dim = 8 * dg + e;
     *reinterpret_cast<uint2 *>(sV + dim * 128 + attn_vt_unit(dim, kgp)) = pk;
   }
@@ -209,18 +227,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
   // the compiler places before their LDS store) also covers the keys, which
   // were issued before them: vector-memory loads complete in order.
   uint4 vreg[4];
-  const __amdgpu_buffer_rsrc_t rqkv =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base), (short)0, -1, 0x00020000);
-  attn_load_k(rqkv, p.ld_qkv, kcol, p.T, 0, wave, lane, sK0);
-  attn_load_v(base, p.ld_qkv, vcol, p.T, 0, tid, vreg);
+  // the rank's T rows of QKV; reads past them return zeros
+  const __amdgpu_buffer_rsrc_t rqkv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(base), (short)0, (int)((uint32_t)p.T * (uint32_t)p.ld_qkv * 2u), 0x00020000);
+  uint32_t ko[4], vo[4];
+  attn_k_offsets(p.ld_qkv, kcol, wave, lane, ko);
+  attn_v_offsets(p.ld_qkv, vcol, tid, vo);
+  const uint32_t blk_bytes = (uint32_t)kAttnBK * (uint32_t)p.ld_qkv * 2u;  // one block of rows
+  attn_load_k(rqkv, ko, 0u, wave, sK0);
+  attn_load_v(rqkv, vo, 0u, vreg);
   // one block: its keys in sKb, the next block's keys stream into sKn
   auto block = [&](const int j, const char *sKb, char *sKn) __attribute__((always_inline)) {
     const int k0 = j * kAttnBK;
     attn_barrier();  // every wave is done with block j - 1 (V^T and the other K buffer)
     attn_store_v(sV, tid, vreg);  // the compiler waits for vreg here: block j's keys are in LDS too
     if (j + 1 < nblk) {
-      attn_load_k(rqkv, p.ld_qkv, kcol, p.T, k0 + kAttnBK, wave, lane, sKn);
-      attn_load_v(base, p.ld_qkv, vcol, p.T, k0 + kAttnBK, tid, vreg);
+      attn_load_k(rqkv, ko, (uint32_t)(j + 1) * blk_bytes, wave, sKn);
+      attn_load_v(rqkv, vo, (uint32_t)(j + 1) * blk_bytes, vreg);
     }
     attn_barrier();  // block j's keys and values are in LDS, for every wave
     if (p.causal && k0 > q0 + 31) return;  // every key of the block is after every query of the wave
@@ -498,8 +521,9 @@ cm_status attention_check(int n_ranks, int T, int heads, int head_dim, int causa
     return CM_ERR_UNSUPPORTED;
   }
   const long long blocks = (long long)n_ranks * heads * ((T + kAttnBQ - 1) / kAttnBQ);
-  // one rank's QKV rows are addressed by 32-bit byte offsets
-  if (blocks > (1ll << 30) || (long long)T * 3 * heads * kAttnD * 2 > 0xFFFFFFFFll) {
+  // one rank's QKV rows, and a block of rows past them, are addressed by
+  // 32-bit byte offsets
+  if (blocks > (1ll << 30) || (long long)(T + kAttnBK) * 3 * heads * kAttnD * 2 > 0x7FFFFFFFll) {
     set_error("attention: problem too large");
     return CM_ERR_SHAPE;
   }
