@@ -197,6 +197,18 @@ def measure(args, workload, steps, warmup, with_naive, with_trace):
             return keys
 
         keys = {"ag": launch_keys(ops_ag, jobs_ag, "ag"), "rs": launch_keys(ops_rs, jobs_rs, "rs")}
+        # the last timed step's operations, start and end relative to each op's first one
+        kind_name = {nat.CM_OPK_GEMM: "gemm", nat.CM_OPK_COPY: "copy", nat.CM_OPK_REDUCE: "add"}
+        timeline = {}
+        for name, i in (("ag", 0), ("rs", 1)):
+            spans = traces[-1][i].read()[0]
+            t0s = min(q[4] for q in spans)
+            timeline[name] = [[kind_name.get(q[0], str(q[0])), q[1], q[2], round(q[4] - t0s, 1), round(q[5] - t0s, 1)]
+                              for q in sorted(spans, key=lambda q: q[4])]
+        res["timeline"] = timeline
+        if getattr(args, "timeline", False):
+            for name in ("ag", "rs"):
+                log("%s timeline (kind, stream, step, start us, end us): %s" % (name, timeline[name]))
         for tr_ag, tr_rs in traces:
             for name, tr in (("ag", tr_ag), ("rs", tr_rs)):
                 spans, total = tr.read()
@@ -896,6 +908,8 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the MLP backward (bulk overlap)")
     ap.add_argument("--no-c4", action="store_true", help="skip the small-chunk grid (d 2048, N 2/4/8, chunks 1/2/4)")
     ap.add_argument("--no-trace", action="store_true", help="time without the per-launch events")
+    ap.add_argument("--timeline", action="store_true",
+                    help="log the last timed step's operations (GEMM launches, copies, adds) with their times")
     ap.add_argument("--sweep", choices=["c4", "c5"], help="instead of the step: the small-chunk grid (c4) or the "
                     "layer's GEMM + collective pairs (c5), one JSON line per case")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -1060,6 +1074,7 @@ def main():
         "alt_rs_bucket": alt_bucket,
         "alt_rs_hop": alt_hop,
         "step_launches": res.get("step_launches"),
+        "timeline": res.get("timeline"),
         "secondary": secondary,
         "one_rank_share": share,
         "layer": layer,

@@ -423,6 +423,11 @@ double estimate_naive(const cm_plan_desc &d) {
 // scaled by the tile's efficiency).
 constexpr double kGroupComputeTflops = 1550.0;
 constexpr double kWeightUnhiddenGBps = 20000.0;
+// A launch of one step per rank is bound by its operand bytes rather than its
+// MFMA work: the GPT-3 MLP AllGather's single-step launch (8 jobs, 1.28 GB)
+// takes about 335 us against about 264 us per step in a two-step launch, an
+// operand stream of about 4.9 TB/s.  The launch time is the larger of the two.
+constexpr double kGroupHbmGBps = 4900.0;
 // Steps per launch when the model chooses: at most three for the AllGather,
 // four for the ReduceScatter.  Four AllGather steps of a rank on the 256x256
 // tile read 1.3-1.4x the weight bytes from HBM (the tiles that share a weight
@@ -446,7 +451,11 @@ double group_launch_us(const cm_plan_desc &d, int jobs, int share, double rows, 
   const double eff = choose_tile((int)rows, (int)cols, jobs, &tm, &tn);
   const double flops = 2.0 * jobs * rows * cols * depth;
   const double wbytes = (double)jobs / std::max(1, share) * cols * depth * 2.0;
-  return d.launch_us + wbytes / (kWeightUnhiddenGBps * 1e9) * 1e6 + flops / (kGroupComputeTflops * 1e12 * eff) * 1e6;
+  const double cbytes = d.op == CM_OP_AG_GEMM && d.out_dtype != CM_F32 ? 2.0 : 4.0;
+  const double bytes = wbytes + (double)jobs * rows * (depth * 2.0 + cols * cbytes);
+  const double compute = flops / (kGroupComputeTflops * 1e12 * eff) * 1e6;
+  return d.launch_us + wbytes / (kWeightUnhiddenGBps * 1e9) * 1e6 +
+         std::max(compute, bytes / (kGroupHbmGBps * 1e9) * 1e6);
 }
 
 // Jobs per rank of step s: AG step 0 multiplies the own shard only; a later
@@ -478,7 +487,7 @@ double group_timeline(const cm_plan &p, const std::vector<int> &len) {
   double t = 0;
   int s = 0;
   if (d.op == CM_OP_AG_GEMM) {
-    const int per_lane = std::max(1, std::min(2, N / std::max(1, lanes)));
+    const int per_lane = 1;  // one copy per lane and hop (shard-indexed receive slots)
     const bool sdma = d.copy_engine == CM_COPY_SDMA;
     const double gbps = sdma ? kGroupSdmaGBps : kGroupCuCopyGBps;
     const double lat = sdma ? kGroupSdmaCopyUs : kGroupCuCopyUs;
@@ -1099,8 +1108,17 @@ struct Builder {
     const int ndir = d.dir == CM_RING_BI ? 2 : 1;
     const int P = std::max(2, p.slots);
     const size_t chunk_bytes = m * k * 2;
-    auto slot_off = [&](int dir, int q, int r) -> size_t {
-      return dir * L.slot_dir_bytes + (((size_t)q * N + r) * chunk_bytes);
+    // Receive slots are indexed by shard: after hop s, rank r holds shard
+    // r - (s + 1) (r + s + 1 on the counter-clockwise arc) at position
+    // `shard` of slot s % P.  Rank r's hop s forwards the shard it received
+    // at hop s - 1, which sits at the same position of the previous slot, so
+    // a hop copies a lane's shard range from one slot to the next in place:
+    // one contiguous copy per lane (indexed by rank, the ring's wrap-around
+    // split every hop into two copies).  A lane owns a fixed shard range for
+    // every hop, so a hop's source was written by the same lane's previous
+    // hop (stream order) and its slot's last copy reader was that lane too.
+    auto slot_off = [&](int dir, int q, int shard) -> size_t {
+      return dir * L.slot_dir_bytes + (((size_t)q * N + shard) * chunk_bytes);
     };
     std::vector<std::vector<Group>> G(ndir);
     for (int dr = 0; dr < ndir; ++dr) G[dr] = groups(dr, ndir);
@@ -1114,31 +1132,18 @@ struct Builder {
       cur_step = s; cur_chunk = 0;
       for (int dr = 0; dr < ndir; ++dr) {
         if (s >= arcs[dr]) continue;
-        const int shift = dr == 0 ? 1 : -1;
         ehop[s][dr].assign(G[dr].size(), -1);
         for (size_t gi = 0; gi < G[dr].size(); ++gi) {
           const Group &g = G[dr][gi];
-          // WAR: slot s % P last held hop(s - P)'s shard, read by the launch of
-          // step s - P + 1 and, as the source of hop(s - P + 1), by the
-          // downstream ranks' copies
-          if (s >= P) {
-            wait(g.stream, egemm[s - P + 1]);
-            for (int r = g.a; r < g.b; ++r) {
-              int down = group_of(G[dr], mod(r + shift, N));
-              if (down != (int)gi) wait(g.stream, ehop[s - P + 1][dr][down]);
-            }
-          }
-          // RAW: the source slot was filled by hop(s-1) from the upstream ranks
-          if (s >= 1)
-            for (int r = g.a; r < g.b; ++r) {
-              int up = group_of(G[dr], mod(r - shift, N));
-              if (up != (int)gi) wait(g.stream, ehop[s - 1][dr][up]);
-            }
+          // WAR: slot s % P last held hop(s - P)'s shards, read by the launch
+          // of step s - P + 1 (and by this lane's hop s - P + 1)
+          if (s >= P) wait(g.stream, egemm[s - P + 1]);
+          // RAW: the source positions were filled by this lane's hop s - 1
+          const size_t bytes = (size_t)(g.b - g.a) * chunk_bytes;
           if (s == 0)
-            shifted_copy(g.stream, CM_BUF_X, 0, CM_BUF_WS, slot_off(dr, 0, 0), chunk_bytes, g.a, g.b, shift);
+            copy(g.stream, CM_BUF_X, (size_t)g.a * chunk_bytes, CM_BUF_WS, slot_off(dr, 0, g.a), bytes);
           else
-            shifted_copy(g.stream, CM_BUF_WS, slot_off(dr, (s - 1) % P, 0), CM_BUF_WS, slot_off(dr, s % P, 0),
-                         chunk_bytes, g.a, g.b, shift);
+            copy(g.stream, CM_BUF_WS, slot_off(dr, (s - 1) % P, g.a), CM_BUF_WS, slot_off(dr, s % P, g.a), bytes);
           ehop[s][dr][gi] = record(g.stream);
         }
       }
@@ -1172,7 +1177,7 @@ struct Builder {
               jb.a_off = (size_t)r * m * k * 2;
             } else {
               jb.a_buf = CM_BUF_WS;
-              jb.a_off = slot_off(dr, (s - 1) % P, r);
+              jb.a_off = slot_off(dr, (s - 1) % P, shard);
             }
             jb.lda = (int)k;
             jb.b_buf = CM_BUF_W;
