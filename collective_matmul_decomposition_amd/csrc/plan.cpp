@@ -927,21 +927,6 @@ struct Builder {
     return s;
   }
 
-  // Copy rank range [a, b) of a per-rank block array to the ranks shifted by
-  // `shift` (+1 clockwise, -1 counter-clockwise) in another array with the
-  // same per-rank block size; splits at the ring's wrap.
-  void shifted_copy(int stream, int sbuf, size_t sbase, int dbuf, size_t dbase, size_t block, int a, int b,
-                    int shift) {
-    int r = a;
-    while (r < b) {
-      int dr = mod(r + shift, N);
-      int run = 1;
-      while (r + run < b && mod(r + run + shift, N) == dr + run) ++run;
-      copy(stream, sbuf, sbase + (size_t)r * block, dbuf, dbase + (size_t)dr * block, block * run);
-      r += run;
-    }
-  }
-
   void entry() {
     cur_step = -1; cur_chunk = 0;
     int e = record(0);
@@ -1010,34 +995,25 @@ struct Builder {
                 ehop[s][j][dr][gi] = record(g.stream);
                 continue;
               }
+              // Ring slots are indexed by shard (as in ag_grouped): the lane
+              // owns shards [a, b) at every hop and copies them in place from
+              // the previous slot, so its hops depend on its own stream only.
               // WAR: the destination slot (parity s%2) was read by GEMM(s-1, j)
-              // and, as the source of hop(s-1, j), by the downstream ranks' copies
-              if (s >= 2) {
-                wait(g.stream, egemm[s - 1][j]);
-                for (int r = g.a; r < g.b; ++r) {
-                  int down = group_of(G[dr], mod(r + shift, N));
-                  if (down != (int)gi) wait(g.stream, ehop[s - 1][j][dr][down]);
-                }
-              }
-              // RAW: the source slot was filled by hop(s-1, j) from the upstream ranks
-              if (s >= 1) {
-                for (int r = g.a; r < g.b; ++r) {
-                  int up = group_of(G[dr], mod(r - shift, N));
-                  if (up != (int)gi) { wait(g.stream, ehop[s - 1][j][dr][up]); }
-                }
-              }
+              // (and, as the source of hop(s-1, j), by this lane)
+              if (s >= 2) wait(g.stream, egemm[s - 1][j]);
+              (void)shift;
               if (s == 0 && c == 1) {
-                // from the user's shards, which are laid out like the slots: a run of
-                // ranks is one copy (two at the ring's wrap)
-                shifted_copy(g.stream, CM_BUF_X, 0, CM_BUF_WS, slot_off(dr, 0, 0, 0), chunk_bytes, g.a, g.b, shift);
+                // from the user's shards, which are laid out like the slots: one copy
+                copy(g.stream, CM_BUF_X, (size_t)g.a * chunk_bytes, CM_BUF_WS, slot_off(dr, 0, 0, g.a),
+                     (size_t)(g.b - g.a) * chunk_bytes);
               } else if (s == 0) {
-                // from the user's shards: rank r's chunk j rows
-                for (int r = g.a; r < g.b; ++r)
-                  copy(g.stream, CM_BUF_X, ((size_t)r * m + (size_t)j * mc) * k * 2, CM_BUF_WS,
-                       slot_off(dr, 0, j, mod(r + shift, N)), chunk_bytes);
+                // from the user's shards: shard q's chunk j rows
+                for (int q = g.a; q < g.b; ++q)
+                  copy(g.stream, CM_BUF_X, ((size_t)q * m + (size_t)j * mc) * k * 2, CM_BUF_WS,
+                       slot_off(dr, 0, j, q), chunk_bytes);
               } else {
-                shifted_copy(g.stream, CM_BUF_WS, slot_off(dr, (s - 1) % 2, j, 0), CM_BUF_WS,
-                             slot_off(dr, s % 2, j, 0), chunk_bytes, g.a, g.b, shift);
+                copy(g.stream, CM_BUF_WS, slot_off(dr, (s - 1) % 2, j, g.a), CM_BUF_WS, slot_off(dr, s % 2, j, g.a),
+                     (size_t)(g.b - g.a) * chunk_bytes);
               }
               ehop[s][j][dr][gi] = record(g.stream);
             }
@@ -1064,7 +1040,7 @@ struct Builder {
                 jb.a_off = ((size_t)r * m + (size_t)j * mc) * k * 2;
               } else {
                 jb.a_buf = CM_BUF_WS;
-                jb.a_off = slot_off(dr, (s - 1) % 2, j, r);
+                jb.a_off = slot_off(dr, (s - 1) % 2, j, direct ? r : shard);
               }
               jb.lda = (int)k;
               jb.b_buf = CM_BUF_W;
@@ -1454,16 +1430,20 @@ struct Builder {
           }
           // clockwise: bucket (r + (Lc - s)) in bi, (r - s - 1) in uni -- both
           // equal r + (arc - s) with arc = N - 1 in uni
+          // Bucket slots are indexed by bucket: the bucket that rank r adds
+          // into at step s is the one rank r + 1 (r - 1 counter-clockwise)
+          // adds into at step s + 1, at the same position of the other slot,
+          // so a hop copies a lane's bucket range in place (one copy per lane).
           int arc = bi ? Lc : N - 1;
           int q = mod(r + (arc - s), N);
           cm_job_rec jb = mk(r, 0, q);
-          jb.c_buf = CM_BUF_WS; jb.c_off = bkt(0, s % 2, j, r); jb.ldc = (int)nc; jb.c_dtype = bdt;
+          jb.c_buf = CM_BUF_WS; jb.c_off = bkt(0, s % 2, j, q); jb.ldc = (int)nc; jb.c_dtype = bdt;
           if (s > 0) { jb.in0_buf = CM_BUF_WS; jb.in0_off = jb.c_off; }
           jobs.push_back(jb);
           if (bi && s >= Lc - R) {
             int qq = mod(r - (Lc - s), N);
             cm_job_rec jc = mk(r, 1, qq);
-            jc.c_buf = CM_BUF_WS; jc.c_off = bkt(1, s % 2, j, r); jc.ldc = (int)nc; jc.c_dtype = bdt;
+            jc.c_buf = CM_BUF_WS; jc.c_off = bkt(1, s % 2, j, qq); jc.ldc = (int)nc; jc.c_dtype = bdt;
             if (s > Lc - R) { jc.in0_buf = CM_BUF_WS; jc.in0_off = jc.c_off; }
             jobs.push_back(jc);
           }
@@ -1480,8 +1460,9 @@ struct Builder {
             // destination slot holds through GEMM(s, j), which waited for
             // hop(s-1, j), the slot's last reader.
             wait(g.stream, eg);
-            shifted_copy(g.stream, CM_BUF_WS, bkt(dr, s % 2, j, 0), CM_BUF_WS, bkt(dr, (s + 1) % 2, j, 0), blk, g.a,
-                         g.b, shift);
+            (void)shift;
+            copy(g.stream, CM_BUF_WS, bkt(dr, s % 2, j, g.a), CM_BUF_WS, bkt(dr, (s + 1) % 2, j, g.a),
+                 (size_t)(g.b - g.a) * blk);
             ehop[j][dr].push_back(record(g.stream));
           }
         }
@@ -1632,7 +1613,9 @@ struct Builder {
             jb.c_dtype = d.out_dtype;
             if (N > 1) { jb.in0_buf = CM_BUF_WS; jb.in0_off = A(j, r); }
           } else {
-            jb.c_buf = CM_BUF_WS; jb.c_off = S(s % 2, j, r); jb.ldc = (int)nc; jb.c_dtype = CM_F32;
+            // send slots indexed by the owner q, so a hop copies a lane's
+            // owner range in place (one copy per lane)
+            jb.c_buf = CM_BUF_WS; jb.c_off = S(s % 2, j, q); jb.ldc = (int)nc; jb.c_dtype = CM_F32;
           }
           jobs.push_back(jb);
         }
@@ -1646,9 +1629,9 @@ struct Builder {
           // WAR: receive slot s%2 was read by add(s-2, j) (on the add lane)
           if (s >= 2 && g.stream != red_stream) wait(g.stream, ered[s - 2][j]);
           if (s == 0)
-            shifted_copy(g.stream, CM_BUF_WS, S(0, j, 0), CM_BUF_WS, A(j, 0), blk, g.a, g.b, -1);
+            copy(g.stream, CM_BUF_WS, S(0, j, g.a), CM_BUF_WS, A(j, g.a), (size_t)(g.b - g.a) * blk);
           else
-            shifted_copy(g.stream, CM_BUF_WS, S(s % 2, j, 0), CM_BUF_WS, Rv(s % 2, j, 0), blk, g.a, g.b, -(s + 1));
+            copy(g.stream, CM_BUF_WS, S(s % 2, j, g.a), CM_BUF_WS, Rv(s % 2, j, g.a), (size_t)(g.b - g.a) * blk);
           const int e = record(g.stream);
           ehop[s][j].push_back(e);
           if (g.stream != red_stream) ecp.push_back(e);
@@ -1878,11 +1861,14 @@ struct Builder {
           if (t == 0) {
             wait(g.stream, eg);                                      // RAW on P[*][j]
             if (g.stream != red_stream) wait(g.stream, prev_chunk_done);  // WAR on the ring slots
+            // ring slots are indexed by bucket: the bucket rank r holds after
+            // hop t is the one rank r + 1 holds after hop t + 1, so later hops
+            // copy a lane's bucket range in place (one copy per lane)
             for (int r = g.a; r < g.b; ++r)
-              copy(g.stream, CM_BUF_WS, part(r, j, mod(r - 1, N)), CM_BUF_WS, ring(0, mod(r + 1, N)), blk);
+              copy(g.stream, CM_BUF_WS, part(r, j, mod(r - 1, N)), CM_BUF_WS, ring(0, mod(r - 1, N)), blk);
           } else {
             if (g.stream != red_stream) wait(g.stream, ered);          // RAW: reduce(t-1) wrote the source
-            shifted_copy(g.stream, CM_BUF_WS, ring((t - 1) % 2, 0), CM_BUF_WS, ring(t % 2, 0), blk, g.a, g.b, 1);
+            copy(g.stream, CM_BUF_WS, ring((t - 1) % 2, g.a), CM_BUF_WS, ring(t % 2, g.a), (size_t)(g.b - g.a) * blk);
           }
           if (g.stream != red_stream) ecp.push_back(record(g.stream));
         }
@@ -1892,14 +1878,14 @@ struct Builder {
           int q = mod(r - 2 - t, N);  // the bucket rank r received at hop t
           cm_job_rec jb = job0();
           jb.rank = r; jb.index = q;
-          jb.in0_buf = CM_BUF_WS; jb.in0_off = ring(t % 2, r);
+          jb.in0_buf = CM_BUF_WS; jb.in0_off = ring(t % 2, q);
           jb.in1_buf = CM_BUF_WS; jb.in1_off = part(r, j, q);
           jb.ld_in = (int)nc;
           if (t == N - 2) {
             jb.c_buf = CM_BUF_Y; jb.c_off = ((size_t)r * m * n + (size_t)j * nc) * osz; jb.ldc = (int)n;
             jb.c_dtype = d.out_dtype;
           } else {
-            jb.c_buf = CM_BUF_WS; jb.c_off = ring(t % 2, r); jb.ldc = (int)nc; jb.c_dtype = CM_F32;
+            jb.c_buf = CM_BUF_WS; jb.c_off = ring(t % 2, q); jb.ldc = (int)nc; jb.c_dtype = CM_F32;
           }
           rj.push_back(jb);
         }
