@@ -335,6 +335,32 @@ def test_hop_volume_is_the_ring_volume(op, dir, N):
     assert total == N * (N - 1) * per
 
 
+@pytest.mark.parametrize("op,dir,group", [("ag", "uni", 0), ("ag", "uni", 1), ("ag", "bi", 0), ("ag", "bi", 1),
+                                          ("rs", "uni", 0), ("rs", "bi", 0)])
+@pytest.mark.parametrize("n_comm", [1, 2, 3])
+def test_every_hop_is_one_copy_per_lane(op, dir, group, n_comm):
+    """Receive slots are indexed by shard (AG) or bucket (copy-hop RS), so a
+    hop moves a lane's range in place: one contiguous copy per lane, never
+    split at the ring's wrap-around (shard-sized copies only at an AllGather's
+    first hop with several chunks per shard, not used here)."""
+    N, m, k, n = 8, 16, 128, 256
+    plan = nat.cm_ring_plan(op=op, n_ranks=N, m=m, k=k, n=n, dir=dir, chunks=1, n_comm=n_comm, group=group)
+    ops, _ = nat.cm_plan_program(plan)
+    copies = [o for o in ops if o.kind == nat.CM_OPK_COPY]
+    per_hop = {}
+    for o in copies:
+        per_hop.setdefault((o.step, o.chunk, o.stream), []).append(o)
+    # one copy per (step, lane, direction) and each covers a whole lane range of
+    # shards or buckets; with one lane the two directions share it
+    lanes = min(n_comm, 3)
+    ndir = 2 if dir == "bi" else 1
+    per_lane = ndir if lanes < ndir else 1
+    assert all(len(v) <= per_lane for v in per_hop.values()), {key: len(v) for key, v in per_hop.items()}
+    blk = m * k * 2 if op == "ag" else m * n * 4
+    assert all(o.bytes % blk == 0 and o.bytes >= blk for o in copies)
+    assert max(o.bytes for o in copies) <= blk * -(-N // max(1, lanes // ndir))
+
+
 def _drop_op(sim, index):
     sim.ops = sim.ops[:index] + sim.ops[index + 1:]
     return sim
