@@ -124,7 +124,8 @@ typedef enum { CM_ACT_NONE = 0, CM_ACT_GELU = 1 } cm_act;
  * by op on the compute and comm streams.  Both run the same operations with
  * the same ordering; the graph form avoids the host-side cost of enqueueing
  * SDMA copies behind cross-stream waits.  Up to 256 graphs are cached per
- * host thread.
+ * process (shared by its host threads, least recently used dropped first,
+ * a quarter at a time, after a device-wide wait).
  */
 typedef enum { CM_EXEC_GRAPH = 0, CM_EXEC_EAGER = 1 } cm_exec_mode;
 
@@ -520,7 +521,8 @@ typedef struct {
   int dir;         /* cm_ring_dir of the QKV, fc1 and fc2 collective matmuls (the
                       output projection's pipeline-chunk ReduceScatter is a one-way ring) */
   int n_comm;      /* comm streams the call passes */
-  int copy_engine; /* cm_copy_engine */
+  int copy_engine; /* cm_copy_engine of every stage's hops; CM_COPY_AUTO lets the
+                      planner choose per stage (the stage plans name the engine chosen) */
   int exec_mode;   /* cm_exec_mode */
   int ag_chunks;   /* chunks of both AllGather->GEMMs (0 = cost model) */
   int rs_chunks;   /* chunks of the fc2 ReduceScatter (0 = cost model) */
@@ -629,8 +631,9 @@ typedef struct {
   int dx_dtype;     /* CM_F32 or CM_BF16: the input gradient */
   int dw_dtype;     /* CM_F32 or CM_BF16: the weight gradient */
   int exec_mode;    /* cm_exec_mode */
-  int copy_engine;  /* cm_copy_engine of the input gradient's ring hops; the
-                       weight gradient's AllGather always uses CM_COPY_CU */
+  int copy_engine;  /* cm_copy_engine of the input gradient's ring hops (CM_COPY_AUTO:
+                       the planner's choice); the weight gradient's AllGather always
+                       uses CM_COPY_CU */
 } cm_bwd_desc;
 
 typedef struct {
