@@ -428,14 +428,20 @@ constexpr double kWeightUnhiddenGBps = 20000.0;
 // takes about 335 us against about 264 us per step in a two-step launch, an
 // operand stream of about 4.9 TB/s.  The launch time is the larger of the two.
 constexpr double kGroupHbmGBps = 4900.0;
-// Steps per launch when the model chooses: at most three for the AllGather,
-// four for the ReduceScatter.  Four AllGather steps of a rank on the 256x256
-// tile read 1.3-1.4x the weight bytes from HBM (the tiles that share a weight
-// column drift further apart than L2 holds), which the model does not see:
-// measured on the GPT-3 MLP, the AllGather took 2251 us as [1, 2, 2, 3]
-// against 2354 us as [2, 2, 4]; the ReduceScatter 2368-2382 us as [4, 2, 2]
-// against 2530-2539 us as [2, 2, 2, 2].
-constexpr int kMaxGroupAutoAG = 3, kMaxGroupAutoRS = 4;
+// Steps per launch when the model chooses: at most four.  Four steps of a
+// rank read 1.3-1.4x the weight bytes from HBM (the tiles that share a
+// weight column drift further apart than L2 holds), which the model does not
+// see; with two copies per AllGather hop the cap was three ([1, 2, 2, 3] in
+// 2251 us against 2354 us as [2, 2, 4]), with one copy per hop [1, 3, 4]
+// measures 2139 us against 2183 us as [1, 2, 2, 3] (GPT-3 MLP, one box).  The
+// ReduceScatter took 2368-2382 us as [4, 2, 2] against 2530-2539 us as
+// [2, 2, 2, 2].
+constexpr int kMaxGroupAutoAG = 4, kMaxGroupAutoRS = 4;
+// The same L2 limit per weight column, in row tiles: the SP layer's
+// AllGather->fc1 (512-row shards, two row tiles per step) took 1894-1946 us
+// as [1, 1, 3, 3] (six row tiles per column) and 2156 us as [1, 1, 2, 4]
+// (eight).
+constexpr int kMaxRowTilesPerB = 6;
 // Hop and add rates beside the step GEMMs, measured in the same runs (GPT-3
 // MLP: a 50 MB AllGather hop step by SDMA takes about 150 us, by the CU copy
 // kernel about 75 us; an add-and-forward step of 302 MB about 110 us).  They
@@ -768,6 +774,13 @@ cm_status plan(const cm_plan_desc *desc, cm_plan *out) {
     if (groupable && d.group != 1) {
       const int ndir = bi ? 2 : 1;
       int gmax = d.group != 0 ? d.group : (d.op == CM_OP_AG_GEMM ? kMaxGroupAutoAG : kMaxGroupAutoRS);
+      if (d.group == 0) {
+        // at most kMaxRowTilesPerB row tiles read each weight column per launch
+        int tm, tn;
+        (void)choose_tile(d.m, d.n, N * ndir, &tm, &tn);
+        const int tiles_m = (d.m + tm - 1) / tm;
+        gmax = std::min(gmax, std::max(1, kMaxRowTilesPerB / tiles_m));
+      }
       gmax = std::min(gmax, std::max(1, kJobCap / (N * ndir)));
       gmax = std::min(gmax, p.n_steps);
       std::vector<int> ones(p.n_steps, 1), best;
