@@ -107,6 +107,25 @@ def rs_hop(args):
     return args.rs_hop if ok else "copy"
 
 
+_STREAMS = {}
+
+
+def streams(n_comm):
+    """The compute stream and n_comm comm streams.  One set for the whole run,
+    created at its start: torch hands out streams from a pool round-robin, and
+    the runtime spreads streams over the process's few hardware queues by
+    creation order, so streams made anew for every measurement landed on
+    different queues from run to run (a backward's bulk stream could share
+    the compute stream's queue and serialise behind it)."""
+    import torch
+    if not _STREAMS:
+        _STREAMS["compute"] = torch.cuda.Stream()
+        _STREAMS["comm"] = [torch.cuda.Stream() for _ in range(3)]
+    if n_comm > len(_STREAMS["comm"]):
+        _STREAMS["comm"] += [torch.cuda.Stream() for _ in range(n_comm - len(_STREAMS["comm"]))]
+    return _STREAMS["compute"], _STREAMS["comm"][:n_comm]
+
+
 def measure(args, workload, steps, warmup, with_naive, with_trace):
     import torch
     from collective_matmul_decomposition_amd import _native as nat
@@ -143,9 +162,8 @@ def measure(args, workload, steps, warmup, with_naive, with_trace):
     y2, ws2 = buffers.alloc_outputs(plan_rs)
     buffers.check_inputs(plan_ag, x, w1, y1, ws1)
     buffers.check_inputs(plan_rs, h, w2, y2, ws2)
-    compute = torch.cuda.Stream()
+    compute, comm = streams(n_comm)
     compute.wait_stream(torch.cuda.current_stream())  # inputs were written on the current stream
-    comm = buffers.comm_streams(n_comm)
     flops_op = 2.0 * N * T * d * fN  # each op: N ranks x [T x d] . [d x f/N]
     flops_step = 2 * flops_op
 
@@ -440,9 +458,8 @@ def measure_op(op, N, m, k, n, chunks, ring, n_comm, reps, copy_engine="sdma"):
     from collective_matmul_decomposition_amd import inputs as gen
     mk = gen.ag_inputs_torch if op == "ag" else gen.rs_inputs_torch
     x, w = mk(N, m, k, n, "normal", 0, "cuda")
-    compute = torch.cuda.Stream()
+    compute, comm = streams(n_comm)
     compute.wait_stream(torch.cuda.current_stream())
-    comm = buffers.comm_streams(n_comm)
     fn = nat.cm_ag_gemm if op == "ag" else nat.cm_gemm_rs
     flops = 2.0 * N * (N * m) * k * n
     out = {"op": op, "N": N, "m": m, "k": k, "n": n, "ring": ring, "n_comm": n_comm, "copy_engine": copy_engine}
@@ -515,7 +532,7 @@ def measure_share(workload, reps):
            "what": "virtual rank 0's ring steps at real shape (one GPU's share of the N-rank group); split-K step "
                    "GEMMs + one reduce launch per step; hops bring in the neighbour's shard / bucket"}
     total_flops, total_us = 0.0, 0.0
-    compute = torch.cuda.Stream()
+    compute, _ = streams(1)
     compute.wait_stream(torch.cuda.current_stream())
 
     def wall(fn, plan, x, w, y, ws, comm, n):
@@ -541,7 +558,7 @@ def measure_share(workload, reps):
             x = x[:1].contiguous()
         w = w[:1].contiguous()
         fn = nat.cm_ag_gemm if op == "ag" else nat.cm_gemm_rs
-        comm = buffers.comm_streams(1)
+        comm = streams(1)[1]
         D = {}
         for ce in ("sdma", "cu"):
             plan = nat.cm_ring_plan(op=op, n_ranks=N, m=m, k=k, n=n, share=1, out_dtype="bf16", n_comm=1,
@@ -662,9 +679,8 @@ def measure_layer(args, steps, warmup):
     x, wqkv, wo, w1, w2 = gen.layer_inputs_torch(N, m, d, H, D, fN, "normal", 0, "cuda")
     out = torch.empty((N, m, d), dtype=torch.float32, device="cuda")
     ws = torch.empty(plan.ws_bytes, dtype=torch.uint8, device="cuda")
-    compute = torch.cuda.Stream()
+    compute, comm = streams(args.n_comm)
     compute.wait_stream(torch.cuda.current_stream())
-    comm = buffers.comm_streams(args.n_comm)
     for _ in range(warmup):
         nat.cm_layer_forward(plan, x, wqkv, wo, w1, w2, out, ws, compute, comm)
     torch.cuda.synchronize()
@@ -746,9 +762,8 @@ def measure_backward(args, workload, steps, warmup):
     wl = WORKLOADS[workload]
     N, T, d, f = wl["N"], wl["T"], wl["d"], wl["f"]
     m, fN = T // N, f // N
-    compute = torch.cuda.Stream()
+    compute, comm = streams(3)
     compute.wait_stream(torch.cuda.current_stream())
-    comm = buffers.comm_streams(3)
     out = {"workload": workload}
     for kind, k, n in (("col", d, fN), ("row", fN, d)):
         act, w, grad = gen.backward_inputs_torch(kind, N, m, k, n, "normal", 0, "cuda")
@@ -928,6 +943,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     nat.lib()
+    streams(3)  # the run's streams, first, so they take the same hardware queues in every run
 
     if args.sweep:
         run_sweep(args.sweep, max(3, args.steps // 2), args.copy_engine)
