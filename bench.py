@@ -1006,14 +1006,23 @@ def main():
         bi_args.dir = "bi"
         bi_args.n_comm = args.bi_n_comm  # one comm lane (copy engine queue) per direction
         rb = measure(bi_args, args.workload, args.steps, args.warmup, False, not args.no_trace)
-        bi = {"ring": "bi", "n_comm_streams": bi_args.n_comm, "value": round(rb["value"], 2), "unit": "TFLOP/s",
-              "ms_per_step": round(rb["ms_per_step"], 4), "hops_on": rb["hops_on"],
-              "steps_per_launch_ag": list(rb["plan_ag"].group_len[:rb["plan_ag"].n_launches]),
-              "steps_per_launch_rs": list(rb["plan_rs"].group_len[:rb["plan_rs"].n_launches]),
-              "pct_of_bf16_peak": round(100 * rb["value"] / PEAK_BF16_TFLOPS, 2), "overlap": rb.get("overlap"),
-              "gemm_launches": rb.get("gemm_launches")}
+        def bi_row(rb):
+            return {"ring": "bi", "n_comm_streams": bi_args.n_comm, "value": round(rb["value"], 2),
+                    "unit": "TFLOP/s", "ms_per_step": round(rb["ms_per_step"], 4), "hops_on": rb["hops_on"],
+                    "steps_per_launch_ag": list(rb["plan_ag"].group_len[:rb["plan_ag"].n_launches]),
+                    "steps_per_launch_rs": list(rb["plan_rs"].group_len[:rb["plan_rs"].n_launches]),
+                    "pct_of_bf16_peak": round(100 * rb["value"] / PEAK_BF16_TFLOPS, 2), "overlap": rb.get("overlap"),
+                    "gemm_launches": rb.get("gemm_launches")}
+        bi = bi_row(rb)
         del rb
         torch.cuda.empty_cache()
+        if bi["hops_on"]["ag"] != "sdma":
+            # the bidirectional ring with its AllGather hops on the SDMA engines as well
+            bi_args.copy_engine = "sdma"
+            rb = measure(bi_args, args.workload, args.steps, args.warmup, False, not args.no_trace)
+            bi["sdma_hops"] = bi_row(rb)
+            del rb
+            torch.cuda.empty_cache()
     secondary = None
     if args.secondary != "none" and args.secondary != args.workload:
         s2 = measure(args, args.secondary, max(5, args.steps // 2), 2, not args.no_naive, not args.no_trace)
