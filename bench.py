@@ -519,8 +519,8 @@ def measure_share(workload, reps):
     hops bring in the neighbour's shard / bucket (N(0, 0.5^2) buckets for
     fc2).  Op time D: wall clock of `reps` graph replays without the trace,
     with the hops on the SDMA engines and on compute units (the faster is
-    reported); compute-only time: the same split step GEMM + reduce with no
-    ring (a one-rank plan), times N; per-launch times from a traced run."""
+    reported); compute-only time: the same program with its hops replaced by
+    empty operations (every edge kept); per-launch times from a traced run."""
     import torch
     from collective_matmul_decomposition_amd import _native as nat
     from collective_matmul_decomposition_amd import buffers
@@ -570,12 +570,15 @@ def measure_share(workload, reps):
             D[ce] = wall(fn, plan, x, w, y, ws, comm, reps)
             del y, ws
         best = min(D, key=D.get)
-        # compute only: one rank, one step, the same split
-        p1 = nat.cm_ring_plan(op=op, n_ranks=1, m=m, k=k, n=n, share=1, out_dtype="bf16", split_k=plan.split)
+        # compute only: the same program with its hops replaced by empty
+        # operations (every edge kept)
+        p1 = nat.cm_ring_plan(op=op, n_ranks=N, m=m, k=k, n=n, share=1, out_dtype="bf16", n_comm=1,
+                              copy_engine=best, skip="hops")
         y1, ws1 = buffers.alloc_outputs(p1)
-        x1 = x[:1] if op == "ag" else x[:, :m].contiguous()
-        g_only = N * wall(fn, p1, x1, w, y1, ws1, comm, 4 * reps)
-        del y1, ws1, x1
+        if op == "rs":
+            ws1[:peer.nbytes].copy_(torch.from_numpy(peer.view(np.uint8).reshape(-1)))
+        g_only = wall(fn, p1, x, w, y1, ws1, comm, reps)
+        del y1, ws1
         # per-launch breakdown (the trace's timing events slow the op down)
         plan = nat.cm_ring_plan(op=op, n_ranks=N, m=m, k=k, n=n, share=1, out_dtype="bf16", n_comm=1, copy_engine=best)
         y, ws = buffers.alloc_outputs(plan)
