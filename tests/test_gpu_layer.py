@@ -85,7 +85,8 @@ def run_attention(qkv_t, N, T, heads, causal):
 
 
 ATTN = [(1, 1, 1, True), (2, 17, 2, True), (1, 128, 1, True), (2, 200, 3, True), (1, 300, 2, False),
-        (3, 64, 1, False), (1, 513, 2, True), (2, 130, 1, False)]
+        (3, 64, 1, False), (1, 513, 2, True), (2, 130, 1, False), (1, 256, 1, True), (1, 384, 2, False),
+        (1, 640, 1, True)]
 
 
 @pytest.mark.parametrize("N,T,heads,causal", ATTN)
